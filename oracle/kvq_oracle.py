@@ -1,0 +1,532 @@
+"""Plain CPU oracle for single-query decode attention over a low-bit KV cache.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import or
+call anything in this package.  It shares no code, table or helper with the HIP
+library and imports nothing from it.
+
+Everything is numpy in float64 (inputs stored as bf16/fp32 upcast exactly), on
+purpose slow and unblocked so that it can be checked against the pages by eye.
+
+Pages cited (titles as they appear on the pages):
+  [P1] nalar.dev, "KV Cache Quantization Perturbs Attention Through Stored Keys
+       and Values"
+  [P2] nalar.dev, "KV cache quantization reduces cache bytes with separate
+       accuracy and kernel costs" (the page's address slug; it prints no title)
+  [P3] mercemay.com, "KV Cache Quantization and Per-Token Scale Placement"
+
+What is computed (the method reaches exact attention on a dequantized cache):
+  * write side: each new key/value vector is quantized as q = clamp(round(x/s))
+    with a scale s (P2 section "Quantization needs a scale convention"); the
+    scale is per token and head by default (P3 section "Per-token scales and
+    where they can live"), optionally with an integer zero point (P1 section
+    "Quantization granularity defines which values share a scale"), per channel
+    for keys with the factor moved onto the query (P3 section "The axis choice
+    is a kernel decision"), or as an 8-bit code relative to a per-head
+    super-scale (P3 section "Per-token scales and where they can live").
+  * read side: s_i = q.k_hat_i / sqrt(D), a = softmax(s), o = sum_i a_i v_hat_i
+    (P1 section "Key error acts before the softmax"; P2 section "Keys and values
+    need not have identical error sensitivity").
+
+Readings where the pages leave a step open (each restated where it is used):
+  R1  rounding is round-half-to-even of the quotient x / s_stored, evaluated as
+      one IEEE fp64 division followed by rint (P3's listing uses Python's
+      round(), which ties to even).
+  R2  scales/zero points are evaluated in fp64 and rounded once to their
+      storage type; codes are computed from the stored (rounded) scale.
+  R3  clamp after rounding; symmetric range [-(2^(b-1)-1), 2^(b-1)-1],
+      unsigned (zero-point) range [0, 2^b - 1].
+  R5  an all-zero vector gets scale 1 and codes 0 (P3's listing).
+  R6  zero point: the integer code that represents 0; the range is widened to
+      include 0; a flat (all-zero) vector gets s = 1, z = 0.
+  R7  1/sqrt(D) is applied (formulas in P1 and P2); P3's score listing only
+      shows the scale fold.
+  R8  grouped-query heads: query head h reads KV head h // G.
+  R9  per-channel key scales come from the absmax over the first append of a
+      sequence (its prefill) and are then frozen; later tokens clamp.
+  R10 super-scaled values: per token sigma = fl64(amax/qmax); per head
+      S = RN32(max sigma / 255) over the prefill, frozen afterwards;
+      u = clamp(rint(fl64(sigma / S)), 1, 255) (0 for an all-zero vector);
+      the effective scale is the exact product u*S.
+  R11 with a recent window of W tokens, exactly the min(W, n) newest tokens
+      are kept unquantized (bf16); older tokens are quantized per token.
+  R13 the output is fp32 on the device; here fp64.
+  Scale underflow: a scale that rounds to 0 in its storage type is replaced by
+  that type's smallest positive value (fp32 2^-149, fp16 2^-24); an fp16 scale
+  above 65504 saturates to 65504.
+  An empty cache (0 tokens) attends to nothing: the output is all zeros.
+
+Parity: every function below is pinned by tests under tests/ (exact rational
+arithmetic, closed forms, special cases, identities from P1).  None is
+"parity unpinned", but the zero-point convention (R6) and the super-scale
+convention (R10) are readings: the pages fix their invariants (range, exact
+zero, error bound, metadata size), not their every bit.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+F32_TINY = 2.0 ** -149   # smallest positive fp32 (subnormal)
+F16_TINY = 2.0 ** -24    # smallest positive fp16 (subnormal)
+F16_MAX = 65504.0
+
+_SCALE_DTYPES = {"f32": np.float32, "f16": np.float16, "f64": np.float64}
+
+
+# --------------------------------------------------------------------------
+# Format description (the oracle's own; the HIP library has its own structs)
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class TensorFormat:
+    """How one of K or V is stored.
+
+    bits:       16 = unquantized (bf16 values kept as is), 8, 4 (2 is accepted
+                by the byte accounting only).
+    axis:       "token" (one scale per token per head, P3 "Per-token scales and
+                where they can live") or "channel" (one scale per feature per
+                head, keys only, moved onto the query per P3 "The axis choice is
+                a kernel decision").
+    zero_point: integer zero point (unsigned codes) when True.
+    scale:      "f32", "f16" (scale and zero point stored in that type) or
+                "u8_super" (8-bit code times a per-head fp32 super-scale).
+    """
+
+    bits: int
+    axis: str = "token"
+    zero_point: bool = False
+    scale: str = "f32"
+
+
+def qmax_symmetric(bits: int) -> int:
+    """Largest magnitude of a symmetric code; -2^(b-1) is never produced (R3)."""
+    return (1 << (bits - 1)) - 1
+
+
+def qmax_unsigned(bits: int) -> int:
+    return (1 << bits) - 1
+
+
+def round_to_storage(x64, scale: str) -> np.ndarray:
+    """Round fp64 values once (ties to even) to the storage type (R2), then
+    apply the underflow/overflow rule stated in the module docstring."""
+    dt = _SCALE_DTYPES[scale]
+    s = np.asarray(x64, dtype=np.float64).astype(dt)
+    if dt is np.float32:
+        s = np.where(s == 0, np.float32(F32_TINY), s).astype(np.float32)
+    elif dt is np.float16:
+        s64 = s.astype(np.float64)
+        s64 = np.where(s64 == 0, F16_TINY, s64)
+        s64 = np.where(s64 > F16_MAX, F16_MAX, s64)
+        s = s64.astype(np.float16)
+    return s
+
+
+def rne_quotient(x, s) -> np.ndarray:
+    """R1: round-half-to-even of x / s, as one IEEE fp64 division then rint.
+
+    x and s hold at most 24 significant bits and |x/s| <= 2^8 (plus the
+    clamp), so the fp64 quotient never crosses or lands on a half-integer that
+    the exact quotient does not: a non-tie quotient lies at least 2^-26 away
+    from any half-integer, while the fp64 rounding error is below 2^-44.
+    """
+    return np.rint(np.asarray(x, np.float64) / np.asarray(s, np.float64))
+
+
+# --------------------------------------------------------------------------
+# Quantizers (write side).  Each works on the last axis of x (one vector).
+# --------------------------------------------------------------------------
+def quantize_sym(x, bits: int, scale: str = "f32"):
+    """Symmetric per-vector quantization, P2 "Quantization needs a scale
+    convention" (q = clamp(round(x/s)), x_hat = q*s) with the scale taken from
+    the vector's absolute maximum as in P3 "The axis choice is a kernel
+    decision" (scale = amax / qmax; all-zero vector -> codes 0, scale 1).
+
+    Returns (codes int32 [..., D], scale [...] in the storage type).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    qmax = qmax_symmetric(bits)
+    amax = np.max(np.abs(x), axis=-1)
+    zero = amax == 0.0
+    s = round_to_storage(np.where(zero, 1.0, amax / qmax), scale)
+    s = np.where(zero, np.asarray(1.0, s.dtype), s).astype(s.dtype)
+    codes = np.clip(rne_quotient(x, s[..., None]), -qmax, qmax)
+    codes = np.where(zero[..., None], 0.0, codes)
+    return codes.astype(np.int32), s
+
+
+def quantize_asym(x, bits: int, scale: str = "f16"):
+    """Zero-point (unsigned) per-vector quantization, reading R6.
+
+    lo = min(min x, 0), hi = max(max x, 0); s = RN((hi - lo) / (2^b - 1));
+    z = clamp(rint(-lo / s), 0, 2^b - 1) is the code that represents 0;
+    c = clamp(rint(x / s) + z, 0, 2^b - 1).  The rounding is applied to x/s
+    before z is added: rint(y) + z differs from rint(y + z) at ties when z is
+    odd.  Reconstruction: x_hat = s * (c - z).
+
+    Returns (codes int32 [..., D], s [...], z [...]) with s and z in the
+    storage type (z is an integer, exact in fp16/fp32).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    qmax = qmax_unsigned(bits)
+    lo = np.minimum(np.min(x, axis=-1), 0.0)
+    hi = np.maximum(np.max(x, axis=-1), 0.0)
+    flat = hi == lo
+    s = round_to_storage(np.where(flat, 1.0, (hi - lo) / qmax), scale)
+    s = np.where(flat, np.asarray(1.0, s.dtype), s).astype(s.dtype)
+    z = np.clip(rne_quotient(-lo, s), 0, qmax)
+    z = np.where(flat, 0.0, z)
+    codes = np.clip(rne_quotient(x, s[..., None]) + z[..., None], 0, qmax)
+    return codes.astype(np.int32), s, z.astype(s.dtype)
+
+
+def channel_scales(k_prefill, bits: int) -> np.ndarray:
+    """Per-channel key scales (reading R9 of P3 "Per-token scales and where they
+    can live"): absmax over the prefill tokens of each feature, divided by qmax,
+    rounded once to fp32; an all-zero channel gets scale 1.
+
+    k_prefill: [..., T, D]  ->  [..., D] fp32.
+    """
+    k = np.asarray(k_prefill, dtype=np.float64)
+    qmax = qmax_symmetric(bits)
+    amax = np.max(np.abs(k), axis=-2)
+    zero = amax == 0.0
+    s = round_to_storage(np.where(zero, 1.0, amax / qmax), "f32")
+    return np.where(zero, np.float32(1.0), s).astype(np.float32)
+
+
+def quantize_with_channel_scales(k, s_chan, bits: int) -> np.ndarray:
+    """Codes of keys under frozen per-channel scales: c = clamp(rint(k / s_d))."""
+    qmax = qmax_symmetric(bits)
+    k = np.asarray(k, dtype=np.float64)
+    codes = np.clip(rne_quotient(k, np.asarray(s_chan)[..., None, :]), -qmax, qmax)
+    return codes.astype(np.int32)
+
+
+def super_scale(v_prefill, bits: int) -> np.ndarray:
+    """Per-head fp32 super-scale (reading R10 of P3 "Per-token scales and where
+    they can live": 8-bit scales relative to a coarser super-scale).
+
+    sigma_t = fl64(amax_t / qmax) per token; S = RN32(max_t sigma_t / 255);
+    S = 1 when every prefill vector is zero.  v_prefill: [..., T, D] -> [...].
+    """
+    v = np.asarray(v_prefill, dtype=np.float64)
+    qmax = qmax_symmetric(bits)
+    sigma = np.max(np.abs(v), axis=-1) / qmax
+    smax = np.max(sigma, axis=-1)
+    zero = smax == 0.0
+    S = round_to_storage(np.where(zero, 1.0, smax / 255.0), "f32")
+    return np.where(zero, np.float32(1.0), S).astype(np.float32)
+
+
+def quantize_superscaled(v, S, bits: int):
+    """Codes and 8-bit scale codes under a frozen super-scale S (reading R10).
+
+    u_t = clamp(rint(fl64(sigma_t / S)), 1, 255), 0 for an all-zero vector;
+    effective scale u_t*S (exact in fp64); c = clamp(rint(v / (u_t*S))).
+    v: [..., T, D], S: [...]  ->  (codes int32 [..., T, D], u uint8 [..., T]).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    qmax = qmax_symmetric(bits)
+    S64 = np.asarray(S, dtype=np.float64)[..., None]
+    amax = np.max(np.abs(v), axis=-1)
+    sigma = amax / qmax
+    u = np.clip(np.rint(sigma / S64), 1, 255)
+    u = np.where(amax == 0.0, 0.0, u)
+    s_eff = u * S64                        # exact: 8-bit times 24-bit significand
+    safe = np.where(u == 0.0, 1.0, s_eff)
+    codes = np.clip(rne_quotient(v, safe[..., None]), -qmax, qmax)
+    codes = np.where((u == 0.0)[..., None], 0.0, codes)
+    return codes.astype(np.int32), u.astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# Dequantization (read side), fp64
+# --------------------------------------------------------------------------
+def dequant_sym(codes, s) -> np.ndarray:
+    return np.asarray(codes, np.float64) * np.asarray(s, np.float64)[..., None]
+
+
+def dequant_asym(codes, s, z) -> np.ndarray:
+    return np.asarray(s, np.float64)[..., None] * (
+        np.asarray(codes, np.float64) - np.asarray(z, np.float64)[..., None])
+
+
+def dequant_channel(codes, s_chan) -> np.ndarray:
+    return np.asarray(codes, np.float64) * np.asarray(s_chan, np.float64)[..., None, :]
+
+
+def dequant_superscaled(codes, u, S) -> np.ndarray:
+    s_eff = np.asarray(u, np.float64) * np.asarray(S, np.float64)[..., None]
+    return np.asarray(codes, np.float64) * s_eff[..., None]
+
+
+# --------------------------------------------------------------------------
+# Attention (read side), the plain definition in fp64
+# --------------------------------------------------------------------------
+def softmax(s) -> np.ndarray:
+    s = np.asarray(s, dtype=np.float64)
+    e = np.exp(s - np.max(s))
+    return e / np.sum(e)
+
+
+def scores(q_head, k_hat_head) -> np.ndarray:
+    """Scores of one query head against one KV head's keys: q . k_hat_i / sqrt(D)
+    (P2 "Keys and values need not have identical error sensitivity")."""
+    q_head = np.asarray(q_head, dtype=np.float64)
+    return (np.asarray(k_hat_head, dtype=np.float64) @ q_head) / math.sqrt(q_head.shape[-1])
+
+
+def attend(q, k_hat, v_hat) -> np.ndarray:
+    """Exact single-query attention over a reconstructed cache.
+
+    P1 "Key error acts before the softmax": s = q K^T / sqrt(d), a = softmax(s),
+    o = a V; P2 "Keys and values need not have identical error sensitivity":
+    score_i = q . k_hat_i / sqrt(D), output = sum_i softmax(score)_i v_hat_i.
+
+    q: [Hq, D]; k_hat, v_hat: [Hkv, T, D]; query head h reads KV head h // G
+    with G = Hq / Hkv (reading R8).  T = 0 gives zeros.  Returns [Hq, D] fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v_hat = np.asarray(v_hat, dtype=np.float64)
+    hq, d = q.shape
+    hkv, t, _ = k_hat.shape
+    assert hq % hkv == 0
+    g = hq // hkv
+    out = np.zeros((hq, d), dtype=np.float64)
+    if t == 0:
+        return out
+    for h in range(hq):
+        kv = h // g
+        a = softmax(scores(q[h], k_hat[kv]))
+        out[h] = a @ v_hat[kv]
+    return out
+
+
+def attention_weights(q, k_hat) -> np.ndarray:
+    """Softmax weights [Hq, T] for the same definition as ``attend``."""
+    q = np.asarray(q, dtype=np.float64)
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    hq, d = q.shape
+    hkv, t, _ = k_hat.shape
+    g = hq // hkv
+    return np.stack([softmax(scores(q[h], k_hat[h // g])) for h in range(hq)])
+
+
+# --------------------------------------------------------------------------
+# A logical cache for one layer: what is stored per token, in position order
+# --------------------------------------------------------------------------
+class _Side:
+    """Stored records of one tensor (K or V) of one sequence: [Hkv, n, ...]."""
+
+    def __init__(self, hkv: int, d: int):
+        self.codes = np.zeros((hkv, 0, d), np.int32)
+        self.s = None          # per-token scale [Hkv, n]
+        self.z = None          # per-token zero point [Hkv, n]
+        self.u = None          # per-token 8-bit scale code [Hkv, n]
+        self.raw = np.zeros((hkv, 0, d), np.float64)   # bits == 16 formats
+        self.chan = None       # per-channel scale [Hkv, D]
+        self.S = None          # per-head super-scale [Hkv]
+
+
+class OracleCache:
+    """Logical contents of one layer's cache for a batch of sequences.
+
+    Appends follow P3 "Per-token scales and where they can live" (each vector
+    quantized from itself at write time and stored with its scale).  With a
+    recent window (P1 "Cache growth changes the serving trade"), the newest
+    min(W, n) tokens stay as their bf16 values and the rest are quantized per
+    token (reading R11).  Paging (P2 "Metadata and block layout remain part of
+    physical memory use") changes placement only, so this model has none.
+    """
+
+    def __init__(self, batch: int, hkv: int, d: int, key: TensorFormat,
+                 value: TensorFormat, window: int = 0):
+        if window and (key.axis == "channel" or key.scale == "u8_super"
+                       or value.scale == "u8_super"):
+            raise ValueError("a recent window is modelled for per-token formats only")
+        self.batch, self.hkv, self.d = batch, hkv, d
+        self.fmt = {"k": key, "v": value}
+        self.window = window
+        self.lens = [0] * batch
+        self.side = [{"k": _Side(hkv, d), "v": _Side(hkv, d)} for _ in range(batch)]
+        self.win = [{"k": np.zeros((hkv, 0, d)), "v": np.zeros((hkv, 0, d))}
+                    for _ in range(batch)]
+
+    # -- write side ---------------------------------------------------------
+    def _quantize_into(self, side: _Side, fmt: TensorFormat, x: np.ndarray,
+                       first: bool):
+        """Quantize vectors x [Hkv, n, D] (position order) and append them."""
+        n = x.shape[1]
+        if n == 0:
+            return
+        if fmt.bits == 16:
+            side.raw = np.concatenate([side.raw, x], axis=1)
+            return
+        if fmt.axis == "channel":
+            if first:
+                side.chan = channel_scales(x, fmt.bits)
+            c = quantize_with_channel_scales(x, side.chan, fmt.bits)
+        elif fmt.scale == "u8_super":
+            if first:
+                side.S = super_scale(x, fmt.bits)
+            c, u = quantize_superscaled(x, side.S, fmt.bits)
+            side.u = u if side.u is None else np.concatenate([side.u, u], axis=1)
+        elif fmt.zero_point:
+            c, s, z = quantize_asym(x, fmt.bits, fmt.scale)
+            side.s = s if side.s is None else np.concatenate([side.s, s], axis=1)
+            side.z = z if side.z is None else np.concatenate([side.z, z], axis=1)
+        else:
+            c, s = quantize_sym(x, fmt.bits, fmt.scale)
+            side.s = s if side.s is None else np.concatenate([side.s, s], axis=1)
+        side.codes = np.concatenate([side.codes, c], axis=1)
+
+    def append(self, b: int, k_new, v_new):
+        """Append n tokens (k_new, v_new: [Hkv, n, D], values exactly
+        representable in the input dtype) to sequence b."""
+        k_new = np.asarray(k_new, np.float64)
+        v_new = np.asarray(v_new, np.float64)
+        n = k_new.shape[1]
+        first = self.lens[b] == 0
+        total = self.lens[b] + n
+        for t, x in (("k", k_new), ("v", v_new)):
+            if self.window:
+                pool = np.concatenate([self.win[b][t], x], axis=1)
+                keep = min(self.window, total)
+                leave = pool.shape[1] - keep
+                self._quantize_into(self.side[b][t], self.fmt[t], pool[:, :leave], first)
+                self.win[b][t] = pool[:, leave:]
+            else:
+                self._quantize_into(self.side[b][t], self.fmt[t], x, first)
+        self.lens[b] = total
+
+    # -- read side ----------------------------------------------------------
+    def _dequant(self, side: _Side, fmt: TensorFormat) -> np.ndarray:
+        if fmt.bits == 16:
+            return side.raw.copy()
+        if side.codes.shape[1] == 0:
+            return np.zeros((self.hkv, 0, self.d))
+        if fmt.axis == "channel":
+            return dequant_channel(side.codes, side.chan)
+        if fmt.scale == "u8_super":
+            return dequant_superscaled(side.codes, side.u, side.S)
+        if fmt.zero_point:
+            return dequant_asym(side.codes, side.s, side.z)
+        return dequant_sym(side.codes, side.s)
+
+    def reconstructed(self, b: int):
+        """(k_hat, v_hat) [Hkv, len, D] fp64 in position order."""
+        out = []
+        for t in ("k", "v"):
+            q = self._dequant(self.side[b][t], self.fmt[t])
+            if self.window:
+                q = np.concatenate([q, self.win[b][t]], axis=1)
+            out.append(q)
+        return out[0], out[1]
+
+    def stored(self, b: int, t: str) -> _Side:
+        """The stored records of sequence b for t in {"k", "v"} (for bit-exact
+        comparison of codes and metadata)."""
+        return self.side[b][t]
+
+    def window_values(self, b: int, t: str) -> np.ndarray:
+        return self.win[b][t]
+
+    def attend(self, b: int, q) -> np.ndarray:
+        k_hat, v_hat = self.reconstructed(b)
+        return attend(q, k_hat, v_hat)
+
+
+# --------------------------------------------------------------------------
+# Byte accounting
+# --------------------------------------------------------------------------
+def meta_bytes_per_token(fmt: TensorFormat) -> int:
+    """Per-token, per-head metadata bytes (P3 "Per-token scales and where they
+    can live" prices a 4-byte scale, and a scale plus zero point)."""
+    if fmt.bits == 16 or fmt.axis == "channel":
+        return 0
+    if fmt.scale == "u8_super":
+        return 1
+    width = {"f32": 4, "f16": 2, "f64": 8}[fmt.scale]
+    return width * (2 if fmt.zero_point else 1)
+
+
+def side_bytes_per_head(fmt: TensorFormat, d: int) -> int:
+    """Per-(sequence, head) metadata: channel scales or the super-scale."""
+    if fmt.bits == 16:
+        return 0
+    if fmt.axis == "channel":
+        return 4 * d
+    if fmt.scale == "u8_super":
+        return 4
+    return 0
+
+
+def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
+                d: int, lens: Sequence[int], window: int = 0,
+                block_tokens: int = 0, max_tokens: Optional[int] = None) -> Dict[str, int]:
+    """Bytes of a cache holding sequences of the given lengths.
+
+    payload   P2 "Cache precision is separate from weight precision":
+              KV_bytes = 2 * L * H_kv * D * T * b, generalised to separate key
+              and value widths: L * H_kv * D * T_q * (b_K + b_V) over the
+              quantized tokens T_q of each sequence.
+    metadata  per-token scales / zero points / 8-bit scale codes plus per-head
+              channel scales or super-scales (P3 "Per-token scales and where
+              they can live"; P2 "Metadata and block layout remain part of
+              physical memory use").
+    window    the bf16 recent tokens, 2 bytes per element for K and V.
+    padding   allocated but unused slots: the unfilled tail of the last block
+              of a paged sequence, or max_tokens - T_q quantized slots and
+              W - n_w window slots of a contiguous one.
+    total     the sum of the four.
+    """
+    def row(fmt):  # bytes of one token's codes
+        return d * fmt.bits // 8
+
+    out = dict(payload=0, metadata=0, window=0, padding=0)
+    per_tok = row(key) + row(value) + meta_bytes_per_token(key) + meta_bytes_per_token(value)
+    for n in lens:
+        n_w = min(window, n)
+        n_q = n - n_w
+        out["payload"] += layers * hkv * n_q * (row(key) + row(value))
+        out["metadata"] += layers * hkv * (
+            n_q * (meta_bytes_per_token(key) + meta_bytes_per_token(value))
+            + side_bytes_per_head(key, d) + side_bytes_per_head(value, d))
+        out["window"] += layers * hkv * n_w * d * 2 * 2
+        if block_tokens:
+            alloc_q = -(-n_q // block_tokens) * block_tokens
+        else:
+            alloc_q = max_tokens if max_tokens is not None else n_q
+        out["padding"] += layers * hkv * (alloc_q - n_q) * per_tok
+        if window and not block_tokens:
+            out["padding"] += layers * hkv * (window - n_w) * d * 2 * 2
+    out["total"] = out["payload"] + out["metadata"] + out["window"] + out["padding"]
+    return out
+
+
+def decode_traffic(key: TensorFormat, value: TensorFormat, hkv: int, d: int,
+                   lens: Sequence[int], window: int = 0) -> int:
+    """Bytes one decode step must read from the cache (one layer): codes,
+    per-token metadata, window values and per-head side data; no padding."""
+    b = cache_bytes(key, value, 1, hkv, d, lens, window)
+    return b["payload"] + b["metadata"] + b["window"]
+
+
+def multiply_adds(hq: int, d: int, lens: Sequence[int]) -> int:
+    """Multiply-adds of one decode step: q.k and a.v, D each per token and
+    query head (P3 "What the cache holds and how it is read")."""
+    return sum(2 * hq * d * n for n in lens)
+
+
+def arithmetic_intensity(bits: int, d: int = 128, group: int = 1,
+                         meta_bytes: int = 4) -> float:
+    """Multiply-adds per cache byte for one token of one KV head read by
+    ``group`` query heads: 2*G*D MACs over 2*D*b/8 code bytes plus a key and a
+    value scale (P3 "What the cache holds and how it is read")."""
+    return (2 * group * d) / (2 * d * bits / 8 + 2 * meta_bytes)

@@ -1,0 +1,582 @@
+"""Pins of the CPU oracle to facts the pages and mathematics fix.
+
+Each ``pin_*`` function takes the oracle module and raises AssertionError when
+the oracle disagrees with something other than itself: hand-worked examples of
+the pages' definitions, the numbers the pages print (tests/golden/), exact
+rational arithmetic (fractions.Fraction, mpmath at 50 digits), closed forms,
+invariants, identities the pages state, and special cases that reduce to a
+library routine.  ``test_oracle_pins.py`` runs them on the oracle;
+``test_oracle_mutations.py`` runs them on copies of the oracle with plausible
+mistakes planted, and expects each mistake to be caught.
+
+Pages: [P1] "KV Cache Quantization Perturbs Attention Through Stored Keys and
+Values"; [P2] "KV cache quantization reduces cache bytes with separate accuracy
+and kernel costs"; [P3] "KV Cache Quantization and Per-Token Scale Placement".
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# Exact helpers (independent of the oracle: rational arithmetic only)
+# ---------------------------------------------------------------------------
+def exact_round_float(fr: Fraction, p: int, emin: int) -> Fraction:
+    """Round a rational to the nearest binary float with p significant bits and
+    minimum normal exponent emin (subnormals included), ties to even."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    quantum = Fraction(2) ** (e - (p - 1))
+    return sign * round(a / quantum) * quantum   # round(): ties to even
+
+
+def rn32(fr):
+    return exact_round_float(Fraction(fr), 24, -126)
+
+
+def rn16(fr):
+    return exact_round_float(Fraction(fr), 11, -14)
+
+
+def rn64(fr):
+    return exact_round_float(Fraction(fr), 53, -1022)
+
+
+def fr(x) -> Fraction:
+    return Fraction(float(x))
+
+
+def exact_sym(vec, bits, scale_round):
+    """Symmetric quantizer of one vector in exact arithmetic.  scale_round maps
+    the exact amax/qmax to the stored scale."""
+    qmax = (1 << (bits - 1)) - 1
+    xs = [fr(v) for v in vec]
+    amax = max(abs(v) for v in xs)
+    if amax == 0:
+        return [0] * len(xs), Fraction(1)
+    s = scale_round(amax / qmax)
+    return [max(-qmax, min(qmax, round(v / s))) for v in xs], s
+
+
+def exact_asym(vec, bits):
+    qmax = (1 << bits) - 1
+    xs = [fr(v) for v in vec]
+    lo = min(min(xs), Fraction(0))
+    hi = max(max(xs), Fraction(0))
+    if hi == lo:
+        return [0] * len(xs), Fraction(1), 0
+    s = rn16((hi - lo) / qmax)
+    z = max(0, min(qmax, round(-lo / s)))
+    return [max(0, min(qmax, round(v / s) + z)) for v in xs], s, z
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _f32(x):
+    return np.asarray(x, np.float32).astype(np.float64)
+
+
+def _random_vectors(n, d, seed, magnitudes=(1e-3, 1.0, 37.0, 1e4)):
+    rng = _rng(seed)
+    out = []
+    for i in range(n):
+        m = magnitudes[i % len(magnitudes)]
+        v = rng.standard_normal(d) * m
+        if i % 3 == 0:
+            v[rng.integers(d)] *= 10.0      # an outlier entry sets the max
+        out.append(_f32(v))
+    return np.stack(out)
+
+
+def _near_ties(s, n, seed):
+    """fp32 values within a few ulps of (k + 1/2) * s, with s an fp32 scale."""
+    rng = _rng(seed)
+    k = rng.integers(-120, 120, n)
+    x = ((k + 0.5) * s).astype(np.float32)
+    steps = rng.integers(-3, 4, n)
+    x = np.array([np.nextafter(np.float32(v), np.float32(np.sign(st) * np.inf)) if st else v
+                  for v, st in zip(x, steps)], dtype=np.float32)
+    return x.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked examples of the pages' definitions
+# ---------------------------------------------------------------------------
+def pin_hand_examples(O):
+    """Small vectors whose scale is a power of two, worked by hand from P2
+    "Quantization needs a scale convention" and P3 "The axis choice is a kernel
+    decision" (scale = amax/qmax, round ties to even, clamp)."""
+    # amax 127 -> scale exactly 1; halves go to the even neighbour.
+    c, s = O.quantize_sym(np.array([127, -63.5, 31.75, 0.5, -1.5, 2.5, 0, -127.0]), 8, "f32")
+    assert float(s) == 1.0 and c.tolist() == [127, -64, 32, 0, -2, 2, 0, -127], (c, s)
+    # amax 254 -> scale exactly 2.
+    c, s = O.quantize_sym(np.array([254.0, 3.0, -5.0, 1.0]), 8, "f32")
+    assert float(s) == 2.0 and c.tolist() == [127, 2, -2, 0], (c, s)
+    # all-zero vector: codes 0, scale 1.
+    c, s = O.quantize_sym(np.zeros(6), 8, "f32")
+    assert float(s) == 1.0 and c.tolist() == [0] * 6
+    # 4-bit symmetric: qmax 7, amax 7 -> scale 1.
+    c, s = O.quantize_sym(np.array([7.0, -3.5, 2.5, 0.5, 1.75, -7.0]), 4, "f32")
+    assert float(s) == 1.0 and c.tolist() == [7, -4, 2, 0, 2, -7], (c, s)
+    # zero point, range [-7.5, 7.5] -> s 1, z = rint(7.5) = 8; 7.5 -> 16 clamps.
+    c, s, z = O.quantize_asym(np.array([-7.5, 0.0, 7.5, 3.75, -2.5]), 4, "f16")
+    assert float(s) == 1.0 and float(z) == 8.0 and c.tolist() == [0, 8, 15, 12, 6], (c, s, z)
+    # all-positive vector: the range is widened to include 0, so z = 0.
+    c, s, z = O.quantize_asym(np.array([1.0, 2.0, 3.0, 15.0]), 4, "f16")
+    assert float(s) == 1.0 and float(z) == 0.0 and c.tolist() == [1, 2, 3, 15]
+    # odd zero point: rint(x/s) + z, not rint(x/s + z): 0.5 -> 0 + 3, 1.5 -> 2 + 3.
+    c, s, z = O.quantize_asym(np.array([-3.0, 12.0, 0.5, 1.5]), 4, "f16")
+    assert float(s) == 1.0 and float(z) == 3.0 and c.tolist() == [0, 15, 3, 5], (c, s, z)
+    # per-channel key scales: channel absmax 127 and 254 -> scales 1 and 2.
+    k = np.array([[127.0, -254.0], [-63.5, 127.0], [0.5, 3.0]])
+    sc = O.channel_scales(k, 8)
+    assert sc.tolist() == [1.0, 2.0], sc
+    assert O.quantize_with_channel_scales(k, sc, 8).tolist() == [[127, -127], [-64, 64], [0, 2]]
+    # super-scale: sigma = amax / 7 = [255, 0.5, 0] -> S = 255/255 = 1;
+    # u = [255, rint(0.5)=0 -> clamp 1, 0 for the zero vector].
+    v = np.array([[1785.0, -892.5, 0.0], [3.5, -1.0, 0.5], [0.0, 0.0, 0.0]])
+    S = O.super_scale(v, 4)
+    assert float(S) == 1.0, S
+    codes, u = O.quantize_superscaled(v, S, 4)
+    assert u.tolist() == [255, 1, 0], u
+    assert codes.tolist() == [[7, -4, 0], [4, -1, 0], [0, 0, 0]], codes
+
+
+def pin_rounding_ties(O):
+    """The numbers tests/golden/rounding_ties.json lists for Python's round(),
+    which P3's quantizer listing uses."""
+    g = json.load(open(os.path.join(GOLDEN, "rounding_ties.json")))
+    xs = np.array([c[0] for c in g["cases"]])
+    want = [c[1] for c in g["cases"]]
+    got = O.rne_quotient(xs, 1.0)
+    assert [int(v) for v in got] == want, (got, want)
+    assert [round(x) for x in xs.tolist()] == want   # the listing's primitive
+
+
+# ---------------------------------------------------------------------------
+# Exact rational arithmetic
+# ---------------------------------------------------------------------------
+def pin_sym_exact(O):
+    """Symmetric codes and scales equal exact rational evaluation: with an fp64
+    scale this is P3's quantizer listing evaluated exactly (Python's float
+    division is correctly rounded, round() ties to even); with an fp32 scale the
+    scale is the exactly rounded amax/qmax (R2)."""
+    vecs = _random_vectors(48, 128, 11)
+    for bits in (8, 4):
+        for scale, rnd in (("f64", rn64), ("f32", rn32)):
+            codes, s = O.quantize_sym(vecs, bits, scale)
+            for i, v in enumerate(vecs):
+                ec, es = exact_sym(v, bits, rnd)
+                assert Fraction(float(s[i])) == es, (bits, scale, i)
+                assert codes[i].tolist() == ec, (bits, scale, i)
+
+
+def pin_near_ties(O):
+    """Quotients within a few ulps of a half-integer round like the exact
+    quotient (R1): fp32 division would get some of these wrong."""
+    rng = _rng(5)
+    for trial in range(24):
+        s = np.float32(rng.uniform(0.003, 0.03))
+        x = _near_ties(s, 64, 100 + trial)
+        x[0] = 127.0 * float(s) * (1 + 1e-7)       # keeps amax/127 close to s
+        codes, st = O.quantize_sym(x, 8, "f32")
+        ec, es = exact_sym(x, 8, rn32)
+        assert Fraction(float(st)) == es
+        assert codes.tolist() == ec, trial
+
+
+def pin_exact_ties(O):
+    """Exact ties (k + 1/2) * s go to the even neighbour, for both signs."""
+    for e in range(-6, 7):
+        s = 2.0 ** e
+        k = np.arange(-126, 126)
+        x = np.concatenate([[127 * s], (k + 0.5) * s])
+        codes, st = O.quantize_sym(x, 8, "f32")
+        assert float(st) == s
+        want = [127] + [int(2 * round((kk + 0.5) / 2)) for kk in k]
+        assert codes.tolist() == want, e
+
+
+def pin_asym_exact(O):
+    """Zero-point codes, fp16 scales and zero points equal exact evaluation of
+    reading R6; x = 0 reconstructs exactly; codes stay in [0, 15]; every
+    unclamped element is within s/2 of its reconstruction."""
+    vecs = _random_vectors(40, 128, 23, magnitudes=(0.05, 1.0, 9.0, 300.0))
+    vecs[5] = np.abs(vecs[5])          # one-signed vectors
+    vecs[6] = -np.abs(vecs[6])
+    vecs[7, :] = 0.0
+    vecs[8, 3] = 0.0
+    codes, s, z = O.quantize_asym(vecs, 4, "f16")
+    for i, v in enumerate(vecs):
+        ec, es, ez = exact_asym(v, 4)
+        assert Fraction(float(s[i])) == es, i
+        assert float(z[i]) == ez, i
+        assert codes[i].tolist() == ec, i
+    assert codes.min() >= 0 and codes.max() <= 15
+    xh = O.dequant_asym(codes, s, z)
+    assert np.all(xh[vecs == 0.0] == 0.0)
+    err = np.abs(xh - vecs)
+    sd = s.astype(np.float64)[:, None]
+    unclamped = (codes > 0) & (codes < 15)
+    assert np.all(err[unclamped] <= sd.repeat(128, 1)[unclamped] / 2 * (1 + 1e-12))
+
+
+def pin_sym_closed_form(O):
+    """The largest-magnitude element maps to +-qmax, every element is within s/2
+    of its reconstruction, codes never reach -2^(b-1), s = RN32(amax/qmax)."""
+    vecs = _random_vectors(64, 128, 31)
+    for bits in (8, 4):
+        qmax = (1 << (bits - 1)) - 1
+        codes, s = O.quantize_sym(vecs, bits, "f32")
+        xh = O.dequant_sym(codes, s)
+        sd = s.astype(np.float64)[:, None]
+        assert np.all(np.abs(xh - vecs) <= sd / 2 * (1 + 1e-12))
+        assert codes.min() >= -qmax and codes.max() <= qmax
+        imax = np.argmax(np.abs(vecs), axis=1)
+        top = codes[np.arange(len(vecs)), imax]
+        assert np.all(np.abs(top) == qmax)
+        assert np.all(np.sign(top) == np.sign(vecs[np.arange(len(vecs)), imax]))
+        for i in range(0, 64, 7):
+            assert Fraction(float(s[i])) == rn32(Fraction(float(np.max(np.abs(vecs[i])))) / qmax)
+
+
+def pin_channel(O):
+    """Per-channel key scales (P3 "Per-token scales and where they can live",
+    reading R9) equal RN32(channel absmax / 127) exactly; codes equal exact
+    rounding; a later token beyond the prefill range clamps; and moving the
+    scales onto the query (P3 "The axis choice is a kernel decision") gives the
+    scores of the dequantized keys exactly in rational arithmetic."""
+    rng = _rng(41)
+    k = _f32(rng.standard_normal((9, 16)) * np.array([1.0] * 12 + [10.0] * 4))
+    sc = O.channel_scales(k, 8)
+    for d in range(16):
+        assert Fraction(float(sc[d])) == rn32(Fraction(float(np.max(np.abs(k[:, d])))) / 127)
+    codes = O.quantize_with_channel_scales(k, sc, 8)
+    for t in range(9):
+        for d in range(16):
+            assert codes[t, d] == max(-127, min(127, round(fr(k[t, d]) / fr(sc[d]))))
+    later = k[:1] * 3.0
+    lc = O.quantize_with_channel_scales(later, sc, 8)
+    assert np.all(np.abs(lc) <= 127) and np.any(np.abs(lc) == 127)
+    q = _f32(rng.standard_normal(16))
+    folded = [sum(fr(q[d]) * fr(sc[d]) * int(codes[t, d]) for d in range(16)) for t in range(9)]
+    kh = O.dequant_channel(codes, sc)
+    got = O.scores(q, kh) * math.sqrt(16)
+    for t in range(9):
+        assert abs(Fraction(float(got[t])) - folded[t]) <= abs(folded[t]) * Fraction(1, 10 ** 13) + Fraction(1, 10 ** 300)
+
+
+def pin_superscale(O):
+    """8-bit scale codes relative to a per-head super-scale (reading R10):
+    S = RN32(max_t(amax_t/7)/255); u in [1, 255] for non-zero vectors and 0 for
+    zero vectors; u equals exact rint(amax/(7 S)) clamped; codes equal exact
+    rounding under u*S; metadata is 1 byte per token."""
+    v = _f32(_rng(53).laplace(0, 1, (64, 128)) * np.exp(_rng(54).uniform(-6, 2, (64, 1))))
+    v[10] = 0.0
+    S = O.super_scale(v, 4)
+    amax = [Fraction(float(np.max(np.abs(r)))) for r in v]
+    assert Fraction(float(S)) == rn32(max(a / 7 for a in amax) / 255)
+    codes, u = O.quantize_superscaled(v, S, 4)
+    for t in range(64):
+        if amax[t] == 0:
+            assert u[t] == 0 and not codes[t].any()
+            continue
+        eu = max(1, min(255, round(amax[t] / 7 / Fraction(float(S)))))
+        assert u[t] == eu, t
+        se = eu * Fraction(float(S))
+        assert codes[t].tolist() == [max(-7, min(7, round(fr(x) / se))) for x in v[t]], t
+        if eu > 1:
+            assert abs(se - amax[t] / 7) <= Fraction(float(S)) / 2
+    fmt = O.TensorFormat(4, "token", False, "u8_super")
+    assert O.meta_bytes_per_token(fmt) == 1
+
+
+def pin_fold(O):
+    """P3 "The axis choice is a kernel decision": with a per-token key scale,
+    scaling the integer dot product once equals the dot product with the
+    dequantized key.  The oracle's score of each dequantized key equals the
+    folded score computed exactly, to 1e-13 relative."""
+    rng = _rng(61)
+    kv = _random_vectors(12, 64, 62)
+    codes, s = O.quantize_sym(kv, 8, "f32")
+    q = _f32(rng.standard_normal(64))
+    got = O.scores(q, O.dequant_sym(codes, s))
+    for t in range(12):
+        acc = sum(fr(q[d]) * int(codes[t, d]) for d in range(64))   # integer-code dot
+        want = acc * fr(s[t])                                       # one multiply per score
+        g = Fraction(float(got[t])) * 8   # * sqrt(64)
+        assert abs(g - want) <= abs(want) * Fraction(1, 10 ** 13), t
+
+
+# ---------------------------------------------------------------------------
+# Attention: library routine, identities, special cases, brute force
+# ---------------------------------------------------------------------------
+def _sdpa_reference(q, k, v):
+    """torch's scaled_dot_product_attention on the CPU in fp64, one query."""
+    import torch
+    hq, d = q.shape
+    hkv = k.shape[0]
+    g = hq // hkv
+    kk = torch.from_numpy(np.repeat(k, g, axis=0))[None]      # [1, Hq, T, D]
+    vv = torch.from_numpy(np.repeat(v, g, axis=0))[None]
+    qq = torch.from_numpy(q)[None, :, None, :]                # [1, Hq, 1, D]
+    out = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)
+    return out[0, :, 0, :].numpy()
+
+
+def pin_exact_cache(O):
+    """With stored unquantized values (bits 16), attention over the cache is
+    standard attention (P1 "Key error acts before the softmax"): equal to
+    torch's scaled_dot_product_attention in fp64 to 1e-12."""
+    rng = _rng(71)
+    for (hq, hkv, t) in ((4, 1, 33), (8, 2, 200), (2, 2, 1), (6, 3, 7)):
+        k = rng.standard_normal((hkv, t, 32)) * 3
+        v = rng.standard_normal((hkv, t, 32))
+        q = rng.standard_normal((hq, 32))
+        cache = O.OracleCache(1, hkv, 32, O.TensorFormat(16), O.TensorFormat(16))
+        cache.append(0, k, v)
+        got = cache.attend(0, q)
+        assert np.max(np.abs(got - _sdpa_reference(q, k, v))) < 1e-12, (hq, hkv, t)
+
+
+def pin_identity_key(O):
+    """P1 "Key error acts before the softmax": with keys stored as K + E_K the
+    scores are s + q E_K^T / sqrt(d)."""
+    rng = _rng(81)
+    k = _f32(rng.standard_normal((50, 128)) * 2)
+    codes, s = O.quantize_sym(k, 4, "f32")
+    kh = O.dequant_sym(codes, s)
+    q = _f32(rng.standard_normal(128))
+    ek = kh - k
+    lhs = O.scores(q, kh)
+    rhs = (k @ q) / math.sqrt(128) + (ek @ q) / math.sqrt(128)
+    assert np.max(np.abs(lhs - rhs)) < 1e-12
+
+
+def pin_identity_value(O):
+    """P1 "Value error acts after attention weights are formed": with exact
+    keys and values stored as V + E_V, the output is o + a E_V."""
+    rng = _rng(91)
+    k = rng.standard_normal((1, 70, 128))
+    v = _f32(rng.standard_normal((1, 70, 128)))
+    codes, s = O.quantize_sym(v, 4, "f32")
+    vh = O.dequant_sym(codes, s)
+    q = rng.standard_normal((1, 128))
+    a = O.attention_weights(q, k)[0]
+    o = O.attend(q, k, v)[0]
+    o2 = O.attend(q, k, vh)[0]
+    assert np.max(np.abs(o2 - (o + a @ (vh[0] - v[0])))) < 1e-12
+
+
+def pin_softmax_weights(O):
+    """Attention weights are non-negative and sum to one (the output is a
+    convex combination, P3 "Keys and values are not symmetric")."""
+    rng = _rng(101)
+    for t in (1, 5, 300):
+        a = O.attention_weights(rng.standard_normal((4, 64)), rng.standard_normal((2, t, 64)) * 5)
+        assert np.all(a >= 0) and np.max(np.abs(a.sum(axis=1) - 1)) < 1e-12
+
+
+def pin_single_token(O):
+    """One cached token: its weight is 1 and the output is its value."""
+    rng = _rng(111)
+    cache = O.OracleCache(1, 2, 128, O.TensorFormat(8), O.TensorFormat(4, zero_point=True, scale="f16"))
+    k = _f32(rng.standard_normal((2, 1, 128)))
+    v = _f32(rng.standard_normal((2, 1, 128)))
+    cache.append(0, k, v)
+    _, vh = cache.reconstructed(0)
+    out = cache.attend(0, rng.standard_normal((4, 128)))
+    assert np.array_equal(out, np.repeat(vh[:, 0, :], 2, axis=0))
+
+
+def pin_uniform_keys(O):
+    """Identical keys give uniform weights: the output is the mean of v_hat."""
+    rng = _rng(121)
+    t = 37
+    kv = np.repeat(_f32(rng.standard_normal((1, 1, 128))), t, axis=1)
+    v = _f32(rng.standard_normal((1, t, 128)))
+    cache = O.OracleCache(1, 1, 128, O.TensorFormat(8), O.TensorFormat(8))
+    cache.append(0, kv, v)
+    _, vh = cache.reconstructed(0)
+    out = cache.attend(0, rng.standard_normal((1, 128)))
+    assert np.max(np.abs(out[0] - vh[0].mean(axis=0))) < 1e-12
+
+
+def pin_gqa_mapping(O):
+    """Grouped-query heads (reading R8): query head h attends KV head h // G,
+    the same as repeating each KV head G times and running one head each."""
+    rng = _rng(125)
+    k = rng.standard_normal((3, 20, 16))
+    v = rng.standard_normal((3, 20, 16))
+    q = rng.standard_normal((12, 16))
+    got = O.attend(q, k, v)
+    for h in range(12):
+        one = O.attend(q[h:h + 1], k[h // 4:h // 4 + 1], v[h // 4:h // 4 + 1])
+        assert np.array_equal(got[h], one[0])
+    assert np.max(np.abs(got - _sdpa_reference(q, k, v))) < 1e-12
+
+
+def pin_brute_force(O):
+    """Whole pipeline on tiny shapes against exact arithmetic: codes by
+    rational rounding, scores and softmax with mpmath at 50 digits."""
+    mpmath.mp.dps = 50
+    rng = _rng(131)
+    for d in (1, 2, 4):
+        for t in (1, 2, 3):
+            for trial in range(3):
+                k = np.round(rng.standard_normal((1, t, d)) * 64) / 16     # dyadic
+                v = np.round(rng.standard_normal((1, t, d)) * 64) / 16
+                q = np.round(rng.standard_normal((2, d)) * 64) / 16
+                cache = O.OracleCache(1, 1, d, O.TensorFormat(8), O.TensorFormat(4, zero_point=True, scale="f16"))
+                cache.append(0, k, v)
+                got = cache.attend(0, q)
+                kh, vh = [], []
+                for i in range(t):
+                    c, s = exact_sym(k[0, i], 8, rn32)
+                    kh.append([ci * s for ci in c])
+                    c, s, z = exact_asym(v[0, i], 4)
+                    vh.append([(ci - z) * s for ci in c])
+                for h in range(2):
+                    sc = [mpmath.mpf(sum(fr(q[h, j]) * kh[i][j] for j in range(d)).numerator)
+                          / sum(fr(q[h, j]) * kh[i][j] for j in range(d)).denominator / mpmath.sqrt(d)
+                          for i in range(t)]
+                    m = max(sc)
+                    e = [mpmath.exp(x - m) for x in sc]
+                    z_ = sum(e)
+                    for j in range(d):
+                        o = sum(e[i] * mpmath.mpf(vh[i][j].numerator) / vh[i][j].denominator
+                                for i in range(t)) / z_
+                        assert abs(float(o) - got[h, j]) <= 1e-13 * max(1.0, abs(float(o))), (d, t, h, j)
+
+
+def pin_drift(O):
+    """P3 "What degrades first": per-token scales follow drifting magnitudes by
+    construction.  Scaling a vector by a power of two scales its scale and
+    leaves its codes unchanged, for magnitudes growing along the sequence."""
+    rng = _rng(141)
+    base = _f32(rng.standard_normal((40, 128)))
+    growth = 2.0 ** np.arange(0, 40, 1)[:, None] / 2 ** 20   # x ~1e-6 .. ~5e5
+    x = base * growth
+    c0, s0 = O.quantize_sym(base, 8, "f32")
+    c1, s1 = O.quantize_sym(x, 8, "f32")
+    assert np.array_equal(c0, c1)
+    assert np.array_equal(s1.astype(np.float64), s0.astype(np.float64) * growth[:, 0])
+    ca, sa, za = O.quantize_asym(base, 4, "f16")
+    cb, sb, zb = O.quantize_asym(base * 4.0, 4, "f16")
+    assert np.array_equal(ca, cb) and np.array_equal(za, zb)
+    assert np.array_equal(sb.astype(np.float64), sa.astype(np.float64) * 4)
+
+
+def pin_window(O):
+    """Reading R11 of P1 "Cache growth changes the serving trade": after a
+    prefill and single-token appends, exactly the newest min(W, n) tokens are
+    unquantized; the rest reconstruct as their own per-token quantization."""
+    rng = _rng(151)
+    w = 8
+    cache = O.OracleCache(1, 2, 128, O.TensorFormat(8), O.TensorFormat(8), window=w)
+    allk = _f32(rng.standard_normal((2, 30, 128)))
+    allv = _f32(rng.standard_normal((2, 30, 128)))
+    cache.append(0, allk[:, :5], allv[:, :5])          # shorter than the window
+    kh, vh = cache.reconstructed(0)
+    assert np.array_equal(kh, allk[:, :5]) and np.array_equal(vh, allv[:, :5])
+    cache.append(0, allk[:, 5:20], allv[:, 5:20])      # crosses the window
+    for t in range(20, 30):
+        cache.append(0, allk[:, t:t + 1], allv[:, t:t + 1])
+    kh, vh = cache.reconstructed(0)
+    ck, sk = O.quantize_sym(allk[:, :30 - w], 8, "f32")
+    assert np.array_equal(kh[:, :30 - w], O.dequant_sym(ck, sk))
+    assert np.array_equal(kh[:, 30 - w:], allk[:, 30 - w:])
+    assert np.array_equal(cache.stored(0, "k").codes, ck)
+
+
+def pin_prefill_then_decode(O):
+    """Per-channel key scales and the value super-scale are fixed by the first
+    append (reading R9/R10); later single-token appends reuse them."""
+    rng = _rng(161)
+    cache = O.OracleCache(1, 1, 128, O.TensorFormat(8, "channel"), O.TensorFormat(4, scale="u8_super"))
+    k = _f32(rng.standard_normal((1, 40, 128)))
+    v = _f32(rng.laplace(0, 1, (1, 40, 128)))
+    cache.append(0, k[:, :32], v[:, :32])
+    sc = O.channel_scales(k[0, :32], 8)
+    S = O.super_scale(v[0, :32], 4)
+    for t in range(32, 40):
+        cache.append(0, k[:, t:t + 1], v[:, t:t + 1])
+    st = cache.stored(0, "k")
+    assert np.array_equal(st.chan[0], sc)
+    assert np.array_equal(st.codes[0], O.quantize_with_channel_scales(k[0], sc, 8))
+    sv = cache.stored(0, "v")
+    assert float(sv.S[0]) == float(S)
+    c, u = O.quantize_superscaled(v[0], S, 4)
+    assert np.array_equal(sv.codes[0], c) and np.array_equal(sv.u[0], u)
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting and intensity
+# ---------------------------------------------------------------------------
+def pin_byte_accounting(O):
+    """P2 "Cache precision is separate from weight precision": payload
+    KV_bytes = 2 L H_kv D T b; halving b halves it.  P3 "Per-token scales and
+    where they can live": metadata 3 / 6 / 6 / 12 percent at D = 128 (golden
+    file; the page truncates 3.125 / 6.25 / 6.25 / 12.5)."""
+    for (L, H, D, T, bits) in ((1, 1, 128, 512, 8), (32, 8, 128, 4096, 8), (2, 4, 64, 100, 4), (3, 2, 128, 7, 16)):
+        f = O.TensorFormat(bits)
+        got = O.cache_bytes(f, f, L, H, D, [T])["payload"]
+        assert got == 2 * L * H * D * T * bits // 8, (L, H, D, T, bits)
+    f16 = O.cache_bytes(O.TensorFormat(16), O.TensorFormat(16), 4, 8, 128, [1000])["payload"]
+    f8 = O.cache_bytes(O.TensorFormat(8), O.TensorFormat(8), 4, 8, 128, [1000])["payload"]
+    assert f16 == 2 * f8
+    g = json.load(open(os.path.join(GOLDEN, "metadata_overhead.json")))
+    for case in g["cases"]:
+        bits, mb = case["code_bits"], case["meta_bytes_per_token"]
+        fmt = O.TensorFormat(bits, "token", mb == 8, "f32")
+        assert O.meta_bytes_per_token(fmt) == mb
+        b = O.cache_bytes(fmt, fmt, 1, 1, g["head_dim"], [1000])
+        pct = 100.0 * b["metadata"] / b["payload"]
+        assert int(pct) == case["printed_percent"], (case, pct)
+        assert pct == 100.0 * mb * 8 / (g["head_dim"] * bits)
+    # closed forms of the five workloads' decode traffic (one layer)
+    i8 = O.TensorFormat(8)
+    assert O.decode_traffic(i8, i8, 1, 128, [512]) == 131072 + 4096
+    assert O.decode_traffic(i8, i8, 8, 128, [4096] * 8) == 67108864 + 2097152
+    a4 = O.TensorFormat(4, "token", True, "f16")
+    assert O.decode_traffic(a4, a4, 8, 128, [8192] * 32) == 268435456 + 16777216
+    kc, vs = O.TensorFormat(8, "channel"), O.TensorFormat(4, scale="u8_super")
+    assert O.decode_traffic(kc, vs, 8, 128, [65536] * 16) == 1073741824 + 536870912 + 8388608 + 128 * (512 + 4)
+    lens = [1024, 5000, 32768]
+    assert O.decode_traffic(i8, i8, 8, 128, lens, window=128) == sum(8 * (65536 + (n - 128) * 264) for n in lens)
+    pad = O.cache_bytes(i8, i8, 1, 8, 128, [145], window=128, block_tokens=16)
+    assert pad["padding"] == 8 * (16 - 17 % 16) * 264
+
+
+def pin_arithmetic_intensity(O):
+    """P3 "What the cache holds and how it is read": about one multiply-add per
+    byte at 8 bits and two at 4 bits for one query per key (golden file)."""
+    g = json.load(open(os.path.join(GOLDEN, "arith_intensity.json")))
+    for case in g["cases"]:
+        ai = O.arithmetic_intensity(case["code_bits"])
+        assert round(ai) == case["printed_ops_per_byte"], (case, ai)
+    assert abs(O.arithmetic_intensity(8) - 256 / 264) < 1e-15
+    assert abs(O.arithmetic_intensity(4) - 256 / 136) < 1e-15
+    assert O.multiply_adds(32, 128, [4096] * 8) == 2 * 32 * 128 * 4096 * 8
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
