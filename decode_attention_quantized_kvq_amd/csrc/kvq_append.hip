@@ -1,0 +1,340 @@
+// Quantize-append kernels of libkvq (gfx950).
+//
+// Each new key/value vector is quantized from itself at write time and its
+// scale stored beside it ([P3] "KV Cache Quantization and Per-Token Scale
+// Placement", section "Per-token scales and where they can live"), following
+// q = clamp(round(x / s)), x_hat = q * s ([P2] "KV cache quantization reduces
+// cache bytes with separate accuracy and kernel costs", section "Quantization
+// needs a scale convention").  Rounding is rint() of the IEEE fp64 quotient
+// (ties to even, the rule of the quantizer listing in [P3] section "The axis
+// choice is a kernel decision"); scales are evaluated in fp64 and rounded once
+// to their storage type, so codes and metadata are bit-exact against any
+// implementation of the same rule.  The write side moves a few hundred bytes
+// per token and head; these kernels favour exactness over speed.
+//
+// Launch order on the caller's stream:
+//   1. append_stats: per-channel key scales / value super-scale of sequences
+//      whose append starts at position 0 (their prefill), then frozen.
+//   2. append_quantize: one workgroup per (token, head, sequence); wave 0
+//      quantizes the key, wave 1 the value.  With a recent window it takes
+//      the tokens leaving the window (from the ring or from the input).
+//   3. append_window: writes the new tokens that stay in the bf16 window
+//      ([P1] "KV Cache Quantization Perturbs Attention Through Stored Keys and
+//      Values", section "Cache growth changes the serving trade").  Runs after
+//      2 so that ring slots are read before they are overwritten.
+
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int D = 128;
+
+__device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ inline uint16_t f32_to_bf16_bits(float f) {
+  // Round to nearest, ties to even (inputs are finite).
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ inline float load_in(const void* p, size_t idx, int bf16) {
+  return bf16 ? bf16_bits_to_f32(((const uint16_t*)p)[idx]) : ((const float*)p)[idx];
+}
+
+__device__ inline float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ inline float wave_min(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// fp64 -> fp32 storage: one rounding, ties to even; 0 becomes 2^-149.
+__device__ inline float store_f32(double v) {
+  float f = (float)v;
+  if (f == 0.0f) f = __uint_as_float(1u);
+  return f;
+}
+
+// fp64 -> fp16 with a single rounding (ties to even): round to odd into fp32
+// first (24 >= 11 + 2 bits, so the second rounding cannot double-round), then
+// let the hardware convert fp32 -> fp16 to nearest even.
+__device__ inline uint16_t f64_to_f16_bits(double x) {
+  float f = (float)x;
+  if ((double)f != x) {
+    uint32_t u = __float_as_uint(f);
+    if (fabs((double)f) > fabs(x)) u -= 1u;  // the fp32 value toward zero
+    u |= 1u;                                 // its odd neighbour: round to odd
+    f = __uint_as_float(u);
+  }
+  const _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// fp64 (positive) -> fp16 storage of a scale: 0 becomes 2^-24, overflow 65504.
+__device__ inline uint16_t store_f16(double v) {
+  uint16_t h = f64_to_f16_bits(v);
+  if ((h & 0x7FFFu) == 0) h = 0x0001u;
+  if ((h & 0x7FFFu) >= 0x7C00u) h = 0x7BFFu;
+  return h;
+}
+
+__device__ inline double f16_bits_to_f64(uint16_t h) {
+  return (double)(float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+__device__ inline int rne_code(double x, double s) { return (int)rint(x / s); }
+
+struct SeqRange {
+  int len, start, newb;
+};
+
+__device__ inline SeqRange seq_range(const AppendArgs& a, int b) {
+  SeqRange r;
+  r.len = a.seq_lens[b] > 0 ? a.seq_lens[b] : 0;
+  int nb = a.new_lens ? a.new_lens[b] : a.n_new;
+  nb = clampi(nb, 0, a.n_new);
+  if (nb > r.len) nb = r.len;
+  r.newb = nb;
+  r.start = r.len - nb;
+  return r;
+}
+
+// Capacity of quantized positions per sequence.
+__device__ inline int q_capacity(const AppendArgs& a) {
+  return a.paged ? a.bt_stride * 16 : a.max_tokens;
+}
+
+// Index (in tokens) of quantized position p of (b, h) in codes/meta arrays.
+__device__ inline size_t slot_index(const AppendArgs& a, int b, int h, int p) {
+  if (a.paged) {
+    int phys = a.block_table[(size_t)b * a.bt_stride + (p >> 4)];
+    phys = clampi(phys, 0, a.num_blocks - 1);
+    return ((size_t)phys * a.hkv + h) * 16 + (p & 15);
+  }
+  return ((size_t)b * a.hkv + h) * a.max_tokens + p;
+}
+
+__device__ inline int meta_size(MetaKind m) {
+  switch (m) {
+    case MK_F32: return 4;
+    case MK_F32Z: return 8;
+    case MK_F16: return 2;
+    case MK_F16Z: return 4;
+    case MK_U8: return 1;
+    default: return 0;
+  }
+}
+
+// Quantizes the vector whose elements 2*lane and 2*lane+1 this lane holds,
+// and stores its codes and metadata at token slot `slot`.
+__device__ void quantize_store(const TensorKind k, float x0, float x1, uint8_t* codes,
+                               uint8_t* meta, size_t slot, const float* chan, float super,
+                               int lane) {
+  const bool b8 = k.code == CK_I8 || k.code == CK_U8;
+  const bool zp = k.meta == MK_F32Z || k.meta == MK_F16Z;
+  int c0 = 0, c1 = 0;
+  if (k.channel) {
+    // Frozen per-channel scales of the keys.
+    const int qmax = b8 ? 127 : 7;
+    c0 = clampi(rne_code(x0, (double)chan[2 * lane]), -qmax, qmax);
+    c1 = clampi(rne_code(x1, (double)chan[2 * lane + 1]), -qmax, qmax);
+  } else if (k.meta == MK_U8) {
+    // 8-bit scale code relative to the frozen per-head super-scale.
+    const int qmax = b8 ? 127 : 7;
+    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    int u = 0;
+    if (amax != 0.0f) {
+      const double sigma = (double)amax / qmax;
+      u = clampi((int)rint(sigma / (double)super), 1, 255);
+      const double seff = (double)u * (double)super;  // exact
+      c0 = clampi(rne_code(x0, seff), -qmax, qmax);
+      c1 = clampi(rne_code(x1, seff), -qmax, qmax);
+    }
+    if (lane == 0) meta[slot] = (uint8_t)u;
+  } else if (!zp) {
+    const int qmax = b8 ? 127 : 7;
+    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    double s = 1.0;
+    uint32_t bits = 0;
+    if (k.meta == MK_F32) {
+      const float sf = amax == 0.0f ? 1.0f : store_f32((double)amax / qmax);
+      s = (double)sf;
+      bits = __float_as_uint(sf);
+    } else {
+      const uint16_t h = amax == 0.0f ? (uint16_t)0x3C00u : store_f16((double)amax / qmax);
+      s = f16_bits_to_f64(h);
+      bits = h;
+    }
+    if (amax != 0.0f) {
+      c0 = clampi(rne_code(x0, s), -qmax, qmax);
+      c1 = clampi(rne_code(x1, s), -qmax, qmax);
+    }
+    if (lane == 0) {
+      if (k.meta == MK_F32)
+        ((uint32_t*)meta)[slot] = bits;
+      else
+        ((uint16_t*)meta)[slot] = (uint16_t)bits;
+    }
+  } else {
+    // Zero point: the range is widened to include 0; z is the code of 0.
+    const int qmax = b8 ? 255 : 15;
+    const float lo = fminf(wave_min(fminf(x0, x1)), 0.0f);
+    const float hi = fmaxf(wave_max(fmaxf(x0, x1)), 0.0f);
+    double s = 1.0;
+    int z = 0;
+    uint32_t sbits;
+    if (k.meta == MK_F32Z) {
+      const float sf = hi == lo ? 1.0f : store_f32(((double)hi - (double)lo) / qmax);
+      s = (double)sf;
+      sbits = __float_as_uint(sf);
+    } else {
+      const uint16_t h = hi == lo ? (uint16_t)0x3C00u : store_f16(((double)hi - (double)lo) / qmax);
+      s = f16_bits_to_f64(h);
+      sbits = h;
+    }
+    if (hi != lo) {
+      z = clampi((int)rint(-(double)lo / s), 0, qmax);
+      c0 = clampi(rne_code(x0, s) + z, 0, qmax);
+      c1 = clampi(rne_code(x1, s) + z, 0, qmax);
+    }
+    if (lane == 0) {
+      if (k.meta == MK_F32Z) {
+        ((uint32_t*)meta)[2 * slot] = sbits;
+        ((float*)meta)[2 * slot + 1] = (float)z;
+      } else {
+        const _Float16 zh = (_Float16)(float)z;
+        ((uint32_t*)meta)[slot] = sbits | ((uint32_t)__builtin_bit_cast(uint16_t, zh) << 16);
+      }
+    }
+  }
+  if (b8) {
+    const uint32_t v = ((uint32_t)(c0 & 0xFF)) | ((uint32_t)(c1 & 0xFF) << 8);
+    ((uint16_t*)(codes + slot * (size_t)D))[lane] = (uint16_t)v;
+  } else {
+    const uint32_t v = ((uint32_t)(c0 & 0xF)) | ((uint32_t)(c1 & 0xF) << 4);
+    (codes + slot * (size_t)(D / 2))[lane] = (uint8_t)v;
+  }
+}
+
+__global__ void __launch_bounds__(256) append_stats(AppendArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const SeqRange r = seq_range(a, b);
+  if (r.start != 0 || r.newb == 0) return;
+  const size_t in_base = ((size_t)b * a.hkv + h) * a.n_new;
+  const int tid = threadIdx.x;
+  if (a.kk.channel && tid < D) {
+    // Absmax of each feature over the prefill, one rounding to fp32.
+    float amax = 0.0f;
+    for (int i = 0; i < r.newb; ++i)
+      amax = fmaxf(amax, fabsf(load_in(a.k_new, (in_base + i) * D + tid, a.in_bf16)));
+    const int qmax = a.kk.code == CK_I8 ? 127 : 7;
+    a.k_chan[((size_t)b * a.hkv + h) * D + tid] =
+        amax == 0.0f ? 1.0f : store_f32((double)amax / qmax);
+  }
+  if (a.vk.meta == MK_U8) {
+    // sigma_t = amax_t / qmax per token; S = RN32(max sigma / 255).
+    __shared__ double wmax[4];
+    const int w = tid >> 6, lane = tid & 63;
+    const int qmax = a.vk.code == CK_I8 ? 127 : 7;
+    double smax = 0.0;
+    for (int i = w; i < r.newb; i += 4) {
+      const size_t row = (in_base + i) * D;
+      const float x0 = load_in(a.v_new, row + 2 * lane, a.in_bf16);
+      const float x1 = load_in(a.v_new, row + 2 * lane + 1, a.in_bf16);
+      const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+      smax = fmax(smax, (double)amax / qmax);
+    }
+    if (lane == 0) wmax[w] = smax;
+    __syncthreads();
+    if (tid == 0) {
+      const double m = fmax(fmax(wmax[0], wmax[1]), fmax(wmax[2], wmax[3]));
+      a.v_super[(size_t)b * a.hkv + h] = m == 0.0 ? 1.0f : store_f32(m / 255.0);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SeqRange r = seq_range(a, b);
+  int p, src_row;     // quantized position; row of the new input or -1
+  if (a.window) {
+    const int qlo = r.start - a.window > 0 ? r.start - a.window : 0;
+    const int qhi = r.len - a.window > 0 ? r.len - a.window : 0;
+    if (i >= qhi - qlo) return;
+    p = qlo + i;
+    src_row = p >= r.start ? p - r.start : -1;
+  } else {
+    if (i >= r.newb) return;
+    p = r.start + i;
+    src_row = i;
+  }
+  if (p >= q_capacity(a)) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const TensorKind k = w == 0 ? a.kk : a.vk;
+  const void* src = w == 0 ? a.k_new : a.v_new;
+  float x0, x1;
+  if (src_row >= 0) {
+    const size_t row = (((size_t)b * a.hkv + h) * a.n_new + src_row) * D;
+    x0 = load_in(src, row + 2 * lane, a.in_bf16);
+    x1 = load_in(src, row + 2 * lane + 1, a.in_bf16);
+  } else {
+    const uint16_t* ring = w == 0 ? a.k_win : a.v_win;
+    const size_t row = (((size_t)b * a.hkv + h) * a.window + (p % a.window)) * D;
+    x0 = bf16_bits_to_f32(ring[row + 2 * lane]);
+    x1 = bf16_bits_to_f32(ring[row + 2 * lane + 1]);
+  }
+  const size_t slot = slot_index(a, b, h, p);
+  uint8_t* codes = w == 0 ? a.k_codes : a.v_codes;
+  uint8_t* meta = w == 0 ? a.k_meta : a.v_meta;
+  const float* chan = (w == 0 && k.channel) ? a.k_chan + ((size_t)b * a.hkv + h) * D : nullptr;
+  const float super = (w == 1 && k.meta == MK_U8) ? a.v_super[(size_t)b * a.hkv + h] : 1.0f;
+  quantize_store(k, x0, x1, codes, meta, slot, chan, super, lane);
+}
+
+__global__ void __launch_bounds__(128) append_window(AppendArgs a) {
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SeqRange r = seq_range(a, b);
+  const int first = r.len - a.window > r.start ? r.len - a.window : r.start;
+  const int p = first + i;
+  if (p >= r.len) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const void* src = w == 0 ? a.k_new : a.v_new;
+  uint16_t* ring = w == 0 ? a.k_win : a.v_win;
+  const size_t in_row = (((size_t)b * a.hkv + h) * a.n_new + (p - r.start)) * D;
+  const size_t out_row = (((size_t)b * a.hkv + h) * a.window + (p % a.window)) * D;
+  for (int e = lane; e < D; e += 64) {
+    const uint16_t v = a.in_bf16 ? ((const uint16_t*)src)[in_row + e]
+                                 : f32_to_bf16_bits(((const float*)src)[in_row + e]);
+    ring[out_row + e] = v;
+  }
+}
+
+}  // namespace
+
+kvq_status launch_append(const AppendArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 heads(a.hkv, a.batch);
+  if (a.kk.channel || a.vk.meta == MK_U8) {
+    hipLaunchKernelGGL(append_stats, heads, dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+  }
+  const int nq = a.window ? a.n_new + a.window : a.n_new;
+  hipLaunchKernelGGL(append_quantize, dim3(nq, a.hkv, a.batch), dim3(128), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+  if (a.window) {
+    const int nw = a.n_new < a.window ? a.n_new : a.window;
+    hipLaunchKernelGGL(append_window, dim3(nw, a.hkv, a.batch), dim3(128), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
+}
+
+}  // namespace kvq

@@ -1,0 +1,851 @@
+// Split-T decode attention over a quantized KV cache (gfx950).
+//
+// Computes, for each query head, s_i = q . k_hat_i / sqrt(D), a = softmax(s),
+// o = sum_i a_i v_hat_i over every cached token ([P1] "KV Cache Quantization
+// Perturbs Attention Through Stored Keys and Values", section "Key error acts
+// before the softmax"; [P2] "KV cache quantization reduces cache bytes with
+// separate accuracy and kernel costs", section "Keys and values need not have
+// identical error sensitivity").  As in [P3] "KV Cache Quantization and
+// Per-Token Scale Placement", section "The axis choice is a kernel decision",
+// the dot product runs on the integer-valued codes, the per-token key scale
+// multiplies each score once after it, and a per-channel key scale is moved
+// onto the query.
+//
+// Kernel 1 (decode_split): one workgroup of 4 waves per (token split, KV
+// head, sequence).  Each wave streams 32-token tiles of its quarter of the
+// split straight from HBM into registers (coalesced 64/128-byte rows, the next
+// tile's loads in flight while the current one computes), converts codes to
+// fp16 exactly, and runs both contractions on the matrix cores:
+//   scores  S[16 tok x 16 col] += K[16 tok x 32 d] Q[32 d x 16 col]
+//   output  O[16 d x 16 col]   += V^T[16 d x 32 tok] P[32 tok x 16 col]
+// The G query heads that share the KV head occupy the 16 columns as fp16
+// high/low halves of the query (and of the weights), so every loaded tile is
+// used by all G heads and both products are exact to about 2^-22.  Online
+// softmax runs in base 2.  The 4 waves merge through LDS and the workgroup
+// writes one partial (max, sum, normalized output) per query head.
+// Kernel 2 (decode_combine): log-sum-exp combine of the partials of each
+// (sequence, query head) into the fp32 output.
+
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int WAVES = 4;
+constexpr int TILE = 32;
+constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float NEG_INF = -__builtin_inff();
+
+// fp16 constants (two per dword)
+constexpr uint32_t MAGIC = 0x64006400u;      // 1024.0 | 1024.0 exponent pattern
+constexpr uint32_t H_M1024 = 0xE400E400u;    // -1024
+constexpr uint32_t H_M1032 = 0xE408E408u;    // -1032 (signed nibble: bias 8)
+constexpr uint32_t H_M1152 = 0xE480E480u;    // -1152 (signed byte: bias 128)
+constexpr uint32_t H_SIXTEENTH = 0x2C002C00u;  // 1/16
+constexpr uint32_t H_M64 = 0xD400D400u;      // -64
+constexpr uint32_t H_M72 = 0xD480D480u;      // -72
+
+__device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ inline uint32_t h2_add(uint32_t a, uint32_t c) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a) + __builtin_bit_cast(half2v, c));
+}
+
+__device__ inline uint32_t h2_fma(uint32_t a, uint32_t m, uint32_t c) {
+  const half2v r = __builtin_bit_cast(half2v, a) * __builtin_bit_cast(half2v, m) +
+                   __builtin_bit_cast(half2v, c);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ inline half8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(half8, u32x4{a, b, c, d});
+}
+
+__device__ inline bf16x8 as_b8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
+}
+
+__device__ inline uint32_t pack_h2(_Float16 lo, _Float16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+__device__ inline uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ inline float bf16_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <int G>
+__device__ inline float ror_g(float v) {
+  // Value of the lane G columns away inside the 16-lane row (DPP row_ror).
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), 0x120 + G, 0xF, 0xF, false));
+}
+
+__device__ inline float rows_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+__device__ inline float rows_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// Smallest power of two >= x (x >= 0 finite); 0 stays 0.
+__device__ inline float pow2_ceil(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u & 0x007FFFFFu) u = (u & 0x7F800000u) + 0x00800000u;
+  return __uint_as_float(u);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Code formats: byte layout per token row and conversion to fp16 MFMA operands
+// ---------------------------------------------------------------------------
+template <int CK>
+struct Codes {
+  static constexpr bool B8 = (CK == CK_I8 || CK == CK_U8);
+  static constexpr bool SIGNED = (CK == CK_I8 || CK == CK_I4);
+  static constexpr int ROW = B8 ? D : D / 2;
+};
+
+// Converts 4 int8 codes of one dword into two fp16 pairs (d0,d1), (d2,d3),
+// exactly: the byte becomes the mantissa of 1024 + u, then the bias goes.
+template <bool SIGNED>
+__device__ inline void cvt_b8(uint32_t w, uint32_t& p01, uint32_t& p23) {
+  if (SIGNED) w ^= 0x80808080u;
+  p01 = h2_add(perm(0x64646464u, w, 0x04010400u), SIGNED ? H_M1152 : H_M1024);
+  p23 = h2_add(perm(0x64646464u, w, 0x04030402u), SIGNED ? H_M1152 : H_M1024);
+}
+
+// Converts 8 int4 codes of one dword into four fp16 pairs, ordered
+// (n0,n4), (n1,n5), (n2,n6), (n3,n7) where n_i is nibble i (bits 4i..4i+3).
+template <bool SIGNED>
+__device__ inline void cvt_b4(uint32_t w, uint32_t out[4]) {
+  if (SIGNED) w ^= 0x88888888u;
+  const uint32_t w8 = w >> 8;
+  out[0] = h2_add((w & 0x000F000Fu) | MAGIC, SIGNED ? H_M1032 : H_M1024);
+  out[1] = h2_fma((w & 0x00F000F0u) | MAGIC, H_SIXTEENTH, SIGNED ? H_M72 : H_M64);
+  out[2] = h2_add((w8 & 0x000F000Fu) | MAGIC, SIGNED ? H_M1032 : H_M1024);
+  out[3] = h2_fma((w8 & 0x00F000F0u) | MAGIC, H_SIXTEENTH, SIGNED ? H_M72 : H_M64);
+}
+
+// Feature index d held by the lane of row group g at k-slot e of the j-th
+// score MFMA.  8-bit keys: the lane loads bytes [16g,16g+16) and
+// [64+16g, 80+16g) of the token row.  4-bit keys: bytes [16g, 16g+16) hold
+// features [32g, 32g+32), and cvt_b4 interleaves nibbles (0,4,1,5,2,6,3,7).
+template <bool B8>
+__device__ inline int key_feature(int j, int g, int e) {
+  if (B8) return (j < 2 ? 16 * g + 8 * j : 64 + 16 * g + 8 * (j - 2)) + e;
+  const int p4 = (e >> 1) + ((e & 1) << 2);
+  return 32 * g + 8 * j + p4;
+}
+
+// ---------------------------------------------------------------------------
+// Per-token metadata
+// ---------------------------------------------------------------------------
+template <int MK>
+struct Meta {
+  static constexpr int BYTES = MK == MK_F32 ? 4 : MK == MK_F32Z ? 8 : MK == MK_F16 ? 2
+                             : MK == MK_F16Z ? 4 : MK == MK_U8 ? 1 : 0;
+  static constexpr bool ZP = (MK == MK_F32Z || MK == MK_F16Z);
+  u32x4 r0, r1;  // raw bytes of 4 consecutive tokens (8-byte formats use both)
+
+  __device__ inline void load(const uint8_t* base, int tok) {
+    if (MK == MK_F32 || MK == MK_F16Z) {
+      r0 = *(const u32x4*)(base + (size_t)tok * 4);
+    } else if (MK == MK_F32Z) {
+      r0 = *(const u32x4*)(base + (size_t)tok * 8);
+      r1 = *(const u32x4*)(base + (size_t)tok * 8 + 16);
+    } else if (MK == MK_F16) {
+      const u32x2 v = *(const u32x2*)(base + (size_t)tok * 2);
+      r0 = u32x4{v.x, v.y, 0u, 0u};
+    } else if (MK == MK_U8) {
+      r0 = u32x4{*(const uint32_t*)(base + tok), 0u, 0u, 0u};
+    }
+  }
+  // scale (and zero point) of token i in 0..3
+  __device__ inline float scale(int i) const {
+    if (MK == MK_F32) return __uint_as_float(r0[i]);
+    if (MK == MK_F32Z) return __uint_as_float(i < 2 ? r0[2 * i] : r1[2 * (i - 2)]);
+    if (MK == MK_F16) {
+      const uint32_t w = r0[i >> 1];
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)(i & 1 ? w >> 16 : w & 0xFFFFu));
+    }
+    if (MK == MK_F16Z) return (float)__builtin_bit_cast(_Float16, (uint16_t)(r0[i] & 0xFFFFu));
+    if (MK == MK_U8) return (float)((r0[0] >> (8 * i)) & 0xFFu);
+    return 1.0f;
+  }
+  __device__ inline float zero(int i) const {
+    if (MK == MK_F32Z) return __uint_as_float(i < 2 ? r0[2 * i + 1] : r1[2 * (i - 2) + 1]);
+    if (MK == MK_F16Z) return (float)__builtin_bit_cast(_Float16, (uint16_t)(r0[i] >> 16));
+    return 0.0f;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Where the 16-token blocks of a (sequence, KV head) live
+// ---------------------------------------------------------------------------
+struct Addr {
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* km;
+  const uint8_t* vm;
+  const int32_t* table;  // paged: row of the block table, else nullptr
+  int num_blocks, hkv, h;
+  size_t head_tok;       // contiguous: first token slot of this head
+  int nblk;              // blocks holding tokens
+
+  // token slot index of block `blk` (clamped to the blocks holding tokens)
+  __device__ inline size_t block_slot(int blk) const {
+    blk = blk < nblk ? blk : nblk - 1;
+    if (table) {
+      int phys = table[blk];
+      phys = phys < 0 ? 0 : (phys >= num_blocks ? num_blocks - 1 : phys);
+      return ((size_t)phys * hkv + h) * 16;
+    }
+    return head_tok + (size_t)blk * 16;
+  }
+};
+
+// Raw registers of one 32-token tile.
+template <int KC, int KM, int VC, int VM>
+struct TileRaw {
+  static constexpr bool KB8 = Codes<KC>::B8;
+  static constexpr bool VB8 = Codes<VC>::B8;
+  u32x4 k[2][KB8 ? 2 : 1];   // per 16-token block
+  u32x2 v8[VB8 ? 8 : 1];     // 8-bit values: 8 tokens x 8 bytes
+  uint32_t v4[VB8 ? 1 : 8];  // 4-bit values: 8 tokens x 4 bytes
+  Meta<KM> km[2];
+  Meta<VM> vm[2];
+};
+
+template <int KC, int KM, int VC, int VM>
+__device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int t0, int c, int g) {
+  constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const size_t slot = ad.block_slot((t0 >> 4) + bb);
+    const uint8_t* kr = ad.k + (slot + c) * KROW;
+    if (Codes<KC>::B8) {
+      t.k[bb][0] = *(const u32x4*)(kr + 16 * g);
+      t.k[bb][KROW == D ? 1 : 0] = *(const u32x4*)(kr + 64 + 16 * g);
+    } else {
+      t.k[bb][0] = *(const u32x4*)(kr + 16 * g);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* vr = ad.v + (slot + 4 * g + i) * VROW;
+      if (Codes<VC>::B8)
+        t.v8[4 * bb + i] = *(const u32x2*)(vr + 8 * c);
+      else
+        t.v4[4 * bb + i] = *(const uint32_t*)(vr + 4 * c);
+    }
+    if (Meta<KM>::BYTES) t.km[bb].load(ad.km, (int)(slot + 4 * g));
+    if (Meta<VM>::BYTES) t.vm[bb].load(ad.vm, (int)(slot + 4 * g));
+  }
+}
+
+// Key operand of the j-th score MFMA for block bb.
+template <int KC, int KM, int VC, int VM>
+__device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, int j) {
+  constexpr bool S = Codes<KC>::SIGNED;
+  if (Codes<KC>::B8) {
+    const u32x4 r = t.k[bb][j >> 1];
+    const uint32_t w0 = (j & 1) ? r.z : r.x, w1 = (j & 1) ? r.w : r.y;
+    uint32_t a, b, c, d;
+    cvt_b8<S>(w0, a, b);
+    cvt_b8<S>(w1, c, d);
+    return as_h8(a, b, c, d);
+  } else {
+    uint32_t o[4];
+    cvt_b4<S>(t.k[bb][0][j], o);
+    return as_h8(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Value operand of the j-th output MFMA: lane (c, g) gives feature 8c + j of
+// its 8 tokens, two tokens per fp16 pair.
+template <int KC, int KM, int VC, int VM>
+__device__ inline void value_frags(const TileRaw<KC, KM, VC, VM>& t, half8 out[8]) {
+  constexpr bool S = Codes<VC>::SIGNED;
+  uint32_t pr[8][4];  // [j][token pair]
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    if (Codes<VC>::B8) {
+      const u32x2 A = t.v8[2 * pp], B = t.v8[2 * pp + 1];
+      uint32_t x[4] = {perm(B.x, A.x, 0x05010400u), perm(B.x, A.x, 0x07030602u),
+                       perm(B.y, A.y, 0x05010400u), perm(B.y, A.y, 0x07030602u)};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t lo, hi;
+        cvt_b8<S>(x[q], lo, hi);  // x[q] holds (A d, B d, A d+1, B d+1)
+        // cvt_b8 pairs bytes (0,1) and (2,3): (A,B) at feature 2q and 2q+1
+        pr[2 * q][pp] = lo;
+        pr[2 * q + 1][pp] = hi;
+      }
+    } else {
+      const uint32_t A = t.v4[2 * pp], B = t.v4[2 * pp + 1];
+      uint32_t o[4];
+      cvt_b4<S>(perm(B, A, 0x05040100u), o);   // bytes (A0, A1, B0, B1)
+      // o pairs nibble n of the low half-word (A) with nibble n of the high
+      // half-word (B): features 0, 1, 2, 3 in the order (n0, n1?, ...)
+      pr[0][pp] = o[0];
+      pr[1][pp] = o[1];
+      pr[2][pp] = o[2];
+      pr[3][pp] = o[3];
+      cvt_b4<S>(perm(B, A, 0x07060302u), o);   // bytes (A2, A3, B2, B3)
+      pr[4][pp] = o[0];
+      pr[5][pp] = o[1];
+      pr[6][pp] = o[2];
+      pr[7][pp] = o[3];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = as_h8(pr[j][0], pr[j][1], pr[j][2], pr[j][3]);
+}
+
+// ---------------------------------------------------------------------------
+// Per-wave state of the online softmax
+// ---------------------------------------------------------------------------
+struct Softmax {
+  float m;   // running max (base-2 units), identical across the 4 row groups
+  float l;   // this lane's share of the running sum of 2^(s - m)
+  float R;   // running power-of-two reference of the folded value scale
+  float z;   // this lane's share of sum w * zero_point (zero-point values)
+  f32x4 o[8];
+};
+
+// Processes one 32-token tile already in registers.
+template <int KC, int KM, bool KCH, int VC, int VM, int G>
+__device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, int tend,
+                                    const half8 qf[4], float qs, float sumq, int c, int g,
+                                    int limb, Softmax& st) {
+  // scores
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag(t, 0, j), qf[j], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag(t, 1, j), qf[j], s1, 0, 0, 0);
+  }
+  float s[8], vs[8], vz[8];
+  bool valid[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int bb = e >> 2, i = e & 3;
+    const float raw0 = bb ? s1[i] : s0[i];
+    const float raw = raw0 + ror_g<G>(raw0);  // high + low half of the query
+    const int tok = t0 + 16 * bb + 4 * g + i;
+    valid[e] = tok < tend;
+    float v;
+    if (KCH) {
+      v = raw * qs;
+    } else {
+      const float ks = t.km[bb].scale(i);
+      v = (Meta<KM>::ZP ? (raw - t.km[bb].zero(i) * sumq) : raw) * (ks * qs);
+    }
+    s[e] = valid[e] ? v : NEG_INF;
+    vs[e] = valid[e] ? t.vm[bb].scale(i) : 0.0f;
+    vz[e] = (Meta<VM>::ZP && valid[e]) ? t.vm[bb].zero(i) : 0.0f;
+  }
+  float mt = s[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[e]);
+  mt = rows_max(mt);
+  const float mn = fmaxf(st.m, mt);
+  const float mu = mn == NEG_INF ? 0.0f : mn;
+  const float alpha = exp2_fast(st.m - mu);
+  float p[8], lsum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = exp2_fast(s[e] - mu);
+    lsum += p[e];
+  }
+  st.l = st.l * alpha + lsum;
+  st.m = mn;
+  // Folded value scale, kept in (0, 1] by a running power-of-two reference.
+  float f = alpha, inv;
+  if (VM == MK_U8) {
+    inv = 1.0f / 256.0f;
+  } else {
+    float sv = vs[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) sv = fmaxf(sv, vs[e]);
+    const float Rn = fmaxf(st.R, pow2_ceil(rows_max(sv)));
+    f = alpha * (st.R / Rn);
+    st.R = Rn;
+    inv = 1.0f / Rn;
+  }
+  if (__any(f != 1.0f)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] *= f;
+    st.z *= f;
+  }
+  float w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    w[e] = p[e] * (vs[e] * inv);
+    if (Meta<VM>::ZP) st.z += w[e] * vz[e];
+  }
+  // weights as fp16 high/low halves, one half per column limb
+  uint32_t pw[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    _Float16 h[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float x = w[2 * pp + k];
+      const _Float16 hi = (_Float16)x;
+      const _Float16 lo = (_Float16)(x - (float)hi);
+      h[k] = limb ? lo : hi;
+    }
+    pw[pp] = pack_h2(h[0], h[1]);
+  }
+  const half8 pf = as_h8(pw[0], pw[1], pw[2], pw[3]);
+  half8 vf[8];
+  value_frags(t, vf);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[j], pf, st.o[j], 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Window tiles: bf16 keys and values, no metadata (bf16 MFMA)
+// ---------------------------------------------------------------------------
+struct WinRaw {
+  u32x4 k[2][4];   // per block: token row c, features [32j + 8g, +8)
+  u32x4 v[8];      // 8 tokens, features [8c, 8c + 8)
+};
+
+__device__ inline void load_win_tile(WinRaw& t, const uint16_t* kw, const uint16_t* vw, int t0,
+                                     int nw, int c, int g) {
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    int tk = t0 + 16 * bb + c;
+    tk = tk < nw ? tk : nw - 1;
+    const uint16_t* kr = kw + (size_t)tk * D;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.k[bb][j] = *(const u32x4*)(kr + 32 * j + 8 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int tv = t0 + 16 * bb + 4 * g + i;
+      tv = tv < nw ? tv : nw - 1;
+      t.v[4 * bb + i] = *(const u32x4*)(vw + (size_t)tv * D + 8 * c);
+    }
+  }
+}
+
+template <int G>
+__device__ inline void compute_win_tile(const WinRaw& t, int t0, int nw, const bf16x8 qf[4],
+                                        float qs, int c, int g, int limb, Softmax& st) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 a = t.k[0][j], b = t.k[1][j];
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(a.x, a.y, a.z, a.w), qf[j], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(b.x, b.y, b.z, b.w), qf[j], s1, 0, 0, 0);
+  }
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int bb = e >> 2, i = e & 3;
+    const float raw0 = bb ? s1[i] : s0[i];
+    const float raw = raw0 + ror_g<G>(raw0);
+    s[e] = (t0 + 16 * bb + 4 * g + i) < nw ? raw * qs : NEG_INF;
+  }
+  float mt = s[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[e]);
+  mt = rows_max(mt);
+  const float mn = fmaxf(st.m, mt);
+  const float mu = mn == NEG_INF ? 0.0f : mn;
+  const float alpha = exp2_fast(st.m - mu);
+  float p[8], lsum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = exp2_fast(s[e] - mu);
+    lsum += p[e];
+  }
+  st.l = st.l * alpha + lsum;
+  st.m = mn;
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
+  }
+  uint32_t pw[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    uint16_t h[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float x = p[2 * pp + k];
+      const uint16_t hi = bf16_rne(x);
+      const uint16_t lo = bf16_rne(x - bf16_f32(hi));
+      h[k] = limb ? lo : hi;
+    }
+    pw[pp] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+  }
+  const bf16x8 pf = as_b8(pw[0], pw[1], pw[2], pw[3]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t pr[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const u32x4 A = t.v[2 * pp], B = t.v[2 * pp + 1];
+      const uint32_t a = A[j >> 1], b = B[j >> 1];
+      pr[pp] = (j & 1) ? perm(b, a, 0x07060302u) : perm(b, a, 0x05040100u);
+    }
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(pr[0], pr[1], pr[2], pr[3]), pf,
+                                                      st.o[j], 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query setup: lane (c, g) holds query head (c mod G), as the high (limb 0)
+// or low (limb 1) fp16 half, for the features its key operand covers.
+// ---------------------------------------------------------------------------
+__device__ inline float load_q(const void* q, size_t idx, int bf16) {
+  return bf16 ? bf16_f32(((const uint16_t*)q)[idx]) : ((const float*)q)[idx];
+}
+
+// Power-of-two scale that brings the head's largest |q| into [2^12, 2^13).
+__device__ inline float q_norm_scale(float amax, float* inv) {
+  if (!(amax > 0.0f)) {
+    *inv = 1.0f;
+    return 1.0f;
+  }
+  int ex;
+  frexpf(amax, &ex);            // amax = m 2^ex, m in [0.5, 1)
+  const int e = 13 - ex;
+  *inv = ldexpf(1.0f, -e);
+  return ldexpf(1.0f, e);
+}
+
+// ---------------------------------------------------------------------------
+// Wave -> workgroup merge and partial write
+// ---------------------------------------------------------------------------
+template <int G>
+struct Shared {
+  float o[WAVES][G][D];
+  float m[WAVES][G];
+  float l[WAVES][G];
+};
+
+template <int G>
+__device__ inline void wave_finish(Softmax& st, float scale_out, int c, int g, int wave,
+                                   Shared<G>& sh) {
+  const float l = rows_sum(st.l);
+  const float z = rows_sum(st.z);
+  float ofs[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ofs[j][i] = st.o[j][i] + ror_g<G>(st.o[j][i]);
+  if (c < G) {
+    const float k = l > 0.0f ? scale_out / l : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sh.o[wave][c][32 * g + 8 * i + j] = (ofs[j][i] - z) * k;
+    if (g == 0) {
+      sh.m[wave][c] = l > 0.0f ? st.m : NEG_INF;
+      sh.l[wave][c] = l;
+    }
+  }
+}
+
+template <int G>
+__device__ inline void block_merge(const DecodeArgs& a, const Shared<G>& sh, int b, int h,
+                                   int split) {
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64) {
+    const int hh = idx / D, d = idx % D;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.m[w][hh]);
+    float ws = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float e = sh.l[w][hh] > 0.0f ? sh.l[w][hh] * exp2_fast(sh.m[w][hh] - M) : 0.0f;
+      ws += e;
+      acc += e * sh.o[w][hh][d];
+    }
+    const size_t row = ((size_t)b * a.hq + (size_t)h * G + hh) * a.nsp + split;
+    a.part_o[row * D + d] = ws > 0.0f ? acc / ws : 0.0f;
+    if (d == 0) {
+      a.part_ml[2 * row] = M;
+      a.part_ml[2 * row + 1] = ws;
+    }
+  }
+}
+
+struct SeqInfo {
+  int len, nw, nq;
+};
+
+__device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
+  SeqInfo s;
+  int len = a.seq_lens[b];
+  len = len > 0 ? len : 0;
+  const int cap = (a.paged ? a.bt_stride * 16 : a.max_tokens) + a.window;
+  len = len < cap ? len : cap;
+  s.len = len;
+  s.nw = len < a.window ? len : a.window;
+  s.nq = len - s.nw;
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1
+// ---------------------------------------------------------------------------
+template <int G>
+__device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G>& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int hh = c % G, limb = (c / G) & 1;
+  const size_t qrow = ((size_t)b * a.hq + (size_t)h * G + hh) * D;
+  float qv[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[8 * j + e] = load_q(a.q, qrow + 32 * j + 8 * g + e, a.in_bf16);
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(qv[k]));
+  float inv;
+  const float sc = q_norm_scale(rows_max(amax), &inv);
+  const float qs = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128)
+  bf16x8 qf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      uint16_t hv[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float x = qv[8 * j + 2 * pp + k] * sc;
+        const uint16_t hi = bf16_rne(x);
+        hv[k] = limb ? bf16_rne(x - bf16_f32(hi)) : hi;
+      }
+      w[pp] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+    }
+    qf[j] = as_b8(w[0], w[1], w[2], w[3]);
+  }
+  Softmax st;
+  st.m = NEG_INF;
+  st.l = 0.0f;
+  st.R = 1.0f;
+  st.z = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const size_t head = ((size_t)b * a.hkv + h) * a.window * D;
+  const int per = (a.window + WAVES - 1) / WAVES;
+  const int w0 = wave * per, w1 = min(w0 + per, nw);
+  for (int t0 = w0; t0 < w1; t0 += TILE) {
+    WinRaw t;
+    load_win_tile(t, a.k_win + head, a.v_win + head, t0, nw, c, g);
+    compute_win_tile<G>(t, t0, w1, qf, qs, c, g, limb, st);
+  }
+  wave_finish<G>(st, 1.0f, c, g, wave, sh);
+  block_merge<G>(a, sh, b, h, a.n_split);
+}
+
+template <int KC, int KM, bool KCH, int VC, int VM, int G>
+__global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
+  __shared__ Shared<G> sh;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SeqInfo si = seq_info(a, b);
+  if (a.window && split == a.n_split) {
+    if (si.nw > 0) window_split<G>(a, b, h, si.nw, sh);
+    return;
+  }
+  const int tok0 = split * a.split_tokens;
+  if (tok0 >= si.nq) return;
+  const int tok1 = min(tok0 + a.split_tokens, si.nq);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int hh = c % G, limb = (c / G) & 1;
+  constexpr bool KB8 = Codes<KC>::B8;
+
+  // query fragments (features as the key operand orders them)
+  const size_t qrow = ((size_t)b * a.hq + (size_t)h * G + hh) * D;
+  const float* chan = KCH ? a.k_chan + ((size_t)b * a.hkv + h) * D : nullptr;
+  float qv[32];
+  float amax = 0.0f, qsum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = key_feature<KB8>(j, g, e);
+      float x = load_q(a.q, qrow + d, a.in_bf16);
+      if (KCH) x *= chan[d];  // per-channel key scale moved onto the query
+      qv[8 * j + e] = x;
+      amax = fmaxf(amax, fabsf(x));
+    }
+  float inv;
+  const float sc = q_norm_scale(rows_max(amax), &inv);
+  const float qs = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128)
+  half8 qf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      _Float16 hv[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float x = qv[8 * j + 2 * pp + k] * sc;
+        qsum += x;
+        const _Float16 hi = (_Float16)x;
+        hv[k] = limb ? (_Float16)(x - (float)hi) : hi;
+      }
+      w[pp] = pack_h2(hv[0], hv[1]);
+    }
+    qf[j] = as_h8(w[0], w[1], w[2], w[3]);
+  }
+  const float sumq = Meta<KM>::ZP ? rows_sum(qsum) : 0.0f;
+
+  Addr ad;
+  ad.k = a.k_codes;
+  ad.v = a.v_codes;
+  ad.km = a.k_meta;
+  ad.vm = a.v_meta;
+  ad.num_blocks = a.num_blocks;
+  ad.hkv = a.hkv;
+  ad.h = h;
+  ad.nblk = (si.nq + 15) >> 4;
+  if (a.paged) {
+    ad.table = a.block_table + (size_t)b * a.bt_stride;
+    ad.head_tok = 0;
+  } else {
+    ad.table = nullptr;
+    ad.head_tok = ((size_t)b * a.hkv + h) * a.max_tokens;
+  }
+
+  Softmax st;
+  st.m = NEG_INF;
+  st.l = 0.0f;
+  st.R = __uint_as_float(0x00800000u);  // 2^-126
+  st.z = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int per = a.split_tokens / WAVES;
+  const int w0 = tok0 + wave * per;
+  const int w1 = min(w0 + per, tok1);
+  TileRaw<KC, KM, VC, VM> ta, tb;
+  int t = w0;
+  if (t < w1) load_tile(ta, ad, t, c, g);
+  while (t < w1) {
+    int tn = t + TILE;
+    if (tn < w1) load_tile(tb, ad, tn, c, g);
+    compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, c, g, limb, st);
+    t = tn;
+    if (t >= w1) break;
+    tn = t + TILE;
+    if (tn < w1) load_tile(ta, ad, tn, c, g);
+    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t, w1, qf, qs, sumq, c, g, limb, st);
+    t = tn;
+  }
+  float scale_out;
+  if (VM == MK_U8)
+    scale_out = 256.0f * a.v_super[(size_t)b * a.hkv + h];
+  else
+    scale_out = st.R;
+  wave_finish<G>(st, scale_out, c, g, wave, sh);
+  block_merge<G>(a, sh, b, h, split);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: log-sum-exp combine of the partials of one (sequence, query head)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) decode_combine(DecodeArgs a) {
+  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const SeqInfo si = seq_info(a, b);
+  const int ns = (si.nq + a.split_tokens - 1) / a.split_tokens;
+  const bool overflow = ns > a.n_split;  // longer than the launch was planned for
+  const size_t row0 = ((size_t)b * a.hq + hq) * a.nsp;
+  auto valid = [&](int j) { return j < a.n_split ? j < ns : si.nw > 0; };
+  float M = NEG_INF;
+  for (int j = lane; j < a.nsp; j += 64)
+    if (valid(j)) M = fmaxf(M, a.part_ml[2 * (row0 + j)]);
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float ws = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int j = 0; j < a.nsp; ++j) {
+    if (!valid(j)) continue;
+    const float m = a.part_ml[2 * (row0 + j)], l = a.part_ml[2 * (row0 + j) + 1];
+    const float e = l > 0.0f ? l * exp2_fast(m - M) : 0.0f;
+    const float2 v = *(const float2*)(a.part_o + (row0 + j) * D + 2 * lane);
+    ws += e;
+    o0 += e * v.x;
+    o1 += e * v.y;
+  }
+  float2 r;
+  if (overflow) {
+    r.x = r.y = __builtin_nanf("");
+  } else if (ws > 0.0f) {
+    r.x = o0 / ws;
+    r.y = o1 / ws;
+  } else {
+    r.x = r.y = 0.0f;
+  }
+  *(float2*)(a.out + ((size_t)b * a.hq + hq) * D + 2 * lane) = r;
+}
+
+template <int KC, int KM, bool KCH, int VC, int VM>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.nsp, a.hkv, a.batch), block(256);
+  if (a.nsp > 0) {
+    switch (a.group) {
+      case 1: hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, 1>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, 2>), grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, 4>), grid, block, 0, s, a); break;
+      case 8: hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, 8>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(decode_combine, dim3(a.hq, a.batch), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+kvq_status launch_decode(const DecodeArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const TensorKind k = a.kk, v = a.vk;
+  hipError_t e = hipErrorInvalidValue;
+  if (k.code == CK_I8 && k.meta == MK_F32 && v.code == CK_I8 && v.meta == MK_F32)
+    e = launch_g<CK_I8, MK_F32, false, CK_I8, MK_F32>(a, s);
+  else if (k.code == CK_U4 && k.meta == MK_F16Z && v.code == CK_U4 && v.meta == MK_F16Z)
+    e = launch_g<CK_U4, MK_F16Z, false, CK_U4, MK_F16Z>(a, s);
+  else if (k.code == CK_I8 && k.channel && v.code == CK_I4 && v.meta == MK_U8)
+    e = launch_g<CK_I8, MK_NONE, true, CK_I4, MK_U8>(a, s);
+  else if (k.code == CK_I4 && k.meta == MK_F32 && v.code == CK_I4 && v.meta == MK_F32)
+    e = launch_g<CK_I4, MK_F32, false, CK_I4, MK_F32>(a, s);
+  else if (k.code == CK_I8 && k.meta == MK_F32 && v.code == CK_I4 && v.meta == MK_F32)
+    e = launch_g<CK_I8, MK_F32, false, CK_I4, MK_F32>(a, s);
+  else if (k.code == CK_U8 && k.meta == MK_F16Z && v.code == CK_U8 && v.meta == MK_F16Z)
+    e = launch_g<CK_U8, MK_F16Z, false, CK_U8, MK_F16Z>(a, s);
+  else
+    return KVQ_ERR_UNSUPPORTED;
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace kvq

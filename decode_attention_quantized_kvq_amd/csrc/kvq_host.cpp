@@ -1,0 +1,364 @@
+// libkvq host side: argument validation, byte accounting, split planning and
+// the C entry points.  No device code here; launches live in the .hip files.
+//
+// Pages: [P1] "KV Cache Quantization Perturbs Attention Through Stored Keys
+// and Values"; [P2] "KV cache quantization reduces cache bytes with separate
+// accuracy and kernel costs"; [P3] "KV Cache Quantization and Per-Token Scale
+// Placement".
+
+#include <algorithm>
+#include <cstdint>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+int meta_bytes(const kvq_tensor_fmt& f) {
+  // P3 "Per-token scales and where they can live": a 4-byte scale per token,
+  // or a scale plus a zero point; an 8-bit scale code under a super-scale.
+  if (f.bits == 16 || f.axis == KVQ_AXIS_CHANNEL) return 0;
+  if (f.scale_fmt == KVQ_SCALE_U8_SUPER) return 1;
+  const int w = f.scale_fmt == KVQ_SCALE_F32 ? 4 : 2;
+  return f.zero_point ? 2 * w : w;
+}
+
+static size_t side_bytes(const kvq_tensor_fmt& f, int d) {
+  if (f.bits == 16) return 0;
+  if (f.axis == KVQ_AXIS_CHANNEL) return size_t(4) * d;
+  if (f.scale_fmt == KVQ_SCALE_U8_SUPER) return 4;
+  return 0;
+}
+
+kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
+  TensorKind k{CK_I8, MK_NONE, false};
+  if (f.scale_fmt != KVQ_SCALE_F32 && f.scale_fmt != KVQ_SCALE_F16 &&
+      f.scale_fmt != KVQ_SCALE_U8_SUPER)
+    return KVQ_ERR_INVALID_ARG;
+  if (f.axis != KVQ_AXIS_TOKEN && f.axis != KVQ_AXIS_CHANNEL) return KVQ_ERR_INVALID_ARG;
+  if (f.zero_point != 0 && f.zero_point != 1) return KVQ_ERR_INVALID_ARG;
+  if (f.bits == 16) {
+    if (f.axis != KVQ_AXIS_TOKEN || f.zero_point) return KVQ_ERR_INVALID_ARG;
+    k.code = CK_BF16;
+    k.meta = MK_NONE;
+    if (out) *out = k;
+    return KVQ_ERR_UNSUPPORTED;  // accounted for, not run by the kernels
+  }
+  if (f.bits != 8 && f.bits != 4 && f.bits != 2) return KVQ_ERR_INVALID_ARG;
+  if (f.scale_fmt == KVQ_SCALE_U8_SUPER && f.zero_point) return KVQ_ERR_INVALID_ARG;
+  if (f.axis == KVQ_AXIS_CHANNEL && (f.zero_point || f.scale_fmt != KVQ_SCALE_F32))
+    return KVQ_ERR_INVALID_ARG;
+  if (f.bits == 2) return KVQ_ERR_UNSUPPORTED;
+  const bool b8 = f.bits == 8;
+  k.code = f.zero_point ? (b8 ? CK_U8 : CK_U4) : (b8 ? CK_I8 : CK_I4);
+  if (f.axis == KVQ_AXIS_CHANNEL) {
+    k.channel = true;
+    k.meta = MK_NONE;
+    if (out) *out = k;
+    return is_key ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
+  }
+  if (f.scale_fmt == KVQ_SCALE_U8_SUPER) {
+    k.meta = MK_U8;
+    if (out) *out = k;
+    return is_key ? KVQ_ERR_UNSUPPORTED : KVQ_OK;
+  }
+  if (f.scale_fmt == KVQ_SCALE_F32)
+    k.meta = f.zero_point ? MK_F32Z : MK_F32;
+  else
+    k.meta = f.zero_point ? MK_F16Z : MK_F16;
+  if (out) *out = k;
+  return KVQ_OK;
+}
+
+// Shape checks shared by accounting and compute.  kernels: also require what
+// the kernels run (D = 128, G in {1,2,4,8}, capacity multiple of 16, ...).
+static kvq_status check_config(const kvq_config* c, bool kernels) {
+  if (!c) return KVQ_ERR_INVALID_ARG;
+  if (c->num_layers < 1 || c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 ||
+      c->head_dim < 1 || c->max_tokens < 0 || c->window < 0 || c->block_tokens < 0)
+    return KVQ_ERR_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads) return KVQ_ERR_INVALID_ARG;
+  if (c->in_dtype != KVQ_DT_F32 && c->in_dtype != KVQ_DT_BF16) return KVQ_ERR_INVALID_ARG;
+  if (c->block_tokens && (c->num_blocks < 1 || c->max_blocks_per_seq < 1))
+    return KVQ_ERR_INVALID_ARG;
+  TensorKind kk, vk;
+  const kvq_status sk = classify(c->key, true, &kk);
+  const kvq_status sv = classify(c->value, false, &vk);
+  if (sk == KVQ_ERR_INVALID_ARG || sv == KVQ_ERR_INVALID_ARG) return KVQ_ERR_INVALID_ARG;
+  if ((c->head_dim * c->key.bits) % 8 || (c->head_dim * c->value.bits) % 8)
+    return KVQ_ERR_INVALID_ARG;
+  if (!kernels) return KVQ_OK;
+  if (sk != KVQ_OK || sv != KVQ_OK) return KVQ_ERR_UNSUPPORTED;
+  const int g = c->num_q_heads / c->num_kv_heads;
+  if (c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return KVQ_ERR_UNSUPPORTED;
+  if (c->max_tokens % 16) return KVQ_ERR_UNSUPPORTED;
+  if (c->block_tokens != 0 && c->block_tokens != 16) return KVQ_ERR_UNSUPPORTED;
+  if (c->window % 16 || c->window > 256) return KVQ_ERR_UNSUPPORTED;
+  if (c->window && (kk.channel || vk.meta == MK_U8)) return KVQ_ERR_UNSUPPORTED;
+  // The decode kernels are instantiated for these key/value pairs.
+  const bool ok =
+      (kk.code == CK_I8 && kk.meta == MK_F32 && vk.code == CK_I8 && vk.meta == MK_F32) ||
+      (kk.code == CK_U4 && kk.meta == MK_F16Z && vk.code == CK_U4 && vk.meta == MK_F16Z) ||
+      (kk.code == CK_I8 && kk.channel && vk.code == CK_I4 && vk.meta == MK_U8) ||
+      (kk.code == CK_I4 && kk.meta == MK_F32 && vk.code == CK_I4 && vk.meta == MK_F32) ||
+      (kk.code == CK_I8 && kk.meta == MK_F32 && vk.code == CK_I4 && vk.meta == MK_F32) ||
+      (kk.code == CK_U8 && kk.meta == MK_F16Z && vk.code == CK_U8 && vk.meta == MK_F16Z);
+  return ok ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
+}
+
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Quantized tokens per workgroup.  Aim at about two workgroups of four
+// waves per compute unit (256 CUs) over the whole batch.
+static int choose_split(const kvq_config* c, int max_seq_len) {
+  const long long nq = std::max(0, max_seq_len - c->window);
+  const long long pairs = (long long)c->batch * c->num_kv_heads;
+  const long long target = 512;
+  long long per = (nq * pairs + target - 1) / target;
+  per = (long long)round_up((size_t)std::max<long long>(per, 1), 128);
+  per = std::min<long long>(std::max<long long>(per, 256), 8192);
+  return (int)per;
+}
+
+struct Plan {
+  int split_tokens, n_split, nsp;
+  size_t o_bytes, ml_bytes, total;
+};
+
+static Plan make_plan(const kvq_config* c, int max_seq_len, int split_tokens) {
+  Plan p{};
+  p.split_tokens = split_tokens > 0 ? split_tokens : choose_split(c, max_seq_len);
+  const int nq = std::max(0, max_seq_len - c->window);
+  p.n_split = (nq + p.split_tokens - 1) / p.split_tokens;
+  p.nsp = p.n_split + (c->window > 0 ? 1 : 0);
+  const size_t rows = (size_t)c->batch * c->num_q_heads * p.nsp;
+  p.o_bytes = round_up(rows * c->head_dim * sizeof(float), 256);
+  p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
+  p.total = p.o_bytes + p.ml_bytes;
+  return p;
+}
+
+struct LayerSizes {  // bytes of one layer of each buffer
+  size_t k_codes, v_codes, k_meta, v_meta, k_win, v_win, k_chan, v_super;
+};
+
+static LayerSizes layer_sizes(const kvq_config* c) {
+  LayerSizes s{};
+  const size_t slots = c->block_tokens ? (size_t)c->num_blocks * c->num_kv_heads * c->block_tokens
+                                       : (size_t)c->batch * c->num_kv_heads * c->max_tokens;
+  s.k_codes = slots * row_bytes(c->key.bits, c->head_dim);
+  s.v_codes = slots * row_bytes(c->value.bits, c->head_dim);
+  s.k_meta = slots * meta_bytes(c->key);
+  s.v_meta = slots * meta_bytes(c->value);
+  const size_t heads = (size_t)c->batch * c->num_kv_heads;
+  s.k_win = s.v_win = heads * c->window * c->head_dim * 2;
+  s.k_chan = (c->key.bits != 16 && c->key.axis == KVQ_AXIS_CHANNEL) ? heads * c->head_dim * 4 : 0;
+  s.v_super = (c->value.bits != 16 && c->value.scale_fmt == KVQ_SCALE_U8_SUPER) ? heads * 4 : 0;
+  return s;
+}
+
+static bool resolve_layer(const kvq_config* c, const kvq_cache* cache, int layer,
+                          const LayerSizes& s, uint8_t** kc, uint8_t** vc, uint8_t** km,
+                          uint8_t** vm, uint16_t** kw, uint16_t** vw, float** kch, float** vsu) {
+  const size_t L = (size_t)layer;
+  auto at = [&](void* base, size_t per) -> uint8_t* {
+    return base ? (uint8_t*)base + L * per : nullptr;
+  };
+  *kc = at(cache->k_codes, s.k_codes);
+  *vc = at(cache->v_codes, s.v_codes);
+  *km = at(cache->k_meta, s.k_meta);
+  *vm = at(cache->v_meta, s.v_meta);
+  *kw = (uint16_t*)at(cache->k_win, s.k_win);
+  *vw = (uint16_t*)at(cache->v_win, s.v_win);
+  *kch = (float*)at(cache->k_chan_scale, s.k_chan);
+  *vsu = (float*)at(cache->v_super, s.v_super);
+  if (!*kc || !*vc) return false;
+  if (s.k_meta && !*km) return false;
+  if (s.v_meta && !*vm) return false;
+  if (s.k_win && (!*kw || !*vw)) return false;
+  if (s.k_chan && !*kch) return false;
+  if (s.v_super && !*vsu) return false;
+  if (!cache->seq_lens) return false;
+  if (c->block_tokens && !cache->block_table) return false;
+  return true;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARG: return "KVQ_ERR_INVALID_ARG";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP";
+  }
+  return "KVQ_ERR_UNKNOWN";
+}
+
+kvq_status kvq_validate(const kvq_config* cfg) { return check_config(cfg, true); }
+
+kvq_status kvq_get_buffer_sizes(const kvq_config* cfg, kvq_buffer_sizes* out) {
+  const kvq_status st = check_config(cfg, false);
+  if (st != KVQ_OK) return st;
+  if (!out) return KVQ_ERR_INVALID_ARG;
+  const LayerSizes s = layer_sizes(cfg);
+  const size_t L = (size_t)cfg->num_layers;
+  out->k_codes = L * s.k_codes;
+  out->v_codes = L * s.v_codes;
+  out->k_meta = L * s.k_meta;
+  out->v_meta = L * s.v_meta;
+  out->k_win = L * s.k_win;
+  out->v_win = L * s.v_win;
+  out->k_chan_scale = L * s.k_chan;
+  out->v_super = L * s.v_super;
+  return KVQ_OK;
+}
+
+size_t kvq_cache_bytes(const kvq_config* cfg, const int32_t* host_seq_lens, kvq_bytes* out) {
+  if (check_config(cfg, false) != KVQ_OK) {
+    if (out) *out = kvq_bytes{};
+    return 0;
+  }
+  const size_t D = cfg->head_dim, H = cfg->num_kv_heads, L = cfg->num_layers;
+  const size_t rk = row_bytes(cfg->key.bits, cfg->head_dim);
+  const size_t rv = row_bytes(cfg->value.bits, cfg->head_dim);
+  const size_t mk = meta_bytes(cfg->key), mv = meta_bytes(cfg->value);
+  const size_t per_tok = rk + rv + mk + mv;
+  const size_t side = side_bytes(cfg->key, cfg->head_dim) + side_bytes(cfg->value, cfg->head_dim);
+  kvq_bytes b{};
+  for (int i = 0; i < cfg->batch; ++i) {
+    const size_t n = host_seq_lens ? (size_t)std::max(0, host_seq_lens[i]) : (size_t)cfg->max_tokens;
+    const size_t nw = std::min<size_t>(cfg->window, n);
+    const size_t nq = n - nw;
+    b.payload += L * H * nq * (rk + rv);  // 2 L H_kv D T b with per-tensor b
+    b.metadata += L * H * (nq * (mk + mv) + side);
+    b.window += L * H * nw * D * 2 * 2;
+    size_t alloc_q;
+    if (cfg->block_tokens)
+      alloc_q = (nq + cfg->block_tokens - 1) / cfg->block_tokens * cfg->block_tokens;
+    else
+      alloc_q = std::max<size_t>((size_t)cfg->max_tokens, nq);
+    b.padding += L * H * (alloc_q - nq) * per_tok;
+    if (cfg->window && !cfg->block_tokens) b.padding += L * H * (cfg->window - nw) * D * 2 * 2;
+  }
+  b.total = b.payload + b.metadata + b.window + b.padding;
+  if (out) *out = b;
+  return b.total;
+}
+
+size_t kvq_decode_traffic_bytes(const kvq_config* cfg, const int32_t* host_seq_lens) {
+  if (check_config(cfg, false) != KVQ_OK) return 0;
+  kvq_config one = *cfg;
+  one.num_layers = 1;
+  kvq_bytes b{};
+  kvq_cache_bytes(&one, host_seq_lens, &b);
+  return b.payload + b.metadata + b.window;
+}
+
+static bool split_ok(int split) { return split >= 0 && split % 128 == 0 && split <= (1 << 20); }
+
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int max_seq_len,
+                                  const kvq_decode_opts* opts) {
+  const int split = opts ? opts->split_tokens : 0;
+  if (check_config(cfg, true) != KVQ_OK || max_seq_len < 0 || !split_ok(split)) return 0;
+  return make_plan(cfg, max_seq_len, split).total;
+}
+
+kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                               const void* k_new, const void* v_new, int n_new,
+                               const int32_t* new_lens, void* stream) {
+  kvq_status st = check_config(cfg, true);
+  if (st != KVQ_OK) return st;
+  if (!cache || layer < 0 || layer >= cfg->num_layers || n_new < 0) return KVQ_ERR_INVALID_ARG;
+  if (n_new == 0) return KVQ_OK;
+  if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+  AppendArgs a{};
+  const LayerSizes s = layer_sizes(cfg);
+  if (!resolve_layer(cfg, cache, layer, s, &a.k_codes, &a.v_codes, &a.k_meta, &a.v_meta,
+                     &a.k_win, &a.v_win, &a.k_chan, &a.v_super))
+    return KVQ_ERR_INVALID_ARG;
+  classify(cfg->key, true, &a.kk);
+  classify(cfg->value, false, &a.vk);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_lens = new_lens;
+  a.seq_lens = cache->seq_lens;
+  a.block_table = cache->block_table;
+  a.batch = cfg->batch;
+  a.hkv = cfg->num_kv_heads;
+  a.n_new = n_new;
+  a.max_tokens = cfg->max_tokens;
+  a.window = cfg->window;
+  a.paged = cfg->block_tokens ? 1 : 0;
+  a.num_blocks = cfg->num_blocks;
+  a.bt_stride = cfg->max_blocks_per_seq;
+  a.in_bf16 = cfg->in_dtype == KVQ_DT_BF16;
+  return launch_append(a, stream);
+}
+
+kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                              const void* q, float* out, void* workspace,
+                              size_t workspace_bytes, int max_seq_len,
+                              const kvq_decode_opts* opts, void* stream) {
+  kvq_status st = check_config(cfg, true);
+  if (st != KVQ_OK) return st;
+  if (!cache || !q || !out || layer < 0 || layer >= cfg->num_layers || max_seq_len < 0)
+    return KVQ_ERR_INVALID_ARG;
+  const int split = opts ? opts->split_tokens : 0;
+  if (!split_ok(split)) return KVQ_ERR_INVALID_ARG;
+  const Plan p = make_plan(cfg, max_seq_len, split);
+  if (p.nsp > 0 && (!workspace || workspace_bytes < p.total)) return KVQ_ERR_WORKSPACE;
+  if (workspace && ((uintptr_t)workspace & 255)) return KVQ_ERR_WORKSPACE;
+  DecodeArgs a{};
+  const LayerSizes s = layer_sizes(cfg);
+  uint8_t *kc, *vc, *km, *vm;
+  uint16_t *kw, *vw;
+  float *kch, *vsu;
+  if (!resolve_layer(cfg, cache, layer, s, &kc, &vc, &km, &vm, &kw, &vw, &kch, &vsu))
+    return KVQ_ERR_INVALID_ARG;
+  a.k_codes = kc;
+  a.v_codes = vc;
+  a.k_meta = km;
+  a.v_meta = vm;
+  a.k_win = kw;
+  a.v_win = vw;
+  a.k_chan = kch;
+  a.v_super = vsu;
+  a.block_table = cache->block_table;
+  a.seq_lens = cache->seq_lens;
+  a.q = q;
+  a.out = out;
+  a.part_o = (float*)workspace;
+  a.part_ml = workspace ? (float*)((uint8_t*)workspace + p.o_bytes) : nullptr;
+  a.batch = cfg->batch;
+  a.hq = cfg->num_q_heads;
+  a.hkv = cfg->num_kv_heads;
+  a.group = cfg->num_q_heads / cfg->num_kv_heads;
+  a.max_tokens = cfg->max_tokens;
+  a.paged = cfg->block_tokens ? 1 : 0;
+  a.num_blocks = cfg->num_blocks;
+  a.bt_stride = cfg->max_blocks_per_seq;
+  a.window = cfg->window;
+  a.split_tokens = p.split_tokens;
+  a.n_split = p.n_split;
+  a.nsp = p.nsp;
+  a.in_bf16 = cfg->in_dtype == KVQ_DT_BF16;
+  classify(cfg->key, true, &a.kk);
+  classify(cfg->value, false, &a.vk);
+  return launch_decode(a, stream);
+}
+
+kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                           const void* q, float* out, void* workspace, size_t workspace_bytes,
+                           int max_seq_len, void* stream) {
+  return kvq_decode_attn_ex(cfg, cache, layer, q, out, workspace, workspace_bytes, max_seq_len,
+                            nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Internal declarations shared by the host code and the HIP kernels of libkvq.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// How the codes of one tensor are stored.
+enum CodeKind : int {
+  CK_I8 = 0,   // signed int8, two's complement
+  CK_U8 = 1,   // unsigned int8 (zero-point formats)
+  CK_I4 = 2,   // signed int4 nibbles, two per byte
+  CK_U4 = 3,   // unsigned int4 nibbles (zero-point formats)
+  CK_BF16 = 4  // unquantized bf16 values
+};
+
+// What is stored per token beside the codes.
+enum MetaKind : int {
+  MK_NONE = 0,  // nothing per token (per-channel scales, or bf16 values)
+  MK_F32 = 1,   // fp32 scale
+  MK_F32Z = 2,  // fp32 scale, fp32 zero point
+  MK_F16 = 3,   // fp16 scale
+  MK_F16Z = 4,  // fp16 scale (low half), fp16 zero point (high half)
+  MK_U8 = 5     // u8 scale code relative to a per-head fp32 super-scale
+};
+
+struct TensorKind {
+  CodeKind code;
+  MetaKind meta;
+  bool channel;   // per-channel scales (keys only)
+};
+
+// Code bytes of one token row of one head (0 for unsupported widths).
+inline int row_bytes(int bits, int d) { return d * bits / 8; }
+
+int meta_bytes(const kvq_tensor_fmt& f);
+
+// Classifies a format; returns KVQ_OK, KVQ_ERR_INVALID_ARG or
+// KVQ_ERR_UNSUPPORTED (for the kernels).  is_key: keys accept channel axis.
+kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out);
+
+// Everything a quantize-append launch needs, resolved to one layer.
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* new_lens;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  uint8_t* k_meta;
+  uint8_t* v_meta;
+  uint16_t* k_win;
+  uint16_t* v_win;
+  float* k_chan;
+  float* v_super;
+  int batch, hkv, n_new, max_tokens, window, paged, num_blocks, bt_stride;
+  int in_bf16;
+  TensorKind kk, vk;
+};
+
+// Everything a decode launch needs, resolved to one layer.
+struct DecodeArgs {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint8_t* k_meta;
+  const uint8_t* v_meta;
+  const uint16_t* k_win;
+  const uint16_t* v_win;
+  const float* k_chan;
+  const float* v_super;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const void* q;
+  float* out;
+  float* part_o;   // [B][Hq][nsp][D]
+  float* part_ml;  // [B][Hq][nsp][2]
+  int batch, hq, hkv, group;
+  int max_tokens, paged, num_blocks, bt_stride, window;
+  int split_tokens;  // quantized tokens per workgroup (multiple of 128)
+  int n_split;       // workgroups over the quantized tokens
+  int nsp;           // n_split + 1 if there is a window
+  int in_bf16;
+  TensorKind kk, vk;
+};
+
+kvq_status launch_append(const AppendArgs& a, void* stream);
+kvq_status launch_decode(const DecodeArgs& a, void* stream);
+
+}  // namespace kvq

@@ -167,3 +167,40 @@ def block_table(wl: dict, lens: List[int], replica: int = 0):
         table[b, :nb] = perm[off:off + nb]
         off += nb
     return table, pool
+
+
+def kv_device(wl: dict, lens: List[int], replica: int = 0, device: str = "cuda"):
+    """Keys and values of every sequence drawn on the device (for the full-size
+    workloads, where drawing on the host takes minutes).
+
+    Same recipe as ``kv_tokens`` (N(0,1) or Laplace(0,1), outlier key channels
+    x10, rounded to the input dtype) but drawn by torch's Philox generator on
+    the device, seeded from the workload and replica; positions past a
+    sequence's length are zero.  Returns (K, V) [B, H_kv, max(lens), D] in the
+    input dtype.  The values differ from ``kv_tokens``'s; tests that compare
+    with the oracle copy the slices they need back to the host.
+    """
+    import torch
+    B, H, D = wl["batch"], wl["hkv"], wl["d"]
+    T = max(lens) if lens else 0
+    dt = torch.bfloat16 if wl["in_dtype"] == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(np.random.SeedSequence([1000 + wl["id"], replica, 5]).generate_state(1)[0]))
+    k = torch.empty((B, H, T, D), dtype=dt, device=device)
+    v = torch.empty((B, H, T, D), dtype=dt, device=device)
+    for b in range(B):                    # one sequence at a time bounds the fp32 temporaries
+        kb = torch.randn((H, T, D), generator=gen, device=device, dtype=torch.float32)
+        for h in range(H):
+            ch = torch.from_numpy(outlier_channels(wl, h)).to(device)
+            if ch.numel():
+                kb[h, :, ch] *= 10.0
+        if wl["value_dist"] == "laplace":
+            u = torch.rand((H, T, D), generator=gen, device=device, dtype=torch.float32) - 0.5
+            vb = -torch.sign(u) * torch.log1p(-2.0 * u.abs())
+        else:
+            vb = torch.randn((H, T, D), generator=gen, device=device, dtype=torch.float32)
+        kb[:, lens[b]:] = 0
+        vb[:, lens[b]:] = 0
+        k[b] = kb.to(dt)
+        v[b] = vb.to(dt)
+    return k, v

@@ -1,0 +1,259 @@
+/*
+ * kvq.h - single-query decode attention over a low-bit KV cache (libkvq).
+ *
+ * C ABI of the library.  Plain pointers and sizes only.  Every compute call is
+ * asynchronous on the caller's HIP stream; the library never allocates,
+ * frees or synchronizes, and keeps no global state (calls are thread-safe as
+ * long as calls that write the same buffers are ordered by their streams).
+ *
+ * Pages this follows (cited by title and section):
+ *  [P1] "KV Cache Quantization Perturbs Attention Through Stored Keys and
+ *       Values" (nalar.dev)
+ *  [P2] "KV cache quantization reduces cache bytes with separate accuracy and
+ *       kernel costs" (nalar.dev)
+ *  [P3] "KV Cache Quantization and Per-Token Scale Placement" (mercemay.com)
+ *
+ * What the library computes:
+ *  - kvq_quantize_append: each new key and value vector is quantized when it
+ *    is written, q = clamp(round(x / s)) with reconstruction x_hat = q * s
+ *    (P2, "Quantization needs a scale convention"), with a scale computed from
+ *    the vector itself and stored beside it (P3, "Per-token scales and where
+ *    they can live").  Variants: an integer zero point (P1, "Quantization
+ *    granularity defines which values share a scale"); per-channel key scales
+ *    fixed by the first append (P3, "Per-token scales and where they can
+ *    live"); an 8-bit scale code relative to a per-head fp32 super-scale
+ *    (same section); the newest tokens kept in bf16 (P1, "Cache growth changes
+ *    the serving trade"); 16-token blocks placed through a block table (P2,
+ *    "Metadata and block layout remain part of physical memory use").
+ *  - kvq_decode_attn: s_i = q . k_hat_i / sqrt(D), a = softmax(s),
+ *    o = sum_i a_i v_hat_i over every cached token (P1, "Key error acts before
+ *    the softmax"; P2, "Keys and values need not have identical error
+ *    sensitivity"), with the per-token key scale applied once to each score
+ *    after the dot product over the integer-valued codes and the per-channel
+ *    key scale moved onto the query (P3, "The axis choice is a kernel
+ *    decision").
+ *  - kvq_cache_bytes: KV_bytes = 2 L H_kv D T b plus metadata, window and
+ *    padding (P2, "Cache precision is separate from weight precision" and
+ *    "Metadata and block layout remain part of physical memory use").
+ *
+ * Rounding contract of the write side (codes and metadata are bit-exact
+ * against a reference that follows it):
+ *  - codes are rint() (ties to even, as the quantizer listing of P3 "The axis
+ *    choice is a kernel decision" rounds with Python's round()) of the IEEE
+ *    fp64 quotient x / s_stored, then clamped to [-(2^(b-1)-1), 2^(b-1)-1]
+ *    (symmetric) or [0, 2^b-1] (zero point; rint(x/s) + z, then clamp);
+ *  - a scale is evaluated in fp64 and rounded once (ties to even) to its
+ *    storage type: s = amax/qmax (symmetric), s = (hi-lo)/(2^b-1) with
+ *    lo = min(min x, 0), hi = max(max x, 0) and z = clamp(rint(-lo/s))
+ *    (zero point); an all-zero vector stores s = 1 (and z = 0) and codes 0;
+ *    a scale that rounds to 0 stores the type's smallest positive value, an
+ *    fp16 scale above 65504 stores 65504;
+ *  - per-channel key scales: RN32(absmax over the first append / qmax) per
+ *    feature, frozen; later tokens clamp;
+ *  - super-scaled values: sigma_t = fl64(amax_t/qmax); per head
+ *    S = RN32(max_t sigma_t / 255) over the first append, frozen;
+ *    u_t = clamp(rint(fl64(sigma_t / S)), 1, 255) (0 for an all-zero vector);
+ *    codes use the exact effective scale u_t * S.
+ *
+ * Device memory layout (all buffers caller-allocated; sizes from
+ * kvq_buffer_sizes; "row" = D * bits / 8 code bytes of one token and head):
+ *  contiguous (block_tokens == 0):
+ *    codes  [L][B][H_kv][max_tokens][row]
+ *    meta   [L][B][H_kv][max_tokens] of the meta element below
+ *  paged (block_tokens == 16):
+ *    codes  [L][num_blocks][H_kv][16][row]
+ *    meta   [L][num_blocks][H_kv][16]
+ *    quantized position p of sequence b lives in block
+ *    block_table[b][p / 16], slot p % 16
+ *  window  [L][B][H_kv][window][D] bf16; position p sits in slot p % window
+ *  k_chan_scale [L][B][H_kv][D] fp32;  v_super [L][B][H_kv] fp32
+ *  code bytes: int8 codes as two's complement bytes (unsigned bytes with a
+ *    zero point); int4 codes packed two per byte, element 2j in the low nibble
+ *    and 2j+1 in the high nibble (two's complement nibbles, or unsigned with a
+ *    zero point)
+ *  meta element per token: f32 scale (4 B); f32 scale + f32 zero point
+ *    (8 B); f16 scale (2 B); f16 scale + f16 zero point (4 B, scale in the
+ *    low half); u8 scale code (1 B)
+ *  With a window, positions [0, len - min(window, len)) are quantized and
+ *  the newest min(window, len) positions are kept as bf16 in the ring.
+ *
+ * Error behaviour: every call validates its arguments on the host before
+ * launching anything and returns a kvq_status; nothing is thrown across the
+ * ABI.  Launch failures return KVQ_ERR_HIP; faults inside kernels surface at
+ * the caller's next synchronization.  Device-resident values the host cannot
+ * see are clamped, never trusted: a sequence length beyond the cache's
+ * capacity is clamped to it, a block-table entry outside [0, num_blocks) is
+ * clamped into it, and a sequence longer than the max_seq_len a decode call
+ * was planned for gets NaN outputs.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent sizes */
+  KVQ_ERR_UNSUPPORTED = 2, /* a valid format or shape the kernels do not run */
+  KVQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  KVQ_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} kvq_status;
+
+/* Which values share a scale (P1, "Quantization granularity defines which
+ * values share a scale"; P3, "Per-token scales and where they can live"). */
+typedef enum {
+  KVQ_AXIS_TOKEN = 0,  /* one scale per token per head */
+  KVQ_AXIS_CHANNEL = 1 /* one scale per feature per head (keys only) */
+} kvq_axis;
+
+/* Storage type of a per-token scale (and zero point). */
+typedef enum {
+  KVQ_SCALE_F32 = 0,
+  KVQ_SCALE_F16 = 1,
+  KVQ_SCALE_U8_SUPER = 2 /* u8 code times a per-head fp32 super-scale */
+} kvq_scale_fmt;
+
+typedef enum { KVQ_DT_F32 = 0, KVQ_DT_BF16 = 1 } kvq_dtype;
+
+/* How one of K or V is stored (P1, "Quantization granularity defines which
+ * values share a scale": bit width, grouping, scale precision and the key /
+ * value treatment together define a format). */
+typedef struct {
+  int bits;                /* 8 or 4; 16 = bf16 kept unquantized; 2 is
+                              accepted by kvq_cache_bytes only */
+  kvq_axis axis;
+  int zero_point;          /* 1: unsigned codes with an integer zero point */
+  kvq_scale_fmt scale_fmt;
+} kvq_tensor_fmt;
+
+/* Shape and format of a cache (P2, "Cache precision is separate from weight
+ * precision": layers, KV heads, head dimension, retained length, bytes per
+ * element). */
+typedef struct {
+  int num_layers;
+  int batch;
+  int num_q_heads;
+  int num_kv_heads;
+  int head_dim;            /* D; the kernels run D = 128 */
+  int max_tokens;          /* capacity per sequence, a multiple of 16 */
+  kvq_tensor_fmt key;
+  kvq_tensor_fmt value;
+  int window;              /* newest tokens kept bf16 (0 = none, else a
+                              multiple of 16, at most 256) */
+  int block_tokens;        /* 0 = contiguous, 16 = paged */
+  int num_blocks;          /* paged: blocks per layer in the pool */
+  int max_blocks_per_seq;  /* paged: columns of block_table */
+  kvq_dtype in_dtype;      /* dtype of k_new, v_new and q */
+} kvq_config;
+
+/* Device pointers of one cache (all layers).  Unused buffers may be NULL. */
+typedef struct {
+  void* k_codes;
+  void* v_codes;
+  void* k_meta;
+  void* v_meta;
+  void* k_win;             /* bf16 window ring of keys */
+  void* v_win;
+  void* k_chan_scale;      /* per-channel key scales */
+  void* v_super;           /* per-head value super-scales */
+  const int32_t* block_table; /* [batch][max_blocks_per_seq], paged only */
+  const int32_t* seq_lens; /* [batch]: tokens of each sequence, counting the
+                              tokens of the current append; the library only
+                              reads it */
+} kvq_cache;
+
+/* Byte breakdown of a cache (P2, "Metadata and block layout remain part of
+ * physical memory use"). */
+typedef struct {
+  size_t payload;   /* code bytes of the quantized tokens: L H_kv D T (bK+bV)/8 */
+  size_t metadata;  /* per-token scales / zero points / scale codes and
+                       per-head channel scales or super-scales */
+  size_t window;    /* bf16 recent tokens of K and V */
+  size_t padding;   /* allocated but unused slots */
+  size_t total;
+} kvq_bytes;
+
+/* Bytes to allocate for each buffer of kvq_cache (0 = not used). */
+typedef struct {
+  size_t k_codes, v_codes, k_meta, v_meta, k_win, v_win, k_chan_scale, v_super;
+} kvq_buffer_sizes;
+
+/* Human-readable name of a status.  Never NULL. */
+const char* kvq_status_string(kvq_status s);
+
+/* Checks that cfg describes a cache the kernels run: KVQ_OK,
+ * KVQ_ERR_INVALID_ARG or KVQ_ERR_UNSUPPORTED. */
+kvq_status kvq_validate(const kvq_config* cfg);
+
+/* Fills *out with the byte size of each buffer of the layout above. */
+kvq_status kvq_get_buffer_sizes(const kvq_config* cfg, kvq_buffer_sizes* out);
+
+/* Byte accounting of P2 "Cache precision is separate from weight precision"
+ * (payload 2 L H_kv D T b, generalised to separate key and value widths) plus
+ * metadata (P3, "Per-token scales and where they can live"), window and
+ * padding.  host_seq_lens: [batch] host array, or NULL for max_tokens each.
+ * Pure host arithmetic; accepts bits 2 as well.  Returns the total (0 on an
+ * invalid configuration) and fills *out when out is not NULL. */
+size_t kvq_cache_bytes(const kvq_config* cfg, const int32_t* host_seq_lens, kvq_bytes* out);
+
+/* Bytes one decode step reads from the cache of one layer: codes, per-token
+ * metadata, window values and per-head side data, without padding. */
+size_t kvq_decode_traffic_bytes(const kvq_config* cfg, const int32_t* host_seq_lens);
+
+
+/* Quantizes and stores new tokens of one layer (P3, "Per-token scales and
+ * where they can live": scale from the vector itself at write time).
+ *  k_new, v_new: device [batch][num_kv_heads][n_new][head_dim] in in_dtype.
+ *  new_lens:     device [batch] int32, tokens of sequence b taken from the
+ *                first new_lens[b] rows (each <= n_new), or NULL for n_new.
+ *  The tokens of sequence b take positions
+ *  [seq_lens[b] - new_lens[b], seq_lens[b]): cache->seq_lens already counts
+ *  them.  A sequence whose first position is 0 fixes its per-channel key
+ *  scales and value super-scale from these tokens.
+ *  stream: a hipStream_t (NULL = the null stream). */
+kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                               const void* k_new, const void* v_new, int n_new,
+                               const int32_t* new_lens, void* stream);
+
+/* Tuning knobs of kvq_decode_attn; zero fields take the library's choice. */
+typedef struct {
+  int split_tokens; /* quantized tokens per workgroup, a multiple of 128 */
+} kvq_decode_opts;
+
+/* Single-query decode attention of one layer over every cached token (P2,
+ * "Keys and values need not have identical error sensitivity").
+ *  q:   device [batch][num_q_heads][head_dim] in in_dtype; query head h reads
+ *       KV head h / (num_q_heads / num_kv_heads).
+ *  out: device [batch][num_q_heads][head_dim] fp32.  A sequence with no
+ *       tokens gets zeros.
+ *  workspace: device scratch of at least
+ *       kvq_decode_workspace_bytes(cfg, max_seq_len) bytes, 256-byte aligned.
+ *  max_seq_len: host upper bound of seq_lens (plans the split of the tokens
+ *       over workgroups).
+ *  Launches a split kernel and a log-sum-exp combine kernel on stream. */
+kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                           const void* q, float* out, void* workspace, size_t workspace_bytes,
+                           int max_seq_len, void* stream);
+
+/* Workspace bytes kvq_decode_attn (opts == NULL) or kvq_decode_attn_ex
+ * (same opts) needs for sequences of at most max_seq_len tokens; 0 on an
+ * invalid configuration or option. */
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int max_seq_len,
+                                  const kvq_decode_opts* opts);
+
+/* kvq_decode_attn with tuning knobs (opts may be NULL). */
+kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                              const void* q, float* out, void* workspace,
+                              size_t workspace_bytes, int max_seq_len,
+                              const kvq_decode_opts* opts, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

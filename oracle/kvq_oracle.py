@@ -49,7 +49,10 @@ Readings where the pages leave a step open (each restated where it is used):
       u = clamp(rint(fl64(sigma / S)), 1, 255) (0 for an all-zero vector);
       the effective scale is the exact product u*S.
   R11 with a recent window of W tokens, exactly the min(W, n) newest tokens
-      are kept unquantized (bf16); older tokens are quantized per token.
+      are kept unquantized, stored in bf16 (fp32 inputs are rounded to bf16,
+      ties to even); older tokens are quantized per token.  A token is
+      quantized from its input value, or from its bf16 window copy when it
+      leaves the window in a later append.
   R13 the output is fp32 on the device; here fp64.
   Scale underflow: a scale that rounds to 0 in its storage type is replaced by
   that type's smallest positive value (fp32 2^-149, fp16 2^-24); an fp16 scale
@@ -100,6 +103,15 @@ class TensorFormat:
     axis: str = "token"
     zero_point: bool = False
     scale: str = "f32"
+
+
+def round_bf16(x) -> np.ndarray:
+    """Values as stored in bf16 (round to nearest, ties to even); finite input.
+    Tokens kept unquantized (bits 16, or the recent window) are stored in bf16."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def qmax_symmetric(bits: int) -> int:
@@ -179,7 +191,7 @@ def quantize_asym(x, bits: int, scale: str = "f16"):
     s = round_to_storage(np.where(flat, 1.0, (hi - lo) / qmax), scale)
     s = np.where(flat, np.asarray(1.0, s.dtype), s).astype(s.dtype)
     z = np.clip(rne_quotient(-lo, s), 0, qmax)
-    z = np.where(flat, 0.0, z)
+    z = np.where(flat | (z == 0), 0.0, z)      # a zero point of 0 is stored as +0
     codes = np.clip(rne_quotient(x, s[..., None]) + z[..., None], 0, qmax)
     return codes.astype(np.int32), s, z.astype(s.dtype)
 
@@ -366,7 +378,7 @@ class OracleCache:
         if n == 0:
             return
         if fmt.bits == 16:
-            side.raw = np.concatenate([side.raw, x], axis=1)
+            side.raw = np.concatenate([side.raw, round_bf16(x)], axis=1)
             return
         if fmt.axis == "channel":
             if first:
@@ -400,7 +412,7 @@ class OracleCache:
                 keep = min(self.window, total)
                 leave = pool.shape[1] - keep
                 self._quantize_into(self.side[b][t], self.fmt[t], pool[:, :leave], first)
-                self.win[b][t] = pool[:, leave:]
+                self.win[b][t] = round_bf16(pool[:, leave:])
             else:
                 self._quantize_into(self.side[b][t], self.fmt[t], x, first)
         self.lens[b] = total

@@ -1,0 +1,226 @@
+"""Helpers of the GPU parity tests: build the same cache on the device (through
+the C ABI) and in the oracle from the same seeded inputs, read the device
+buffers back in the documented layout, and compare.
+
+The unpacking below restates the memory layout that include/kvq.h documents;
+it is test code, not a second implementation of the method.
+"""
+from __future__ import annotations
+
+import math
+import sys
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from decode_attention_quantized_kvq_amd import kvq as K
+from decode_attention_quantized_kvq_amd import synth
+from oracle import kvq_oracle as O
+
+ATOL = 2e-3      # max |gpu - oracle| allowed by the acceptance bar
+RTOL_F = 1e-2    # ||gpu - oracle||_F / ||oracle||_F allowed
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_fmt(spec):
+    return O.TensorFormat(spec["bits"], spec.get("axis", "token"), bool(spec.get("zero_point")),
+                          spec.get("scale", "f32"))
+
+
+def to_device(x_f32: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Values exact in dtype (float32 array) -> device tensor of that dtype."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x_f32, np.float32)).to(device)
+    bits = synth.bf16_bits(x_f32)
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+@dataclass
+class Built:
+    wl: dict
+    cfg: K.Config
+    cache: K.KvqCache
+    oracle: O.OracleCache
+    lens: List[int]
+    table: Optional[np.ndarray] = None
+    inputs: dict = field(default_factory=dict)
+
+
+def make_config(wl, lens, num_blocks=0, max_blocks=0):
+    return K.make_config(batch=wl["batch"], num_q_heads=wl["hq"], num_kv_heads=wl["hkv"],
+                         head_dim=wl["d"], max_tokens=wl["tokens"], key=wl["key"],
+                         value=wl["value"], window=wl["window"], block_tokens=wl["block_tokens"],
+                         num_blocks=num_blocks, max_blocks_per_seq=max_blocks,
+                         in_dtype=wl["in_dtype"])
+
+
+def build(wl: dict, lens: List[int], decode_steps: int = 0, replica: int = 0,
+          oracle: bool = True, chunks: int = 1) -> Built:
+    """Prefill each sequence with lens[b] - decode_steps tokens (split into
+    `chunks` appends of ragged sizes), then append decode_steps single tokens;
+    the device and the oracle see the same tokens in the same appends."""
+    B, H, D = wl["batch"], wl["hkv"], wl["d"]
+    table = None
+    nb = mb = 0
+    if wl["block_tokens"]:
+        table, pool = synth.block_table(wl, lens, replica)
+        nb, mb = max(pool, 1), table.shape[1]
+    cfg = make_config(wl, lens, nb, mb)
+    assert K.validate(cfg) == K.KVQ_OK
+    cache = K.KvqCache(cfg, "cuda", None if table is None else torch.from_numpy(table))
+    orc = O.OracleCache(B, H, D, oracle_fmt(wl["key"]), oracle_fmt(wl["value"]), wl["window"]) if oracle else None
+    full = {}
+    for b in range(B):
+        for h in range(H):
+            full[b, h] = synth.kv_tokens(wl, b, h, lens[b], replica)
+    pre = [max(n - decode_steps, 0) for n in lens]
+    # prefill, possibly in several ragged appends
+    bounds = [[(pre[b] * i) // chunks for i in range(chunks + 1)] for b in range(B)]
+    appends = []
+    for i in range(chunks):
+        appends.append([(bounds[b][i], bounds[b][i + 1]) for b in range(B)])
+    for s in range(decode_steps):
+        appends.append([(pre[b] + s, min(pre[b] + s + 1, lens[b])) for b in range(B)])
+    for ap in appends:
+        n_new = max(e - s for s, e in ap)
+        if n_new == 0:
+            continue
+        k = np.zeros((B, H, n_new, D), np.float32)
+        v = np.zeros((B, H, n_new, D), np.float32)
+        for b, (s, e) in enumerate(ap):
+            for h in range(H):
+                k[b, h, :e - s] = full[b, h][0][s:e]
+                v[b, h, :e - s] = full[b, h][1][s:e]
+            if orc is not None and e > s:
+                orc.append(b, k[b, :, :e - s], v[b, :, :e - s])
+        new_lens = torch.tensor([e - s for s, e in ap], dtype=torch.int32, device="cuda")
+        cache.seq_lens.copy_(torch.tensor([e for s, e in ap], dtype=torch.int32))
+        K.quantize_append(cache, 0, to_device(k, wl["in_dtype"]), to_device(v, wl["in_dtype"]),
+                          new_lens)
+    torch.cuda.synchronize()
+    return Built(wl, cfg, cache, orc, list(lens), table, {"kv": full})
+
+
+def queries(wl, step=0, replica=0):
+    return np.stack([synth.queries(wl, b, replica, step) for b in range(wl["batch"])])
+
+
+def run_decode(bt: Built, q: np.ndarray, split_tokens=0) -> np.ndarray:
+    qd = to_device(q, bt.wl["in_dtype"])
+    out = K.decode_attn(bt.cache, 0, qd, max(bt.lens) if bt.lens else 0, split_tokens=split_tokens)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def check_close(got: np.ndarray, want: np.ndarray, what: str, atol=ATOL, rtol_f=RTOL_F):
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    d = np.abs(got - want)
+    mx = float(d.max()) if d.size else 0.0
+    nref = float(np.linalg.norm(want))
+    rel = float(np.linalg.norm(got - want) / nref) if nref > 0 else float(np.linalg.norm(got))
+    log(f"  {what}: max|d|={mx:.3e} relF={rel:.3e}")
+    assert mx <= atol, f"{what}: max abs error {mx} > {atol}"
+    assert rel <= rtol_f, f"{what}: relative Frobenius error {rel} > {rtol_f}"
+    return mx, rel
+
+
+# ---------------------------------------------------------------------------
+# Reading device buffers back in the documented layout
+# ---------------------------------------------------------------------------
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def token_slots(bt: Built, b: int, h: int, n: int) -> np.ndarray:
+    """Slot index (in tokens) of quantized positions 0..n-1 of (b, h)."""
+    cfg = bt.cfg
+    p = np.arange(n)
+    if cfg.block_tokens:
+        phys = bt.table[b, p // 16].astype(np.int64)
+        return (phys * cfg.num_kv_heads + h) * 16 + p % 16
+    return (b * cfg.num_kv_heads + h) * cfg.max_tokens + p
+
+
+def unpack_codes(raw: np.ndarray, bits: int, signed: bool) -> np.ndarray:
+    """[..., row bytes] -> [..., D] integer codes."""
+    if bits == 8:
+        return raw.view(np.int8).astype(np.int32) if signed else raw.astype(np.int32)
+    lo = (raw & 0xF).astype(np.int32)
+    hi = (raw >> 4).astype(np.int32)
+    c = np.stack([lo, hi], axis=-1).reshape(*raw.shape[:-1], raw.shape[-1] * 2)
+    if signed:
+        c = np.where(c >= 8, c - 16, c)
+    return c
+
+
+def device_records(bt: Built, t: str, b: int, h: int, n: int) -> dict:
+    """Codes and metadata of the first n quantized positions of (b, h)."""
+    spec = bt.wl["key" if t == "k" else "value"]
+    bits, zp, scale = spec["bits"], bool(spec.get("zero_point")), spec.get("scale", "f32")
+    D = bt.wl["d"]
+    row = D * bits // 8
+    codes_buf = host(bt.cache.buffers[f"{t}_codes"]).reshape(-1, row)
+    slots = token_slots(bt, b, h, n)
+    out = {"codes": unpack_codes(codes_buf[slots], bits, not zp)}
+    if spec.get("axis") == "channel":
+        ch = host(bt.cache.buffers["k_chan_scale"]).view(np.float32).reshape(-1, D)
+        out["chan"] = ch[b * bt.cfg.num_kv_heads + h]
+        return out
+    meta = host(bt.cache.buffers[f"{t}_meta"])
+    if scale == "u8_super":
+        out["u"] = meta[slots]
+        out["S"] = host(bt.cache.buffers["v_super"]).view(np.float32)[b * bt.cfg.num_kv_heads + h]
+    elif scale == "f32" and not zp:
+        out["s"] = meta.view(np.float32)[slots]
+    elif scale == "f32":
+        m = meta.view(np.float32).reshape(-1, 2)[slots]
+        out["s"], out["z"] = m[:, 0], m[:, 1]
+    elif scale == "f16" and not zp:
+        out["s"] = meta.view(np.float16)[slots]
+    else:
+        m = meta.view(np.float16).reshape(-1, 2)[slots]
+        out["s"], out["z"] = m[:, 0], m[:, 1]
+    return out
+
+
+def window_values(bt: Built, t: str, b: int, h: int, nw: int) -> np.ndarray:
+    """bf16 window ring of (b, h) as float64, slots 0..nw-1."""
+    W, D = bt.wl["window"], bt.wl["d"]
+    ring = host(bt.cache.buffers[f"{t}_win"]).view(np.uint16).reshape(-1, W, D)
+    r = ring[b * bt.cfg.num_kv_heads + h][:nw]
+    return (r.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_records(bt: Built, b: int, h: int):
+    """Bit-exact codes and metadata of sequence b, KV head h."""
+    for t in ("k", "v"):
+        st = bt.oracle.stored(b, t)
+        n = st.codes.shape[1]
+        dev = device_records(bt, t, b, h, n)
+        assert np.array_equal(dev["codes"], st.codes[h]), f"{t} codes differ at b={b} h={h}"
+        if "chan" in dev:
+            assert np.array_equal(dev["chan"].view(np.uint32), st.chan[h].view(np.uint32))
+        if "u" in dev:
+            assert np.array_equal(dev["u"], st.u[h]), f"{t} scale codes differ"
+            assert dev["S"].view(np.uint32) == st.S[h].view(np.uint32)
+        if "s" in dev:
+            want = st.s[h]
+            assert dev["s"].dtype == want.dtype
+            assert np.array_equal(dev["s"].view(np.uint8), want.view(np.uint8)), f"{t} scales differ b={b} h={h}"
+        if "z" in dev:
+            assert np.array_equal(dev["z"].view(np.uint8), st.z[h].view(np.uint8)), f"{t} zero points differ"
+        if bt.wl["window"]:
+            # ring slots hold positions p with slot p % W; compare as a set of rows
+            wv = bt.oracle.window_values(b, t)[h]
+            nw = wv.shape[0]
+            n_tot = bt.oracle.lens[b]
+            pos = np.arange(n_tot - nw, n_tot)
+            ring = window_values(bt, t, b, h, bt.wl["window"])
+            assert np.array_equal(ring[pos % bt.wl["window"]], wv), f"{t} window differs b={b} h={h}"

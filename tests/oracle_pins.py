@@ -91,6 +91,12 @@ def _rng(seed):
     return np.random.default_rng(seed)
 
 
+def _bf16(x):
+    """Values exact in bf16, rounded by torch (a library routine, not the oracle)."""
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
 def _f32(x):
     return np.asarray(x, np.float32).astype(np.float64)
 
@@ -349,8 +355,8 @@ def pin_exact_cache(O):
     torch's scaled_dot_product_attention in fp64 to 1e-12."""
     rng = _rng(71)
     for (hq, hkv, t) in ((4, 1, 33), (8, 2, 200), (2, 2, 1), (6, 3, 7)):
-        k = rng.standard_normal((hkv, t, 32)) * 3
-        v = rng.standard_normal((hkv, t, 32))
+        k = _bf16(rng.standard_normal((hkv, t, 32)) * 3)
+        v = _bf16(rng.standard_normal((hkv, t, 32)))
         q = rng.standard_normal((hq, 32))
         cache = O.OracleCache(1, hkv, 32, O.TensorFormat(16), O.TensorFormat(16))
         cache.append(0, k, v)
@@ -493,8 +499,8 @@ def pin_window(O):
     rng = _rng(151)
     w = 8
     cache = O.OracleCache(1, 2, 128, O.TensorFormat(8), O.TensorFormat(8), window=w)
-    allk = _f32(rng.standard_normal((2, 30, 128)))
-    allv = _f32(rng.standard_normal((2, 30, 128)))
+    allk = _bf16(rng.standard_normal((2, 30, 128)))
+    allv = _bf16(rng.standard_normal((2, 30, 128)))
     cache.append(0, allk[:, :5], allv[:, :5])          # shorter than the window
     kh, vh = cache.reconstructed(0)
     assert np.array_equal(kh, allk[:, :5]) and np.array_equal(vh, allv[:, :5])
@@ -506,6 +512,26 @@ def pin_window(O):
     assert np.array_equal(kh[:, :30 - w], O.dequant_sym(ck, sk))
     assert np.array_equal(kh[:, 30 - w:], allk[:, 30 - w:])
     assert np.array_equal(cache.stored(0, "k").codes, ck)
+
+
+def pin_window_stores_bf16(O):
+    """Unquantized tokens (bits 16, or the recent window) are stored in bf16:
+    fp32 inputs come back rounded to nearest-even bf16 (torch's conversion)."""
+    rng = _rng(155)
+    x = _f32(rng.standard_normal((1, 6, 128)))
+    cache = O.OracleCache(1, 1, 128, O.TensorFormat(8), O.TensorFormat(8), window=16)
+    cache.append(0, x, x)
+    kh, _ = cache.reconstructed(0)
+    assert np.array_equal(kh, _bf16(x)) and not np.array_equal(kh, x)
+    c2 = O.OracleCache(1, 1, 128, O.TensorFormat(16), O.TensorFormat(16))
+    c2.append(0, x, x)
+    assert np.array_equal(c2.reconstructed(0)[1], _bf16(x))
+
+
+def pin_zero_point_positive_zero(O):
+    """A zero point of 0 is stored as +0 (its fp16 bits are 0x0000)."""
+    _, _, z = O.quantize_asym(np.array([[0.0, 1.0, 2.0], [0.0, 0.0, 0.0]]), 4, "f16")
+    assert z.view(np.uint16).tolist() == [0, 0]
 
 
 def pin_prefill_then_decode(O):

@@ -1,0 +1,169 @@
+"""GPU parity of libkvq against the CPU oracle, through the C ABI.
+
+Codes, scales, zero points, 8-bit scale codes, channel scales, super-scales
+and window values are compared bit for bit; attention outputs within the
+acceptance bar (max |d| <= 2e-3 and relative Frobenius error <= 1e-2 against
+the fp64 oracle on the same reconstructed cache).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+from decode_attention_quantized_kvq_amd import kvq as K
+from decode_attention_quantized_kvq_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def full_check(bt, steps=(0,), split_tokens=0, records=True):
+    wl = bt.wl
+    if records:
+        for b in range(wl["batch"]):
+            for h in range(wl["hkv"]):
+                H.check_records(bt, b, h)
+    errs = []
+    for step in steps:
+        q = H.queries(wl, step)
+        got = H.run_decode(bt, q, split_tokens)
+        want = np.stack([bt.oracle.attend(b, q[b]) for b in range(wl["batch"])])
+        errs.append(H.check_close(got, want, f"{wl['name']} step {step} split {split_tokens}"))
+    return errs
+
+
+def test_tiny_full_size():
+    """Workload 1 at its full size (batch 1, 1 head, 512 tokens, fp32 inputs)."""
+    H.log("case: workload 1 full size")
+    wl = synth.workload(1)
+    bt = H.build(wl, [512])
+    full_check(bt, steps=(0, 1, 2))
+
+
+@pytest.mark.parametrize("wid,over,lens,decode_steps,chunks", [
+    (2, dict(batch=2, tokens=1024), [1000, 777], 3, 1),
+    (3, dict(batch=2, tokens=1024), [1000, 651], 3, 2),
+    (4, dict(batch=3, tokens=1024), [1024, 300, 131], 5, 2),
+    (5, dict(batch=2, tokens=1024), [1000, 613], 4, 1),
+], ids=["w2", "w3", "w4", "w5"])
+def test_workload_reduced(wid, over, lens, decode_steps, chunks):
+    """Each workload's formats at a size the oracle finishes in seconds, with
+    ragged lengths, a prefill in one or two appends, then decode appends."""
+    H.log(f"case: workload {wid} reduced {over} lens={lens}")
+    wl = synth.workload(wid, **over)
+    bt = H.build(wl, lens, decode_steps=decode_steps, chunks=chunks)
+    full_check(bt, steps=(0, 1))
+    for split in (128, 384):
+        full_check(bt, steps=(0,), split_tokens=split, records=False)
+
+
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 300])
+@pytest.mark.parametrize("wid", [2, 3, 5])
+def test_tile_edges(wid, n):
+    """Lengths around the 16-token block and 32-token tile edges."""
+    H.log(f"case: tile edges workload {wid} n={n}")
+    wl = synth.workload(wid, batch=1, tokens=304)
+    bt = H.build(wl, [n])
+    full_check(bt, steps=(0,), split_tokens=128)
+
+
+@pytest.mark.parametrize("n", [1, 5, 16, 127, 128, 129, 150, 300])
+def test_window_edges(n):
+    """Paged cache with a bf16 window: lengths shorter than, equal to and
+    longer than the window; single-token appends move tokens out of it."""
+    H.log(f"case: window edges n={n}")
+    wl = synth.workload(4, batch=2, tokens=320)
+    bt = H.build(wl, [n, max(1, n // 2)], decode_steps=min(n, 3))
+    full_check(bt, steps=(0,))
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 8), (4, 2)])
+@pytest.mark.parametrize("fmt", ["i8", "u4z", "i4", "i8k_i4v", "u8z", "chan_super"])
+def test_formats_and_groups(fmt, hq, hkv):
+    """Every instantiated key/value format pair at every group size G."""
+    H.log(f"case: format {fmt} hq={hq} hkv={hkv}")
+    specs = {
+        "i8": (dict(bits=8), dict(bits=8)),
+        "u4z": (dict(bits=4, zero_point=True, scale="f16"), dict(bits=4, zero_point=True, scale="f16")),
+        "i4": (dict(bits=4), dict(bits=4)),
+        "i8k_i4v": (dict(bits=8), dict(bits=4)),
+        "u8z": (dict(bits=8, zero_point=True, scale="f16"), dict(bits=8, zero_point=True, scale="f16")),
+        "chan_super": (dict(bits=8, axis="channel"), dict(bits=4, scale="u8_super")),
+    }
+    k, v = specs[fmt]
+    wl = synth.workload(2, batch=2, hq=hq, hkv=hkv, tokens=512, key=k, value=v)
+    bt = H.build(wl, [500, 77], decode_steps=2)
+    full_check(bt, steps=(0,), split_tokens=128)
+
+
+def test_empty_and_zero_sequences():
+    """A sequence with no tokens gives zeros; all-zero vectors quantize to
+    codes 0 with scale 1 and attend like any other token."""
+    H.log("case: empty sequence")
+    wl = synth.workload(2, batch=3, tokens=256)
+    bt = H.build(wl, [200, 0, 37])
+    q = H.queries(wl)
+    got = H.run_decode(bt, q)
+    assert np.all(got[1] == 0.0)
+    want = np.stack([bt.oracle.attend(b, q[b]) for b in range(3)])
+    H.check_close(got, want, "empty sequence")
+    # all-zero tokens appended to sequence 2
+    z = torch.zeros((3, wl["hkv"], 4, 128), dtype=torch.bfloat16, device="cuda")
+    bt.cache.seq_lens.copy_(torch.tensor([200, 0, 41], dtype=torch.int32))
+    K.quantize_append(bt.cache, 0, z, z, torch.tensor([0, 0, 4], dtype=torch.int32, device="cuda"))
+    bt.oracle.append(2, np.zeros((wl["hkv"], 4, 128)), np.zeros((wl["hkv"], 4, 128)))
+    bt.lens[2] = 41
+    for h in range(wl["hkv"]):
+        H.check_records(bt, 2, h)
+    full_check(bt, steps=(1,), records=False)
+
+
+def test_overflowing_plan_gives_nan():
+    """A sequence longer than the max_seq_len a decode was planned for gets NaN
+    outputs (the documented error behaviour); the others are unaffected."""
+    H.log("case: overflowing plan")
+    wl = synth.workload(2, batch=2, tokens=1024)
+    bt = H.build(wl, [1000, 100])
+    q = H.queries(wl)
+    out = K.decode_attn(bt.cache, 0, H.to_device(q, "bf16"), 300, split_tokens=128)
+    got = out.cpu().numpy()
+    assert np.all(np.isnan(got[0]))
+    H.check_close(got[1].astype(np.float64), bt.oracle.attend(1, q[1]), "unaffected sequence")
+
+
+def test_paged_equals_contiguous():
+    """Paging changes placement only: the same tokens in a shuffled paged
+    layout and in a contiguous layout give bit-identical outputs."""
+    H.log("case: paged vs contiguous")
+    lens = [700, 333]
+    wl_p = synth.workload(4, batch=2, tokens=768, window=0)
+    wl_c = synth.workload(4, batch=2, tokens=768, window=0, block_tokens=0)
+    bp = H.build(wl_p, lens, oracle=False)
+    bc = H.build(wl_c, lens, oracle=False)
+    q = H.queries(wl_p)
+    a = H.run_decode(bp, q, 256)
+    b = H.run_decode(bc, q, 256)
+    assert np.array_equal(a, b)
+
+
+def test_multi_layer_isolation():
+    """Appends and decodes address their own layer only."""
+    H.log("case: layers")
+    wl = synth.workload(2, batch=1, tokens=256)
+    cfg = K.make_config(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, max_tokens=256,
+                        key=wl["key"], value=wl["value"], num_layers=3)
+    cache = K.KvqCache(cfg)
+    ks = []
+    for layer in range(3):
+        k, v = synth.kv_tokens(wl, 0, 0, 100, replica=layer)
+        kk = np.broadcast_to(k, (1, 8, 100, 128)).copy()
+        vv = np.broadcast_to(v, (1, 8, 100, 128)).copy()
+        ks.append((kk, vv))
+        cache.seq_lens.fill_(100)
+        K.quantize_append(cache, layer, H.to_device(kk, "bf16"), H.to_device(vv, "bf16"))
+    q = H.queries(wl)
+    from oracle import kvq_oracle as O
+    for layer in range(3):
+        out = K.decode_attn(cache, layer, H.to_device(q, "bf16"), 100).cpu().numpy()
+        oc = O.OracleCache(1, 8, 128, O.TensorFormat(8), O.TensorFormat(8))
+        oc.append(0, ks[layer][0][0], ks[layer][1][0])
+        H.check_close(out[0].astype(np.float64), oc.attend(0, q[0]), f"layer {layer}")
