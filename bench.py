@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+One step = one kvq_decode_attn call (split kernel + log-sum-exp combine) over
+the whole batch of one layer, the hot path of single-query decode attention
+over a quantized KV cache.  The cache is built on the device by
+kvq_quantize_append from seeded synthetic inputs before timing; inputs are
+resident in HBM when the timed region starts.  Caches smaller than 1 GiB are
+replicated and the steps rotate over the replicas so that the 256 MB
+Infinity Cache cannot hold the working set.
+
+Prints one JSON line: metric, value (effective KV GB/s = algorithmic cache
+bytes per step / time per step), ms_per_step, roofline of the split kernel
+(algorithmic bytes per launch / its average duration, measured with HIP
+events around that kernel on its stream) and the CPU oracle baseline.
+
+  python bench.py [--config 2] [--steps 200] [--warmup 20]
+  python bench.py --copy-probe 1073741824   (plain copy kernel, for counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step + effective KV HBM GB/s (% of MI355X peak), 1 GPU"
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: GQA int8)")
+    p.add_argument("--replicas", type=int, default=0, help="cache copies (0 = enough for 1 GiB)")
+    p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU baseline time budget")
+    p.add_argument("--copy-probe", type=int, default=0,
+                   help="run only a plain device copy of this many bytes (counter calibration)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_quantized_kvq_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe(nbytes: int, steps: int):
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "steps": steps}))
+
+
+def build_cache(wl, lens, K, synth, torch):
+    """One cache of the workload built on the device by kvq_quantize_append."""
+    table = None
+    nb = mb = 0
+    if wl["block_tokens"]:
+        table, pool = synth.block_table(wl, lens)
+        nb, mb = pool, table.shape[1]
+    cfg = K.make_config(batch=wl["batch"], num_q_heads=wl["hq"], num_kv_heads=wl["hkv"],
+                        head_dim=wl["d"], max_tokens=wl["tokens"], key=wl["key"],
+                        value=wl["value"], window=wl["window"], block_tokens=wl["block_tokens"],
+                        num_blocks=nb, max_blocks_per_seq=mb, in_dtype=wl["in_dtype"])
+    st = K.validate(cfg)
+    if st != K.KVQ_OK:
+        raise SystemExit(f"workload not supported: {K.status_string(st)}")
+    cache = K.KvqCache(cfg, "cuda", None if table is None else torch.from_numpy(table))
+    k, v = synth.kv_device(wl, lens)
+    cache.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+    K.quantize_append(cache, 0, k, v, torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    del k, v
+    return cfg, cache
+
+
+def replicate(cache, K, torch):
+    c = K.KvqCache(cache.cfg, "cuda", cache.block_table)
+    for name, buf in cache.buffers.items():
+        if buf is not None:
+            c.buffers[name].copy_(buf)
+    c.seq_lens.copy_(cache.seq_lens)
+    return c
+
+
+def cpu_baseline(wl, lens, seconds: float):
+    """The oracle as it stands, timed on the host: dequantize-then-attend of
+    one decode step over whole (sequence, KV head) groups of the same
+    workload, as many groups as fit the time budget, scaled to the full step."""
+    import numpy as np
+    from decode_attention_quantized_kvq_amd import synth
+    from oracle import kvq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    fmt = lambda s: O.TensorFormat(s["bits"], s.get("axis", "token"), bool(s.get("zero_point")),
+                                   s.get("scale", "f32"))
+    G = wl["hq"] // wl["hkv"]
+    groups = [(b, h) for b in range(wl["batch"]) for h in range(wl["hkv"])]
+    # the same groups in the same order every run; quantization is not timed
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(len(groups))
+    done_tokens = 0
+    done_bytes = 0
+    elapsed = 0.0
+    n_groups = 0
+    for gi in order:
+        b, h = groups[gi]
+        n = lens[b]
+        k, v = synth.kv_tokens(wl, b, h, n)
+        cache = O.OracleCache(1, 1, wl["d"], fmt(wl["key"]), fmt(wl["value"]), wl["window"])
+        cache.append(0, k[None], v[None])
+        q = synth.queries(wl, b)[h * G:(h + 1) * G]
+        t0 = time.perf_counter()
+        cache.attend(0, q)               # dequantize + attend, fp64
+        elapsed += time.perf_counter() - t0
+        done_bytes += O.decode_traffic(fmt(wl["key"]), fmt(wl["value"]), 1, wl["d"], [n], wl["window"])
+        done_tokens += n
+        n_groups += 1
+        if elapsed >= seconds:
+            break
+    total_bytes = O.decode_traffic(fmt(wl["key"]), fmt(wl["value"]), wl["hkv"], wl["d"], lens, wl["window"])
+    step_s = elapsed * total_bytes / done_bytes
+    return {
+        "value": round(total_bytes / step_s / 1e9, 3), "unit": "GB/s",
+        "us_per_step": round(step_s * 1e6, 1), "cores": threads, "kind": "oracle",
+        "sample": f"{n_groups} of {len(groups)} (sequence, KV head) groups of the same workload, "
+                  f"{done_tokens} tokens, {elapsed:.1f} s of fp64 dequantize-then-attend, "
+                  f"scaled by bytes to one full step",
+    }
+
+
+def load_traffic(kernel: str, workload: str, sha: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+    when they were taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha") != sha:
+        return None
+    return int(d["hbm_bytes_per_launch"])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the decode "
+              "path has no multi-GPU mode (sequences and KV heads are independent, so several "
+              "GPUs would each run this same single-GPU kernel on their share).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+    import numpy as np
+    import torch
+    from decode_attention_quantized_kvq_amd import kvq as K
+    from decode_attention_quantized_kvq_amd import synth
+
+    wl = synth.workload(args.config)
+    lens = synth.seq_lengths(wl)
+    max_len = max(lens)
+    log(f"[bench] workload {args.config} {wl['name']}: building cache")
+    t0 = time.time()
+    cfg, cache = build_cache(wl, lens, K, synth, torch)
+    traffic = K.decode_traffic_bytes(cfg, lens)
+    reps = args.replicas
+    if reps <= 0:
+        reps = 1 if traffic < (16 << 20) else max(1, math.ceil((1 << 30) / traffic))
+    caches = [cache] + [replicate(cache, K, torch) for _ in range(reps - 1)]
+    torch.cuda.synchronize()
+    log(f"[bench] {reps} replica(s) of {traffic / 1e6:.1f} MB built in {time.time() - t0:.1f} s")
+
+    q = torch.from_numpy(np.stack([synth.queries(wl, b) for b in range(wl["batch"])]))
+    q = q.to(torch.bfloat16 if wl["in_dtype"] == "bf16" else torch.float32).cuda()
+    out = torch.empty((wl["batch"], wl["hq"], wl["d"]), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(K.decode_workspace_bytes(cfg, max_len, args.split), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(i, events=None):
+        K.decode_attn(caches[i % reps], 0, q, max_len, out=out, workspace=ws,
+                      split_tokens=args.split, split_events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: K steps between two events on the stream
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.2f} us/step")
+
+    # split-kernel duration: events recorded by the library around it
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for a, b in pairs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, pairs[i])
+    torch.cuda.synchronize()
+    split_ms = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
+    log(f"[bench] split kernel: {split_ms * 1e3:.2f} us/launch")
+
+    value = traffic / (ms_step * 1e-3) / 1e9
+    achieved = traffic / (split_ms * 1e-3) / 1e9
+    sha = kernel_source_sha()
+    hbm = load_traffic("decode_split", wl["name"], sha)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "us_per_step": round(ms_step * 1e3, 2),
+        "pct_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",   # MFMA operands (exact fp16 codes, fp16 hi/lo query and
+                          # weights); fp32 accumulation and softmax
+        "data": "synthetic (seeded; no dataset on the pages)",
+        "config": {"workload": wl["name"], "batch": wl["batch"], "q_heads": wl["hq"],
+                   "kv_heads": wl["hkv"], "head_dim": wl["d"], "tokens": max_len,
+                   "key": wl["key"], "value": wl["value"], "window": wl["window"],
+                   "block_tokens": wl["block_tokens"], "replicas": reps,
+                   "split_tokens": args.split or "auto", "kernel_sources": sha},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": hbm, "kernel": "decode_split",
+                     "algorithmic_bytes_per_launch": traffic,
+                     "avg_launch_us": round(split_ms * 1e3, 2)},
+    }
+    if not args.no_cpu:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(wl, lens, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

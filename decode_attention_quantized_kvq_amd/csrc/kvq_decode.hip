@@ -166,7 +166,7 @@ struct Meta {
   static constexpr bool ZP = (MK == MK_F32Z || MK == MK_F16Z);
   u32x4 r0, r1;  // raw bytes of 4 consecutive tokens (8-byte formats use both)
 
-  __device__ inline void load(const uint8_t* base, int tok) {
+  __device__ inline void load(const uint8_t* base, size_t tok) {
     if (MK == MK_F32 || MK == MK_F16Z) {
       r0 = *(const u32x4*)(base + (size_t)tok * 4);
     } else if (MK == MK_F32Z) {
@@ -244,7 +244,7 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int
     const uint8_t* kr = ad.k + (slot + c) * KROW;
     if (Codes<KC>::B8) {
       t.k[bb][0] = *(const u32x4*)(kr + 16 * g);
-      t.k[bb][KROW == D ? 1 : 0] = *(const u32x4*)(kr + 64 + 16 * g);
+      t.k[bb][1] = *(const u32x4*)(kr + 64 + 16 * g);
     } else {
       t.k[bb][0] = *(const u32x4*)(kr + 16 * g);
     }
@@ -256,8 +256,8 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int
       else
         t.v4[4 * bb + i] = *(const uint32_t*)(vr + 4 * c);
     }
-    if (Meta<KM>::BYTES) t.km[bb].load(ad.km, (int)(slot + 4 * g));
-    if (Meta<VM>::BYTES) t.vm[bb].load(ad.vm, (int)(slot + 4 * g));
+    if (Meta<KM>::BYTES) t.km[bb].load(ad.km, slot + 4 * g);
+    if (Meta<VM>::BYTES) t.vm[bb].load(ad.vm, slot + 4 * g);
   }
 }
 
@@ -302,14 +302,15 @@ __device__ inline void value_frags(const TileRaw<KC, KM, VC, VM>& t, half8 out[8
     } else {
       const uint32_t A = t.v4[2 * pp], B = t.v4[2 * pp + 1];
       uint32_t o[4];
-      cvt_b4<S>(perm(B, A, 0x05040100u), o);   // bytes (A0, A1, B0, B1)
-      // o pairs nibble n of the low half-word (A) with nibble n of the high
-      // half-word (B): features 0, 1, 2, 3 in the order (n0, n1?, ...)
+      // bytes (A0, A1, B0, B1): cvt_b4 pairs nibble n of the low half-word
+      // (token A) with nibble n of the high half-word (token B), i.e. feature
+      // n of both tokens, for n = 0..3 in that order.
+      cvt_b4<S>(perm(B, A, 0x05040100u), o);
       pr[0][pp] = o[0];
       pr[1][pp] = o[1];
       pr[2][pp] = o[2];
       pr[3][pp] = o[3];
-      cvt_b4<S>(perm(B, A, 0x07060302u), o);   // bytes (A2, A3, B2, B3)
+      cvt_b4<S>(perm(B, A, 0x07060302u), o);   // bytes (A2, A3, B2, B3): features 4..7
       pr[4][pp] = o[0];
       pr[5][pp] = o[1];
       pr[6][pp] = o[2];
@@ -810,6 +811,7 @@ __global__ void __launch_bounds__(64) decode_combine(DecodeArgs a) {
 template <int KC, int KM, bool KCH, int VC, int VM>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.nsp, a.hkv, a.batch), block(256);
+  if (a.ev_begin && hipEventRecord((hipEvent_t)a.ev_begin, s) != hipSuccess) return hipErrorInvalidValue;
   if (a.nsp > 0) {
     switch (a.group) {
       case 1: hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, 1>), grid, block, 0, s, a); break;
@@ -821,6 +823,7 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (a.ev_end && hipEventRecord((hipEvent_t)a.ev_end, s) != hipSuccess) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_combine, dim3(a.hq, a.batch), dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -351,6 +351,8 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   a.in_bf16 = cfg->in_dtype == KVQ_DT_BF16;
   classify(cfg->key, true, &a.kk);
   classify(cfg->value, false, &a.vk);
+  a.ev_begin = opts ? opts->split_begin_event : nullptr;
+  a.ev_end = opts ? opts->split_end_event : nullptr;
   return launch_decode(a, stream);
 }
 

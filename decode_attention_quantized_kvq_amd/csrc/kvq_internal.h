@@ -85,6 +85,8 @@ struct DecodeArgs {
   int nsp;           // n_split + 1 if there is a window
   int in_bf16;
   TensorKind kk, vk;
+  void* ev_begin;    // hipEvent_t recorded before the split kernel, or null
+  void* ev_end;      // hipEvent_t recorded after it, or null
 };
 
 kvq_status launch_append(const AppendArgs& a, void* stream);

@@ -66,7 +66,8 @@ class BufferSizes(ctypes.Structure):
 
 
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("split_tokens", ctypes.c_int)]
+    _fields_ = [("split_tokens", ctypes.c_int), ("split_begin_event", ctypes.c_void_p),
+                ("split_end_event", ctypes.c_void_p)]
 
 
 class KvqError(RuntimeError):
@@ -246,8 +247,11 @@ def quantize_append(cache: KvqCache, layer: int, k_new: torch.Tensor, v_new: tor
 
 def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                split_tokens: int = 0, stream=None) -> torch.Tensor:
-    """kvq_decode_attn: q [B][Hq][D] -> out [B][Hq][D] fp32."""
+                split_tokens: int = 0, stream=None, split_events=None) -> torch.Tensor:
+    """kvq_decode_attn: q [B][Hq][D] -> out [B][Hq][D] fp32.
+
+    split_events: optional (begin, end) torch.cuda.Event pair recorded around
+    the split kernel (already created, e.g. by one record() call)."""
     cfg = cache.cfg
     _check_input(q, cfg, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "q")
     if out is None:
@@ -261,6 +265,9 @@ def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     desc = cache.desc()
     opts = DecodeOpts(int(split_tokens))
+    if split_events is not None:
+        opts.split_begin_event = split_events[0].cuda_event
+        opts.split_end_event = split_events[1].cuda_event
     _check(lib().kvq_decode_attn_ex(ctypes.byref(cfg), ctypes.byref(desc), int(layer),
                                     _ptr(q), _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),

@@ -220,9 +220,13 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
                                const void* k_new, const void* v_new, int n_new,
                                const int32_t* new_lens, void* stream);
 
-/* Tuning knobs of kvq_decode_attn; zero fields take the library's choice. */
+/* Tuning and measurement knobs of kvq_decode_attn; zero / NULL fields take
+ * the library's choice. */
 typedef struct {
-  int split_tokens; /* quantized tokens per workgroup, a multiple of 128 */
+  int split_tokens;         /* quantized tokens per workgroup, a multiple of 128 */
+  void* split_begin_event;  /* hipEvent_t recorded on the stream right before
+                               the split kernel, or NULL */
+  void* split_end_event;    /* hipEvent_t recorded right after it, or NULL */
 } kvq_decode_opts;
 
 /* Single-query decode attention of one layer over every cached token (P2,

@@ -198,26 +198,30 @@ def window_values(bt: Built, t: str, b: int, h: int, nw: int) -> np.ndarray:
     return (r.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _bits(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x)).view(np.uint8)
+
+
 def check_records(bt: Built, b: int, h: int):
     """Bit-exact codes and metadata of sequence b, KV head h."""
     for t in ("k", "v"):
         st = bt.oracle.stored(b, t)
         n = st.codes.shape[1]
-        dev = device_records(bt, t, b, h, n)
-        assert np.array_equal(dev["codes"], st.codes[h]), f"{t} codes differ at b={b} h={h}"
-        if "chan" in dev:
-            assert np.array_equal(dev["chan"].view(np.uint32), st.chan[h].view(np.uint32))
-        if "u" in dev:
-            assert np.array_equal(dev["u"], st.u[h]), f"{t} scale codes differ"
-            assert dev["S"].view(np.uint32) == st.S[h].view(np.uint32)
-        if "s" in dev:
-            want = st.s[h]
-            assert dev["s"].dtype == want.dtype
-            assert np.array_equal(dev["s"].view(np.uint8), want.view(np.uint8)), f"{t} scales differ b={b} h={h}"
-        if "z" in dev:
-            assert np.array_equal(dev["z"].view(np.uint8), st.z[h].view(np.uint8)), f"{t} zero points differ"
+        if n:   # else every token is still in the window
+            dev = device_records(bt, t, b, h, n)
+            assert np.array_equal(dev["codes"], st.codes[h]), f"{t} codes differ at b={b} h={h}"
+            if "chan" in dev:
+                assert np.array_equal(_bits(dev["chan"]), _bits(st.chan[h])), "channel scales differ"
+            if "u" in dev:
+                assert np.array_equal(dev["u"], st.u[h]), f"{t} scale codes differ"
+                assert np.array_equal(_bits(np.float32(dev["S"])), _bits(np.float32(st.S[h])))
+            if "s" in dev:
+                assert dev["s"].dtype == st.s.dtype
+                assert np.array_equal(_bits(dev["s"]), _bits(st.s[h])), f"{t} scales differ b={b} h={h}"
+            if "z" in dev:
+                assert np.array_equal(_bits(dev["z"]), _bits(st.z[h])), f"{t} zero points differ"
         if bt.wl["window"]:
-            # ring slots hold positions p with slot p % W; compare as a set of rows
+            # ring slot of position p is p % W
             wv = bt.oracle.window_values(b, t)[h]
             nw = wv.shape[0]
             n_tot = bt.oracle.lens[b]
