@@ -21,28 +21,32 @@ FLAGS = [
     "-shared",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: no AGPR round trips when the softmax
+    # rescales them
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every source into libkvq.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compiles every source into libkvq.so (or `out`); returns its path.
+    defines: extra -D macros (e.g. KVQ_PREFETCH=1) for variant builds."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = (res.stdout + res.stderr).strip()
+    text = (res.stdout + res.stderr).strip()
     # the host pass does not know the device target feature; that is expected
-    lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l]
+    lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
     if verbose and lines:
         print("\n".join(lines))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -40,6 +40,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// Tiles in flight ahead of the one being computed (1 or 2).
+#ifndef KVQ_PREFETCH
+#define KVQ_PREFETCH 1
+#endif
+
 constexpr int D = 128;
 constexpr int WAVES = 4;
 constexpr int TILE = 32;
@@ -133,16 +138,34 @@ __device__ inline void cvt_b8(uint32_t w, uint32_t& p01, uint32_t& p23) {
   p23 = h2_add(perm(0x64646464u, w, 0x04030402u), SIGNED ? H_M1152 : H_M1024);
 }
 
+// A constant held in a VGPR.  VOP3 instructions of gfx9 cannot encode a
+// literal, so (w & mask) | magic with literal operands costs two
+// instructions; with both in VGPRs it is one v_and_or_b32.
+__device__ inline uint32_t in_vgpr(uint32_t x) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(x));
+  return r;
+}
+
+struct NibbleMasks {
+  uint32_t lo, hi, magic;  // 0x000F000F, 0x00F000F0, 0x64006400
+  __device__ inline void init() {
+    lo = in_vgpr(0x000F000Fu);
+    hi = in_vgpr(0x00F000F0u);
+    magic = in_vgpr(MAGIC);
+  }
+};
+
 // Converts 8 int4 codes of one dword into four fp16 pairs, ordered
 // (n0,n4), (n1,n5), (n2,n6), (n3,n7) where n_i is nibble i (bits 4i..4i+3).
 template <bool SIGNED>
-__device__ inline void cvt_b4(uint32_t w, uint32_t out[4]) {
+__device__ inline void cvt_b4(uint32_t w, uint32_t out[4], const NibbleMasks& nm) {
   if (SIGNED) w ^= 0x88888888u;
   const uint32_t w8 = w >> 8;
-  out[0] = h2_add((w & 0x000F000Fu) | MAGIC, SIGNED ? H_M1032 : H_M1024);
-  out[1] = h2_fma((w & 0x00F000F0u) | MAGIC, H_SIXTEENTH, SIGNED ? H_M72 : H_M64);
-  out[2] = h2_add((w8 & 0x000F000Fu) | MAGIC, SIGNED ? H_M1032 : H_M1024);
-  out[3] = h2_fma((w8 & 0x00F000F0u) | MAGIC, H_SIXTEENTH, SIGNED ? H_M72 : H_M64);
+  out[0] = h2_add((w & nm.lo) | nm.magic, SIGNED ? H_M1032 : H_M1024);
+  out[1] = h2_fma((w & nm.hi) | nm.magic, H_SIXTEENTH, SIGNED ? H_M72 : H_M64);
+  out[2] = h2_add((w8 & nm.lo) | nm.magic, SIGNED ? H_M1032 : H_M1024);
+  out[3] = h2_fma((w8 & nm.hi) | nm.magic, H_SIXTEENTH, SIGNED ? H_M72 : H_M64);
 }
 
 // Feature index d held by the lane of row group g at k-slot e of the j-th
@@ -166,17 +189,18 @@ struct Meta {
   static constexpr bool ZP = (MK == MK_F32Z || MK == MK_F16Z);
   u32x4 r0, r1;  // raw bytes of 4 consecutive tokens (8-byte formats use both)
 
-  __device__ inline void load(const uint8_t* base, size_t tok) {
+  // p: metadata of 4 consecutive tokens
+  __device__ inline void load(const uint8_t* p) {
     if (MK == MK_F32 || MK == MK_F16Z) {
-      r0 = *(const u32x4*)(base + (size_t)tok * 4);
+      r0 = *(const u32x4*)p;
     } else if (MK == MK_F32Z) {
-      r0 = *(const u32x4*)(base + (size_t)tok * 8);
-      r1 = *(const u32x4*)(base + (size_t)tok * 8 + 16);
+      r0 = *(const u32x4*)p;
+      r1 = *(const u32x4*)(p + 16);
     } else if (MK == MK_F16) {
-      const u32x2 v = *(const u32x2*)(base + (size_t)tok * 2);
+      const u32x2 v = *(const u32x2*)p;
       r0 = u32x4{v.x, v.y, 0u, 0u};
     } else if (MK == MK_U8) {
-      r0 = u32x4{*(const uint32_t*)(base + tok), 0u, 0u, 0u};
+      r0 = u32x4{*(const uint32_t*)p, 0u, 0u, 0u};
     }
   }
   // scale (and zero point) of token i in 0..3
@@ -211,7 +235,8 @@ struct Addr {
   size_t head_tok;       // contiguous: first token slot of this head
   int nblk;              // blocks holding tokens
 
-  // token slot index of block `blk` (clamped to the blocks holding tokens)
+  // token slot index of block `blk` (clamped to the blocks holding tokens);
+  // wave-uniform
   __device__ inline size_t block_slot(int blk) const {
     blk = blk < nblk ? blk : nblk - 1;
     if (table) {
@@ -222,6 +247,26 @@ struct Addr {
     return head_tok + (size_t)blk * 16;
   }
 };
+
+// Byte offsets of this lane's data inside a 16-token block; fixed for the
+// whole kernel, so every load is a wave-uniform base plus a 32-bit offset.
+struct LaneOff {
+  uint32_t k0, k1, v[4], km, vm;
+};
+
+template <int KC, int KM, int VC, int VM>
+__device__ inline LaneOff lane_offsets(int c, int g) {
+  constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
+  LaneOff o;
+  o.k0 = c * KROW + 16 * g;   // key row c
+  o.k1 = o.k0 + 64;           // 8-bit keys: second half of the row
+#pragma unroll
+  for (int i = 0; i < 4; ++i)  // value rows 4g+i, features [8c, 8c+8)
+    o.v[i] = (4 * g + i) * VROW + (Codes<VC>::B8 ? 8 * c : 4 * c);
+  o.km = 4 * g * Meta<KM>::BYTES;
+  o.vm = 4 * g * Meta<VM>::BYTES;
+  return o;
+}
 
 // Raw registers of one 32-token tile.
 template <int KC, int KM, int VC, int VM>
@@ -236,34 +281,32 @@ struct TileRaw {
 };
 
 template <int KC, int KM, int VC, int VM>
-__device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int t0, int c, int g) {
+__device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int t0,
+                                 const LaneOff& o) {
   constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const size_t slot = ad.block_slot((t0 >> 4) + bb);
-    const uint8_t* kr = ad.k + (slot + c) * KROW;
-    if (Codes<KC>::B8) {
-      t.k[bb][0] = *(const u32x4*)(kr + 16 * g);
-      t.k[bb][1] = *(const u32x4*)(kr + 64 + 16 * g);
-    } else {
-      t.k[bb][0] = *(const u32x4*)(kr + 16 * g);
-    }
+    const uint8_t* kb = ad.k + slot * KROW;
+    t.k[bb][0] = *(const u32x4*)(kb + o.k0);
+    if (Codes<KC>::B8) t.k[bb][1] = *(const u32x4*)(kb + o.k1);
+    const uint8_t* vb = ad.v + slot * VROW;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint8_t* vr = ad.v + (slot + 4 * g + i) * VROW;
       if (Codes<VC>::B8)
-        t.v8[4 * bb + i] = *(const u32x2*)(vr + 8 * c);
+        t.v8[4 * bb + i] = *(const u32x2*)(vb + o.v[i]);
       else
-        t.v4[4 * bb + i] = *(const uint32_t*)(vr + 4 * c);
+        t.v4[4 * bb + i] = *(const uint32_t*)(vb + o.v[i]);
     }
-    if (Meta<KM>::BYTES) t.km[bb].load(ad.km, slot + 4 * g);
-    if (Meta<VM>::BYTES) t.vm[bb].load(ad.vm, slot + 4 * g);
+    if (Meta<KM>::BYTES) t.km[bb].load(ad.km + slot * Meta<KM>::BYTES + o.km);
+    if (Meta<VM>::BYTES) t.vm[bb].load(ad.vm + slot * Meta<VM>::BYTES + o.vm);
   }
 }
 
 // Key operand of the j-th score MFMA for block bb.
 template <int KC, int KM, int VC, int VM>
-__device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, int j) {
+__device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, int j,
+                                 const NibbleMasks& nm) {
   constexpr bool S = Codes<KC>::SIGNED;
   if (Codes<KC>::B8) {
     const u32x4 r = t.k[bb][j >> 1];
@@ -274,47 +317,39 @@ __device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, int j
     return as_h8(a, b, c, d);
   } else {
     uint32_t o[4];
-    cvt_b4<S>(t.k[bb][0][j], o);
+    cvt_b4<S>(t.k[bb][0][j], o, nm);
     return as_h8(o[0], o[1], o[2], o[3]);
   }
 }
 
-// Value operand of the j-th output MFMA: lane (c, g) gives feature 8c + j of
+// Value operands of the 8 output MFMAs: lane (c, g) gives feature 8c + j of
 // its 8 tokens, two tokens per fp16 pair.
 template <int KC, int KM, int VC, int VM>
-__device__ inline void value_frags(const TileRaw<KC, KM, VC, VM>& t, half8 out[8]) {
+__device__ inline void value_frags(const TileRaw<KC, KM, VC, VM>& t, half8 out[8],
+                                   const NibbleMasks& nm) {
   constexpr bool S = Codes<VC>::SIGNED;
   uint32_t pr[8][4];  // [j][token pair]
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
     if (Codes<VC>::B8) {
       const u32x2 A = t.v8[2 * pp], B = t.v8[2 * pp + 1];
-      uint32_t x[4] = {perm(B.x, A.x, 0x05010400u), perm(B.x, A.x, 0x07030602u),
-                       perm(B.y, A.y, 0x05010400u), perm(B.y, A.y, 0x07030602u)};
+      // bytes (A f, B f, A f+1, B f+1) for f = 0, 2, 4, 6
+      const uint32_t x[4] = {perm(B.x, A.x, 0x05010400u), perm(B.x, A.x, 0x07030602u),
+                             perm(B.y, A.y, 0x05010400u), perm(B.y, A.y, 0x07030602u)};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t lo, hi;
-        cvt_b8<S>(x[q], lo, hi);  // x[q] holds (A d, B d, A d+1, B d+1)
-        // cvt_b8 pairs bytes (0,1) and (2,3): (A,B) at feature 2q and 2q+1
-        pr[2 * q][pp] = lo;
-        pr[2 * q + 1][pp] = hi;
-      }
+      for (int q = 0; q < 4; ++q) cvt_b8<S>(x[q], pr[2 * q][pp], pr[2 * q + 1][pp]);
     } else {
       const uint32_t A = t.v4[2 * pp], B = t.v4[2 * pp + 1];
       uint32_t o[4];
       // bytes (A0, A1, B0, B1): cvt_b4 pairs nibble n of the low half-word
       // (token A) with nibble n of the high half-word (token B), i.e. feature
       // n of both tokens, for n = 0..3 in that order.
-      cvt_b4<S>(perm(B, A, 0x05040100u), o);
-      pr[0][pp] = o[0];
-      pr[1][pp] = o[1];
-      pr[2][pp] = o[2];
-      pr[3][pp] = o[3];
-      cvt_b4<S>(perm(B, A, 0x07060302u), o);   // bytes (A2, A3, B2, B3): features 4..7
-      pr[4][pp] = o[0];
-      pr[5][pp] = o[1];
-      pr[6][pp] = o[2];
-      pr[7][pp] = o[3];
+      cvt_b4<S>(perm(B, A, 0x05040100u), o, nm);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pr[q][pp] = o[q];
+      cvt_b4<S>(perm(B, A, 0x07060302u), o, nm);  // bytes (A2, A3, B2, B3): features 4..7
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pr[4 + q][pp] = o[q];
     }
   }
 #pragma unroll
@@ -322,37 +357,62 @@ __device__ inline void value_frags(const TileRaw<KC, KM, VC, VM>& t, half8 out[8
 }
 
 // ---------------------------------------------------------------------------
-// Per-wave state of the online softmax
+// Per-wave state of the online softmax.  The reference max m and the
+// reference value scale R move only when exceeded by 2^8 and 2^6, so the
+// accumulators are rescaled on few tiles; weights stay below 2^14 and the
+// fp16 halves keep full precision.
 // ---------------------------------------------------------------------------
+constexpr float M_SLACK = 8.0f;
+constexpr float R_SLACK = 64.0f;
+
 struct Softmax {
-  float m;   // running max (base-2 units), identical across the 4 row groups
+  float m;   // reference max (base-2 units), identical across the 4 row groups
   float l;   // this lane's share of the running sum of 2^(s - m)
-  float R;   // running power-of-two reference of the folded value scale
+  float R;   // power-of-two reference of the folded value scale
   float z;   // this lane's share of sum w * zero_point (zero-point values)
   f32x4 o[8];
+
+  __device__ inline void init(float r0) {
+    m = NEG_INF;
+    l = 0.0f;
+    R = r0;
+    z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Moves the reference max if the tile max exceeds it by more than M_SLACK;
+  // returns the rescale factor of the accumulators and the max to use.
+  __device__ inline float update_max(float mt, float* mu) {
+    float alpha = 1.0f;
+    if (mt > m + M_SLACK) {
+      alpha = exp2_fast(m - mt);  // 0 when m = -inf
+      m = mt;
+    }
+    *mu = m == NEG_INF ? 0.0f : m;
+    return alpha;
+  }
 };
 
 // Processes one 32-token tile already in registers.
 template <int KC, int KM, bool KCH, int VC, int VM, int G>
 __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, int tend,
-                                    const half8 qf[4], float qs, float sumq, int c, int g,
-                                    int limb, Softmax& st) {
+                                    const half8 qf[4], float qs, float sumq, int g,
+                                    int limb, const NibbleMasks& nm, Softmax& st) {
   // scores
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag(t, 0, j), qf[j], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag(t, 1, j), qf[j], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag(t, 0, j, nm), qf[j], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag(t, 1, j, nm), qf[j], s1, 0, 0, 0);
   }
   float s[8], vs[8], vz[8];
-  bool valid[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int bb = e >> 2, i = e & 3;
     const float raw0 = bb ? s1[i] : s0[i];
     const float raw = raw0 + ror_g<G>(raw0);  // high + low half of the query
-    const int tok = t0 + 16 * bb + 4 * g + i;
-    valid[e] = tok < tend;
+    const bool valid = t0 + 16 * bb + 4 * g + i < tend;
     float v;
     if (KCH) {
       v = raw * qs;
@@ -360,37 +420,36 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
       const float ks = t.km[bb].scale(i);
       v = (Meta<KM>::ZP ? (raw - t.km[bb].zero(i) * sumq) : raw) * (ks * qs);
     }
-    s[e] = valid[e] ? v : NEG_INF;
-    vs[e] = valid[e] ? t.vm[bb].scale(i) : 0.0f;
-    vz[e] = (Meta<VM>::ZP && valid[e]) ? t.vm[bb].zero(i) : 0.0f;
+    s[e] = valid ? v : NEG_INF;
+    vs[e] = valid ? t.vm[bb].scale(i) : 0.0f;
+    vz[e] = (Meta<VM>::ZP && valid) ? t.vm[bb].zero(i) : 0.0f;
   }
   float mt = s[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[e]);
-  mt = rows_max(mt);
-  const float mn = fmaxf(st.m, mt);
-  const float mu = mn == NEG_INF ? 0.0f : mn;
-  const float alpha = exp2_fast(st.m - mu);
+  float mu;
+  float f = st.update_max(rows_max(mt), &mu);
   float p[8], lsum = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     p[e] = exp2_fast(s[e] - mu);
     lsum += p[e];
   }
-  st.l = st.l * alpha + lsum;
-  st.m = mn;
-  // Folded value scale, kept in (0, 1] by a running power-of-two reference.
-  float f = alpha, inv;
+  st.l = st.l * f + lsum;
+  float inv;
   if (VM == MK_U8) {
     inv = 1.0f / 256.0f;
   } else {
     float sv = vs[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) sv = fmaxf(sv, vs[e]);
-    const float Rn = fmaxf(st.R, pow2_ceil(rows_max(sv)));
-    f = alpha * (st.R / Rn);
-    st.R = Rn;
-    inv = 1.0f / Rn;
+    sv = rows_max(sv);
+    if (sv > st.R * R_SLACK) {
+      const float Rn = pow2_ceil(sv);
+      f *= st.R / Rn;
+      st.R = Rn;
+    }
+    inv = 1.0f / st.R;
   }
   if (__any(f != 1.0f)) {
 #pragma unroll
@@ -419,7 +478,7 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
   }
   const half8 pf = as_h8(pw[0], pw[1], pw[2], pw[3]);
   half8 vf[8];
-  value_frags(t, vf);
+  value_frags(t, vf, nm);
 #pragma unroll
   for (int j = 0; j < 8; ++j) st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[j], pf, st.o[j], 0, 0, 0);
 }
@@ -451,8 +510,8 @@ __device__ inline void load_win_tile(WinRaw& t, const uint16_t* kw, const uint16
 }
 
 template <int G>
-__device__ inline void compute_win_tile(const WinRaw& t, int t0, int nw, const bf16x8 qf[4],
-                                        float qs, int c, int g, int limb, Softmax& st) {
+__device__ inline void compute_win_tile(const WinRaw& t, int t0, int tend, const bf16x8 qf[4],
+                                        float qs, int g, int limb, Softmax& st) {
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -466,15 +525,13 @@ __device__ inline void compute_win_tile(const WinRaw& t, int t0, int nw, const b
     const int bb = e >> 2, i = e & 3;
     const float raw0 = bb ? s1[i] : s0[i];
     const float raw = raw0 + ror_g<G>(raw0);
-    s[e] = (t0 + 16 * bb + 4 * g + i) < nw ? raw * qs : NEG_INF;
+    s[e] = (t0 + 16 * bb + 4 * g + i) < tend ? raw * qs : NEG_INF;
   }
   float mt = s[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[e]);
-  mt = rows_max(mt);
-  const float mn = fmaxf(st.m, mt);
-  const float mu = mn == NEG_INF ? 0.0f : mn;
-  const float alpha = exp2_fast(st.m - mu);
+  float mu;
+  const float alpha = st.update_max(rows_max(mt), &mu);
   float p[8], lsum = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -482,7 +539,6 @@ __device__ inline void compute_win_tile(const WinRaw& t, int t0, int nw, const b
     lsum += p[e];
   }
   st.l = st.l * alpha + lsum;
-  st.m = mn;
   if (__any(alpha != 1.0f)) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) st.o[j] *= alpha;
@@ -517,10 +573,41 @@ __device__ inline void compute_win_tile(const WinRaw& t, int t0, int nw, const b
 
 // ---------------------------------------------------------------------------
 // Query setup: lane (c, g) holds query head (c mod G), as the high (limb 0)
-// or low (limb 1) fp16 half, for the features its key operand covers.
+// or low (limb 1) half, for the 32 features its key operand covers, read as
+// runs of consecutive features with vector loads.
 // ---------------------------------------------------------------------------
-__device__ inline float load_q(const void* q, size_t idx, int bf16) {
-  return bf16 ? bf16_f32(((const uint16_t*)q)[idx]) : ((const float*)q)[idx];
+__device__ inline void unpack_bf16x8(const u32x4 r, float* out) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    out[2 * k] = __uint_as_float(r[k] << 16);
+    out[2 * k + 1] = __uint_as_float(r[k] & 0xFFFF0000u);
+  }
+}
+
+// Loads features run0 .. run0+nrun-1 (nrun 16 or 32) of one query row.
+struct QRaw {
+  u32x4 r[8];
+};
+
+__device__ inline void load_q_run(QRaw& q, const void* base, size_t row, int start, int len,
+                                  int slot, int bf16) {
+  // bf16: len/8 vectors of 8 values; f32: len/4 vectors of 4 values
+  if (bf16) {
+    const uint16_t* p = (const uint16_t*)base + row + start;
+    for (int k = 0; k < len / 8; ++k) q.r[slot + k] = *(const u32x4*)(p + 8 * k);
+  } else {
+    const float* p = (const float*)base + row + start;
+    for (int k = 0; k < len / 4; ++k) q.r[slot + k] = *(const u32x4*)(p + 4 * k);
+  }
+}
+
+__device__ inline void unpack_q(const QRaw& q, int nvals, int bf16, float* out) {
+  if (bf16) {
+    for (int k = 0; k < nvals / 8; ++k) unpack_bf16x8(q.r[k], out + 8 * k);
+  } else {
+    for (int k = 0; k < nvals / 4; ++k)
+      for (int i = 0; i < 4; ++i) out[4 * k + i] = __uint_as_float(q.r[k][i]);
+  }
 }
 
 // Power-of-two scale that brings the head's largest |q| into [2^12, 2^13).
@@ -615,15 +702,31 @@ __device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
 // ---------------------------------------------------------------------------
 template <int G>
 __device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G>& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int hh = c % G, limb = (c / G) & 1;
   const size_t qrow = ((size_t)b * a.hq + (size_t)h * G + hh) * D;
+  // features 32j + 8g + e: four runs of 8
+  QRaw qr;
   float qv[32];
+  if (a.in_bf16) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) qr.r[j] = *(const u32x4*)((const uint16_t*)a.q + qrow + 32 * j + 8 * g);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[8 * j + e] = load_q(a.q, qrow + 32 * j + 8 * g + e, a.in_bf16);
+    for (int j = 0; j < 4; ++j) unpack_bf16x8(qr.r[j], qv + 8 * j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qr.r[2 * j] = *(const u32x4*)((const float*)a.q + qrow + 32 * j + 8 * g);
+      qr.r[2 * j + 1] = *(const u32x4*)((const float*)a.q + qrow + 32 * j + 8 * g + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[4 * k + i] = __uint_as_float(qr.r[k][i]);
+  }
   float amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(qv[k]));
@@ -648,19 +751,14 @@ __device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G
     qf[j] = as_b8(w[0], w[1], w[2], w[3]);
   }
   Softmax st;
-  st.m = NEG_INF;
-  st.l = 0.0f;
-  st.R = 1.0f;
-  st.z = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.init(1.0f);
   const size_t head = ((size_t)b * a.hkv + h) * a.window * D;
   const int per = (a.window + WAVES - 1) / WAVES;
   const int w0 = wave * per, w1 = min(w0 + per, nw);
   for (int t0 = w0; t0 < w1; t0 += TILE) {
     WinRaw t;
     load_win_tile(t, a.k_win + head, a.v_win + head, t0, nw, c, g);
-    compute_win_tile<G>(t, t0, w1, qf, qs, c, g, limb, st);
+    compute_win_tile<G>(t, t0, w1, qf, qs, g, limb, st);
   }
   wave_finish<G>(st, 1.0f, c, g, wave, sh);
   block_merge<G>(a, sh, b, h, a.n_split);
@@ -678,49 +776,33 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const int tok0 = split * a.split_tokens;
   if (tok0 >= si.nq) return;
   const int tok1 = min(tok0 + a.split_tokens, si.nq);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int hh = c % G, limb = (c / G) & 1;
   constexpr bool KB8 = Codes<KC>::B8;
 
-  // query fragments (features as the key operand orders them)
+  // 1. query (and per-channel key scale) loads, issued first
   const size_t qrow = ((size_t)b * a.hq + (size_t)h * G + hh) * D;
-  const float* chan = KCH ? a.k_chan + ((size_t)b * a.hkv + h) * D : nullptr;
-  float qv[32];
-  float amax = 0.0f, qsum = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = key_feature<KB8>(j, g, e);
-      float x = load_q(a.q, qrow + d, a.in_bf16);
-      if (KCH) x *= chan[d];  // per-channel key scale moved onto the query
-      qv[8 * j + e] = x;
-      amax = fmaxf(amax, fabsf(x));
-    }
-  float inv;
-  const float sc = q_norm_scale(rows_max(amax), &inv);
-  const float qs = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128)
-  half8 qf[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t w[4];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      _Float16 hv[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const float x = qv[8 * j + 2 * pp + k] * sc;
-        qsum += x;
-        const _Float16 hi = (_Float16)x;
-        hv[k] = limb ? (_Float16)(x - (float)hi) : hi;
-      }
-      w[pp] = pack_h2(hv[0], hv[1]);
-    }
-    qf[j] = as_h8(w[0], w[1], w[2], w[3]);
+  // the lane's 32 key features as runs: 8-bit [16g, +16) and [64+16g, +16);
+  // 4-bit [32g, +32)
+  const int run0 = KB8 ? 16 * g : 32 * g;
+  const int run1 = 64 + 16 * g;
+  QRaw qr, cr;
+  if (KB8) {
+    load_q_run(qr, a.q, qrow, run0, 16, 0, a.in_bf16);
+    load_q_run(qr, a.q, qrow, run1, 16, a.in_bf16 ? 2 : 4, a.in_bf16);
+  } else {
+    load_q_run(qr, a.q, qrow, run0, 32, 0, a.in_bf16);
   }
-  const float sumq = Meta<KM>::ZP ? rows_sum(qsum) : 0.0f;
+  const size_t crow = ((size_t)b * a.hkv + h) * D;
+  if (KCH) {
+    load_q_run(cr, a.k_chan, crow, run0, KB8 ? 16 : 32, 0, 0);
+    if (KB8) load_q_run(cr, a.k_chan, crow, run1, 16, 4, 0);
+  }
 
+  // 2. the first tiles of this wave's range
   Addr ad;
   ad.k = a.k_codes;
   ad.v = a.v_codes;
@@ -737,32 +819,92 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
     ad.table = nullptr;
     ad.head_tok = ((size_t)b * a.hkv + h) * a.max_tokens;
   }
-
-  Softmax st;
-  st.m = NEG_INF;
-  st.l = 0.0f;
-  st.R = __uint_as_float(0x00800000u);  // 2^-126
-  st.z = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  const LaneOff lo = lane_offsets<KC, KM, VC, VM>(c, g);
   const int per = a.split_tokens / WAVES;
   const int w0 = tok0 + wave * per;
   const int w1 = min(w0 + per, tok1);
-  TileRaw<KC, KM, VC, VM> ta, tb;
-  int t = w0;
-  if (t < w1) load_tile(ta, ad, t, c, g);
-  while (t < w1) {
-    int tn = t + TILE;
-    if (tn < w1) load_tile(tb, ad, tn, c, g);
-    compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, c, g, limb, st);
-    t = tn;
-    if (t >= w1) break;
-    tn = t + TILE;
-    if (tn < w1) load_tile(ta, ad, tn, c, g);
-    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t, w1, qf, qs, sumq, c, g, limb, st);
-    t = tn;
+  // last tile start of the range; prefetches past it re-read that tile
+  const int tlast = w0 < w1 ? w0 + ((w1 - w0 - 1) / TILE) * TILE : w0;
+#if KVQ_PREFETCH == 1
+  TileRaw<KC, KM, VC, VM> t0r, t1r;
+  if (w0 < w1) load_tile(t0r, ad, w0, lo);
+#else
+  TileRaw<KC, KM, VC, VM> t0r, t1r, t2r;
+  if (w0 < w1) {
+    load_tile(t0r, ad, w0, lo);
+    load_tile(t1r, ad, min(w0 + TILE, tlast), lo);
   }
+#endif
+
+  // 3. query fragments (wait for the query loads only)
+  float qv[32];
+  unpack_q(qr, 32, a.in_bf16, qv);
+  if (KCH) {
+    float cv[32];
+    unpack_q(cr, 32, 0, cv);
+#pragma unroll
+    for (int n = 0; n < 32; ++n) qv[n] *= cv[n];  // per-channel key scale moved onto the query
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(qv[n]));
+  float inv;
+  const float sc = q_norm_scale(rows_max(amax), &inv);
+  const float qs = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128)
+  float qsum = 0.0f;
+  half8 qf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      _Float16 hv[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = 2 * pp + k;
+        const int n = 8 * j + (KB8 ? e : (e >> 1) + ((e & 1) << 2));
+        const float x = qv[n] * sc;
+        qsum += x;
+        const _Float16 hi = (_Float16)x;
+        hv[k] = limb ? (_Float16)(x - (float)hi) : hi;
+      }
+      w[pp] = pack_h2(hv[0], hv[1]);
+    }
+    qf[j] = as_h8(w[0], w[1], w[2], w[3]);
+  }
+  const float sumq = Meta<KM>::ZP ? rows_sum(qsum) : 0.0f;
+
+  // 4. stream the range with the next tile(s) in flight
+  NibbleMasks nm;
+  nm.init();
+  Softmax st;
+  st.init(__uint_as_float(0x00800000u));  // 2^-126
+  int t = w0;
+#if KVQ_PREFETCH == 1
+  while (t < w1) {
+    load_tile(t1r, ad, min(t + TILE, tlast), lo);
+    compute_tile<KC, KM, KCH, VC, VM, G>(t0r, t, w1, qf, qs, sumq, g, limb, nm, st);
+    t += TILE;
+    if (t >= w1) break;
+    load_tile(t0r, ad, min(t + TILE, tlast), lo);
+    compute_tile<KC, KM, KCH, VC, VM, G>(t1r, t, w1, qf, qs, sumq, g, limb, nm, st);
+    t += TILE;
+  }
+#else
+  while (t < w1) {
+    load_tile(t2r, ad, min(t + 2 * TILE, tlast), lo);
+    compute_tile<KC, KM, KCH, VC, VM, G>(t0r, t, w1, qf, qs, sumq, g, limb, nm, st);
+    t += TILE;
+    if (t >= w1) break;
+    load_tile(t0r, ad, min(t + 2 * TILE, tlast), lo);
+    compute_tile<KC, KM, KCH, VC, VM, G>(t1r, t, w1, qf, qs, sumq, g, limb, nm, st);
+    t += TILE;
+    if (t >= w1) break;
+    load_tile(t1r, ad, min(t + 2 * TILE, tlast), lo);
+    compute_tile<KC, KM, KCH, VC, VM, G>(t2r, t, w1, qf, qs, sumq, g, limb, nm, st);
+    t += TILE;
+  }
+#endif
   float scale_out;
   if (VM == MK_U8)
     scale_out = 256.0f * a.v_super[(size_t)b * a.hkv + h];
@@ -780,28 +922,57 @@ __global__ void __launch_bounds__(64) decode_combine(DecodeArgs a) {
   const SeqInfo si = seq_info(a, b);
   const int ns = (si.nq + a.split_tokens - 1) / a.split_tokens;
   const bool overflow = ns > a.n_split;  // longer than the launch was planned for
+  const int nq_used = overflow ? a.n_split : ns;
   const size_t row0 = ((size_t)b * a.hq + hq) * a.nsp;
-  auto valid = [&](int j) { return j < a.n_split ? j < ns : si.nw > 0; };
+  const bool win = si.nw > 0;
   float M = NEG_INF;
-  for (int j = lane; j < a.nsp; j += 64)
-    if (valid(j)) M = fmaxf(M, a.part_ml[2 * (row0 + j)]);
+  for (int j = lane; j < nq_used; j += 64) M = fmaxf(M, a.part_ml[2 * (row0 + j)]);
+  float mw = NEG_INF, lw = 0.0f;
+  if (win) {
+    mw = a.part_ml[2 * (row0 + a.n_split)];
+    lw = a.part_ml[2 * (row0 + a.n_split) + 1];
+    M = fmaxf(M, mw);
+  }
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float ws = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int j = 0; j < a.nsp; ++j) {
-    if (!valid(j)) continue;
-    const float m = a.part_ml[2 * (row0 + j)], l = a.part_ml[2 * (row0 + j) + 1];
-    const float e = l > 0.0f ? l * exp2_fast(m - M) : 0.0f;
-    const float2 v = *(const float2*)(a.part_o + (row0 + j) * D + 2 * lane);
+  float ws = 0.0f;
+  float2 acc = {0.0f, 0.0f};
+  for (int j0 = 0; j0 < nq_used; j0 += 64) {
+    const int j = j0 + lane;
+    float e = 0.0f;
+    if (j < nq_used) {
+      const float m = a.part_ml[2 * (row0 + j)], l = a.part_ml[2 * (row0 + j) + 1];
+      e = l > 0.0f ? l * exp2_fast(m - M) : 0.0f;
+    }
     ws += e;
-    o0 += e * v.x;
-    o1 += e * v.y;
+    const int cnt = min(64, nq_used - j0);
+    const float2* po = (const float2*)(a.part_o + (row0 + j0) * D) + lane;
+    for (int k0 = 0; k0 < cnt; k0 += 8) {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int k = k0 + kk;
+        if (k < cnt) {
+          const float ek = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), k));
+          const float2 v = po[(size_t)k * (D / 2)];
+          acc.x += ek * v.x;
+          acc.y += ek * v.y;
+        }
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+  if (win) {
+    const float e = lw > 0.0f ? lw * exp2_fast(mw - M) : 0.0f;
+    const float2 v = *((const float2*)(a.part_o + (row0 + a.n_split) * D) + lane);
+    ws += e;
+    acc.x += e * v.x;
+    acc.y += e * v.y;
   }
   float2 r;
   if (overflow) {
     r.x = r.y = __builtin_nanf("");
   } else if (ws > 0.0f) {
-    r.x = o0 / ws;
-    r.y = o1 / ws;
+    r.x = acc.x / ws;
+    r.y = acc.y / ws;
   } else {
     r.x = r.y = 0.0f;
   }

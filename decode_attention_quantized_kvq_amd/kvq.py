@@ -18,7 +18,9 @@ from typing import Optional, Sequence
 
 import torch  # first: libkvq then binds to the HIP runtime torch loaded
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+# KVQ_LIB names another build of the library (for A/B comparisons of builds)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libkvq.so")
 
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = range(5)
 AXIS = {"token": 0, "channel": 1}
