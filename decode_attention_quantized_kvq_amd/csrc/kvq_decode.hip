@@ -11,7 +11,7 @@
 // multiplies each score once after it, and a per-channel key scale is moved
 // onto the query.
 //
-// Kernel 1 (decode_split): one workgroup of 4 waves per (token split, KV
+// decode_split: one workgroup of 4 waves per (token split, KV
 // head, sequence).  Each wave streams 32-token tiles of its quarter of the
 // split straight from HBM into registers (coalesced 64/128-byte rows, the next
 // tile's loads in flight while the current one computes), converts codes to
@@ -23,10 +23,13 @@
 // used by all G heads and both products are exact to about 2^-22.  Online
 // softmax runs in base 2.  The 4 waves merge through LDS and the workgroup
 // writes one partial (max, sum, normalized output) per query head.
-// Kernel 2 (decode_combine): log-sum-exp combine of the partials of each
-// (sequence, query head) into the fp32 output.
+// decode_combine: log-sum-exp combine of the partials of each (sequence,
+// query head) into the fp32 output.
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "kvq_internal.h"
 
@@ -35,15 +38,11 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// Tiles in flight ahead of the one being computed (1 or 2).
-#ifndef KVQ_PREFETCH
-#define KVQ_PREFETCH 1
-#endif
 
 constexpr int D = 128;
 constexpr int WAVES = 4;
@@ -100,14 +99,23 @@ __device__ inline float ror_g(float v) {
       0, __builtin_bit_cast(int, v), 0x120 + G, 0xF, 0xF, false));
 }
 
+// Reductions over the four 16-lane rows (lanes c, c+16, c+32, c+48).  A
+// self-swap with v_permlane32_swap gives each lane its partner 32 lanes away
+// in one of the two results (the other keeps its own value), so combining
+// both results reduces lane pairs; v_permlane16_swap does the same for rows
+// (0,1) and (2,3).  VALU only, no LDS crossbar.
 __device__ inline float rows_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ inline float rows_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Smallest power of two >= x (x >= 0 finite); 0 stays 0.
@@ -136,6 +144,36 @@ __device__ inline void cvt_b8(uint32_t w, uint32_t& p01, uint32_t& p23) {
   if (SIGNED) w ^= 0x80808080u;
   p01 = h2_add(perm(0x64646464u, w, 0x04010400u), SIGNED ? H_M1152 : H_M1024);
   p23 = h2_add(perm(0x64646464u, w, 0x04030402u), SIGNED ? H_M1152 : H_M1024);
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time
+// indices, needed by instructions that encode a byte or lane selector).
+template <typename F, int... I>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// fp16 pair (byte BA of a, byte BB of b) of 8-bit codes, one instruction per
+// code: SDWA selects the byte (sign-extended when S) and the half it writes.
+template <bool S, int BA, int BB>
+__device__ inline uint32_t cvt_pair_b8(uint32_t a, uint32_t b) {
+  uint32_t r;
+  if (S) {
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%2"
+        : "=v"(r) : "v"(a), "n"(BA));
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%2"
+        : "+v"(r) : "v"(b), "n"(BB));
+  } else {
+    asm("v_cvt_f16_u16_sdwa %0, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%2"
+        : "=v"(r) : "v"(a), "n"(BA));
+    asm("v_cvt_f16_u16_sdwa %0, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%2"
+        : "+v"(r) : "v"(b), "n"(BB));
+  }
+  return r;
 }
 
 // A constant held in a VGPR.  VOP3 instructions of gfx9 cannot encode a
@@ -303,23 +341,34 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int
   }
 }
 
-// Key operand of the j-th score MFMA for block bb.
-template <int KC, int KM, int VC, int VM>
-__device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, int j,
-                                 const NibbleMasks& nm) {
+// Key operand of the J-th score MFMA for block bb.
+template <int J, int KC, int KM, int VC, int VM>
+__device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, const NibbleMasks& nm) {
   constexpr bool S = Codes<KC>::SIGNED;
-  if (Codes<KC>::B8) {
-    const u32x4 r = t.k[bb][j >> 1];
-    const uint32_t w0 = (j & 1) ? r.z : r.x, w1 = (j & 1) ? r.w : r.y;
-    uint32_t a, b, c, d;
-    cvt_b8<S>(w0, a, b);
-    cvt_b8<S>(w1, c, d);
-    return as_h8(a, b, c, d);
+  if constexpr (Codes<KC>::B8) {
+    const u32x4 r = t.k[bb][J >> 1];
+    const uint32_t w0 = (J & 1) ? r.z : r.x, w1 = (J & 1) ? r.w : r.y;
+    return as_h8(cvt_pair_b8<S, 0, 1>(w0, w0), cvt_pair_b8<S, 2, 3>(w0, w0),
+                 cvt_pair_b8<S, 0, 1>(w1, w1), cvt_pair_b8<S, 2, 3>(w1, w1));
   } else {
     uint32_t o[4];
-    cvt_b4<S>(t.k[bb][0][j], o, nm);
+    cvt_b4<S>(t.k[bb][0][J], o, nm);
     return as_h8(o[0], o[1], o[2], o[3]);
   }
+}
+
+// Value operand of the J-th output MFMA for 8-bit codes: feature 8c + J of
+// the lane's 8 tokens, tokens (2pp, 2pp+1) in pair pp.
+template <int J, int KC, int KM, int VC, int VM>
+__device__ inline half8 value_frag_b8(const TileRaw<KC, KM, VC, VM>& t) {
+  constexpr bool S = Codes<VC>::SIGNED;
+  uint32_t pr[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const u32x2 A = t.v8[2 * pp], B = t.v8[2 * pp + 1];
+    pr[pp] = cvt_pair_b8<S, J & 3, J & 3>(J < 4 ? A.x : A.y, J < 4 ? B.x : B.y);
+  }
+  return as_h8(pr[0], pr[1], pr[2], pr[3]);
 }
 
 // Value operands of the 8 output MFMAs: lane (c, g) gives feature 8c + j of
@@ -398,41 +447,48 @@ struct Softmax {
 template <int KC, int KM, bool KCH, int VC, int VM, int G>
 __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, int tend,
                                     const half8 qf[4], float qs, float sumq, int g,
-                                    int limb, const NibbleMasks& nm, Softmax& st) {
+                                    float limbf, const NibbleMasks& nm, Softmax& st) {
   // scores
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag(t, 0, j, nm), qf[j], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag(t, 1, j, nm), qf[j], s1, 0, 0, 0);
-  }
-  float s[8], vs[8], vz[8];
+  static_for<4>([&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag<J>(t, 0, nm), qf[J], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag<J>(t, 1, nm), qf[J], s1, 0, 0, 0);
+  });
+  // sk: score before the query scale qs (> 0), so max and exp fold qs in
+  float sk[8], vs[8], vz[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int bb = e >> 2, i = e & 3;
     const float raw0 = bb ? s1[i] : s0[i];
     const float raw = raw0 + ror_g<G>(raw0);  // high + low half of the query
-    const bool valid = t0 + 16 * bb + 4 * g + i < tend;
-    float v;
     if (KCH) {
-      v = raw * qs;
+      sk[e] = raw;
     } else {
       const float ks = t.km[bb].scale(i);
-      v = (Meta<KM>::ZP ? (raw - t.km[bb].zero(i) * sumq) : raw) * (ks * qs);
+      sk[e] = (Meta<KM>::ZP ? (raw - t.km[bb].zero(i) * sumq) : raw) * ks;
     }
-    s[e] = valid ? v : NEG_INF;
-    vs[e] = valid ? t.vm[bb].scale(i) : 0.0f;
-    vz[e] = (Meta<VM>::ZP && valid) ? t.vm[bb].zero(i) : 0.0f;
+    vs[e] = t.vm[bb].scale(i);
+    vz[e] = Meta<VM>::ZP ? t.vm[bb].zero(i) : 0.0f;
   }
-  float mt = s[0];
+  if (t0 + TILE > tend) {  // the last tile of a range: mask tokens past its end
 #pragma unroll
-  for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[e]);
+    for (int e = 0; e < 8; ++e) {
+      const bool valid = t0 + 16 * (e >> 2) + 4 * g + (e & 3) < tend;
+      sk[e] = valid ? sk[e] : NEG_INF;
+      vs[e] = valid ? vs[e] : 0.0f;
+      vz[e] = valid ? vz[e] : 0.0f;
+    }
+  }
+  float mt = sk[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sk[e]);
   float mu;
-  float f = st.update_max(rows_max(mt), &mu);
+  float f = st.update_max(rows_max(mt) * qs, &mu);
   float p[8], lsum = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = exp2_fast(s[e] - mu);
+    p[e] = exp2_fast(fmaf(sk[e], qs, -mu));
     lsum += p[e];
   }
   st.l = st.l * f + lsum;
@@ -456,31 +512,28 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
     for (int j = 0; j < 8; ++j) st.o[j] *= f;
     st.z *= f;
   }
-  float w[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    w[e] = p[e] * (vs[e] * inv);
-    if (Meta<VM>::ZP) st.z += w[e] * vz[e];
-  }
-  // weights as fp16 high/low halves, one half per column limb
+  // weights: the high fp16 half (limb 0) or the low half (limb 1) per column
   uint32_t pw[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
-    _Float16 h[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const float x = w[2 * pp + k];
-      const _Float16 hi = (_Float16)x;
-      const _Float16 lo = (_Float16)(x - (float)hi);
-      h[k] = limb ? lo : hi;
-    }
-    pw[pp] = pack_h2(h[0], h[1]);
+    const float w0 = p[2 * pp] * (vs[2 * pp] * inv), w1 = p[2 * pp + 1] * (vs[2 * pp + 1] * inv);
+    if (Meta<VM>::ZP) st.z += w0 * vz[2 * pp] + w1 * vz[2 * pp + 1];
+    const half2v hi = __builtin_convertvector((float2v){w0, w1}, half2v);
+    const float2v rem = {fmaf(-limbf, (float)hi.x, w0), fmaf(-limbf, (float)hi.y, w1)};
+    pw[pp] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, half2v));
   }
   const half8 pf = as_h8(pw[0], pw[1], pw[2], pw[3]);
-  half8 vf[8];
-  value_frags(t, vf, nm);
+  if constexpr (Codes<VC>::B8) {
+    static_for<8>([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      st.o[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(value_frag_b8<J>(t), pf, st.o[J], 0, 0, 0);
+    });
+  } else {
+    half8 vf[8];
+    value_frags(t, vf, nm);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[j], pf, st.o[j], 0, 0, 0);
+    for (int j = 0; j < 8; ++j) st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[j], pf, st.o[j], 0, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -698,7 +751,7 @@ __device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1
+// Window split: the newest tokens, kept as bf16
 // ---------------------------------------------------------------------------
 template <int G>
 __device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G>& sh) {
@@ -781,6 +834,7 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int hh = c % G, limb = (c / G) & 1;
+  const float limbf = (float)limb;
   constexpr bool KB8 = Codes<KC>::B8;
 
   // 1. query (and per-channel key scale) loads, issued first
@@ -802,7 +856,8 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
     if (KB8) load_q_run(cr, a.k_chan, crow, run1, 16, 4, 0);
   }
 
-  // 2. the first tiles of this wave's range
+  // 2. the first two tiles of this wave's range, in flight while the query
+  //    is prepared
   Addr ad;
   ad.k = a.k_codes;
   ad.v = a.v_codes;
@@ -825,16 +880,11 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const int w1 = min(w0 + per, tok1);
   // last tile start of the range; prefetches past it re-read that tile
   const int tlast = w0 < w1 ? w0 + ((w1 - w0 - 1) / TILE) * TILE : w0;
-#if KVQ_PREFETCH == 1
-  TileRaw<KC, KM, VC, VM> t0r, t1r;
-  if (w0 < w1) load_tile(t0r, ad, w0, lo);
-#else
-  TileRaw<KC, KM, VC, VM> t0r, t1r, t2r;
+  TileRaw<KC, KM, VC, VM> ta, tb;
   if (w0 < w1) {
-    load_tile(t0r, ad, w0, lo);
-    load_tile(t1r, ad, min(w0 + TILE, tlast), lo);
+    load_tile(ta, ad, w0, lo);
+    load_tile(tb, ad, min(w0 + TILE, tlast), lo);
   }
-#endif
 
   // 3. query fragments (wait for the query loads only)
   float qv[32];
@@ -858,53 +908,37 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
     uint32_t w[4];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      _Float16 hv[2];
+      float x[2];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int e = 2 * pp + k;
         const int n = 8 * j + (KB8 ? e : (e >> 1) + ((e & 1) << 2));
-        const float x = qv[n] * sc;
-        qsum += x;
-        const _Float16 hi = (_Float16)x;
-        hv[k] = limb ? (_Float16)(x - (float)hi) : hi;
+        x[k] = qv[n] * sc;
+        qsum += x[k];
       }
-      w[pp] = pack_h2(hv[0], hv[1]);
+      const half2v hi = __builtin_convertvector((float2v){x[0], x[1]}, half2v);
+      const float2v rem = {fmaf(-limbf, (float)hi.x, x[0]), fmaf(-limbf, (float)hi.y, x[1])};
+      w[pp] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, half2v));
     }
     qf[j] = as_h8(w[0], w[1], w[2], w[3]);
   }
   const float sumq = Meta<KM>::ZP ? rows_sum(qsum) : 0.0f;
 
-  // 4. stream the range with the next tile(s) in flight
+  // 4. stream the range: compute one buffer, refill it two tiles ahead
   NibbleMasks nm;
   nm.init();
   Softmax st;
   st.init(__uint_as_float(0x00800000u));  // 2^-126
   int t = w0;
-#if KVQ_PREFETCH == 1
   while (t < w1) {
-    load_tile(t1r, ad, min(t + TILE, tlast), lo);
-    compute_tile<KC, KM, KCH, VC, VM, G>(t0r, t, w1, qf, qs, sumq, g, limb, nm, st);
+    compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, g, limbf, nm, st);
+    load_tile(ta, ad, min(t + 2 * TILE, tlast), lo);
     t += TILE;
     if (t >= w1) break;
-    load_tile(t0r, ad, min(t + TILE, tlast), lo);
-    compute_tile<KC, KM, KCH, VC, VM, G>(t1r, t, w1, qf, qs, sumq, g, limb, nm, st);
+    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t, w1, qf, qs, sumq, g, limbf, nm, st);
+    load_tile(tb, ad, min(t + 2 * TILE, tlast), lo);
     t += TILE;
   }
-#else
-  while (t < w1) {
-    load_tile(t2r, ad, min(t + 2 * TILE, tlast), lo);
-    compute_tile<KC, KM, KCH, VC, VM, G>(t0r, t, w1, qf, qs, sumq, g, limb, nm, st);
-    t += TILE;
-    if (t >= w1) break;
-    load_tile(t0r, ad, min(t + 2 * TILE, tlast), lo);
-    compute_tile<KC, KM, KCH, VC, VM, G>(t1r, t, w1, qf, qs, sumq, g, limb, nm, st);
-    t += TILE;
-    if (t >= w1) break;
-    load_tile(t1r, ad, min(t + 2 * TILE, tlast), lo);
-    compute_tile<KC, KM, KCH, VC, VM, G>(t2r, t, w1, qf, qs, sumq, g, limb, nm, st);
-    t += TILE;
-  }
-#endif
   float scale_out;
   if (VM == MK_U8)
     scale_out = 256.0f * a.v_super[(size_t)b * a.hkv + h];
@@ -915,7 +949,8 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: log-sum-exp combine of the partials of one (sequence, query head)
+// decode_combine: log-sum-exp combine of the partials of one (sequence,
+// query head)
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(64) decode_combine(DecodeArgs a) {
   const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;

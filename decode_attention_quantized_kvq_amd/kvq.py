@@ -252,6 +252,8 @@ def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
                 split_tokens: int = 0, stream=None, split_events=None) -> torch.Tensor:
     """kvq_decode_attn: q [B][Hq][D] -> out [B][Hq][D] fp32.
 
+    workspace: scratch of decode_workspace_bytes() bytes; one is allocated
+    per call when omitted.
     split_events: optional (begin, end) torch.cuda.Event pair recorded around
     the split kernel (already created, e.g. by one record() call)."""
     cfg = cache.cfg

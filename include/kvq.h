@@ -236,10 +236,15 @@ typedef struct {
  *  out: device [batch][num_q_heads][head_dim] fp32.  A sequence with no
  *       tokens gets zeros.
  *  workspace: device scratch of at least
- *       kvq_decode_workspace_bytes(cfg, max_seq_len) bytes, 256-byte aligned.
+ *       kvq_decode_workspace_bytes(cfg, max_seq_len) bytes, 256-byte aligned,
+ *       owned by the caller; its contents need no initialisation.  Calls
+ *       that overlap in time must not share a workspace.
  *  max_seq_len: host upper bound of seq_lens (plans the split of the tokens
- *       over workgroups).
- *  Launches a split kernel and a log-sum-exp combine kernel on stream. */
+ *       over workgroups).  A sequence longer than max_seq_len gets NaN.
+ *  Launches two kernels on stream: a split kernel, whose workgroups each
+ *  attend over one split of a sequence's tokens for the G query heads of
+ *  one KV head, and a log-sum-exp combine of the splits (P2, "Decode
+ *  kernels are split-T and memory bound"). */
 kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, int layer,
                            const void* q, float* out, void* workspace, size_t workspace_bytes,
                            int max_seq_len, void* stream);

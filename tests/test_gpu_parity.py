@@ -167,3 +167,21 @@ def test_multi_layer_isolation():
         oc = O.OracleCache(1, 8, 128, O.TensorFormat(8), O.TensorFormat(8))
         oc.append(0, ks[layer][0][0], ks[layer][1][0])
         H.check_close(out[0].astype(np.float64), oc.attend(0, q[0]), f"layer {layer}")
+
+
+def test_workspace_reuse():
+    """One workspace serves consecutive calls with different queries, and the
+    outputs equal those of calls with a fresh workspace."""
+    H.log("case: workspace reuse")
+    wl = synth.workload(4, batch=3, tokens=1024)  # paged, with a bf16 window
+    lens = [1000, 0, 333]
+    bt = H.build(wl, lens, decode_steps=2, oracle=False)
+    split, max_len = 128, 1024
+    need = K.decode_workspace_bytes(bt.cfg, max_len, split)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN patterns
+    for step in (0, 1, 0, 2):
+        q = H.to_device(H.queries(wl, step), wl["in_dtype"])
+        got = K.decode_attn(bt.cache, 0, q, max_len, workspace=ws, split_tokens=split)
+        fresh = K.decode_attn(bt.cache, 0, q, max_len, split_tokens=split)
+        torch.cuda.synchronize()
+        assert torch.equal(got, fresh), f"step {step}: reused workspace changed the output"
