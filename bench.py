@@ -12,7 +12,10 @@ Infinity Cache cannot hold the working set.
 Prints one JSON line: metric, value (effective KV GB/s = algorithmic cache
 bytes per step / time per step), ms_per_step, roofline of the split kernel
 (algorithmic bytes per launch / its average duration, measured with HIP
-events around that kernel on its stream) and the CPU oracle baseline.
+events around that kernel on its stream; HBM traffic per launch from the
+committed rocprofv3 counter summary when it matches the kernel sources), a
+warm single-replica step time, the decode-append time for one token per
+sequence, and the CPU oracle baseline.
 
   python bench.py [--config 2] [--steps 200] [--warmup 20]
   python bench.py --copy-probe 1073741824   (plain copy kernel, for counters)
@@ -148,6 +151,7 @@ def cpu_baseline(wl, lens, seconds: float):
     return {
         "value": round(total_bytes / step_s / 1e9, 3), "unit": "GB/s",
         "us_per_step": round(step_s * 1e6, 1), "cores": threads, "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": f"{n_groups} of {len(groups)} (sequence, KV head) groups of the same workload, "
                   f"{done_tokens} tokens, {elapsed:.1f} s of fp64 dequantize-then-attend, "
                   f"scaled by bytes to one full step",
@@ -155,16 +159,37 @@ def cpu_baseline(wl, lens, seconds: float):
 
 
 def load_traffic(kernel: str, workload: str, sha: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
-    when they were taken on other kernel sources."""
-    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    profiles/<kernel>_<workload>_counters.md (its `key: value` lines), or None
+    when it is missing or was taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        d = json.load(f)
-    if d.get("source_sha") != sha:
+        for line in f:
+            if ":" in line and not line.startswith(("|", "#", " ", "`")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha") != sha or "hbm_bytes_per_launch" not in fields:
         return None
-    return int(d["hbm_bytes_per_launch"])
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def percentile(xs, p):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(p / 100.0 * (len(xs) - 1)))))]
 
 
 def main():
@@ -231,8 +256,32 @@ def main():
     for i in range(args.steps):
         step(i, pairs[i])
     torch.cuda.synchronize()
-    split_ms = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
+    split_each = [a.elapsed_time(b) for a, b in pairs]
+    split_ms = sum(split_each) / args.steps
     log(f"[bench] split kernel: {split_ms * 1e3:.2f} us/launch")
+
+    # warm: the same replica every step (working set may sit in the 256 MB
+    # Infinity Cache; context only)
+    e0.record()
+    for i in range(args.steps):
+        step(0)
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / args.steps
+
+    # decode-append: one new token per sequence (rewrites each sequence's
+    # last position of replica 0, after all timing that reads it)
+    k1, v1 = (torch.randn((wl["batch"], wl["hkv"], 1, wl["d"]), device="cuda").to(q.dtype)
+              for _ in range(2))
+    ones = torch.ones(wl["batch"], dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        K.quantize_append(caches[0], 0, k1, v1, ones)
+    e0.record()
+    for _ in range(20):
+        K.quantize_append(caches[0], 0, k1, v1, ones)
+    e1.record()
+    torch.cuda.synchronize()
+    append_us = e0.elapsed_time(e1) / 20 * 1e3
 
     value = traffic / (ms_step * 1e-3) / 1e9
     achieved = traffic / (split_ms * 1e-3) / 1e9
@@ -263,7 +312,11 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": hbm, "kernel": "decode_split",
                      "algorithmic_bytes_per_launch": traffic,
-                     "avg_launch_us": round(split_ms * 1e3, 2)},
+                     "avg_launch_us": round(split_ms * 1e3, 2),
+                     "launch_us_p10_p50_p90": [round(percentile(split_each, p) * 1e3, 2)
+                                               for p in (10, 50, 90)]},
+        "warm_us_per_step": round(warm_ms * 1e3, 2),
+        "decode_append_us": round(append_us, 2),
     }
     if not args.no_cpu:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")

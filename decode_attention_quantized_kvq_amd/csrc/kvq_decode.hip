@@ -157,24 +157,40 @@ __device__ inline void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// fp16 pair (byte BA of a, byte BB of b) of 8-bit codes, one instruction per
-// code: SDWA selects the byte (sign-extended when S) and the half it writes.
-template <bool S, int BA, int BB>
-__device__ inline uint32_t cvt_pair_b8(uint32_t a, uint32_t b) {
-  uint32_t r;
-  if (S) {
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%2"
-        : "=v"(r) : "v"(a), "n"(BA));
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%2"
-        : "+v"(r) : "v"(b), "n"(BB));
-  } else {
-    asm("v_cvt_f16_u16_sdwa %0, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%2"
-        : "=v"(r) : "v"(a), "n"(BA));
-    asm("v_cvt_f16_u16_sdwa %0, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%2"
-        : "+v"(r) : "v"(b), "n"(BB));
-  }
-  return r;
+// Four fp16 pairs of 8-bit codes, one instruction per code: pair i is
+// (byte A_i of a_i, byte B_i of b_i); SDWA selects the byte (sign-extended
+// when S) and the half-word it writes.  The conversions sit in inline asm,
+// which the compiler's hazard recognizer does not count as VALU, so it would
+// not keep the two wait states an MFMA needs before reading a VGPR that a
+// VALU instruction wrote: the block ends with them (s_nop 1) itself.
+#define KVQ_CVT8(OP, SO, SC)                                                                  \
+  OP " %0, " SO "%4" SC " dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%12\n\t"         \
+  OP " %1, " SO "%6" SC " dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%14\n\t"         \
+  OP " %2, " SO "%8" SC " dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%16\n\t"         \
+  OP " %3, " SO "%10" SC " dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%18\n\t"        \
+  OP " %0, " SO "%5" SC " dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%13\n\t"    \
+  OP " %1, " SO "%7" SC " dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%15\n\t"    \
+  OP " %2, " SO "%9" SC " dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%17\n\t"    \
+  OP " %3, " SO "%11" SC " dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%19\n\t"   \
+  "s_nop 1"
+
+template <bool S, int A0, int B0, int A1, int B1, int A2, int B2, int A3, int B3>
+__device__ inline half8 cvt_pairs_b8(uint32_t a0, uint32_t b0, uint32_t a1, uint32_t b1,
+                                     uint32_t a2, uint32_t b2, uint32_t a3, uint32_t b3) {
+  uint32_t r0, r1, r2, r3;
+  if constexpr (S)
+    asm(KVQ_CVT8("v_cvt_f16_i16_sdwa", "sext(", ")")
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3),
+          "n"(A0), "n"(B0), "n"(A1), "n"(B1), "n"(A2), "n"(B2), "n"(A3), "n"(B3));
+  else
+    asm(KVQ_CVT8("v_cvt_f16_u16_sdwa", "", "")
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3),
+          "n"(A0), "n"(B0), "n"(A1), "n"(B1), "n"(A2), "n"(B2), "n"(A3), "n"(B3));
+  return as_h8(r0, r1, r2, r3);
 }
+#undef KVQ_CVT8
 
 // A constant held in a VGPR.  VOP3 instructions of gfx9 cannot encode a
 // literal, so (w & mask) | magic with literal operands costs two
@@ -348,8 +364,7 @@ __device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, const
   if constexpr (Codes<KC>::B8) {
     const u32x4 r = t.k[bb][J >> 1];
     const uint32_t w0 = (J & 1) ? r.z : r.x, w1 = (J & 1) ? r.w : r.y;
-    return as_h8(cvt_pair_b8<S, 0, 1>(w0, w0), cvt_pair_b8<S, 2, 3>(w0, w0),
-                 cvt_pair_b8<S, 0, 1>(w1, w1), cvt_pair_b8<S, 2, 3>(w1, w1));
+    return cvt_pairs_b8<S, 0, 1, 2, 3, 0, 1, 2, 3>(w0, w0, w0, w0, w1, w1, w1, w1);
   } else {
     uint32_t o[4];
     cvt_b4<S>(t.k[bb][0][J], o, nm);
@@ -362,13 +377,15 @@ __device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, const
 template <int J, int KC, int KM, int VC, int VM>
 __device__ inline half8 value_frag_b8(const TileRaw<KC, KM, VC, VM>& t) {
   constexpr bool S = Codes<VC>::SIGNED;
-  uint32_t pr[4];
+  constexpr int BY = J & 3;
+  uint32_t a[4], b[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
-    const u32x2 A = t.v8[2 * pp], B = t.v8[2 * pp + 1];
-    pr[pp] = cvt_pair_b8<S, J & 3, J & 3>(J < 4 ? A.x : A.y, J < 4 ? B.x : B.y);
+    a[pp] = J < 4 ? t.v8[2 * pp].x : t.v8[2 * pp].y;
+    b[pp] = J < 4 ? t.v8[2 * pp + 1].x : t.v8[2 * pp + 1].y;
   }
-  return as_h8(pr[0], pr[1], pr[2], pr[3]);
+  return cvt_pairs_b8<S, BY, BY, BY, BY, BY, BY, BY, BY>(a[0], b[0], a[1], b[1], a[2], b[2],
+                                                         a[3], b[3]);
 }
 
 // Value operands of the 8 output MFMAs: lane (c, g) gives feature 8c + j of
@@ -878,13 +895,9 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const int per = a.split_tokens / WAVES;
   const int w0 = tok0 + wave * per;
   const int w1 = min(w0 + per, tok1);
-  // last tile start of the range; prefetches past it re-read that tile
-  const int tlast = w0 < w1 ? w0 + ((w1 - w0 - 1) / TILE) * TILE : w0;
   TileRaw<KC, KM, VC, VM> ta, tb;
-  if (w0 < w1) {
-    load_tile(ta, ad, w0, lo);
-    load_tile(tb, ad, min(w0 + TILE, tlast), lo);
-  }
+  if (w0 < w1) load_tile(ta, ad, w0, lo);
+  if (w0 + TILE < w1) load_tile(tb, ad, w0 + TILE, lo);
 
   // 3. query fragments (wait for the query loads only)
   float qv[32];
@@ -929,14 +942,15 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   nm.init();
   Softmax st;
   st.init(__uint_as_float(0x00800000u));  // 2^-126
+  // (t and w1 are wave-uniform: the refill branches are scalar)
   int t = w0;
   while (t < w1) {
     compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, g, limbf, nm, st);
-    load_tile(ta, ad, min(t + 2 * TILE, tlast), lo);
+    if (t + 2 * TILE < w1) load_tile(ta, ad, t + 2 * TILE, lo);
     t += TILE;
     if (t >= w1) break;
     compute_tile<KC, KM, KCH, VC, VM, G>(tb, t, w1, qf, qs, sumq, g, limbf, nm, st);
-    load_tile(tb, ad, min(t + 2 * TILE, tlast), lo);
+    if (t + 2 * TILE < w1) load_tile(tb, ad, t + 2 * TILE, lo);
     t += TILE;
   }
   float scale_out;
