@@ -257,6 +257,20 @@ struct Meta {
       r0 = u32x4{*(const uint32_t*)p, 0u, 0u, 0u};
     }
   }
+  // the same bytes through a buffer resource, at byte offset off
+  __device__ inline void load_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    if (MK == MK_F32 || MK == MK_F16Z) {
+      r0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    } else if (MK == MK_F32Z) {
+      r0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      r1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+    } else if (MK == MK_F16) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+      r0 = u32x4{v.x, v.y, 0u, 0u};
+    } else if (MK == MK_U8) {
+      r0 = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0), 0u, 0u, 0u};
+    }
+  }
   // scale (and zero point) of token i in 0..3
   __device__ inline float scale(int i) const {
     if (MK == MK_F32) return __uint_as_float(r0[i]);
@@ -284,23 +298,41 @@ struct Addr {
   const uint8_t* v;
   const uint8_t* km;
   const uint8_t* vm;
-  const int32_t* table;  // paged: row of the block table, else nullptr
+  const int32_t* table;  // paged: row of the block table
   int num_blocks, hkv, h;
   size_t head_tok;       // contiguous: first token slot of this head
   int nblk;              // blocks holding tokens
-
-  // token slot index of block `blk` (clamped to the blocks holding tokens);
-  // wave-uniform
-  __device__ inline size_t block_slot(int blk) const {
-    blk = blk < nblk ? blk : nblk - 1;
-    if (table) {
-      int phys = table[blk];
-      phys = phys < 0 ? 0 : (phys >= num_blocks ? num_blocks - 1 : phys);
-      return ((size_t)phys * hkv + h) * 16;
-    }
-    return head_tok + (size_t)blk * 16;
-  }
 };
+
+// Token slot index of block `blk` (clamped to the blocks holding tokens and,
+// when paged, to the pool); wave-uniform.
+template <bool PAGED>
+__device__ inline size_t block_slot(const Addr& ad, int blk) {
+  blk = blk < ad.nblk ? blk : ad.nblk - 1;
+  if constexpr (PAGED) {
+    int phys = ad.table[blk];
+    phys = phys < 0 ? 0 : (phys >= ad.num_blocks ? ad.num_blocks - 1 : phys);
+    return ((size_t)phys * ad.hkv + ad.h) * 16;
+  } else {
+    return ad.head_tok + (size_t)blk * 16;
+  }
+}
+
+// Descriptor word 3 of a raw (byte-addressed, unswizzled) buffer resource.
+constexpr int RSRC_WORD3 = 0x00020000;
+
+// Buffer resource over `bytes` bytes at p.  A resource of 0 bytes makes every
+// load through it out of range: it returns zeros and reads no memory.  The
+// arguments are wave-uniform; readfirstlane says so to the compiler, which
+// would otherwise wrap each load in a loop over distinct descriptors.
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const uint8_t* p, int bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint8_t* q = (const uint8_t*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)q, 0, __builtin_amdgcn_readfirstlane(bytes),
+                                           RSRC_WORD3);
+}
 
 // Byte offsets of this lane's data inside a 16-token block; fixed for the
 // whole kernel, so every load is a wave-uniform base plus a 32-bit offset.
@@ -334,26 +366,35 @@ struct TileRaw {
   Meta<VM> vm[2];
 };
 
-template <int KC, int KM, int VC, int VM>
-__device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int t0,
+// Loads the 32-token tile at t0 of a wave whose range ends at tend.  Every
+// load is issued whatever t0 is, so the wait counts the compiler derives stay
+// exact; a 16-token block at or past tend is read through an empty resource
+// (zeros, no memory traffic) and its tokens are masked by compute_tile.
+template <bool PAGED, int KC, int KM, int VC, int VM>
+__device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int t0, int tend,
                                  const LaneOff& o) {
   constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    const size_t slot = ad.block_slot((t0 >> 4) + bb);
-    const uint8_t* kb = ad.k + slot * KROW;
-    t.k[bb][0] = *(const u32x4*)(kb + o.k0);
-    if (Codes<KC>::B8) t.k[bb][1] = *(const u32x4*)(kb + o.k1);
-    const uint8_t* vb = ad.v + slot * VROW;
+    const bool live = t0 + 16 * bb < tend;
+    const size_t slot = block_slot<PAGED>(ad, (t0 >> 4) + bb);
+    const auto rk = rsrc(ad.k + slot * KROW, live ? 16 * KROW : 0);
+    t.k[bb][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k0, 0, 0);
+    if (Codes<KC>::B8) t.k[bb][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k1, 0, 0);
+    const auto rv = rsrc(ad.v + slot * VROW, live ? 16 * VROW : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (Codes<VC>::B8)
-        t.v8[4 * bb + i] = *(const u32x2*)(vb + o.v[i]);
+        t.v8[4 * bb + i] = __builtin_amdgcn_raw_buffer_load_b64(rv, o.v[i], 0, 0);
       else
-        t.v4[4 * bb + i] = *(const uint32_t*)(vb + o.v[i]);
+        t.v4[4 * bb + i] = __builtin_amdgcn_raw_buffer_load_b32(rv, o.v[i], 0, 0);
     }
-    if (Meta<KM>::BYTES) t.km[bb].load(ad.km + slot * Meta<KM>::BYTES + o.km);
-    if (Meta<VM>::BYTES) t.vm[bb].load(ad.vm + slot * Meta<VM>::BYTES + o.vm);
+    if (Meta<KM>::BYTES)
+      t.km[bb].load_buf(rsrc(ad.km + slot * Meta<KM>::BYTES, live ? 16 * Meta<KM>::BYTES : 0),
+                        o.km);
+    if (Meta<VM>::BYTES)
+      t.vm[bb].load_buf(rsrc(ad.vm + slot * Meta<VM>::BYTES, live ? 16 * Meta<VM>::BYTES : 0),
+                        o.vm);
   }
 }
 
@@ -659,10 +700,11 @@ struct QRaw {
   u32x4 r[8];
 };
 
+template <bool BF16>
 __device__ inline void load_q_run(QRaw& q, const void* base, size_t row, int start, int len,
-                                  int slot, int bf16) {
+                                  int slot) {
   // bf16: len/8 vectors of 8 values; f32: len/4 vectors of 4 values
-  if (bf16) {
+  if constexpr (BF16) {
     const uint16_t* p = (const uint16_t*)base + row + start;
     for (int k = 0; k < len / 8; ++k) q.r[slot + k] = *(const u32x4*)(p + 8 * k);
   } else {
@@ -671,8 +713,9 @@ __device__ inline void load_q_run(QRaw& q, const void* base, size_t row, int sta
   }
 }
 
-__device__ inline void unpack_q(const QRaw& q, int nvals, int bf16, float* out) {
-  if (bf16) {
+template <bool BF16>
+__device__ inline void unpack_q(const QRaw& q, int nvals, float* out) {
+  if constexpr (BF16) {
     for (int k = 0; k < nvals / 8; ++k) unpack_bf16x8(q.r[k], out + 8 * k);
   } else {
     for (int k = 0; k < nvals / 4; ++k)
@@ -770,7 +813,7 @@ __device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
 // ---------------------------------------------------------------------------
 // Window split: the newest tokens, kept as bf16
 // ---------------------------------------------------------------------------
-template <int G>
+template <int G, bool QB>
 __device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G>& sh) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
@@ -781,7 +824,7 @@ __device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G
   // features 32j + 8g + e: four runs of 8
   QRaw qr;
   float qv[32];
-  if (a.in_bf16) {
+  if constexpr (QB) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) qr.r[j] = *(const u32x4*)((const uint16_t*)a.q + qrow + 32 * j + 8 * g);
 #pragma unroll
@@ -834,13 +877,13 @@ __device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G
   block_merge<G>(a, sh, b, h, a.n_split);
 }
 
-template <int KC, int KM, bool KCH, int VC, int VM, int G>
+template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB>
 __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   __shared__ Shared<G> sh;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqInfo si = seq_info(a, b);
   if (a.window && split == a.n_split) {
-    if (si.nw > 0) window_split<G>(a, b, h, si.nw, sh);
+    if (si.nw > 0) window_split<G, QB>(a, b, h, si.nw, sh);
     return;
   }
   const int tok0 = split * a.split_tokens;
@@ -862,15 +905,15 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const int run1 = 64 + 16 * g;
   QRaw qr, cr;
   if (KB8) {
-    load_q_run(qr, a.q, qrow, run0, 16, 0, a.in_bf16);
-    load_q_run(qr, a.q, qrow, run1, 16, a.in_bf16 ? 2 : 4, a.in_bf16);
+    load_q_run<QB>(qr, a.q, qrow, run0, 16, 0);
+    load_q_run<QB>(qr, a.q, qrow, run1, 16, QB ? 2 : 4);
   } else {
-    load_q_run(qr, a.q, qrow, run0, 32, 0, a.in_bf16);
+    load_q_run<QB>(qr, a.q, qrow, run0, 32, 0);
   }
   const size_t crow = ((size_t)b * a.hkv + h) * D;
   if (KCH) {
-    load_q_run(cr, a.k_chan, crow, run0, KB8 ? 16 : 32, 0, 0);
-    if (KB8) load_q_run(cr, a.k_chan, crow, run1, 16, 4, 0);
+    load_q_run<false>(cr, a.k_chan, crow, run0, KB8 ? 16 : 32, 0);
+    if (KB8) load_q_run<false>(cr, a.k_chan, crow, run1, 16, 4);
   }
 
   // 2. the first two tiles of this wave's range, in flight while the query
@@ -884,7 +927,7 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   ad.hkv = a.hkv;
   ad.h = h;
   ad.nblk = (si.nq + 15) >> 4;
-  if (a.paged) {
+  if constexpr (PAGED) {
     ad.table = a.block_table + (size_t)b * a.bt_stride;
     ad.head_tok = 0;
   } else {
@@ -893,18 +936,24 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   }
   const LaneOff lo = lane_offsets<KC, KM, VC, VM>(c, g);
   const int per = a.split_tokens / WAVES;
-  const int w0 = tok0 + wave * per;
-  const int w1 = min(w0 + per, tok1);
+  const int w0 = __builtin_amdgcn_readfirstlane(tok0 + wave * per);
+  const int w1 = __builtin_amdgcn_readfirstlane(min(w0 + per, tok1));
+  // The scheduling barriers keep each tile's loads together and in order
+  // (first tile, then second, then the refills): the compiler derives its
+  // wait counts from that order, and interleaved loads would make every wait
+  // in the loop a wait for all of them.
   TileRaw<KC, KM, VC, VM> ta, tb;
-  if (w0 < w1) load_tile(ta, ad, w0, lo);
-  if (w0 + TILE < w1) load_tile(tb, ad, w0 + TILE, lo);
+  load_tile<PAGED>(ta, ad, w0, w1, lo);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile<PAGED>(tb, ad, w0 + TILE, w1, lo);
+  __builtin_amdgcn_sched_barrier(0);
 
   // 3. query fragments (wait for the query loads only)
   float qv[32];
-  unpack_q(qr, 32, a.in_bf16, qv);
+  unpack_q<QB>(qr, 32, qv);
   if (KCH) {
     float cv[32];
-    unpack_q(cr, 32, 0, cv);
+    unpack_q<false>(cr, 32, cv);
 #pragma unroll
     for (int n = 0; n < 32; ++n) qv[n] *= cv[n];  // per-channel key scale moved onto the query
   }
@@ -942,17 +991,23 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   nm.init();
   Softmax st;
   st.init(__uint_as_float(0x00800000u));  // 2^-126
-  // (t and w1 are wave-uniform: the refill branches are scalar)
+  // Pairs of tiles, then an odd last one.  No exit in the middle of the
+  // loop body: an edge from there back to the loop head would make the
+  // compiler wait there as if only the first refill were in flight.
+  const int ntile = w1 > w0 ? (w1 - w0 + TILE - 1) / TILE : 0;
   int t = w0;
-  while (t < w1) {
+  for (int i = 0; i < (ntile >> 1); ++i) {
     compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, g, limbf, nm, st);
-    if (t + 2 * TILE < w1) load_tile(ta, ad, t + 2 * TILE, lo);
-    t += TILE;
-    if (t >= w1) break;
-    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t, w1, qf, qs, sumq, g, limbf, nm, st);
-    if (t + 2 * TILE < w1) load_tile(tb, ad, t + 2 * TILE, lo);
-    t += TILE;
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile<PAGED>(ta, ad, t + 2 * TILE, w1, lo);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t + TILE, w1, qf, qs, sumq, g, limbf, nm, st);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile<PAGED>(tb, ad, t + 3 * TILE, w1, lo);
+    __builtin_amdgcn_sched_barrier(0);
+    t += 2 * TILE;
   }
+  if (ntile & 1) compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, g, limbf, nm, st);
   float scale_out;
   if (VM == MK_U8)
     scale_out = 256.0f * a.v_super[(size_t)b * a.hkv + h];
@@ -1028,16 +1083,32 @@ __global__ void __launch_bounds__(64) decode_combine(DecodeArgs a) {
   *(float2*)(a.out + ((size_t)b * a.hq + hq) * D + 2 * lane) = r;
 }
 
+template <int KC, int KM, bool KCH, int VC, int VM, int G>
+void launch_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(256);
+  if (a.paged) {
+    if (a.in_bf16)
+      hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, G, true, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, G, true, false>), grid, block, 0, s, a);
+  } else {
+    if (a.in_bf16)
+      hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, G, false, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, G, false, false>), grid, block, 0, s, a);
+  }
+}
+
 template <int KC, int KM, bool KCH, int VC, int VM>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.nsp, a.hkv, a.batch), block(256);
+  const dim3 grid(a.nsp, a.hkv, a.batch);
   if (a.ev_begin && hipEventRecord((hipEvent_t)a.ev_begin, s) != hipSuccess) return hipErrorInvalidValue;
   if (a.nsp > 0) {
     switch (a.group) {
-      case 1: hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, 1>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, 2>), grid, block, 0, s, a); break;
-      case 4: hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, 4>), grid, block, 0, s, a); break;
-      case 8: hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, 8>), grid, block, 0, s, a); break;
+      case 1: launch_split<KC, KM, KCH, VC, VM, 1>(a, grid, s); break;
+      case 2: launch_split<KC, KM, KCH, VC, VM, 2>(a, grid, s); break;
+      case 4: launch_split<KC, KM, KCH, VC, VM, 4>(a, grid, s); break;
+      case 8: launch_split<KC, KM, KCH, VC, VM, 8>(a, grid, s); break;
       default: return hipErrorInvalidValue;
     }
     const hipError_t e = hipGetLastError();
