@@ -127,34 +127,43 @@ def cpu_baseline(wl, lens, seconds: float):
     # the same groups in the same order every run; quantization is not timed
     rng = np.random.default_rng(12345)
     order = rng.permutation(len(groups))
-    done_tokens = 0
-    done_bytes = 0
+    keep = sum(lens) * wl["hkv"] <= (1 << 20)   # small caches are built once
+    built = {}
+    done_tokens = done_bytes = n_groups = passes = 0
     elapsed = 0.0
-    n_groups = 0
-    for gi in order:
-        b, h = groups[gi]
-        n = lens[b]
-        k, v = synth.kv_tokens(wl, b, h, n)
-        cache = O.OracleCache(1, 1, wl["d"], fmt(wl["key"]), fmt(wl["value"]), wl["window"])
-        cache.append(0, k[None], v[None])
-        q = synth.queries(wl, b)[h * G:(h + 1) * G]
-        t0 = time.perf_counter()
-        cache.attend(0, q)               # dequantize + attend, fp64
-        elapsed += time.perf_counter() - t0
-        done_bytes += O.decode_traffic(fmt(wl["key"]), fmt(wl["value"]), 1, wl["d"], [n], wl["window"])
-        done_tokens += n
-        n_groups += 1
-        if elapsed >= seconds:
-            break
+    wall0 = time.perf_counter()
+    while elapsed < seconds and time.perf_counter() - wall0 < 3 * seconds:
+        for gi in order:
+            b, h = groups[gi]
+            n = lens[b]
+            if gi in built:
+                cache = built[gi]
+            else:
+                k, v = synth.kv_tokens(wl, b, h, n)
+                cache = O.OracleCache(1, 1, wl["d"], fmt(wl["key"]), fmt(wl["value"]), wl["window"])
+                cache.append(0, k[None], v[None])
+                if keep:
+                    built[gi] = cache
+            q = synth.queries(wl, b)[h * G:(h + 1) * G]
+            t0 = time.perf_counter()
+            cache.attend(0, q)               # dequantize + attend, fp64
+            elapsed += time.perf_counter() - t0
+            done_bytes += O.decode_traffic(fmt(wl["key"]), fmt(wl["value"]), 1, wl["d"], [n],
+                                           wl["window"])
+            done_tokens += n
+            n_groups += 1
+            if elapsed >= seconds:
+                break
+        passes += 1
     total_bytes = O.decode_traffic(fmt(wl["key"]), fmt(wl["value"]), wl["hkv"], wl["d"], lens, wl["window"])
     step_s = elapsed * total_bytes / done_bytes
     return {
         "value": round(total_bytes / step_s / 1e9, 3), "unit": "GB/s",
         "us_per_step": round(step_s * 1e6, 1), "cores": threads, "kind": "oracle",
         "cpu": cpu_model(),
-        "sample": f"{n_groups} of {len(groups)} (sequence, KV head) groups of the same workload, "
-                  f"{done_tokens} tokens, {elapsed:.1f} s of fp64 dequantize-then-attend, "
-                  f"scaled by bytes to one full step",
+        "sample": f"{n_groups} (sequence, KV head) group attends ({len(groups)} per step, "
+                  f"{passes} pass(es) over them), {done_tokens} tokens, {elapsed:.2f} s of fp64 "
+                  f"dequantize-then-attend, scaled by bytes to one full step",
     }
 
 

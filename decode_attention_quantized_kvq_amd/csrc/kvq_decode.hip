@@ -26,6 +26,7 @@
 // decode_combine: log-sum-exp combine of the partials of each (sequence,
 // query head) into the fp32 output.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -1083,26 +1084,37 @@ __global__ void __launch_bounds__(64) decode_combine(DecodeArgs a) {
   *(float2*)(a.out + ((size_t)b * a.hq + hq) * D + 2 * lane) = r;
 }
 
+// Launches one decode_split variant.  With events, hipExtLaunchKernel stamps
+// them with the start and end of the dispatch itself, so their difference
+// is the kernel's own duration.
+template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB>
+void launch_one(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  const auto k = decode_split<KC, KM, KCH, VC, VM, G, PAGED, QB>;
+  if (a.ev_begin)
+    hipExtLaunchKernelGGL(k, grid, dim3(256), 0, s, (hipEvent_t)a.ev_begin, (hipEvent_t)a.ev_end, 0,
+                          a);
+  else
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
+}
+
 template <int KC, int KM, bool KCH, int VC, int VM, int G>
 void launch_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  const dim3 block(256);
   if (a.paged) {
     if (a.in_bf16)
-      hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, G, true, true>), grid, block, 0, s, a);
+      launch_one<KC, KM, KCH, VC, VM, G, true, true>(a, grid, s);
     else
-      hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, G, true, false>), grid, block, 0, s, a);
+      launch_one<KC, KM, KCH, VC, VM, G, true, false>(a, grid, s);
   } else {
     if (a.in_bf16)
-      hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, G, false, true>), grid, block, 0, s, a);
+      launch_one<KC, KM, KCH, VC, VM, G, false, true>(a, grid, s);
     else
-      hipLaunchKernelGGL((decode_split<KC, KM, KCH, VC, VM, G, false, false>), grid, block, 0, s, a);
+      launch_one<KC, KM, KCH, VC, VM, G, false, false>(a, grid, s);
   }
 }
 
 template <int KC, int KM, bool KCH, int VC, int VM>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.nsp, a.hkv, a.batch);
-  if (a.ev_begin && hipEventRecord((hipEvent_t)a.ev_begin, s) != hipSuccess) return hipErrorInvalidValue;
   if (a.nsp > 0) {
     switch (a.group) {
       case 1: launch_split<KC, KM, KCH, VC, VM, 1>(a, grid, s); break;
@@ -1114,7 +1126,6 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.ev_end && hipEventRecord((hipEvent_t)a.ev_end, s) != hipSuccess) return hipErrorInvalidValue;
   hipLaunchKernelGGL(decode_combine, dim3(a.hq, a.batch), dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -312,6 +312,7 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
     return KVQ_ERR_INVALID_ARG;
   const int split = opts ? opts->split_tokens : 0;
   if (!split_ok(split)) return KVQ_ERR_INVALID_ARG;
+  if (opts && (!opts->split_begin_event != !opts->split_end_event)) return KVQ_ERR_INVALID_ARG;
   const Plan p = make_plan(cfg, max_seq_len, split);
   if (p.nsp > 0 && (!workspace || workspace_bytes < p.total)) return KVQ_ERR_WORKSPACE;
   if (workspace && ((uintptr_t)workspace & 255)) return KVQ_ERR_WORKSPACE;

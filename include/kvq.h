@@ -224,9 +224,10 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
  * the library's choice. */
 typedef struct {
   int split_tokens;         /* quantized tokens per workgroup, a multiple of 128 */
-  void* split_begin_event;  /* hipEvent_t recorded on the stream right before
-                               the split kernel, or NULL */
-  void* split_end_event;    /* hipEvent_t recorded right after it, or NULL */
+  void* split_begin_event;  /* hipEvent_t stamped with the start of the split
+                               kernel's dispatch, or NULL */
+  void* split_end_event;    /* hipEvent_t stamped with its end; both events or
+                               neither (KVQ_ERR_INVALID_ARG otherwise) */
 } kvq_decode_opts;
 
 /* Single-query decode attention of one layer over every cached token (P2,
