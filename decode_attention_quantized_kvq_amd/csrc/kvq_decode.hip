@@ -120,6 +120,22 @@ __device__ inline float rows_sum(float v) {
 }
 
 // Smallest power of two >= x (x >= 0 finite); 0 stays 0.
+// Max / sum over the 16 lanes of this lane's row (DPP rotations inside a row).
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false)));
+  return v;
+}
+__device__ inline float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
+  return v;
+}
+
 __device__ inline float pow2_ceil(float x) {
   uint32_t u = __float_as_uint(x);
   if (u & 0x007FFFFFu) u = (u & 0x7F800000u) + 0x00800000u;
@@ -158,40 +174,6 @@ __device__ inline void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Four fp16 pairs of 8-bit codes, one instruction per code: pair i is
-// (byte A_i of a_i, byte B_i of b_i); SDWA selects the byte (sign-extended
-// when S) and the half-word it writes.  The conversions sit in inline asm,
-// which the compiler's hazard recognizer does not count as VALU, so it would
-// not keep the two wait states an MFMA needs before reading a VGPR that a
-// VALU instruction wrote: the block ends with them (s_nop 1) itself.
-#define KVQ_CVT8(OP, SO, SC)                                                                  \
-  OP " %0, " SO "%4" SC " dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%12\n\t"         \
-  OP " %1, " SO "%6" SC " dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%14\n\t"         \
-  OP " %2, " SO "%8" SC " dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%16\n\t"         \
-  OP " %3, " SO "%10" SC " dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%18\n\t"        \
-  OP " %0, " SO "%5" SC " dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%13\n\t"    \
-  OP " %1, " SO "%7" SC " dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%15\n\t"    \
-  OP " %2, " SO "%9" SC " dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%17\n\t"    \
-  OP " %3, " SO "%11" SC " dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%19\n\t"   \
-  "s_nop 1"
-
-template <bool S, int A0, int B0, int A1, int B1, int A2, int B2, int A3, int B3>
-__device__ inline half8 cvt_pairs_b8(uint32_t a0, uint32_t b0, uint32_t a1, uint32_t b1,
-                                     uint32_t a2, uint32_t b2, uint32_t a3, uint32_t b3) {
-  uint32_t r0, r1, r2, r3;
-  if constexpr (S)
-    asm(KVQ_CVT8("v_cvt_f16_i16_sdwa", "sext(", ")")
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3),
-          "n"(A0), "n"(B0), "n"(A1), "n"(B1), "n"(A2), "n"(B2), "n"(A3), "n"(B3));
-  else
-    asm(KVQ_CVT8("v_cvt_f16_u16_sdwa", "", "")
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3),
-          "n"(A0), "n"(B0), "n"(A1), "n"(B1), "n"(A2), "n"(B2), "n"(A3), "n"(B3));
-  return as_h8(r0, r1, r2, r3);
-}
-#undef KVQ_CVT8
 
 // A constant held in a VGPR.  VOP3 instructions of gfx9 cannot encode a
 // literal, so (w & mask) | magic with literal operands costs two
@@ -223,15 +205,12 @@ __device__ inline void cvt_b4(uint32_t w, uint32_t out[4], const NibbleMasks& nm
   out[3] = h2_fma((w8 & nm.hi) | nm.magic, H_SIXTEENTH, SIGNED ? H_M72 : H_M64);
 }
 
-// Feature index d held by the lane of row group g at k-slot e of the j-th
-// score MFMA.  8-bit keys: the lane loads bytes [16g,16g+16) and
-// [64+16g, 80+16g) of the token row.  4-bit keys: bytes [16g, 16g+16) hold
-// features [32g, 32g+32), and cvt_b4 interleaves nibbles (0,4,1,5,2,6,3,7).
+// Feature index held by the lanes of k-group g at k-slot e of the j-th score
+// MFMA.  Both key formats cover features [32g, 32g + 32); 8-bit keys in
+// order, 4-bit keys with cvt_b4's nibble interleave (0,4,1,5,2,6,3,7).
 template <bool B8>
 __device__ inline int key_feature(int j, int g, int e) {
-  if (B8) return (j < 2 ? 16 * g + 8 * j : 64 + 16 * g + 8 * (j - 2)) + e;
-  const int p4 = (e >> 1) + ((e & 1) << 2);
-  return 32 * g + 8 * j + p4;
+  return 32 * g + 8 * j + (B8 ? e : (e >> 1) + ((e & 1) << 2));
 }
 
 // ---------------------------------------------------------------------------
@@ -242,51 +221,32 @@ struct Meta {
   static constexpr int BYTES = MK == MK_F32 ? 4 : MK == MK_F32Z ? 8 : MK == MK_F16 ? 2
                              : MK == MK_F16Z ? 4 : MK == MK_U8 ? 1 : 0;
   static constexpr bool ZP = (MK == MK_F32Z || MK == MK_F16Z);
-  u32x4 r0, r1;  // raw bytes of 4 consecutive tokens (8-byte formats use both)
+  uint32_t r0, r1;  // raw bytes of one token's metadata (r1: fp32 zero point)
 
-  // p: metadata of 4 consecutive tokens
-  __device__ inline void load(const uint8_t* p) {
-    if (MK == MK_F32 || MK == MK_F16Z) {
-      r0 = *(const u32x4*)p;
-    } else if (MK == MK_F32Z) {
-      r0 = *(const u32x4*)p;
-      r1 = *(const u32x4*)(p + 16);
-    } else if (MK == MK_F16) {
-      const u32x2 v = *(const u32x2*)p;
-      r0 = u32x4{v.x, v.y, 0u, 0u};
-    } else if (MK == MK_U8) {
-      r0 = u32x4{*(const uint32_t*)p, 0u, 0u, 0u};
-    }
-  }
-  // the same bytes through a buffer resource, at byte offset off
+  // metadata of one token through a buffer resource, at byte offset off
   __device__ inline void load_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     if (MK == MK_F32 || MK == MK_F16Z) {
-      r0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      r0 = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
     } else if (MK == MK_F32Z) {
-      r0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-      r1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
-    } else if (MK == MK_F16) {
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
-      r0 = u32x4{v.x, v.y, 0u, 0u};
+      r0 = v.x;
+      r1 = v.y;
+    } else if (MK == MK_F16) {
+      r0 = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
     } else if (MK == MK_U8) {
-      r0 = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0), 0u, 0u, 0u};
+      r0 = __builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
     }
   }
-  // scale (and zero point) of token i in 0..3
-  __device__ inline float scale(int i) const {
-    if (MK == MK_F32) return __uint_as_float(r0[i]);
-    if (MK == MK_F32Z) return __uint_as_float(i < 2 ? r0[2 * i] : r1[2 * (i - 2)]);
-    if (MK == MK_F16) {
-      const uint32_t w = r0[i >> 1];
-      return (float)__builtin_bit_cast(_Float16, (uint16_t)(i & 1 ? w >> 16 : w & 0xFFFFu));
-    }
-    if (MK == MK_F16Z) return (float)__builtin_bit_cast(_Float16, (uint16_t)(r0[i] & 0xFFFFu));
-    if (MK == MK_U8) return (float)((r0[0] >> (8 * i)) & 0xFFu);
+  __device__ inline float scale() const {
+    if (MK == MK_F32 || MK == MK_F32Z) return __uint_as_float(r0);
+    if (MK == MK_F16 || MK == MK_F16Z)
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)(r0 & 0xFFFFu));
+    if (MK == MK_U8) return (float)(r0 & 0xFFu);
     return 1.0f;
   }
-  __device__ inline float zero(int i) const {
-    if (MK == MK_F32Z) return __uint_as_float(i < 2 ? r0[2 * i + 1] : r1[2 * (i - 2) + 1]);
-    if (MK == MK_F16Z) return (float)__builtin_bit_cast(_Float16, (uint16_t)(r0[i] >> 16));
+  __device__ inline float zero() const {
+    if (MK == MK_F32Z) return __uint_as_float(r1);
+    if (MK == MK_F16Z) return (float)__builtin_bit_cast(_Float16, (uint16_t)(r0 >> 16));
     return 0.0f;
   }
 };
@@ -335,23 +295,25 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const uint8_t* p, int bytes) {
                                            RSRC_WORD3);
 }
 
-// Byte offsets of this lane's data inside a 16-token block; fixed for the
-// whole kernel, so every load is a wave-uniform base plus a 32-bit offset.
+// Byte offsets of lane (t, g) = (lane & 15, lane >> 4) inside a 16-token
+// block; fixed for the whole kernel, so every load is a wave-uniform base plus
+// a 32-bit offset.  Keys: token row t, bytes [32g, 32g + 32) (8-bit) or
+// [16g, 16g + 16) (4-bit), i.e. features [32g, 32g + 32) either way.  Values:
+// token rows 4g + i (i = 0..3), features [8t, 8t + 8).  Metadata: token t.
 struct LaneOff {
   uint32_t k0, k1, v[4], km, vm;
 };
 
 template <int KC, int KM, int VC, int VM>
-__device__ inline LaneOff lane_offsets(int c, int g) {
+__device__ inline LaneOff lane_offsets(int t, int g) {
   constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
   LaneOff o;
-  o.k0 = c * KROW + 16 * g;   // key row c
-  o.k1 = o.k0 + 64;           // 8-bit keys: second half of the row
+  o.k0 = t * KROW + (Codes<KC>::B8 ? 32 * g : 16 * g);
+  o.k1 = o.k0 + 16;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)  // value rows 4g+i, features [8c, 8c+8)
-    o.v[i] = (4 * g + i) * VROW + (Codes<VC>::B8 ? 8 * c : 4 * c);
-  o.km = 4 * g * Meta<KM>::BYTES;
-  o.vm = 4 * g * Meta<VM>::BYTES;
+  for (int i = 0; i < 4; ++i) o.v[i] = (4 * g + i) * VROW + (Codes<VC>::B8 ? 8 * t : 4 * t);
+  o.km = t * Meta<KM>::BYTES;
+  o.vm = t * Meta<VM>::BYTES;
   return o;
 }
 
@@ -405,29 +367,15 @@ __device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, const
   constexpr bool S = Codes<KC>::SIGNED;
   if constexpr (Codes<KC>::B8) {
     const u32x4 r = t.k[bb][J >> 1];
-    const uint32_t w0 = (J & 1) ? r.z : r.x, w1 = (J & 1) ? r.w : r.y;
-    return cvt_pairs_b8<S, 0, 1, 2, 3, 0, 1, 2, 3>(w0, w0, w0, w0, w1, w1, w1, w1);
+    uint32_t o[4];
+    cvt_b8<S>((J & 1) ? r.z : r.x, o[0], o[1]);
+    cvt_b8<S>((J & 1) ? r.w : r.y, o[2], o[3]);
+    return as_h8(o[0], o[1], o[2], o[3]);
   } else {
     uint32_t o[4];
     cvt_b4<S>(t.k[bb][0][J], o, nm);
     return as_h8(o[0], o[1], o[2], o[3]);
   }
-}
-
-// Value operand of the J-th output MFMA for 8-bit codes: feature 8c + J of
-// the lane's 8 tokens, tokens (2pp, 2pp+1) in pair pp.
-template <int J, int KC, int KM, int VC, int VM>
-__device__ inline half8 value_frag_b8(const TileRaw<KC, KM, VC, VM>& t) {
-  constexpr bool S = Codes<VC>::SIGNED;
-  constexpr int BY = J & 3;
-  uint32_t a[4], b[4];
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    a[pp] = J < 4 ? t.v8[2 * pp].x : t.v8[2 * pp].y;
-    b[pp] = J < 4 ? t.v8[2 * pp + 1].x : t.v8[2 * pp + 1].y;
-  }
-  return cvt_pairs_b8<S, BY, BY, BY, BY, BY, BY, BY, BY>(a[0], b[0], a[1], b[1], a[2], b[2],
-                                                         a[3], b[3]);
 }
 
 // Value operands of the 8 output MFMAs: lane (c, g) gives feature 8c + j of
@@ -502,97 +450,145 @@ struct Softmax {
   }
 };
 
+// Per-wave state of the quantized-token path.  The scores come out of the
+// matrix cores transposed (query rows x token columns), so lane (t, g) holds
+// whole scores of the HPG query heads of row group g for token t of each
+// block: HPG = 2 when G = 8, else 1 (row group g is query head g).
+template <int G>
+struct RowState {
+  static constexpr int HPG = G == 8 ? 2 : 1;
+  float m[HPG];  // reference max per head (base-2 units), uniform over the row
+  float l[HPG];  // this lane's share of the running sum of 2^(s - m)
+  float z[HPG];  // this lane's share of sum w * zero_point (zero-point values)
+  float R;       // power-of-two reference of the folded value scale
+  float invR;    // 1 / R (exact)
+  f32x4 o[8];    // O^T: rows 4g + i = (head, limb), columns = features 8t + J
+
+  __device__ inline void init(float r0) {
+#pragma unroll
+    for (int u = 0; u < HPG; ++u) {
+      m[u] = NEG_INF;
+      l[u] = 0.0f;
+      z[u] = 0.0f;
+    }
+    R = r0;
+    invR = 1.0f / r0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// Query operand row r of the score MFMAs: the query head it holds and which
+// fp16 half (limb 0 high, 1 low); rows holding no head are zero.
+template <int G>
+__device__ inline int row_head(int r) { return G == 8 ? r >> 1 : r >> 2; }
+template <int G>
+__device__ inline int row_limb(int r) { return G == 8 ? (r & 1) : (r & 3); }
+
 // Processes one 32-token tile already in registers.
+//   scores  S^T[16 rows x 16 tok] += Q'[16 rows x 32 d] K^T[32 d x 16 tok]
+//   output  O^T[16 rows x 16 d]   += P^T[16 rows x 32 tok] V[32 tok x 16 d]
+// Rows are (query head, fp16 limb) pairs.  The weights P^T go through LDS
+// (pw, this wave's region) from the score layout to the operand layout.
+// qs[u], sumq[u]: score scale and query sum of local head u.
 template <int KC, int KM, bool KCH, int VC, int VM, int G>
 __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, int tend,
-                                    const half8 qf[4], float qs, float sumq, int g,
-                                    float limbf, const NibbleMasks& nm, Softmax& st) {
-  // scores
+                                    const half8 qf[4], const float* qs, const float* sumq,
+                                    int lt, int g, uint32_t psel, const uint32_t* prd,
+                                    uint32_t* pwr, const NibbleMasks& nm, RowState<G>& st) {
+  constexpr int HPG = RowState<G>::HPG;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
   static_for<4>([&](auto jc) {
     constexpr int J = decltype(jc)::value;
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag<J>(t, 0, nm), qf[J], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_frag<J>(t, 1, nm), qf[J], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[J], key_frag<J>(t, 0, nm), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[J], key_frag<J>(t, 1, nm), s1, 0, 0, 0);
   });
-  // sk: score before the query scale qs (> 0), so max and exp fold qs in
-  float sk[8], vs[8], vz[8];
+  // scores before the query scale qs (> 0): sk[u][bb] for token t of block bb
+  float sk[HPG][2], vs[2], vz[2];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int bb = e >> 2, i = e & 3;
-    const float raw0 = bb ? s1[i] : s0[i];
-    const float raw = raw0 + ror_g<G>(raw0);  // high + low half of the query
-    if (KCH) {
-      sk[e] = raw;
-    } else {
-      const float ks = t.km[bb].scale(i);
-      sk[e] = (Meta<KM>::ZP ? (raw - t.km[bb].zero(i) * sumq) : raw) * ks;
+  for (int bb = 0; bb < 2; ++bb) {
+    const f32x4 c = bb ? s1 : s0;
+    const bool valid = t0 + 16 * bb + lt < tend;
+#pragma unroll
+    for (int u = 0; u < HPG; ++u) {
+      const float raw = c[2 * u] + c[2 * u + 1];  // high + low half of the query
+      float v;
+      if (KCH)
+        v = raw;
+      else
+        v = (Meta<KM>::ZP ? raw - t.km[bb].zero() * sumq[u] : raw) * t.km[bb].scale();
+      sk[u][bb] = valid ? v : NEG_INF;
     }
-    vs[e] = t.vm[bb].scale(i);
-    vz[e] = Meta<VM>::ZP ? t.vm[bb].zero(i) : 0.0f;
+    vs[bb] = valid ? t.vm[bb].scale() : 0.0f;
+    vz[bb] = Meta<VM>::ZP && valid ? t.vm[bb].zero() : 0.0f;
   }
-  if (t0 + TILE > tend) {  // the last tile of a range: mask tokens past its end
+  float f[HPG], p[HPG][2];
+  bool moved = false;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool valid = t0 + 16 * (e >> 2) + 4 * g + (e & 3) < tend;
-      sk[e] = valid ? sk[e] : NEG_INF;
-      vs[e] = valid ? vs[e] : 0.0f;
-      vz[e] = valid ? vz[e] : 0.0f;
+  for (int u = 0; u < HPG; ++u) {
+    const float mt = row16_max(fmaxf(sk[u][0], sk[u][1])) * qs[u];
+    f[u] = 1.0f;
+    if (mt > st.m[u] + M_SLACK) {  // move the reference max (rarely)
+      f[u] = exp2_fast(st.m[u] - mt);  // 0 when m = -inf
+      st.m[u] = mt;
+      moved = true;
     }
+    const float mu = st.m[u] == NEG_INF ? 0.0f : st.m[u];
+    p[u][0] = exp2_fast(fmaf(sk[u][0], qs[u], -mu));
+    p[u][1] = exp2_fast(fmaf(sk[u][1], qs[u], -mu));
+    st.l[u] = st.l[u] * f[u] + (p[u][0] + p[u][1]);
   }
-  float mt = sk[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sk[e]);
-  float mu;
-  float f = st.update_max(rows_max(mt) * qs, &mu);
-  float p[8], lsum = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    p[e] = exp2_fast(fmaf(sk[e], qs, -mu));
-    lsum += p[e];
-  }
-  st.l = st.l * f + lsum;
-  float inv;
-  if (VM == MK_U8) {
-    inv = 1.0f / 256.0f;
-  } else {
-    float sv = vs[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) sv = fmaxf(sv, vs[e]);
-    sv = rows_max(sv);
+  if (VM != MK_U8) {
+    // every row group sees the same tokens, so this max is wave-uniform
+    const float sv = row16_max(fmaxf(vs[0], vs[1]));
     if (sv > st.R * R_SLACK) {
       const float Rn = pow2_ceil(sv);
-      f *= st.R / Rn;
+#pragma unroll
+      for (int u = 0; u < HPG; ++u) f[u] *= st.R / Rn;
       st.R = Rn;
+      st.invR = 1.0f / Rn;
+      moved = true;
     }
-    inv = 1.0f / st.R;
   }
-  if (__any(f != 1.0f)) {
+  if (__any(moved)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) st.o[j] *= f;
-    st.z *= f;
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.o[j][i] *= f[HPG == 2 ? (i >> 1) : 0];
+#pragma unroll
+    for (int u = 0; u < HPG; ++u) st.z[u] *= f[u];
   }
-  // weights: the high fp16 half (limb 0) or the low half (limb 1) per column
-  uint32_t pw[4];
+  // weights w = p * s_V / R as fp16 (high, low) pairs into LDS: pwr[u] is
+  // this lane's (head, token) slot, 2 words: block 0, block 1
+  const float sc0 = VM == MK_U8 ? vs[0] * (1.0f / 256.0f) : vs[0] * st.invR;
+  const float sc1 = VM == MK_U8 ? vs[1] * (1.0f / 256.0f) : vs[1] * st.invR;
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    const float w0 = p[2 * pp] * (vs[2 * pp] * inv), w1 = p[2 * pp + 1] * (vs[2 * pp + 1] * inv);
-    if (Meta<VM>::ZP) st.z += w0 * vz[2 * pp] + w1 * vz[2 * pp + 1];
+  for (int u = 0; u < HPG; ++u) {
+    const float w0 = p[u][0] * sc0, w1 = p[u][1] * sc1;
+    if (Meta<VM>::ZP) st.z[u] += w0 * vz[0] + w1 * vz[1];
     const half2v hi = __builtin_convertvector((float2v){w0, w1}, half2v);
-    const float2v rem = {fmaf(-limbf, (float)hi.x, w0), fmaf(-limbf, (float)hi.y, w1)};
-    pw[pp] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, half2v));
+    const half2v lo = __builtin_convertvector((float2v){w0 - (float)hi.x, w1 - (float)hi.y}, half2v);
+    // word per block: high half in bits 0..15, low half in bits 16..31
+    const uint32_t hb = __builtin_bit_cast(uint32_t, hi), lb = __builtin_bit_cast(uint32_t, lo);
+    *(u32x2*)(pwr + 32 * u) = u32x2{perm(lb, hb, 0x05040100u), perm(lb, hb, 0x07060302u)};
   }
-  const half8 pf = as_h8(pw[0], pw[1], pw[2], pw[3]);
-  if constexpr (Codes<VC>::B8) {
-    static_for<8>([&](auto jc) {
-      constexpr int J = decltype(jc)::value;
-      st.o[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(value_frag_b8<J>(t), pf, st.o[J], 0, 0, 0);
-    });
-  } else {
-    half8 vf[8];
-    value_frags(t, vf, nm);
+  // Other lanes read these words next.  A wave's LDS instructions issue in
+  // order, but a read may start before all passes of the preceding 64-lane
+  // write have landed (runs without this wait were not repeatable): wait for
+  // the write to complete first.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // operand row r = (head, limb), k-group kg: tokens 4kg .. 4kg+3 of both
+  // blocks (k-slot e = 4 bb + i); 8 words: token-major, block-minor
+  const u32x4 A = *(const u32x4*)prd, B = *(const u32x4*)(prd + 4);
+  const uint32_t M[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+  const uint32_t pa0 = perm(M[2], M[0], psel), pa1 = perm(M[6], M[4], psel);
+  const uint32_t pa2 = perm(M[3], M[1], psel), pa3 = perm(M[7], M[5], psel);
+  const half8 pf = as_h8(pa0, pa1, pa2, pa3);
+  __builtin_amdgcn_wave_barrier();
+  half8 vf[8];
+  value_frags(t, vf, nm);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[j], pf, st.o[j], 0, 0, 0);
-  }
+  for (int j = 0; j < 8; ++j) st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf[j], st.o[j], 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -745,6 +741,8 @@ struct Shared {
   float o[WAVES][G][D];
   float m[WAVES][G];
   float l[WAVES][G];
+  // per wave: fp16 (high, low) weight pairs [head][token][block] of one tile
+  uint32_t pw[WAVES][G == 8 ? 8 : 4][16][2];
 };
 
 template <int G>
@@ -766,6 +764,30 @@ __device__ inline void wave_finish(Softmax& st, float scale_out, int c, int g, i
     if (g == 0) {
       sh.m[wave][c] = l > 0.0f ? st.m : NEG_INF;
       sh.l[wave][c] = l;
+    }
+  }
+}
+
+// Wave epilogue of the quantized-token path: lane (t, g) writes features
+// 8t + J of its row group's heads.
+template <int G>
+__device__ inline void row_finish(RowState<G>& st, float scale_out, int t, int g, int wave,
+                                  Shared<G>& sh) {
+  constexpr int HPG = RowState<G>::HPG;
+#pragma unroll
+  for (int u = 0; u < HPG; ++u) {
+    const int head = G == 8 ? 2 * g + u : g;
+    const float l = row16_sum(st.l[u]);
+    const float z = row16_sum(st.z[u]);
+    if (head < G) {
+      const float k = l > 0.0f ? scale_out / l : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        sh.o[wave][head][8 * t + j] = (st.o[j][2 * u] + st.o[j][2 * u + 1] - z) * k;
+      if (t == 0) {
+        sh.m[wave][head] = l > 0.0f ? st.m[u] : NEG_INF;
+        sh.l[wave][head] = l;
+      }
     }
   }
 }
@@ -893,29 +915,21 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15, g = lane >> 4;
-  const int hh = c % G, limb = (c / G) & 1;
-  const float limbf = (float)limb;
+  const int lt = lane & 15, g = lane >> 4;
   constexpr bool KB8 = Codes<KC>::B8;
+  constexpr int HPG = RowState<G>::HPG;
 
-  // 1. query (and per-channel key scale) loads, issued first
-  const size_t qrow = ((size_t)b * a.hq + (size_t)h * G + hh) * D;
-  // the lane's 32 key features as runs: 8-bit [16g, +16) and [64+16g, +16);
-  // 4-bit [32g, +32)
-  const int run0 = KB8 ? 16 * g : 32 * g;
-  const int run1 = 64 + 16 * g;
+  // 1. query (and per-channel key scale) loads, issued first.  Operand row
+  //    lt of the score MFMAs holds query head qh as limb ql; the lane covers
+  //    features [32g, 32g + 32) of it.
+  const int qh = row_head<G>(lt), ql = row_limb<G>(lt);
+  const bool qvalid = qh < G && ql < 2;
+  const int qhc = qh < G ? qh : G - 1;
+  const size_t qrow = ((size_t)b * a.hq + (size_t)h * G + qhc) * D;
   QRaw qr, cr;
-  if (KB8) {
-    load_q_run<QB>(qr, a.q, qrow, run0, 16, 0);
-    load_q_run<QB>(qr, a.q, qrow, run1, 16, QB ? 2 : 4);
-  } else {
-    load_q_run<QB>(qr, a.q, qrow, run0, 32, 0);
-  }
+  load_q_run<QB>(qr, a.q, qrow, 32 * g, 32, 0);
   const size_t crow = ((size_t)b * a.hkv + h) * D;
-  if (KCH) {
-    load_q_run<false>(cr, a.k_chan, crow, run0, KB8 ? 16 : 32, 0);
-    if (KB8) load_q_run<false>(cr, a.k_chan, crow, run1, 16, 4);
-  }
+  if (KCH) load_q_run<false>(cr, a.k_chan, crow, 32 * g, 32, 0);
 
   // 2. the first two tiles of this wave's range, in flight while the query
   //    is prepared
@@ -935,7 +949,7 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
     ad.table = nullptr;
     ad.head_tok = ((size_t)b * a.hkv + h) * a.max_tokens;
   }
-  const LaneOff lo = lane_offsets<KC, KM, VC, VM>(c, g);
+  const LaneOff lo = lane_offsets<KC, KM, VC, VM>(lt, g);
   const int per = a.split_tokens / WAVES;
   const int w0 = __builtin_amdgcn_readfirstlane(tok0 + wave * per);
   const int w1 = __builtin_amdgcn_readfirstlane(min(w0 + per, tok1));
@@ -962,8 +976,7 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
 #pragma unroll
   for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(qv[n]));
   float inv;
-  const float sc = q_norm_scale(rows_max(amax), &inv);
-  const float qs = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128)
+  const float sc = q_norm_scale(rows_max(amax), &inv);  // max over the row's 4 lanes
   float qsum = 0.0f;
   half8 qf[4];
 #pragma unroll
@@ -975,22 +988,45 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int e = 2 * pp + k;
-        const int n = 8 * j + (KB8 ? e : (e >> 1) + ((e & 1) << 2));
-        x[k] = qv[n] * sc;
+        x[k] = qv[key_feature<KB8>(j, 0, e)] * sc;
         qsum += x[k];
       }
       const half2v hi = __builtin_convertvector((float2v){x[0], x[1]}, half2v);
-      const float2v rem = {fmaf(-limbf, (float)hi.x, x[0]), fmaf(-limbf, (float)hi.y, x[1])};
-      w[pp] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rem, half2v));
+      const half2v lo = __builtin_convertvector((float2v){x[0] - (float)hi.x, x[1] - (float)hi.y}, half2v);
+      const uint32_t v = __builtin_bit_cast(uint32_t, ql == 0 ? hi : lo);
+      w[pp] = qvalid ? v : 0u;
     }
     qf[j] = as_h8(w[0], w[1], w[2], w[3]);
   }
-  const float sumq = Meta<KM>::ZP ? rows_sum(qsum) : 0.0f;
+  // score scale and query sum of each head, from the lanes of its limb-0 row,
+  // to the lanes that score that head
+  const float qs_row = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128)
+  const float sumq_row = Meta<KM>::ZP ? rows_sum(qsum) : 0.0f;
+  float qs[HPG], sumq[HPG];
+#pragma unroll
+  for (int u = 0; u < HPG; ++u) {
+    const int mine = G == 8 ? 2 * g + u : (g < G ? g : G - 1);
+    qs[u] = 0.0f;
+    sumq[u] = 0.0f;
+#pragma unroll
+    for (int hd = 0; hd < G; ++hd) {
+      const int src = G == 8 ? 2 * hd : 4 * hd;  // operand row of (hd, limb 0), k-group 0
+      const float a_qs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qs_row), src));
+      const float a_sq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sumq_row), src));
+      qs[u] = mine == hd ? a_qs : qs[u];
+      sumq[u] = mine == hd ? a_sq : sumq[u];
+    }
+  }
+  // weight exchange: this lane writes (head of row group g, token lt), reads
+  // operand row lt's head, tokens 4g .. 4g+3
+  uint32_t* pwr = &sh.pw[wave][G == 8 ? 2 * g : g][lt][0];
+  const uint32_t* prd = &sh.pw[wave][qhc][4 * g][0];
+  const uint32_t psel = !qvalid ? 0x0c0c0c0cu : (ql == 0 ? 0x05040100u : 0x07060302u);
 
   // 4. stream the range: compute one buffer, refill it two tiles ahead
   NibbleMasks nm;
   nm.init();
-  Softmax st;
+  RowState<G> st;
   st.init(__uint_as_float(0x00800000u));  // 2^-126
   // Pairs of tiles, then an odd last one.  No exit in the middle of the
   // loop body: an edge from there back to the loop head would make the
@@ -998,23 +1034,23 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const int ntile = w1 > w0 ? (w1 - w0 + TILE - 1) / TILE : 0;
   int t = w0;
   for (int i = 0; i < (ntile >> 1); ++i) {
-    compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, g, limbf, nm, st);
+    compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, lt, g, psel, prd, pwr, nm, st);
     __builtin_amdgcn_sched_barrier(0);
     load_tile<PAGED>(ta, ad, t + 2 * TILE, w1, lo);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t + TILE, w1, qf, qs, sumq, g, limbf, nm, st);
+    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t + TILE, w1, qf, qs, sumq, lt, g, psel, prd, pwr, nm, st);
     __builtin_amdgcn_sched_barrier(0);
     load_tile<PAGED>(tb, ad, t + 3 * TILE, w1, lo);
     __builtin_amdgcn_sched_barrier(0);
     t += 2 * TILE;
   }
-  if (ntile & 1) compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, g, limbf, nm, st);
+  if (ntile & 1) compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, lt, g, psel, prd, pwr, nm, st);
   float scale_out;
   if (VM == MK_U8)
     scale_out = 256.0f * a.v_super[(size_t)b * a.hkv + h];
   else
     scale_out = st.R;
-  wave_finish<G>(st, scale_out, c, g, wave, sh);
+  row_finish<G>(st, scale_out, lt, g, wave, sh);
   block_merge<G>(a, sh, b, h, split);
 }
 
