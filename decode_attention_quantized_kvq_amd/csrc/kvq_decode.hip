@@ -43,6 +43,7 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
@@ -206,11 +207,12 @@ __device__ inline void cvt_b4(uint32_t w, uint32_t out[4], const NibbleMasks& nm
 }
 
 // Feature index held by the lanes of k-group g at k-slot e of the j-th score
-// MFMA.  Both key formats cover features [32g, 32g + 32); 8-bit keys in
-// order, 4-bit keys with cvt_b4's nibble interleave (0,4,1,5,2,6,3,7).
+// MFMA.  Both key formats cover features [32g, 32g + 32).  8-bit keys are
+// used as stored; 4-bit keys are widened to bytes, even nibbles (features
+// 2e) in slots 0..3 and odd nibbles (features 2e - 7) in slots 4..7.
 template <bool B8>
 __device__ inline int key_feature(int j, int g, int e) {
-  return 32 * g + 8 * j + (B8 ? e : (e >> 1) + ((e & 1) << 2));
+  return 32 * g + 8 * j + (B8 ? e : (e < 4 ? 2 * e : 2 * e - 7));
 }
 
 // ---------------------------------------------------------------------------
@@ -361,21 +363,34 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int
   }
 }
 
-// Key operand of the J-th score MFMA for block bb.
+// Key operand of the J-th score MFMA for block bb: 8 int8 values, the codes
+// themselves for signed 8-bit keys, offset to signed range for the others
+// (u - 128 for unsigned bytes; nibble + 8 or the unsigned nibble, widened).
 template <int J, int KC, int KM, int VC, int VM>
-__device__ inline half8 key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb, const NibbleMasks& nm) {
-  constexpr bool S = Codes<KC>::SIGNED;
+__device__ inline long key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb) {
+  uint32_t lo, hi;
   if constexpr (Codes<KC>::B8) {
     const u32x4 r = t.k[bb][J >> 1];
-    uint32_t o[4];
-    cvt_b8<S>((J & 1) ? r.z : r.x, o[0], o[1]);
-    cvt_b8<S>((J & 1) ? r.w : r.y, o[2], o[3]);
-    return as_h8(o[0], o[1], o[2], o[3]);
+    lo = (J & 1) ? r.z : r.x;
+    hi = (J & 1) ? r.w : r.y;
+    if (KC == CK_U8) {
+      lo ^= 0x80808080u;
+      hi ^= 0x80808080u;
+    }
   } else {
-    uint32_t o[4];
-    cvt_b4<S>(t.k[bb][0][J], o, nm);
-    return as_h8(o[0], o[1], o[2], o[3]);
+    uint32_t w = t.k[bb][0][J];
+    if (KC == CK_I4) w ^= 0x88888888u;  // two's complement nibble c -> c + 8
+    lo = w & 0x0F0F0F0Fu;
+    hi = (w >> 4) & 0x0F0F0F0Fu;
   }
+  return (long)(((uint64_t)hi << 32) | lo);
+}
+
+// What the key operand adds to the code value (the dot is taken over
+// code + KOFF, so KOFF * sum(Q) comes off the score).
+template <int KC>
+__device__ inline float key_offset() {
+  return KC == CK_U8 ? -128.0f : KC == CK_I4 ? 8.0f : 0.0f;
 }
 
 // Value operands of the 8 output MFMAs: lane (c, g) gives feature 8c + j of
@@ -493,30 +508,40 @@ __device__ inline int row_limb(int r) { return G == 8 ? (r & 1) : (r & 3); }
 // qs[u], sumq[u]: score scale and query sum of local head u.
 template <int KC, int KM, bool KCH, int VC, int VM, int G>
 __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, int tend,
-                                    const half8 qf[4], const float* qs, const float* sumq,
+                                    const long (*qa)[4], const float* qs, const float* sq,
                                     int lt, int g, uint32_t psel, const uint32_t* prd,
                                     uint32_t* pwr, const NibbleMasks& nm, RowState<G>& st) {
   constexpr int HPG = RowState<G>::HPG;
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  // scores on the int8 matrix cores: rows (head, limb) of the query, exact
+  // int32 dot products per limb
+  i32x4 sa[HPG][2];
+#pragma unroll
+  for (int u = 0; u < HPG; ++u) sa[u][0] = sa[u][1] = i32x4{0, 0, 0, 0};
   static_for<4>([&](auto jc) {
     constexpr int J = decltype(jc)::value;
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[J], key_frag<J>(t, 0, nm), s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[J], key_frag<J>(t, 1, nm), s1, 0, 0, 0);
+    const long k0 = key_frag<J>(t, 0), k1 = key_frag<J>(t, 1);
+#pragma unroll
+    for (int u = 0; u < HPG; ++u) {
+      sa[u][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa[u][J], k0, sa[u][0], 0, 0, 0);
+      sa[u][1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa[u][J], k1, sa[u][1], 0, 0, 0);
+    }
   });
   // scores before the query scale qs (> 0): sk[u][bb] for token t of block bb
   float sk[HPG][2], vs[2], vz[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    const f32x4 c = bb ? s1 : s0;
     const bool valid = t0 + 16 * bb + lt < tend;
 #pragma unroll
     for (int u = 0; u < HPG; ++u) {
-      const float raw = c[2 * u] + c[2 * u + 1];  // high + low half of the query
+      const i32x4 c = sa[u][bb];  // limbs of weight 2^16, 2^8, 1
+      const float raw = fmaf((float)c[0], 65536.0f, fmaf((float)c[1], 256.0f, (float)c[2]));
       float v;
-      if (KCH)
+      if (KCH) {
         v = raw;
-      else
-        v = (Meta<KM>::ZP ? raw - t.km[bb].zero() * sumq[u] : raw) * t.km[bb].scale();
+      } else {
+        const float off = key_offset<KC>() + (Meta<KM>::ZP ? t.km[bb].zero() : 0.0f);
+        v = (off != 0.0f ? fmaf(-off, sq[u], raw) : raw) * t.km[bb].scale();
+      }
       sk[u][bb] = valid ? v : NEG_INF;
     }
     vs[bb] = valid ? t.vm[bb].scale() : 0.0f;
@@ -733,6 +758,20 @@ __device__ inline float q_norm_scale(float amax, float* inv) {
   return ldexpf(1.0f, e);
 }
 
+// Power-of-two scale 2^e that brings the head's largest |q| into
+// [2^21, 2^22), so rint(q 2^e) splits into three int8 limbs; *inv = 2^-e.
+__device__ inline float q_int_scale(float amax, float* inv) {
+  if (!(amax > 0.0f)) {
+    *inv = 1.0f;
+    return 1.0f;
+  }
+  int ex;
+  frexpf(amax, &ex);            // amax = m 2^ex, m in [0.5, 1)
+  const int e = 22 - ex;
+  *inv = ldexpf(1.0f, -e);
+  return ldexpf(1.0f, e);
+}
+
 // ---------------------------------------------------------------------------
 // Wave -> workgroup merge and partial write
 // ---------------------------------------------------------------------------
@@ -903,7 +942,14 @@ __device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G
 template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB>
 __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   __shared__ Shared<G> sh;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // 1-D grid, the splits of one (sequence, KV head) pair consecutive, their
+  // order rotated by the pair index.  Workgroups go to the 8 XCDs
+  // round-robin by index: without the rotation a split count that is a
+  // multiple of 8 would send split k of every pair to XCD k, and with
+  // sequences of mixed length the XCDs of the late splits would idle.
+  const int pr = blockIdx.x / a.nsp, r = blockIdx.x - pr * a.nsp;
+  const int split = (r + pr) % a.nsp;
+  const int h = pr % a.hkv, b = pr / a.hkv;
   const SeqInfo si = seq_info(a, b);
   if (a.window && split == a.n_split) {
     if (si.nw > 0) window_split<G, QB>(a, b, h, si.nw, sh);
@@ -919,17 +965,22 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   constexpr bool KB8 = Codes<KC>::B8;
   constexpr int HPG = RowState<G>::HPG;
 
-  // 1. query (and per-channel key scale) loads, issued first.  Operand row
-  //    lt of the score MFMAs holds query head qh as limb ql; the lane covers
-  //    features [32g, 32g + 32) of it.
-  const int qh = row_head<G>(lt), ql = row_limb<G>(lt);
-  const bool qvalid = qh < G && ql < 2;
-  const int qhc = qh < G ? qh : G - 1;
-  const size_t qrow = ((size_t)b * a.hq + (size_t)h * G + qhc) * D;
-  QRaw qr, cr;
-  load_q_run<QB>(qr, a.q, qrow, 32 * g, 32, 0);
+  // 1. query (and per-channel key scale) loads, issued first.  Score operand
+  //    row lt holds limb qlimb (0..2) of query head qhead(u) in row tile u;
+  //    the lane covers features [32g, 32g + 32) of it.
+  const int hl = lt >> 2, qlimb = lt & 3;
+  int qhead[HPG];
+  QRaw qr[HPG], cr;
+#pragma unroll
+  for (int u = 0; u < HPG; ++u) {
+    const int hd = G == 8 ? 2 * hl + u : hl;
+    qhead[u] = hd < G ? hd : G - 1;
+    const size_t qrow = ((size_t)b * a.hq + (size_t)h * G + qhead[u]) * D;
+    load_q_run<QB>(qr[u], a.q, qrow, 32 * g, 32, 0);
+  }
   const size_t crow = ((size_t)b * a.hkv + h) * D;
   if (KCH) load_q_run<false>(cr, a.k_chan, crow, 32 * g, 32, 0);
+  const bool qvalid = qlimb < 3 && (G == 8 || hl < G);
 
   // 2. the first two tiles of this wave's range, in flight while the query
   //    is prepared
@@ -963,65 +1014,71 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   load_tile<PAGED>(tb, ad, w0 + TILE, w1, lo);
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. query fragments (wait for the query loads only)
-  float qv[32];
-  unpack_q<QB>(qr, 32, qv);
-  if (KCH) {
-    float cv[32];
-    unpack_q<false>(cr, 32, cv);
+  // 3. query operand: Q = rint(q 2^e) per head, |Q| < 2^22, as three int8
+  //    limbs Q = l0 2^16 + l1 2^8 + l2 (each in [-128, 127])
+  long qa[HPG][4];
+  float qs_row[HPG], sq_row[HPG];
+  float cv[32];
+  if (KCH) unpack_q<false>(cr, 32, cv);
 #pragma unroll
-    for (int n = 0; n < 32; ++n) qv[n] *= cv[n];  // per-channel key scale moved onto the query
-  }
-  float amax = 0.0f;
+  for (int u = 0; u < HPG; ++u) {
+    float qv[32];
+    unpack_q<QB>(qr[u], 32, qv);
+    if (KCH) {
 #pragma unroll
-  for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(qv[n]));
-  float inv;
-  const float sc = q_norm_scale(rows_max(amax), &inv);  // max over the row's 4 lanes
-  float qsum = 0.0f;
-  half8 qf[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t w[4];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      float x[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int e = 2 * pp + k;
-        x[k] = qv[key_feature<KB8>(j, 0, e)] * sc;
-        qsum += x[k];
-      }
-      const half2v hi = __builtin_convertvector((float2v){x[0], x[1]}, half2v);
-      const half2v lo = __builtin_convertvector((float2v){x[0] - (float)hi.x, x[1] - (float)hi.y}, half2v);
-      const uint32_t v = __builtin_bit_cast(uint32_t, ql == 0 ? hi : lo);
-      w[pp] = qvalid ? v : 0u;
+      for (int n = 0; n < 32; ++n) qv[n] *= cv[n];  // per-channel key scale moved onto the query
     }
-    qf[j] = as_h8(w[0], w[1], w[2], w[3]);
+    float amax = 0.0f;
+#pragma unroll
+    for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(qv[n]));
+    float inv;
+    const float sc = q_int_scale(rows_max(amax), &inv);  // max over the row's 4 lanes
+    float qsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint64_t pk = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = rintf(qv[key_feature<KB8>(j, 0, e)] * sc);
+        qsum += x;
+        const int Q = (int)x;
+        const int l2 = (int)(int8_t)(Q & 0xFF);
+        const int Q1 = (Q - l2) >> 8;
+        const int l1 = (int)(int8_t)(Q1 & 0xFF);
+        const int l0 = (Q1 - l1) >> 8;
+        const int lv = qlimb == 0 ? l0 : (qlimb == 1 ? l1 : l2);
+        pk |= (uint64_t)(uint8_t)(qvalid ? lv : 0) << (8 * e);
+      }
+      qa[u][j] = (long)pk;
+    }
+    qs_row[u] = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128) / 2^e
+    sq_row[u] = rows_sum(qsum);
   }
-  // score scale and query sum of each head, from the lanes of its limb-0 row,
-  // to the lanes that score that head
-  const float qs_row = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128)
-  const float sumq_row = Meta<KM>::ZP ? rows_sum(qsum) : 0.0f;
+  // score scale and query sum of each head, from the lane of its limb-0 row
+  // (row 4 hl, k-group 0) to the lanes that score that head (row group hl)
   float qs[HPG], sumq[HPG];
 #pragma unroll
   for (int u = 0; u < HPG; ++u) {
-    const int mine = G == 8 ? 2 * g + u : (g < G ? g : G - 1);
     qs[u] = 0.0f;
     sumq[u] = 0.0f;
 #pragma unroll
-    for (int hd = 0; hd < G; ++hd) {
-      const int src = G == 8 ? 2 * hd : 4 * hd;  // operand row of (hd, limb 0), k-group 0
-      const float a_qs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qs_row), src));
-      const float a_sq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sumq_row), src));
-      qs[u] = mine == hd ? a_qs : qs[u];
-      sumq[u] = mine == hd ? a_sq : sumq[u];
+    for (int src = 0; src < 4; ++src) {
+      const float a_qs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qs_row[u]), 4 * src));
+      const float a_sq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sq_row[u]), 4 * src));
+      const bool mine = src == g;  // row tile u's head of row group g sits in row 4g
+      qs[u] = mine ? a_qs : qs[u];
+      sumq[u] = mine ? a_sq : sumq[u];
     }
   }
+  // output operand rows (P^T): head and fp16 limb of row lt
+  const int ph = row_head<G>(lt), pl = row_limb<G>(lt);
+  const bool pvalid = ph < G && pl < 2;
+  const int phc = ph < G ? ph : G - 1;
   // weight exchange: this lane writes (head of row group g, token lt), reads
   // operand row lt's head, tokens 4g .. 4g+3
   uint32_t* pwr = &sh.pw[wave][G == 8 ? 2 * g : g][lt][0];
-  const uint32_t* prd = &sh.pw[wave][qhc][4 * g][0];
-  const uint32_t psel = !qvalid ? 0x0c0c0c0cu : (ql == 0 ? 0x05040100u : 0x07060302u);
+  const uint32_t* prd = &sh.pw[wave][phc][4 * g][0];
+  const uint32_t psel = !pvalid ? 0x0c0c0c0cu : (pl == 0 ? 0x05040100u : 0x07060302u);
 
   // 4. stream the range: compute one buffer, refill it two tiles ahead
   NibbleMasks nm;
@@ -1034,17 +1091,17 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const int ntile = w1 > w0 ? (w1 - w0 + TILE - 1) / TILE : 0;
   int t = w0;
   for (int i = 0; i < (ntile >> 1); ++i) {
-    compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, lt, g, psel, prd, pwr, nm, st);
+    compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qa, qs, sumq, lt, g, psel, prd, pwr, nm, st);
     __builtin_amdgcn_sched_barrier(0);
     load_tile<PAGED>(ta, ad, t + 2 * TILE, w1, lo);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t + TILE, w1, qf, qs, sumq, lt, g, psel, prd, pwr, nm, st);
+    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t + TILE, w1, qa, qs, sumq, lt, g, psel, prd, pwr, nm, st);
     __builtin_amdgcn_sched_barrier(0);
     load_tile<PAGED>(tb, ad, t + 3 * TILE, w1, lo);
     __builtin_amdgcn_sched_barrier(0);
     t += 2 * TILE;
   }
-  if (ntile & 1) compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qf, qs, sumq, lt, g, psel, prd, pwr, nm, st);
+  if (ntile & 1) compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qa, qs, sumq, lt, g, psel, prd, pwr, nm, st);
   float scale_out;
   if (VM == MK_U8)
     scale_out = 256.0f * a.v_super[(size_t)b * a.hkv + h];
@@ -1150,7 +1207,7 @@ void launch_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
 
 template <int KC, int KM, bool KCH, int VC, int VM>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.nsp, a.hkv, a.batch);
+  const dim3 grid((unsigned)a.nsp * a.hkv * a.batch);
   if (a.nsp > 0) {
     switch (a.group) {
       case 1: launch_split<KC, KM, KCH, VC, VM, 1>(a, grid, s); break;

@@ -314,6 +314,9 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   if (!split_ok(split)) return KVQ_ERR_INVALID_ARG;
   if (opts && (!opts->split_begin_event != !opts->split_end_event)) return KVQ_ERR_INVALID_ARG;
   const Plan p = make_plan(cfg, max_seq_len, split);
+  // one 1-D grid of nsp x H_kv x B workgroups of 256 threads
+  if ((unsigned long long)p.nsp * cfg->num_kv_heads * cfg->batch >= (1ull << 24))
+    return KVQ_ERR_UNSUPPORTED;
   if (p.nsp > 0 && (!workspace || workspace_bytes < p.total)) return KVQ_ERR_WORKSPACE;
   if (workspace && ((uintptr_t)workspace & 255)) return KVQ_ERR_WORKSPACE;
   DecodeArgs a{};

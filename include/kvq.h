@@ -241,7 +241,9 @@ typedef struct {
  *       owned by the caller; its contents need no initialisation.  Calls
  *       that overlap in time must not share a workspace.
  *  max_seq_len: host upper bound of seq_lens (plans the split of the tokens
- *       over workgroups).  A sequence longer than max_seq_len gets NaN.
+ *       over workgroups).  A sequence longer than max_seq_len gets NaN.  A
+ *       plan of 2^24 or more workgroups (splits x H_kv x batch) returns
+ *       KVQ_ERR_UNSUPPORTED.
  *  Launches two kernels on stream: a split kernel, whose workgroups each
  *  attend over one split of a sequence's tokens for the G query heads of
  *  one KV head, and a log-sum-exp combine of the splits (P2, "Decode
