@@ -261,19 +261,30 @@ struct Addr {
   const uint8_t* v;
   const uint8_t* km;
   const uint8_t* vm;
-  const int32_t* table;  // paged: row of the block table
   int num_blocks, hkv, h;
   size_t head_tok;       // contiguous: first token slot of this head
   int nblk;              // blocks holding tokens
+  // paged: block-table entries of this wave's blocks blk0 .. blk0 + 127,
+  // entry blk0 + i in lane i & 63 of ent[i >> 6]
+  int blk0;
+  int ent[2];
 };
 
+// Blocks a wave can address through its table entries (2048 tokens).
+constexpr int WAVE_BLOCKS = 128;
+
 // Token slot index of block `blk` (clamped to the blocks holding tokens and,
-// when paged, to the pool); wave-uniform.
+// when paged, to the pool); wave-uniform.  Paged lookups read the entries
+// preloaded into the wave's registers (v_readlane), so the token loop issues
+// no memory access for them.
 template <bool PAGED>
 __device__ inline size_t block_slot(const Addr& ad, int blk) {
   blk = blk < ad.nblk ? blk : ad.nblk - 1;
   if constexpr (PAGED) {
-    int phys = ad.table[blk];
+    int i = blk - ad.blk0;
+    i = i < 0 ? 0 : (i >= WAVE_BLOCKS ? WAVE_BLOCKS - 1 : i);
+    int phys = i < 64 ? __builtin_amdgcn_readlane(ad.ent[0], i)
+                      : __builtin_amdgcn_readlane(ad.ent[1], i - 64);
     phys = phys < 0 ? 0 : (phys >= ad.num_blocks ? ad.num_blocks - 1 : phys);
     return ((size_t)phys * ad.hkv + ad.h) * 16;
   } else {
@@ -993,17 +1004,24 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   ad.hkv = a.hkv;
   ad.h = h;
   ad.nblk = (si.nq + 15) >> 4;
+  ad.blk0 = 0;
+  ad.ent[0] = ad.ent[1] = 0;
   if constexpr (PAGED) {
-    ad.table = a.block_table + (size_t)b * a.bt_stride;
     ad.head_tok = 0;
   } else {
-    ad.table = nullptr;
     ad.head_tok = ((size_t)b * a.hkv + h) * a.max_tokens;
   }
   const LaneOff lo = lane_offsets<KC, KM, VC, VM>(lt, g);
   const int per = a.split_tokens / WAVES;
   const int w0 = __builtin_amdgcn_readfirstlane(tok0 + wave * per);
   const int w1 = __builtin_amdgcn_readfirstlane(min(w0 + per, tok1));
+  if constexpr (PAGED) {  // this wave's block-table entries (at most 128 blocks)
+    const int32_t* row = a.block_table + (size_t)b * a.bt_stride;
+    const int lim = a.bt_stride - 1;
+    ad.blk0 = w0 >> 4;
+    ad.ent[0] = row[min(ad.blk0 + lane, lim)];
+    ad.ent[1] = row[min(ad.blk0 + 64 + lane, lim)];
+  }
   // The scheduling barriers keep each tile's loads together and in order
   // (first tile, then second, then the refills): the compiler derives its
   // wait counts from that order, and interleaved loads would make every wait

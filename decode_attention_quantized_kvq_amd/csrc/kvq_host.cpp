@@ -267,6 +267,7 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int max_seq_len,
                                   const kvq_decode_opts* opts) {
   const int split = opts ? opts->split_tokens : 0;
   if (check_config(cfg, true) != KVQ_OK || max_seq_len < 0 || !split_ok(split)) return 0;
+  if (cfg->block_tokens && split > 8192) return 0;
   return make_plan(cfg, max_seq_len, split).total;
 }
 
@@ -313,6 +314,8 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   const int split = opts ? opts->split_tokens : 0;
   if (!split_ok(split)) return KVQ_ERR_INVALID_ARG;
   if (opts && (!opts->split_begin_event != !opts->split_end_event)) return KVQ_ERR_INVALID_ARG;
+  // a paged wave addresses at most 128 blocks: splits of at most 4 x 2048 tokens
+  if (cfg->block_tokens && split > 8192) return KVQ_ERR_INVALID_ARG;
   const Plan p = make_plan(cfg, max_seq_len, split);
   // one 1-D grid of nsp x H_kv x B workgroups of 256 threads
   if ((unsigned long long)p.nsp * cfg->num_kv_heads * cfg->batch >= (1ull << 24))

@@ -223,7 +223,8 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
 /* Tuning and measurement knobs of kvq_decode_attn; zero / NULL fields take
  * the library's choice. */
 typedef struct {
-  int split_tokens;         /* quantized tokens per workgroup, a multiple of 128 */
+  int split_tokens;         /* quantized tokens per workgroup, a multiple of 128
+                               (at most 8192 for a paged cache) */
   void* split_begin_event;  /* hipEvent_t stamped with the start of the split
                                kernel's dispatch, or NULL */
   void* split_end_event;    /* hipEvent_t stamped with its end; both events or

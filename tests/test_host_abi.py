@@ -165,3 +165,16 @@ def test_workspace_grows_with_length():
     # partial outputs [B][Hq][splits][D] fp32 and partial (max, sum) pairs,
     # each region 256-aligned
     assert b == -(-8 * 32 * 16 * 128 * 4 // 256) * 256 + -(-8 * 32 * 16 * 2 * 4 // 256) * 256
+
+
+def test_paged_split_limit():
+    """A paged wave addresses at most 128 blocks, so explicit splits above
+    8192 tokens are rejected for paged caches (contiguous ones accept them)."""
+    wl = synth.workload(4)
+    cfg = K.make_config(batch=2, num_q_heads=64, num_kv_heads=8, head_dim=128, max_tokens=32768,
+                        key=wl["key"], value=wl["value"], window=128, block_tokens=16,
+                        num_blocks=4096, max_blocks_per_seq=2048)
+    assert K.decode_workspace_bytes(cfg, 32768, 8192) > 0
+    assert K.decode_workspace_bytes(cfg, 32768, 8320) == 0
+    cfg_c = cfg_of(synth.workload(2))
+    assert K.decode_workspace_bytes(cfg_c, 4096, 16384) > 0
