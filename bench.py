@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark on one MI355X.
 
-One step = one kvq_decode_attn call (split kernel + log-sum-exp combine) over
+One step = one kvq_decode_attn call (one kernel: split attention, then the
+log-sum-exp combine by the last workgroup of each sequence and KV head) over
 the whole batch of one layer, the hot path of single-query decode attention
 over a quantized KV cache.  The cache is built on the device by
 kvq_quantize_append from seeded synthetic inputs before timing; inputs are
@@ -233,7 +234,7 @@ def main():
     q = torch.from_numpy(np.stack([synth.queries(wl, b) for b in range(wl["batch"])]))
     q = q.to(torch.bfloat16 if wl["in_dtype"] == "bf16" else torch.float32).cuda()
     out = torch.empty((wl["batch"], wl["hq"], wl["d"]), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(K.decode_workspace_bytes(cfg, max_len, args.split), 1),
+    ws = torch.zeros(max(K.decode_workspace_bytes(cfg, max_len, args.split), 1),
                      dtype=torch.uint8, device="cuda")
 
     def step(i, events=None):

@@ -22,9 +22,9 @@
 // high/low halves of the query (and of the weights), so every loaded tile is
 // used by all G heads and both products are exact to about 2^-22.  Online
 // softmax runs in base 2.  The 4 waves merge through LDS and the workgroup
-// writes one partial (max, sum, normalized output) per query head.
-// decode_combine: log-sum-exp combine of the partials of each (sequence,
-// query head) into the fp32 output.
+// writes one partial (max, sum, normalized output) per query head.  The last
+// workgroup of a (sequence, KV head) to finish, found with an arrival
+// counter, merges the partials by log-sum-exp into the fp32 output.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -49,6 +49,11 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int D = 128;
 constexpr int WAVES = 4;
 constexpr int TILE = 32;
+// Tiles in flight per wave.
+#ifndef KVQ_NB
+#define KVQ_NB 2
+#endif
+constexpr int NB = KVQ_NB;
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float NEG_INF = -__builtin_inff();
 
@@ -842,6 +847,13 @@ __device__ inline void row_finish(RowState<G>& st, float scale_out, int t, int g
   }
 }
 
+__device__ inline void store_agent(float* p, float v) {
+  __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 template <int G>
 __device__ inline void block_merge(const DecodeArgs& a, const Shared<G>& sh, int b, int h,
                                    int split) {
@@ -859,10 +871,12 @@ __device__ inline void block_merge(const DecodeArgs& a, const Shared<G>& sh, int
       acc += e * sh.o[w][hh][d];
     }
     const size_t row = ((size_t)b * a.hq + (size_t)h * G + hh) * a.nsp + split;
-    a.part_o[row * D + d] = ws > 0.0f ? acc / ws : 0.0f;
+    // agent-scope stores write through this XCD's L2: the workgroup that
+    // merges the splits may run on another XCD
+    store_agent(a.part_o + row * D + d, ws > 0.0f ? acc / ws : 0.0f);
     if (d == 0) {
-      a.part_ml[2 * row] = M;
-      a.part_ml[2 * row + 1] = ws;
+      store_agent(a.part_ml + 2 * row, M);
+      store_agent(a.part_ml + 2 * row + 1, ws);
     }
   }
 }
@@ -950,6 +964,103 @@ __device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G
   block_merge<G>(a, sh, b, h, a.n_split);
 }
 
+// ---------------------------------------------------------------------------
+// Log-sum-exp combine of the splits, by the last workgroup of each
+// (sequence, KV head) to finish
+// ---------------------------------------------------------------------------
+// Splits of sequence b holding quantized tokens (at most the n_split
+// launched; a longer sequence is an overflow of the plan).
+struct Plan {
+  int ns;
+  bool overflow, win;
+  int total;  // workgroups that write a partial
+};
+
+__device__ inline Plan plan_of(const DecodeArgs& a, const SeqInfo& si) {
+  Plan p;
+  const int need = (si.nq + a.split_tokens - 1) / a.split_tokens;
+  p.overflow = need > a.n_split;
+  p.ns = p.overflow ? a.n_split : need;
+  p.win = si.nw > 0;
+  p.total = p.ns + (p.win ? 1 : 0);
+  return p;
+}
+
+// Wave w merges query heads w, w + 4 (G = 8) of KV head h: lane j reads
+// split j's (m, l), each lane then two output features of every split.
+template <int G>
+__device__ void combine_heads(const DecodeArgs& a, int b, int h, const Plan& pl) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int hh = wave; hh < G; hh += WAVES) {
+    const size_t row0 = ((size_t)b * a.hq + (size_t)h * G + hh) * a.nsp;
+    const int nr = pl.ns + (pl.win ? 1 : 0);  // partial rows: splits, then the window
+    auto prow = [&](int j) { return row0 + (j < pl.ns ? j : a.n_split); };
+    float M = NEG_INF;
+    for (int j = lane; j < nr; j += 64) M = fmaxf(M, load_agent(a.part_ml + 2 * prow(j)));
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float ws = 0.0f;
+    float2 acc = {0.0f, 0.0f};
+    for (int j0 = 0; j0 < nr; j0 += 64) {
+      const int j = j0 + lane;
+      float e = 0.0f;
+      if (j < nr) {
+        const size_t rj = prow(j);
+        const float m = load_agent(a.part_ml + 2 * rj), l = load_agent(a.part_ml + 2 * rj + 1);
+        e = l > 0.0f ? l * exp2_fast(m - M) : 0.0f;
+      }
+      ws += e;
+      const int cnt = min(64, nr - j0);
+      for (int k0 = 0; k0 < cnt; k0 += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {  // eight loads in flight
+          const int k = min(k0 + kk, cnt - 1);
+          const float* po = a.part_o + prow(j0 + k) * D + 2 * lane;
+          v[kk] = float2{load_agent(po), load_agent(po + 1)};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const float ek = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), min(k0 + kk, 63)));
+          const float w = k0 + kk < cnt ? ek : 0.0f;
+          acc.x += w * v[kk].x;
+          acc.y += w * v[kk].y;
+        }
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+    float2 r;
+    if (pl.overflow) {
+      r.x = r.y = __builtin_nanf("");
+    } else if (ws > 0.0f) {
+      r.x = acc.x / ws;
+      r.y = acc.y / ws;
+    } else {
+      r.x = r.y = 0.0f;
+    }
+    *(float2*)(a.out + ((size_t)b * a.hq + (size_t)h * G + hh) * D + 2 * lane) = r;
+  }
+}
+
+// After this workgroup's partial is written: count it in the arrival
+// counter of (b, h); the last of the pl.total workgroups resets the counter
+// and merges.  Each thread first waits for its own partial stores to
+// complete (they write through to memory), so the counter cannot run ahead
+// of the data it announces; no cache-wide fence is needed.
+template <int G>
+__device__ void arrive_and_combine(const DecodeArgs& a, int b, int h, const Plan& pl, int* flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = a.counters + (size_t)b * a.hkv + h;
+    const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev + 1 == (uint32_t)pl.total;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  if (*flag) combine_heads<G>(a, b, h, pl);
+}
+
 template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB>
 __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   __shared__ Shared<G> sh;
@@ -961,9 +1072,20 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const int pr = blockIdx.x / a.nsp, r = blockIdx.x - pr * a.nsp;
   const int split = (r + pr) % a.nsp;
   const int h = pr % a.hkv, b = pr / a.hkv;
+  __shared__ int last_flag;
   const SeqInfo si = seq_info(a, b);
+  const Plan pl = plan_of(a, si);
+  if (pl.total == 0) {  // no tokens: zeros (NaN if the plan had no room for them)
+    if (split == 0)
+      for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64)
+        a.out[((size_t)b * a.hq + (size_t)h * G) * D + idx] = pl.overflow ? __builtin_nanf("") : 0.0f;
+    return;
+  }
   if (a.window && split == a.n_split) {
-    if (si.nw > 0) window_split<G, QB>(a, b, h, si.nw, sh);
+    if (si.nw > 0) {
+      window_split<G, QB>(a, b, h, si.nw, sh);
+      arrive_and_combine<G>(a, b, h, pl, &last_flag);
+    }
     return;
   }
   const int tok0 = split * a.split_tokens;
@@ -1023,14 +1145,15 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
     ad.ent[1] = row[min(ad.blk0 + 64 + lane, lim)];
   }
   // The scheduling barriers keep each tile's loads together and in order
-  // (first tile, then second, then the refills): the compiler derives its
+  // (first tile, second, ..., then the refills): the compiler derives its
   // wait counts from that order, and interleaved loads would make every wait
   // in the loop a wait for all of them.
-  TileRaw<KC, KM, VC, VM> ta, tb;
-  load_tile<PAGED>(ta, ad, w0, w1, lo);
-  __builtin_amdgcn_sched_barrier(0);
-  load_tile<PAGED>(tb, ad, w0 + TILE, w1, lo);
-  __builtin_amdgcn_sched_barrier(0);
+  TileRaw<KC, KM, VC, VM> buf[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    load_tile<PAGED>(buf[k], ad, w0 + k * TILE, w1, lo);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // 3. query operand: Q = rint(q 2^e) per head, |Q| < 2^22, as three int8
   //    limbs Q = l0 2^16 + l1 2^8 + l2 (each in [-128, 127])
@@ -1089,37 +1212,42 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
     }
   }
   // output operand rows (P^T): head and fp16 limb of row lt
-  const int ph = row_head<G>(lt), pl = row_limb<G>(lt);
-  const bool pvalid = ph < G && pl < 2;
+  const int ph = row_head<G>(lt), plimb = row_limb<G>(lt);
+  const bool pvalid = ph < G && plimb < 2;
   const int phc = ph < G ? ph : G - 1;
   // weight exchange: this lane writes (head of row group g, token lt), reads
   // operand row lt's head, tokens 4g .. 4g+3
   uint32_t* pwr = &sh.pw[wave][G == 8 ? 2 * g : g][lt][0];
   const uint32_t* prd = &sh.pw[wave][phc][4 * g][0];
-  const uint32_t psel = !pvalid ? 0x0c0c0c0cu : (pl == 0 ? 0x05040100u : 0x07060302u);
+  const uint32_t psel = !pvalid ? 0x0c0c0c0cu : (plimb == 0 ? 0x05040100u : 0x07060302u);
 
   // 4. stream the range: compute one buffer, refill it two tiles ahead
   NibbleMasks nm;
   nm.init();
   RowState<G> st;
   st.init(__uint_as_float(0x00800000u));  // 2^-126
-  // Pairs of tiles, then an odd last one.  No exit in the middle of the
-  // loop body: an edge from there back to the loop head would make the
+  // Groups of NB tiles, then the remaining ones.  No exit in the middle of
+  // the loop body: an edge from there back to the loop head would make the
   // compiler wait there as if only the first refill were in flight.
   const int ntile = w1 > w0 ? (w1 - w0 + TILE - 1) / TILE : 0;
   int t = w0;
-  for (int i = 0; i < (ntile >> 1); ++i) {
-    compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qa, qs, sumq, lt, g, psel, prd, pwr, nm, st);
-    __builtin_amdgcn_sched_barrier(0);
-    load_tile<PAGED>(ta, ad, t + 2 * TILE, w1, lo);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_tile<KC, KM, KCH, VC, VM, G>(tb, t + TILE, w1, qa, qs, sumq, lt, g, psel, prd, pwr, nm, st);
-    __builtin_amdgcn_sched_barrier(0);
-    load_tile<PAGED>(tb, ad, t + 3 * TILE, w1, lo);
-    __builtin_amdgcn_sched_barrier(0);
-    t += 2 * TILE;
+  for (int i = 0; i < ntile / NB; ++i) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      compute_tile<KC, KM, KCH, VC, VM, G>(buf[k], t + k * TILE, w1, qa, qs, sumq, lt, g, psel, prd,
+                                           pwr, nm, st);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile<PAGED>(buf[k], ad, t + (k + NB) * TILE, w1, lo);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    t += NB * TILE;
   }
-  if (ntile & 1) compute_tile<KC, KM, KCH, VC, VM, G>(ta, t, w1, qa, qs, sumq, lt, g, psel, prd, pwr, nm, st);
+  const int rem = ntile - (ntile / NB) * NB;
+#pragma unroll
+  for (int k = 0; k < NB - 1; ++k)
+    if (k < rem)
+      compute_tile<KC, KM, KCH, VC, VM, G>(buf[k], t + k * TILE, w1, qa, qs, sumq, lt, g, psel, prd,
+                                           pwr, nm, st);
   float scale_out;
   if (VM == MK_U8)
     scale_out = 256.0f * a.v_super[(size_t)b * a.hkv + h];
@@ -1127,72 +1255,7 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
     scale_out = st.R;
   row_finish<G>(st, scale_out, lt, g, wave, sh);
   block_merge<G>(a, sh, b, h, split);
-}
-
-// ---------------------------------------------------------------------------
-// decode_combine: log-sum-exp combine of the partials of one (sequence,
-// query head)
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(64) decode_combine(DecodeArgs a) {
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const SeqInfo si = seq_info(a, b);
-  const int ns = (si.nq + a.split_tokens - 1) / a.split_tokens;
-  const bool overflow = ns > a.n_split;  // longer than the launch was planned for
-  const int nq_used = overflow ? a.n_split : ns;
-  const size_t row0 = ((size_t)b * a.hq + hq) * a.nsp;
-  const bool win = si.nw > 0;
-  float M = NEG_INF;
-  for (int j = lane; j < nq_used; j += 64) M = fmaxf(M, a.part_ml[2 * (row0 + j)]);
-  float mw = NEG_INF, lw = 0.0f;
-  if (win) {
-    mw = a.part_ml[2 * (row0 + a.n_split)];
-    lw = a.part_ml[2 * (row0 + a.n_split) + 1];
-    M = fmaxf(M, mw);
-  }
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float ws = 0.0f;
-  float2 acc = {0.0f, 0.0f};
-  for (int j0 = 0; j0 < nq_used; j0 += 64) {
-    const int j = j0 + lane;
-    float e = 0.0f;
-    if (j < nq_used) {
-      const float m = a.part_ml[2 * (row0 + j)], l = a.part_ml[2 * (row0 + j) + 1];
-      e = l > 0.0f ? l * exp2_fast(m - M) : 0.0f;
-    }
-    ws += e;
-    const int cnt = min(64, nq_used - j0);
-    const float2* po = (const float2*)(a.part_o + (row0 + j0) * D) + lane;
-    for (int k0 = 0; k0 < cnt; k0 += 8) {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int k = k0 + kk;
-        if (k < cnt) {
-          const float ek = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), k));
-          const float2 v = po[(size_t)k * (D / 2)];
-          acc.x += ek * v.x;
-          acc.y += ek * v.y;
-        }
-      }
-    }
-  }
-  for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
-  if (win) {
-    const float e = lw > 0.0f ? lw * exp2_fast(mw - M) : 0.0f;
-    const float2 v = *((const float2*)(a.part_o + (row0 + a.n_split) * D) + lane);
-    ws += e;
-    acc.x += e * v.x;
-    acc.y += e * v.y;
-  }
-  float2 r;
-  if (overflow) {
-    r.x = r.y = __builtin_nanf("");
-  } else if (ws > 0.0f) {
-    r.x = acc.x / ws;
-    r.y = acc.y / ws;
-  } else {
-    r.x = r.y = 0.0f;
-  }
-  *(float2*)(a.out + ((size_t)b * a.hq + hq) * D + 2 * lane) = r;
+  arrive_and_combine<G>(a, b, h, pl, &last_flag);
 }
 
 // Launches one decode_split variant.  With events, hipExtLaunchKernel stamps
@@ -1237,8 +1300,7 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_combine, dim3(a.hq, a.batch), dim3(64), 0, s, a);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace

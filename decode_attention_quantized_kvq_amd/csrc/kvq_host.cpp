@@ -123,19 +123,21 @@ static int choose_split(const kvq_config* c, int max_seq_len) {
 
 struct Plan {
   int split_tokens, n_split, nsp;
-  size_t o_bytes, ml_bytes, total;
+  size_t o_bytes, ml_bytes, cnt_bytes, total;
 };
 
 static Plan make_plan(const kvq_config* c, int max_seq_len, int split_tokens) {
   Plan p{};
   p.split_tokens = split_tokens > 0 ? split_tokens : choose_split(c, max_seq_len);
   const int nq = std::max(0, max_seq_len - c->window);
-  p.n_split = (nq + p.split_tokens - 1) / p.split_tokens;
+  // at least one split: its workgroup writes the zeros of empty sequences
+  p.n_split = std::max(1, (nq + p.split_tokens - 1) / p.split_tokens);
   p.nsp = p.n_split + (c->window > 0 ? 1 : 0);
   const size_t rows = (size_t)c->batch * c->num_q_heads * p.nsp;
   p.o_bytes = round_up(rows * c->head_dim * sizeof(float), 256);
   p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
-  p.total = p.o_bytes + p.ml_bytes;
+  p.cnt_bytes = round_up((size_t)c->batch * c->num_kv_heads * sizeof(uint32_t), 256);
+  p.total = p.o_bytes + p.ml_bytes + p.cnt_bytes;
   return p;
 }
 
@@ -320,8 +322,8 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   // one 1-D grid of nsp x H_kv x B workgroups of 256 threads
   if ((unsigned long long)p.nsp * cfg->num_kv_heads * cfg->batch >= (1ull << 24))
     return KVQ_ERR_UNSUPPORTED;
-  if (p.nsp > 0 && (!workspace || workspace_bytes < p.total)) return KVQ_ERR_WORKSPACE;
-  if (workspace && ((uintptr_t)workspace & 255)) return KVQ_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < p.total) return KVQ_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 255) return KVQ_ERR_WORKSPACE;
   DecodeArgs a{};
   const LayerSizes s = layer_sizes(cfg);
   uint8_t *kc, *vc, *km, *vm;
@@ -342,7 +344,8 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   a.q = q;
   a.out = out;
   a.part_o = (float*)workspace;
-  a.part_ml = workspace ? (float*)((uint8_t*)workspace + p.o_bytes) : nullptr;
+  a.part_ml = (float*)((uint8_t*)workspace + p.o_bytes);
+  a.counters = (uint32_t*)((uint8_t*)workspace + p.o_bytes + p.ml_bytes);
   a.batch = cfg->batch;
   a.hq = cfg->num_q_heads;
   a.hkv = cfg->num_kv_heads;

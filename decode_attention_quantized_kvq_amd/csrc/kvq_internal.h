@@ -78,6 +78,7 @@ struct DecodeArgs {
   float* out;
   float* part_o;   // [B][Hq][nsp][D]
   float* part_ml;  // [B][Hq][nsp][2]
+  uint32_t* counters;  // [B][H_kv] arrival counters, zero between calls
   int batch, hq, hkv, group;
   int max_tokens, paged, num_blocks, bt_stride, window;
   int split_tokens;  // quantized tokens per workgroup (multiple of 128)

@@ -252,10 +252,11 @@ def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
                 split_tokens: int = 0, stream=None, split_events=None) -> torch.Tensor:
     """kvq_decode_attn: q [B][Hq][D] -> out [B][Hq][D] fp32.
 
-    workspace: scratch of decode_workspace_bytes() bytes; one is allocated
-    per call when omitted.
-    split_events: optional (begin, end) torch.cuda.Event pair recorded around
-    the split kernel (already created, e.g. by one record() call)."""
+    workspace: scratch of decode_workspace_bytes() bytes, zero-filled before
+    its first use (the library leaves it reusable); one is allocated per
+    call when omitted.
+    split_events: optional (begin, end) torch.cuda.Event pair stamped with
+    the decode kernel's dispatch (already created, e.g. by one record() call)."""
     cfg = cache.cfg
     _check_input(q, cfg, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "q")
     if out is None:
@@ -266,7 +267,7 @@ def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
         raise ValueError("out: expected contiguous fp32 [B][Hq][D]")
     if workspace is None:
         need = decode_workspace_bytes(cfg, max_seq_len, split_tokens)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     desc = cache.desc()
     opts = DecodeOpts(int(split_tokens))
     if split_events is not None:

@@ -225,7 +225,7 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
 typedef struct {
   int split_tokens;         /* quantized tokens per workgroup, a multiple of 128
                                (at most 8192 for a paged cache) */
-  void* split_begin_event;  /* hipEvent_t stamped with the start of the split
+  void* split_begin_event;  /* hipEvent_t stamped with the start of the decode
                                kernel's dispatch, or NULL */
   void* split_end_event;    /* hipEvent_t stamped with its end; both events or
                                neither (KVQ_ERR_INVALID_ARG otherwise) */
@@ -239,16 +239,18 @@ typedef struct {
  *       tokens gets zeros.
  *  workspace: device scratch of at least
  *       kvq_decode_workspace_bytes(cfg, max_seq_len) bytes, 256-byte aligned,
- *       owned by the caller; its contents need no initialisation.  Calls
- *       that overlap in time must not share a workspace.
+ *       owned by the caller.  It must be zero before the first call that
+ *       uses it: it holds one arrival counter per (sequence, KV head), and
+ *       every call leaves them at zero again.  Calls that overlap in time
+ *       must not share a workspace.
  *  max_seq_len: host upper bound of seq_lens (plans the split of the tokens
  *       over workgroups).  A sequence longer than max_seq_len gets NaN.  A
  *       plan of 2^24 or more workgroups (splits x H_kv x batch) returns
  *       KVQ_ERR_UNSUPPORTED.
- *  Launches two kernels on stream: a split kernel, whose workgroups each
- *  attend over one split of a sequence's tokens for the G query heads of
- *  one KV head, and a log-sum-exp combine of the splits (P2, "Decode
- *  kernels are split-T and memory bound"). */
+ *  Launches one kernel on stream.  Each workgroup attends over one split of
+ *  a sequence's tokens for the G query heads of one KV head; the last
+ *  workgroup of each (sequence, KV head) to finish merges the splits by
+ *  log-sum-exp (P2, "Decode kernels are split-T and memory bound"). */
 kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, int layer,
                            const void* q, float* out, void* workspace, size_t workspace_bytes,
                            int max_seq_len, void* stream);

@@ -170,18 +170,41 @@ def test_multi_layer_isolation():
 
 
 def test_workspace_reuse():
-    """One workspace serves consecutive calls with different queries, and the
-    outputs equal those of calls with a fresh workspace."""
+    """One workspace serves consecutive calls with different queries: the
+    arrival counters the last workgroup of each (sequence, KV head) resets
+    are zero after every call, and the outputs equal those of calls with a
+    fresh workspace."""
     H.log("case: workspace reuse")
     wl = synth.workload(4, batch=3, tokens=1024)  # paged, with a bf16 window
     lens = [1000, 0, 333]
     bt = H.build(wl, lens, decode_steps=2, oracle=False)
     split, max_len = 128, 1024
     need = K.decode_workspace_bytes(bt.cfg, max_len, split)
-    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN patterns
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    nsp = -(-(max_len - wl["window"]) // split) + (1 if wl["window"] else 0)
+    rows = wl["batch"] * wl["hq"] * nsp
+    cnt_off = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256
     for step in (0, 1, 0, 2):
         q = H.to_device(H.queries(wl, step), wl["in_dtype"])
         got = K.decode_attn(bt.cache, 0, q, max_len, workspace=ws, split_tokens=split)
         fresh = K.decode_attn(bt.cache, 0, q, max_len, split_tokens=split)
         torch.cuda.synchronize()
         assert torch.equal(got, fresh), f"step {step}: reused workspace changed the output"
+        assert int(ws[cnt_off:].count_nonzero()) == 0, "arrival counters not reset"
+
+
+def test_repeatable_outputs():
+    """The merge reads partials written by other workgroups, possibly on
+    other XCDs: repeated calls must give bit-identical outputs."""
+    H.log("case: repeatable outputs")
+    for wid, over, lens, split in [(2, dict(batch=2, tokens=1024), [1000, 777], 128),
+                                   (3, dict(batch=2, tokens=1024), [1000, 651], 256),
+                                   (4, dict(batch=3, tokens=1024), [1000, 300, 131], 128)]:
+        wl = synth.workload(wid, **over)
+        bt = H.build(wl, lens)
+        q = H.queries(wl)
+        first = H.run_decode(bt, q, split)
+        want = np.stack([bt.oracle.attend(b, q[b]) for b in range(wl["batch"])])
+        H.check_close(first, want, f"{wl['name']} split {split}")
+        for _ in range(20):
+            assert np.array_equal(H.run_decode(bt, q, split), first), f"{wl['name']}: outputs differ between runs"

@@ -162,9 +162,11 @@ def test_workspace_grows_with_length():
     a = K.decode_workspace_bytes(cfg, 1024)
     b = K.decode_workspace_bytes(cfg, 4096, 256)
     assert 0 < a and 0 < b
-    # partial outputs [B][Hq][splits][D] fp32 and partial (max, sum) pairs,
-    # each region 256-aligned
-    assert b == -(-8 * 32 * 16 * 128 * 4 // 256) * 256 + -(-8 * 32 * 16 * 2 * 4 // 256) * 256
+    # partial outputs [B][Hq][splits][D] fp32, partial (max, sum) pairs and
+    # one arrival counter per (sequence, KV head), each region 256-aligned
+    hkv = cfg.num_kv_heads
+    assert b == (-(-8 * 32 * 16 * 128 * 4 // 256) * 256 + -(-8 * 32 * 16 * 2 * 4 // 256) * 256
+                 + -(-8 * hkv * 4 // 256) * 256)
 
 
 def test_paged_split_limit():
