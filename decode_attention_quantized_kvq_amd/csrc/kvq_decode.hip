@@ -613,11 +613,9 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
     const uint32_t hb = __builtin_bit_cast(uint32_t, hi), lb = __builtin_bit_cast(uint32_t, lo);
     *(u32x2*)(pwr + 32 * u) = u32x2{perm(lb, hb, 0x05040100u), perm(lb, hb, 0x07060302u)};
   }
-  // Other lanes read these words next.  A wave's LDS instructions issue in
-  // order, but a read may start before all passes of the preceding 64-lane
-  // write have landed (runs without this wait were not repeatable): wait for
-  // the write to complete first.
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // Other lanes of this wave read these words next; a wavefront's LDS
+  // operations complete in issue order, so only the compiler needs fencing.
+  __builtin_amdgcn_wave_barrier();
   // operand row r = (head, limb), k-group kg: tokens 4kg .. 4kg+3 of both
   // blocks (k-slot e = 4 bb + i); 8 words: token-major, block-minor
   const u32x4 A = *(const u32x4*)prd, B = *(const u32x4*)(prd + 4);
