@@ -54,6 +54,10 @@ constexpr int TILE = 32;
 #define KVQ_NB 2
 #endif
 constexpr int NB = KVQ_NB;
+// Minimum waves per SIMD the decode kernel is compiled for.
+#ifndef KVQ_MINW
+#define KVQ_MINW 1
+#endif
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float NEG_INF = -__builtin_inff();
 
@@ -317,7 +321,9 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const uint8_t* p, int bytes) {
 // block; fixed for the whole kernel, so every load is a wave-uniform base plus
 // a 32-bit offset.  Keys: token row t, bytes [32g, 32g + 32) (8-bit) or
 // [16g, 16g + 16) (4-bit), i.e. features [32g, 32g + 32) either way.  Values:
-// token rows 4g + i (i = 0..3), features [8t, 8t + 8).  Metadata: token t.
+// token rows 4i + g (i = 0..3), features [8t, 8t + 8), so that one load
+// instruction (fixed i) covers 4 consecutive rows, whole 128-byte lines even
+// for 64-byte (4-bit) rows.  Metadata: token t.
 struct LaneOff {
   uint32_t k0, k1, v[4], km, vm;
 };
@@ -329,7 +335,7 @@ __device__ inline LaneOff lane_offsets(int t, int g) {
   o.k0 = t * KROW + (Codes<KC>::B8 ? 32 * g : 16 * g);
   o.k1 = o.k0 + 16;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o.v[i] = (4 * g + i) * VROW + (Codes<VC>::B8 ? 8 * t : 4 * t);
+  for (int i = 0; i < 4; ++i) o.v[i] = (4 * i + g) * VROW + (Codes<VC>::B8 ? 8 * t : 4 * t);
   o.km = t * Meta<KM>::BYTES;
   o.vm = t * Meta<VM>::BYTES;
   return o;
@@ -616,8 +622,9 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
   // Other lanes of this wave read these words next; a wavefront's LDS
   // operations complete in issue order, so only the compiler needs fencing.
   __builtin_amdgcn_wave_barrier();
-  // operand row r = (head, limb), k-group kg: tokens 4kg .. 4kg+3 of both
-  // blocks (k-slot e = 4 bb + i); 8 words: token-major, block-minor
+  // operand row r = (head, limb), k-group kg: tokens 4i + kg (i = 0..3) of
+  // both blocks (k-slot e = 4 bb + i); they sit in slots 4kg .. 4kg+3 of the
+  // exchange, 8 words, slot-major, block-minor
   const u32x4 A = *(const u32x4*)prd, B = *(const u32x4*)(prd + 4);
   const uint32_t M[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
   const uint32_t pa0 = perm(M[2], M[0], psel), pa1 = perm(M[6], M[4], psel);
@@ -1060,7 +1067,7 @@ __device__ void arrive_and_combine(const DecodeArgs& a, int b, int h, const Plan
 }
 
 template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB>
-__global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
+__global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   __shared__ Shared<G> sh;
   // 1-D grid, the splits of one (sequence, KV head) pair consecutive, their
   // order rotated by the pair index.  Workgroups go to the 8 XCDs
@@ -1214,8 +1221,9 @@ __global__ void __launch_bounds__(256) decode_split(DecodeArgs a) {
   const bool pvalid = ph < G && plimb < 2;
   const int phc = ph < G ? ph : G - 1;
   // weight exchange: this lane writes (head of row group g, token lt), reads
-  // operand row lt's head, tokens 4g .. 4g+3
-  uint32_t* pwr = &sh.pw[wave][G == 8 ? 2 * g : g][lt][0];
+  // operand row lt's head, tokens 4i + g
+  // token lt goes to exchange slot 4 (lt mod 4) + lt / 4
+  uint32_t* pwr = &sh.pw[wave][G == 8 ? 2 * g : g][4 * (lt & 3) + (lt >> 2)][0];
   const uint32_t* prd = &sh.pw[wave][phc][4 * g][0];
   const uint32_t psel = !pvalid ? 0x0c0c0c0cu : (plimb == 0 ? 0x05040100u : 0x07060302u);
 
