@@ -1066,27 +1066,169 @@ __device__ void arrive_and_combine(const DecodeArgs& a, int b, int h, const Plan
   if (*flag) combine_heads<G>(a, b, h, pl);
 }
 
+// ---------------------------------------------------------------------------
+// Workgroup -> work item.  Items in dispatch order, largest first, so that
+// with sequences of mixed length the last workgroups to start are the
+// shortest ones and the compute units finish together:
+//   1. every full chunk of split_tokens quantized tokens: sequence-major,
+//      then KV-head-major, the chunk order of each (sequence, KV head) pair
+//      rotated by the pair index (consecutive workgroups go to different
+//      XCDs; this way the chunks that start together on one XCD lie at
+//      different offsets of their pairs),
+//   2. the remainder chunk of each sequence, by size class from large to
+//      small (NSIZE classes of split_tokens / NSIZE tokens),
+//   3. one item per (sequence, KV head) for the bf16 window, if any,
+//   4. workgroups past the last item return at once.
+// Every wave derives the workgroup's item on its own from the sequence
+// lengths (one length per lane, 64 sequences per pass), with wave scans and
+// ballots: no workgroup barrier before the first tile loads.
+// ---------------------------------------------------------------------------
+constexpr int NSIZE = 32;
+
+struct Item {
+  int kind;  // 0 quantized chunk, 1 window, 2 nothing
+  int b, h, split;
+  SeqInfo si;
+};
+
+struct Chunks {
+  int full, part, rem;  // full chunks, remainder chunk (0/1), its tokens
+};
+
+__device__ inline Chunks chunks_of(const DecodeArgs& a, const SeqInfo& si) {
+  Chunks c;
+  const int S = a.split_tokens;
+  const int ns = min((si.nq + S - 1) / S, a.n_split);  // a longer sequence overflows the plan
+  c.full = min(si.nq / S, ns);
+  c.part = ns - c.full;
+  c.rem = c.part ? si.nq - c.full * S : 0;
+  return c;
+}
+
+__device__ inline int size_class(const DecodeArgs& a, int rem) {
+  return NSIZE - 1 - min(NSIZE - 1, (int)(((long long)rem * NSIZE) / a.split_tokens));
+}
+
+// Inclusive scan over the 64 lanes: shifts within rows of 16, then the row
+// totals carried across rows.
+__device__ inline int wave_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+__device__ inline int lane_of(uint64_t m) { return __builtin_ctzll(m); }
+__device__ inline int rdl(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+__device__ inline SeqInfo read_si(const SeqInfo& s, int l) {
+  return SeqInfo{rdl(s.len, l), rdl(s.nw, l), rdl(s.nq, l)};
+}
+
+// hist: this wave's NSIZE counters in LDS
+__device__ Item map_item(const DecodeArgs& a, int item, int* hist) {
+  const int lane = threadIdx.x & 63;
+  Item it{2, 0, 0, 0, {0, 0, 0}};
+  if (lane < NSIZE) hist[lane] = 0;
+  __builtin_amdgcn_wave_barrier();
+  // 1. full chunks
+  int carry = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int b = b0 + lane;
+    SeqInfo si{0, 0, 0};
+    Chunks c{0, 0, 0};
+    if (b < a.batch) {
+      si = seq_info(a, b);
+      c = chunks_of(a, si);
+    }
+    const int inc = wave_scan(c.full);
+    const long long lo = (long long)a.hkv * (carry + inc - c.full);
+    const uint64_t m = __ballot(item >= lo && item < lo + (long long)a.hkv * c.full);
+    if (m) {
+      const int L = lane_of(m);
+      const int n = rdl(c.full, L);
+      const int j = item - (int)(__builtin_amdgcn_readlane((int)lo, L));
+      it.kind = 0;
+      it.b = b0 + L;
+      it.h = j / n;
+      it.split = (j % n + it.b * a.hkv + it.h) % n;
+      it.si = read_si(si, L);
+      return it;
+    }
+    if (c.part) atomicAdd(&hist[size_class(a, c.rem)], 1);
+    carry += rdl(inc, 63);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // 2. remainder chunks: the rank-th one in (size class, sequence) order
+  const int cnt = lane < NSIZE ? hist[lane] : 0;
+  const int cinc = wave_scan(cnt);
+  const int np = rdl(cinc, 63);
+  long long r = item - (long long)a.hkv * carry;
+  if (r < (long long)a.hkv * np) {
+    const int rank = (int)(r / a.hkv);
+    const int cls = lane_of(__ballot(lane < NSIZE && cinc > rank));
+    int k = rank - (rdl(cinc, cls) - rdl(cnt, cls));
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+      const int b = b0 + lane;
+      SeqInfo si{0, 0, 0};
+      Chunks c{0, 0, 0};
+      if (b < a.batch) {
+        si = seq_info(a, b);
+        c = chunks_of(a, si);
+      }
+      const uint64_t m = __ballot(c.part && size_class(a, c.rem) == cls);
+      const int here = __builtin_popcountll(m);
+      if (k < here) {
+        const int before = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const int L = lane_of(__ballot(((m >> lane) & 1) && before == k));
+        it.kind = 0;
+        it.b = b0 + L;
+        it.h = (int)(r % a.hkv);
+        it.split = rdl(c.full, L);
+        it.si = read_si(si, L);
+        return it;
+      }
+      k -= here;
+    }
+    return it;  // not reached: the rank-th remainder chunk exists
+  }
+  r -= (long long)a.hkv * np;
+  if (a.window && r < (long long)a.batch * a.hkv) {  // 3. window items
+    it.kind = 1;
+    it.b = (int)(r / a.hkv);
+    it.h = (int)(r % a.hkv);
+    it.split = a.n_split;
+    it.si = seq_info(a, it.b);
+  }
+  return it;
+}
+
 template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB>
 __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   __shared__ Shared<G> sh;
-  // 1-D grid, the splits of one (sequence, KV head) pair consecutive, their
-  // order rotated by the pair index.  Workgroups go to the 8 XCDs
-  // round-robin by index: without the rotation a split count that is a
-  // multiple of 8 would send split k of every pair to XCD k, and with
-  // sequences of mixed length the XCDs of the late splits would idle.
-  const int pr = blockIdx.x / a.nsp, r = blockIdx.x - pr * a.nsp;
-  const int split = (r + pr) % a.nsp;
-  const int h = pr % a.hkv, b = pr / a.hkv;
+  // 1-D grid of work items, largest first (map_item).  Consecutive items,
+  // which the hardware sends to different XCDs, are mostly the KV heads of
+  // one chunk.
   __shared__ int last_flag;
-  const SeqInfo si = seq_info(a, b);
-  const Plan pl = plan_of(a, si);
-  if (pl.total == 0) {  // no tokens: zeros (NaN if the plan had no room for them)
-    if (split == 0)
-      for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64)
-        a.out[((size_t)b * a.hq + (size_t)h * G) * D + idx] = pl.overflow ? __builtin_nanf("") : 0.0f;
-    return;
+  __shared__ int hist[WAVES][NSIZE];
+  // workgroup p < batch * hkv also writes the (zero) output of pair p if
+  // its sequence is empty
+  const bool zduty = blockIdx.x < (unsigned)(a.batch * a.hkv);
+  const int zlen = zduty ? a.seq_lens[blockIdx.x / a.hkv] : 1;
+  const Item it = map_item(a, blockIdx.x, hist[threadIdx.x >> 6]);
+  if (zduty && zlen <= 0) {
+    const int zb = blockIdx.x / a.hkv, zh = blockIdx.x % a.hkv;
+    for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64)
+      a.out[((size_t)zb * a.hq + (size_t)zh * G) * D + idx] = 0.0f;
   }
-  if (a.window && split == a.n_split) {
+  if (it.kind == 2) return;
+  const int b = it.b, h = it.h, split = it.split;
+  const SeqInfo si = it.si;
+  const Plan pl = plan_of(a, si);
+  if (it.kind == 1) {
     if (si.nw > 0) {
       window_split<G, QB>(a, b, h, si.nw, sh);
       arrive_and_combine<G>(a, b, h, pl, &last_flag);
@@ -1094,7 +1236,6 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
     return;
   }
   const int tok0 = split * a.split_tokens;
-  if (tok0 >= si.nq) return;
   const int tok1 = min(tok0 + a.split_tokens, si.nq);
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
@@ -1139,7 +1280,8 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
     ad.head_tok = ((size_t)b * a.hkv + h) * a.max_tokens;
   }
   const LaneOff lo = lane_offsets<KC, KM, VC, VM>(lt, g);
-  const int per = a.split_tokens / WAVES;
+  // the chunk's tiles spread evenly over the waves
+  const int per = (tok1 - tok0 + WAVES * TILE - 1) / (WAVES * TILE) * TILE;
   const int w0 = __builtin_amdgcn_readfirstlane(tok0 + wave * per);
   const int w1 = __builtin_amdgcn_readfirstlane(min(w0 + per, tok1));
   if constexpr (PAGED) {  // this wave's block-table entries (at most 128 blocks)

@@ -117,6 +117,27 @@ def test_empty_and_zero_sequences():
     full_check(bt, steps=(1,), records=False)
 
 
+@pytest.mark.parametrize("wid", [2, 4])
+def test_large_mixed_batch(wid):
+    """More sequences than one 64-sequence pass of the work-item mapping,
+    with mixed and empty lengths: every full chunk, remainder chunk (of many
+    size classes) and window item must be taken by exactly one workgroup."""
+    rng = np.random.default_rng(2024 + wid)
+    B = 150
+    lens = [int(x) for x in rng.integers(0, 400, B)]
+    lens[3] = lens[70] = lens[149] = 0
+    H.log(f"case: large mixed batch workload {wid} B={B}")
+    wl = synth.workload(wid, batch=B, hq=4, hkv=2, tokens=400)
+    bt = H.build(wl, lens, oracle=True)
+    q = H.queries(wl)
+    want = np.stack([bt.oracle.attend(b, q[b]) for b in range(B)])
+    for split in (128, 256, 0):
+        got = H.run_decode(bt, q, split)
+        for b in (3, 70, 149):
+            assert np.all(got[b] == 0.0)
+        H.check_close(got, want, f"large mixed batch split {split}")
+
+
 def test_overflowing_plan_gives_nan():
     """A sequence longer than the max_seq_len a decode was planned for gets NaN
     outputs (the documented error behaviour); the others are unaffected."""
