@@ -991,14 +991,79 @@ __device__ inline Plan plan_of(const DecodeArgs& a, const SeqInfo& si) {
   return p;
 }
 
-// Wave w merges query heads w, w + 4 (G = 8) of KV head h: lane j reads
-// split j's (m, l), each lane then two output features of every split.
+__device__ inline float2 load_agent2(const float* p) {
+  const uint64_t u = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return float2{__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32))};
+}
+
+__device__ inline void write_combined(const DecodeArgs& a, int b, int h, int G, int hh, const Plan& pl,
+                                      float ws, float2 acc, int lane) {
+  float2 r;
+  if (pl.overflow) {
+    r.x = r.y = __builtin_nanf("");
+  } else if (ws > 0.0f) {
+    r.x = acc.x / ws;
+    r.y = acc.y / ws;
+  } else {
+    r.x = r.y = 0.0f;
+  }
+  *(float2*)(a.out + ((size_t)b * a.hq + (size_t)h * G + hh) * D + 2 * lane) = r;
+}
+
+// Wave w merges query heads w, w + 4 (G = 8) of KV head h.  Up to 64
+// partial rows: lane j reads row j's (m, l) while every lane reads its two
+// output features of the first CB rows, all in flight together (one memory
+// round trip); further rows follow CB at a time.
 template <int G>
 __device__ void combine_heads(const DecodeArgs& a, int b, int h, const Plan& pl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nr = pl.ns + (pl.win ? 1 : 0);  // partial rows: splits, then the window
+  if (nr <= 64) {
+    constexpr int HPW = G > WAVES ? G / WAVES : 1;
+    constexpr int CB = 16;
+    if (wave >= G) return;
+    size_t row0[HPW];
+    float2 ml[HPW], v[HPW][CB];
+    auto prow = [&](int u, int j) { return row0[u] + (j < pl.ns ? j : a.n_split); };
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+      row0[u] = ((size_t)b * a.hq + (size_t)h * G + wave + u * WAVES) * a.nsp;
+      ml[u] = load_agent2(a.part_ml + 2 * prow(u, min(lane, nr - 1)));
+#pragma unroll
+      for (int k = 0; k < CB; ++k) v[u][k] = load_agent2(a.part_o + prow(u, min(k, nr - 1)) * D + 2 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+      const bool mine = lane < nr;
+      float M = mine ? ml[u].x : NEG_INF;
+      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      const float e = mine && ml[u].y > 0.0f ? ml[u].y * exp2_fast(ml[u].x - M) : 0.0f;
+      float ws = e;
+      for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+      float2 acc = {0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < CB; ++k) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), k));
+        acc.x += w * v[u][k].x;  // e is 0 on lanes k >= nr
+        acc.y += w * v[u][k].y;
+      }
+      for (int k0 = CB; k0 < nr; k0 += CB) {
+        float2 x[CB];
+#pragma unroll
+        for (int k = 0; k < CB; ++k) x[k] = load_agent2(a.part_o + prow(u, min(k0 + k, nr - 1)) * D + 2 * lane);
+#pragma unroll
+        for (int k = 0; k < CB; ++k) {
+          const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), k0 + k));
+          acc.x += w * x[k].x;
+          acc.y += w * x[k].y;
+        }
+      }
+      write_combined(a, b, h, G, wave + u * WAVES, pl, ws, acc, lane);
+    }
+    return;
+  }
   for (int hh = wave; hh < G; hh += WAVES) {
     const size_t row0 = ((size_t)b * a.hq + (size_t)h * G + hh) * a.nsp;
-    const int nr = pl.ns + (pl.win ? 1 : 0);  // partial rows: splits, then the window
     auto prow = [&](int j) { return row0 + (j < pl.ns ? j : a.n_split); };
     float M = NEG_INF;
     for (int j = lane; j < nr; j += 64) M = fmaxf(M, load_agent(a.part_ml + 2 * prow(j)));
@@ -1033,16 +1098,7 @@ __device__ void combine_heads(const DecodeArgs& a, int b, int h, const Plan& pl)
       }
     }
     for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
-    float2 r;
-    if (pl.overflow) {
-      r.x = r.y = __builtin_nanf("");
-    } else if (ws > 0.0f) {
-      r.x = acc.x / ws;
-      r.y = acc.y / ws;
-    } else {
-      r.x = r.y = 0.0f;
-    }
-    *(float2*)(a.out + ((size_t)b * a.hq + (size_t)h * G + hh) * D + 2 * lane) = r;
+    write_combined(a, b, h, G, hh, pl, ws, acc, lane);
   }
 }
 
