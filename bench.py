@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: GQA int8)")
+    p.add_argument("--config", type=int, default=2, help="workload 1..6 (default 2: GQA int8)")
     p.add_argument("--replicas", type=int, default=0, help="cache copies (0 = enough for 1 GiB)")
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

@@ -13,8 +13,9 @@
 // per token and head; these kernels favour exactness over speed.
 //
 // Launch order on the caller's stream:
-//   1. append_stats: per-channel key scales / value super-scale of sequences
-//      whose append starts at position 0 (their prefill), then frozen.
+//   1. append_stats: per-channel key scales and key / value super-scales of
+//      sequences whose append starts at position 0 (their prefill), then
+//      frozen.
 //   2. append_quantize: one workgroup per (token, head, sequence); wave 0
 //      quantizes the key, wave 1 the value.  With a recent window it takes
 //      the tokens leaving the window (from the ring or from the input).
@@ -135,20 +136,28 @@ __device__ inline int meta_size(MetaKind m) {
 
 // Quantizes the vector whose elements 2*lane and 2*lane+1 this lane holds,
 // and stores its codes and metadata at token slot `slot`.
+__device__ inline int code_bits(CodeKind c) {
+  return (c == CK_I8 || c == CK_U8) ? 8 : (c == CK_I4 || c == CK_U4) ? 4 : 2;
+}
+
+// Largest code magnitude: 2^(b-1) - 1 (symmetric) or 2^b - 1 (zero point).
+__device__ inline int qmax_sym(int bits) { return (1 << (bits - 1)) - 1; }
+__device__ inline int qmax_zp(int bits) { return (1 << bits) - 1; }
+
 __device__ void quantize_store(const TensorKind k, float x0, float x1, uint8_t* codes,
                                uint8_t* meta, size_t slot, const float* chan, float super,
                                int lane) {
-  const bool b8 = k.code == CK_I8 || k.code == CK_U8;
+  const int bits = code_bits(k.code);
   const bool zp = k.meta == MK_F32Z || k.meta == MK_F16Z;
   int c0 = 0, c1 = 0;
   if (k.channel) {
     // Frozen per-channel scales of the keys.
-    const int qmax = b8 ? 127 : 7;
+    const int qmax = qmax_sym(bits);
     c0 = clampi(rne_code(x0, (double)chan[2 * lane]), -qmax, qmax);
     c1 = clampi(rne_code(x1, (double)chan[2 * lane + 1]), -qmax, qmax);
   } else if (k.meta == MK_U8) {
     // 8-bit scale code relative to the frozen per-head super-scale.
-    const int qmax = b8 ? 127 : 7;
+    const int qmax = qmax_sym(bits);
     const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
     int u = 0;
     if (amax != 0.0f) {
@@ -160,7 +169,7 @@ __device__ void quantize_store(const TensorKind k, float x0, float x1, uint8_t* 
     }
     if (lane == 0) meta[slot] = (uint8_t)u;
   } else if (!zp) {
-    const int qmax = b8 ? 127 : 7;
+    const int qmax = qmax_sym(bits);
     const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
     double s = 1.0;
     uint32_t bits = 0;
@@ -185,7 +194,7 @@ __device__ void quantize_store(const TensorKind k, float x0, float x1, uint8_t* 
     }
   } else {
     // Zero point: the range is widened to include 0; z is the code of 0.
-    const int qmax = b8 ? 255 : 15;
+    const int qmax = qmax_zp(bits);
     const float lo = fminf(wave_min(fminf(x0, x1)), 0.0f);
     const float hi = fmaxf(wave_max(fmaxf(x0, x1)), 0.0f);
     double s = 1.0;
@@ -215,12 +224,17 @@ __device__ void quantize_store(const TensorKind k, float x0, float x1, uint8_t* 
       }
     }
   }
-  if (b8) {
+  if (bits == 8) {
     const uint32_t v = ((uint32_t)(c0 & 0xFF)) | ((uint32_t)(c1 & 0xFF) << 8);
     ((uint16_t*)(codes + slot * (size_t)D))[lane] = (uint16_t)v;
-  } else {
+  } else if (bits == 4) {
     const uint32_t v = ((uint32_t)(c0 & 0xF)) | ((uint32_t)(c1 & 0xF) << 4);
     (codes + slot * (size_t)(D / 2))[lane] = (uint8_t)v;
+  } else {
+    // four 2-bit codes per byte: elements 4j .. 4j+3 come from lanes 2j, 2j+1
+    const uint32_t v = ((uint32_t)(c0 & 3)) | ((uint32_t)(c1 & 3) << 2);
+    const uint32_t odd = (uint32_t)__shfl_xor((int)v, 1);
+    if ((lane & 1) == 0) (codes + slot * (size_t)(D / 4))[lane >> 1] = (uint8_t)(v | (odd << 4));
   }
 }
 
@@ -235,29 +249,34 @@ __global__ void __launch_bounds__(256) append_stats(AppendArgs a) {
     float amax = 0.0f;
     for (int i = 0; i < r.newb; ++i)
       amax = fmaxf(amax, fabsf(load_in(a.k_new, (in_base + i) * D + tid, a.in_bf16)));
-    const int qmax = a.kk.code == CK_I8 ? 127 : 7;
+    const int qmax = qmax_sym(code_bits(a.kk.code));
     a.k_chan[((size_t)b * a.hkv + h) * D + tid] =
         amax == 0.0f ? 1.0f : store_f32((double)amax / qmax);
   }
-  if (a.vk.meta == MK_U8) {
+  for (int w = 0; w < 2; ++w) {
+    const TensorKind k = w == 0 ? a.kk : a.vk;
+    if (k.channel || k.meta != MK_U8) continue;
     // sigma_t = amax_t / qmax per token; S = RN32(max sigma / 255).
     __shared__ double wmax[4];
-    const int w = tid >> 6, lane = tid & 63;
-    const int qmax = a.vk.code == CK_I8 ? 127 : 7;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int qmax = qmax_sym(code_bits(k.code));
+    const void* src = w == 0 ? a.k_new : a.v_new;
     double smax = 0.0;
-    for (int i = w; i < r.newb; i += 4) {
+    for (int i = wave; i < r.newb; i += 4) {
       const size_t row = (in_base + i) * D;
-      const float x0 = load_in(a.v_new, row + 2 * lane, a.in_bf16);
-      const float x1 = load_in(a.v_new, row + 2 * lane + 1, a.in_bf16);
+      const float x0 = load_in(src, row + 2 * lane, a.in_bf16);
+      const float x1 = load_in(src, row + 2 * lane + 1, a.in_bf16);
       const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
       smax = fmax(smax, (double)amax / qmax);
     }
-    if (lane == 0) wmax[w] = smax;
+    if (lane == 0) wmax[wave] = smax;
     __syncthreads();
     if (tid == 0) {
       const double m = fmax(fmax(wmax[0], wmax[1]), fmax(wmax[2], wmax[3]));
-      a.v_super[(size_t)b * a.hkv + h] = m == 0.0 ? 1.0f : store_f32(m / 255.0);
+      float* super = w == 0 ? a.k_super : a.v_super;
+      super[(size_t)b * a.hkv + h] = m == 0.0 ? 1.0f : store_f32(m / 255.0);
     }
+    __syncthreads();
   }
 }
 
@@ -295,7 +314,8 @@ __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   uint8_t* codes = w == 0 ? a.k_codes : a.v_codes;
   uint8_t* meta = w == 0 ? a.k_meta : a.v_meta;
   const float* chan = (w == 0 && k.channel) ? a.k_chan + ((size_t)b * a.hkv + h) * D : nullptr;
-  const float super = (w == 1 && k.meta == MK_U8) ? a.v_super[(size_t)b * a.hkv + h] : 1.0f;
+  const float* sup = w == 0 ? a.k_super : a.v_super;
+  const float super = k.meta == MK_U8 ? sup[(size_t)b * a.hkv + h] : 1.0f;
   quantize_store(k, x0, x1, codes, meta, slot, chan, super, lane);
 }
 
@@ -322,7 +342,7 @@ __global__ void __launch_bounds__(128) append_window(AppendArgs a) {
 kvq_status launch_append(const AppendArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const dim3 heads(a.hkv, a.batch);
-  if (a.kk.channel || a.vk.meta == MK_U8) {
+  if (a.kk.channel || a.kk.meta == MK_U8 || a.vk.meta == MK_U8) {
     hipLaunchKernelGGL(append_stats, heads, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
   }

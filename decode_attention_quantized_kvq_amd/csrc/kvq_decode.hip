@@ -69,6 +69,15 @@ constexpr uint32_t H_M1152 = 0xE480E480u;    // -1152 (signed byte: bias 128)
 constexpr uint32_t H_SIXTEENTH = 0x2C002C00u;  // 1/16
 constexpr uint32_t H_M64 = 0xD400D400u;      // -64
 constexpr uint32_t H_M72 = 0xD480D480u;      // -72
+// 2-bit fields at bit 2r (r = 0..3) of each half, scaled by 4^-r back to units
+constexpr uint32_t H_QUARTER = 0x34003400u;    // 1/4
+constexpr uint32_t H_1_64 = 0x24002400u;       // 1/64
+constexpr uint32_t H_M1026 = 0xE402E402u;      // -1026 (signed 2-bit: bias 2)
+constexpr uint32_t H_M256 = 0xDC00DC00u;       // -256
+constexpr uint32_t H_M258 = 0xDC08DC08u;       // -258
+constexpr uint32_t H_M66 = 0xD420D420u;        // -66
+constexpr uint32_t H_M16 = 0xCC00CC00u;        // -16
+constexpr uint32_t H_M18 = 0xCC80CC80u;        // -18
 
 __device__ inline uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -160,8 +169,9 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 template <int CK>
 struct Codes {
   static constexpr bool B8 = (CK == CK_I8 || CK == CK_U8);
-  static constexpr bool SIGNED = (CK == CK_I8 || CK == CK_I4);
-  static constexpr int ROW = B8 ? D : D / 2;
+  static constexpr bool B2 = (CK == CK_I2 || CK == CK_U2);
+  static constexpr bool SIGNED = (CK == CK_I8 || CK == CK_I4 || CK == CK_I2);
+  static constexpr int ROW = B8 ? D : B2 ? D / 4 : D / 2;
 };
 
 // Converts 4 int8 codes of one dword into two fp16 pairs (d0,d1), (d2,d3),
@@ -196,10 +206,13 @@ __device__ inline uint32_t in_vgpr(uint32_t x) {
 
 struct NibbleMasks {
   uint32_t lo, hi, magic;  // 0x000F000F, 0x00F000F0, 0x64006400
+  uint32_t c[4];           // 2-bit fields: 0x00030003 << 2r
   __device__ inline void init() {
     lo = in_vgpr(0x000F000Fu);
     hi = in_vgpr(0x00F000F0u);
     magic = in_vgpr(MAGIC);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) c[r] = in_vgpr(0x00030003u << (2 * r));
   }
 };
 
@@ -215,13 +228,36 @@ __device__ inline void cvt_b4(uint32_t w, uint32_t out[4], const NibbleMasks& nm
   out[3] = h2_fma((w8 & nm.hi) | nm.magic, H_SIXTEENTH, SIGNED ? H_M72 : H_M64);
 }
 
+// Converts the 2-bit codes of two tokens (token A in the low half-word of x,
+// token B in the high one, feature f at bits 2f) into eight fp16 pairs
+// (feature f of A, feature f of B), f = 0..7.  Field r of a byte, or'ed into
+// the exponent pattern of 1024, reads 1024 + c 4^r; scaling by 4^-r and
+// removing the bias leaves c exactly.
+template <bool SIGNED>
+__device__ inline void cvt_b2(uint32_t x, uint32_t out[8], const NibbleMasks& nm) {
+  if (SIGNED) x ^= 0xAAAAAAAAu;  // two's complement c -> c + 2
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t y = m ? x >> 8 : x;
+    out[4 * m + 0] = h2_add((y & nm.c[0]) | nm.magic, SIGNED ? H_M1026 : H_M1024);
+    out[4 * m + 1] = h2_fma((y & nm.c[1]) | nm.magic, H_QUARTER, SIGNED ? H_M258 : H_M256);
+    out[4 * m + 2] = h2_fma((y & nm.c[2]) | nm.magic, H_SIXTEENTH, SIGNED ? H_M66 : H_M64);
+    out[4 * m + 3] = h2_fma((y & nm.c[3]) | nm.magic, H_1_64, SIGNED ? H_M18 : H_M16);
+  }
+}
+
 // Feature index held by the lanes of k-group g at k-slot e of the j-th score
-// MFMA.  Both key formats cover features [32g, 32g + 32).  8-bit keys are
+// MFMA.  Every key format covers features [32g, 32g + 32).  8-bit keys are
 // used as stored; 4-bit keys are widened to bytes, even nibbles (features
-// 2e) in slots 0..3 and odd nibbles (features 2e - 7) in slots 4..7.
-template <bool B8>
+// 2e) in slots 0..3 and odd nibbles (features 2e - 7) in slots 4..7; 2-bit
+// keys come from dword j / 2 (features 16 (j / 2) + i at bits 2i), shifted
+// right by 4 (j % 2) and 4 (j % 2) + 2 bits and masked to one code per
+// byte: slot e holds code 4 (e % 4) + 2 (j % 2) + e / 4 of that dword.
+template <int KC>
 __device__ inline int key_feature(int j, int g, int e) {
-  return 32 * g + 8 * j + (B8 ? e : (e < 4 ? 2 * e : 2 * e - 7));
+  if (Codes<KC>::B8) return 32 * g + 8 * j + e;
+  if (Codes<KC>::B2) return 32 * g + 16 * (j >> 1) + 4 * (e & 3) + 2 * (j & 1) + (e >> 2);
+  return 32 * g + 8 * j + (e < 4 ? 2 * e : 2 * e - 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -332,10 +368,11 @@ template <int KC, int KM, int VC, int VM>
 __device__ inline LaneOff lane_offsets(int t, int g) {
   constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
   LaneOff o;
-  o.k0 = t * KROW + (Codes<KC>::B8 ? 32 * g : 16 * g);
+  o.k0 = t * KROW + (Codes<KC>::B8 ? 32 * g : Codes<KC>::B2 ? 8 * g : 16 * g);
   o.k1 = o.k0 + 16;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o.v[i] = (4 * i + g) * VROW + (Codes<VC>::B8 ? 8 * t : 4 * t);
+  for (int i = 0; i < 4; ++i)
+    o.v[i] = (4 * i + g) * VROW + (Codes<VC>::B8 ? 8 * t : Codes<VC>::B2 ? 2 * t : 4 * t);
   o.km = t * Meta<KM>::BYTES;
   o.vm = t * Meta<VM>::BYTES;
   return o;
@@ -346,9 +383,9 @@ template <int KC, int KM, int VC, int VM>
 struct TileRaw {
   static constexpr bool KB8 = Codes<KC>::B8;
   static constexpr bool VB8 = Codes<VC>::B8;
-  u32x4 k[2][KB8 ? 2 : 1];   // per 16-token block
+  u32x4 k[2][KB8 ? 2 : 1];   // per 16-token block (2-bit keys: .x, .y)
   u32x2 v8[VB8 ? 8 : 1];     // 8-bit values: 8 tokens x 8 bytes
-  uint32_t v4[VB8 ? 1 : 8];  // 4-bit values: 8 tokens x 4 bytes
+  uint32_t v4[VB8 ? 1 : 8];  // 4-bit values: 8 tokens x 4 bytes; 2-bit: 2 bytes
   Meta<KM> km[2];
   Meta<VM> vm[2];
 };
@@ -366,13 +403,20 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int
     const bool live = t0 + 16 * bb < tend;
     const size_t slot = block_slot<PAGED>(ad, (t0 >> 4) + bb);
     const auto rk = rsrc(ad.k + slot * KROW, live ? 16 * KROW : 0);
-    t.k[bb][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k0, 0, 0);
+    if (Codes<KC>::B2) {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rk, o.k0, 0, 0);
+      t.k[bb][0] = u32x4{w.x, w.y, 0u, 0u};
+    } else {
+      t.k[bb][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k0, 0, 0);
+    }
     if (Codes<KC>::B8) t.k[bb][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k1, 0, 0);
     const auto rv = rsrc(ad.v + slot * VROW, live ? 16 * VROW : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (Codes<VC>::B8)
         t.v8[4 * bb + i] = __builtin_amdgcn_raw_buffer_load_b64(rv, o.v[i], 0, 0);
+      else if (Codes<VC>::B2)
+        t.v4[4 * bb + i] = __builtin_amdgcn_raw_buffer_load_b16(rv, o.v[i], 0, 0);
       else
         t.v4[4 * bb + i] = __builtin_amdgcn_raw_buffer_load_b32(rv, o.v[i], 0, 0);
     }
@@ -399,6 +443,12 @@ __device__ inline long key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb) {
       lo ^= 0x80808080u;
       hi ^= 0x80808080u;
     }
+  } else if constexpr (Codes<KC>::B2) {
+    uint32_t w = t.k[bb][0][J >> 1];
+    if (KC == CK_I2) w ^= 0xAAAAAAAAu;  // two's complement 2-bit c -> c + 2
+    constexpr int SH = 4 * (J & 1);
+    lo = (w >> SH) & 0x03030303u;
+    hi = (w >> (SH + 2)) & 0x03030303u;
   } else {
     uint32_t w = t.k[bb][0][J];
     if (KC == CK_I4) w ^= 0x88888888u;  // two's complement nibble c -> c + 8
@@ -412,7 +462,7 @@ __device__ inline long key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb) {
 // code + KOFF, so KOFF * sum(Q) comes off the score).
 template <int KC>
 __device__ inline float key_offset() {
-  return KC == CK_U8 ? -128.0f : KC == CK_I4 ? 8.0f : 0.0f;
+  return KC == CK_U8 ? -128.0f : KC == CK_I4 ? 8.0f : KC == CK_I2 ? 2.0f : 0.0f;
 }
 
 // Value operands of the 8 output MFMAs: lane (c, g) gives feature 8c + j of
@@ -431,6 +481,12 @@ __device__ inline void value_frags(const TileRaw<KC, KM, VC, VM>& t, half8 out[8
                              perm(B.y, A.y, 0x05010400u), perm(B.y, A.y, 0x07030602u)};
 #pragma unroll
       for (int q = 0; q < 4; ++q) cvt_b8<S>(x[q], pr[2 * q][pp], pr[2 * q + 1][pp]);
+    } else if (Codes<VC>::B2) {
+      // bytes (A0, A1, B0, B1): features 0..7 of tokens A and B
+      uint32_t o[8];
+      cvt_b2<S>(perm(t.v4[2 * pp + 1], t.v4[2 * pp], 0x05040100u), o, nm);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pr[q][pp] = o[q];
     } else {
       const uint32_t A = t.v4[2 * pp], B = t.v4[2 * pp + 1];
       uint32_t o[4];
@@ -1297,7 +1353,6 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lt = lane & 15, g = lane >> 4;
-  constexpr bool KB8 = Codes<KC>::B8;
   constexpr int HPG = RowState<G>::HPG;
 
   // 1. query (and per-channel key scale) loads, issued first.  Score operand
@@ -1315,6 +1370,8 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   }
   const size_t crow = ((size_t)b * a.hkv + h) * D;
   if (KCH) load_q_run<false>(cr, a.k_chan, crow, 32 * g, 32, 0);
+  // 8-bit key scale codes: their per-head super-scale joins the score scale
+  const float ksup = KM == MK_U8 ? a.k_super[(size_t)b * a.hkv + h] : 1.0f;
   const bool qvalid = qlimb < 3 && (G == 8 || hl < G);
 
   // 2. the first two tiles of this wave's range, in flight while the query
@@ -1383,7 +1440,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
       uint64_t pk = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = rintf(qv[key_feature<KB8>(j, 0, e)] * sc);
+        const float x = rintf(qv[key_feature<KC>(j, 0, e)] * sc);
         qsum += x;
         const int Q = (int)x;
         const int l2 = (int)(int8_t)(Q & 0xFF);
@@ -1395,7 +1452,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
       }
       qa[u][j] = (long)pk;
     }
-    qs_row[u] = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128) / 2^e
+    qs_row[u] = LOG2E * 0.08838834764831845f * inv * ksup;  // log2(e) / sqrt(128) / 2^e
     sq_row[u] = rows_sum(qsum);
   }
   // score scale and query sum of each head, from the lane of its limb-0 row
@@ -1525,6 +1582,12 @@ kvq_status launch_decode(const DecodeArgs& a, void* stream) {
     e = launch_g<CK_I8, MK_F32, false, CK_I4, MK_F32>(a, s);
   else if (k.code == CK_U8 && k.meta == MK_F16Z && v.code == CK_U8 && v.meta == MK_F16Z)
     e = launch_g<CK_U8, MK_F16Z, false, CK_U8, MK_F16Z>(a, s);
+  else if (k.code == CK_I2 && k.meta == MK_F32 && v.code == CK_I2 && v.meta == MK_F32)
+    e = launch_g<CK_I2, MK_F32, false, CK_I2, MK_F32>(a, s);
+  else if (k.code == CK_I2 && k.meta == MK_U8 && v.code == CK_I2 && v.meta == MK_U8)
+    e = launch_g<CK_I2, MK_U8, false, CK_I2, MK_U8>(a, s);
+  else if (k.code == CK_U2 && k.meta == MK_F16Z && v.code == CK_U2 && v.meta == MK_F16Z)
+    e = launch_g<CK_U2, MK_F16Z, false, CK_U2, MK_F16Z>(a, s);
   else
     return KVQ_ERR_UNSUPPORTED;
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;

@@ -48,10 +48,14 @@ kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
   if (f.scale_fmt == KVQ_SCALE_U8_SUPER && f.zero_point) return KVQ_ERR_INVALID_ARG;
   if (f.axis == KVQ_AXIS_CHANNEL && (f.zero_point || f.scale_fmt != KVQ_SCALE_F32))
     return KVQ_ERR_INVALID_ARG;
-  if (f.bits == 2) return KVQ_ERR_UNSUPPORTED;
-  const bool b8 = f.bits == 8;
-  k.code = f.zero_point ? (b8 ? CK_U8 : CK_U4) : (b8 ? CK_I8 : CK_I4);
+  if (f.bits == 8)
+    k.code = f.zero_point ? CK_U8 : CK_I8;
+  else if (f.bits == 4)
+    k.code = f.zero_point ? CK_U4 : CK_I4;
+  else
+    k.code = f.zero_point ? CK_U2 : CK_I2;
   if (f.axis == KVQ_AXIS_CHANNEL) {
+    if (f.bits == 2) return KVQ_ERR_UNSUPPORTED;
     k.channel = true;
     k.meta = MK_NONE;
     if (out) *out = k;
@@ -60,7 +64,7 @@ kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
   if (f.scale_fmt == KVQ_SCALE_U8_SUPER) {
     k.meta = MK_U8;
     if (out) *out = k;
-    return is_key ? KVQ_ERR_UNSUPPORTED : KVQ_OK;
+    return KVQ_OK;
   }
   if (f.scale_fmt == KVQ_SCALE_F32)
     k.meta = f.zero_point ? MK_F32Z : MK_F32;
@@ -95,7 +99,7 @@ static kvq_status check_config(const kvq_config* c, bool kernels) {
   if (c->max_tokens % 16) return KVQ_ERR_UNSUPPORTED;
   if (c->block_tokens != 0 && c->block_tokens != 16) return KVQ_ERR_UNSUPPORTED;
   if (c->window % 16 || c->window > 256) return KVQ_ERR_UNSUPPORTED;
-  if (c->window && (kk.channel || vk.meta == MK_U8)) return KVQ_ERR_UNSUPPORTED;
+  if (c->window && (kk.channel || kk.meta == MK_U8 || vk.meta == MK_U8)) return KVQ_ERR_UNSUPPORTED;
   // The decode kernels are instantiated for these key/value pairs.
   const bool ok =
       (kk.code == CK_I8 && kk.meta == MK_F32 && vk.code == CK_I8 && vk.meta == MK_F32) ||
@@ -103,7 +107,10 @@ static kvq_status check_config(const kvq_config* c, bool kernels) {
       (kk.code == CK_I8 && kk.channel && vk.code == CK_I4 && vk.meta == MK_U8) ||
       (kk.code == CK_I4 && kk.meta == MK_F32 && vk.code == CK_I4 && vk.meta == MK_F32) ||
       (kk.code == CK_I8 && kk.meta == MK_F32 && vk.code == CK_I4 && vk.meta == MK_F32) ||
-      (kk.code == CK_U8 && kk.meta == MK_F16Z && vk.code == CK_U8 && vk.meta == MK_F16Z);
+      (kk.code == CK_U8 && kk.meta == MK_F16Z && vk.code == CK_U8 && vk.meta == MK_F16Z) ||
+      (kk.code == CK_I2 && kk.meta == MK_F32 && vk.code == CK_I2 && vk.meta == MK_F32) ||
+      (kk.code == CK_I2 && kk.meta == MK_U8 && vk.code == CK_I2 && vk.meta == MK_U8) ||
+      (kk.code == CK_U2 && kk.meta == MK_F16Z && vk.code == CK_U2 && vk.meta == MK_F16Z);
   return ok ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
 }
 
@@ -142,7 +149,7 @@ static Plan make_plan(const kvq_config* c, int max_seq_len, int split_tokens) {
 }
 
 struct LayerSizes {  // bytes of one layer of each buffer
-  size_t k_codes, v_codes, k_meta, v_meta, k_win, v_win, k_chan, v_super;
+  size_t k_codes, v_codes, k_meta, v_meta, k_win, v_win, k_chan, v_super, k_super;
 };
 
 static LayerSizes layer_sizes(const kvq_config* c) {
@@ -157,12 +164,15 @@ static LayerSizes layer_sizes(const kvq_config* c) {
   s.k_win = s.v_win = heads * c->window * c->head_dim * 2;
   s.k_chan = (c->key.bits != 16 && c->key.axis == KVQ_AXIS_CHANNEL) ? heads * c->head_dim * 4 : 0;
   s.v_super = (c->value.bits != 16 && c->value.scale_fmt == KVQ_SCALE_U8_SUPER) ? heads * 4 : 0;
+  s.k_super = (c->key.bits != 16 && c->key.axis == KVQ_AXIS_TOKEN &&
+               c->key.scale_fmt == KVQ_SCALE_U8_SUPER) ? heads * 4 : 0;
   return s;
 }
 
 static bool resolve_layer(const kvq_config* c, const kvq_cache* cache, int layer,
                           const LayerSizes& s, uint8_t** kc, uint8_t** vc, uint8_t** km,
-                          uint8_t** vm, uint16_t** kw, uint16_t** vw, float** kch, float** vsu) {
+                          uint8_t** vm, uint16_t** kw, uint16_t** vw, float** kch, float** vsu,
+                          float** ksu) {
   const size_t L = (size_t)layer;
   auto at = [&](void* base, size_t per) -> uint8_t* {
     return base ? (uint8_t*)base + L * per : nullptr;
@@ -175,12 +185,14 @@ static bool resolve_layer(const kvq_config* c, const kvq_cache* cache, int layer
   *vw = (uint16_t*)at(cache->v_win, s.v_win);
   *kch = (float*)at(cache->k_chan_scale, s.k_chan);
   *vsu = (float*)at(cache->v_super, s.v_super);
+  *ksu = (float*)at(cache->k_super, s.k_super);
   if (!*kc || !*vc) return false;
   if (s.k_meta && !*km) return false;
   if (s.v_meta && !*vm) return false;
   if (s.k_win && (!*kw || !*vw)) return false;
   if (s.k_chan && !*kch) return false;
   if (s.v_super && !*vsu) return false;
+  if (s.k_super && !*ksu) return false;
   if (!cache->seq_lens) return false;
   if (c->block_tokens && !cache->block_table) return false;
   return true;
@@ -219,6 +231,7 @@ kvq_status kvq_get_buffer_sizes(const kvq_config* cfg, kvq_buffer_sizes* out) {
   out->v_win = L * s.v_win;
   out->k_chan_scale = L * s.k_chan;
   out->v_super = L * s.v_super;
+  out->k_super = L * s.k_super;
   return KVQ_OK;
 }
 
@@ -284,7 +297,7 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
   AppendArgs a{};
   const LayerSizes s = layer_sizes(cfg);
   if (!resolve_layer(cfg, cache, layer, s, &a.k_codes, &a.v_codes, &a.k_meta, &a.v_meta,
-                     &a.k_win, &a.v_win, &a.k_chan, &a.v_super))
+                     &a.k_win, &a.v_win, &a.k_chan, &a.v_super, &a.k_super))
     return KVQ_ERR_INVALID_ARG;
   classify(cfg->key, true, &a.kk);
   classify(cfg->value, false, &a.vk);
@@ -328,8 +341,8 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   const LayerSizes s = layer_sizes(cfg);
   uint8_t *kc, *vc, *km, *vm;
   uint16_t *kw, *vw;
-  float *kch, *vsu;
-  if (!resolve_layer(cfg, cache, layer, s, &kc, &vc, &km, &vm, &kw, &vw, &kch, &vsu))
+  float *kch, *vsu, *ksu;
+  if (!resolve_layer(cfg, cache, layer, s, &kc, &vc, &km, &vm, &kw, &vw, &kch, &vsu, &ksu))
     return KVQ_ERR_INVALID_ARG;
   a.k_codes = kc;
   a.v_codes = vc;
@@ -339,6 +352,7 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   a.v_win = vw;
   a.k_chan = kch;
   a.v_super = vsu;
+  a.k_super = ksu;
   a.block_table = cache->block_table;
   a.seq_lens = cache->seq_lens;
   a.q = q;

@@ -14,7 +14,9 @@ enum CodeKind : int {
   CK_U8 = 1,   // unsigned int8 (zero-point formats)
   CK_I4 = 2,   // signed int4 nibbles, two per byte
   CK_U4 = 3,   // unsigned int4 nibbles (zero-point formats)
-  CK_BF16 = 4  // unquantized bf16 values
+  CK_BF16 = 4, // unquantized bf16 values
+  CK_I2 = 5,   // signed int2, four per byte (symmetric codes -1..1)
+  CK_U2 = 6    // unsigned int2 (zero-point formats)
 };
 
 // What is stored per token beside the codes.
@@ -57,6 +59,7 @@ struct AppendArgs {
   uint16_t* v_win;
   float* k_chan;
   float* v_super;
+  float* k_super;
   int batch, hkv, n_new, max_tokens, window, paged, num_blocks, bt_stride;
   int in_bf16;
   TensorKind kk, vk;
@@ -72,6 +75,7 @@ struct DecodeArgs {
   const uint16_t* v_win;
   const float* k_chan;
   const float* v_super;
+  const float* k_super;
   const int32_t* block_table;
   const int32_t* seq_lens;
   const void* q;

@@ -55,7 +55,8 @@ class CacheDesc(ctypes.Structure):
                 ("k_meta", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
                 ("k_win", ctypes.c_void_p), ("v_win", ctypes.c_void_p),
                 ("k_chan_scale", ctypes.c_void_p), ("v_super", ctypes.c_void_p),
-                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("k_super", ctypes.c_void_p)]
 
 
 class Bytes(ctypes.Structure):
@@ -64,7 +65,8 @@ class Bytes(ctypes.Structure):
 
 class BufferSizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("k_codes", "v_codes", "k_meta", "v_meta",
-                                                "k_win", "v_win", "k_chan_scale", "v_super")]
+                                                "k_win", "v_win", "k_chan_scale", "v_super",
+                                                "k_super")]
 
 
 class DecodeOpts(ctypes.Structure):
@@ -219,7 +221,7 @@ class KvqCache:
         return CacheDesc(_ptr(b["k_codes"]), _ptr(b["v_codes"]), _ptr(b["k_meta"]),
                          _ptr(b["v_meta"]), _ptr(b["k_win"]), _ptr(b["v_win"]),
                          _ptr(b["k_chan_scale"]), _ptr(b["v_super"]),
-                         _ptr(self.block_table), _ptr(self.seq_lens))
+                         _ptr(self.block_table), _ptr(self.seq_lens), _ptr(b["k_super"]))
 
 
 def _check_input(t: torch.Tensor, cfg: Config, shape, what: str):

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five decode workloads.
+"""Seeded synthetic inputs for the decode workloads.
 
 This module only draws random numbers and rounds them to the input dtype; it
 holds none of the quantization or attention arithmetic.  Both the HIP path and
@@ -18,6 +18,11 @@ synthetic):
   5 asym_kv      batch 16, 32/8 heads, 65536 tokens; keys int8 per-channel
                  (outlier channels as in 2), values Laplace(0,1) int4 with an
                  8-bit scale relative to a per-head fp32 super-scale.
+  6 int2_super   batch 32, 32/8 heads, 8192 tokens, same values as 2; keys and
+                 values 2-bit symmetric with an 8-bit scale code relative to a
+                 per-head fp32 super-scale (the 2-bit metadata remedy of "KV
+                 Cache Quantization and Per-Token Scale Placement", section
+                 "Per-token scales and where they can live").
 
 Recipe: every draw comes from ``np.random.default_rng(SeedSequence(key))``
 with a key that names the workload, the replica and the tensor, so any
@@ -58,6 +63,11 @@ WORKLOADS: Dict[int, dict] = {
             key=dict(bits=8, axis="channel", zero_point=False, scale="f32"),
             value=dict(bits=4, axis="token", zero_point=False, scale="u8_super"),
             window=0, block_tokens=0, outlier_keys=4, value_dist="laplace"),
+    6: dict(name="int2_super", batch=32, hq=32, hkv=8, d=128, tokens=8192,
+            lengths=None, in_dtype="bf16",
+            key=dict(bits=2, axis="token", zero_point=False, scale="u8_super"),
+            value=dict(bits=2, axis="token", zero_point=False, scale="u8_super"),
+            window=0, block_tokens=0, outlier_keys=4, value_dist="normal"),
 }
 
 
@@ -196,7 +206,9 @@ def kv_device(wl: dict, lens: List[int], replica: int = 0, device: str = "cuda")
                 kb[h, :, ch] *= 10.0
         if wl["value_dist"] == "laplace":
             u = torch.rand((H, T, D), generator=gen, device=device, dtype=torch.float32) - 0.5
-            vb = -torch.sign(u) * torch.log1p(-2.0 * u.abs())
+            # inverse CDF; rand() can return exactly 0 (u = -1/2, log 0), so the
+            # tail is cut at the smallest nonzero draw, 2^-24
+            vb = -torch.sign(u) * torch.log1p(-2.0 * u.abs()).clamp_min(-16.635532333438686)
         else:
             vb = torch.randn((H, T, D), generator=gen, device=device, dtype=torch.float32)
         kb[:, lens[b]:] = 0

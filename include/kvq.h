@@ -22,7 +22,9 @@
  *    granularity defines which values share a scale"); per-channel key scales
  *    fixed by the first append (P3, "Per-token scales and where they can
  *    live"); an 8-bit scale code relative to a per-head fp32 super-scale
- *    (same section); the newest tokens kept in bf16 (P1, "Cache growth changes
+ *    for keys or values, and 2-bit codes, the width at which the same
+ *    section says 4-byte per-token scales cost 12 percent and schemes move
+ *    to such 8-bit relative scales; the newest tokens kept in bf16 (P1, "Cache growth changes
  *    the serving trade"); 16-token blocks placed through a block table (P2,
  *    "Metadata and block layout remain part of physical memory use").
  *  - kvq_decode_attn: s_i = q . k_hat_i / sqrt(D), a = softmax(s),
@@ -50,7 +52,7 @@
  *    fp16 scale above 65504 stores 65504;
  *  - per-channel key scales: RN32(absmax over the first append / qmax) per
  *    feature, frozen; later tokens clamp;
- *  - super-scaled values: sigma_t = fl64(amax_t/qmax); per head
+ *  - super-scaled keys or values: sigma_t = fl64(amax_t/qmax); per head
  *    S = RN32(max_t sigma_t / 255) over the first append, frozen;
  *    u_t = clamp(rint(fl64(sigma_t / S)), 1, 255) (0 for an all-zero vector);
  *    codes use the exact effective scale u_t * S.
@@ -66,11 +68,13 @@
  *    quantized position p of sequence b lives in block
  *    block_table[b][p / 16], slot p % 16
  *  window  [L][B][H_kv][window][D] bf16; position p sits in slot p % window
- *  k_chan_scale [L][B][H_kv][D] fp32;  v_super [L][B][H_kv] fp32
+ *  k_chan_scale [L][B][H_kv][D] fp32;  k_super, v_super [L][B][H_kv] fp32
  *  code bytes: int8 codes as two's complement bytes (unsigned bytes with a
  *    zero point); int4 codes packed two per byte, element 2j in the low nibble
  *    and 2j+1 in the high nibble (two's complement nibbles, or unsigned with a
- *    zero point)
+ *    zero point); int2 codes packed four per byte, element 4j+i in bits
+ *    [2i, 2i+2) of byte j (two's complement, symmetric codes in [-1, 1], or
+ *    unsigned in [0, 3] with a zero point)
  *  meta element per token: f32 scale (4 B); f32 scale + f32 zero point
  *    (8 B); f16 scale (2 B); f16 scale + f16 zero point (4 B, scale in the
  *    low half); u8 scale code (1 B)
@@ -124,8 +128,7 @@ typedef enum { KVQ_DT_F32 = 0, KVQ_DT_BF16 = 1 } kvq_dtype;
  * values share a scale": bit width, grouping, scale precision and the key /
  * value treatment together define a format). */
 typedef struct {
-  int bits;                /* 8 or 4; 16 = bf16 kept unquantized; 2 is
-                              accepted by kvq_cache_bytes only */
+  int bits;                /* 8, 4 or 2; 16 = bf16 kept unquantized */
   kvq_axis axis;
   int zero_point;          /* 1: unsigned codes with an integer zero point */
   kvq_scale_fmt scale_fmt;
@@ -165,6 +168,8 @@ typedef struct {
   const int32_t* seq_lens; /* [batch]: tokens of each sequence, counting the
                               tokens of the current append; the library only
                               reads it */
+  void* k_super;           /* per-head key super-scales (keys with an 8-bit
+                              scale code) */
 } kvq_cache;
 
 /* Byte breakdown of a cache (P2, "Metadata and block layout remain part of
@@ -181,13 +186,21 @@ typedef struct {
 /* Bytes to allocate for each buffer of kvq_cache (0 = not used). */
 typedef struct {
   size_t k_codes, v_codes, k_meta, v_meta, k_win, v_win, k_chan_scale, v_super;
+  size_t k_super;
 } kvq_buffer_sizes;
 
 /* Human-readable name of a status.  Never NULL. */
 const char* kvq_status_string(kvq_status s);
 
 /* Checks that cfg describes a cache the kernels run: KVQ_OK,
- * KVQ_ERR_INVALID_ARG or KVQ_ERR_UNSUPPORTED. */
+ * KVQ_ERR_INVALID_ARG or KVQ_ERR_UNSUPPORTED.  The decode kernels run these
+ * (key; value) pairs, per token unless marked:
+ *   int8 f32 scale; int8 f32 scale          int8 f32; int4 f32
+ *   int4 f32; int4 f32                      int8 per-channel; int4 u8 super
+ *   uint4 f16 scale + zero; the same        uint8 f16 scale + zero; the same
+ *   int2 f32; int2 f32                      int2 u8 super; int2 u8 super
+ *   uint2 f16 scale + zero; the same
+ * An 8-bit scale code (u8 super) or per-channel keys exclude a window. */
 kvq_status kvq_validate(const kvq_config* cfg);
 
 /* Fills *out with the byte size of each buffer of the layout above. */
@@ -197,7 +210,7 @@ kvq_status kvq_get_buffer_sizes(const kvq_config* cfg, kvq_buffer_sizes* out);
  * (payload 2 L H_kv D T b, generalised to separate key and value widths) plus
  * metadata (P3, "Per-token scales and where they can live"), window and
  * padding.  host_seq_lens: [batch] host array, or NULL for max_tokens each.
- * Pure host arithmetic; accepts bits 2 as well.  Returns the total (0 on an
+ * Pure host arithmetic.  Returns the total (0 on an
  * invalid configuration) and fills *out when out is not NULL. */
 size_t kvq_cache_bytes(const kvq_config* cfg, const int32_t* host_seq_lens, kvq_bytes* out);
 

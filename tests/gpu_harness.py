@@ -107,6 +107,25 @@ def build(wl: dict, lens: List[int], decode_steps: int = 0, replica: int = 0,
     return Built(wl, cfg, cache, orc, list(lens), table, {"kv": full})
 
 
+def build_full(wl: dict, lens: List[int]) -> Built:
+    """A full-size cache built the way the benchmark builds it: inputs drawn on
+    the device (synth.kv_device), one append of every sequence.  No oracle:
+    tests copy the input slices they sample back to the host."""
+    table = None
+    nb = mb = 0
+    if wl["block_tokens"]:
+        table, pool = synth.block_table(wl, lens)
+        nb, mb = max(pool, 1), table.shape[1]
+    cfg = make_config(wl, lens, nb, mb)
+    assert K.validate(cfg) == K.KVQ_OK
+    cache = K.KvqCache(cfg, "cuda", None if table is None else torch.from_numpy(table))
+    k, v = synth.kv_device(wl, lens)
+    cache.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+    K.quantize_append(cache, 0, k, v, torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    return Built(wl, cfg, cache, None, list(lens), table, {"k": k, "v": v})
+
+
 def queries(wl, step=0, replica=0):
     return np.stack([synth.queries(wl, b, replica, step) for b in range(wl["batch"])])
 
@@ -152,6 +171,11 @@ def unpack_codes(raw: np.ndarray, bits: int, signed: bool) -> np.ndarray:
     """[..., row bytes] -> [..., D] integer codes."""
     if bits == 8:
         return raw.view(np.int8).astype(np.int32) if signed else raw.astype(np.int32)
+    if bits == 2:
+        # four codes per byte, element 4j + i in bits [2i, 2i + 2) of byte j
+        c = np.stack([(raw >> (2 * i)) & 3 for i in range(4)], axis=-1).astype(np.int32)
+        c = c.reshape(*raw.shape[:-1], raw.shape[-1] * 4)
+        return np.where(c >= 2, c - 4, c) if signed else c
     lo = (raw & 0xF).astype(np.int32)
     hi = (raw >> 4).astype(np.int32)
     c = np.stack([lo, hi], axis=-1).reshape(*raw.shape[:-1], raw.shape[-1] * 2)
@@ -176,7 +200,7 @@ def device_records(bt: Built, t: str, b: int, h: int, n: int) -> dict:
     meta = host(bt.cache.buffers[f"{t}_meta"])
     if scale == "u8_super":
         out["u"] = meta[slots]
-        out["S"] = host(bt.cache.buffers["v_super"]).view(np.float32)[b * bt.cfg.num_kv_heads + h]
+        out["S"] = host(bt.cache.buffers[f"{t}_super"]).view(np.float32)[b * bt.cfg.num_kv_heads + h]
     elif scale == "f32" and not zp:
         out["s"] = meta.view(np.float32)[slots]
     elif scale == "f32":

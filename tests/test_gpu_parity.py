@@ -39,12 +39,59 @@ def test_tiny_full_size():
     full_check(bt, steps=(0, 1, 2))
 
 
+@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6])
+def test_full_size_sampled(wid):
+    """Each workload at its full size, decoded in the launch configuration the
+    benchmark times (library-chosen split).  For sampled (sequence, KV head)
+    pairs the oracle quantizes that pair's input tokens (copied back from the
+    device) and attends its G query heads: codes and metadata bit for bit,
+    outputs within the acceptance bar."""
+    wl = synth.workload(wid)
+    lens = synth.seq_lengths(wl)
+    H.log(f"case: workload {wid} {wl['name']} full size, {sum(lens)} tokens")
+    bt = H.build_full(wl, lens)
+    q = H.queries(wl)
+    got = H.run_decode(bt, q)
+    G = wl["hq"] // wl["hkv"]
+    rng = np.random.default_rng(77 + wid)
+    longest = int(np.argmax(lens))
+    pairs = {(0, 0), (longest, wl["hkv"] - 1)}
+    while len(pairs) < 4:
+        pairs.add((int(rng.integers(wl["batch"])), int(rng.integers(wl["hkv"]))))
+    kf, vf = H.oracle_fmt(wl["key"]), H.oracle_fmt(wl["value"])
+    for b, h in sorted(pairs):
+        n = lens[b]
+        kx = bt.inputs["k"][b, h, :n].float().cpu().numpy().astype(np.float64)
+        vx = bt.inputs["v"][b, h, :n].float().cpu().numpy().astype(np.float64)
+        orc = H.O.OracleCache(1, 1, wl["d"], kf, vf, wl["window"])
+        orc.append(0, kx[None], vx[None])
+        for t in ("k", "v"):
+            st = orc.stored(0, t)
+            m = st.codes.shape[1]
+            if m:
+                dev = H.device_records(bt, t, b, h, m)
+                assert np.array_equal(dev["codes"], st.codes[0]), f"{t} codes differ at b={b} h={h}"
+                for key, ref in (("s", st.s), ("z", st.z)):
+                    if key in dev:
+                        assert np.array_equal(H._bits(dev[key]), H._bits(ref[0])), f"{t} {key} b={b} h={h}"
+                if "u" in dev:
+                    assert np.array_equal(dev["u"], st.u[0]), f"{t} scale codes b={b} h={h}"
+                    assert np.array_equal(H._bits(np.float32(dev["S"])), H._bits(np.float32(st.S[0])))
+                if "chan" in dev:
+                    assert np.array_equal(H._bits(dev["chan"]), H._bits(st.chan[0])), "channel scales"
+        want = orc.attend(0, q[b, h * G:(h + 1) * G])
+        H.check_close(got[b, h * G:(h + 1) * G], want, f"{wl['name']} full size b={b} h={h}")
+    del bt
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("wid,over,lens,decode_steps,chunks", [
     (2, dict(batch=2, tokens=1024), [1000, 777], 3, 1),
     (3, dict(batch=2, tokens=1024), [1000, 651], 3, 2),
     (4, dict(batch=3, tokens=1024), [1024, 300, 131], 5, 2),
     (5, dict(batch=2, tokens=1024), [1000, 613], 4, 1),
-], ids=["w2", "w3", "w4", "w5"])
+    (6, dict(batch=2, tokens=1024), [1000, 555], 3, 2),
+], ids=["w2", "w3", "w4", "w5", "w6"])
 def test_workload_reduced(wid, over, lens, decode_steps, chunks):
     """Each workload's formats at a size the oracle finishes in seconds, with
     ragged lengths, a prefill in one or two appends, then decode appends."""
@@ -57,7 +104,7 @@ def test_workload_reduced(wid, over, lens, decode_steps, chunks):
 
 
 @pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 300])
-@pytest.mark.parametrize("wid", [2, 3, 5])
+@pytest.mark.parametrize("wid", [2, 3, 5, 6])
 def test_tile_edges(wid, n):
     """Lengths around the 16-token block and 32-token tile edges."""
     H.log(f"case: tile edges workload {wid} n={n}")
@@ -77,7 +124,8 @@ def test_window_edges(n):
 
 
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 8), (4, 2)])
-@pytest.mark.parametrize("fmt", ["i8", "u4z", "i4", "i8k_i4v", "u8z", "chan_super"])
+@pytest.mark.parametrize("fmt", ["i8", "u4z", "i4", "i8k_i4v", "u8z", "chan_super", "i2", "i2_super",
+                                 "u2z"])
 def test_formats_and_groups(fmt, hq, hkv):
     """Every instantiated key/value format pair at every group size G."""
     H.log(f"case: format {fmt} hq={hq} hkv={hkv}")
@@ -88,6 +136,9 @@ def test_formats_and_groups(fmt, hq, hkv):
         "i8k_i4v": (dict(bits=8), dict(bits=4)),
         "u8z": (dict(bits=8, zero_point=True, scale="f16"), dict(bits=8, zero_point=True, scale="f16")),
         "chan_super": (dict(bits=8, axis="channel"), dict(bits=4, scale="u8_super")),
+        "i2": (dict(bits=2), dict(bits=2)),
+        "i2_super": (dict(bits=2, scale="u8_super"), dict(bits=2, scale="u8_super")),
+        "u2z": (dict(bits=2, zero_point=True, scale="f16"), dict(bits=2, zero_point=True, scale="f16")),
     }
     k, v = specs[fmt]
     wl = synth.workload(2, batch=2, hq=hq, hkv=hkv, tokens=512, key=k, value=v)

@@ -52,12 +52,12 @@ def oracle_fmt(spec):
                           spec.get("scale", "f32"))
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6])
 def test_workloads_validate(wid):
     assert K.validate(cfg_of(synth.workload(wid))) == K.KVQ_OK
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6])
 def test_cache_bytes_match_oracle(wid):
     wl = synth.workload(wid)
     lens = synth.seq_lengths(wl)
@@ -97,6 +97,15 @@ def test_buffer_sizes():
     sz5 = K.buffer_sizes(cfg_of(wl5))
     assert sz5.k_chan_scale == 16 * 8 * 128 * 4 and sz5.v_super == 16 * 8 * 4
     assert sz5.v_codes == 16 * 8 * 65536 * 64 and sz5.v_meta == 16 * 8 * 65536
+    assert sz5.k_super == 0
+    # 2-bit codes with 8-bit scale codes for keys and values
+    s2 = dict(bits=2, scale="u8_super")
+    cfg2 = K.make_config(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, max_tokens=64,
+                         key=s2, value=s2, num_layers=2)
+    sz2 = K.buffer_sizes(cfg2)
+    assert sz2.k_codes == sz2.v_codes == 2 * 3 * 2 * 64 * 32
+    assert sz2.k_meta == sz2.v_meta == 2 * 3 * 2 * 64
+    assert sz2.k_super == sz2.v_super == 2 * 3 * 2 * 4
 
 
 def test_validation_errors():
@@ -113,7 +122,10 @@ def test_validation_errors():
         (dict(head_dim=64), K.KVQ_ERR_UNSUPPORTED),
         (dict(num_q_heads=32, num_kv_heads=2), K.KVQ_ERR_UNSUPPORTED),   # G = 16
         (dict(max_tokens=40), K.KVQ_ERR_UNSUPPORTED),
-        (dict(key=dict(bits=2), value=dict(bits=2)), K.KVQ_ERR_UNSUPPORTED),
+        (dict(key=dict(bits=2), value=dict(bits=8)), K.KVQ_ERR_UNSUPPORTED),   # no such pair
+        (dict(key=dict(bits=2, axis="channel"), value=dict(bits=2)), K.KVQ_ERR_UNSUPPORTED),
+        (dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super"),
+              window=16), K.KVQ_ERR_UNSUPPORTED),
         (dict(key=dict(bits=16), value=dict(bits=16)), K.KVQ_ERR_UNSUPPORTED),
         (dict(value=dict(bits=8, axis="channel")), K.KVQ_ERR_UNSUPPORTED),
         (dict(window=20), K.KVQ_ERR_UNSUPPORTED),
@@ -123,6 +135,14 @@ def test_validation_errors():
     for over, want in bad:
         cfg = K.make_config(**{**base, **over})
         assert K.validate(cfg) == want, over
+    good = [
+        dict(key=dict(bits=2), value=dict(bits=2)),
+        dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super")),
+        dict(key=dict(bits=2, zero_point=True, scale="f16"),
+             value=dict(bits=2, zero_point=True, scale="f16")),
+    ]
+    for over in good:
+        assert K.validate(K.make_config(**{**base, **over})) == K.KVQ_OK, over
 
 
 def test_calls_fail_before_launch():
@@ -138,7 +158,7 @@ def test_calls_fail_before_launch():
     st = lib.kvq_decode_attn(ctypes.byref(cfg), ctypes.byref(desc), 3, 1, 1, None, 0, 64, None)
     assert st == K.KVQ_ERR_INVALID_ARG
     # workspace too small (cache pointers are fake; validation stops first)
-    fake = K.CacheDesc(*([256] * 8), None, 256)
+    fake = K.CacheDesc(*([256] * 8), None, 256, 256)
     st = lib.kvq_decode_attn(ctypes.byref(cfg), ctypes.byref(fake), 0, 256, 256, 256, 16, 64, None)
     assert st == K.KVQ_ERR_WORKSPACE
     # misaligned workspace
