@@ -88,8 +88,8 @@ _SCALE_DTYPES = {"f32": np.float32, "f16": np.float16, "f64": np.float64}
 class TensorFormat:
     """How one of K or V is stored.
 
-    bits:       16 = unquantized (bf16 values kept as is), 8, 4 (2 is accepted
-                by the byte accounting only).
+    bits:       16 = unquantized (bf16 values kept as is), 8, 4 or 2 (2-bit
+                symmetric codes are -1, 0, 1; with a zero point 0..3).
     axis:       "token" (one scale per token per head, P3 "Per-token scales and
                 where they can live") or "channel" (one scale per feature per
                 head, keys only, moved onto the query per P3 "The axis choice is

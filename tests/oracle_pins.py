@@ -187,7 +187,7 @@ def pin_sym_exact(O):
     division is correctly rounded, round() ties to even); with an fp32 scale the
     scale is the exactly rounded amax/qmax (R2)."""
     vecs = _random_vectors(48, 128, 11)
-    for bits in (8, 4):
+    for bits in (8, 4, 2):
         for scale, rnd in (("f64", rn64), ("f32", rn32)):
             codes, s = O.quantize_sym(vecs, bits, scale)
             for i, v in enumerate(vecs):
@@ -224,33 +224,36 @@ def pin_exact_ties(O):
 
 def pin_asym_exact(O):
     """Zero-point codes, fp16 scales and zero points equal exact evaluation of
-    reading R6; x = 0 reconstructs exactly; codes stay in [0, 15]; every
-    unclamped element is within s/2 of its reconstruction."""
+    reading R6 (4 and 2 bits); x = 0 reconstructs exactly; codes stay in
+    [0, 2^b - 1]; every unclamped element is within s/2 of its
+    reconstruction."""
     vecs = _random_vectors(40, 128, 23, magnitudes=(0.05, 1.0, 9.0, 300.0))
     vecs[5] = np.abs(vecs[5])          # one-signed vectors
     vecs[6] = -np.abs(vecs[6])
     vecs[7, :] = 0.0
     vecs[8, 3] = 0.0
-    codes, s, z = O.quantize_asym(vecs, 4, "f16")
-    for i, v in enumerate(vecs):
-        ec, es, ez = exact_asym(v, 4)
-        assert Fraction(float(s[i])) == es, i
-        assert float(z[i]) == ez, i
-        assert codes[i].tolist() == ec, i
-    assert codes.min() >= 0 and codes.max() <= 15
-    xh = O.dequant_asym(codes, s, z)
-    assert np.all(xh[vecs == 0.0] == 0.0)
-    err = np.abs(xh - vecs)
-    sd = s.astype(np.float64)[:, None]
-    unclamped = (codes > 0) & (codes < 15)
-    assert np.all(err[unclamped] <= sd.repeat(128, 1)[unclamped] / 2 * (1 + 1e-12))
+    for bits in (4, 2):
+        top = (1 << bits) - 1
+        codes, s, z = O.quantize_asym(vecs, bits, "f16")
+        for i, v in enumerate(vecs):
+            ec, es, ez = exact_asym(v, bits)
+            assert Fraction(float(s[i])) == es, (bits, i)
+            assert float(z[i]) == ez, (bits, i)
+            assert codes[i].tolist() == ec, (bits, i)
+        assert codes.min() >= 0 and codes.max() <= top
+        xh = O.dequant_asym(codes, s, z)
+        assert np.all(xh[vecs == 0.0] == 0.0)
+        err = np.abs(xh - vecs)
+        sd = s.astype(np.float64)[:, None]
+        unclamped = (codes > 0) & (codes < top)
+        assert np.all(err[unclamped] <= sd.repeat(128, 1)[unclamped] / 2 * (1 + 1e-12))
 
 
 def pin_sym_closed_form(O):
     """The largest-magnitude element maps to +-qmax, every element is within s/2
     of its reconstruction, codes never reach -2^(b-1), s = RN32(amax/qmax)."""
     vecs = _random_vectors(64, 128, 31)
-    for bits in (8, 4):
+    for bits in (8, 4, 2):
         qmax = (1 << (bits - 1)) - 1
         codes, s = O.quantize_sym(vecs, bits, "f32")
         xh = O.dequant_sym(codes, s)
@@ -292,28 +295,31 @@ def pin_channel(O):
 
 
 def pin_superscale(O):
-    """8-bit scale codes relative to a per-head super-scale (reading R10):
-    S = RN32(max_t(amax_t/7)/255); u in [1, 255] for non-zero vectors and 0 for
-    zero vectors; u equals exact rint(amax/(7 S)) clamped; codes equal exact
-    rounding under u*S; metadata is 1 byte per token."""
+    """8-bit scale codes relative to a per-head super-scale (reading R10), at
+    4 and 2 bits: S = RN32(max_t(amax_t/qmax)/255); u in [1, 255] for non-zero
+    vectors and 0 for zero vectors; u equals exact rint(amax/(qmax S))
+    clamped; codes equal exact rounding under u*S; metadata is 1 byte per
+    token."""
     v = _f32(_rng(53).laplace(0, 1, (64, 128)) * np.exp(_rng(54).uniform(-6, 2, (64, 1))))
     v[10] = 0.0
-    S = O.super_scale(v, 4)
     amax = [Fraction(float(np.max(np.abs(r)))) for r in v]
-    assert Fraction(float(S)) == rn32(max(a / 7 for a in amax) / 255)
-    codes, u = O.quantize_superscaled(v, S, 4)
-    for t in range(64):
-        if amax[t] == 0:
-            assert u[t] == 0 and not codes[t].any()
-            continue
-        eu = max(1, min(255, round(amax[t] / 7 / Fraction(float(S)))))
-        assert u[t] == eu, t
-        se = eu * Fraction(float(S))
-        assert codes[t].tolist() == [max(-7, min(7, round(fr(x) / se))) for x in v[t]], t
-        if eu > 1:
-            assert abs(se - amax[t] / 7) <= Fraction(float(S)) / 2
-    fmt = O.TensorFormat(4, "token", False, "u8_super")
-    assert O.meta_bytes_per_token(fmt) == 1
+    for bits in (4, 2):
+        qmax = (1 << (bits - 1)) - 1
+        S = O.super_scale(v, bits)
+        assert Fraction(float(S)) == rn32(max(a / qmax for a in amax) / 255)
+        codes, u = O.quantize_superscaled(v, S, bits)
+        for t in range(64):
+            if amax[t] == 0:
+                assert u[t] == 0 and not codes[t].any()
+                continue
+            eu = max(1, min(255, round(amax[t] / qmax / Fraction(float(S)))))
+            assert u[t] == eu, (bits, t)
+            se = eu * Fraction(float(S))
+            assert codes[t].tolist() == [max(-qmax, min(qmax, round(fr(x) / se))) for x in v[t]], t
+            if eu > 1:
+                assert abs(se - amax[t] / qmax) <= Fraction(float(S)) / 2
+        fmt = O.TensorFormat(bits, "token", False, "u8_super")
+        assert O.meta_bytes_per_token(fmt) == 1
 
 
 def pin_fold(O):
