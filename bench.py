@@ -310,8 +310,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",   # MFMA operands (exact fp16 codes, fp16 hi/lo query and
-                          # weights); fp32 accumulation and softmax
+        "dtype": "i8,f16",  # matrix-core operands: int8 query limbs x int8 key codes
+                            # (int32 sums), fp16 weights x exact fp16 value codes;
+                            # fp32 scales, softmax and accumulation
         "data": "synthetic (seeded; no dataset on the pages)",
         "config": {"workload": wl["name"], "batch": wl["batch"], "q_heads": wl["hq"],
                    "kv_heads": wl["hkv"], "head_dim": wl["d"], "tokens": max_len,

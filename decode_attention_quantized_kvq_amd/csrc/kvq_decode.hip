@@ -49,11 +49,17 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int D = 128;
 constexpr int WAVES = 4;
 constexpr int TILE = 32;
-// Tiles in flight per wave.
-#ifndef KVQ_NB
-#define KVQ_NB 2
+// Tiles each wave keeps in flight, by bytes per token (key + value codes):
+// narrow tiles need more of them to cover the memory latency.
+#ifndef KVQ_NB8
+#define KVQ_NB8 2
 #endif
-constexpr int NB = KVQ_NB;
+#ifndef KVQ_NB4
+#define KVQ_NB4 2
+#endif
+#ifndef KVQ_NB2
+#define KVQ_NB2 2
+#endif
 // Minimum waves per SIMD the decode kernel is compiled for.
 #ifndef KVQ_MINW
 #define KVQ_MINW 1
@@ -1408,6 +1414,8 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   // (first tile, second, ..., then the refills): the compiler derives its
   // wait counts from that order, and interleaved loads would make every wait
   // in the loop a wait for all of them.
+  constexpr int ROWB = Codes<KC>::ROW + Codes<VC>::ROW;
+  constexpr int NB = ROWB >= 192 ? KVQ_NB8 : ROWB >= 128 ? KVQ_NB4 : KVQ_NB2;
   TileRaw<KC, KM, VC, VM> buf[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
