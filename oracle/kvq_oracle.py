@@ -54,6 +54,13 @@ Readings where the pages leave a step open (each restated where it is used):
       quantized from its input value, or from its bf16 window copy when it
       leaves the window in a later append.
   R13 the output is fp32 on the device; here fp64.
+  R20 token groups (P3 "Per-token scales and where they can live": several
+      tokens under one scale): with a group size g, one scale (and zero
+      point) is taken over all g*D values of g consecutive positions of a
+      (sequence, head), i.e. the group is quantized as one vector.  A group
+      is quantized once it is complete and older than the window: positions
+      [0, Q) with Q = floor(max(n - W, 0) / g) * g are quantized, the newest
+      n - Q stay in bf16 as the window's do (R11).  g = 1 is per token.
   Scale underflow: a scale that rounds to 0 in its storage type is replaced by
   that type's smallest positive value (fp32 2^-149, fp16 2^-24); an fp16 scale
   above 65504 saturates to 65504.
@@ -121,6 +128,13 @@ def qmax_symmetric(bits: int) -> int:
 
 def qmax_unsigned(bits: int) -> int:
     return (1 << bits) - 1
+
+
+def quantized_count(n: int, window: int = 0, group: int = 1) -> int:
+    """Positions [0, Q) of an n-token sequence are quantized (readings R11,
+    R20): the newest min(W, n) stay in bf16, and of the rest only whole groups
+    of g positions are quantized."""
+    return max(n - window, 0) // group * group
 
 
 def round_to_storage(x64, scale: str) -> np.ndarray:
@@ -338,8 +352,8 @@ class _Side:
 
     def __init__(self, hkv: int, d: int):
         self.codes = np.zeros((hkv, 0, d), np.int32)
-        self.s = None          # per-token scale [Hkv, n]
-        self.z = None          # per-token zero point [Hkv, n]
+        self.s = None          # per-token (per-group) scale [Hkv, n / g]
+        self.z = None          # per-token (per-group) zero point [Hkv, n / g]
         self.u = None          # per-token 8-bit scale code [Hkv, n]
         self.raw = np.zeros((hkv, 0, d), np.float64)   # bits == 16 formats
         self.chan = None       # per-channel scale [Hkv, D]
@@ -355,16 +369,24 @@ class OracleCache:
     min(W, n) tokens stay as their bf16 values and the rest are quantized per
     token (reading R11).  Paging (P2 "Metadata and block layout remain part of
     physical memory use") changes placement only, so this model has none.
+
+    With a token group size g > 1 (reading R20) one scale covers g
+    consecutive positions, and the positions of a group not yet complete stay
+    in bf16 beside the window.
     """
 
     def __init__(self, batch: int, hkv: int, d: int, key: TensorFormat,
-                 value: TensorFormat, window: int = 0):
-        if window and (key.axis == "channel" or key.scale == "u8_super"
-                       or value.scale == "u8_super"):
-            raise ValueError("a recent window is modelled for per-token formats only")
+                 value: TensorFormat, window: int = 0, group: int = 1):
+        if (window or group > 1) and (key.axis == "channel" or key.scale == "u8_super"
+                                      or value.scale == "u8_super"):
+            raise ValueError("a recent window and token groups are modelled for "
+                             "per-token formats only")
+        if group < 1:
+            raise ValueError("group size must be at least 1")
         self.batch, self.hkv, self.d = batch, hkv, d
         self.fmt = {"k": key, "v": value}
         self.window = window
+        self.group = group
         self.lens = [0] * batch
         self.side = [{"k": _Side(hkv, d), "v": _Side(hkv, d)} for _ in range(batch)]
         self.win = [{"k": np.zeros((hkv, 0, d)), "v": np.zeros((hkv, 0, d))}
@@ -373,12 +395,26 @@ class OracleCache:
     # -- write side ---------------------------------------------------------
     def _quantize_into(self, side: _Side, fmt: TensorFormat, x: np.ndarray,
                        first: bool):
-        """Quantize vectors x [Hkv, n, D] (position order) and append them."""
+        """Quantize vectors x [Hkv, n, D] (position order, n a multiple of the
+        group size) and append them."""
         n = x.shape[1]
         if n == 0:
             return
         if fmt.bits == 16:
             side.raw = np.concatenate([side.raw, round_bf16(x)], axis=1)
+            return
+        g = self.group
+        if g > 1:
+            # reading R20: each group of g positions is one vector of g*D values
+            assert n % g == 0
+            xg = x.reshape(x.shape[0], n // g, g * x.shape[2])
+            if fmt.zero_point:
+                c, s, z = quantize_asym(xg, fmt.bits, fmt.scale)
+                side.z = z if side.z is None else np.concatenate([side.z, z], axis=1)
+            else:
+                c, s = quantize_sym(xg, fmt.bits, fmt.scale)
+            side.s = s if side.s is None else np.concatenate([side.s, s], axis=1)
+            side.codes = np.concatenate([side.codes, c.reshape(x.shape)], axis=1)
             return
         if fmt.axis == "channel":
             if first:
@@ -407,9 +443,9 @@ class OracleCache:
         first = self.lens[b] == 0
         total = self.lens[b] + n
         for t, x in (("k", k_new), ("v", v_new)):
-            if self.window:
+            if self.window or self.group > 1:
                 pool = np.concatenate([self.win[b][t], x], axis=1)
-                keep = min(self.window, total)
+                keep = total - quantized_count(total, self.window, self.group)
                 leave = pool.shape[1] - keep
                 self._quantize_into(self.side[b][t], self.fmt[t], pool[:, :leave], first)
                 self.win[b][t] = round_bf16(pool[:, leave:])
@@ -427,16 +463,18 @@ class OracleCache:
             return dequant_channel(side.codes, side.chan)
         if fmt.scale == "u8_super":
             return dequant_superscaled(side.codes, side.u, side.S)
+        # per-group metadata applies to each of the group's positions
+        s = np.repeat(side.s, self.group, axis=1)
         if fmt.zero_point:
-            return dequant_asym(side.codes, side.s, side.z)
-        return dequant_sym(side.codes, side.s)
+            return dequant_asym(side.codes, s, np.repeat(side.z, self.group, axis=1))
+        return dequant_sym(side.codes, s)
 
     def reconstructed(self, b: int):
         """(k_hat, v_hat) [Hkv, len, D] fp64 in position order."""
         out = []
         for t in ("k", "v"):
             q = self._dequant(self.side[b][t], self.fmt[t])
-            if self.window:
+            if self.window or self.group > 1:
                 q = np.concatenate([q, self.win[b][t]], axis=1)
             out.append(q)
         return out[0], out[1]
@@ -479,54 +517,64 @@ def side_bytes_per_head(fmt: TensorFormat, d: int) -> int:
     return 0
 
 
+def ring_slots(window: int = 0, group: int = 1) -> int:
+    """bf16 slots per (sequence, head): the window plus room for the
+    positions of an incomplete token group (at most g - 1)."""
+    return window + (group if group > 1 else 0)
+
+
 def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
                 d: int, lens: Sequence[int], window: int = 0,
-                block_tokens: int = 0, max_tokens: Optional[int] = None) -> Dict[str, int]:
+                block_tokens: int = 0, max_tokens: Optional[int] = None,
+                group: int = 1) -> Dict[str, int]:
     """Bytes of a cache holding sequences of the given lengths.
 
     payload   P2 "Cache precision is separate from weight precision":
               KV_bytes = 2 * L * H_kv * D * T * b, generalised to separate key
               and value widths: L * H_kv * D * T_q * (b_K + b_V) over the
               quantized tokens T_q of each sequence.
-    metadata  per-token scales / zero points / 8-bit scale codes plus per-head
-              channel scales or super-scales (P3 "Per-token scales and where
-              they can live"; P2 "Metadata and block layout remain part of
-              physical memory use").
-    window    the bf16 recent tokens, 2 bytes per element for K and V.
+    metadata  per-token (per-group) scales / zero points / 8-bit scale codes
+              plus per-head channel scales or super-scales (P3 "Per-token
+              scales and where they can live"; P2 "Metadata and block layout
+              remain part of physical memory use").
+    window    the bf16 tokens (window and incomplete group), 2 bytes per
+              element for K and V.
     padding   allocated but unused slots: the unfilled tail of the last block
-              of a paged sequence, or max_tokens - T_q quantized slots and
-              W - n_w window slots of a contiguous one.
+              of a paged sequence, or max_tokens - T_q quantized slots and the
+              unused bf16 ring slots of a contiguous one.
     total     the sum of the four.
     """
     def row(fmt):  # bytes of one token's codes
         return d * fmt.bits // 8
 
     out = dict(payload=0, metadata=0, window=0, padding=0)
-    per_tok = row(key) + row(value) + meta_bytes_per_token(key) + meta_bytes_per_token(value)
+    codes = row(key) + row(value)
+    meta = meta_bytes_per_token(key) + meta_bytes_per_token(value)   # per group
+    ring = ring_slots(window, group)
     for n in lens:
-        n_w = min(window, n)
-        n_q = n - n_w
-        out["payload"] += layers * hkv * n_q * (row(key) + row(value))
+        n_q = quantized_count(n, window, group)
+        n_w = n - n_q
+        out["payload"] += layers * hkv * n_q * codes
         out["metadata"] += layers * hkv * (
-            n_q * (meta_bytes_per_token(key) + meta_bytes_per_token(value))
-            + side_bytes_per_head(key, d) + side_bytes_per_head(value, d))
+            n_q // group * meta + side_bytes_per_head(key, d) + side_bytes_per_head(value, d))
         out["window"] += layers * hkv * n_w * d * 2 * 2
         if block_tokens:
             alloc_q = -(-n_q // block_tokens) * block_tokens
         else:
             alloc_q = max_tokens if max_tokens is not None else n_q
-        out["padding"] += layers * hkv * (alloc_q - n_q) * per_tok
-        if window and not block_tokens:
-            out["padding"] += layers * hkv * (window - n_w) * d * 2 * 2
+        out["padding"] += layers * hkv * ((alloc_q - n_q) * codes + (alloc_q - n_q) // group * meta)
+        if ring and not block_tokens:
+            out["padding"] += layers * hkv * (ring - n_w) * d * 2 * 2
     out["total"] = out["payload"] + out["metadata"] + out["window"] + out["padding"]
     return out
 
 
 def decode_traffic(key: TensorFormat, value: TensorFormat, hkv: int, d: int,
-                   lens: Sequence[int], window: int = 0) -> int:
+                   lens: Sequence[int], window: int = 0, group: int = 1) -> int:
     """Bytes one decode step must read from the cache (one layer): codes,
-    per-token metadata, window values and per-head side data; no padding."""
-    b = cache_bytes(key, value, 1, hkv, d, lens, window)
+    per-token (per-group) metadata, bf16 values and per-head side data; no
+    padding."""
+    b = cache_bytes(key, value, 1, hkv, d, lens, window, group=group)
     return b["payload"] + b["metadata"] + b["window"]
 
 

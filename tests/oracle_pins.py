@@ -520,6 +520,84 @@ def pin_window(O):
     assert np.array_equal(cache.stored(0, "k").codes, ck)
 
 
+def pin_group_scales_exact(O):
+    """Token groups (reading R20 of P3 "Per-token scales and where they can
+    live": several tokens under one scale): each group's stored scale (and
+    zero point) and its codes equal exact rational quantization of the
+    group's g*D values taken as one vector, at 8, 4 and 2 bits."""
+    rng = _rng(171)
+    d = 8
+    for g in (2, 4, 16):
+        x = _bf16(rng.standard_normal((2, 3 * g, d)) * np.exp(rng.uniform(-3, 3, (2, 3 * g, 1))))
+        x[0, 0:g] = 0.0                                  # an all-zero group
+        for fmt in (O.TensorFormat(8), O.TensorFormat(4), O.TensorFormat(2),
+                    O.TensorFormat(4, "token", True, "f16"), O.TensorFormat(2, "token", True, "f16")):
+            cache = O.OracleCache(1, 2, d, fmt, fmt, group=g)
+            cache.append(0, x, x)
+            st = cache.stored(0, "k")
+            assert st.codes.shape == (2, 3 * g, d) and st.s.shape == (2, 3)
+            for h in range(2):
+                for j in range(3):
+                    vec = x[h, j * g:(j + 1) * g].reshape(-1)
+                    codes = st.codes[h, j * g:(j + 1) * g].reshape(-1).tolist()
+                    if fmt.zero_point:
+                        ec, es, ez = exact_asym(vec, fmt.bits)
+                        assert float(st.z[h, j]) == ez, (g, fmt, h, j)
+                    else:
+                        ec, es = exact_sym(vec, fmt.bits, rn32)
+                    assert Fraction(float(st.s[h, j])) == es, (g, fmt, h, j)
+                    assert codes == ec, (g, fmt, h, j)
+
+
+def pin_group_residual(O):
+    """Token groups with a window: after every append exactly
+    Q = floor(max(n - W, 0) / g) * g positions are quantized and the newest
+    n - Q are their bf16 values; with bf16-exact inputs the records do not
+    depend on how the tokens were split into appends; g = 1 is per token."""
+    rng = _rng(173)
+    d = 16
+    allk = _bf16(rng.standard_normal((2, 70, d)))
+    allv = _bf16(rng.standard_normal((2, 70, d)) * 3)
+    fmt = O.TensorFormat(2, "token", True, "f16")
+    for w, g in ((0, 4), (8, 16), (16, 2)):
+        one = O.OracleCache(1, 2, d, fmt, fmt, window=w, group=g)
+        one.append(0, allk, allv)
+        many = O.OracleCache(1, 2, d, fmt, fmt, window=w, group=g)
+        n = 0
+        for step in (5, 1, 1, 17, 2, 3, 1, 40):
+            many.append(0, allk[:, n:n + step], allv[:, n:n + step])
+            n += step
+            q = O.quantized_count(n, w, g)
+            assert q == max(n - w, 0) // g * g and q % g == 0
+            assert many.stored(0, "k").codes.shape[1] == q, (w, g, n)
+            kh, vh = many.reconstructed(0)
+            assert np.array_equal(kh[:, q:], allk[:, q:n]) and np.array_equal(vh[:, q:], allv[:, q:n])
+        for t in ("k", "v"):
+            a, b = one.stored(0, t), many.stored(0, t)
+            assert np.array_equal(a.codes, b.codes) and np.array_equal(a.s, b.s) and np.array_equal(a.z, b.z)
+    per_tok = O.OracleCache(1, 2, d, fmt, fmt, window=8)
+    g1 = O.OracleCache(1, 2, d, fmt, fmt, window=8, group=1)
+    per_tok.append(0, allk, allv)
+    g1.append(0, allk, allv)
+    assert np.array_equal(per_tok.reconstructed(0)[0], g1.reconstructed(0)[0])
+
+
+def pin_group_bytes(O):
+    """Byte accounting with token groups: g tokens share one metadata element,
+    so 2-bit codes with a 4-byte scale per 16 tokens carry 12.5 % / 16 of
+    metadata at D = 128 ([P3]'s 12 % case, divided by the group size)."""
+    f = O.TensorFormat(2)
+    lens = [16 * 37 + 5, 16, 3, 0]
+    for g in (1, 2, 16):
+        b = O.cache_bytes(f, f, 1, 1, 128, lens, window=0, group=g)
+        q = [O.quantized_count(n, 0, g) for n in lens]
+        assert b["payload"] == sum(q) * 2 * 32
+        assert b["metadata"] == sum(x // g for x in q) * 2 * 4
+        assert b["window"] == sum(n - x for n, x in zip(lens, q)) * 128 * 4
+    b = O.cache_bytes(f, f, 1, 1, 128, [16 * 100], group=16)
+    assert Fraction(b["metadata"], b["payload"]) == Fraction(125, 1000) / 16
+
+
 def pin_window_stores_bf16(O):
     """Unquantized tokens (bits 16, or the recent window) are stored in bf16:
     fp32 inputs come back rounded to nearest-even bf16 (torch's conversion)."""

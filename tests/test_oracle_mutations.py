@@ -52,6 +52,14 @@ def m_qmax_128(O):
     O.qmax_symmetric = lambda b: 1 << (b - 1)
 
 
+def m_group_count_ignores_window(O):
+    O.quantized_count = lambda n, window=0, group=1: n // group * group
+
+
+def m_group_count_rounds_up(O):
+    O.quantized_count = lambda n, window=0, group=1: -(-max(n - window, 0) // group) * group
+
+
 def m_no_inv_sqrt_d(O):
     O.scores = lambda q, k: np.asarray(k, np.float64) @ np.asarray(q, np.float64)
 
