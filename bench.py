@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2, help="workload 1..6 (default 2: GQA int8)")
+    p.add_argument("--config", type=int, default=2, help="workload 1..7 (default 2: GQA int8)")
     p.add_argument("--replicas", type=int, default=0, help="cache copies (0 = enough for 1 GiB)")
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -87,7 +87,8 @@ def build_cache(wl, lens, K, synth, torch):
     cfg = K.make_config(batch=wl["batch"], num_q_heads=wl["hq"], num_kv_heads=wl["hkv"],
                         head_dim=wl["d"], max_tokens=wl["tokens"], key=wl["key"],
                         value=wl["value"], window=wl["window"], block_tokens=wl["block_tokens"],
-                        num_blocks=nb, max_blocks_per_seq=mb, in_dtype=wl["in_dtype"])
+                        num_blocks=nb, max_blocks_per_seq=mb, in_dtype=wl["in_dtype"],
+                        group_tokens=wl.get("group", 1))
     st = K.validate(cfg)
     if st != K.KVQ_OK:
         raise SystemExit(f"workload not supported: {K.status_string(st)}")
@@ -141,7 +142,8 @@ def cpu_baseline(wl, lens, seconds: float):
                 cache = built[gi]
             else:
                 k, v = synth.kv_tokens(wl, b, h, n)
-                cache = O.OracleCache(1, 1, wl["d"], fmt(wl["key"]), fmt(wl["value"]), wl["window"])
+                cache = O.OracleCache(1, 1, wl["d"], fmt(wl["key"]), fmt(wl["value"]), wl["window"],
+                                      group=wl.get("group", 1))
                 cache.append(0, k[None], v[None])
                 if keep:
                     built[gi] = cache

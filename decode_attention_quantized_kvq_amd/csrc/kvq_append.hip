@@ -134,8 +134,6 @@ __device__ inline int meta_size(MetaKind m) {
   }
 }
 
-// Quantizes the vector whose elements 2*lane and 2*lane+1 this lane holds,
-// and stores its codes and metadata at token slot `slot`.
 __device__ inline int code_bits(CodeKind c) {
   return (c == CK_I8 || c == CK_U8) ? 8 : (c == CK_I4 || c == CK_U4) ? 4 : 2;
 }
@@ -144,97 +142,117 @@ __device__ inline int code_bits(CodeKind c) {
 __device__ inline int qmax_sym(int bits) { return (1 << (bits - 1)) - 1; }
 __device__ inline int qmax_zp(int bits) { return (1 << bits) - 1; }
 
-__device__ void quantize_store(const TensorKind k, float x0, float x1, uint8_t* codes,
-                               uint8_t* meta, size_t slot, const float* chan, float super,
-                               int lane) {
+// Quantizes the token group at positions p0 .. p0+g-1 of one (sequence,
+// head): one scale (and zero point, or 8-bit scale code) over all its g*D
+// values, then the codes of each token.  ld(p, x0, x1) loads elements 2*lane
+// and 2*lane+1 of position p; slot(p) is its code slot; metadata element m
+// belongs to the group.  g = 1 is the per-token case.
+template <typename Load, typename Slot>
+__device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, int g,
+                               uint8_t* codes, uint8_t* meta, size_t m, const float* chan,
+                               float super, int lane) {
   const int bits = code_bits(k.code);
   const bool zp = k.meta == MK_F32Z || k.meta == MK_F16Z;
-  int c0 = 0, c1 = 0;
+  // 1. group statistics
+  float amax = 0.0f, lo = 0.0f, hi = 0.0f;
+  if (!k.channel) {
+    float mx = 0.0f, mn = 0.0f, ab = 0.0f;
+    for (int j = 0; j < g; ++j) {
+      float x0, x1;
+      ld(p0 + j, x0, x1);
+      ab = fmaxf(ab, fmaxf(fabsf(x0), fabsf(x1)));
+      mx = fmaxf(mx, fmaxf(x0, x1));
+      mn = fminf(mn, fminf(x0, x1));
+    }
+    amax = wave_max(ab);
+    hi = wave_max(mx);  // zero point: the range includes 0 (mx, mn start at 0)
+    lo = wave_min(mn);
+  }
+  // 2. the group's scale (fp64, rounded once to its storage type)
+  double s = 1.0;  // scale the codes divide by
+  int z = 0, qmax = 0, u = 0;
+  bool nonzero = true;
+  uint32_t sbits = 0;
   if (k.channel) {
-    // Frozen per-channel scales of the keys.
-    const int qmax = qmax_sym(bits);
-    c0 = clampi(rne_code(x0, (double)chan[2 * lane]), -qmax, qmax);
-    c1 = clampi(rne_code(x1, (double)chan[2 * lane + 1]), -qmax, qmax);
+    qmax = qmax_sym(bits);
   } else if (k.meta == MK_U8) {
-    // 8-bit scale code relative to the frozen per-head super-scale.
-    const int qmax = qmax_sym(bits);
-    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    int u = 0;
-    if (amax != 0.0f) {
+    // 8-bit scale code relative to the frozen per-head super-scale
+    qmax = qmax_sym(bits);
+    nonzero = amax != 0.0f;
+    if (nonzero) {
       const double sigma = (double)amax / qmax;
       u = clampi((int)rint(sigma / (double)super), 1, 255);
-      const double seff = (double)u * (double)super;  // exact
-      c0 = clampi(rne_code(x0, seff), -qmax, qmax);
-      c1 = clampi(rne_code(x1, seff), -qmax, qmax);
+      s = (double)u * (double)super;  // exact
     }
-    if (lane == 0) meta[slot] = (uint8_t)u;
   } else if (!zp) {
-    const int qmax = qmax_sym(bits);
-    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    double s = 1.0;
-    uint32_t bits = 0;
+    qmax = qmax_sym(bits);
+    nonzero = amax != 0.0f;
     if (k.meta == MK_F32) {
-      const float sf = amax == 0.0f ? 1.0f : store_f32((double)amax / qmax);
-      s = (double)sf;
-      bits = __float_as_uint(sf);
-    } else {
-      const uint16_t h = amax == 0.0f ? (uint16_t)0x3C00u : store_f16((double)amax / qmax);
-      s = f16_bits_to_f64(h);
-      bits = h;
-    }
-    if (amax != 0.0f) {
-      c0 = clampi(rne_code(x0, s), -qmax, qmax);
-      c1 = clampi(rne_code(x1, s), -qmax, qmax);
-    }
-    if (lane == 0) {
-      if (k.meta == MK_F32)
-        ((uint32_t*)meta)[slot] = bits;
-      else
-        ((uint16_t*)meta)[slot] = (uint16_t)bits;
-    }
-  } else {
-    // Zero point: the range is widened to include 0; z is the code of 0.
-    const int qmax = qmax_zp(bits);
-    const float lo = fminf(wave_min(fminf(x0, x1)), 0.0f);
-    const float hi = fmaxf(wave_max(fmaxf(x0, x1)), 0.0f);
-    double s = 1.0;
-    int z = 0;
-    uint32_t sbits;
-    if (k.meta == MK_F32Z) {
-      const float sf = hi == lo ? 1.0f : store_f32(((double)hi - (double)lo) / qmax);
+      const float sf = nonzero ? store_f32((double)amax / qmax) : 1.0f;
       s = (double)sf;
       sbits = __float_as_uint(sf);
     } else {
-      const uint16_t h = hi == lo ? (uint16_t)0x3C00u : store_f16(((double)hi - (double)lo) / qmax);
-      s = f16_bits_to_f64(h);
-      sbits = h;
+      const uint16_t hb = nonzero ? store_f16((double)amax / qmax) : (uint16_t)0x3C00u;
+      s = f16_bits_to_f64(hb);
+      sbits = hb;
     }
-    if (hi != lo) {
-      z = clampi((int)rint(-(double)lo / s), 0, qmax);
+  } else {
+    qmax = qmax_zp(bits);
+    nonzero = hi != lo;
+    if (k.meta == MK_F32Z) {
+      const float sf = nonzero ? store_f32(((double)hi - (double)lo) / qmax) : 1.0f;
+      s = (double)sf;
+      sbits = __float_as_uint(sf);
+    } else {
+      const uint16_t hb = nonzero ? store_f16(((double)hi - (double)lo) / qmax) : (uint16_t)0x3C00u;
+      s = f16_bits_to_f64(hb);
+      sbits = hb;
+    }
+    if (nonzero) z = clampi((int)rint(-(double)lo / s), 0, qmax);
+  }
+  if (lane == 0 && !k.channel) {
+    if (k.meta == MK_U8) {
+      meta[m] = (uint8_t)u;
+    } else if (k.meta == MK_F32) {
+      ((uint32_t*)meta)[m] = sbits;
+    } else if (k.meta == MK_F16) {
+      ((uint16_t*)meta)[m] = (uint16_t)sbits;
+    } else if (k.meta == MK_F32Z) {
+      ((uint32_t*)meta)[2 * m] = sbits;
+      ((float*)meta)[2 * m + 1] = (float)z;
+    } else {
+      const _Float16 zh = (_Float16)(float)z;
+      ((uint32_t*)meta)[m] = sbits | ((uint32_t)__builtin_bit_cast(uint16_t, zh) << 16);
+    }
+  }
+  // 3. codes of each token of the group
+  for (int j = 0; j < g; ++j) {
+    float x0, x1;
+    ld(p0 + j, x0, x1);
+    int c0 = 0, c1 = 0;
+    if (k.channel) {
+      c0 = clampi(rne_code(x0, (double)chan[2 * lane]), -qmax, qmax);
+      c1 = clampi(rne_code(x1, (double)chan[2 * lane + 1]), -qmax, qmax);
+    } else if (nonzero && !zp) {
+      c0 = clampi(rne_code(x0, s), -qmax, qmax);
+      c1 = clampi(rne_code(x1, s), -qmax, qmax);
+    } else if (nonzero) {
       c0 = clampi(rne_code(x0, s) + z, 0, qmax);
       c1 = clampi(rne_code(x1, s) + z, 0, qmax);
     }
-    if (lane == 0) {
-      if (k.meta == MK_F32Z) {
-        ((uint32_t*)meta)[2 * slot] = sbits;
-        ((float*)meta)[2 * slot + 1] = (float)z;
-      } else {
-        const _Float16 zh = (_Float16)(float)z;
-        ((uint32_t*)meta)[slot] = sbits | ((uint32_t)__builtin_bit_cast(uint16_t, zh) << 16);
-      }
+    const size_t sl = slot(p0 + j);
+    if (bits == 8) {
+      const uint32_t v = ((uint32_t)(c0 & 0xFF)) | ((uint32_t)(c1 & 0xFF) << 8);
+      ((uint16_t*)(codes + sl * (size_t)D))[lane] = (uint16_t)v;
+    } else if (bits == 4) {
+      const uint32_t v = ((uint32_t)(c0 & 0xF)) | ((uint32_t)(c1 & 0xF) << 4);
+      (codes + sl * (size_t)(D / 2))[lane] = (uint8_t)v;
+    } else {
+      // four 2-bit codes per byte: elements 4j .. 4j+3 come from lanes 2j, 2j+1
+      const uint32_t v = ((uint32_t)(c0 & 3)) | ((uint32_t)(c1 & 3) << 2);
+      const uint32_t odd = (uint32_t)__shfl_xor((int)v, 1);
+      if ((lane & 1) == 0) (codes + sl * (size_t)(D / 4))[lane >> 1] = (uint8_t)(v | (odd << 4));
     }
-  }
-  if (bits == 8) {
-    const uint32_t v = ((uint32_t)(c0 & 0xFF)) | ((uint32_t)(c1 & 0xFF) << 8);
-    ((uint16_t*)(codes + slot * (size_t)D))[lane] = (uint16_t)v;
-  } else if (bits == 4) {
-    const uint32_t v = ((uint32_t)(c0 & 0xF)) | ((uint32_t)(c1 & 0xF) << 4);
-    (codes + slot * (size_t)(D / 2))[lane] = (uint8_t)v;
-  } else {
-    // four 2-bit codes per byte: elements 4j .. 4j+3 come from lanes 2j, 2j+1
-    const uint32_t v = ((uint32_t)(c0 & 3)) | ((uint32_t)(c1 & 3) << 2);
-    const uint32_t odd = (uint32_t)__shfl_xor((int)v, 1);
-    if ((lane & 1) == 0) (codes + slot * (size_t)(D / 4))[lane >> 1] = (uint8_t)(v | (odd << 4));
   }
 }
 
@@ -280,56 +298,62 @@ __global__ void __launch_bounds__(256) append_stats(AppendArgs a) {
   }
 }
 
+// Quantized positions of an n-token sequence: whole token groups older than
+// the window.
+__device__ inline int quantized_count(const AppendArgs& a, int n) {
+  const int m = n - a.window > 0 ? n - a.window : 0;
+  return (m >> a.tgshift) << a.tgshift;
+}
+
 __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqRange r = seq_range(a, b);
-  int p, src_row;     // quantized position; row of the new input or -1
-  if (a.window) {
-    const int qlo = r.start - a.window > 0 ? r.start - a.window : 0;
-    const int qhi = r.len - a.window > 0 ? r.len - a.window : 0;
-    if (i >= qhi - qlo) return;
-    p = qlo + i;
-    src_row = p >= r.start ? p - r.start : -1;
-  } else {
-    if (i >= r.newb) return;
-    p = r.start + i;
-    src_row = i;
-  }
-  if (p >= q_capacity(a)) return;
+  // token groups completed by this append: positions [qlo, qhi)
+  const int qlo = quantized_count(a, r.start), qhi = quantized_count(a, r.len);
+  const int g = a.tgroup;
+  const int p0 = qlo + i * g;
+  if (p0 >= qhi || p0 + g > q_capacity(a)) return;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const TensorKind k = w == 0 ? a.kk : a.vk;
   const void* src = w == 0 ? a.k_new : a.v_new;
-  float x0, x1;
-  if (src_row >= 0) {
-    const size_t row = (((size_t)b * a.hkv + h) * a.n_new + src_row) * D;
-    x0 = load_in(src, row + 2 * lane, a.in_bf16);
-    x1 = load_in(src, row + 2 * lane + 1, a.in_bf16);
-  } else {
-    const uint16_t* ring = w == 0 ? a.k_win : a.v_win;
-    const size_t row = (((size_t)b * a.hkv + h) * a.window + (p % a.window)) * D;
-    x0 = bf16_bits_to_f32(ring[row + 2 * lane]);
-    x1 = bf16_bits_to_f32(ring[row + 2 * lane + 1]);
-  }
-  const size_t slot = slot_index(a, b, h, p);
+  const uint16_t* ring = w == 0 ? a.k_win : a.v_win;
+  const size_t head = (size_t)b * a.hkv + h;
+  // a position of this append comes from the input, an older one from its
+  // bf16 copy in the ring
+  auto ld = [&](int p, float& x0, float& x1) {
+    if (p >= r.start) {
+      const size_t row = (head * a.n_new + (p - r.start)) * D;
+      x0 = load_in(src, row + 2 * lane, a.in_bf16);
+      x1 = load_in(src, row + 2 * lane + 1, a.in_bf16);
+    } else {
+      const size_t row = (head * a.ring + (p % a.ring)) * D;
+      x0 = bf16_bits_to_f32(ring[row + 2 * lane]);
+      x1 = bf16_bits_to_f32(ring[row + 2 * lane + 1]);
+    }
+  };
+  auto slot = [&](int p) { return slot_index(a, b, h, p); };
   uint8_t* codes = w == 0 ? a.k_codes : a.v_codes;
   uint8_t* meta = w == 0 ? a.k_meta : a.v_meta;
-  const float* chan = (w == 0 && k.channel) ? a.k_chan + ((size_t)b * a.hkv + h) * D : nullptr;
+  const float* chan = (w == 0 && k.channel) ? a.k_chan + head * D : nullptr;
   const float* sup = w == 0 ? a.k_super : a.v_super;
-  const float super = k.meta == MK_U8 ? sup[(size_t)b * a.hkv + h] : 1.0f;
-  quantize_store(k, x0, x1, codes, meta, slot, chan, super, lane);
+  const float super = k.meta == MK_U8 ? sup[head] : 1.0f;
+  quantize_group(k, ld, slot, p0, g, codes, meta, slot_index(a, b, h, p0) >> a.tgshift, chan,
+                 super, lane);
 }
 
 __global__ void __launch_bounds__(128) append_window(AppendArgs a) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqRange r = seq_range(a, b);
-  const int first = r.len - a.window > r.start ? r.len - a.window : r.start;
+  // the new positions that stay unquantized: [max(Q, start), len)
+  const int q = quantized_count(a, r.len);
+  const int first = q > r.start ? q : r.start;
   const int p = first + i;
   if (p >= r.len) return;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const void* src = w == 0 ? a.k_new : a.v_new;
   uint16_t* ring = w == 0 ? a.k_win : a.v_win;
   const size_t in_row = (((size_t)b * a.hkv + h) * a.n_new + (p - r.start)) * D;
-  const size_t out_row = (((size_t)b * a.hkv + h) * a.window + (p % a.window)) * D;
+  const size_t out_row = (((size_t)b * a.hkv + h) * a.ring + (p % a.ring)) * D;
   for (int e = lane; e < D; e += 64) {
     const uint16_t v = a.in_bf16 ? ((const uint16_t*)src)[in_row + e]
                                  : f32_to_bf16_bits(((const float*)src)[in_row + e]);
@@ -346,11 +370,12 @@ kvq_status launch_append(const AppendArgs& a, void* stream) {
     hipLaunchKernelGGL(append_stats, heads, dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
   }
-  const int nq = a.window ? a.n_new + a.window : a.n_new;
-  hipLaunchKernelGGL(append_quantize, dim3(nq, a.hkv, a.batch), dim3(128), 0, s, a);
+  // groups completed by an append: at most (n_new + ring) / g + 1
+  const int ng = (a.n_new + a.ring) / a.tgroup + 1;
+  hipLaunchKernelGGL(append_quantize, dim3(ng, a.hkv, a.batch), dim3(128), 0, s, a);
   if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
-  if (a.window) {
-    const int nw = a.n_new < a.window ? a.n_new : a.window;
+  if (a.ring) {
+    const int nw = a.n_new < a.ring ? a.n_new : a.ring;
     hipLaunchKernelGGL(append_window, dim3(nw, a.hkv, a.batch), dim3(128), 0, s, a);
     if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
   }

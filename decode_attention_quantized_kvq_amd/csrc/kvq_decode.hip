@@ -313,6 +313,7 @@ struct Addr {
   const uint8_t* km;
   const uint8_t* vm;
   int num_blocks, hkv, h;
+  int gs;                // log2 of the token group size (metadata per group)
   size_t head_tok;       // contiguous: first token slot of this head
   int nblk;              // blocks holding tokens
   // paged: block-table entries of this wave's blocks blk0 .. blk0 + 127,
@@ -365,13 +366,13 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const uint8_t* p, int bytes) {
 // [16g, 16g + 16) (4-bit), i.e. features [32g, 32g + 32) either way.  Values:
 // token rows 4i + g (i = 0..3), features [8t, 8t + 8), so that one load
 // instruction (fixed i) covers 4 consecutive rows, whole 128-byte lines even
-// for 64-byte (4-bit) rows.  Metadata: token t.
+// for 64-byte (4-bit) rows.  Metadata: the element of token t's group.
 struct LaneOff {
   uint32_t k0, k1, v[4], km, vm;
 };
 
 template <int KC, int KM, int VC, int VM>
-__device__ inline LaneOff lane_offsets(int t, int g) {
+__device__ inline LaneOff lane_offsets(int t, int g, int gs) {
   constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
   LaneOff o;
   o.k0 = t * KROW + (Codes<KC>::B8 ? 32 * g : Codes<KC>::B2 ? 8 * g : 16 * g);
@@ -379,8 +380,8 @@ __device__ inline LaneOff lane_offsets(int t, int g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     o.v[i] = (4 * i + g) * VROW + (Codes<VC>::B8 ? 8 * t : Codes<VC>::B2 ? 2 * t : 4 * t);
-  o.km = t * Meta<KM>::BYTES;
-  o.vm = t * Meta<VM>::BYTES;
+  o.km = (t >> gs) * Meta<KM>::BYTES;  // token t's group
+  o.vm = (t >> gs) * Meta<VM>::BYTES;
   return o;
 }
 
@@ -426,11 +427,14 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int
       else
         t.v4[4 * bb + i] = __builtin_amdgcn_raw_buffer_load_b32(rv, o.v[i], 0, 0);
     }
+    // metadata element of token slot s: s >> gs (one per token group)
     if (Meta<KM>::BYTES)
-      t.km[bb].load_buf(rsrc(ad.km + slot * Meta<KM>::BYTES, live ? 16 * Meta<KM>::BYTES : 0),
+      t.km[bb].load_buf(rsrc(ad.km + (slot >> ad.gs) * Meta<KM>::BYTES,
+                             live ? (16 >> ad.gs) * Meta<KM>::BYTES : 0),
                         o.km);
     if (Meta<VM>::BYTES)
-      t.vm[bb].load_buf(rsrc(ad.vm + slot * Meta<VM>::BYTES, live ? 16 * Meta<VM>::BYTES : 0),
+      t.vm[bb].load_buf(rsrc(ad.vm + (slot >> ad.gs) * Meta<VM>::BYTES,
+                             live ? (16 >> ad.gs) * Meta<VM>::BYTES : 0),
                         o.vm);
   }
 }
@@ -707,19 +711,23 @@ struct WinRaw {
   u32x4 v[8];      // 8 tokens, features [8c, 8c + 8)
 };
 
+// Ring slot of live bf16 token i (0 <= i < nw): (r0 + i) mod ring.
+__device__ inline int ring_slot(int i, int nw, int r0, int ring) {
+  i = i < nw ? i : nw - 1;
+  const int s = r0 + i;
+  return s < ring ? s : s - ring;
+}
+
 __device__ inline void load_win_tile(WinRaw& t, const uint16_t* kw, const uint16_t* vw, int t0,
-                                     int nw, int c, int g) {
+                                     int nw, int r0, int ring, int c, int g) {
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    int tk = t0 + 16 * bb + c;
-    tk = tk < nw ? tk : nw - 1;
-    const uint16_t* kr = kw + (size_t)tk * D;
+    const uint16_t* kr = kw + (size_t)ring_slot(t0 + 16 * bb + c, nw, r0, ring) * D;
 #pragma unroll
     for (int j = 0; j < 4; ++j) t.k[bb][j] = *(const u32x4*)(kr + 32 * j + 8 * g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int tv = t0 + 16 * bb + 4 * g + i;
-      tv = tv < nw ? tv : nw - 1;
+      const int tv = ring_slot(t0 + 16 * bb + 4 * g + i, nw, r0, ring);
       t.v[4 * bb + i] = *(const u32x4*)(vw + (size_t)tv * D + 8 * c);
     }
   }
@@ -959,8 +967,10 @@ __device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
   const int cap = (a.paged ? a.bt_stride * 16 : a.max_tokens) + a.window;
   len = len < cap ? len : cap;
   s.len = len;
-  s.nw = len < a.window ? len : a.window;
-  s.nq = len - s.nw;
+  // quantized: whole token groups older than the window; the rest is bf16
+  const int m = len - a.window > 0 ? len - a.window : 0;
+  s.nq = (m >> a.tgshift) << a.tgshift;
+  s.nw = len - s.nq;
   return s;
 }
 
@@ -968,7 +978,7 @@ __device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
 // Window split: the newest tokens, kept as bf16
 // ---------------------------------------------------------------------------
 template <int G, bool QB>
-__device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G>& sh) {
+__device__ void window_split(const DecodeArgs& a, int b, int h, int nq, int nw, Shared<G>& sh) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1019,12 +1029,14 @@ __device__ void window_split(const DecodeArgs& a, int b, int h, int nw, Shared<G
   }
   Softmax st;
   st.init(1.0f);
-  const size_t head = ((size_t)b * a.hkv + h) * a.window * D;
-  const int per = (a.window + WAVES - 1) / WAVES;
+  const size_t head = ((size_t)b * a.hkv + h) * a.ring * D;
+  // the nw live positions [nq, nq + nw) sit in ring slots (nq + i) mod ring
+  const int r0 = nq % a.ring;
+  const int per = (nw + WAVES * TILE - 1) / (WAVES * TILE) * TILE;
   const int w0 = wave * per, w1 = min(w0 + per, nw);
   for (int t0 = w0; t0 < w1; t0 += TILE) {
     WinRaw t;
-    load_win_tile(t, a.k_win + head, a.v_win + head, t0, nw, c, g);
+    load_win_tile(t, a.k_win + head, a.v_win + head, t0, nw, r0, a.ring, c, g);
     compute_win_tile<G>(t, t0, w1, qf, qs, g, limb, st);
   }
   wave_finish<G>(st, 1.0f, c, g, wave, sh);
@@ -1314,7 +1326,7 @@ __device__ Item map_item(const DecodeArgs& a, int item, int* hist) {
     return it;  // not reached: the rank-th remainder chunk exists
   }
   r -= (long long)a.hkv * np;
-  if (a.window && r < (long long)a.batch * a.hkv) {  // 3. window items
+  if (a.ring && r < (long long)a.batch * a.hkv) {  // 3. bf16 items (window, open group)
     it.kind = 1;
     it.b = (int)(r / a.hkv);
     it.h = (int)(r % a.hkv);
@@ -1348,7 +1360,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   const Plan pl = plan_of(a, si);
   if (it.kind == 1) {
     if (si.nw > 0) {
-      window_split<G, QB>(a, b, h, si.nw, sh);
+      window_split<G, QB>(a, b, h, si.nq, si.nw, sh);
       arrive_and_combine<G>(a, b, h, pl, &last_flag);
     }
     return;
@@ -1390,6 +1402,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   ad.num_blocks = a.num_blocks;
   ad.hkv = a.hkv;
   ad.h = h;
+  ad.gs = a.tgshift;
   ad.nblk = (si.nq + 15) >> 4;
   ad.blk0 = 0;
   ad.ent[0] = ad.ent[1] = 0;
@@ -1398,7 +1411,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   } else {
     ad.head_tok = ((size_t)b * a.hkv + h) * a.max_tokens;
   }
-  const LaneOff lo = lane_offsets<KC, KM, VC, VM>(lt, g);
+  const LaneOff lo = lane_offsets<KC, KM, VC, VM>(lt, g, a.tgshift);
   // the chunk's tiles spread evenly over the waves
   const int per = (tok1 - tok0 + WAVES * TILE - 1) / (WAVES * TILE) * TILE;
   const int w0 = __builtin_amdgcn_readfirstlane(tok0 + wave * per);

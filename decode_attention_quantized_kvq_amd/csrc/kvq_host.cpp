@@ -23,6 +23,22 @@ int meta_bytes(const kvq_tensor_fmt& f) {
   return f.zero_point ? 2 * w : w;
 }
 
+// Tokens per scale (1 = per token).
+static int token_group(const kvq_config* c) { return c->group_tokens > 1 ? c->group_tokens : 1; }
+
+// bf16 ring slots per (sequence, head): the window plus room for the
+// positions of a token group not yet complete.
+static int ring_slots(const kvq_config* c) {
+  return c->window + (token_group(c) > 1 ? token_group(c) : 0);
+}
+
+// Quantized positions of an n-token sequence: whole groups older than the
+// window.
+static size_t quantized_count(const kvq_config* c, size_t n) {
+  const size_t g = (size_t)token_group(c);
+  return (n > (size_t)c->window ? n - c->window : 0) / g * g;
+}
+
 static size_t side_bytes(const kvq_tensor_fmt& f, int d) {
   if (f.bits == 16) return 0;
   if (f.axis == KVQ_AXIS_CHANNEL) return size_t(4) * d;
@@ -79,12 +95,16 @@ kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
 static kvq_status check_config(const kvq_config* c, bool kernels) {
   if (!c) return KVQ_ERR_INVALID_ARG;
   if (c->num_layers < 1 || c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 ||
-      c->head_dim < 1 || c->max_tokens < 0 || c->window < 0 || c->block_tokens < 0)
+      c->head_dim < 1 || c->max_tokens < 0 || c->window < 0 || c->block_tokens < 0 ||
+      c->group_tokens < 0)
     return KVQ_ERR_INVALID_ARG;
   if (c->num_q_heads % c->num_kv_heads) return KVQ_ERR_INVALID_ARG;
   if (c->in_dtype != KVQ_DT_F32 && c->in_dtype != KVQ_DT_BF16) return KVQ_ERR_INVALID_ARG;
   if (c->block_tokens && (c->num_blocks < 1 || c->max_blocks_per_seq < 1))
     return KVQ_ERR_INVALID_ARG;
+  const int tg = token_group(c);
+  if (tg != 1 && tg != 2 && tg != 4 && tg != 8 && tg != 16) return KVQ_ERR_INVALID_ARG;
+  if (c->max_tokens % tg || (c->block_tokens && c->block_tokens % tg)) return KVQ_ERR_INVALID_ARG;
   TensorKind kk, vk;
   const kvq_status sk = classify(c->key, true, &kk);
   const kvq_status sv = classify(c->value, false, &vk);
@@ -99,7 +119,8 @@ static kvq_status check_config(const kvq_config* c, bool kernels) {
   if (c->max_tokens % 16) return KVQ_ERR_UNSUPPORTED;
   if (c->block_tokens != 0 && c->block_tokens != 16) return KVQ_ERR_UNSUPPORTED;
   if (c->window % 16 || c->window > 256) return KVQ_ERR_UNSUPPORTED;
-  if (c->window && (kk.channel || kk.meta == MK_U8 || vk.meta == MK_U8)) return KVQ_ERR_UNSUPPORTED;
+  if ((c->window || token_group(c) > 1) && (kk.channel || kk.meta == MK_U8 || vk.meta == MK_U8))
+    return KVQ_ERR_UNSUPPORTED;
   // The decode kernels are instantiated for these key/value pairs.
   const bool ok =
       (kk.code == CK_I8 && kk.meta == MK_F32 && vk.code == CK_I8 && vk.meta == MK_F32) ||
@@ -139,7 +160,7 @@ static Plan make_plan(const kvq_config* c, int max_seq_len, int split_tokens) {
   const int nq = std::max(0, max_seq_len - c->window);
   // at least one split: its workgroup writes the zeros of empty sequences
   p.n_split = std::max(1, (nq + p.split_tokens - 1) / p.split_tokens);
-  p.nsp = p.n_split + (c->window > 0 ? 1 : 0);
+  p.nsp = p.n_split + (ring_slots(c) > 0 ? 1 : 0);
   const size_t rows = (size_t)c->batch * c->num_q_heads * p.nsp;
   p.o_bytes = round_up(rows * c->head_dim * sizeof(float), 256);
   p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
@@ -158,10 +179,10 @@ static LayerSizes layer_sizes(const kvq_config* c) {
                                        : (size_t)c->batch * c->num_kv_heads * c->max_tokens;
   s.k_codes = slots * row_bytes(c->key.bits, c->head_dim);
   s.v_codes = slots * row_bytes(c->value.bits, c->head_dim);
-  s.k_meta = slots * meta_bytes(c->key);
-  s.v_meta = slots * meta_bytes(c->value);
+  s.k_meta = slots / token_group(c) * meta_bytes(c->key);
+  s.v_meta = slots / token_group(c) * meta_bytes(c->value);
   const size_t heads = (size_t)c->batch * c->num_kv_heads;
-  s.k_win = s.v_win = heads * c->window * c->head_dim * 2;
+  s.k_win = s.v_win = heads * ring_slots(c) * c->head_dim * 2;
   s.k_chan = (c->key.bits != 16 && c->key.axis == KVQ_AXIS_CHANNEL) ? heads * c->head_dim * 4 : 0;
   s.v_super = (c->value.bits != 16 && c->value.scale_fmt == KVQ_SCALE_U8_SUPER) ? heads * 4 : 0;
   s.k_super = (c->key.bits != 16 && c->key.axis == KVQ_AXIS_TOKEN &&
@@ -243,24 +264,24 @@ size_t kvq_cache_bytes(const kvq_config* cfg, const int32_t* host_seq_lens, kvq_
   const size_t D = cfg->head_dim, H = cfg->num_kv_heads, L = cfg->num_layers;
   const size_t rk = row_bytes(cfg->key.bits, cfg->head_dim);
   const size_t rv = row_bytes(cfg->value.bits, cfg->head_dim);
-  const size_t mk = meta_bytes(cfg->key), mv = meta_bytes(cfg->value);
-  const size_t per_tok = rk + rv + mk + mv;
+  const size_t mk = meta_bytes(cfg->key), mv = meta_bytes(cfg->value);  // per group
   const size_t side = side_bytes(cfg->key, cfg->head_dim) + side_bytes(cfg->value, cfg->head_dim);
+  const size_t g = (size_t)token_group(cfg), ring = (size_t)ring_slots(cfg);
   kvq_bytes b{};
   for (int i = 0; i < cfg->batch; ++i) {
     const size_t n = host_seq_lens ? (size_t)std::max(0, host_seq_lens[i]) : (size_t)cfg->max_tokens;
-    const size_t nw = std::min<size_t>(cfg->window, n);
-    const size_t nq = n - nw;
+    const size_t nq = quantized_count(cfg, n);
+    const size_t nw = n - nq;
     b.payload += L * H * nq * (rk + rv);  // 2 L H_kv D T b with per-tensor b
-    b.metadata += L * H * (nq * (mk + mv) + side);
+    b.metadata += L * H * (nq / g * (mk + mv) + side);
     b.window += L * H * nw * D * 2 * 2;
     size_t alloc_q;
     if (cfg->block_tokens)
       alloc_q = (nq + cfg->block_tokens - 1) / cfg->block_tokens * cfg->block_tokens;
     else
       alloc_q = std::max<size_t>((size_t)cfg->max_tokens, nq);
-    b.padding += L * H * (alloc_q - nq) * per_tok;
-    if (cfg->window && !cfg->block_tokens) b.padding += L * H * (cfg->window - nw) * D * 2 * 2;
+    b.padding += L * H * ((alloc_q - nq) * (rk + rv) + (alloc_q - nq) / g * (mk + mv));
+    if (ring && !cfg->block_tokens) b.padding += L * H * (ring > nw ? ring - nw : 0) * D * 2 * 2;
   }
   b.total = b.payload + b.metadata + b.window + b.padding;
   if (out) *out = b;
@@ -274,6 +295,12 @@ size_t kvq_decode_traffic_bytes(const kvq_config* cfg, const int32_t* host_seq_l
   kvq_bytes b{};
   kvq_cache_bytes(&one, host_seq_lens, &b);
   return b.payload + b.metadata + b.window;
+}
+
+static void set_groups(const kvq_config* c, int* g, int* gshift, int* ring) {
+  *g = token_group(c);
+  *gshift = *g == 16 ? 4 : *g == 8 ? 3 : *g == 4 ? 2 : *g == 2 ? 1 : 0;
+  *ring = ring_slots(c);
 }
 
 static bool split_ok(int split) { return split >= 0 && split % 128 == 0 && split <= (1 << 20); }
@@ -311,6 +338,7 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
   a.n_new = n_new;
   a.max_tokens = cfg->max_tokens;
   a.window = cfg->window;
+  set_groups(cfg, &a.tgroup, &a.tgshift, &a.ring);
   a.paged = cfg->block_tokens ? 1 : 0;
   a.num_blocks = cfg->num_blocks;
   a.bt_stride = cfg->max_blocks_per_seq;
@@ -369,6 +397,7 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   a.num_blocks = cfg->num_blocks;
   a.bt_stride = cfg->max_blocks_per_seq;
   a.window = cfg->window;
+  set_groups(cfg, &a.tgroup, &a.tgshift, &a.ring);
   a.split_tokens = p.split_tokens;
   a.n_split = p.n_split;
   a.nsp = p.nsp;

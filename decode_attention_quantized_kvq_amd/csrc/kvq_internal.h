@@ -62,6 +62,8 @@ struct AppendArgs {
   float* k_super;
   int batch, hkv, n_new, max_tokens, window, paged, num_blocks, bt_stride;
   int in_bf16;
+  int tgroup, tgshift;  // token group size g (1 = per token) and log2 g
+  int ring;           // bf16 ring slots per (sequence, head): window (+ g if g > 1)
   TensorKind kk, vk;
 };
 
@@ -85,6 +87,8 @@ struct DecodeArgs {
   uint32_t* counters;  // [B][H_kv] arrival counters, zero between calls
   int batch, hq, hkv, group;
   int max_tokens, paged, num_blocks, bt_stride, window;
+  int tgroup, tgshift;  // token group size g (1 = per token) and log2 g
+  int ring;           // bf16 ring slots per (sequence, head): window (+ g if g > 1)
   int split_tokens;  // quantized tokens per workgroup (multiple of 128)
   int n_split;       // workgroups over the quantized tokens
   int nsp;           // n_split + 1 if there is a window

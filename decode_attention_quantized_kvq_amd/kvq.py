@@ -47,7 +47,8 @@ class Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int), ("max_tokens", ctypes.c_int),
                 ("key", TensorFmt), ("value", TensorFmt), ("window", ctypes.c_int),
                 ("block_tokens", ctypes.c_int), ("num_blocks", ctypes.c_int),
-                ("max_blocks_per_seq", ctypes.c_int), ("in_dtype", ctypes.c_int)]
+                ("max_blocks_per_seq", ctypes.c_int), ("in_dtype", ctypes.c_int),
+                ("group_tokens", ctypes.c_int)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -132,10 +133,10 @@ def tensor_fmt(spec: dict) -> TensorFmt:
 def make_config(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                 max_tokens: int, key: dict, value: dict, window: int = 0,
                 block_tokens: int = 0, num_blocks: int = 0, max_blocks_per_seq: int = 0,
-                in_dtype: str = "bf16", num_layers: int = 1) -> Config:
+                in_dtype: str = "bf16", num_layers: int = 1, group_tokens: int = 1) -> Config:
     return Config(num_layers, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
                   tensor_fmt(key), tensor_fmt(value), window, block_tokens, num_blocks,
-                  max_blocks_per_seq, DTYPE[in_dtype])
+                  max_blocks_per_seq, DTYPE[in_dtype], group_tokens)
 
 
 def validate(cfg: Config) -> int:

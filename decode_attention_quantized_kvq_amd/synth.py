@@ -23,6 +23,10 @@ synthetic):
                  per-head fp32 super-scale (the 2-bit metadata remedy of "KV
                  Cache Quantization and Per-Token Scale Placement", section
                  "Per-token scales and where they can live").
+  7 int2_group   batch 32, 32/8 heads, 8192 tokens, same values as 2; keys and
+                 values uint2 with one fp16 scale + zero point per 16-token
+                 group (the other 2-bit remedy of the same section: several
+                 tokens under one scale).
 
 Recipe: every draw comes from ``np.random.default_rng(SeedSequence(key))``
 with a key that names the workload, the replica and the tensor, so any
@@ -68,6 +72,11 @@ WORKLOADS: Dict[int, dict] = {
             key=dict(bits=2, axis="token", zero_point=False, scale="u8_super"),
             value=dict(bits=2, axis="token", zero_point=False, scale="u8_super"),
             window=0, block_tokens=0, outlier_keys=4, value_dist="normal"),
+    7: dict(name="int2_group", batch=32, hq=32, hkv=8, d=128, tokens=8192,
+            lengths=None, in_dtype="bf16",
+            key=dict(bits=2, axis="token", zero_point=True, scale="f16"),
+            value=dict(bits=2, axis="token", zero_point=True, scale="f16"),
+            window=0, block_tokens=0, outlier_keys=4, value_dist="normal", group=16),
 }
 
 

@@ -45,7 +45,8 @@
  *    fp64 quotient x / s_stored, then clamped to [-(2^(b-1)-1), 2^(b-1)-1]
  *    (symmetric) or [0, 2^b-1] (zero point; rint(x/s) + z, then clamp);
  *  - a scale is evaluated in fp64 and rounded once (ties to even) to its
- *    storage type: s = amax/qmax (symmetric), s = (hi-lo)/(2^b-1) with
+ *    storage type, over the D values of a token (or the g D values of a
+ *    token group): s = amax/qmax (symmetric), s = (hi-lo)/(2^b-1) with
  *    lo = min(min x, 0), hi = max(max x, 0) and z = clamp(rint(-lo/s))
  *    (zero point); an all-zero vector stores s = 1 (and z = 0) and codes 0;
  *    a scale that rounds to 0 stores the type's smallest positive value, an
@@ -61,13 +62,14 @@
  * kvq_buffer_sizes; "row" = D * bits / 8 code bytes of one token and head):
  *  contiguous (block_tokens == 0):
  *    codes  [L][B][H_kv][max_tokens][row]
- *    meta   [L][B][H_kv][max_tokens] of the meta element below
+ *    meta   [L][B][H_kv][max_tokens / g] of the meta element below
  *  paged (block_tokens == 16):
  *    codes  [L][num_blocks][H_kv][16][row]
- *    meta   [L][num_blocks][H_kv][16]
+ *    meta   [L][num_blocks][H_kv][16 / g]
  *    quantized position p of sequence b lives in block
  *    block_table[b][p / 16], slot p % 16
- *  window  [L][B][H_kv][window][D] bf16; position p sits in slot p % window
+ *  ring   [L][B][H_kv][R][D] bf16 with R = window (+ g if g > 1); position
+ *    p sits in slot p % R
  *  k_chan_scale [L][B][H_kv][D] fp32;  k_super, v_super [L][B][H_kv] fp32
  *  code bytes: int8 codes as two's complement bytes (unsigned bytes with a
  *    zero point); int4 codes packed two per byte, element 2j in the low nibble
@@ -78,8 +80,11 @@
  *  meta element per token: f32 scale (4 B); f32 scale + f32 zero point
  *    (8 B); f16 scale (2 B); f16 scale + f16 zero point (4 B, scale in the
  *    low half); u8 scale code (1 B)
- *  With a window, positions [0, len - min(window, len)) are quantized and
- *  the newest min(window, len) positions are kept as bf16 in the ring.
+ *  Positions [0, Q) with Q = floor(max(len - window, 0) / g) * g are
+ *  quantized; the newest len - Q (the window, plus the positions of a token
+ *  group not yet complete) are kept as bf16 in the ring.  g = group_tokens
+ *  (1 when 0).  Metadata element j of a (sequence, head) belongs to
+ *  positions [j g, j g + g).
  *
  * Error behaviour: every call validates its arguments on the host before
  * launching anything and returns a kvq_status; nothing is thrown across the
@@ -152,6 +157,11 @@ typedef struct {
   int num_blocks;          /* paged: blocks per layer in the pool */
   int max_blocks_per_seq;  /* paged: columns of block_table */
   kvq_dtype in_dtype;      /* dtype of k_new, v_new and q */
+  int group_tokens;        /* 0 or 1: one scale per token; 2, 4, 8 or 16: one
+                              scale (and zero point) per group of that many
+                              consecutive positions of a sequence and head
+                              (P3, "Per-token scales and where they can
+                              live": several tokens under one scale) */
 } kvq_config;
 
 /* Device pointers of one cache (all layers).  Unused buffers may be NULL. */
@@ -200,7 +210,8 @@ const char* kvq_status_string(kvq_status s);
  *   uint4 f16 scale + zero; the same        uint8 f16 scale + zero; the same
  *   int2 f32; int2 f32                      int2 u8 super; int2 u8 super
  *   uint2 f16 scale + zero; the same
- * An 8-bit scale code (u8 super) or per-channel keys exclude a window. */
+ * An 8-bit scale code (u8 super) or per-channel keys exclude a window and
+ * token groups. */
 kvq_status kvq_validate(const kvq_config* cfg);
 
 /* Fills *out with the byte size of each buffer of the layout above. */

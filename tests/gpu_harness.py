@@ -56,6 +56,7 @@ def make_config(wl, lens, num_blocks=0, max_blocks=0):
     return K.make_config(batch=wl["batch"], num_q_heads=wl["hq"], num_kv_heads=wl["hkv"],
                          head_dim=wl["d"], max_tokens=wl["tokens"], key=wl["key"],
                          value=wl["value"], window=wl["window"], block_tokens=wl["block_tokens"],
+                         group_tokens=wl.get("group", 1),
                          num_blocks=num_blocks, max_blocks_per_seq=max_blocks,
                          in_dtype=wl["in_dtype"])
 
@@ -74,7 +75,8 @@ def build(wl: dict, lens: List[int], decode_steps: int = 0, replica: int = 0,
     cfg = make_config(wl, lens, nb, mb)
     assert K.validate(cfg) == K.KVQ_OK
     cache = K.KvqCache(cfg, "cuda", None if table is None else torch.from_numpy(table))
-    orc = O.OracleCache(B, H, D, oracle_fmt(wl["key"]), oracle_fmt(wl["value"]), wl["window"]) if oracle else None
+    orc = O.OracleCache(B, H, D, oracle_fmt(wl["key"]), oracle_fmt(wl["value"]), wl["window"],
+                        group=wl.get("group", 1)) if oracle else None
     full = {}
     for b in range(B):
         for h in range(H):
@@ -86,7 +88,8 @@ def build(wl: dict, lens: List[int], decode_steps: int = 0, replica: int = 0,
     for i in range(chunks):
         appends.append([(bounds[b][i], bounds[b][i + 1]) for b in range(B)])
     for s in range(decode_steps):
-        appends.append([(pre[b] + s, min(pre[b] + s + 1, lens[b])) for b in range(B)])
+        # a sequence shorter than decode_steps has nothing left to append
+        appends.append([(min(pre[b] + s, lens[b]), min(pre[b] + s + 1, lens[b])) for b in range(B)])
     for ap in appends:
         n_new = max(e - s for s, e in ap)
         if n_new == 0:
@@ -198,6 +201,9 @@ def device_records(bt: Built, t: str, b: int, h: int, n: int) -> dict:
         out["chan"] = ch[b * bt.cfg.num_kv_heads + h]
         return out
     meta = host(bt.cache.buffers[f"{t}_meta"])
+    # one metadata element per token group: element slot // g of its first slot
+    g = bt.wl.get("group", 1)
+    slots = slots[::g] // g
     if scale == "u8_super":
         out["u"] = meta[slots]
         out["S"] = host(bt.cache.buffers[f"{t}_super"]).view(np.float32)[b * bt.cfg.num_kv_heads + h]
@@ -214,10 +220,16 @@ def device_records(bt: Built, t: str, b: int, h: int, n: int) -> dict:
     return out
 
 
+def ring_slots(wl) -> int:
+    """bf16 ring slots per (sequence, head): the window, plus g with token groups."""
+    g = wl.get("group", 1)
+    return wl["window"] + (g if g > 1 else 0)
+
+
 def window_values(bt: Built, t: str, b: int, h: int, nw: int) -> np.ndarray:
-    """bf16 window ring of (b, h) as float64, slots 0..nw-1."""
-    W, D = bt.wl["window"], bt.wl["d"]
-    ring = host(bt.cache.buffers[f"{t}_win"]).view(np.uint16).reshape(-1, W, D)
+    """bf16 ring of (b, h) as float64, slots 0..nw-1."""
+    R, D = ring_slots(bt.wl), bt.wl["d"]
+    ring = host(bt.cache.buffers[f"{t}_win"]).view(np.uint16).reshape(-1, R, D)
     r = ring[b * bt.cfg.num_kv_heads + h][:nw]
     return (r.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
@@ -244,11 +256,12 @@ def check_records(bt: Built, b: int, h: int):
                 assert np.array_equal(_bits(dev["s"]), _bits(st.s[h])), f"{t} scales differ b={b} h={h}"
             if "z" in dev:
                 assert np.array_equal(_bits(dev["z"]), _bits(st.z[h])), f"{t} zero points differ"
-        if bt.wl["window"]:
-            # ring slot of position p is p % W
+        R = ring_slots(bt.wl)
+        if R:
+            # ring slot of position p is p % R
             wv = bt.oracle.window_values(b, t)[h]
             nw = wv.shape[0]
             n_tot = bt.oracle.lens[b]
             pos = np.arange(n_tot - nw, n_tot)
-            ring = window_values(bt, t, b, h, bt.wl["window"])
-            assert np.array_equal(ring[pos % bt.wl["window"]], wv), f"{t} window differs b={b} h={h}"
+            ring = window_values(bt, t, b, h, R)
+            assert np.array_equal(ring[pos % R], wv), f"{t} bf16 ring differs b={b} h={h}"

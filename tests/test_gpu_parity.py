@@ -39,7 +39,7 @@ def test_tiny_full_size():
     full_check(bt, steps=(0, 1, 2))
 
 
-@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6, 7])
 def test_full_size_sampled(wid):
     """Each workload at its full size, decoded in the launch configuration the
     benchmark times (library-chosen split).  For sampled (sequence, KV head)
@@ -63,7 +63,7 @@ def test_full_size_sampled(wid):
         n = lens[b]
         kx = bt.inputs["k"][b, h, :n].float().cpu().numpy().astype(np.float64)
         vx = bt.inputs["v"][b, h, :n].float().cpu().numpy().astype(np.float64)
-        orc = H.O.OracleCache(1, 1, wl["d"], kf, vf, wl["window"])
+        orc = H.O.OracleCache(1, 1, wl["d"], kf, vf, wl["window"], group=wl.get("group", 1))
         orc.append(0, kx[None], vx[None])
         for t in ("k", "v"):
             st = orc.stored(0, t)
@@ -91,7 +91,8 @@ def test_full_size_sampled(wid):
     (4, dict(batch=3, tokens=1024), [1024, 300, 131], 5, 2),
     (5, dict(batch=2, tokens=1024), [1000, 613], 4, 1),
     (6, dict(batch=2, tokens=1024), [1000, 555], 3, 2),
-], ids=["w2", "w3", "w4", "w5", "w6"])
+    (7, dict(batch=2, tokens=1024), [1000, 557], 19, 2),
+], ids=["w2", "w3", "w4", "w5", "w6", "w7"])
 def test_workload_reduced(wid, over, lens, decode_steps, chunks):
     """Each workload's formats at a size the oracle finishes in seconds, with
     ragged lengths, a prefill in one or two appends, then decode appends."""
@@ -104,7 +105,7 @@ def test_workload_reduced(wid, over, lens, decode_steps, chunks):
 
 
 @pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 300])
-@pytest.mark.parametrize("wid", [2, 3, 5, 6])
+@pytest.mark.parametrize("wid", [2, 3, 5, 6, 7])
 def test_tile_edges(wid, n):
     """Lengths around the 16-token block and 32-token tile edges."""
     H.log(f"case: tile edges workload {wid} n={n}")
@@ -144,6 +145,31 @@ def test_formats_and_groups(fmt, hq, hkv):
     wl = synth.workload(2, batch=2, hq=hq, hkv=hkv, tokens=512, key=k, value=v)
     bt = H.build(wl, [500, 77], decode_steps=2)
     full_check(bt, steps=(0,), split_tokens=128)
+
+
+@pytest.mark.parametrize("g,window,paged,fmt", [
+    (2, 0, False, "u2z"), (4, 16, False, "i8"), (8, 0, True, "u4z"), (16, 128, True, "i2"),
+    (16, 0, False, "u8z"), (4, 32, True, "i4"),
+])
+def test_token_groups(g, window, paged, fmt):
+    """One scale per g consecutive positions: groups completed by a prefill,
+    by ragged appends and by single-token decode appends (crossing group and
+    window edges); the incomplete group and the window stay bf16 in the
+    ring.  Records bit for bit, outputs within the bar."""
+    specs = {
+        "u2z": dict(bits=2, zero_point=True, scale="f16"), "i8": dict(bits=8),
+        "u4z": dict(bits=4, zero_point=True, scale="f16"), "i2": dict(bits=2),
+        "u8z": dict(bits=8, zero_point=True, scale="f16"), "i4": dict(bits=4),
+    }
+    H.log(f"case: token groups g={g} window={window} paged={paged} {fmt}")
+    over = dict(batch=3, hq=16, hkv=4, tokens=512, key=specs[fmt], value=specs[fmt],
+                window=window, group=g)
+    if not paged:
+        over["block_tokens"] = 0
+    wl = synth.workload(4 if paged else 2, **over)
+    bt = H.build(wl, [500, 2 * g + 1, g - 1 + window], decode_steps=2 * g + 3, chunks=2)
+    full_check(bt, steps=(0, 1))
+    full_check(bt, steps=(0,), split_tokens=128, records=False)
 
 
 def test_empty_and_zero_sequences():

@@ -39,7 +39,8 @@ def test_status_strings():
 def cfg_of(wl, **kw):
     d = dict(batch=wl["batch"], num_q_heads=wl["hq"], num_kv_heads=wl["hkv"], head_dim=wl["d"],
              max_tokens=wl["tokens"], key=wl["key"], value=wl["value"], window=wl["window"],
-             block_tokens=wl["block_tokens"], in_dtype=wl["in_dtype"])
+             block_tokens=wl["block_tokens"], in_dtype=wl["in_dtype"],
+             group_tokens=wl.get("group", 1))
     if wl["block_tokens"]:
         d["num_blocks"] = 100
         d["max_blocks_per_seq"] = -(-(wl["tokens"] - wl["window"]) // 16)
@@ -52,12 +53,12 @@ def oracle_fmt(spec):
                           spec.get("scale", "f32"))
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6, 7])
 def test_workloads_validate(wid):
     assert K.validate(cfg_of(synth.workload(wid))) == K.KVQ_OK
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6, 7])
 def test_cache_bytes_match_oracle(wid):
     wl = synth.workload(wid)
     lens = synth.seq_lengths(wl)
@@ -65,10 +66,10 @@ def test_cache_bytes_match_oracle(wid):
     got = K.cache_bytes(cfg, lens)
     want = O.cache_bytes(oracle_fmt(wl["key"]), oracle_fmt(wl["value"]), 1, wl["hkv"], wl["d"],
                          lens, wl["window"], wl["block_tokens"],
-                         None if wl["block_tokens"] else wl["tokens"])
+                         None if wl["block_tokens"] else wl["tokens"], group=wl.get("group", 1))
     assert got == want
     traffic = O.decode_traffic(oracle_fmt(wl["key"]), oracle_fmt(wl["value"]), wl["hkv"], wl["d"],
-                               lens, wl["window"])
+                               lens, wl["window"], group=wl.get("group", 1))
     assert K.decode_traffic_bytes(cfg, lens) == traffic
 
 
