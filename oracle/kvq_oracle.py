@@ -54,6 +54,13 @@ Readings where the pages leave a step open (each restated where it is used):
       quantized from its input value, or from its bf16 window copy when it
       leaves the window in a later append.
   R13 the output is fp32 on the device; here fp64.
+  R21 integer query (P3 "Precision floors and mixed cache formats": an 8-bit
+      query against integer key codes, the integer sum converted to float
+      once before the exponential): per query head, symmetric,
+      s = fl32(amax / 127) and Q = clamp(rint(fl32(q / s)), -127, 127), both
+      divisions IEEE fp32, the kernel's precision (the pages fix none); an
+      all-zero head gets s = 1 and codes 0.  Attention then uses Q * s for
+      every token.  The exact path (the default) never quantizes the query.
   R20 token groups (P3 "Per-token scales and where they can live": several
       tokens under one scale): with a group size g, one scale (and zero
       point) is taken over all g*D values of g consecutive positions of a
@@ -268,6 +275,18 @@ def quantize_superscaled(v, S, bits: int):
     codes = np.clip(rne_quotient(v, safe[..., None]), -qmax, qmax)
     codes = np.where((u == 0.0)[..., None], 0.0, codes)
     return codes.astype(np.int32), u.astype(np.uint8)
+
+
+def quantize_query_int8(q):
+    """Reading R21: the query quantized to int8 per head (last axis), with
+    the scale and the quotient evaluated in IEEE fp32.  q holds values exact
+    in fp32.  Returns (codes int32 [..., D], scale float32 [...])."""
+    q32 = np.asarray(q, np.float32)
+    amax = np.max(np.abs(q32), axis=-1)
+    zero = amax == 0
+    s = np.where(zero, np.float32(1.0), amax / np.float32(127.0)).astype(np.float32)
+    codes = np.clip(np.rint(q32 / s[..., None]), -127, 127)
+    return codes.astype(np.int32), s
 
 
 # --------------------------------------------------------------------------
@@ -487,8 +506,15 @@ class OracleCache:
     def window_values(self, b: int, t: str) -> np.ndarray:
         return self.win[b][t]
 
-    def attend(self, b: int, q) -> np.ndarray:
+    def attend(self, b: int, q, query_bits: int = 0) -> np.ndarray:
+        """Attention of the queries q [Hq, D] of sequence b; query_bits = 8
+        takes the integer-query path (reading R21)."""
         k_hat, v_hat = self.reconstructed(b)
+        if query_bits == 8:
+            codes, s = quantize_query_int8(q)
+            q = dequant_sym(codes, s)
+        elif query_bits != 0:
+            raise ValueError("query_bits is 0 (exact) or 8")
         return attend(q, k_hat, v_hat)
 
 

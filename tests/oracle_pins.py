@@ -598,6 +598,50 @@ def pin_group_bytes(O):
     assert Fraction(b["metadata"], b["payload"]) == Fraction(125, 1000) / 16
 
 
+def pin_int_query(O):
+    """Integer query (reading R21 of P3 "Precision floors and mixed cache
+    formats"): s is the correctly rounded fp32 quotient amax/127; each code is
+    the round-half-even of the correctly rounded fp32 quotient q/s (checked
+    on constructed near-ties too, where an fp64 quotient rounds the other
+    way); the largest element maps to +-127; |q - Q s| <= s/2 up to the fp32
+    quotient's rounding; an all-zero head gets s = 1, codes 0; and attention
+    on the integer path is attention on Q s."""
+    rng = _rng(181)
+    q = _f32(rng.standard_normal((6, 64)) * np.exp(rng.uniform(-4, 4, (6, 1))))
+    q[2] = 0.0
+    near = []
+    for trial in range(10):                       # quotients within ulps of k + 1/2
+        st = np.float32(rng.uniform(0.003, 0.03))
+        row = _near_ties(st, 64, 300 + trial)
+        row[0] = np.float32(127.0 * float(st) * (1 + 1e-7))  # fl32(amax/127) close to st
+        near.append(row)
+    q = np.concatenate([q, np.stack(near)])
+    codes, s = O.quantize_query_int8(q)
+    for h in range(len(q)):
+        amax = max(abs(fr(x)) for x in q[h])
+        if amax == 0:
+            assert float(s[h]) == 1.0 and not codes[h].any()
+            continue
+        assert Fraction(float(s[h])) == rn32(amax / 127), h
+        for i in range(64):
+            quot = rn32(fr(q[h, i]) / Fraction(float(s[h])))   # the fp32 division
+            assert codes[h, i] == max(-127, min(127, round(quot))), (h, i)
+        top = int(np.argmax(np.abs(q[h])))
+        assert abs(codes[h, top]) == 127
+        err = np.abs(q[h] - codes[h] * np.float64(s[h]))
+        # half a step, plus the fp32 quotient's rounding (|q / s| <= 127.5 < 2^7)
+        assert np.all(err <= float(s[h]) * (0.5 + 2.0 ** -16))
+    # attention on the integer path equals attention on the reconstructed query
+    fmt = O.TensorFormat(8)
+    cache = O.OracleCache(1, 2, 64, fmt, fmt)
+    k = _bf16(rng.standard_normal((2, 40, 64)))
+    cache.append(0, k, k)
+    qq = _bf16(rng.standard_normal((4, 64)))
+    c, sq = O.quantize_query_int8(qq)
+    assert np.array_equal(cache.attend(0, qq, query_bits=8), cache.attend(0, c * sq.astype(np.float64)[:, None]))
+    assert not np.array_equal(cache.attend(0, qq, query_bits=8), cache.attend(0, qq))
+
+
 def pin_window_stores_bf16(O):
     """Unquantized tokens (bits 16, or the recent window) are stored in bf16:
     fp32 inputs come back rounded to nearest-even bf16 (torch's conversion)."""

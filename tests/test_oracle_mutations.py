@@ -60,6 +60,15 @@ def m_group_count_rounds_up(O):
     O.quantized_count = lambda n, window=0, group=1: -(-max(n - window, 0) // group) * group
 
 
+def m_int_query_fp64_division(O):
+    def qq(q):
+        q = np.asarray(q, np.float64)
+        amax = np.max(np.abs(q), axis=-1)
+        s = np.where(amax == 0, 1.0, amax / 127.0)
+        return np.clip(np.rint(q / s[..., None]), -127, 127).astype(np.int32), s.astype(np.float32)
+    O.quantize_query_int8 = qq
+
+
 def m_no_inv_sqrt_d(O):
     O.scores = lambda q, k: np.asarray(k, np.float64) @ np.asarray(q, np.float64)
 
