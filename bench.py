@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--config", type=int, default=2, help="workload 1..7 (default 2: GQA int8)")
     p.add_argument("--replicas", type=int, default=0, help="cache copies (0 = enough for 1 GiB)")
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
+    p.add_argument("--query-bits", type=int, default=0,
+                   help="0: exact query; 8: the integer-query path")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU baseline time budget")
     p.add_argument("--copy-probe", type=int, default=0,
@@ -241,7 +243,7 @@ def main():
 
     def step(i, events=None):
         K.decode_attn(caches[i % reps], 0, q, max_len, out=out, workspace=ws,
-                      split_tokens=args.split, split_events=events)
+                      split_tokens=args.split, split_events=events, query_bits=args.query_bits)
 
     for i in range(args.warmup):
         step(i)
@@ -320,7 +322,8 @@ def main():
                    "kv_heads": wl["hkv"], "head_dim": wl["d"], "tokens": max_len,
                    "key": wl["key"], "value": wl["value"], "window": wl["window"],
                    "block_tokens": wl["block_tokens"], "replicas": reps,
-                   "split_tokens": args.split or "auto", "kernel_sources": sha},
+                   "split_tokens": args.split or "auto", "query_bits": args.query_bits,
+                   "kernel_sources": sha},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": hbm, "kernel": "decode_split",

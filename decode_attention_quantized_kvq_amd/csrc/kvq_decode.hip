@@ -1007,6 +1007,17 @@ __device__ void window_split(const DecodeArgs& a, int b, int h, int nq, int nw, 
   float amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(qv[k]));
+  if (a.qbits == 8) {
+    // integer query: the bf16 tokens are attended with Q s as well
+    const float hmax = rows_max(amax);
+    const float s = hmax > 0.0f ? hmax / 127.0f : 1.0f;
+    amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      qv[k] = fminf(fmaxf(rintf(qv[k] / s), -127.0f), 127.0f) * s;
+      amax = fmaxf(amax, fabsf(qv[k]));
+    }
+  }
   float inv;
   const float sc = q_norm_scale(rows_max(amax), &inv);
   const float qs = LOG2E * 0.08838834764831845f * inv;  // log2(e) / sqrt(128)
@@ -1453,15 +1464,20 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
     float amax = 0.0f;
 #pragma unroll
     for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(qv[n]));
-    float inv;
-    const float sc = q_int_scale(rows_max(amax), &inv);  // max over the row's 4 lanes
+    const float hmax = rows_max(amax);  // max over the row's 4 lanes: the head's
+    float inv, sc = 0.0f;
+    if (a.qbits == 8)  // integer query: s = fl32(amax / 127), Q = rint(fl32(q / s))
+      inv = hmax > 0.0f ? hmax / 127.0f : 1.0f;
+    else
+      sc = q_int_scale(hmax, &inv);
     float qsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint64_t pk = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = rintf(qv[key_feature<KC>(j, 0, e)] * sc);
+        const float y = qv[key_feature<KC>(j, 0, e)];
+        const float x = a.qbits == 8 ? fminf(fmaxf(rintf(y / inv), -127.0f), 127.0f) : rintf(y * sc);
         qsum += x;
         const int Q = (int)x;
         const int l2 = (int)(int8_t)(Q & 0xFF);
@@ -1473,7 +1489,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
       }
       qa[u][j] = (long)pk;
     }
-    qs_row[u] = LOG2E * 0.08838834764831845f * inv * ksup;  // log2(e) / sqrt(128) / 2^e
+    qs_row[u] = LOG2E * 0.08838834764831845f * inv * ksup;  // log2(e) / sqrt(128) / 2^e (or s)
     sq_row[u] = rows_sum(qsum);
   }
   // score scale and query sum of each head, from the lane of its limb-0 row

@@ -357,6 +357,11 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   const int split = opts ? opts->split_tokens : 0;
   if (!split_ok(split)) return KVQ_ERR_INVALID_ARG;
   if (opts && (!opts->split_begin_event != !opts->split_end_event)) return KVQ_ERR_INVALID_ARG;
+  const int qbits = opts ? opts->query_bits : 0;
+  if (qbits != 0 && qbits != 8) return KVQ_ERR_INVALID_ARG;
+  // the per-channel key scale is folded onto the query in fp32; an int8 query
+  // of the folded product is not a path the kernels run
+  if (qbits == 8 && cfg->key.axis == KVQ_AXIS_CHANNEL) return KVQ_ERR_UNSUPPORTED;
   // a paged wave addresses at most 128 blocks: splits of at most 4 x 2048 tokens
   if (cfg->block_tokens && split > 8192) return KVQ_ERR_INVALID_ARG;
   const Plan p = make_plan(cfg, max_seq_len, split);
@@ -404,6 +409,7 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   a.in_bf16 = cfg->in_dtype == KVQ_DT_BF16;
   classify(cfg->key, true, &a.kk);
   classify(cfg->value, false, &a.vk);
+  a.qbits = qbits;
   a.ev_begin = opts ? opts->split_begin_event : nullptr;
   a.ev_end = opts ? opts->split_end_event : nullptr;
   return launch_decode(a, stream);

@@ -89,6 +89,7 @@ struct DecodeArgs {
   int max_tokens, paged, num_blocks, bt_stride, window;
   int tgroup, tgshift;  // token group size g (1 = per token) and log2 g
   int ring;           // bf16 ring slots per (sequence, head): window (+ g if g > 1)
+  int qbits;          // 0: exact query limbs; 8: the query quantized to int8 per head
   int split_tokens;  // quantized tokens per workgroup (multiple of 128)
   int n_split;       // workgroups over the quantized tokens
   int nsp;           // n_split + 1 if there is a window

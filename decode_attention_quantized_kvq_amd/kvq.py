@@ -72,7 +72,7 @@ class BufferSizes(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("split_tokens", ctypes.c_int), ("split_begin_event", ctypes.c_void_p),
-                ("split_end_event", ctypes.c_void_p)]
+                ("split_end_event", ctypes.c_void_p), ("query_bits", ctypes.c_int)]
 
 
 class KvqError(RuntimeError):
@@ -252,8 +252,11 @@ def quantize_append(cache: KvqCache, layer: int, k_new: torch.Tensor, v_new: tor
 
 def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                split_tokens: int = 0, stream=None, split_events=None) -> torch.Tensor:
+                split_tokens: int = 0, stream=None, split_events=None,
+                query_bits: int = 0) -> torch.Tensor:
     """kvq_decode_attn: q [B][Hq][D] -> out [B][Hq][D] fp32.
+
+    query_bits: 0 (the query is not quantized) or 8 (the integer-query path).
 
     workspace: scratch of decode_workspace_bytes() bytes, zero-filled before
     its first use (the library leaves it reusable); one is allocated per
@@ -273,6 +276,7 @@ def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     desc = cache.desc()
     opts = DecodeOpts(int(split_tokens))
+    opts.query_bits = int(query_bits)
     if split_events is not None:
         opts.split_begin_event = split_events[0].cuda_event
         opts.split_end_event = split_events[1].cuda_event

@@ -253,6 +253,14 @@ typedef struct {
                                kernel's dispatch, or NULL */
   void* split_end_event;    /* hipEvent_t stamped with its end; both events or
                                neither (KVQ_ERR_INVALID_ARG otherwise) */
+  int query_bits;           /* 0: the query is not quantized (its scale moves
+                               onto integer limbs exactly); 8: the integer-query
+                               path of P3, "Precision floors and mixed cache
+                               formats": per query head s = fl32(amax / 127),
+                               Q = rint(fl32(q / s)) in [-127, 127], and every
+                               score uses Q s (window tokens too).  8 is not
+                               run with per-channel keys (KVQ_ERR_UNSUPPORTED);
+                               other values are KVQ_ERR_INVALID_ARG. */
 } kvq_decode_opts;
 
 /* Single-query decode attention of one layer over every cached token (P2,

@@ -133,9 +133,10 @@ def queries(wl, step=0, replica=0):
     return np.stack([synth.queries(wl, b, replica, step) for b in range(wl["batch"])])
 
 
-def run_decode(bt: Built, q: np.ndarray, split_tokens=0) -> np.ndarray:
+def run_decode(bt: Built, q: np.ndarray, split_tokens=0, query_bits=0) -> np.ndarray:
     qd = to_device(q, bt.wl["in_dtype"])
-    out = K.decode_attn(bt.cache, 0, qd, max(bt.lens) if bt.lens else 0, split_tokens=split_tokens)
+    out = K.decode_attn(bt.cache, 0, qd, max(bt.lens) if bt.lens else 0, split_tokens=split_tokens,
+                        query_bits=query_bits)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
 

@@ -172,6 +172,36 @@ def test_token_groups(g, window, paged, fmt):
     full_check(bt, steps=(0,), split_tokens=128, records=False)
 
 
+@pytest.mark.parametrize("wid,over,lens", [
+    (2, dict(batch=3, tokens=1024), [1000, 333, 0]),
+    (3, dict(batch=2, tokens=512), [500, 77]),
+    (4, dict(batch=3, tokens=512), [500, 100, 129]),
+    (6, dict(batch=2, tokens=512), [500, 31]),
+    (1, dict(tokens=512), [512]),
+], ids=["w2", "w3", "w4", "w6", "w1"])
+def test_integer_query(wid, over, lens):
+    """The integer-query path (the query quantized to int8 per head, fp32
+    scale and quotient) against the oracle's same path, window tokens
+    included; and it is a different computation from the exact path."""
+    H.log(f"case: integer query workload {wid} {over}")
+    wl = synth.workload(wid, **over)
+    bt = H.build(wl, lens)
+    q = H.queries(wl)
+    want = np.stack([bt.oracle.attend(b, q[b], query_bits=8) for b in range(wl["batch"])])
+    exact = np.stack([bt.oracle.attend(b, q[b]) for b in range(wl["batch"])])
+    for split in (0, 128):
+        got = H.run_decode(bt, q, split, query_bits=8)
+        H.check_close(got, want, f"{wl['name']} int8 query split {split}")
+    assert np.abs(want - exact).max() > 0.0
+
+
+def test_integer_query_rejected_with_channel_keys():
+    wl = synth.workload(5, batch=1, tokens=256)
+    bt = H.build(wl, [100], oracle=False)
+    with pytest.raises(K.KvqError):
+        H.run_decode(bt, H.queries(wl), query_bits=8)
+
+
 def test_empty_and_zero_sequences():
     """A sequence with no tokens gives zeros; all-zero vectors quantize to
     codes 0 with scale 1 and attend like any other token."""

@@ -172,6 +172,18 @@ def test_calls_fail_before_launch():
                                 ctypes.byref(opts), None)
     assert st == K.KVQ_ERR_INVALID_ARG
     assert K.decode_workspace_bytes(cfg, 64, 100) == 0
+    # query_bits: 0 or 8, and 8 is not run with per-channel keys
+    opts = K.DecodeOpts(0)
+    opts.query_bits = 4
+    st = lib.kvq_decode_attn_ex(ctypes.byref(cfg), ctypes.byref(fake), 0, 256, 256, 256, need, 64,
+                                ctypes.byref(opts), None)
+    assert st == K.KVQ_ERR_INVALID_ARG
+    cfg_ch = K.make_config(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, max_tokens=64,
+                           key=dict(bits=8, axis="channel"), value=dict(bits=4, scale="u8_super"))
+    opts.query_bits = 8
+    st = lib.kvq_decode_attn_ex(ctypes.byref(cfg_ch), ctypes.byref(fake), 0, 256, 256, 256, need, 64,
+                                ctypes.byref(opts), None)
+    assert st == K.KVQ_ERR_UNSUPPORTED
     # n_new == 0 is a no-op
     st = lib.kvq_quantize_append(ctypes.byref(cfg), ctypes.byref(fake), 0, 256, 256, 0, None, None)
     assert st == K.KVQ_OK
