@@ -128,6 +128,17 @@ def round_bf16(x) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+def round_bf16_from_f64(x) -> np.ndarray:
+    """fp64 values rounded once to bf16 (nearest, ties to even), directly on
+    the fp64 bit pattern: drop 45 of its 52 fraction bits.  For values that
+    are not exact in fp32 (a dequantized code times a scale), rounding to
+    fp32 first could round twice.  Finite values in the normal bf16 range."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float64)).view(np.uint64)
+    u = ((u + np.uint64((1 << 44) - 1) + ((u >> np.uint64(45)) & np.uint64(1)))
+         >> np.uint64(45)) << np.uint64(45)
+    return u.view(np.float64).copy()
+
+
 def qmax_symmetric(bits: int) -> int:
     """Largest magnitude of a symmetric code; -2^(b-1) is never produced (R3)."""
     return (1 << (bits - 1)) - 1
@@ -602,6 +613,13 @@ def decode_traffic(key: TensorFormat, value: TensorFormat, hkv: int, d: int,
     padding."""
     b = cache_bytes(key, value, 1, hkv, d, lens, window, group=group)
     return b["payload"] + b["metadata"] + b["window"]
+
+
+def dequantized_bf16(cache: "OracleCache", b: int):
+    """Reconstructed keys and values of sequence b rounded once to bf16: the
+    cache a dequantize-into-temporary-storage path attends over."""
+    k_hat, v_hat = cache.reconstructed(b)
+    return round_bf16_from_f64(k_hat), round_bf16_from_f64(v_hat)
 
 
 def multiply_adds(hq: int, d: int, lens: Sequence[int]) -> int:

@@ -642,6 +642,40 @@ def pin_int_query(O):
     assert not np.array_equal(cache.attend(0, qq, query_bits=8), cache.attend(0, qq))
 
 
+def pin_bf16_from_f64(O):
+    """Rounding fp64 values once to bf16 equals exact rational rounding to 8
+    significant bits (ties to even), including values a hair off a bf16
+    midpoint, where rounding to fp32 first would round the other way."""
+    rng = _rng(191)
+    xs = list(rng.standard_normal(300) * np.exp(rng.uniform(-20, 20, 300)))
+    for _ in range(200):                          # midpoints +- a few fp64 ulps
+        m = np.float64(np.float32(rng.standard_normal()))
+        e = math.frexp(m)[1]
+        mid = math.ldexp(round(math.ldexp(m, 8 - e)) + 0.5, e - 8)
+        xs += [mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf),
+               mid + math.ldexp(1, e - 33), mid - math.ldexp(1, e - 33)]
+    got = O.round_bf16_from_f64(np.array(xs))
+    for x, g in zip(xs, got):
+        f = Fraction(float(x))
+        if f == 0:
+            assert g == 0
+            continue
+        e = math.floor(math.log2(abs(f)))
+        while Fraction(2) ** e > abs(f):
+            e -= 1
+        while Fraction(2) ** (e + 1) <= abs(f):
+            e += 1
+        ulp = Fraction(2) ** (e - 7)
+        q = f / ulp
+        n = math.floor(q)
+        r = q - n
+        n = n + 1 if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2) else n
+        assert Fraction(float(g)) == n * ulp, (x, g)
+    # rounding through fp32 first gets some of the near-midpoint values wrong
+    near = np.array(xs[300:])
+    assert np.count_nonzero(O.round_bf16_from_f64(near) != O.round_bf16(near)) > 0
+
+
 def pin_window_stores_bf16(O):
     """Unquantized tokens (bits 16, or the recent window) are stored in bf16:
     fp32 inputs come back rounded to nearest-even bf16 (torch's conversion)."""
