@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     p.add_argument("--query-bits", type=int, default=0,
                    help="0: exact query; 8: the integer-query path")
+    p.add_argument("--ab", action="store_true",
+                   help="also time the dequantize-into-temporary-storage path")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU baseline time budget")
     p.add_argument("--copy-probe", type=int, default=0,
@@ -206,6 +208,41 @@ def percentile(xs, p):
     return xs[min(len(xs) - 1, max(0, int(round(p / 100.0 * (len(xs) - 1)))))]
 
 
+def ab_path(args, wl, caches, q, out, max_len, K, torch):
+    """The dequantize-into-temporary-storage alternative: kvq_dequantize writes
+    each replica as a bf16 cache (one bf16 copy per replica, so the copies do
+    not sit in the Infinity Cache either), then the decode kernel reads that.
+    Times the dequantize, the bf16 decode and the two in sequence per step."""
+    reps = len(caches)
+    T16 = -(-max_len // 16) * 16
+    tmps = [K.bf16_cache_like(c, T16) for c in caches]
+    ws = torch.zeros(max(K.decode_workspace_bytes(tmps[0].cfg, max_len, args.split), 1),
+                     dtype=torch.uint8, device="cuda")
+    deq = lambda i: K.dequantize(caches[i % reps], 0, T16, out=tmps[i % reps])
+    dec = lambda i: K.decode_attn(tmps[i % reps], 0, q, max_len, out=out, workspace=ws,
+                                  split_tokens=args.split, query_bits=args.query_bits)
+    for i in range(reps + 3):
+        deq(i)
+        dec(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("dequantize_us", lambda i: deq(i)), ("bf16_decode_us", lambda i: dec(i)),
+                     ("dequantize_then_decode_us", lambda i: (deq(i), dec(i)))):
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
+    lens = [int(x) for x in caches[0].seq_lens.cpu().tolist()]
+    res["bf16_bytes_per_step"] = K.decode_traffic_bytes(tmps[0].cfg, lens)
+    log(f"[bench] dequantize-then-decode: {res}")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,6 +334,8 @@ def main():
     torch.cuda.synchronize()
     append_us = e0.elapsed_time(e1) / 20 * 1e3
 
+    ab = ab_path(args, wl, caches, q, out, max_len, K, torch) if args.ab else None
+
     value = traffic / (ms_step * 1e-3) / 1e9
     achieved = traffic / (split_ms * 1e-3) / 1e9
     sha = kernel_source_sha()
@@ -334,6 +373,8 @@ def main():
         "warm_us_per_step": round(warm_ms * 1e3, 2),
         "decode_append_us": round(append_us, 2),
     }
+    if ab is not None:
+        result["ab_dequantize_then_decode"] = ab
     if not args.no_cpu:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(wl, lens, args.cpu_seconds)

@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_dequant.hip"]
+OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -18,7 +19,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in VGPRs: no AGPR round trips when the softmax
@@ -29,22 +29,37 @@ FLAGS = [
 ]
 
 
+def _run(cmds, verbose):
+    """Runs the commands in parallel; raises with their messages on failure."""
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                      text=True))
+    failed, msgs = False, []
+    for p in procs:
+        text = p.communicate()[0].strip()
+        # the host pass does not know the device target feature; that is expected
+        msgs += [l for l in text.splitlines() if "packed-fp32-ops" not in l]
+        failed |= p.returncode != 0
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+
+
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compiles every source into libkvq.so (or `out`); returns its path.
-    defines: extra -D macros (e.g. KVQ_PREFETCH=1) for variant builds."""
+    """Compiles every source (in parallel) and links libkvq.so (or `out`);
+    returns its path.  defines: extra -D macros for variant builds."""
+    objdir = os.path.join(OBJDIR, os.path.basename(out))
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s + ".o") for s in SOURCES]
+    _run([[HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)],
+         verbose)
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
-           "-I", CSRC, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    text = (res.stdout + res.stderr).strip()
-    # the host pass does not know the device target feature; that is expected
-    lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
-    if verbose and lines:
-        print("\n".join(lines))
+    _run([[HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]], verbose)
     os.replace(tmp, out)
     return out
 

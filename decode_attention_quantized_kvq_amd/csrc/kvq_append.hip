@@ -333,6 +333,15 @@ __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   };
   auto slot = [&](int p) { return slot_index(a, b, h, p); };
   uint8_t* codes = w == 0 ? a.k_codes : a.v_codes;
+  if (k.code == CK_BF16) {  // unquantized (bits 16): the bf16 values themselves
+    for (int j = 0; j < g; ++j) {
+      float x0, x1;
+      ld(p0 + j, x0, x1);
+      const uint32_t v = (uint32_t)f32_to_bf16_bits(x0) | ((uint32_t)f32_to_bf16_bits(x1) << 16);
+      ((uint32_t*)(codes + slot(p0 + j) * (size_t)(2 * D)))[lane] = v;
+    }
+    return;
+  }
   uint8_t* meta = w == 0 ? a.k_meta : a.v_meta;
   const float* chan = (w == 0 && k.channel) ? a.k_chan + head * D : nullptr;
   const float* sup = w == 0 ? a.k_super : a.v_super;

@@ -711,11 +711,12 @@ struct WinRaw {
   u32x4 v[8];      // 8 tokens, features [8c, 8c + 8)
 };
 
-// Ring slot of live bf16 token i (0 <= i < nw): (r0 + i) mod ring.
+// Slot of bf16 token i (0 <= i < n, clamped) of a range: (r0 + i) mod ring in
+// a ring, or r0 + i in a linear cache (ring = 0).
 __device__ inline int ring_slot(int i, int nw, int r0, int ring) {
   i = i < nw ? i : nw - 1;
   const int s = r0 + i;
-  return s < ring ? s : s - ring;
+  return ring == 0 || s < ring ? s : s - ring;
 }
 
 __device__ inline void load_win_tile(WinRaw& t, const uint16_t* kw, const uint16_t* vw, int t0,
@@ -977,8 +978,12 @@ __device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
 // ---------------------------------------------------------------------------
 // Window split: the newest tokens, kept as bf16
 // ---------------------------------------------------------------------------
-template <int G, bool QB>
-__device__ void window_split(const DecodeArgs& a, int b, int h, int nq, int nw, Shared<G>& sh) {
+// Attends the n bf16 tokens at slots ring_slot(i, n, r0, ring) of kw / vw
+// with the G query heads of KV head h, and writes the partial row `row`.
+// PF: keep two tiles in flight per wave (long ranges of a bf16 cache).
+template <int G, bool QB, bool PF>
+__device__ void bf16_tokens(const DecodeArgs& a, int b, int h, const uint16_t* kw,
+                            const uint16_t* vw, int r0, int ring, int nw, int row, Shared<G>& sh) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1040,18 +1045,45 @@ __device__ void window_split(const DecodeArgs& a, int b, int h, int nq, int nw, 
   }
   Softmax st;
   st.init(1.0f);
-  const size_t head = ((size_t)b * a.hkv + h) * a.ring * D;
-  // the nw live positions [nq, nq + nw) sit in ring slots (nq + i) mod ring
-  const int r0 = nq % a.ring;
   const int per = (nw + WAVES * TILE - 1) / (WAVES * TILE) * TILE;
   const int w0 = wave * per, w1 = min(w0 + per, nw);
-  for (int t0 = w0; t0 < w1; t0 += TILE) {
-    WinRaw t;
-    load_win_tile(t, a.k_win + head, a.v_win + head, t0, nw, r0, a.ring, c, g);
-    compute_win_tile<G>(t, t0, w1, qf, qs, g, limb, st);
+  if constexpr (PF) {
+    // tile pairs, loads of tile i+2 issued after tile i's compute; the last
+    // tile index is reused past the end, so every load stays in range (an L2
+    // hit) and the loop has no exit in its middle
+    const int ntile = w1 > w0 ? (w1 - w0 + TILE - 1) / TILE : 0;
+    if (ntile > 0) {
+      auto tl = [&](int i) { return w0 + min(i, ntile - 1) * TILE; };
+      WinRaw t0r, t1r;
+      load_win_tile(t0r, kw, vw, tl(0), nw, r0, ring, c, g);
+      load_win_tile(t1r, kw, vw, tl(1), nw, r0, ring, c, g);
+      int i = 0;
+      for (; i + 1 < ntile; i += 2) {
+        compute_win_tile<G>(t0r, tl(i), w1, qf, qs, g, limb, st);
+        load_win_tile(t0r, kw, vw, tl(i + 2), nw, r0, ring, c, g);
+        compute_win_tile<G>(t1r, tl(i + 1), w1, qf, qs, g, limb, st);
+        load_win_tile(t1r, kw, vw, tl(i + 3), nw, r0, ring, c, g);
+      }
+      if (i < ntile) compute_win_tile<G>(t0r, tl(i), w1, qf, qs, g, limb, st);
+    }
+  } else {
+    for (int t0 = w0; t0 < w1; t0 += TILE) {
+      WinRaw t;
+      load_win_tile(t, kw, vw, t0, nw, r0, ring, c, g);
+      compute_win_tile<G>(t, t0, w1, qf, qs, g, limb, st);
+    }
   }
   wave_finish<G>(st, 1.0f, c, g, wave, sh);
-  block_merge<G>(a, sh, b, h, a.n_split);
+  block_merge<G>(a, sh, b, h, row);
+}
+
+// The bf16 tokens of a quantized cache: the window and an open token group,
+// positions [nq, nq + nw) in ring slots (nq + i) mod ring.
+template <int G, bool QB>
+__device__ void window_split(const DecodeArgs& a, int b, int h, int nq, int nw, Shared<G>& sh) {
+  const size_t head = ((size_t)b * a.hkv + h) * a.ring * D;
+  bf16_tokens<G, QB, false>(a, b, h, a.k_win + head, a.v_win + head, nq % a.ring, a.ring, nw,
+                            a.n_split, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1556,6 +1588,54 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   arrive_and_combine<G>(a, b, h, pl, &last_flag);
 }
 
+// Decode over an unquantized (bf16) contiguous cache, e.g. the output of
+// kvq_dequantize: the same work items (chunks, largest first) and the same
+// combine as decode_split, the tokens attended by bf16_tokens.
+template <int G, bool QB>
+__global__ void __launch_bounds__(256) decode_bf16(DecodeArgs a) {
+  __shared__ Shared<G> sh;
+  __shared__ int last_flag;
+  __shared__ int hist[WAVES][NSIZE];
+  const bool zduty = blockIdx.x < (unsigned)(a.batch * a.hkv);
+  const int zlen = zduty ? a.seq_lens[blockIdx.x / a.hkv] : 1;
+  const Item it = map_item(a, blockIdx.x, hist[threadIdx.x >> 6]);
+  if (zduty && zlen <= 0) {
+    const int zb = blockIdx.x / a.hkv, zh = blockIdx.x % a.hkv;
+    for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64)
+      a.out[((size_t)zb * a.hq + (size_t)zh * G) * D + idx] = 0.0f;
+  }
+  if (it.kind != 0) return;  // a bf16 cache has no window items
+  const int b = it.b, h = it.h, split = it.split;
+  const int tok0 = split * a.split_tokens;
+  const int tok1 = min(tok0 + a.split_tokens, it.si.nq);
+  const size_t head = ((size_t)b * a.hkv + h) * a.max_tokens * D;
+  bf16_tokens<G, QB, true>(a, b, h, (const uint16_t*)a.k_codes + head,
+                           (const uint16_t*)a.v_codes + head, tok0, 0, tok1 - tok0, split, sh);
+  arrive_and_combine<G>(a, b, h, plan_of(a, it.si), &last_flag);
+}
+
+template <int G>
+void launch_bf16(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  const auto k = a.in_bf16 ? decode_bf16<G, true> : decode_bf16<G, false>;
+  if (a.ev_begin)
+    hipExtLaunchKernelGGL(k, grid, dim3(256), 0, s, (hipEvent_t)a.ev_begin, (hipEvent_t)a.ev_end, 0,
+                          a);
+  else
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
+}
+
+hipError_t launch_bf16_g(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.nsp * a.hkv * a.batch);
+  switch (a.group) {
+    case 1: launch_bf16<1>(a, grid, s); break;
+    case 2: launch_bf16<2>(a, grid, s); break;
+    case 4: launch_bf16<4>(a, grid, s); break;
+    case 8: launch_bf16<8>(a, grid, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Launches one decode_split variant.  With events, hipExtLaunchKernel stamps
 // them with the start and end of the dispatch itself, so their difference
 // is the kernel's own duration.
@@ -1625,6 +1705,8 @@ kvq_status launch_decode(const DecodeArgs& a, void* stream) {
     e = launch_g<CK_I2, MK_U8, false, CK_I2, MK_U8>(a, s);
   else if (k.code == CK_U2 && k.meta == MK_F16Z && v.code == CK_U2 && v.meta == MK_F16Z)
     e = launch_g<CK_U2, MK_F16Z, false, CK_U2, MK_F16Z>(a, s);
+  else if (k.code == CK_BF16 && v.code == CK_BF16)
+    e = launch_bf16_g(a, s);
   else
     return KVQ_ERR_UNSUPPORTED;
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;

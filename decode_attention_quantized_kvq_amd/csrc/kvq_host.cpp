@@ -58,7 +58,7 @@ kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
     k.code = CK_BF16;
     k.meta = MK_NONE;
     if (out) *out = k;
-    return KVQ_ERR_UNSUPPORTED;  // accounted for, not run by the kernels
+    return KVQ_OK;  // unquantized: the kernels run it as a key/value pair, contiguous
   }
   if (f.bits != 8 && f.bits != 4 && f.bits != 2) return KVQ_ERR_INVALID_ARG;
   if (f.scale_fmt == KVQ_SCALE_U8_SUPER && f.zero_point) return KVQ_ERR_INVALID_ARG;
@@ -131,7 +131,8 @@ static kvq_status check_config(const kvq_config* c, bool kernels) {
       (kk.code == CK_U8 && kk.meta == MK_F16Z && vk.code == CK_U8 && vk.meta == MK_F16Z) ||
       (kk.code == CK_I2 && kk.meta == MK_F32 && vk.code == CK_I2 && vk.meta == MK_F32) ||
       (kk.code == CK_I2 && kk.meta == MK_U8 && vk.code == CK_I2 && vk.meta == MK_U8) ||
-      (kk.code == CK_U2 && kk.meta == MK_F16Z && vk.code == CK_U2 && vk.meta == MK_F16Z);
+      (kk.code == CK_U2 && kk.meta == MK_F16Z && vk.code == CK_U2 && vk.meta == MK_F16Z) ||
+      (kk.code == CK_BF16 && vk.code == CK_BF16 && !c->block_tokens && !c->window && tg == 1);
   return ok ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
 }
 
@@ -301,6 +302,48 @@ static void set_groups(const kvq_config* c, int* g, int* gshift, int* ring) {
   *g = token_group(c);
   *gshift = *g == 16 ? 4 : *g == 8 ? 3 : *g == 4 ? 2 : *g == 2 ? 1 : 0;
   *ring = ring_slots(c);
+}
+
+kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int layer, void* k_out,
+                          void* v_out, int out_tokens, void* stream) {
+  const kvq_status st = check_config(cfg, true);
+  if (st != KVQ_OK) return st;
+  if (!cache || !k_out || !v_out || layer < 0 || layer >= cfg->num_layers || out_tokens < 0)
+    return KVQ_ERR_INVALID_ARG;
+  DequantArgs a{};
+  classify(cfg->key, true, &a.kk);
+  classify(cfg->value, false, &a.vk);
+  if (a.kk.code == CK_BF16 || a.vk.code == CK_BF16) return KVQ_ERR_UNSUPPORTED;
+  const LayerSizes s = layer_sizes(cfg);
+  uint8_t *kc, *vc, *km, *vm;
+  uint16_t *kw, *vw;
+  float *kch, *vsu, *ksu;
+  if (!resolve_layer(cfg, cache, layer, s, &kc, &vc, &km, &vm, &kw, &vw, &kch, &vsu, &ksu))
+    return KVQ_ERR_INVALID_ARG;
+  a.k_codes = kc;
+  a.v_codes = vc;
+  a.k_meta = km;
+  a.v_meta = vm;
+  a.k_win = kw;
+  a.v_win = vw;
+  a.k_chan = kch;
+  a.v_super = vsu;
+  a.k_super = ksu;
+  a.seq_lens = cache->seq_lens;
+  a.block_table = cache->block_table;
+  a.k_out = (uint16_t*)k_out;
+  a.v_out = (uint16_t*)v_out;
+  a.out_tokens = out_tokens;
+  a.batch = cfg->batch;
+  a.hkv = cfg->num_kv_heads;
+  a.max_tokens = cfg->max_tokens;
+  a.window = cfg->window;
+  a.paged = cfg->block_tokens ? 1 : 0;
+  a.num_blocks = cfg->num_blocks;
+  a.bt_stride = cfg->max_blocks_per_seq;
+  int g;
+  set_groups(cfg, &g, &a.tgshift, &a.ring);
+  return launch_dequant(a, stream);
 }
 
 static bool split_ok(int split) { return split >= 0 && split % 128 == 0 && split <= (1 << 20); }

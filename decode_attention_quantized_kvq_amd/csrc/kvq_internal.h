@@ -99,7 +99,29 @@ struct DecodeArgs {
   void* ev_end;      // hipEvent_t recorded after it, or null
 };
 
+// Everything a dequantize launch needs, resolved to one layer.
+struct DequantArgs {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint8_t* k_meta;
+  const uint8_t* v_meta;
+  const uint16_t* k_win;
+  const uint16_t* v_win;
+  const float* k_chan;
+  const float* v_super;
+  const float* k_super;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  uint16_t* k_out;  // [B][H_kv][out_tokens][D] bf16
+  uint16_t* v_out;
+  int out_tokens;
+  int batch, hkv, max_tokens, window, paged, num_blocks, bt_stride;
+  int tgshift, ring;
+  TensorKind kk, vk;
+};
+
 kvq_status launch_append(const AppendArgs& a, void* stream);
+kvq_status launch_dequant(const DequantArgs& a, void* stream);
 kvq_status launch_decode(const DecodeArgs& a, void* stream);
 
 }  // namespace kvq

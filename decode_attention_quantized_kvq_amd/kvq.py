@@ -32,7 +32,7 @@ TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 EXPORTS = (
     "kvq_status_string", "kvq_validate", "kvq_get_buffer_sizes", "kvq_cache_bytes",
     "kvq_decode_traffic_bytes", "kvq_decode_workspace_bytes", "kvq_quantize_append",
-    "kvq_decode_attn", "kvq_decode_attn_ex",
+    "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_dequantize",
 )
 
 
@@ -112,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn_ex.restype = I
         L.kvq_decode_attn_ex.argtypes = [P(Config), P(CacheDesc), I, VP, VP, VP, S, I,
                                          P(DecodeOpts), VP]
+        L.kvq_dequantize.restype = I
+        L.kvq_dequantize.argtypes = [P(Config), P(CacheDesc), I, VP, VP, I, VP]
         _lib = L
     return _lib
 
@@ -285,4 +287,33 @@ def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
                                     workspace.numel() * workspace.element_size(),
                                     int(max_seq_len), ctypes.byref(opts), _stream(stream)),
            "kvq_decode_attn")
+    return out
+
+
+def bf16_cache_like(cache: KvqCache, out_tokens: int) -> "KvqCache":
+    """An empty unquantized (bits 16) cache shaped like `cache`, with room for
+    out_tokens positions (a multiple of 16)."""
+    cfg = cache.cfg
+    cfg16 = make_config(batch=cfg.batch, num_q_heads=cfg.num_q_heads,
+                        num_kv_heads=cfg.num_kv_heads, head_dim=cfg.head_dim,
+                        max_tokens=int(out_tokens), key=dict(bits=16), value=dict(bits=16),
+                        in_dtype="bf16" if cfg.in_dtype == DTYPE["bf16"] else "f32")
+    return KvqCache(cfg16, cache.device)
+
+
+def dequantize(cache: KvqCache, layer: int, out_tokens: int, out: Optional["KvqCache"] = None,
+               stream=None) -> "KvqCache":
+    """kvq_dequantize: the layer's keys and values as an unquantized bf16
+    cache (key/value bits 16, max_tokens = out_tokens, contiguous, no
+    window), with the same sequence lengths; into `out` (from
+    bf16_cache_like) when given.  out_tokens: a multiple of 16 at least the
+    longest sequence."""
+    cfg = cache.cfg
+    if out is None:
+        out = bf16_cache_like(cache, out_tokens)
+    out.seq_lens.copy_(cache.seq_lens)
+    desc = cache.desc()
+    _check(lib().kvq_dequantize(ctypes.byref(cfg), ctypes.byref(desc), int(layer),
+                                _ptr(out.buffers["k_codes"]), _ptr(out.buffers["v_codes"]),
+                                int(out_tokens), _stream(stream)), "kvq_dequantize")
     return out

@@ -71,7 +71,8 @@
  *  ring   [L][B][H_kv][R][D] bf16 with R = window (+ g if g > 1); position
  *    p sits in slot p % R
  *  k_chan_scale [L][B][H_kv][D] fp32;  k_super, v_super [L][B][H_kv] fp32
- *  code bytes: int8 codes as two's complement bytes (unsigned bytes with a
+ *  code bytes: bits 16 stores the bf16 values themselves (2 bytes each);
+ *    int8 codes as two's complement bytes (unsigned bytes with a
  *    zero point); int4 codes packed two per byte, element 2j in the low nibble
  *    and 2j+1 in the high nibble (two's complement nibbles, or unsigned with a
  *    zero point); int2 codes packed four per byte, element 4j+i in bits
@@ -209,7 +210,8 @@ const char* kvq_status_string(kvq_status s);
  *   int4 f32; int4 f32                      int8 per-channel; int4 u8 super
  *   uint4 f16 scale + zero; the same        uint8 f16 scale + zero; the same
  *   int2 f32; int2 f32                      int2 u8 super; int2 u8 super
- *   uint2 f16 scale + zero; the same
+ *   uint2 f16 scale + zero; the same        bf16 (bits 16); bf16, contiguous,
+ *                                           no window, no token groups
  * An 8-bit scale code (u8 super) or per-channel keys exclude a window and
  * token groups. */
 kvq_status kvq_validate(const kvq_config* cfg);
@@ -243,6 +245,23 @@ size_t kvq_decode_traffic_bytes(const kvq_config* cfg, const int32_t* host_seq_l
 kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, int layer,
                                const void* k_new, const void* v_new, int n_new,
                                const int32_t* new_lens, void* stream);
+
+/* Dequantizes one layer into bf16 copies of its keys and values: the
+ * dequantize-into-temporary-storage path of P1, "Cache growth changes the
+ * serving trade" (its cost is what P2, "Lower payload does not imply
+ * proportional latency reduction", weighs against the fused path).
+ *  k_out, v_out: device [batch][num_kv_heads][out_tokens][head_dim] bf16,
+ *    caller-owned.  Position p < min(seq_lens[b], out_tokens) of each
+ *    sequence and head gets the exact reconstruction (code x scale, or
+ *    scale x (code - zero point), code x u x S, code x channel scale) rounded
+ *    once to bf16, or the stored bf16 value of a window / open-group token;
+ *    other positions are left untouched.  The two buffers are then the codes
+ *    of an unquantized cache (key and value bits 16, max_tokens = out_tokens,
+ *    no window, contiguous) that kvq_decode_attn reads.
+ *  A format with bits 16 has nothing to dequantize: KVQ_ERR_UNSUPPORTED.
+ *  Launches one kernel on stream. */
+kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                          void* k_out, void* v_out, int out_tokens, void* stream);
 
 /* Tuning and measurement knobs of kvq_decode_attn; zero / NULL fields take
  * the library's choice. */

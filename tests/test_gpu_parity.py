@@ -202,6 +202,64 @@ def test_integer_query_rejected_with_channel_keys():
         H.run_decode(bt, H.queries(wl), query_bits=8)
 
 
+DEQ_CASES = [
+    # (workload, overrides, lens, decode steps)
+    (2, dict(batch=2, tokens=512), [500, 77], 2),
+    (3, dict(batch=2, tokens=512), [500, 33], 2),
+    (4, dict(batch=3, tokens=512), [500, 131, 100], 3),                 # paged + window
+    (5, dict(batch=2, tokens=512), [500, 65], 0),                       # channel K, u8 V
+    (6, dict(batch=2, tokens=512), [500, 17], 2),                       # int2 u8 super
+    (7, dict(batch=2, tokens=512), [500, 29], 5),                       # uint2 groups of 16
+    (2, dict(batch=2, tokens=512, key=dict(bits=8), value=dict(bits=4), window=32, group=4),
+     [500, 45], 6),
+]
+
+
+@pytest.mark.parametrize("wid,over,lens,steps", DEQ_CASES,
+                         ids=[f"w{c[0]}-{i}" for i, c in enumerate(DEQ_CASES)])
+def test_dequantize_then_decode(wid, over, lens, steps):
+    """The dequantize-into-temporary-storage path: kvq_dequantize writes the
+    exact reconstruction rounded once to bf16 (bit for bit), and decode over
+    that bf16 copy matches the oracle's attention over the same values."""
+    H.log(f"case: dequantize then decode, workload {wid} {over}")
+    wl = synth.workload(wid, **over)
+    bt = H.build(wl, lens, decode_steps=steps)
+    T16 = -(-max(lens) // 16) * 16
+    c16 = K.dequantize(bt.cache, 0, T16)
+    torch.cuda.synchronize()
+    kd = H.host(c16.buffers["k_codes"]).view(np.uint16).reshape(wl["batch"], wl["hkv"], T16, wl["d"])
+    vd = H.host(c16.buffers["v_codes"]).view(np.uint16).reshape(wl["batch"], wl["hkv"], T16, wl["d"])
+    q = H.queries(wl)
+    want = []
+    for b in range(wl["batch"]):
+        kb, vb = H.O.dequantized_bf16(bt.oracle, b)
+        n = lens[b]
+        for got, ref, t in ((kd[b, :, :n], kb, "k"), (vd[b, :, :n], vb, "v")):
+            ref16 = (ref.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            assert np.array_equal(got, ref16), f"{t} dequantized differs b={b}"
+        want.append(H.O.attend(q[b], kb, vb))
+    for split in (0, 128):
+        got = K.decode_attn(c16, 0, H.to_device(q, wl["in_dtype"]), max(lens), split_tokens=split)
+        torch.cuda.synchronize()
+        H.check_close(got.cpu().numpy().astype(np.float64), np.stack(want),
+                      f"bf16 decode of {wl['name']} split {split}")
+
+
+def test_unquantized_cache():
+    """An unquantized (bits 16) cache written by kvq_quantize_append and read
+    by the decode kernel: bf16 values stored, attention within the bar."""
+    H.log("case: unquantized cache")
+    wl = synth.workload(2, batch=3, hq=16, hkv=4, tokens=1024, key=dict(bits=16),
+                        value=dict(bits=16))
+    bt = H.build(wl, [1000, 300, 0], decode_steps=3, chunks=2)
+    full_check(bt, steps=(0, 1), records=False)
+    full_check(bt, steps=(0,), split_tokens=256, records=False)
+    kd = H.host(bt.cache.buffers["k_codes"]).view(np.uint16).reshape(3, 4, 1024, 128)
+    kb = bt.oracle.stored(0, "k").raw
+    ref16 = (kb.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(kd[0, :, :1000], ref16)
+
+
 def test_empty_and_zero_sequences():
     """A sequence with no tokens gives zeros; all-zero vectors quantize to
     codes 0 with scale 1 and attend like any other token."""

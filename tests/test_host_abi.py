@@ -127,7 +127,10 @@ def test_validation_errors():
         (dict(key=dict(bits=2, axis="channel"), value=dict(bits=2)), K.KVQ_ERR_UNSUPPORTED),
         (dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super"),
               window=16), K.KVQ_ERR_UNSUPPORTED),
-        (dict(key=dict(bits=16), value=dict(bits=16)), K.KVQ_ERR_UNSUPPORTED),
+        (dict(key=dict(bits=16), value=dict(bits=8)), K.KVQ_ERR_UNSUPPORTED),   # mixed pair
+        (dict(key=dict(bits=16), value=dict(bits=16), window=16), K.KVQ_ERR_UNSUPPORTED),
+        (dict(key=dict(bits=16), value=dict(bits=16), block_tokens=16, num_blocks=8,
+              max_blocks_per_seq=4), K.KVQ_ERR_UNSUPPORTED),
         (dict(value=dict(bits=8, axis="channel")), K.KVQ_ERR_UNSUPPORTED),
         (dict(window=20), K.KVQ_ERR_UNSUPPORTED),
         (dict(block_tokens=16, num_blocks=0, max_blocks_per_seq=4), K.KVQ_ERR_INVALID_ARG),
@@ -137,6 +140,7 @@ def test_validation_errors():
         cfg = K.make_config(**{**base, **over})
         assert K.validate(cfg) == want, over
     good = [
+        dict(key=dict(bits=16), value=dict(bits=16)),   # unquantized, contiguous
         dict(key=dict(bits=2), value=dict(bits=2)),
         dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super")),
         dict(key=dict(bits=2, zero_point=True, scale="f16"),
