@@ -43,7 +43,16 @@ Readings where the pages leave a step open (each restated where it is used):
       shows the scale fold.
   R8  grouped-query heads: query head h reads KV head h // G.
   R9  per-channel key scales come from the absmax over the first append of a
-      sequence (its prefill) and are then frozen; later tokens clamp.
+      sequence (its prefill; all of its tokens, also those that stay in the
+      window) and are then frozen; later tokens clamp.  The same holds for
+      super-scales (R10).
+  R22 a per-channel key scale that tracks a running estimate (axis
+      "channel_grow", P3 "Per-token scales and where they can live": the
+      estimate must be updated as the sequence grows): before tokens are
+      quantized, a channel whose largest |k| among them exceeds qmax * s gets
+      s' = RN32(that max / qmax), and its stored codes become
+      clamp(rint(fl64(c s / s'))) (re-quantized on growth); the recent
+      window holds keys in bf16 until they leave it.
   R10 super-scaled values: per token sigma = fl64(amax/qmax); per head
       S = RN32(max sigma / 255) over the prefill, frozen afterwards;
       u = clamp(rint(fl64(sigma / S)), 1, 255) (0 for an all-zero vector);
@@ -105,9 +114,11 @@ class TensorFormat:
     bits:       16 = unquantized (bf16 values kept as is), 8, 4 or 2 (2-bit
                 symmetric codes are -1, 0, 1; with a zero point 0..3).
     axis:       "token" (one scale per token per head, P3 "Per-token scales and
-                where they can live") or "channel" (one scale per feature per
+                where they can live"), "channel" (one scale per feature per
                 head, keys only, moved onto the query per P3 "The axis choice is
-                a kernel decision").
+                a kernel decision") or "channel_grow" (per channel, the scale
+                grows with the running absmax and the stored codes are
+                re-quantized, reading R22).
     zero_point: integer zero point (unsigned codes) when True.
     scale:      "f32", "f16" (scale and zero point stored in that type) or
                 "u8_super" (8-bit code times a per-head fp32 super-scale).
@@ -407,10 +418,9 @@ class OracleCache:
 
     def __init__(self, batch: int, hkv: int, d: int, key: TensorFormat,
                  value: TensorFormat, window: int = 0, group: int = 1):
-        if (window or group > 1) and (key.axis == "channel" or key.scale == "u8_super"
-                                      or value.scale == "u8_super"):
-            raise ValueError("a recent window and token groups are modelled for "
-                             "per-token formats only")
+        if group > 1 and (key.axis != "token" or key.scale == "u8_super"
+                          or value.scale == "u8_super"):
+            raise ValueError("token groups are modelled for per-token formats only")
         if group < 1:
             raise ValueError("group size must be at least 1")
         self.batch, self.hkv, self.d = batch, hkv, d
@@ -446,13 +456,9 @@ class OracleCache:
             side.s = s if side.s is None else np.concatenate([side.s, s], axis=1)
             side.codes = np.concatenate([side.codes, c.reshape(x.shape)], axis=1)
             return
-        if fmt.axis == "channel":
-            if first:
-                side.chan = channel_scales(x, fmt.bits)
+        if fmt.axis != "token":
             c = quantize_with_channel_scales(x, side.chan, fmt.bits)
         elif fmt.scale == "u8_super":
-            if first:
-                side.S = super_scale(x, fmt.bits)
             c, u = quantize_superscaled(x, side.S, fmt.bits)
             side.u = u if side.u is None else np.concatenate([side.u, u], axis=1)
         elif fmt.zero_point:
@@ -473,15 +479,42 @@ class OracleCache:
         first = self.lens[b] == 0
         total = self.lens[b] + n
         for t, x in (("k", k_new), ("v", v_new)):
+            side, fmt = self.side[b][t], self.fmt[t]
+            if first and n and fmt.bits != 16:
+                # readings R9, R10: side data from every token of the first append
+                if fmt.axis != "token":
+                    side.chan = channel_scales(x, fmt.bits)
+                elif fmt.scale == "u8_super":
+                    side.S = super_scale(x, fmt.bits)
             if self.window or self.group > 1:
                 pool = np.concatenate([self.win[b][t], x], axis=1)
                 keep = total - quantized_count(total, self.window, self.group)
                 leave = pool.shape[1] - keep
-                self._quantize_into(self.side[b][t], self.fmt[t], pool[:, :leave], first)
-                self.win[b][t] = round_bf16(pool[:, leave:])
+                q, self.win[b][t] = pool[:, :leave], round_bf16(pool[:, leave:])
             else:
-                self._quantize_into(self.side[b][t], self.fmt[t], x, first)
+                q = x
+            if fmt.axis == "channel_grow" and not first and q.shape[1]:
+                self._grow_channels(side, fmt, q)
+            self._quantize_into(side, fmt, q, first)
         self.lens[b] = total
+
+    @staticmethod
+    def _grow_channels(side: _Side, fmt: TensorFormat, x: np.ndarray):
+        """Reading R22: channels whose new absmax exceeds qmax * s get the
+        scale of that absmax, and their stored codes are re-quantized."""
+        qmax = qmax_symmetric(fmt.bits)
+        amax = np.max(np.abs(x), axis=1)                          # [Hkv, D]
+        old = side.chan.astype(np.float64)
+        grown = amax > qmax * old                                 # exact in fp64
+        if not grown.any():
+            return
+        new = np.where(grown, round_to_storage(np.where(grown, amax, 1.0) / qmax, "f32"),
+                       side.chan).astype(np.float32)
+        c = np.asarray(side.codes, np.float64)
+        requant = np.clip(rne_quotient(c * old[:, None, :], new.astype(np.float64)[:, None, :]),
+                          -qmax, qmax)
+        side.codes = np.where(grown[:, None, :], requant, c).astype(np.int32)
+        side.chan = new
 
     # -- read side ----------------------------------------------------------
     def _dequant(self, side: _Side, fmt: TensorFormat) -> np.ndarray:
@@ -489,7 +522,7 @@ class OracleCache:
             return side.raw.copy()
         if side.codes.shape[1] == 0:
             return np.zeros((self.hkv, 0, self.d))
-        if fmt.axis == "channel":
+        if fmt.axis != "token":
             return dequant_channel(side.codes, side.chan)
         if fmt.scale == "u8_super":
             return dequant_superscaled(side.codes, side.u, side.S)
@@ -535,7 +568,7 @@ class OracleCache:
 def meta_bytes_per_token(fmt: TensorFormat) -> int:
     """Per-token, per-head metadata bytes (P3 "Per-token scales and where they
     can live" prices a 4-byte scale, and a scale plus zero point)."""
-    if fmt.bits == 16 or fmt.axis == "channel":
+    if fmt.bits == 16 or fmt.axis != "token":
         return 0
     if fmt.scale == "u8_super":
         return 1
@@ -547,7 +580,7 @@ def side_bytes_per_head(fmt: TensorFormat, d: int) -> int:
     """Per-(sequence, head) metadata: channel scales or the super-scale."""
     if fmt.bits == 16:
         return 0
-    if fmt.axis == "channel":
+    if fmt.axis != "token":
         return 4 * d
     if fmt.scale == "u8_super":
         return 4

@@ -676,6 +676,78 @@ def pin_bf16_from_f64(O):
     assert np.count_nonzero(O.round_bf16_from_f64(near) != O.round_bf16(near)) > 0
 
 
+def pin_channel_scales_with_window(O):
+    """Per-channel key scales with a recent window (readings R9, R11): the
+    scales come from every token of the first append, also when that append
+    is shorter than the window, and tokens leaving the window later are
+    quantized with them (clamped)."""
+    rng = _rng(201)
+    d = 16
+    k = _bf16(rng.standard_normal((1, 40, d)) * np.array([1.0] * 12 + [10.0] * 4))
+    v = _bf16(rng.standard_normal((1, 40, d)))
+    fk, fv = O.TensorFormat(8, "channel"), O.TensorFormat(4, "token", False, "u8_super")
+    cache = O.OracleCache(1, 1, d, fk, fv, window=16)
+    cache.append(0, k[:, :10], v[:, :10])             # shorter than the window
+    st = cache.stored(0, "k")
+    assert st.codes.shape[1] == 0
+    for c in range(d):
+        assert Fraction(float(st.chan[0, c])) == rn32(max(abs(fr(x)) for x in k[0, :10, c]) / 127)
+    assert Fraction(float(cache.stored(0, "v").S[0])) == rn32(
+        max(max(abs(fr(x)) for x in v[0, t]) / 7 for t in range(10)) / 255)
+    for t in range(10, 40):
+        cache.append(0, k[:, t:t + 1], v[:, t:t + 1])
+    st = cache.stored(0, "k")
+    assert st.codes.shape[1] == 40 - 16
+    for t in range(24):
+        for c in range(d):
+            assert st.codes[0, t, c] == max(-127, min(127, round(fr(k[0, t, c]) / fr(st.chan[0, c]))))
+    kh, _ = cache.reconstructed(0)
+    assert np.array_equal(kh[:, 24:], k[:, 24:40])
+
+
+def pin_channel_growth(O):
+    """Reading R22: a channel whose new keys exceed qmax * s gets
+    s' = RN32(max / 127); its stored codes become clamp(round(c s / s'))
+    exactly; other channels keep theirs; the new tokens are quantized with
+    the grown scales and stay within s'/2."""
+    rng = _rng(203)
+    d = 8
+    k1 = _bf16(rng.standard_normal((2, 20, d)))
+    k2 = _bf16(rng.standard_normal((2, 5, d)) * np.array([1, 1, 1, 1, 5, 5, 0.1, 9.0]))
+    v = _bf16(rng.standard_normal((2, 25, d)))
+    f = O.TensorFormat(8, "channel_grow")
+    cache = O.OracleCache(1, 2, d, f, O.TensorFormat(8), window=0)
+    cache.append(0, k1, v[:, :20])
+    old_s = cache.stored(0, "k").chan.copy()
+    old_c = cache.stored(0, "k").codes.copy()
+    cache.append(0, k2, v[:, 20:])
+    st = cache.stored(0, "k")
+    for h in range(2):
+        for c in range(d):
+            m = max(abs(fr(x)) for x in k2[h, :, c])
+            s0 = Fraction(float(old_s[h, c]))
+            if m > 127 * s0:
+                s1 = rn32(m / 127)
+                assert Fraction(float(st.chan[h, c])) == s1, (h, c)
+                for t in range(20):
+                    want = max(-127, min(127, round(int(old_c[h, t, c]) * s0 / s1)))
+                    assert st.codes[h, t, c] == want, (h, c, t)
+            else:
+                s1 = s0
+                assert st.chan[h, c] == old_s[h, c]
+                assert np.array_equal(st.codes[h, :20, c], old_c[h, :, c])
+            for t in range(5):
+                x = fr(k2[h, t, c])
+                code = int(st.codes[h, 20 + t, c])
+                assert code == max(-127, min(127, round(x / s1)))
+                assert abs(x - code * s1) <= s1 / 2
+    assert (st.chan != old_s).any() and (st.chan == old_s).any()   # both cases exercised
+    frozen = O.OracleCache(1, 2, d, O.TensorFormat(8, "channel"), O.TensorFormat(8))
+    frozen.append(0, k1, v[:, :20])
+    frozen.append(0, k2, v[:, 20:])
+    assert np.array_equal(frozen.stored(0, "k").chan, old_s)       # "channel" stays frozen
+
+
 def pin_window_stores_bf16(O):
     """Unquantized tokens (bits 16, or the recent window) are stored in bf16:
     fp32 inputs come back rounded to nearest-even bf16 (torch's conversion)."""

@@ -69,6 +69,23 @@ def m_int_query_fp64_division(O):
     O.quantize_query_int8 = qq
 
 
+def m_growth_requant_truncates(O):
+    orig = O.OracleCache._grow_channels
+
+    def grow(side, fmt, x):
+        saved = O.rne_quotient
+        O.rne_quotient = lambda a, b: np.trunc(np.asarray(a, np.float64) / np.asarray(b, np.float64))
+        try:
+            orig(side, fmt, x)
+        finally:
+            O.rne_quotient = saved
+    O.OracleCache._grow_channels = staticmethod(grow)
+
+
+def m_growth_never(O):
+    O.OracleCache._grow_channels = staticmethod(lambda side, fmt, x: None)
+
+
 def m_no_inv_sqrt_d(O):
     O.scores = lambda q, k: np.asarray(k, np.float64) @ np.asarray(q, np.float64)
 
