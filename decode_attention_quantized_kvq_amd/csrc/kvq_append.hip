@@ -15,7 +15,8 @@
 // Launch order on the caller's stream:
 //   1. append_stats: per-channel key scales and key / value super-scales of
 //      sequences whose append starts at position 0 (their prefill), then
-//      frozen.
+//      frozen; or, for growing channel scales, their update and the
+//      re-quantization of the stored codes of the channels that grew.
 //   2. append_quantize: one workgroup per (token, head, sequence); wave 0
 //      quantizes the key, wave 1 the value.  With a recent window it takes
 //      the tokens leaving the window (from the ring or from the input).
@@ -256,10 +257,63 @@ __device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, i
   }
 }
 
+// Quantized positions of an n-token sequence: whole token groups older than
+// the window.
+__device__ inline int quantized_count(const AppendArgs& a, int n) {
+  const int m = n - a.window > 0 ? n - a.window : 0;
+  return (m >> a.tgshift) << a.tgshift;
+}
+
+// A later append of a sequence whose per-channel key scales follow the
+// running absmax: a channel whose keys quantized by this append exceed
+// qmax * s gets s' = RN32(max / qmax), and its stored codes are re-quantized,
+// c' = clamp(rint(fl64(c s / s'))); then the new scales are stored.
+__device__ void grow_channels(const AppendArgs& a, int b, int h, const SeqRange& r) {
+  const int qlo = quantized_count(a, r.start);
+  int qhi = quantized_count(a, r.len);
+  qhi = qhi < q_capacity(a) ? qhi : q_capacity(a);
+  if (qhi <= qlo) return;
+  __shared__ float snew[D];
+  const int tid = threadIdx.x;
+  const size_t head = (size_t)b * a.hkv + h;
+  const int qmax = qmax_sym(code_bits(a.kk.code));
+  float* chan = a.k_chan + head * D;
+  bool grow = false;
+  if (tid < D) {
+    float amax = 0.0f;
+    for (int p = qlo; p < qhi; ++p) {
+      const float x = p >= r.start
+                          ? load_in(a.k_new, (head * a.n_new + (p - r.start)) * D + tid, a.in_bf16)
+                          : bf16_bits_to_f32(a.k_win[(head * a.ring + (p % a.ring)) * D + tid]);
+      amax = fmaxf(amax, fabsf(x));
+    }
+    const float s = chan[tid];
+    grow = (double)amax > (double)qmax * (double)s;
+    snew[tid] = grow ? store_f32((double)amax / qmax) : s;
+  }
+  if (!__syncthreads_or(grow)) return;
+  // two code rows per pass, one byte per thread: coalesced over the channels
+  const int d = tid & (D - 1);
+  const float s0 = chan[d], s1 = snew[d];
+  if (s1 != s0) {
+    for (int t = tid >> 7; t < qlo; t += 2) {
+      uint8_t* cp = a.k_codes + slot_index(a, b, h, t) * (size_t)D + d;
+      const int c = (int)(int8_t)*cp;
+      *cp = (uint8_t)clampi((int)rint((double)c * (double)s0 / (double)s1), -qmax, qmax);
+    }
+  }
+  __syncthreads();
+  if (tid < D) chan[tid] = snew[tid];
+}
+
 __global__ void __launch_bounds__(256) append_stats(AppendArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const SeqRange r = seq_range(a, b);
-  if (r.start != 0 || r.newb == 0) return;
+  if (r.newb == 0) return;
+  if (r.start != 0) {  // a later append: only growing channel scales change
+    if (a.kk.grow) grow_channels(a, b, h, r);
+    return;
+  }
   const size_t in_base = ((size_t)b * a.hkv + h) * a.n_new;
   const int tid = threadIdx.x;
   if (a.kk.channel && tid < D) {
@@ -296,13 +350,6 @@ __global__ void __launch_bounds__(256) append_stats(AppendArgs a) {
     }
     __syncthreads();
   }
-}
-
-// Quantized positions of an n-token sequence: whole token groups older than
-// the window.
-__device__ inline int quantized_count(const AppendArgs& a, int n) {
-  const int m = n - a.window > 0 ? n - a.window : 0;
-  return (m >> a.tgshift) << a.tgshift;
 }
 
 __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {

@@ -17,7 +17,7 @@ namespace kvq {
 int meta_bytes(const kvq_tensor_fmt& f) {
   // P3 "Per-token scales and where they can live": a 4-byte scale per token,
   // or a scale plus a zero point; an 8-bit scale code under a super-scale.
-  if (f.bits == 16 || f.axis == KVQ_AXIS_CHANNEL) return 0;
+  if (f.bits == 16 || f.axis != KVQ_AXIS_TOKEN) return 0;
   if (f.scale_fmt == KVQ_SCALE_U8_SUPER) return 1;
   const int w = f.scale_fmt == KVQ_SCALE_F32 ? 4 : 2;
   return f.zero_point ? 2 * w : w;
@@ -41,17 +41,18 @@ static size_t quantized_count(const kvq_config* c, size_t n) {
 
 static size_t side_bytes(const kvq_tensor_fmt& f, int d) {
   if (f.bits == 16) return 0;
-  if (f.axis == KVQ_AXIS_CHANNEL) return size_t(4) * d;
+  if (f.axis != KVQ_AXIS_TOKEN) return size_t(4) * d;
   if (f.scale_fmt == KVQ_SCALE_U8_SUPER) return 4;
   return 0;
 }
 
 kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
-  TensorKind k{CK_I8, MK_NONE, false};
+  TensorKind k{CK_I8, MK_NONE, false, false};
   if (f.scale_fmt != KVQ_SCALE_F32 && f.scale_fmt != KVQ_SCALE_F16 &&
       f.scale_fmt != KVQ_SCALE_U8_SUPER)
     return KVQ_ERR_INVALID_ARG;
-  if (f.axis != KVQ_AXIS_TOKEN && f.axis != KVQ_AXIS_CHANNEL) return KVQ_ERR_INVALID_ARG;
+  if (f.axis != KVQ_AXIS_TOKEN && f.axis != KVQ_AXIS_CHANNEL && f.axis != KVQ_AXIS_CHANNEL_GROW)
+    return KVQ_ERR_INVALID_ARG;
   if (f.zero_point != 0 && f.zero_point != 1) return KVQ_ERR_INVALID_ARG;
   if (f.bits == 16) {
     if (f.axis != KVQ_AXIS_TOKEN || f.zero_point) return KVQ_ERR_INVALID_ARG;
@@ -62,7 +63,7 @@ kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
   }
   if (f.bits != 8 && f.bits != 4 && f.bits != 2) return KVQ_ERR_INVALID_ARG;
   if (f.scale_fmt == KVQ_SCALE_U8_SUPER && f.zero_point) return KVQ_ERR_INVALID_ARG;
-  if (f.axis == KVQ_AXIS_CHANNEL && (f.zero_point || f.scale_fmt != KVQ_SCALE_F32))
+  if (f.axis != KVQ_AXIS_TOKEN && (f.zero_point || f.scale_fmt != KVQ_SCALE_F32))
     return KVQ_ERR_INVALID_ARG;
   if (f.bits == 8)
     k.code = f.zero_point ? CK_U8 : CK_I8;
@@ -70,9 +71,10 @@ kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
     k.code = f.zero_point ? CK_U4 : CK_I4;
   else
     k.code = f.zero_point ? CK_U2 : CK_I2;
-  if (f.axis == KVQ_AXIS_CHANNEL) {
+  if (f.axis != KVQ_AXIS_TOKEN) {
     if (f.bits == 2) return KVQ_ERR_UNSUPPORTED;
     k.channel = true;
+    k.grow = f.axis == KVQ_AXIS_CHANNEL_GROW;
     k.meta = MK_NONE;
     if (out) *out = k;
     return is_key ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
@@ -119,7 +121,7 @@ static kvq_status check_config(const kvq_config* c, bool kernels) {
   if (c->max_tokens % 16) return KVQ_ERR_UNSUPPORTED;
   if (c->block_tokens != 0 && c->block_tokens != 16) return KVQ_ERR_UNSUPPORTED;
   if (c->window % 16 || c->window > 256) return KVQ_ERR_UNSUPPORTED;
-  if ((c->window || token_group(c) > 1) && (kk.channel || kk.meta == MK_U8 || vk.meta == MK_U8))
+  if (token_group(c) > 1 && (kk.channel || kk.meta == MK_U8 || vk.meta == MK_U8))
     return KVQ_ERR_UNSUPPORTED;
   // The decode kernels are instantiated for these key/value pairs.
   const bool ok =
@@ -184,7 +186,7 @@ static LayerSizes layer_sizes(const kvq_config* c) {
   s.v_meta = slots / token_group(c) * meta_bytes(c->value);
   const size_t heads = (size_t)c->batch * c->num_kv_heads;
   s.k_win = s.v_win = heads * ring_slots(c) * c->head_dim * 2;
-  s.k_chan = (c->key.bits != 16 && c->key.axis == KVQ_AXIS_CHANNEL) ? heads * c->head_dim * 4 : 0;
+  s.k_chan = (c->key.bits != 16 && c->key.axis != KVQ_AXIS_TOKEN) ? heads * c->head_dim * 4 : 0;
   s.v_super = (c->value.bits != 16 && c->value.scale_fmt == KVQ_SCALE_U8_SUPER) ? heads * 4 : 0;
   s.k_super = (c->key.bits != 16 && c->key.axis == KVQ_AXIS_TOKEN &&
                c->key.scale_fmt == KVQ_SCALE_U8_SUPER) ? heads * 4 : 0;
@@ -404,7 +406,7 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   if (qbits != 0 && qbits != 8) return KVQ_ERR_INVALID_ARG;
   // the per-channel key scale is folded onto the query in fp32; an int8 query
   // of the folded product is not a path the kernels run
-  if (qbits == 8 && cfg->key.axis == KVQ_AXIS_CHANNEL) return KVQ_ERR_UNSUPPORTED;
+  if (qbits == 8 && cfg->key.axis != KVQ_AXIS_TOKEN) return KVQ_ERR_UNSUPPORTED;
   // a paged wave addresses at most 128 blocks: splits of at most 4 x 2048 tokens
   if (cfg->block_tokens && split > 8192) return KVQ_ERR_INVALID_ARG;
   const Plan p = make_plan(cfg, max_seq_len, split);

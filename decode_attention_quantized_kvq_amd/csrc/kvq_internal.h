@@ -33,6 +33,7 @@ struct TensorKind {
   CodeKind code;
   MetaKind meta;
   bool channel;   // per-channel scales (keys only)
+  bool grow;      // ... that follow the running absmax (stored codes re-quantized)
 };
 
 // Code bytes of one token row of one head (0 for unsupported widths).

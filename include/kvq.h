@@ -52,7 +52,8 @@
  *    a scale that rounds to 0 stores the type's smallest positive value, an
  *    fp16 scale above 65504 stores 65504;
  *  - per-channel key scales: RN32(absmax over the first append / qmax) per
- *    feature, frozen; later tokens clamp;
+ *    feature (every token of it, also those that stay in the window), frozen
+ *    (later tokens clamp) or growing (KVQ_AXIS_CHANNEL_GROW);
  *  - super-scaled keys or values: sigma_t = fl64(amax_t/qmax); per head
  *    S = RN32(max_t sigma_t / 255) over the first append, frozen;
  *    u_t = clamp(rint(fl64(sigma_t / S)), 1, 255) (0 for an all-zero vector);
@@ -118,7 +119,15 @@ typedef enum {
  * values share a scale"; P3, "Per-token scales and where they can live"). */
 typedef enum {
   KVQ_AXIS_TOKEN = 0,  /* one scale per token per head */
-  KVQ_AXIS_CHANNEL = 1 /* one scale per feature per head (keys only) */
+  KVQ_AXIS_CHANNEL = 1, /* one scale per feature per head (keys only), from
+                           a sequence's first append, then frozen */
+  KVQ_AXIS_CHANNEL_GROW = 2 /* per feature per head (keys only), following the
+                           running absmax: before tokens are quantized, a
+                           channel whose new keys exceed qmax s gets
+                           s' = RN32(max / qmax) and its stored codes become
+                           clamp(rint(fl64(c s / s'))) (P3, "Per-token scales
+                           and where they can live": the estimate has to be
+                           updated as the sequence grows) */
 } kvq_axis;
 
 /* Storage type of a per-token scale (and zero point). */
@@ -212,8 +221,7 @@ const char* kvq_status_string(kvq_status s);
  *   int2 f32; int2 f32                      int2 u8 super; int2 u8 super
  *   uint2 f16 scale + zero; the same        bf16 (bits 16); bf16, contiguous,
  *                                           no window, no token groups
- * An 8-bit scale code (u8 super) or per-channel keys exclude a window and
- * token groups. */
+ * An 8-bit scale code (u8 super) or per-channel keys exclude token groups. */
 kvq_status kvq_validate(const kvq_config* cfg);
 
 /* Fills *out with the byte size of each buffer of the layout above. */

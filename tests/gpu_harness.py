@@ -197,7 +197,7 @@ def device_records(bt: Built, t: str, b: int, h: int, n: int) -> dict:
     codes_buf = host(bt.cache.buffers[f"{t}_codes"]).reshape(-1, row)
     slots = token_slots(bt, b, h, n)
     out = {"codes": unpack_codes(codes_buf[slots], bits, not zp)}
-    if spec.get("axis") == "channel":
+    if spec.get("axis", "token") != "token":
         ch = host(bt.cache.buffers["k_chan_scale"]).view(np.float32).reshape(-1, D)
         out["chan"] = ch[b * bt.cfg.num_kv_heads + h]
         return out

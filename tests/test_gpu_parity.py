@@ -260,6 +260,47 @@ def test_unquantized_cache():
     assert np.array_equal(kd[0, :, :1000], ref16)
 
 
+# contiguous only: the appends below go past the lengths a block table would
+# have been sized for
+@pytest.mark.parametrize("axis,window,paged", [
+    ("channel_grow", 0, False), ("channel_grow", 32, False), ("channel", 32, False),
+])
+def test_channel_scales_running(axis, window, paged):
+    """Per-channel key scales with a bf16 window (held in float until the
+    tokens leave it) and growing with the running absmax: later appends with
+    larger keys grow the scales of some channels and re-quantize their stored
+    codes.  Records bit for bit, outputs within the bar."""
+    H.log(f"case: per-channel keys {axis} window={window} paged={paged}")
+    over = dict(batch=2, tokens=512, key=dict(bits=8, axis=axis),
+                value=dict(bits=4, scale="u8_super"), window=window)
+    if paged:
+        over.update(block_tokens=16)
+    wl = synth.workload(5, **over)
+    lens = [400, 150]
+    bt = H.build(wl, lens, decode_steps=0)
+    full_check(bt, steps=(0,))
+    prefill_scales = [bt.oracle.stored(b, "k").chan.copy() for b in range(wl["batch"])]
+    # appends whose keys are larger than the prefill's in some channels
+    rng = np.random.default_rng(31 + window)
+    for step, n_new in enumerate((3, 1, 60)):   # the last one pushes larger keys out of the window
+        grow = np.ones(wl["d"])
+        grow[rng.choice(wl["d"], 6, replace=False)] = rng.uniform(1.5, 4.0, 6)
+        k = synth.round_to_dtype(rng.standard_normal((wl["batch"], wl["hkv"], n_new, wl["d"])) * 3 * grow,
+                                 wl["in_dtype"])
+        v = synth.round_to_dtype(rng.standard_normal((wl["batch"], wl["hkv"], n_new, wl["d"])),
+                                 wl["in_dtype"])
+        for b in range(wl["batch"]):
+            bt.oracle.append(b, k[b], v[b])
+            bt.lens[b] += n_new
+        bt.cache.seq_lens.copy_(torch.tensor(bt.lens, dtype=torch.int32))
+        K.quantize_append(bt.cache, 0, H.to_device(k, wl["in_dtype"]), H.to_device(v, wl["in_dtype"]))
+        torch.cuda.synchronize()
+        full_check(bt, steps=(step,))
+    changed = sum(int((bt.oracle.stored(b, "k").chan != prefill_scales[b]).sum())
+                  for b in range(wl["batch"]))
+    assert (changed > 0) == (axis == "channel_grow")   # growth exercised; frozen stays
+
+
 def test_empty_and_zero_sequences():
     """A sequence with no tokens gives zeros; all-zero vectors quantize to
     codes 0 with scale 1 and attend like any other token."""

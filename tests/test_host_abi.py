@@ -126,7 +126,9 @@ def test_validation_errors():
         (dict(key=dict(bits=2), value=dict(bits=8)), K.KVQ_ERR_UNSUPPORTED),   # no such pair
         (dict(key=dict(bits=2, axis="channel"), value=dict(bits=2)), K.KVQ_ERR_UNSUPPORTED),
         (dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super"),
-              window=16), K.KVQ_ERR_UNSUPPORTED),
+              group_tokens=4), K.KVQ_ERR_UNSUPPORTED),
+        (dict(key=dict(bits=8, axis="channel_grow"), value=dict(bits=4, scale="u8_super"),
+              group_tokens=2), K.KVQ_ERR_UNSUPPORTED),
         (dict(key=dict(bits=16), value=dict(bits=8)), K.KVQ_ERR_UNSUPPORTED),   # mixed pair
         (dict(key=dict(bits=16), value=dict(bits=16), window=16), K.KVQ_ERR_UNSUPPORTED),
         (dict(key=dict(bits=16), value=dict(bits=16), block_tokens=16, num_blocks=8,
@@ -141,6 +143,9 @@ def test_validation_errors():
         assert K.validate(cfg) == want, over
     good = [
         dict(key=dict(bits=16), value=dict(bits=16)),   # unquantized, contiguous
+        dict(key=dict(bits=8, axis="channel_grow"), value=dict(bits=4, scale="u8_super"),
+             window=32),
+        dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super"), window=16),
         dict(key=dict(bits=2), value=dict(bits=2)),
         dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super")),
         dict(key=dict(bits=2, zero_point=True, scale="f16"),
