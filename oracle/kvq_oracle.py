@@ -77,6 +77,19 @@ Readings where the pages leave a step open (each restated where it is used):
       is quantized once it is complete and older than the window: positions
       [0, Q) with Q = floor(max(n - W, 0) / g) * g are quantized, the newest
       n - Q stay in bf16 as the window's do (R11).  g = 1 is per token.
+  R24 precision by recency beyond one window (P3 "Precision floors and mixed
+      cache formats": precision that depends on how recent an entry is; P1
+      "Cache growth changes the serving trade": recent tokens kept wider than
+      older ones): between the bf16 window and the cache's format sits a
+      middle tier of M positions (M a positive multiple of 32) stored as int8,
+      symmetric, one fp32 scale per token.  With Q = max(n - W, 0) and
+      A = floor(max(Q - M, 0) / 32) * 32, positions [0, A) hold the cache's
+      format, [A, Q) the middle tier and [Q, n) bf16.  A token leaves the
+      window into the middle tier (quantized as R11 says); it leaves the
+      middle tier, 32 positions at a time, re-quantized to the cache's format
+      from its middle-tier reconstruction c * s (exact).  The cache's format
+      is then a per-token one (no channel axes, no 8-bit scale codes, no token
+      groups).
   Scale underflow: a scale that rounds to 0 in its storage type is replaced by
   that type's smallest positive value (fp32 2^-149, fp16 2^-24); an fp16 scale
   above 65504 saturates to 65504.
@@ -166,6 +179,27 @@ def quantized_count(n: int, window: int = 0, group: int = 1) -> int:
     return max(n - window, 0) // group * group
 
 
+TIER_BLOCK = 32   # positions that leave the middle tier together (R24)
+MID_BITS, MID_SCALE = 8, "f32"   # the middle tier's format (R24)
+
+
+def tier_counts(n: int, window: int = 0, mid: int = 0, group: int = 1):
+    """Reading R24: (main, middle, bf16) position counts of an n-token
+    sequence; without a middle tier (mid = 0) the middle count is 0 and the
+    split is R11's / R20's."""
+    q = quantized_count(n, window, group)
+    if not mid:
+        return q, 0, n - q
+    a = max(q - mid, 0) // TIER_BLOCK * TIER_BLOCK
+    return a, q - a, n - q
+
+
+def mid_ring_slots(mid: int) -> int:
+    """Middle-tier slots per (sequence, head): M plus one block of 32, since
+    the tier holds between M and M + 31 positions once full (R24)."""
+    return mid + TIER_BLOCK if mid else 0
+
+
 def round_to_storage(x64, scale: str) -> np.ndarray:
     """Round fp64 values once (ties to even) to the storage type (R2), then
     apply the underflow/overflow rule stated in the module docstring."""
@@ -187,7 +221,11 @@ def rne_quotient(x, s) -> np.ndarray:
     x and s hold at most 24 significant bits and |x/s| <= 2^8 (plus the
     clamp), so the fp64 quotient never crosses or lands on a half-integer that
     the exact quotient does not: a non-tie quotient lies at least 2^-26 away
-    from any half-integer, while the fp64 rounding error is below 2^-44.
+    from any half-integer, while the fp64 rounding error is below 2^-44.  A
+    middle-tier reconstruction x = c * s8 (R24; |c| <= 127) has up to 31
+    significant bits, but its granule is s8's and s lies between s8 / 4 and
+    128 s8, so a non-tie quotient still lies at least 2^-34 from a
+    half-integer.
     """
     return np.rint(np.asarray(x, np.float64) / np.asarray(s, np.float64))
 
@@ -414,19 +452,32 @@ class OracleCache:
     With a token group size g > 1 (reading R20) one scale covers g
     consecutive positions, and the positions of a group not yet complete stay
     in bf16 beside the window.
+
+    With a middle tier of `mid` positions (reading R24) the tokens between the
+    window and the cache's format are held as int8 with one fp32 scale each.
     """
 
     def __init__(self, batch: int, hkv: int, d: int, key: TensorFormat,
-                 value: TensorFormat, window: int = 0, group: int = 1):
+                 value: TensorFormat, window: int = 0, group: int = 1, mid: int = 0):
         if group > 1 and (key.axis != "token" or key.scale == "u8_super"
                           or value.scale == "u8_super"):
             raise ValueError("token groups are modelled for per-token formats only")
         if group < 1:
             raise ValueError("group size must be at least 1")
+        if mid:
+            if mid < 0 or mid % TIER_BLOCK:
+                raise ValueError("the middle tier holds a positive multiple of 32 positions")
+            if group > 1 or any(f.axis != "token" or f.scale == "u8_super" or f.bits == 16
+                                for f in (key, value)):
+                raise ValueError("a middle tier is modelled for per-token formats only")
         self.batch, self.hkv, self.d = batch, hkv, d
         self.fmt = {"k": key, "v": value}
         self.window = window
         self.group = group
+        self.mid = mid
+        # middle tier (R24): codes [Hkv, n_mid, D] and fp32 scales [Hkv, n_mid]
+        self.midq = [{t: (np.zeros((hkv, 0, d), np.int32), np.zeros((hkv, 0), np.float32))
+                      for t in ("k", "v")} for _ in range(batch)]
         self.lens = [0] * batch
         self.side = [{"k": _Side(hkv, d), "v": _Side(hkv, d)} for _ in range(batch)]
         self.win = [{"k": np.zeros((hkv, 0, d)), "v": np.zeros((hkv, 0, d))}
@@ -493,10 +544,28 @@ class OracleCache:
                 q, self.win[b][t] = pool[:, :leave], round_bf16(pool[:, leave:])
             else:
                 q = x
+            if self.mid:
+                # reading R24: the tokens leaving the window enter the middle
+                # tier; its oldest whole blocks of 32 leave it for the cache's
+                # format, re-quantized from their exact reconstruction c * s
+                c8, s8 = quantize_sym(q, MID_BITS, MID_SCALE)
+                mc, ms = self.midq[b][t]
+                mc = np.concatenate([mc, c8], axis=1)
+                ms = np.concatenate([ms, s8], axis=1)
+                n_out = (tier_counts(total, self.window, self.mid)[0]
+                         - tier_counts(self.lens[b], self.window, self.mid)[0])
+                q = self._mid_reconstruction(mc[:, :n_out], ms[:, :n_out])
+                self.midq[b][t] = (mc[:, n_out:], ms[:, n_out:])
             if fmt.axis == "channel_grow" and not first and q.shape[1]:
                 self._grow_channels(side, fmt, q)
             self._quantize_into(side, fmt, q, first)
         self.lens[b] = total
+
+    @staticmethod
+    def _mid_reconstruction(codes, s):
+        """Reading R24: the exact value c * s of middle-tier tokens (fp64 holds
+        it: 7 bits times 24), from which they are re-quantized."""
+        return dequant_sym(codes, s)
 
     @staticmethod
     def _grow_channels(side: _Side, fmt: TensorFormat, x: np.ndarray):
@@ -537,6 +606,9 @@ class OracleCache:
         out = []
         for t in ("k", "v"):
             q = self._dequant(self.side[b][t], self.fmt[t])
+            if self.mid:
+                mc, ms = self.midq[b][t]
+                q = np.concatenate([q, dequant_sym(mc, ms)], axis=1)
             if self.window or self.group > 1:
                 q = np.concatenate([q, self.win[b][t]], axis=1)
             out.append(q)
@@ -546,6 +618,11 @@ class OracleCache:
         """The stored records of sequence b for t in {"k", "v"} (for bit-exact
         comparison of codes and metadata)."""
         return self.side[b][t]
+
+    def mid_stored(self, b: int, t: str):
+        """Middle-tier codes [Hkv, n_mid, D] and fp32 scales [Hkv, n_mid] of
+        sequence b, oldest first (reading R24)."""
+        return self.midq[b][t]
 
     def window_values(self, b: int, t: str) -> np.ndarray:
         return self.win[b][t]
@@ -596,7 +673,7 @@ def ring_slots(window: int = 0, group: int = 1) -> int:
 def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
                 d: int, lens: Sequence[int], window: int = 0,
                 block_tokens: int = 0, max_tokens: Optional[int] = None,
-                group: int = 1) -> Dict[str, int]:
+                group: int = 1, mid: int = 0) -> Dict[str, int]:
     """Bytes of a cache holding sequences of the given lengths.
 
     payload   P2 "Cache precision is separate from weight precision":
@@ -609,6 +686,8 @@ def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
               remain part of physical memory use").
     window    the bf16 tokens (window and incomplete group), 2 bytes per
               element for K and V.
+    A middle tier (R24) adds its int8 codes to payload and its fp32 scales
+    to metadata; its unused ring slots are padding.
     padding   allocated but unused slots: the unfilled tail of the last block
               of a paged sequence, or max_tokens - T_q quantized slots and the
               unused bf16 ring slots of a contiguous one.
@@ -621,12 +700,15 @@ def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
     codes = row(key) + row(value)
     meta = meta_bytes_per_token(key) + meta_bytes_per_token(value)   # per group
     ring = ring_slots(window, group)
+    mid_row, mid_meta = 2 * d, 2 * 4   # int8 K and V rows, fp32 scale each
     for n in lens:
-        n_q = quantized_count(n, window, group)
-        n_w = n - n_q
-        out["payload"] += layers * hkv * n_q * codes
+        n_q, n_m, n_w = tier_counts(n, window, mid, group)
+        out["payload"] += layers * hkv * (n_q * codes + n_m * mid_row)
         out["metadata"] += layers * hkv * (
-            n_q // group * meta + side_bytes_per_head(key, d) + side_bytes_per_head(value, d))
+            n_q // group * meta + n_m * mid_meta
+            + side_bytes_per_head(key, d) + side_bytes_per_head(value, d))
+        if mid:
+            out["padding"] += layers * hkv * (mid_ring_slots(mid) - n_m) * (mid_row + mid_meta)
         out["window"] += layers * hkv * n_w * d * 2 * 2
         if block_tokens:
             alloc_q = -(-n_q // block_tokens) * block_tokens
@@ -640,11 +722,12 @@ def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
 
 
 def decode_traffic(key: TensorFormat, value: TensorFormat, hkv: int, d: int,
-                   lens: Sequence[int], window: int = 0, group: int = 1) -> int:
+                   lens: Sequence[int], window: int = 0, group: int = 1,
+                   mid: int = 0) -> int:
     """Bytes one decode step must read from the cache (one layer): codes,
-    per-token (per-group) metadata, bf16 values and per-head side data; no
-    padding."""
-    b = cache_bytes(key, value, 1, hkv, d, lens, window, group=group)
+    per-token (per-group) metadata, middle-tier codes and scales, bf16 values
+    and per-head side data; no padding."""
+    b = cache_bytes(key, value, 1, hkv, d, lens, window, group=group, mid=mid)
     return b["payload"] + b["metadata"] + b["window"]
 
 

@@ -748,6 +748,137 @@ def pin_channel_growth(O):
     assert np.array_equal(frozen.stored(0, "k").chan, old_s)       # "channel" stays frozen
 
 
+def pin_tier_counts(O):
+    """Reading R24 by brute force: a position is in the cache's format when
+    its whole block of 32 positions is at least M older than the first
+    window position, in bf16 when it is among the W newest, in the middle
+    tier otherwise; the middle tier then holds M..M+31 positions once full and
+    never more than its ring.  Its bytes follow P2's 2 L H_kv D T b per tier
+    ("Cache precision is separate from weight precision")."""
+    for W in (0, 16, 100):
+        for M in (32, 64, 96):
+            for n in range(0, 420, 7):
+                q = max(n - W, 0)
+                main = sum(1 for p in range(q) if 32 * (p // 32 + 1) <= q - M)
+                got = O.tier_counts(n, W, M)
+                assert got == (main, q - main, n - q), (W, M, n, got)
+                if q >= M:
+                    assert M <= got[1] <= M + 31
+                assert got[1] <= O.mid_ring_slots(M)
+            assert O.tier_counts(50, W, 0) == (max(50 - W, 0), 0, min(W, 50))
+    k4, v4 = O.TensorFormat(4), O.TensorFormat(4)
+    lens = [300, 37, 1000]
+    b = O.cache_bytes(k4, v4, 2, 8, 128, lens, window=16, mid=64)
+    want = 0
+    for n in lens:
+        a, m, _ = O.tier_counts(n, 16, 64)
+        want += 2 * 2 * 8 * 128 * (a * Fraction(1, 2) + m * 1)
+    assert b["payload"] == want
+
+
+def _tier_stream(seed, hkv, n, d=128):
+    rng = _rng(seed)
+    mags = np.exp(rng.uniform(-6, 6, (hkv, n, 1)))
+    x = rng.standard_normal((hkv, n, d)) * mags
+    x[:, ::5, 3] *= 12.0                       # outlier entries set some maxima
+    x[:, 7] = 0.0                              # an all-zero token
+    return _bf16(x)
+
+
+def pin_tier_requantize(O):
+    """Reading R24 in exact arithmetic: a middle-tier token holds the int8
+    codes and RN32 scale of its value; a token in the cache's format holds
+    that format's codes of the exact middle-tier value c * s (symmetric,
+    zero point, 2 and 4 bits); window tokens hold their bf16 values."""
+    d, W, M = 128, 16, 64
+    x = _tier_stream(301, 1, 260)
+    y = _tier_stream(302, 1, 260)
+    fmts = [(O.TensorFormat(4), lambda v: exact_sym(v, 4, rn32)),
+            (O.TensorFormat(4, zero_point=True, scale="f16"), lambda v: exact_asym(v, 4)),
+            (O.TensorFormat(2, zero_point=True, scale="f16"), lambda v: exact_asym(v, 2))]
+    for fmt, exact in fmts:
+        cache = O.OracleCache(1, 1, d, fmt, fmt, window=W, mid=M)
+        cache.append(0, x[:, :200], y[:, :200])
+        cache.append(0, x[:, 200:], y[:, 200:])
+        a, m, w = O.tier_counts(260, W, M)
+        assert a > 0 and m > 0 and w == W
+        for t, src in (("k", x), ("v", y)):
+            st = cache.stored(0, t)
+            mc, ms = cache.mid_stored(0, t)
+            assert st.codes.shape[1] == a and mc.shape[1] == m
+            for p in range(a + m):
+                c8, s8 = exact_sym(src[0, p], 8, rn32)
+                if p >= a:
+                    assert list(mc[0, p - a]) == c8 and Fraction(float(ms[0, p - a])) == s8, (t, p)
+                    continue
+                rec = [float(c * s8) for c in c8]      # exact in fp64
+                want = exact(rec)
+                assert list(st.codes[0, p]) == want[0], (fmt, t, p)
+                assert Fraction(float(st.s[0, p])) == want[1], (fmt, t, p)
+                if fmt.zero_point:
+                    assert int(st.z[0, p]) == want[2]
+            assert np.array_equal(cache.window_values(0, t)[0], src[0, a + m:])
+
+
+def pin_tier_chunking(O):
+    """Reading R24: where a token is stored depends only on its age, so the
+    stored records are the same whether a stream is appended at once, token
+    by token, or in uneven pieces."""
+    d, W, M, n = 128, 8, 32, 150
+    x = _tier_stream(303, 2, n)
+    y = _tier_stream(304, 2, n)
+    fmt = O.TensorFormat(4, zero_point=True, scale="f16")
+    cuts = [[0, n], list(range(n + 1)), [0, 3, 40, 41, 90, 131, n]]
+    caches = []
+    for cut in cuts:
+        c = O.OracleCache(1, 2, d, fmt, fmt, window=W, mid=M)
+        for lo, hi in zip(cut[:-1], cut[1:]):
+            c.append(0, x[:, lo:hi], y[:, lo:hi])
+        caches.append(c)
+    ref = caches[0]
+    for c in caches[1:]:
+        for t in ("k", "v"):
+            for f in ("codes", "s", "z"):
+                assert np.array_equal(getattr(c.stored(0, t), f), getattr(ref.stored(0, t), f)), (t, f)
+            for i in range(2):
+                assert np.array_equal(c.mid_stored(0, t)[i], ref.mid_stored(0, t)[i])
+            assert np.array_equal(c.window_values(0, t), ref.window_values(0, t))
+        assert np.array_equal(c.reconstructed(0)[0], ref.reconstructed(0)[0])
+
+
+def pin_tier_int8_identity(O):
+    """Re-quantizing an int8 reconstruction to int8 with an fp32 scale gives
+    back the same codes and scale (its largest code is 127, so the scale is
+    RN32(127 s / 127) = s), so an int8 cache with a middle tier equals a plain
+    int8 cache with the same window; and with fewer than M + 32 tokens past
+    the window the cache's format holds nothing, whatever it is."""
+    d, W, M = 128, 16, 64
+    x = _tier_stream(305, 2, 300)
+    y = _tier_stream(306, 2, 300)
+    i8 = O.TensorFormat(8)
+    tier = O.OracleCache(1, 2, d, i8, i8, window=W, mid=M)
+    flat = O.OracleCache(1, 2, d, i8, i8, window=W)
+    for lo, hi in ((0, 120), (120, 121), (121, 300)):
+        tier.append(0, x[:, lo:hi], y[:, lo:hi])
+        flat.append(0, x[:, lo:hi], y[:, lo:hi])
+        for u, v in zip(tier.reconstructed(0), flat.reconstructed(0)):
+            assert np.array_equal(u, v)
+    a = O.tier_counts(300, W, M)[0]
+    assert np.array_equal(tier.stored(0, "k").codes, flat.stored(0, "k").codes[:, :a])
+    q4 = O.TensorFormat(4)
+    short = O.OracleCache(1, 2, d, q4, q4, window=W, mid=M)
+    short.append(0, x[:, :W + M + 31], y[:, :W + M + 31])
+    assert short.stored(0, "k").codes.shape[1] == 0
+    for u, v in zip(short.reconstructed(0), _flat_prefix(O, x, y, W, W + M + 31)):
+        assert np.array_equal(u, v)
+
+
+def _flat_prefix(O, x, y, W, n):
+    c = O.OracleCache(1, x.shape[0], x.shape[2], O.TensorFormat(8), O.TensorFormat(8), window=W)
+    c.append(0, x[:, :n], y[:, :n])
+    return c.reconstructed(0)
+
+
 def pin_window_stores_bf16(O):
     """Unquantized tokens (bits 16, or the recent window) are stored in bf16:
     fp32 inputs come back rounded to nearest-even bf16 (torch's conversion)."""

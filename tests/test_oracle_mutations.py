@@ -86,6 +86,29 @@ def m_growth_never(O):
     O.OracleCache._grow_channels = staticmethod(lambda side, fmt, x: None)
 
 
+def m_tier_reconstruction_fp32(O):
+    O.OracleCache._mid_reconstruction = staticmethod(
+        lambda c, s: O.dequant_sym(c, s).astype(np.float32).astype(np.float64))
+
+
+def m_tier_mid_scale_fp16(O):
+    O.MID_SCALE = "f16"
+
+
+def m_tier_unaligned(O):
+    def tier_counts(n, window=0, mid=0, group=1):
+        q = O.quantized_count(n, window, group)
+        a = max(q - mid, 0) if mid else q
+        return a, q - a, n - q
+    O.tier_counts = tier_counts
+
+
+def m_tier_ignores_window(O):
+    orig = O.tier_counts
+    O.tier_counts = lambda n, window=0, mid=0, group=1: (
+        orig(n, 0, mid, group)[0] if mid else orig(n, window, mid, group)[0],) + orig(n, window, mid, group)[1:]
+
+
 def m_no_inv_sqrt_d(O):
     O.scores = lambda q, k: np.asarray(k, np.float64) @ np.asarray(q, np.float64)
 
