@@ -56,6 +56,16 @@ __device__ inline float wave_min(float v) {
   return v;
 }
 
+__device__ inline double wave_max(double v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ inline double wave_min(double v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmin(v, __shfl_xor(v, o));
+  return v;
+}
+
 // fp64 -> fp32 storage: one rounding, ties to even; 0 becomes 2^-149.
 __device__ inline float store_f32(double v) {
   float f = (float)v;
@@ -147,7 +157,8 @@ __device__ inline int qmax_zp(int bits) { return (1 << bits) - 1; }
 // head): one scale (and zero point, or 8-bit scale code) over all its g*D
 // values, then the codes of each token.  ld(p, x0, x1) loads elements 2*lane
 // and 2*lane+1 of position p; slot(p) is its code slot; metadata element m
-// belongs to the group.  g = 1 is the per-token case.
+// belongs to the group.  g = 1 is the per-token case.  Values are taken in
+// fp64: inputs are exact in it, and so is a middle-tier value c * s.
 template <typename Load, typename Slot>
 __device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, int g,
                                uint8_t* codes, uint8_t* meta, size_t m, const float* chan,
@@ -155,15 +166,15 @@ __device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, i
   const int bits = code_bits(k.code);
   const bool zp = k.meta == MK_F32Z || k.meta == MK_F16Z;
   // 1. group statistics
-  float amax = 0.0f, lo = 0.0f, hi = 0.0f;
+  double amax = 0.0, lo = 0.0, hi = 0.0;
   if (!k.channel) {
-    float mx = 0.0f, mn = 0.0f, ab = 0.0f;
+    double mx = 0.0, mn = 0.0, ab = 0.0;
     for (int j = 0; j < g; ++j) {
-      float x0, x1;
+      double x0, x1;
       ld(p0 + j, x0, x1);
-      ab = fmaxf(ab, fmaxf(fabsf(x0), fabsf(x1)));
-      mx = fmaxf(mx, fmaxf(x0, x1));
-      mn = fminf(mn, fminf(x0, x1));
+      ab = fmax(ab, fmax(fabs(x0), fabs(x1)));
+      mx = fmax(mx, fmax(x0, x1));
+      mn = fmin(mn, fmin(x0, x1));
     }
     amax = wave_max(ab);
     hi = wave_max(mx);  // zero point: the range includes 0 (mx, mn start at 0)
@@ -179,21 +190,21 @@ __device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, i
   } else if (k.meta == MK_U8) {
     // 8-bit scale code relative to the frozen per-head super-scale
     qmax = qmax_sym(bits);
-    nonzero = amax != 0.0f;
+    nonzero = amax != 0.0;
     if (nonzero) {
-      const double sigma = (double)amax / qmax;
+      const double sigma = amax / qmax;
       u = clampi((int)rint(sigma / (double)super), 1, 255);
       s = (double)u * (double)super;  // exact
     }
   } else if (!zp) {
     qmax = qmax_sym(bits);
-    nonzero = amax != 0.0f;
+    nonzero = amax != 0.0;
     if (k.meta == MK_F32) {
-      const float sf = nonzero ? store_f32((double)amax / qmax) : 1.0f;
+      const float sf = nonzero ? store_f32(amax / qmax) : 1.0f;
       s = (double)sf;
       sbits = __float_as_uint(sf);
     } else {
-      const uint16_t hb = nonzero ? store_f16((double)amax / qmax) : (uint16_t)0x3C00u;
+      const uint16_t hb = nonzero ? store_f16(amax / qmax) : (uint16_t)0x3C00u;
       s = f16_bits_to_f64(hb);
       sbits = hb;
     }
@@ -201,15 +212,15 @@ __device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, i
     qmax = qmax_zp(bits);
     nonzero = hi != lo;
     if (k.meta == MK_F32Z) {
-      const float sf = nonzero ? store_f32(((double)hi - (double)lo) / qmax) : 1.0f;
+      const float sf = nonzero ? store_f32((hi - lo) / qmax) : 1.0f;
       s = (double)sf;
       sbits = __float_as_uint(sf);
     } else {
-      const uint16_t hb = nonzero ? store_f16(((double)hi - (double)lo) / qmax) : (uint16_t)0x3C00u;
+      const uint16_t hb = nonzero ? store_f16((hi - lo) / qmax) : (uint16_t)0x3C00u;
       s = f16_bits_to_f64(hb);
       sbits = hb;
     }
-    if (nonzero) z = clampi((int)rint(-(double)lo / s), 0, qmax);
+    if (nonzero) z = clampi((int)rint(-lo / s), 0, qmax);
   }
   if (lane == 0 && !k.channel) {
     if (k.meta == MK_U8) {
@@ -228,7 +239,7 @@ __device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, i
   }
   // 3. codes of each token of the group
   for (int j = 0; j < g; ++j) {
-    float x0, x1;
+    double x0, x1;
     ld(p0 + j, x0, x1);
     int c0 = 0, c1 = 0;
     if (k.channel) {
@@ -352,24 +363,27 @@ __global__ void __launch_bounds__(256) append_stats(AppendArgs a) {
   }
 }
 
-__global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const SeqRange r = seq_range(a, b);
-  // token groups completed by this append: positions [qlo, qhi)
-  const int qlo = quantized_count(a, r.start), qhi = quantized_count(a, r.len);
-  const int g = a.tgroup;
-  const int p0 = qlo + i * g;
-  if (p0 >= qhi || p0 + g > q_capacity(a)) return;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const TensorKind k = w == 0 ? a.kk : a.vk;
-  const void* src = w == 0 ? a.k_new : a.v_new;
-  const uint16_t* ring = w == 0 ? a.k_win : a.v_win;
-  const size_t head = (size_t)b * a.hkv + h;
-  // a position of this append comes from the input, an older one from its
-  // bf16 copy in the ring
-  auto ld = [&](int p, float& x0, float& x1) {
-    if (p >= r.start) {
-      const size_t row = (head * a.n_new + (p - r.start)) * D;
+// Positions of an n-token sequence held in the cache's format: with a middle
+// tier of M positions, whole blocks of 32 at least M older than the window;
+// otherwise every quantized position.
+__device__ inline int main_count(const AppendArgs& a, int n) {
+  const int q = quantized_count(a, n);
+  if (!a.mid.tokens) return q;
+  const int m = q - a.mid.tokens;
+  return m > 0 ? m / MID_BLOCK * MID_BLOCK : 0;
+}
+
+// Loads elements 2 lane, 2 lane + 1 of position p of (b, h) for wave w
+// (0 = key, 1 = value): a position of this append from the input, an older
+// one from its bf16 copy in the ring.
+struct InputLoader {
+  const void* src;
+  const uint16_t* ring;
+  size_t head;
+  int start, lane;
+  __device__ void operator()(const AppendArgs& a, int p, double& x0, double& x1) const {
+    if (p >= start) {
+      const size_t row = (head * a.n_new + (p - start)) * D;
       x0 = load_in(src, row + 2 * lane, a.in_bf16);
       x1 = load_in(src, row + 2 * lane + 1, a.in_bf16);
     } else {
@@ -377,14 +391,50 @@ __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
       x0 = bf16_bits_to_f32(ring[row + 2 * lane]);
       x1 = bf16_bits_to_f32(ring[row + 2 * lane + 1]);
     }
-  };
+  }
+};
+
+__device__ inline InputLoader input_loader(const AppendArgs& a, int w, size_t head, int start,
+                                           int lane) {
+  return InputLoader{w == 0 ? a.k_new : a.v_new, w == 0 ? a.k_win : a.v_win, head, start, lane};
+}
+
+constexpr TensorKind MID_KIND{CK_I8, MK_F32, false, false};
+
+__global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SeqRange r = seq_range(a, b);
+  // token groups completed by this append: positions [qlo, qhi); with a
+  // middle tier, those of them that stay in it
+  int qlo = quantized_count(a, r.start);
+  const int qhi = quantized_count(a, r.len);
+  if (a.mid.tokens) {
+    const int na = main_count(a, r.len);
+    qlo = qlo > na ? qlo : na;
+  }
+  const int g = a.tgroup;
+  const int p0 = qlo + i * g;
+  if (p0 >= qhi) return;
+  if (!a.mid.tokens && p0 + g > q_capacity(a)) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const TensorKind k = w == 0 ? a.kk : a.vk;
+  const size_t head = (size_t)b * a.hkv + h;
+  const InputLoader in = input_loader(a, w, head, r.start, lane);
+  auto ld = [&](int p, double& x0, double& x1) { in(a, p, x0, x1); };
+  if (a.mid.tokens) {  // into the middle tier: int8, fp32 scale, ring slot p % slots
+    auto mslot = [&](int p) { return head * a.mid.slots + (size_t)(p % a.mid.slots); };
+    quantize_group(MID_KIND, ld, mslot, p0, 1, w == 0 ? a.mid.k : a.mid.v,
+                   (uint8_t*)(w == 0 ? a.mid.ks : a.mid.vs), mslot(p0), nullptr, 1.0f, lane);
+    return;
+  }
   auto slot = [&](int p) { return slot_index(a, b, h, p); };
   uint8_t* codes = w == 0 ? a.k_codes : a.v_codes;
   if (k.code == CK_BF16) {  // unquantized (bits 16): the bf16 values themselves
     for (int j = 0; j < g; ++j) {
-      float x0, x1;
+      double x0, x1;
       ld(p0 + j, x0, x1);
-      const uint32_t v = (uint32_t)f32_to_bf16_bits(x0) | ((uint32_t)f32_to_bf16_bits(x1) << 16);
+      const uint32_t v = (uint32_t)f32_to_bf16_bits((float)x0) |
+                         ((uint32_t)f32_to_bf16_bits((float)x1) << 16);
       ((uint32_t*)(codes + slot(p0 + j) * (size_t)(2 * D)))[lane] = v;
     }
     return;
@@ -395,6 +445,50 @@ __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   const float super = k.meta == MK_U8 ? sup[head] : 1.0f;
   quantize_group(k, ld, slot, p0, g, codes, meta, slot_index(a, b, h, p0) >> a.tgshift, chan,
                  super, lane);
+}
+
+// Middle tier: the positions an append moves into the cache's format,
+// [main_count(start), main_count(len)), re-quantized from their exact
+// middle-tier value c * s.  One that was in the middle tier before this
+// append is read from its ring slot; one that passes through it within the
+// append (a long append) is quantized to int8 here first, as
+// append_quantize would have stored it.  Runs before append_quantize, which
+// may reuse those ring slots.
+__global__ void __launch_bounds__(128) append_demote(AppendArgs a) {
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SeqRange r = seq_range(a, b);
+  const int p = main_count(a, r.start) + i;
+  if (p >= main_count(a, r.len) || p >= a.max_tokens) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t head = (size_t)b * a.hkv + h;
+  double v0, v1;  // the middle-tier value c * s (exact in fp64)
+  if (p < quantized_count(a, r.start)) {
+    const size_t ms = head * a.mid.slots + (size_t)(p % a.mid.slots);
+    const uint8_t* row = (w == 0 ? a.mid.k : a.mid.v) + ms * D;
+    const double sc = (double)(w == 0 ? a.mid.ks : a.mid.vs)[ms];
+    v0 = (double)(int8_t)row[2 * lane] * sc;
+    v1 = (double)(int8_t)row[2 * lane + 1] * sc;
+  } else {
+    double x0, x1;
+    input_loader(a, w, head, r.start, lane)(a, p, x0, x1);
+    // int8, one fp32 scale: the middle tier's quantizer
+    const double amax = wave_max(fmax(fabs(x0), fabs(x1)));
+    if (amax == 0.0) {
+      v0 = v1 = 0.0;
+    } else {
+      const double sc = (double)store_f32(amax / 127);
+      v0 = (double)clampi(rne_code(x0, sc), -127, 127) * sc;
+      v1 = (double)clampi(rne_code(x1, sc), -127, 127) * sc;
+    }
+  }
+  auto ld = [&](int, double& x0, double& x1) {
+    x0 = v0;
+    x1 = v1;
+  };
+  auto slot = [&](int q) { return slot_index(a, b, h, q); };
+  const TensorKind k = w == 0 ? a.kk : a.vk;
+  quantize_group(k, ld, slot, p, 1, w == 0 ? a.k_codes : a.v_codes, w == 0 ? a.k_meta : a.v_meta,
+                 slot_index(a, b, h, p), nullptr, 1.0f, lane);
 }
 
 __global__ void __launch_bounds__(128) append_window(AppendArgs a) {
@@ -424,6 +518,12 @@ kvq_status launch_append(const AppendArgs& a, void* stream) {
   const dim3 heads(a.hkv, a.batch);
   if (a.kk.channel || a.kk.meta == MK_U8 || a.vk.meta == MK_U8) {
     hipLaunchKernelGGL(append_stats, heads, dim3(256), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+  }
+  if (a.mid.tokens) {
+    // positions an append moves into the cache's format: at most n_new + 31
+    hipLaunchKernelGGL(append_demote, dim3(a.n_new + MID_BLOCK, a.hkv, a.batch), dim3(128), 0, s,
+                       a);
     if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
   }
   // groups completed by an append: at most (n_new + ring) / g + 1

@@ -316,6 +316,7 @@ struct Addr {
   int gs;                // log2 of the token group size (metadata per group)
   size_t head_tok;       // contiguous: first token slot of this head
   int nblk;              // blocks holding tokens
+  int rblk;              // ring (middle tier): blocks of the ring, block i in slot i mod rblk
   // paged: block-table entries of this wave's blocks blk0 .. blk0 + 127,
   // entry blk0 + i in lane i & 63 of ent[i >> 6]
   int blk0;
@@ -328,11 +329,13 @@ constexpr int WAVE_BLOCKS = 128;
 // Token slot index of block `blk` (clamped to the blocks holding tokens and,
 // when paged, to the pool); wave-uniform.  Paged lookups read the entries
 // preloaded into the wave's registers (v_readlane), so the token loop issues
-// no memory access for them.
-template <bool PAGED>
+// no memory access for them.  RING: the middle tier's ring of rblk blocks.
+template <bool PAGED, bool RING = false>
 __device__ inline size_t block_slot(const Addr& ad, int blk) {
   blk = blk < ad.nblk ? blk : ad.nblk - 1;
-  if constexpr (PAGED) {
+  if constexpr (RING) {
+    return ad.head_tok + (size_t)(blk % ad.rblk) * 16;
+  } else if constexpr (PAGED) {
     int i = blk - ad.blk0;
     i = i < 0 ? 0 : (i >= WAVE_BLOCKS ? WAVE_BLOCKS - 1 : i);
     int phys = i < 64 ? __builtin_amdgcn_readlane(ad.ent[0], i)
@@ -401,14 +404,14 @@ struct TileRaw {
 // load is issued whatever t0 is, so the wait counts the compiler derives stay
 // exact; a 16-token block at or past tend is read through an empty resource
 // (zeros, no memory traffic) and its tokens are masked by compute_tile.
-template <bool PAGED, int KC, int KM, int VC, int VM>
+template <bool PAGED, bool RING, int KC, int KM, int VC, int VM>
 __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int t0, int tend,
                                  const LaneOff& o) {
   constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const bool live = t0 + 16 * bb < tend;
-    const size_t slot = block_slot<PAGED>(ad, (t0 >> 4) + bb);
+    const size_t slot = block_slot<PAGED, RING>(ad, (t0 >> 4) + bb);
     const auto rk = rsrc(ad.k + slot * KROW, live ? 16 * KROW : 0);
     if (Codes<KC>::B2) {
       const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rk, o.k0, 0, 0);
@@ -957,21 +960,28 @@ __device__ inline void block_merge(const DecodeArgs& a, const Shared<G>& sh, int
   }
 }
 
+// Positions of a sequence: [0, nq) in the cache's format, [nq, nq + nm) in
+// the middle tier, the last nw in bf16.
 struct SeqInfo {
-  int len, nw, nq;
+  int len, nw, nq, nm;
 };
 
 __device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
   SeqInfo s;
   int len = a.seq_lens[b];
   len = len > 0 ? len : 0;
-  const int cap = (a.paged ? a.bt_stride * 16 : a.max_tokens) + a.window;
+  const int cap = (a.paged ? a.bt_stride * 16 : a.max_tokens) + a.window + a.mid.tokens;
   len = len < cap ? len : cap;
   s.len = len;
   // quantized: whole token groups older than the window; the rest is bf16
   const int m = len - a.window > 0 ? len - a.window : 0;
-  s.nq = (m >> a.tgshift) << a.tgshift;
-  s.nw = len - s.nq;
+  const int q = (m >> a.tgshift) << a.tgshift;
+  // middle tier: the cache's format holds whole blocks of 32 positions at
+  // least M older than the window
+  const int r = q - a.mid.tokens;
+  s.nq = a.mid.tokens ? (r > 0 ? r / MID_BLOCK * MID_BLOCK : 0) : q;
+  s.nm = q - s.nq;
+  s.nw = len - q;
   return s;
 }
 
@@ -1080,9 +1090,9 @@ __device__ void bf16_tokens(const DecodeArgs& a, int b, int h, const uint16_t* k
 // The bf16 tokens of a quantized cache: the window and an open token group,
 // positions [nq, nq + nw) in ring slots (nq + i) mod ring.
 template <int G, bool QB>
-__device__ void window_split(const DecodeArgs& a, int b, int h, int nq, int nw, Shared<G>& sh) {
+__device__ void window_split(const DecodeArgs& a, int b, int h, int q0, int nw, Shared<G>& sh) {
   const size_t head = ((size_t)b * a.hkv + h) * a.ring * D;
-  bf16_tokens<G, QB, false>(a, b, h, a.k_win + head, a.v_win + head, nq % a.ring, a.ring, nw,
+  bf16_tokens<G, QB, false>(a, b, h, a.k_win + head, a.v_win + head, q0 % a.ring, a.ring, nw,
                             a.n_split, sh);
 }
 
@@ -1094,7 +1104,7 @@ __device__ void window_split(const DecodeArgs& a, int b, int h, int nq, int nw, 
 // launched; a longer sequence is an overflow of the plan).
 struct Plan {
   int ns;
-  bool overflow, win;
+  bool overflow, win, mid;
   int total;  // workgroups that write a partial
 };
 
@@ -1104,8 +1114,21 @@ __device__ inline Plan plan_of(const DecodeArgs& a, const SeqInfo& si) {
   p.overflow = need > a.n_split;
   p.ns = p.overflow ? a.n_split : need;
   p.win = si.nw > 0;
-  p.total = p.ns + (p.win ? 1 : 0);
+  p.mid = si.nm > 0;
+  p.total = p.ns + (p.win ? 1 : 0) + (p.mid ? 1 : 0);
   return p;
+}
+
+// Partial row slots of a (sequence, query head): the splits in 0 ..
+// n_split - 1, the bf16 item in n_split (if the cache has a ring), the middle
+// tier after it.
+__device__ inline int mid_row(const DecodeArgs& a) { return a.n_split + (a.ring ? 1 : 0); }
+
+// Slot of the j-th partial row that a pair's combine reads: its splits,
+// then its bf16 item, then its middle tier (those it has).
+__device__ inline int partial_slot(const DecodeArgs& a, const Plan& pl, int j) {
+  if (j < pl.ns) return j;
+  return (j == pl.ns && pl.win) ? a.n_split : mid_row(a);
 }
 
 __device__ inline float2 load_agent2(const float* p) {
@@ -1134,14 +1157,14 @@ __device__ inline void write_combined(const DecodeArgs& a, int b, int h, int G, 
 template <int G>
 __device__ void combine_heads(const DecodeArgs& a, int b, int h, const Plan& pl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nr = pl.ns + (pl.win ? 1 : 0);  // partial rows: splits, then the window
+  const int nr = pl.total;  // partial rows: splits, then the window, then the middle tier
   if (nr <= 64) {
     constexpr int HPW = G > WAVES ? G / WAVES : 1;
     constexpr int CB = 16;
     if (wave >= G) return;
     size_t row0[HPW];
     float2 ml[HPW], v[HPW][CB];
-    auto prow = [&](int u, int j) { return row0[u] + (j < pl.ns ? j : a.n_split); };
+    auto prow = [&](int u, int j) { return row0[u] + partial_slot(a, pl, j); };
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
       row0[u] = ((size_t)b * a.hq + (size_t)h * G + wave + u * WAVES) * a.nsp;
@@ -1181,7 +1204,7 @@ __device__ void combine_heads(const DecodeArgs& a, int b, int h, const Plan& pl)
   }
   for (int hh = wave; hh < G; hh += WAVES) {
     const size_t row0 = ((size_t)b * a.hq + (size_t)h * G + hh) * a.nsp;
-    auto prow = [&](int j) { return row0 + (j < pl.ns ? j : a.n_split); };
+    auto prow = [&](int j) { return row0 + partial_slot(a, pl, j); };
     float M = NEG_INF;
     for (int j = lane; j < nr; j += 64) M = fmaxf(M, load_agent(a.part_ml + 2 * prow(j)));
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
@@ -1248,10 +1271,12 @@ __device__ void arrive_and_combine(const DecodeArgs& a, int b, int h, const Plan
 //      rotated by the pair index (consecutive workgroups go to different
 //      XCDs; this way the chunks that start together on one XCD lie at
 //      different offsets of their pairs),
-//   2. the remainder chunk of each sequence, by size class from large to
+//   2. with a middle tier, one item per (sequence, KV head) for it (up to
+//      M + 31 int8 tokens: about a full chunk's work or less),
+//   3. the remainder chunk of each sequence, by size class from large to
 //      small (NSIZE classes of split_tokens / NSIZE tokens),
-//   3. one item per (sequence, KV head) for the bf16 window, if any,
-//   4. workgroups past the last item return at once.
+//   4. one item per (sequence, KV head) for the bf16 window, if any,
+//   5. workgroups past the last item return at once.
 // Every wave derives the workgroup's item on its own from the sequence
 // lengths (one length per lane, 64 sequences per pass), with wave scans and
 // ballots: no workgroup barrier before the first tile loads.
@@ -1259,7 +1284,7 @@ __device__ void arrive_and_combine(const DecodeArgs& a, int b, int h, const Plan
 constexpr int NSIZE = 32;
 
 struct Item {
-  int kind;  // 0 quantized chunk, 1 window, 2 nothing
+  int kind;  // 0 quantized chunk, 1 bf16 tokens, 2 nothing, 3 middle tier
   int b, h, split;
   SeqInfo si;
 };
@@ -1298,13 +1323,13 @@ __device__ inline int lane_of(uint64_t m) { return __builtin_ctzll(m); }
 __device__ inline int rdl(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 
 __device__ inline SeqInfo read_si(const SeqInfo& s, int l) {
-  return SeqInfo{rdl(s.len, l), rdl(s.nw, l), rdl(s.nq, l)};
+  return SeqInfo{rdl(s.len, l), rdl(s.nw, l), rdl(s.nq, l), rdl(s.nm, l)};
 }
 
 // hist: this wave's NSIZE counters in LDS
-__device__ Item map_item(const DecodeArgs& a, int item, int* hist) {
+__device__ Item map_item(const DecodeArgs& a, int item, int* hist, bool tier) {
   const int lane = threadIdx.x & 63;
-  Item it{2, 0, 0, 0, {0, 0, 0}};
+  Item it{2, 0, 0, 0, {0, 0, 0, 0}};
   if (lane < NSIZE) hist[lane] = 0;
   __builtin_amdgcn_wave_barrier();
   // 1. full chunks
@@ -1335,11 +1360,22 @@ __device__ Item map_item(const DecodeArgs& a, int item, int* hist) {
     carry += rdl(inc, 63);
   }
   __builtin_amdgcn_wave_barrier();
-  // 2. remainder chunks: the rank-th one in (size class, sequence) order
+  long long r = item - (long long)a.hkv * carry;
+  if (tier) {  // 2. middle tiers
+    if (r < (long long)a.batch * a.hkv) {
+      it.kind = 3;
+      it.b = (int)(r / a.hkv);
+      it.h = (int)(r % a.hkv);
+      it.split = mid_row(a);
+      it.si = seq_info(a, it.b);
+      return it;
+    }
+    r -= (long long)a.batch * a.hkv;
+  }
+  // 3. remainder chunks: the rank-th one in (size class, sequence) order
   const int cnt = lane < NSIZE ? hist[lane] : 0;
   const int cinc = wave_scan(cnt);
   const int np = rdl(cinc, 63);
-  long long r = item - (long long)a.hkv * carry;
   if (r < (long long)a.hkv * np) {
     const int rank = (int)(r / a.hkv);
     const int cls = lane_of(__ballot(lane < NSIZE && cinc > rank));
@@ -1369,7 +1405,7 @@ __device__ Item map_item(const DecodeArgs& a, int item, int* hist) {
     return it;  // not reached: the rank-th remainder chunk exists
   }
   r -= (long long)a.hkv * np;
-  if (a.ring && r < (long long)a.batch * a.hkv) {  // 3. bf16 items (window, open group)
+  if (a.ring && r < (long long)a.batch * a.hkv) {  // 4. bf16 items (window, open group)
     it.kind = 1;
     it.b = (int)(r / a.hkv);
     it.h = (int)(r % a.hkv);
@@ -1379,37 +1415,15 @@ __device__ Item map_item(const DecodeArgs& a, int item, int* hist) {
   return it;
 }
 
-template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB>
-__global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
-  __shared__ Shared<G> sh;
-  // 1-D grid of work items, largest first (map_item).  Consecutive items,
-  // which the hardware sends to different XCDs, are mostly the KV heads of
-  // one chunk.
-  __shared__ int last_flag;
-  __shared__ int hist[WAVES][NSIZE];
-  // workgroup p < batch * hkv also writes the (zero) output of pair p if
-  // its sequence is empty
-  const bool zduty = blockIdx.x < (unsigned)(a.batch * a.hkv);
-  const int zlen = zduty ? a.seq_lens[blockIdx.x / a.hkv] : 1;
-  const Item it = map_item(a, blockIdx.x, hist[threadIdx.x >> 6]);
-  if (zduty && zlen <= 0) {
-    const int zb = blockIdx.x / a.hkv, zh = blockIdx.x % a.hkv;
-    for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64)
-      a.out[((size_t)zb * a.hq + (size_t)zh * G) * D + idx] = 0.0f;
-  }
-  if (it.kind == 2) return;
-  const int b = it.b, h = it.h, split = it.split;
-  const SeqInfo si = it.si;
-  const Plan pl = plan_of(a, si);
-  if (it.kind == 1) {
-    if (si.nw > 0) {
-      window_split<G, QB>(a, b, h, si.nq, si.nw, sh);
-      arrive_and_combine<G>(a, b, h, pl, &last_flag);
-    }
-    return;
-  }
-  const int tok0 = split * a.split_tokens;
-  const int tok1 = min(tok0 + a.split_tokens, si.nq);
+// Attends quantized positions [tok0, tok1) of (sequence b, KV head h) with
+// the G query heads of h and writes partial row `row`.  The codes and
+// metadata live at kc, vc, km, vm: token slot head_tok + position
+// (contiguous), through the block table (PAGED), or in a ring of rblk
+// 16-token blocks (RING, the middle tier); nend bounds the blocks read.
+template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool RING>
+__device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok1, int nend,
+                            int row, const uint8_t* kc, const uint8_t* vc, const uint8_t* km,
+                            const uint8_t* vm, size_t head_tok, int rblk, Shared<G>& sh) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1438,22 +1452,19 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   // 2. the first two tiles of this wave's range, in flight while the query
   //    is prepared
   Addr ad;
-  ad.k = a.k_codes;
-  ad.v = a.v_codes;
-  ad.km = a.k_meta;
-  ad.vm = a.v_meta;
+  ad.k = kc;
+  ad.v = vc;
+  ad.km = km;
+  ad.vm = vm;
   ad.num_blocks = a.num_blocks;
   ad.hkv = a.hkv;
   ad.h = h;
   ad.gs = a.tgshift;
-  ad.nblk = (si.nq + 15) >> 4;
+  ad.nblk = (nend + 15) >> 4;
+  ad.rblk = rblk;
   ad.blk0 = 0;
   ad.ent[0] = ad.ent[1] = 0;
-  if constexpr (PAGED) {
-    ad.head_tok = 0;
-  } else {
-    ad.head_tok = ((size_t)b * a.hkv + h) * a.max_tokens;
-  }
+  ad.head_tok = head_tok;
   const LaneOff lo = lane_offsets<KC, KM, VC, VM>(lt, g, a.tgshift);
   // the chunk's tiles spread evenly over the waves
   const int per = (tok1 - tok0 + WAVES * TILE - 1) / (WAVES * TILE) * TILE;
@@ -1475,7 +1486,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   TileRaw<KC, KM, VC, VM> buf[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
-    load_tile<PAGED>(buf[k], ad, w0 + k * TILE, w1, lo);
+    load_tile<PAGED, RING>(buf[k], ad, w0 + k * TILE, w1, lo);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -1567,7 +1578,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
       compute_tile<KC, KM, KCH, VC, VM, G>(buf[k], t + k * TILE, w1, qa, qs, sumq, lt, g, psel, prd,
                                            pwr, nm, st);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile<PAGED>(buf[k], ad, t + (k + NB) * TILE, w1, lo);
+      load_tile<PAGED, RING>(buf[k], ad, t + (k + NB) * TILE, w1, lo);
       __builtin_amdgcn_sched_barrier(0);
     }
     t += NB * TILE;
@@ -1584,7 +1595,57 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   else
     scale_out = st.R;
   row_finish<G>(st, scale_out, lt, g, wave, sh);
-  block_merge<G>(a, sh, b, h, split);
+  block_merge<G>(a, sh, b, h, row);
+}
+
+
+template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool TIER>
+__global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
+  __shared__ Shared<G> sh;
+  // 1-D grid of work items, largest first (map_item).  Consecutive items,
+  // which the hardware sends to different XCDs, are mostly the KV heads of
+  // one chunk.
+  __shared__ int last_flag;
+  __shared__ int hist[WAVES][NSIZE];
+  // workgroup p < batch * hkv also writes the (zero) output of pair p if
+  // its sequence is empty
+  const bool zduty = blockIdx.x < (unsigned)(a.batch * a.hkv);
+  const int zlen = zduty ? a.seq_lens[blockIdx.x / a.hkv] : 1;
+  const Item it = map_item(a, blockIdx.x, hist[threadIdx.x >> 6], TIER);
+  if (zduty && zlen <= 0) {
+    const int zb = blockIdx.x / a.hkv, zh = blockIdx.x % a.hkv;
+    for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64)
+      a.out[((size_t)zb * a.hq + (size_t)zh * G) * D + idx] = 0.0f;
+  }
+  if (it.kind == 2) return;
+  const int b = it.b, h = it.h, split = it.split;
+  const SeqInfo si = it.si;
+  const Plan pl = plan_of(a, si);
+  if (it.kind == 1) {
+    if (si.nw > 0) {
+      window_split<G, QB>(a, b, h, si.nq + si.nm, si.nw, sh);
+      arrive_and_combine<G>(a, b, h, pl, &last_flag);
+    }
+    return;
+  }
+  const size_t pair = (size_t)b * a.hkv + h;
+  if constexpr (TIER) {
+    if (it.kind == 3) {  // the middle tier: int8 codes, fp32 scales, in its ring
+      if (si.nm > 0) {
+        quant_range<CK_I8, MK_F32, false, CK_I8, MK_F32, G, false, QB, true>(
+            a, b, h, si.nq, si.nq + si.nm, si.nq + si.nm, split, a.mid.k, a.mid.v,
+            (const uint8_t*)a.mid.ks, (const uint8_t*)a.mid.vs, pair * a.mid.slots,
+            a.mid.slots >> 4, sh);
+        arrive_and_combine<G>(a, b, h, pl, &last_flag);
+      }
+      return;
+    }
+  }
+  const int tok0 = split * a.split_tokens;
+  const int tok1 = min(tok0 + a.split_tokens, si.nq);
+  quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
+      a, b, h, tok0, tok1, si.nq, split, a.k_codes, a.v_codes, a.k_meta, a.v_meta,
+      PAGED ? 0 : pair * a.max_tokens, 0, sh);
   arrive_and_combine<G>(a, b, h, pl, &last_flag);
 }
 
@@ -1598,7 +1659,7 @@ __global__ void __launch_bounds__(256) decode_bf16(DecodeArgs a) {
   __shared__ int hist[WAVES][NSIZE];
   const bool zduty = blockIdx.x < (unsigned)(a.batch * a.hkv);
   const int zlen = zduty ? a.seq_lens[blockIdx.x / a.hkv] : 1;
-  const Item it = map_item(a, blockIdx.x, hist[threadIdx.x >> 6]);
+  const Item it = map_item(a, blockIdx.x, hist[threadIdx.x >> 6], false);
   if (zduty && zlen <= 0) {
     const int zb = blockIdx.x / a.hkv, zh = blockIdx.x % a.hkv;
     for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64)
@@ -1639,9 +1700,9 @@ hipError_t launch_bf16_g(const DecodeArgs& a, hipStream_t s) {
 // Launches one decode_split variant.  With events, hipExtLaunchKernel stamps
 // them with the start and end of the dispatch itself, so their difference
 // is the kernel's own duration.
-template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB>
+template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool TIER = false>
 void launch_one(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  const auto k = decode_split<KC, KM, KCH, VC, VM, G, PAGED, QB>;
+  const auto k = decode_split<KC, KM, KCH, VC, VM, G, PAGED, QB, TIER>;
   if (a.ev_begin)
     hipExtLaunchKernelGGL(k, grid, dim3(256), 0, s, (hipEvent_t)a.ev_begin, (hipEvent_t)a.ev_end, 0,
                           a);
@@ -1649,8 +1710,25 @@ void launch_one(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
 }
 
+// Pairs that run with a middle tier (contiguous, per token).
+template <int KC, int KM, bool KCH, int VC, int VM>
+constexpr bool tier_pair() {
+  return !KCH && KC == VC && KM == VM &&
+         ((KC == CK_I8 && KM == MK_F32) || (KC == CK_I4 && KM == MK_F32) ||
+          (KC == CK_U4 && KM == MK_F16Z) || (KC == CK_U2 && KM == MK_F16Z));
+}
+
 template <int KC, int KM, bool KCH, int VC, int VM, int G>
 void launch_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (tier_pair<KC, KM, KCH, VC, VM>()) {
+    if (a.mid.tokens) {
+      if (a.in_bf16)
+        launch_one<KC, KM, KCH, VC, VM, G, false, true, true>(a, grid, s);
+      else
+        launch_one<KC, KM, KCH, VC, VM, G, false, false, true>(a, grid, s);
+      return;
+    }
+  }
   if (a.paged) {
     if (a.in_bf16)
       launch_one<KC, KM, KCH, VC, VM, G, true, true>(a, grid, s);

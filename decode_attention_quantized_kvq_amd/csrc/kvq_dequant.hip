@@ -12,7 +12,8 @@
 //
 // Each value is the exact product code x scale (or scale x (code - zero),
 // code x u x S, code x channel scale) rounded once to bf16; bf16 window and
-// open-group tokens are copied.
+// open-group tokens are copied.  Positions of a middle tier are its int8
+// codes times their fp32 scales.
 
 #include <hip/hip_runtime.h>
 
@@ -61,11 +62,12 @@ __device__ inline int code_of(uint64_t raw, int bits, bool sgn, int e) {
 }
 
 // Writes features [f0, f0 + 8) of position p (< the sequence's length) of
-// (sequence, KV head) head, for K and for V.
+// (sequence, KV head) head, for K and for V.  Positions [0, na) hold the
+// cache's format, [na, nq) the middle tier, the rest bf16.
 __device__ inline void dequant_position(const DequantArgs& a, size_t head, int b, int h, int p,
-                                        int nq, int f0) {
+                                        int na, int nq, int f0) {
   size_t slot = 0;
-  if (p < nq) {
+  if (p < na) {
     if (a.paged) {
       int phys = a.block_table[(size_t)b * a.bt_stride + (p >> 4)];
       phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
@@ -82,6 +84,12 @@ __device__ inline void dequant_position(const DequantArgs& a, size_t head, int b
       const uint16_t* src = ring + (head * a.ring + (p % a.ring)) * D + f0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = src[e];
+    } else if (p >= na) {  // middle tier: int8 codes, one fp32 scale
+      const size_t ms = head * a.mid.slots + (p % a.mid.slots);
+      const uint64_t raw = codes8((w ? a.mid.v : a.mid.k) + ms * D, 8, f0);
+      const float s = (w ? a.mid.vs : a.mid.ks)[ms];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = bf16_of_product((float)code_of(raw, 8, true, e), s);
     } else {
       const TensorKind k = w ? a.vk : a.kk;
       const int rowb = D * bits_of(k.code) / 8;
@@ -136,17 +144,20 @@ __global__ void __launch_bounds__(256) dequant_kernel(DequantArgs a) {
   const int t = threadIdx.x >> 4, f0 = (threadIdx.x & 15) * 8;
   int len = a.seq_lens[b];
   len = len > 0 ? len : 0;
-  const int cap = (a.paged ? a.bt_stride * 16 : a.max_tokens) + a.window;
+  const int cap = (a.paged ? a.bt_stride * 16 : a.max_tokens) + a.window + a.mid.tokens;
   len = len < cap ? len : cap;
   const int lim = len < a.out_tokens ? len : a.out_tokens;
   const int m = len - a.window > 0 ? len - a.window : 0;
   const int nq = (m >> a.tgshift) << a.tgshift;  // quantized positions
+  // of which the cache's format holds whole blocks of 32 older than the middle tier
+  const int na = a.mid.tokens ? (nq - a.mid.tokens > 0 ? nq - a.mid.tokens : 0) / MID_BLOCK * MID_BLOCK
+                              : nq;
   const size_t head = (size_t)b * a.hkv + h;
 #pragma unroll 4
   for (int i = 0; i < TPW / 16; ++i) {
     const int p = blockIdx.x * TPW + 16 * i + t;
     if (p >= lim) break;
-    dequant_position(a, head, b, h, p, nq, f0);
+    dequant_position(a, head, b, h, p, na, nq, f0);
   }
 }
 

@@ -39,6 +39,25 @@ static size_t quantized_count(const kvq_config* c, size_t n) {
   return (n > (size_t)c->window ? n - c->window : 0) / g * g;
 }
 
+// Middle-tier slots per (sequence, head): M plus one block, since the tier
+// holds M .. M + 31 positions once full.
+static int mid_slots(const kvq_config* c) { return c->mid_tokens > 0 ? c->mid_tokens + MID_BLOCK : 0; }
+
+// (cache format, middle tier, bf16) positions of an n-token sequence.
+struct TierCounts {
+  size_t main, mid, bf16;
+};
+static TierCounts tier_counts(const kvq_config* c, size_t n) {
+  const size_t q = quantized_count(c, n);
+  TierCounts t{q, 0, n - q};
+  if (c->mid_tokens > 0) {
+    const size_t m = (size_t)c->mid_tokens;
+    t.main = (q > m ? q - m : 0) / MID_BLOCK * MID_BLOCK;
+    t.mid = q - t.main;
+  }
+  return t;
+}
+
 static size_t side_bytes(const kvq_tensor_fmt& f, int d) {
   if (f.bits == 16) return 0;
   if (f.axis != KVQ_AXIS_TOKEN) return size_t(4) * d;
@@ -98,7 +117,7 @@ static kvq_status check_config(const kvq_config* c, bool kernels) {
   if (!c) return KVQ_ERR_INVALID_ARG;
   if (c->num_layers < 1 || c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 ||
       c->head_dim < 1 || c->max_tokens < 0 || c->window < 0 || c->block_tokens < 0 ||
-      c->group_tokens < 0)
+      c->group_tokens < 0 || c->mid_tokens < 0 || c->mid_tokens % MID_BLOCK)
     return KVQ_ERR_INVALID_ARG;
   if (c->num_q_heads % c->num_kv_heads) return KVQ_ERR_INVALID_ARG;
   if (c->in_dtype != KVQ_DT_F32 && c->in_dtype != KVQ_DT_BF16) return KVQ_ERR_INVALID_ARG;
@@ -123,6 +142,16 @@ static kvq_status check_config(const kvq_config* c, bool kernels) {
   if (c->window % 16 || c->window > 256) return KVQ_ERR_UNSUPPORTED;
   if (token_group(c) > 1 && (kk.channel || kk.meta == MK_U8 || vk.meta == MK_U8))
     return KVQ_ERR_UNSUPPORTED;
+  if (c->mid_tokens > 0) {
+    // a middle tier runs with these per-token pairs, contiguous, per token
+    if (c->block_tokens || tg != 1) return KVQ_ERR_UNSUPPORTED;
+    const bool tier_ok =
+        (kk.code == CK_I8 && kk.meta == MK_F32 && vk.code == CK_I8 && vk.meta == MK_F32) ||
+        (kk.code == CK_I4 && kk.meta == MK_F32 && vk.code == CK_I4 && vk.meta == MK_F32) ||
+        (kk.code == CK_U4 && kk.meta == MK_F16Z && vk.code == CK_U4 && vk.meta == MK_F16Z) ||
+        (kk.code == CK_U2 && kk.meta == MK_F16Z && vk.code == CK_U2 && vk.meta == MK_F16Z);
+    if (!tier_ok) return KVQ_ERR_UNSUPPORTED;
+  }
   // The decode kernels are instantiated for these key/value pairs.
   const bool ok =
       (kk.code == CK_I8 && kk.meta == MK_F32 && vk.code == CK_I8 && vk.meta == MK_F32) ||
@@ -143,7 +172,7 @@ static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Quantized tokens per workgroup.  Aim at about two workgroups of four
 // waves per compute unit (256 CUs) over the whole batch.
 static int choose_split(const kvq_config* c, int max_seq_len) {
-  const long long nq = std::max(0, max_seq_len - c->window);
+  const long long nq = std::max(0, max_seq_len - c->window - c->mid_tokens);
   const long long pairs = (long long)c->batch * c->num_kv_heads;
   const long long target = 512;
   long long per = (nq * pairs + target - 1) / target;
@@ -163,7 +192,8 @@ static Plan make_plan(const kvq_config* c, int max_seq_len, int split_tokens) {
   const int nq = std::max(0, max_seq_len - c->window);
   // at least one split: its workgroup writes the zeros of empty sequences
   p.n_split = std::max(1, (nq + p.split_tokens - 1) / p.split_tokens);
-  p.nsp = p.n_split + (ring_slots(c) > 0 ? 1 : 0);
+  // partial rows per query head: the splits, the bf16 item, the middle tier
+  p.nsp = p.n_split + (ring_slots(c) > 0 ? 1 : 0) + (c->mid_tokens > 0 ? 1 : 0);
   const size_t rows = (size_t)c->batch * c->num_q_heads * p.nsp;
   p.o_bytes = round_up(rows * c->head_dim * sizeof(float), 256);
   p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
@@ -174,6 +204,7 @@ static Plan make_plan(const kvq_config* c, int max_seq_len, int split_tokens) {
 
 struct LayerSizes {  // bytes of one layer of each buffer
   size_t k_codes, v_codes, k_meta, v_meta, k_win, v_win, k_chan, v_super, k_super;
+  size_t mid_codes, mid_scale;  // each of K and V
 };
 
 static LayerSizes layer_sizes(const kvq_config* c) {
@@ -190,7 +221,26 @@ static LayerSizes layer_sizes(const kvq_config* c) {
   s.v_super = (c->value.bits != 16 && c->value.scale_fmt == KVQ_SCALE_U8_SUPER) ? heads * 4 : 0;
   s.k_super = (c->key.bits != 16 && c->key.axis == KVQ_AXIS_TOKEN &&
                c->key.scale_fmt == KVQ_SCALE_U8_SUPER) ? heads * 4 : 0;
+  s.mid_codes = heads * mid_slots(c) * c->head_dim;
+  s.mid_scale = heads * mid_slots(c) * 4;
   return s;
+}
+
+// The middle tier of one layer (tokens = 0 without one); false if a buffer
+// it needs is missing.
+static bool resolve_mid(const kvq_config* c, const kvq_cache* cache, int layer,
+                        const LayerSizes& s, MidTier* m) {
+  *m = MidTier{};
+  if (c->mid_tokens <= 0) return true;
+  if (!cache->k_mid || !cache->v_mid || !cache->k_mid_scale || !cache->v_mid_scale) return false;
+  const size_t L = (size_t)layer;
+  m->k = (uint8_t*)cache->k_mid + L * s.mid_codes;
+  m->v = (uint8_t*)cache->v_mid + L * s.mid_codes;
+  m->ks = (float*)((uint8_t*)cache->k_mid_scale + L * s.mid_scale);
+  m->vs = (float*)((uint8_t*)cache->v_mid_scale + L * s.mid_scale);
+  m->tokens = c->mid_tokens;
+  m->slots = mid_slots(c);
+  return true;
 }
 
 static bool resolve_layer(const kvq_config* c, const kvq_cache* cache, int layer,
@@ -256,6 +306,8 @@ kvq_status kvq_get_buffer_sizes(const kvq_config* cfg, kvq_buffer_sizes* out) {
   out->k_chan_scale = L * s.k_chan;
   out->v_super = L * s.v_super;
   out->k_super = L * s.k_super;
+  out->k_mid = out->v_mid = L * s.mid_codes;
+  out->k_mid_scale = out->v_mid_scale = L * s.mid_scale;
   return KVQ_OK;
 }
 
@@ -270,13 +322,16 @@ size_t kvq_cache_bytes(const kvq_config* cfg, const int32_t* host_seq_lens, kvq_
   const size_t mk = meta_bytes(cfg->key), mv = meta_bytes(cfg->value);  // per group
   const size_t side = side_bytes(cfg->key, cfg->head_dim) + side_bytes(cfg->value, cfg->head_dim);
   const size_t g = (size_t)token_group(cfg), ring = (size_t)ring_slots(cfg);
+  const size_t mslots = (size_t)mid_slots(cfg), mrow = 2 * D, mmeta = 2 * 4;  // int8 K, V + fp32 scales
   kvq_bytes b{};
   for (int i = 0; i < cfg->batch; ++i) {
     const size_t n = host_seq_lens ? (size_t)std::max(0, host_seq_lens[i]) : (size_t)cfg->max_tokens;
-    const size_t nq = quantized_count(cfg, n);
-    const size_t nw = n - nq;
-    b.payload += L * H * nq * (rk + rv);  // 2 L H_kv D T b with per-tensor b
-    b.metadata += L * H * (nq / g * (mk + mv) + side);
+    const TierCounts t = tier_counts(cfg, n);
+    const size_t nq = t.main, nw = t.bf16;
+    // 2 L H_kv D T b with per-tensor b, per tier
+    b.payload += L * H * (nq * (rk + rv) + t.mid * mrow);
+    b.metadata += L * H * (nq / g * (mk + mv) + t.mid * mmeta + side);
+    if (mslots) b.padding += L * H * (mslots > t.mid ? mslots - t.mid : 0) * (mrow + mmeta);
     b.window += L * H * nw * D * 2 * 2;
     size_t alloc_q;
     if (cfg->block_tokens)
@@ -345,6 +400,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int lay
   a.bt_stride = cfg->max_blocks_per_seq;
   int g;
   set_groups(cfg, &g, &a.tgshift, &a.ring);
+  if (!resolve_mid(cfg, cache, layer, s, &a.mid)) return KVQ_ERR_INVALID_ARG;
   return launch_dequant(a, stream);
 }
 
@@ -388,6 +444,7 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
   a.num_blocks = cfg->num_blocks;
   a.bt_stride = cfg->max_blocks_per_seq;
   a.in_bf16 = cfg->in_dtype == KVQ_DT_BF16;
+  if (!resolve_mid(cfg, cache, layer, s, &a.mid)) return KVQ_ERR_INVALID_ARG;
   return launch_append(a, stream);
 }
 
@@ -457,6 +514,7 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   a.qbits = qbits;
   a.ev_begin = opts ? opts->split_begin_event : nullptr;
   a.ev_end = opts ? opts->split_end_event : nullptr;
+  if (!resolve_mid(cfg, cache, layer, s, &a.mid)) return KVQ_ERR_INVALID_ARG;
   return launch_decode(a, stream);
 }
 

@@ -45,6 +45,19 @@ int meta_bytes(const kvq_tensor_fmt& f);
 // KVQ_ERR_UNSUPPORTED (for the kernels).  is_key: keys accept channel axis.
 kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out);
 
+// Middle tier of a cache (int8 codes, one fp32 scale per token; positions
+// [A, Q) with Q = max(len - window, 0), A = floor(max(Q - tokens, 0) / 32) 32),
+// resolved to one layer; tokens == 0: none.
+constexpr int MID_BLOCK = 32;
+struct MidTier {
+  uint8_t* k;       // [B][H_kv][slots][D] int8
+  uint8_t* v;
+  float* ks;        // [B][H_kv][slots] fp32
+  float* vs;
+  int tokens;       // M
+  int slots;        // M + 32; position p sits in slot p % slots
+};
+
 // Everything a quantize-append launch needs, resolved to one layer.
 struct AppendArgs {
   const void* k_new;
@@ -65,6 +78,7 @@ struct AppendArgs {
   int in_bf16;
   int tgroup, tgshift;  // token group size g (1 = per token) and log2 g
   int ring;           // bf16 ring slots per (sequence, head): window (+ g if g > 1)
+  MidTier mid;
   TensorKind kk, vk;
 };
 
@@ -91,9 +105,10 @@ struct DecodeArgs {
   int tgroup, tgshift;  // token group size g (1 = per token) and log2 g
   int ring;           // bf16 ring slots per (sequence, head): window (+ g if g > 1)
   int qbits;          // 0: exact query limbs; 8: the query quantized to int8 per head
+  MidTier mid;
   int split_tokens;  // quantized tokens per workgroup (multiple of 128)
   int n_split;       // workgroups over the quantized tokens
-  int nsp;           // n_split + 1 if there is a window
+  int nsp;           // n_split, + 1 if there is a window, + 1 with a middle tier
   int in_bf16;
   TensorKind kk, vk;
   void* ev_begin;    // hipEvent_t recorded before the split kernel, or null
@@ -118,6 +133,7 @@ struct DequantArgs {
   int out_tokens;
   int batch, hkv, max_tokens, window, paged, num_blocks, bt_stride;
   int tgshift, ring;
+  MidTier mid;
   TensorKind kk, vk;
 };
 

@@ -48,7 +48,7 @@ class Config(ctypes.Structure):
                 ("key", TensorFmt), ("value", TensorFmt), ("window", ctypes.c_int),
                 ("block_tokens", ctypes.c_int), ("num_blocks", ctypes.c_int),
                 ("max_blocks_per_seq", ctypes.c_int), ("in_dtype", ctypes.c_int),
-                ("group_tokens", ctypes.c_int)]
+                ("group_tokens", ctypes.c_int), ("mid_tokens", ctypes.c_int)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -57,7 +57,9 @@ class CacheDesc(ctypes.Structure):
                 ("k_win", ctypes.c_void_p), ("v_win", ctypes.c_void_p),
                 ("k_chan_scale", ctypes.c_void_p), ("v_super", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
-                ("k_super", ctypes.c_void_p)]
+                ("k_super", ctypes.c_void_p), ("k_mid", ctypes.c_void_p),
+                ("v_mid", ctypes.c_void_p), ("k_mid_scale", ctypes.c_void_p),
+                ("v_mid_scale", ctypes.c_void_p)]
 
 
 class Bytes(ctypes.Structure):
@@ -67,7 +69,8 @@ class Bytes(ctypes.Structure):
 class BufferSizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("k_codes", "v_codes", "k_meta", "v_meta",
                                                 "k_win", "v_win", "k_chan_scale", "v_super",
-                                                "k_super")]
+                                                "k_super", "k_mid", "v_mid", "k_mid_scale",
+                                                "v_mid_scale")]
 
 
 class DecodeOpts(ctypes.Structure):
@@ -135,10 +138,11 @@ def tensor_fmt(spec: dict) -> TensorFmt:
 def make_config(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                 max_tokens: int, key: dict, value: dict, window: int = 0,
                 block_tokens: int = 0, num_blocks: int = 0, max_blocks_per_seq: int = 0,
-                in_dtype: str = "bf16", num_layers: int = 1, group_tokens: int = 1) -> Config:
+                in_dtype: str = "bf16", num_layers: int = 1, group_tokens: int = 1,
+                mid_tokens: int = 0) -> Config:
     return Config(num_layers, batch, num_q_heads, num_kv_heads, head_dim, max_tokens,
                   tensor_fmt(key), tensor_fmt(value), window, block_tokens, num_blocks,
-                  max_blocks_per_seq, DTYPE[in_dtype], group_tokens)
+                  max_blocks_per_seq, DTYPE[in_dtype], group_tokens, mid_tokens)
 
 
 def validate(cfg: Config) -> int:
@@ -224,7 +228,9 @@ class KvqCache:
         return CacheDesc(_ptr(b["k_codes"]), _ptr(b["v_codes"]), _ptr(b["k_meta"]),
                          _ptr(b["v_meta"]), _ptr(b["k_win"]), _ptr(b["v_win"]),
                          _ptr(b["k_chan_scale"]), _ptr(b["v_super"]),
-                         _ptr(self.block_table), _ptr(self.seq_lens), _ptr(b["k_super"]))
+                         _ptr(self.block_table), _ptr(self.seq_lens), _ptr(b["k_super"]),
+                         _ptr(b["k_mid"]), _ptr(b["v_mid"]), _ptr(b["k_mid_scale"]),
+                         _ptr(b["v_mid_scale"]))
 
 
 def _check_input(t: torch.Tensor, cfg: Config, shape, what: str):

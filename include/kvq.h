@@ -71,6 +71,9 @@
  *    block_table[b][p / 16], slot p % 16
  *  ring   [L][B][H_kv][R][D] bf16 with R = window (+ g if g > 1); position
  *    p sits in slot p % R
+ *  middle tier (mid_tokens = M > 0): codes [L][B][H_kv][M + 32][D] int8 and
+ *    scales [L][B][H_kv][M + 32] fp32, for K and V each; position p sits in
+ *    slot p % (M + 32)
  *  k_chan_scale [L][B][H_kv][D] fp32;  k_super, v_super [L][B][H_kv] fp32
  *  code bytes: bits 16 stores the bf16 values themselves (2 bytes each);
  *    int8 codes as two's complement bytes (unsigned bytes with a
@@ -87,6 +90,14 @@
  *  group not yet complete) are kept as bf16 in the ring.  g = group_tokens
  *  (1 when 0).  Metadata element j of a (sequence, head) belongs to
  *  positions [j g, j g + g).
+ *  With a middle tier of M positions, Q = max(len - window, 0) and
+ *  A = floor(max(Q - M, 0) / 32) * 32: positions [0, A) hold the cache's
+ *  format, [A, Q) the middle tier, [Q, len) the bf16 ring.  A token leaving
+ *  the window is quantized into the middle tier (int8, symmetric, fp32 scale,
+ *  by the rounding contract above); a token leaving the middle tier, 32
+ *  positions at a time, is re-quantized to the cache's format from its exact
+ *  middle-tier value c * s.  The cache's format is then per token, contiguous,
+ *  without token groups or 8-bit scale codes; max_tokens bounds A.
  *
  * Error behaviour: every call validates its arguments on the host before
  * launching anything and returns a kvq_status; nothing is thrown across the
@@ -172,6 +183,12 @@ typedef struct {
                               consecutive positions of a sequence and head
                               (P3, "Per-token scales and where they can
                               live": several tokens under one scale) */
+  int mid_tokens;          /* 0 = none; else a multiple of 32: a middle tier
+                              of that many positions between the window and
+                              the cache's format, stored as int8 with one fp32
+                              scale per token, for keys and values (precision
+                              by recency, P3 "Precision floors and mixed cache
+                              formats"; layout and rules below) */
 } kvq_config;
 
 /* Device pointers of one cache (all layers).  Unused buffers may be NULL. */
@@ -190,6 +207,10 @@ typedef struct {
                               reads it */
   void* k_super;           /* per-head key super-scales (keys with an 8-bit
                               scale code) */
+  void* k_mid;             /* middle tier: int8 key codes, value codes, and */
+  void* v_mid;             /* their fp32 scales (mid_tokens > 0 only) */
+  void* k_mid_scale;
+  void* v_mid_scale;
 } kvq_cache;
 
 /* Byte breakdown of a cache (P2, "Metadata and block layout remain part of
@@ -207,6 +228,7 @@ typedef struct {
 typedef struct {
   size_t k_codes, v_codes, k_meta, v_meta, k_win, v_win, k_chan_scale, v_super;
   size_t k_super;
+  size_t k_mid, v_mid, k_mid_scale, v_mid_scale;
 } kvq_buffer_sizes;
 
 /* Human-readable name of a status.  Never NULL. */
@@ -221,7 +243,10 @@ const char* kvq_status_string(kvq_status s);
  *   int2 f32; int2 f32                      int2 u8 super; int2 u8 super
  *   uint2 f16 scale + zero; the same        bf16 (bits 16); bf16, contiguous,
  *                                           no window, no token groups
- * An 8-bit scale code (u8 super) or per-channel keys exclude token groups. */
+ * An 8-bit scale code (u8 super) or per-channel keys exclude token groups.
+ * A middle tier (mid_tokens > 0) runs with the pairs int8 f32 / int8 f32,
+ * int4 f32 / int4 f32, uint4 f16 scale + zero (both) and uint2 f16 scale +
+ * zero (both), contiguous, per token, without token groups. */
 kvq_status kvq_validate(const kvq_config* cfg);
 
 /* Fills *out with the byte size of each buffer of the layout above. */

@@ -56,7 +56,7 @@ def make_config(wl, lens, num_blocks=0, max_blocks=0):
     return K.make_config(batch=wl["batch"], num_q_heads=wl["hq"], num_kv_heads=wl["hkv"],
                          head_dim=wl["d"], max_tokens=wl["tokens"], key=wl["key"],
                          value=wl["value"], window=wl["window"], block_tokens=wl["block_tokens"],
-                         group_tokens=wl.get("group", 1),
+                         group_tokens=wl.get("group", 1), mid_tokens=wl.get("mid", 0),
                          num_blocks=num_blocks, max_blocks_per_seq=max_blocks,
                          in_dtype=wl["in_dtype"])
 
@@ -76,7 +76,7 @@ def build(wl: dict, lens: List[int], decode_steps: int = 0, replica: int = 0,
     assert K.validate(cfg) == K.KVQ_OK
     cache = K.KvqCache(cfg, "cuda", None if table is None else torch.from_numpy(table))
     orc = O.OracleCache(B, H, D, oracle_fmt(wl["key"]), oracle_fmt(wl["value"]), wl["window"],
-                        group=wl.get("group", 1)) if oracle else None
+                        group=wl.get("group", 1), mid=wl.get("mid", 0)) if oracle else None
     full = {}
     for b in range(B):
         for h in range(H):
@@ -257,6 +257,18 @@ def check_records(bt: Built, b: int, h: int):
                 assert np.array_equal(_bits(dev["s"]), _bits(st.s[h])), f"{t} scales differ b={b} h={h}"
             if "z" in dev:
                 assert np.array_equal(_bits(dev["z"]), _bits(st.z[h])), f"{t} zero points differ"
+        M = bt.wl.get("mid", 0)
+        if M:
+            # middle tier: int8 codes and fp32 scales, position p in slot p % (M + 32)
+            mc, ms = bt.oracle.mid_stored(b, t)
+            nm = mc.shape[1]
+            S, D = O.mid_ring_slots(M), bt.wl["d"]
+            head = b * bt.cfg.num_kv_heads + h
+            pos = np.arange(n, n + nm) % S
+            codes = host(bt.cache.buffers[f"{t}_mid"]).view(np.int8).reshape(-1, S, D)[head][pos]
+            scales = host(bt.cache.buffers[f"{t}_mid_scale"]).view(np.float32).reshape(-1, S)[head][pos]
+            assert np.array_equal(codes.astype(np.int32), mc[h]), f"{t} middle-tier codes differ b={b} h={h}"
+            assert np.array_equal(_bits(scales), _bits(ms[h])), f"{t} middle-tier scales differ b={b} h={h}"
         R = ring_slots(bt.wl)
         if R:
             # ring slot of position p is p % R

@@ -172,6 +172,51 @@ def test_token_groups(g, window, paged, fmt):
     full_check(bt, steps=(0,), split_tokens=128, records=False)
 
 
+TIER_SPECS = {
+    "i8": dict(bits=8), "i4": dict(bits=4),
+    "u4z": dict(bits=4, zero_point=True, scale="f16"),
+    "u2z": dict(bits=2, zero_point=True, scale="f16"),
+}
+
+
+@pytest.mark.parametrize("fmt,window,mid,hq", [
+    ("u4z", 16, 64, 32), ("i4", 0, 32, 16), ("u2z", 128, 256, 32), ("i8", 32, 96, 8),
+    ("u4z", 0, 512, 4),
+])
+def test_middle_tier(fmt, window, mid, hq):
+    """Precision by recency beyond one window: the newest W tokens in bf16,
+    the next M (+ up to 31) as int8 with fp32 scales, the older ones in the
+    cache's format re-quantized from their int8 values.  Prefills in two
+    ragged appends then single-token appends move tokens across both edges;
+    lengths from empty to past several tiles.  Records of all three tiers
+    bit for bit, outputs within the bar at two split sizes."""
+    H.log(f"case: middle tier {fmt} window={window} mid={mid} hq={hq}")
+    spec = TIER_SPECS[fmt]
+    wl = synth.workload(2, batch=5, hq=hq, hkv=4, tokens=1024, key=spec, value=spec,
+                        window=window, mid=mid)
+    lens = [1000, window + mid + 33, window + mid + 31, 97, 0]
+    bt = H.build(wl, lens, decode_steps=5, chunks=2)
+    full_check(bt, steps=(0, 1))
+    full_check(bt, steps=(0,), split_tokens=128, records=False)
+
+
+def test_middle_tier_dequantize():
+    """kvq_dequantize over a cache with a middle tier: each tier's exact
+    values rounded once to bf16, bit for bit."""
+    H.log("case: middle tier dequantize")
+    spec = TIER_SPECS["u4z"]
+    wl = synth.workload(2, batch=2, hq=8, hkv=2, tokens=512, key=spec, value=spec, window=16, mid=64)
+    lens = [500, 150]
+    bt = H.build(wl, lens, decode_steps=3)
+    c16 = K.dequantize(bt.cache, 0, 512)
+    torch.cuda.synchronize()
+    kd = H.host(c16.buffers["k_codes"]).view(np.uint16).reshape(2, 2, 512, 128)
+    for b in range(2):
+        kb, _ = H.O.dequantized_bf16(bt.oracle, b)
+        ref16 = (kb.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(kd[b, :, :lens[b]], ref16), f"dequantized keys differ b={b}"
+
+
 @pytest.mark.parametrize("wid,over,lens", [
     (2, dict(batch=3, tokens=1024), [1000, 333, 0]),
     (3, dict(batch=2, tokens=512), [500, 77]),

@@ -73,6 +73,27 @@ def test_cache_bytes_match_oracle(wid):
     assert K.decode_traffic_bytes(cfg, lens) == traffic
 
 
+@pytest.mark.parametrize("window,mid", [(0, 32), (16, 64), (128, 256)])
+def test_middle_tier_bytes_match_oracle(window, mid):
+    """Byte accounting and buffer sizes of a cache with a middle tier: the
+    int8 codes and fp32 scales of the tier, and its unused ring slots."""
+    spec = dict(bits=4, zero_point=True, scale="f16")
+    wl = synth.workload(2, key=spec, value=spec, window=window, mid=mid, batch=4, tokens=2048)
+    lens = [0, window + mid + 31, window + mid + 32, 2000]
+    cfg = cfg_of(wl, mid_tokens=mid, num_layers=3)
+    got = K.cache_bytes(cfg, lens)
+    want = O.cache_bytes(oracle_fmt(spec), oracle_fmt(spec), 3, wl["hkv"], wl["d"], lens, window,
+                         0, wl["tokens"], mid=mid)
+    assert got == want
+    assert K.decode_traffic_bytes(cfg, lens) == O.decode_traffic(
+        oracle_fmt(spec), oracle_fmt(spec), wl["hkv"], wl["d"], lens, window, mid=mid)
+    sz = K.buffer_sizes(cfg)
+    slots = mid + 32
+    assert sz.k_mid == sz.v_mid == 3 * 4 * wl["hkv"] * slots * 128
+    assert sz.k_mid_scale == sz.v_mid_scale == 3 * 4 * wl["hkv"] * slots * 4
+    assert K.buffer_sizes(cfg_of(wl)).k_mid == 0
+
+
 def test_cache_bytes_metadata_cases():
     """The overhead cases the metadata section prices (scale; scale + zero
     point; 4-bit; 2-bit), through the C accounting, several layers."""
@@ -137,6 +158,17 @@ def test_validation_errors():
         (dict(window=20), K.KVQ_ERR_UNSUPPORTED),
         (dict(block_tokens=16, num_blocks=0, max_blocks_per_seq=4), K.KVQ_ERR_INVALID_ARG),
         (dict(block_tokens=32, num_blocks=8, max_blocks_per_seq=4), K.KVQ_ERR_UNSUPPORTED),
+        (dict(mid_tokens=-32), K.KVQ_ERR_INVALID_ARG),
+        (dict(mid_tokens=48), K.KVQ_ERR_INVALID_ARG),                    # not a multiple of 32
+        (dict(mid_tokens=32, block_tokens=16, num_blocks=8, max_blocks_per_seq=4),
+         K.KVQ_ERR_UNSUPPORTED),                                         # middle tier: contiguous
+        (dict(mid_tokens=32, group_tokens=2), K.KVQ_ERR_UNSUPPORTED),
+        (dict(mid_tokens=32, key=dict(bits=8), value=dict(bits=4)), K.KVQ_ERR_UNSUPPORTED),
+        (dict(mid_tokens=32, key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super")),
+         K.KVQ_ERR_UNSUPPORTED),
+        (dict(mid_tokens=32, key=dict(bits=8, axis="channel"), value=dict(bits=4, scale="u8_super")),
+         K.KVQ_ERR_UNSUPPORTED),
+        (dict(mid_tokens=32, key=dict(bits=16), value=dict(bits=16)), K.KVQ_ERR_UNSUPPORTED),
     ]
     for over, want in bad:
         cfg = K.make_config(**{**base, **over})
@@ -149,6 +181,12 @@ def test_validation_errors():
         dict(key=dict(bits=2), value=dict(bits=2)),
         dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super")),
         dict(key=dict(bits=2, zero_point=True, scale="f16"),
+             value=dict(bits=2, zero_point=True, scale="f16")),
+        dict(mid_tokens=32),
+        dict(mid_tokens=256, window=16, key=dict(bits=4), value=dict(bits=4)),
+        dict(mid_tokens=64, key=dict(bits=4, zero_point=True, scale="f16"),
+             value=dict(bits=4, zero_point=True, scale="f16")),
+        dict(mid_tokens=64, window=128, key=dict(bits=2, zero_point=True, scale="f16"),
              value=dict(bits=2, zero_point=True, scale="f16")),
     ]
     for over in good:
