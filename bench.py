@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2, help="workload 1..7 (default 2: GQA int8)")
+    p.add_argument("--config", type=int, default=2, help="workload 1..8 (default 2: GQA int8)")
     p.add_argument("--replicas", type=int, default=0, help="cache copies (0 = enough for 1 GiB)")
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     p.add_argument("--query-bits", type=int, default=0,
@@ -92,7 +92,7 @@ def build_cache(wl, lens, K, synth, torch):
                         head_dim=wl["d"], max_tokens=wl["tokens"], key=wl["key"],
                         value=wl["value"], window=wl["window"], block_tokens=wl["block_tokens"],
                         num_blocks=nb, max_blocks_per_seq=mb, in_dtype=wl["in_dtype"],
-                        group_tokens=wl.get("group", 1))
+                        group_tokens=wl.get("group", 1), mid_tokens=wl.get("mid", 0))
     st = K.validate(cfg)
     if st != K.KVQ_OK:
         raise SystemExit(f"workload not supported: {K.status_string(st)}")
@@ -147,7 +147,7 @@ def cpu_baseline(wl, lens, seconds: float):
             else:
                 k, v = synth.kv_tokens(wl, b, h, n)
                 cache = O.OracleCache(1, 1, wl["d"], fmt(wl["key"]), fmt(wl["value"]), wl["window"],
-                                      group=wl.get("group", 1))
+                                      group=wl.get("group", 1), mid=wl.get("mid", 0))
                 cache.append(0, k[None], v[None])
                 if keep:
                     built[gi] = cache
@@ -156,13 +156,14 @@ def cpu_baseline(wl, lens, seconds: float):
             cache.attend(0, q)               # dequantize + attend, fp64
             elapsed += time.perf_counter() - t0
             done_bytes += O.decode_traffic(fmt(wl["key"]), fmt(wl["value"]), 1, wl["d"], [n],
-                                           wl["window"])
+                                           wl["window"], wl.get("group", 1), wl.get("mid", 0))
             done_tokens += n
             n_groups += 1
             if elapsed >= seconds:
                 break
         passes += 1
-    total_bytes = O.decode_traffic(fmt(wl["key"]), fmt(wl["value"]), wl["hkv"], wl["d"], lens, wl["window"])
+    total_bytes = O.decode_traffic(fmt(wl["key"]), fmt(wl["value"]), wl["hkv"], wl["d"], lens,
+                                   wl["window"], wl.get("group", 1), wl.get("mid", 0))
     step_s = elapsed * total_bytes / done_bytes
     return {
         "value": round(total_bytes / step_s / 1e9, 3), "unit": "GB/s",
@@ -360,7 +361,8 @@ def main():
         "config": {"workload": wl["name"], "batch": wl["batch"], "q_heads": wl["hq"],
                    "kv_heads": wl["hkv"], "head_dim": wl["d"], "tokens": max_len,
                    "key": wl["key"], "value": wl["value"], "window": wl["window"],
-                   "block_tokens": wl["block_tokens"], "replicas": reps,
+                   "block_tokens": wl["block_tokens"], "group_tokens": wl.get("group", 1),
+                   "mid_tokens": wl.get("mid", 0), "replicas": reps,
                    "split_tokens": args.split or "auto", "query_bits": args.query_bits,
                    "kernel_sources": sha},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,

@@ -27,6 +27,12 @@ synthetic):
                  values uint2 with one fp16 scale + zero point per 16-token
                  group (the other 2-bit remedy of the same section: several
                  tokens under one scale).
+  8 int4_tiered  batch 32, 32/8 heads, 8192 tokens, same values as 2; the
+                 newest 128 in bf16, the next 1024 (to 1055) as int8 with fp32
+                 scales, the older ones uint4 with fp16 scale + zero point
+                 (precision that varies with recency, "KV Cache Quantization
+                 and Per-Token Scale Placement", section "Precision floors and
+                 mixed cache formats").
 
 Recipe: every draw comes from ``np.random.default_rng(SeedSequence(key))``
 with a key that names the workload, the replica and the tensor, so any
@@ -77,6 +83,11 @@ WORKLOADS: Dict[int, dict] = {
             key=dict(bits=2, axis="token", zero_point=True, scale="f16"),
             value=dict(bits=2, axis="token", zero_point=True, scale="f16"),
             window=0, block_tokens=0, outlier_keys=4, value_dist="normal", group=16),
+    8: dict(name="int4_tiered", batch=32, hq=32, hkv=8, d=128, tokens=8192,
+            lengths=None, in_dtype="bf16",
+            key=dict(bits=4, axis="token", zero_point=True, scale="f16"),
+            value=dict(bits=4, axis="token", zero_point=True, scale="f16"),
+            window=128, block_tokens=0, outlier_keys=4, value_dist="normal", mid=1024),
 }
 
 

@@ -239,6 +239,22 @@ def _bits(x) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(x)).view(np.uint8)
 
 
+def check_mid(bt: Built, orc, t: str, b: int, h: int, ob: int, oh: int):
+    """Middle tier of (b, h) on the device against sequence ob, head oh of the
+    oracle cache orc: int8 codes and fp32 scales bit for bit, position p in
+    ring slot p % (M + 32)."""
+    M = bt.wl["mid"]
+    n_main = orc.stored(ob, t).codes.shape[1]
+    mc, ms = orc.mid_stored(ob, t)
+    S, D = O.mid_ring_slots(M), bt.wl["d"]
+    head = b * bt.cfg.num_kv_heads + h
+    pos = np.arange(n_main, n_main + mc.shape[1]) % S
+    codes = host(bt.cache.buffers[f"{t}_mid"]).view(np.int8).reshape(-1, S, D)[head][pos]
+    scales = host(bt.cache.buffers[f"{t}_mid_scale"]).view(np.float32).reshape(-1, S)[head][pos]
+    assert np.array_equal(codes.astype(np.int32), mc[oh]), f"{t} middle-tier codes differ b={b} h={h}"
+    assert np.array_equal(_bits(scales), _bits(ms[oh])), f"{t} middle-tier scales differ b={b} h={h}"
+
+
 def check_records(bt: Built, b: int, h: int):
     """Bit-exact codes and metadata of sequence b, KV head h."""
     for t in ("k", "v"):
@@ -257,18 +273,8 @@ def check_records(bt: Built, b: int, h: int):
                 assert np.array_equal(_bits(dev["s"]), _bits(st.s[h])), f"{t} scales differ b={b} h={h}"
             if "z" in dev:
                 assert np.array_equal(_bits(dev["z"]), _bits(st.z[h])), f"{t} zero points differ"
-        M = bt.wl.get("mid", 0)
-        if M:
-            # middle tier: int8 codes and fp32 scales, position p in slot p % (M + 32)
-            mc, ms = bt.oracle.mid_stored(b, t)
-            nm = mc.shape[1]
-            S, D = O.mid_ring_slots(M), bt.wl["d"]
-            head = b * bt.cfg.num_kv_heads + h
-            pos = np.arange(n, n + nm) % S
-            codes = host(bt.cache.buffers[f"{t}_mid"]).view(np.int8).reshape(-1, S, D)[head][pos]
-            scales = host(bt.cache.buffers[f"{t}_mid_scale"]).view(np.float32).reshape(-1, S)[head][pos]
-            assert np.array_equal(codes.astype(np.int32), mc[h]), f"{t} middle-tier codes differ b={b} h={h}"
-            assert np.array_equal(_bits(scales), _bits(ms[h])), f"{t} middle-tier scales differ b={b} h={h}"
+        if bt.wl.get("mid", 0):
+            check_mid(bt, bt.oracle, t, b, h, b, h)
         R = ring_slots(bt.wl)
         if R:
             # ring slot of position p is p % R

@@ -39,7 +39,7 @@ def test_tiny_full_size():
     full_check(bt, steps=(0, 1, 2))
 
 
-@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6, 7, 8])
 def test_full_size_sampled(wid):
     """Each workload at its full size, decoded in the launch configuration the
     benchmark times (library-chosen split).  For sampled (sequence, KV head)
@@ -63,9 +63,12 @@ def test_full_size_sampled(wid):
         n = lens[b]
         kx = bt.inputs["k"][b, h, :n].float().cpu().numpy().astype(np.float64)
         vx = bt.inputs["v"][b, h, :n].float().cpu().numpy().astype(np.float64)
-        orc = H.O.OracleCache(1, 1, wl["d"], kf, vf, wl["window"], group=wl.get("group", 1))
+        orc = H.O.OracleCache(1, 1, wl["d"], kf, vf, wl["window"], group=wl.get("group", 1),
+                              mid=wl.get("mid", 0))
         orc.append(0, kx[None], vx[None])
         for t in ("k", "v"):
+            if wl.get("mid", 0):
+                H.check_mid(bt, orc, t, b, h, 0, 0)
             st = orc.stored(0, t)
             m = st.codes.shape[1]
             if m:
@@ -92,7 +95,8 @@ def test_full_size_sampled(wid):
     (5, dict(batch=2, tokens=1024), [1000, 613], 4, 1),
     (6, dict(batch=2, tokens=1024), [1000, 555], 3, 2),
     (7, dict(batch=2, tokens=1024), [1000, 557], 19, 2),
-], ids=["w2", "w3", "w4", "w5", "w6", "w7"])
+    (8, dict(batch=2, tokens=2048), [2000, 1180], 35, 2),
+], ids=["w2", "w3", "w4", "w5", "w6", "w7", "w8"])
 def test_workload_reduced(wid, over, lens, decode_steps, chunks):
     """Each workload's formats at a size the oracle finishes in seconds, with
     ragged lengths, a prefill in one or two appends, then decode appends."""

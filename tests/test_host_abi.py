@@ -40,7 +40,7 @@ def cfg_of(wl, **kw):
     d = dict(batch=wl["batch"], num_q_heads=wl["hq"], num_kv_heads=wl["hkv"], head_dim=wl["d"],
              max_tokens=wl["tokens"], key=wl["key"], value=wl["value"], window=wl["window"],
              block_tokens=wl["block_tokens"], in_dtype=wl["in_dtype"],
-             group_tokens=wl.get("group", 1))
+             group_tokens=wl.get("group", 1), mid_tokens=wl.get("mid", 0))
     if wl["block_tokens"]:
         d["num_blocks"] = 100
         d["max_blocks_per_seq"] = -(-(wl["tokens"] - wl["window"]) // 16)
@@ -53,12 +53,12 @@ def oracle_fmt(spec):
                           spec.get("scale", "f32"))
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_workloads_validate(wid):
     assert K.validate(cfg_of(synth.workload(wid))) == K.KVQ_OK
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_cache_bytes_match_oracle(wid):
     wl = synth.workload(wid)
     lens = synth.seq_lengths(wl)
@@ -66,10 +66,11 @@ def test_cache_bytes_match_oracle(wid):
     got = K.cache_bytes(cfg, lens)
     want = O.cache_bytes(oracle_fmt(wl["key"]), oracle_fmt(wl["value"]), 1, wl["hkv"], wl["d"],
                          lens, wl["window"], wl["block_tokens"],
-                         None if wl["block_tokens"] else wl["tokens"], group=wl.get("group", 1))
+                         None if wl["block_tokens"] else wl["tokens"], group=wl.get("group", 1),
+                         mid=wl.get("mid", 0))
     assert got == want
     traffic = O.decode_traffic(oracle_fmt(wl["key"]), oracle_fmt(wl["value"]), wl["hkv"], wl["d"],
-                               lens, wl["window"], group=wl.get("group", 1))
+                               lens, wl["window"], group=wl.get("group", 1), mid=wl.get("mid", 0))
     assert K.decode_traffic_bytes(cfg, lens) == traffic
 
 
@@ -91,7 +92,7 @@ def test_middle_tier_bytes_match_oracle(window, mid):
     slots = mid + 32
     assert sz.k_mid == sz.v_mid == 3 * 4 * wl["hkv"] * slots * 128
     assert sz.k_mid_scale == sz.v_mid_scale == 3 * 4 * wl["hkv"] * slots * 4
-    assert K.buffer_sizes(cfg_of(wl)).k_mid == 0
+    assert K.buffer_sizes(cfg_of(wl, mid_tokens=0)).k_mid == 0
 
 
 def test_cache_bytes_metadata_cases():
