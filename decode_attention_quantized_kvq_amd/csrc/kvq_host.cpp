@@ -169,15 +169,24 @@ static kvq_status check_config(const kvq_config* c, bool kernels) {
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Quantized tokens per workgroup.  Aim at about two workgroups of four
-// waves per compute unit (256 CUs) over the whole batch.
+// Quantized tokens per workgroup, aiming at one round of workgroups of four
+// waves over the 256 compute units (a second round pays each workgroup's
+// fixed start and merge again; on one MI355X it measured slower):
+//  - codes of at most 4 bits on both sides, no middle tier: 768 workgroups.
+//    Those kernels hold about 150 VGPRs per lane, three waves per SIMD, and
+//    their VALU-heavy tiles need the third wave to hide load latency.
+//  - otherwise 512.  Kernels with 8-bit per-token codes or the middle tier's
+//    second tile loop hold about 200 VGPRs (two waves per SIMD); per-channel
+//    8-bit keys over long caches measured faster with fewer, longer splits.
+// A paged wave addresses at most 128 blocks, so paged splits stop at 8192.
 static int choose_split(const kvq_config* c, int max_seq_len) {
   const long long nq = std::max(0, max_seq_len - c->window - c->mid_tokens);
   const long long pairs = (long long)c->batch * c->num_kv_heads;
-  const long long target = 512;
+  const bool narrow = c->key.bits <= 4 && c->value.bits <= 4 && c->mid_tokens == 0;
+  const long long target = narrow ? 768 : 512;
   long long per = (nq * pairs + target - 1) / target;
   per = (long long)round_up((size_t)std::max<long long>(per, 1), 128);
-  per = std::min<long long>(std::max<long long>(per, 256), 8192);
+  per = std::min<long long>(std::max<long long>(per, 256), c->block_tokens ? 8192 : 16384);
   return (int)per;
 }
 
@@ -198,7 +207,10 @@ static Plan make_plan(const kvq_config* c, int max_seq_len, int split_tokens) {
   p.o_bytes = round_up(rows * c->head_dim * sizeof(float), 256);
   p.ml_bytes = round_up(rows * 2 * sizeof(float), 256);
   p.cnt_bytes = round_up((size_t)c->batch * c->num_kv_heads * sizeof(uint32_t), 256);
-  p.total = p.o_bytes + p.ml_bytes + p.cnt_bytes;
+  // the arrival counters come first, at an offset that does not depend on
+  // the plan: a workspace that stays zero there serves calls with any
+  // max_seq_len or split whose plan fits it
+  p.total = p.cnt_bytes + p.ml_bytes + p.o_bytes;
   return p;
 }
 
@@ -492,9 +504,9 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   a.seq_lens = cache->seq_lens;
   a.q = q;
   a.out = out;
-  a.part_o = (float*)workspace;
-  a.part_ml = (float*)((uint8_t*)workspace + p.o_bytes);
-  a.counters = (uint32_t*)((uint8_t*)workspace + p.o_bytes + p.ml_bytes);
+  a.counters = (uint32_t*)workspace;
+  a.part_ml = (float*)((uint8_t*)workspace + p.cnt_bytes);
+  a.part_o = (float*)((uint8_t*)workspace + p.cnt_bytes + p.ml_bytes);
   a.batch = cfg->batch;
   a.hq = cfg->num_q_heads;
   a.hkv = cfg->num_kv_heads;

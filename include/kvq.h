@@ -323,10 +323,14 @@ typedef struct {
  *       tokens gets zeros.
  *  workspace: device scratch of at least
  *       kvq_decode_workspace_bytes(cfg, max_seq_len) bytes, 256-byte aligned,
- *       owned by the caller.  It must be zero before the first call that
- *       uses it: it holds one arrival counter per (sequence, KV head), and
- *       every call leaves them at zero again.  Calls that overlap in time
- *       must not share a workspace.
+ *       owned by the caller.  Its first bytes hold one uint32 arrival counter
+ *       per (sequence, KV head), at the same place whatever the plan; they
+ *       must be zero before the first call, and every call leaves them at
+ *       zero again, so one workspace sized for the largest max_seq_len serves
+ *       every later call whose kvq_decode_workspace_bytes is no larger (a
+ *       growing or shrinking bound, another split).  The rest holds the
+ *       split partials.  Calls that overlap in time must not share a
+ *       workspace.
  *  max_seq_len: host upper bound of seq_lens (plans the split of the tokens
  *       over workgroups).  A sequence longer than max_seq_len gets NaN.  A
  *       plan of 2^24 or more workgroups (splits x H_kv x batch) returns

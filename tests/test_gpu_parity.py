@@ -446,27 +446,28 @@ def test_multi_layer_isolation():
 
 
 def test_workspace_reuse():
-    """One workspace serves consecutive calls with different queries: the
-    arrival counters the last workgroup of each (sequence, KV head) resets
-    are zero after every call, and the outputs equal those of calls with a
-    fresh workspace."""
+    """One workspace serves consecutive calls with different queries, host
+    length bounds and split sizes (a decode loop whose bound grows, or
+    shrinks): the arrival counters sit at the start of the workspace whatever
+    the plan, the last workgroup of each (sequence, KV head) resets them, and
+    the outputs equal those of calls with a fresh workspace."""
     H.log("case: workspace reuse")
     wl = synth.workload(4, batch=3, tokens=1024)  # paged, with a bf16 window
     lens = [1000, 0, 333]
     bt = H.build(wl, lens, decode_steps=2, oracle=False)
-    split, max_len = 128, 1024
-    need = K.decode_workspace_bytes(bt.cfg, max_len, split)
+    calls = [(0, 1024, 128), (1, 1024, 128), (0, 1000, 256), (2, 1024, 128), (1, 1010, 0),
+             (0, 1024, 384), (2, 1000, 128)]
+    need = max(K.decode_workspace_bytes(bt.cfg, m, sp) for _, m, sp in calls)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    nsp = -(-(max_len - wl["window"]) // split) + (1 if wl["window"] else 0)
-    rows = wl["batch"] * wl["hq"] * nsp
-    cnt_off = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256
-    for step in (0, 1, 0, 2):
+    cnt_bytes = -(-wl["batch"] * wl["hkv"] * 4 // 256) * 256
+    for step, max_len, split in calls:
         q = H.to_device(H.queries(wl, step), wl["in_dtype"])
         got = K.decode_attn(bt.cache, 0, q, max_len, workspace=ws, split_tokens=split)
         fresh = K.decode_attn(bt.cache, 0, q, max_len, split_tokens=split)
         torch.cuda.synchronize()
-        assert torch.equal(got, fresh), f"step {step}: reused workspace changed the output"
-        assert int(ws[cnt_off:].count_nonzero()) == 0, "arrival counters not reset"
+        assert torch.equal(got, fresh), \
+            f"step {step} max_len {max_len} split {split}: reused workspace changed the output"
+        assert int(ws[:cnt_bytes].count_nonzero()) == 0, "arrival counters not reset"
 
 
 def test_repeatable_outputs():
