@@ -18,7 +18,7 @@ committed rocprofv3 counter summary when it matches the kernel sources), a
 warm single-replica step time, the decode-append time for one token per
 sequence, and the CPU oracle baseline.
 
-  python bench.py [--config 2] [--steps 200] [--warmup 20]
+  python bench.py [--config 2] [--steps 200] [--warmup 500]
   python bench.py --copy-probe 1073741824   (plain copy kernel, for counters)
 """
 from __future__ import annotations
@@ -43,7 +43,11 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    # untimed steps before the timed region; the GPU's clocks take some tens
+    # of milliseconds of sustained decode to settle (measured on one MI355X:
+    # after 20 warm-up steps the VALU-heavy 2-bit step ran 45.8 us, after 500
+    # steps 39.3 us)
+    p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--config", type=int, default=2, help="workload 1..8 (default 2: GQA int8)")
     p.add_argument("--replicas", type=int, default=0, help="cache copies (0 = enough for 1 GiB)")
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
