@@ -194,9 +194,12 @@ def device_records(bt: Built, t: str, b: int, h: int, n: int) -> dict:
     bits, zp, scale = spec["bits"], bool(spec.get("zero_point")), spec.get("scale", "f32")
     D = bt.wl["d"]
     row = D * bits // 8
-    codes_buf = host(bt.cache.buffers[f"{t}_codes"]).reshape(-1, row)
     slots = token_slots(bt, b, h, n)
-    out = {"codes": unpack_codes(codes_buf[slots], bits, not zp)}
+    # gather the pair's rows on the device: a full-size code buffer can hold
+    # several GiB
+    codes_dev = bt.cache.buffers[f"{t}_codes"].view(-1, row)
+    idx = torch.from_numpy(slots.astype(np.int64)).to(codes_dev.device)
+    out = {"codes": unpack_codes(host(codes_dev.index_select(0, idx)), bits, not zp)}
     if spec.get("axis", "token") != "token":
         ch = host(bt.cache.buffers["k_chan_scale"]).view(np.float32).reshape(-1, D)
         out["chan"] = ch[b * bt.cfg.num_kv_heads + h]

@@ -39,24 +39,20 @@ def test_tiny_full_size():
     full_check(bt, steps=(0, 1, 2))
 
 
-@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6, 7, 8])
-def test_full_size_sampled(wid):
-    """Each workload at its full size, decoded in the launch configuration the
-    benchmark times (library-chosen split).  For sampled (sequence, KV head)
-    pairs the oracle quantizes that pair's input tokens (copied back from the
-    device) and attends its G query heads: codes and metadata bit for bit,
-    outputs within the acceptance bar."""
-    wl = synth.workload(wid)
-    lens = synth.seq_lengths(wl)
-    H.log(f"case: workload {wid} {wl['name']} full size, {sum(lens)} tokens")
+def sampled_check(wl, lens, extra_pairs=()):
+    """Builds the cache the way the benchmark does, decodes it in the launch
+    configuration the benchmark times (library-chosen split) and, for sampled
+    (sequence, KV head) pairs, has the oracle quantize that pair's input
+    tokens (copied back from the device) and attend its G query heads: codes
+    and metadata bit for bit, outputs within the acceptance bar."""
     bt = H.build_full(wl, lens)
     q = H.queries(wl)
     got = H.run_decode(bt, q)
     G = wl["hq"] // wl["hkv"]
-    rng = np.random.default_rng(77 + wid)
+    rng = np.random.default_rng(77 + wl["id"])
     longest = int(np.argmax(lens))
-    pairs = {(0, 0), (longest, wl["hkv"] - 1)}
-    while len(pairs) < 4:
+    pairs = {(0, 0), (longest, wl["hkv"] - 1), *extra_pairs}
+    while len(pairs) < 4 + len(extra_pairs):
         pairs.add((int(rng.integers(wl["batch"])), int(rng.integers(wl["hkv"]))))
     kf, vf = H.oracle_fmt(wl["key"]), H.oracle_fmt(wl["value"])
     for b, h in sorted(pairs):
@@ -83,9 +79,30 @@ def test_full_size_sampled(wid):
                 if "chan" in dev:
                     assert np.array_equal(H._bits(dev["chan"]), H._bits(st.chan[0])), "channel scales"
         want = orc.attend(0, q[b, h * G:(h + 1) * G])
-        H.check_close(got[b, h * G:(h + 1) * G], want, f"{wl['name']} full size b={b} h={h}")
+        H.check_close(got[b, h * G:(h + 1) * G], want, f"{wl['name']} b={b} h={h}")
     del bt
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4, 5, 6, 7, 8])
+def test_full_size_sampled(wid):
+    """Each workload at its full size, sampled (sequence, KV head) pairs
+    checked against the oracle (sampled_check)."""
+    wl = synth.workload(wid)
+    lens = synth.seq_lengths(wl)
+    H.log(f"case: workload {wid} {wl['name']} full size, {sum(lens)} tokens")
+    sampled_check(wl, lens)
+
+
+def test_codes_beyond_4gib():
+    """Workload 2's format over 32 sequences of 135,168 tokens: each code
+    buffer holds 4.13 GiB of one layer, so the last (sequence, KV head) pairs
+    sit past byte 2^32 (addresses that a 32-bit offset would wrap).  Sampled
+    pairs include the last one, whose codes start at 4.11 GiB; pair (31, 0) spans byte 2^32."""
+    wl = synth.workload(2, batch=32, tokens=135168)
+    lens = synth.seq_lengths(wl)
+    H.log(f"case: codes beyond 4 GiB, {sum(lens)} tokens")
+    sampled_check(wl, lens, extra_pairs=((31, 7), (31, 0)))
 
 
 @pytest.mark.parametrize("wid,over,lens,decode_steps,chunks", [
