@@ -526,8 +526,11 @@ kvq_status launch_append(const AppendArgs& a, void* stream) {
                        a);
     if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
   }
-  // groups completed by an append: at most (n_new + ring) / g + 1
-  const int ng = (a.n_new + a.ring) / a.tgroup + 1;
+  // Token groups an append completes: the quantized count Q(n) = g floor((n
+  // - W)^+ / g) grows by at most floor(n_new / g) + 1 groups when a sequence
+  // grows by n_new positions, so that many workgroups cover every sequence
+  // (one new token behind a 128-token window launches 2 per head, not 130).
+  const int ng = a.n_new / a.tgroup + 1;
   hipLaunchKernelGGL(append_quantize, dim3(ng, a.hkv, a.batch), dim3(128), 0, s, a);
   if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
   if (a.ring) {
