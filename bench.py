@@ -16,7 +16,8 @@ bytes per step / time per step), ms_per_step, roofline of the split kernel
 events around that kernel on its stream; HBM traffic per launch from the
 committed rocprofv3 counter summary when it matches the kernel sources), a
 warm single-replica step time, the decode-append time for one token per
-sequence, and the CPU oracle baseline.
+sequence, the time of append + attention back to back (the whole decode step
+of one layer), and the CPU oracle baseline.
 
   python bench.py [--config 2] [--steps 200] [--warmup 500]
   python bench.py --copy-probe 1073741824   (plain copy kernel, for counters)
@@ -360,6 +361,21 @@ def main():
     torch.cuda.synchronize()
     append_us = e0.elapsed_time(e1) / 100 * 1e3
 
+    # the whole decode step of one layer: quantize-append one token per
+    # sequence, then attend (each step rewrites the last position of the
+    # replica it attends; the work is the same every step)
+    for i in range(reps):
+        K.quantize_append(caches[i], 0, k1, v1, ones)
+        step(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        K.quantize_append(caches[i % reps], 0, k1, v1, ones)
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    full_step_us = e0.elapsed_time(e1) / args.steps * 1e3
+
     ab = ab_path(args, wl, caches, q, out, max_len, K, torch) if args.ab else None
 
     value = traffic / (ms_step * 1e-3) / 1e9
@@ -400,6 +416,7 @@ def main():
         "warm_us_per_step": round(warm_ms * 1e3, 2),
         "decode_append_us": round(append_us, 2),          # GPU time (graph replay)
         "decode_append_eager_us": round(append_eager_us, 2),  # per eager call
+        "step_with_append_us": round(full_step_us, 2),  # append one token, then attend
     }
     if ab is not None:
         result["ab_dequantize_then_decode"] = ab
