@@ -261,3 +261,31 @@ def test_paged_split_limit():
     assert K.decode_workspace_bytes(cfg, 32768, 8320) == 0
     cfg_c = cfg_of(synth.workload(2))
     assert K.decode_workspace_bytes(cfg_c, 4096, 16384) > 0
+
+
+def _workspace_rows(cfg, max_len, nsp):
+    """Workspace bytes for nsp partial rows per query head: the arrival
+    counters, (max, sum) pairs and partial outputs, each region 256-aligned."""
+    r = lambda x: -(-x // 256) * 256
+    rows = cfg.batch * cfg.num_q_heads * nsp
+    return r(cfg.batch * cfg.num_kv_heads * 4) + r(rows * 2 * 4) + r(rows * cfg.head_dim * 4)
+
+
+@pytest.mark.parametrize("wid,nsp", [
+    (2, 8),   # int8: 512 workgroups of 512 tokens over 64 (sequence, KV head) pairs
+    (3, 3),   # uint4 on both sides: 768 workgroups, splits of 2816 tokens
+    (5, 4),   # per-channel int8 keys: 512 workgroups of 16384 tokens
+    (6, 3),   # int2 with 8-bit scale codes: 768 workgroups
+    (8, 5),   # middle tier: splits of 3584 tokens (512 workgroups over the 7040 older
+              # tokens); the plan counts splits over every token past the window (3),
+              # then the window's row and the tier's row
+])
+def test_library_split_choice(wid, nsp):
+    """The library's split aims at one round of workgroups at the decode
+    kernel's occupancy: 768 for codes of at most 4 bits without a middle tier,
+    512 otherwise (contiguous splits up to 16384 tokens).  Checked through
+    the workspace it asks for, which holds nsp partial rows per query head."""
+    wl = synth.workload(wid)
+    cfg = cfg_of(wl)
+    max_len = max(synth.seq_lengths(wl))
+    assert K.decode_workspace_bytes(cfg, max_len) == _workspace_rows(cfg, max_len, nsp)
