@@ -642,12 +642,17 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
   bool moved = false;
 #pragma unroll
   for (int u = 0; u < HPG; ++u) {
-    const float mt = row16_max(fmaxf(sk[u][0], sk[u][1])) * qs[u];
     f[u] = 1.0f;
-    if (mt > st.m[u] + M_SLACK) {  // move the reference max (rarely)
-      f[u] = exp2_fast(st.m[u] - mt);  // 0 when m = -inf
-      st.m[u] = mt;
-      moved = true;
+    // The row maximum is needed only when it moves the reference max, which
+    // is rare: test each lane's own scores first (qs > 0, so scaling keeps
+    // the order) and reduce across the row only if some lane exceeds.
+    if (__any(fmaxf(sk[u][0], sk[u][1]) * qs[u] > st.m[u] + M_SLACK)) {
+      const float mt = row16_max(fmaxf(sk[u][0], sk[u][1])) * qs[u];
+      if (mt > st.m[u] + M_SLACK) {  // move the reference max
+        f[u] = exp2_fast(st.m[u] - mt);  // 0 when m = -inf
+        st.m[u] = mt;
+        moved = true;
+      }
     }
     const float mu = st.m[u] == NEG_INF ? 0.0f : st.m[u];
     p[u][0] = exp2_fast(fmaf(sk[u][0], qs[u], -mu));
@@ -655,9 +660,10 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
     st.l[u] = st.l[u] * f[u] + (p[u][0] + p[u][1]);
   }
   if (VM != MK_U8) {
-    // every row group sees the same tokens, so this max is wave-uniform
-    const float sv = row16_max(fmaxf(vs[0], vs[1]));
-    if (sv > st.R * R_SLACK) {
+    // every row group sees the same tokens, so the row maximum is
+    // wave-uniform; it is needed only when some lane's scale exceeds R SLACK
+    if (__any(fmaxf(vs[0], vs[1]) > st.R * R_SLACK)) {
+      const float sv = row16_max(fmaxf(vs[0], vs[1]));
       const float Rn = pow2_ceil(sv);
 #pragma unroll
       for (int u = 0; u < HPG; ++u) f[u] *= st.R / Rn;
