@@ -939,6 +939,11 @@ __device__ inline float load_agent(const float* p) {
   return __uint_as_float(__hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
+// The 4 waves' partials merged by log-sum-exp into partial row `split` of
+// each of the G query heads, or, with split = DIRECT_OUT (the pair has this
+// one partial), straight into the output: no arrival, no combine.
+constexpr int DIRECT_OUT = -1;
+
 template <int G>
 __device__ inline void block_merge(const DecodeArgs& a, const Shared<G>& sh, int b, int h,
                                    int split) {
@@ -954,6 +959,10 @@ __device__ inline void block_merge(const DecodeArgs& a, const Shared<G>& sh, int
       const float e = sh.l[w][hh] > 0.0f ? sh.l[w][hh] * exp2_fast(sh.m[w][hh] - M) : 0.0f;
       ws += e;
       acc += e * sh.o[w][hh][d];
+    }
+    if (split == DIRECT_OUT) {
+      a.out[((size_t)b * a.hq + (size_t)h * G + hh) * D + d] = ws > 0.0f ? acc / ws : 0.0f;
+      continue;
     }
     const size_t row = ((size_t)b * a.hq + (size_t)h * G + hh) * a.nsp + split;
     // agent-scope stores write through this XCD's L2: the workgroup that
@@ -995,7 +1004,8 @@ __device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
 // Window split: the newest tokens, kept as bf16
 // ---------------------------------------------------------------------------
 // Attends the n bf16 tokens at slots ring_slot(i, n, r0, ring) of kw / vw
-// with the G query heads of KV head h, and writes the partial row `row`.
+// with the G query heads of KV head h, and writes the partial row `row`
+// (DIRECT_OUT: the output).
 // PF: keep two tiles in flight per wave (long ranges of a bf16 cache).
 template <int G, bool QB, bool PF>
 __device__ void bf16_tokens(const DecodeArgs& a, int b, int h, const uint16_t* kw,
@@ -1096,10 +1106,11 @@ __device__ void bf16_tokens(const DecodeArgs& a, int b, int h, const uint16_t* k
 // The bf16 tokens of a quantized cache: the window and an open token group,
 // positions [nq, nq + nw) in ring slots (nq + i) mod ring.
 template <int G, bool QB>
-__device__ void window_split(const DecodeArgs& a, int b, int h, int q0, int nw, Shared<G>& sh) {
+__device__ void window_split(const DecodeArgs& a, int b, int h, int q0, int nw, bool direct,
+                             Shared<G>& sh) {
   const size_t head = ((size_t)b * a.hkv + h) * a.ring * D;
   bf16_tokens<G, QB, false>(a, b, h, a.k_win + head, a.v_win + head, q0 % a.ring, a.ring, nw,
-                            a.n_split, sh);
+                            direct ? DIRECT_OUT : a.n_split, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1422,7 +1433,8 @@ __device__ Item map_item(const DecodeArgs& a, int item, int* hist, bool tier) {
 }
 
 // Attends quantized positions [tok0, tok1) of (sequence b, KV head h) with
-// the G query heads of h and writes partial row `row`.  The codes and
+// the G query heads of h and writes partial row `row` (DIRECT_OUT: the
+// output).  The codes and
 // metadata live at kc, vc, km, vm: token slot head_tok + position
 // (contiguous), through the block table (PAGED), or in a ring of rblk
 // 16-token blocks (RING, the middle tier); nend bounds the blocks read.
@@ -1627,10 +1639,12 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   const int b = it.b, h = it.h, split = it.split;
   const SeqInfo si = it.si;
   const Plan pl = plan_of(a, si);
+  // a pair whose tokens one workgroup attends writes its output directly
+  const bool direct = pl.total == 1 && !pl.overflow;
   if (it.kind == 1) {
     if (si.nw > 0) {
-      window_split<G, QB>(a, b, h, si.nq + si.nm, si.nw, sh);
-      arrive_and_combine<G>(a, b, h, pl, &last_flag);
+      window_split<G, QB>(a, b, h, si.nq + si.nm, si.nw, direct, sh);
+      if (!direct) arrive_and_combine<G>(a, b, h, pl, &last_flag);
     }
     return;
   }
@@ -1639,10 +1653,10 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
     if (it.kind == 3) {  // the middle tier: int8 codes, fp32 scales, in its ring
       if (si.nm > 0) {
         quant_range<CK_I8, MK_F32, false, CK_I8, MK_F32, G, false, QB, true>(
-            a, b, h, si.nq, si.nq + si.nm, si.nq + si.nm, split, a.mid.k, a.mid.v,
-            (const uint8_t*)a.mid.ks, (const uint8_t*)a.mid.vs, pair * a.mid.slots,
+            a, b, h, si.nq, si.nq + si.nm, si.nq + si.nm, direct ? DIRECT_OUT : split, a.mid.k,
+            a.mid.v, (const uint8_t*)a.mid.ks, (const uint8_t*)a.mid.vs, pair * a.mid.slots,
             a.mid.slots >> 4, sh);
-        arrive_and_combine<G>(a, b, h, pl, &last_flag);
+        if (!direct) arrive_and_combine<G>(a, b, h, pl, &last_flag);
       }
       return;
     }
@@ -1650,9 +1664,9 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   const int tok0 = split * a.split_tokens;
   const int tok1 = min(tok0 + a.split_tokens, si.nq);
   quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
-      a, b, h, tok0, tok1, si.nq, split, a.k_codes, a.v_codes, a.k_meta, a.v_meta,
-      PAGED ? 0 : pair * a.max_tokens, 0, sh);
-  arrive_and_combine<G>(a, b, h, pl, &last_flag);
+      a, b, h, tok0, tok1, si.nq, direct ? DIRECT_OUT : split, a.k_codes, a.v_codes, a.k_meta,
+      a.v_meta, PAGED ? 0 : pair * a.max_tokens, 0, sh);
+  if (!direct) arrive_and_combine<G>(a, b, h, pl, &last_flag);
 }
 
 // Decode over an unquantized (bf16) contiguous cache, e.g. the output of
@@ -1676,9 +1690,12 @@ __global__ void __launch_bounds__(256) decode_bf16(DecodeArgs a) {
   const int tok0 = split * a.split_tokens;
   const int tok1 = min(tok0 + a.split_tokens, it.si.nq);
   const size_t head = ((size_t)b * a.hkv + h) * a.max_tokens * D;
+  const Plan pl = plan_of(a, it.si);
+  const bool direct = pl.total == 1 && !pl.overflow;
   bf16_tokens<G, QB, true>(a, b, h, (const uint16_t*)a.k_codes + head,
-                           (const uint16_t*)a.v_codes + head, tok0, 0, tok1 - tok0, split, sh);
-  arrive_and_combine<G>(a, b, h, plan_of(a, it.si), &last_flag);
+                           (const uint16_t*)a.v_codes + head, tok0, 0, tok1 - tok0,
+                           direct ? DIRECT_OUT : split, sh);
+  if (!direct) arrive_and_combine<G>(a, b, h, pl, &last_flag);
 }
 
 template <int G>

@@ -272,6 +272,7 @@ def _workspace_rows(cfg, max_len, nsp):
 
 
 @pytest.mark.parametrize("wid,nsp", [
+    (1, 1),   # 512 tokens: one workgroup, which writes the output directly
     (2, 8),   # int8: 512 workgroups of 512 tokens over 64 (sequence, KV head) pairs
     (3, 3),   # uint4 on both sides: 768 workgroups, splits of 2816 tokens
     (5, 4),   # per-channel int8 keys: 512 workgroups of 16384 tokens
@@ -283,7 +284,8 @@ def _workspace_rows(cfg, max_len, nsp):
 def test_library_split_choice(wid, nsp):
     """The library's split aims at one round of workgroups at the decode
     kernel's occupancy: 768 for codes of at most 4 bits without a middle tier,
-    512 otherwise (contiguous splits up to 16384 tokens).  Checked through
+    512 otherwise (contiguous splits up to 16384 tokens); a cache of at most
+    512 quantized tokens gets one split.  Checked through
     the workspace it asks for, which holds nsp partial rows per query head."""
     wl = synth.workload(wid)
     cfg = cfg_of(wl)
