@@ -528,9 +528,10 @@ kvq_status launch_append(const AppendArgs& a, void* stream) {
   }
   // Token groups an append completes: the quantized count Q(n) = g floor((n
   // - W)^+ / g) grows by at most floor(n_new / g) + 1 groups when a sequence
-  // grows by n_new positions, so that many workgroups cover every sequence
-  // (one new token behind a 128-token window launches 2 per head, not 130).
-  const int ng = a.n_new / a.tgroup + 1;
+  // grows by n_new positions, and by at most n_new positions when g = 1, so
+  // that many workgroups cover every sequence (one new token behind a
+  // 128-token window launches one per head, not 130).
+  const int ng = a.tgroup == 1 ? a.n_new : a.n_new / a.tgroup + 1;
   hipLaunchKernelGGL(append_quantize, dim3(ng, a.hkv, a.batch), dim3(128), 0, s, a);
   if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
   if (a.ring) {
