@@ -338,7 +338,10 @@ typedef struct {
  *  Launches one kernel on stream.  Each workgroup attends over one split of
  *  a sequence's tokens for the G query heads of one KV head; the last
  *  workgroup of each (sequence, KV head) to finish merges the splits by
- *  log-sum-exp (P2, "Decode kernels are split-T and memory bound"). */
+ *  log-sum-exp (P2, "Decode kernels are split-T and memory bound").  A
+ *  (sequence, KV head) that one workgroup covers is written directly.  The
+ *  library's split aims at one round of workgroups over the GPU; a cache of
+ *  at most 512 quantized tokens per sequence gets a single split. */
 kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, int layer,
                            const void* q, float* out, void* workspace, size_t workspace_bytes,
                            int max_seq_len, void* stream);
