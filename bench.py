@@ -69,7 +69,7 @@ def log(*a):
 
 # The sources that define the decode kernel and its launch (split plan, grid,
 # workspace layout): the counter summaries are valid while these are unchanged.
-DECODE_SOURCES = ("kvq_decode.hip", "kvq_host.cpp", "kvq_internal.h")
+DECODE_SOURCES = ("kvq_decode.hip", "kvq_host.cpp", "kvq_internal.h", "kvq_quantize.h")
 
 
 def kernel_source_sha() -> str:
@@ -375,6 +375,16 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     full_step_us = e0.elapsed_time(e1) / args.steps * 1e3
+    # the same step through kvq_decode_step (one kernel for formats it fuses)
+    for i in range(reps):
+        K.decode_step(caches[i], 0, k1, v1, q, max_len, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        K.decode_step(caches[i % reps], 0, k1, v1, q, max_len, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    decode_step_us = e0.elapsed_time(e1) / args.steps * 1e3
 
     ab = ab_path(args, wl, caches, q, out, max_len, K, torch) if args.ab else None
 
@@ -417,6 +427,7 @@ def main():
         "decode_append_us": round(append_us, 2),          # GPU time (graph replay)
         "decode_append_eager_us": round(append_eager_us, 2),  # per eager call
         "step_with_append_us": round(full_step_us, 2),  # append one token, then attend
+        "decode_step_us": round(decode_step_us, 2),     # the same through kvq_decode_step
     }
     if ab is not None:
         result["ab_dequantize_then_decode"] = ab

@@ -33,6 +33,7 @@
 #include <utility>
 
 #include "kvq_internal.h"
+#include "kvq_quantize.h"
 
 namespace kvq {
 namespace {
@@ -1617,6 +1618,37 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
 }
 
 
+// Decode step: quantizes the new token of (b, h), at position p, into the
+// cache with the append kernels' own quantizer (wave 0 the key, wave 1 the
+// value), and waits until the stores are done, so that this workgroup's
+// tile loads, which cover p, read it.  Only runs for per-token scales
+// without a window, a middle tier or token groups (checked on the host).
+__device__ void step_append(const DecodeArgs& a, int b, int h, int p) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (w < 2) {
+    const TensorKind k = w == 0 ? a.kk : a.vk;
+    const size_t head = (size_t)b * a.hkv + h;
+    const void* src = w == 0 ? a.k_new : a.v_new;
+    auto ld = [&](int, double& x0, double& x1) {
+      x0 = qz::load_in(src, head * D + 2 * lane, a.in_bf16);
+      x1 = qz::load_in(src, head * D + 2 * lane + 1, a.in_bf16);
+    };
+    auto slot = [&](int pos) -> size_t {
+      if (a.paged) {
+        int phys = a.block_table[(size_t)b * a.bt_stride + (pos >> 4)];
+        phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
+        return ((size_t)phys * a.hkv + h) * 16 + (pos & 15);
+      }
+      return head * a.max_tokens + pos;
+    };
+    uint8_t* codes = const_cast<uint8_t*>(w == 0 ? a.k_codes : a.v_codes);
+    uint8_t* meta = const_cast<uint8_t*>(w == 0 ? a.k_meta : a.v_meta);
+    qz::quantize_group(k, ld, slot, p, 1, codes, meta, slot(p), nullptr, 1.0f, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+}
+
 template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool TIER>
 __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   __shared__ Shared<G> sh;
@@ -1663,6 +1695,12 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   }
   const int tok0 = split * a.split_tokens;
   const int tok1 = min(tok0 + a.split_tokens, si.nq);
+  if (a.k_new != nullptr && si.len > 0) {
+    // the decode step's new token: the split that holds it stores it first
+    // (the last split if the sequence overflows the plan)
+    const int p = si.len - 1;
+    if (split == min(p / a.split_tokens, pl.ns - 1)) step_append(a, b, h, p);
+  }
   quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
       a, b, h, tok0, tok1, si.nq, direct ? DIRECT_OUT : split, a.k_codes, a.v_codes, a.k_meta,
       a.v_meta, PAGED ? 0 : pair * a.max_tokens, 0, sh);

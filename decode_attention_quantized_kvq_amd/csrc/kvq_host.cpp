@@ -464,10 +464,12 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
   return launch_append(a, stream);
 }
 
-kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int layer,
+// kvq_decode_attn_ex, and the decode step when k_new / v_new are given.
+static kvq_status decode_impl(const kvq_config* cfg, const kvq_cache* cache, int layer,
                               const void* q, float* out, void* workspace,
                               size_t workspace_bytes, int max_seq_len,
-                              const kvq_decode_opts* opts, void* stream) {
+                              const kvq_decode_opts* opts, const void* k_new,
+                              const void* v_new, void* stream) {
   kvq_status st = check_config(cfg, true);
   if (st != KVQ_OK) return st;
   if (!cache || !q || !out || layer < 0 || layer >= cfg->num_layers || max_seq_len < 0)
@@ -530,8 +532,47 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
   a.qbits = qbits;
   a.ev_begin = opts ? opts->split_begin_event : nullptr;
   a.ev_end = opts ? opts->split_end_event : nullptr;
+  a.k_new = k_new;
+  a.v_new = v_new;
   if (!resolve_mid(cfg, cache, layer, s, &a.mid)) return KVQ_ERR_INVALID_ARG;
   return launch_decode(a, stream);
+}
+
+kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                              const void* q, float* out, void* workspace,
+                              size_t workspace_bytes, int max_seq_len,
+                              const kvq_decode_opts* opts, void* stream) {
+  return decode_impl(cfg, cache, layer, q, out, workspace, workspace_bytes, max_seq_len, opts,
+                     nullptr, nullptr, stream);
+}
+
+// The decode kernel quantizes the new token itself when the cache keeps
+// per-token scales (fp32 or fp16, with or without a zero point) and has no
+// bf16 window, middle tier or token groups; otherwise the step is the append
+// followed by the decode.
+static bool step_fusable(const kvq_config* c) {
+  auto ok = [](const kvq_tensor_fmt& f) {
+    return f.bits != 16 && f.axis == KVQ_AXIS_TOKEN && f.scale_fmt != KVQ_SCALE_U8_SUPER;
+  };
+  return c->window == 0 && c->mid_tokens == 0 && token_group(c) == 1 && ok(c->key) &&
+         ok(c->value);
+}
+
+kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                           const void* k_new, const void* v_new, const void* q, float* out,
+                           void* workspace, size_t workspace_bytes, int max_seq_len,
+                           void* stream) {
+  kvq_status st = check_config(cfg, true);
+  if (st != KVQ_OK) return st;
+  if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+  if (!step_fusable(cfg)) {
+    st = kvq_quantize_append(cfg, cache, layer, k_new, v_new, 1, nullptr, stream);
+    if (st != KVQ_OK) return st;
+    return kvq_decode_attn(cfg, cache, layer, q, out, workspace, workspace_bytes, max_seq_len,
+                           stream);
+  }
+  return decode_impl(cfg, cache, layer, q, out, workspace, workspace_bytes, max_seq_len, nullptr,
+                     k_new, v_new, stream);
 }
 
 kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, int layer,

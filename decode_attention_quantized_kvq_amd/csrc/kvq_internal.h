@@ -113,6 +113,11 @@ struct DecodeArgs {
   TensorKind kk, vk;
   void* ev_begin;    // hipEvent_t recorded before the split kernel, or null
   void* ev_end;      // hipEvent_t recorded after it, or null
+  // decode step: one new token per sequence ([B][H_kv][D] in the input
+  // dtype) that the kernel quantizes into the cache before attending; null
+  // for a plain decode
+  const void* k_new;
+  const void* v_new;
 };
 
 // Everything a dequantize launch needs, resolved to one layer.

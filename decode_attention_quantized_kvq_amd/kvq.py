@@ -32,7 +32,7 @@ TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 EXPORTS = (
     "kvq_status_string", "kvq_validate", "kvq_get_buffer_sizes", "kvq_cache_bytes",
     "kvq_decode_traffic_bytes", "kvq_decode_workspace_bytes", "kvq_quantize_append",
-    "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_dequantize",
+    "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_dequantize", "kvq_decode_step",
 )
 
 
@@ -117,6 +117,8 @@ def lib() -> ctypes.CDLL:
                                          P(DecodeOpts), VP]
         L.kvq_dequantize.restype = I
         L.kvq_dequantize.argtypes = [P(Config), P(CacheDesc), I, VP, VP, I, VP]
+        L.kvq_decode_step.restype = I
+        L.kvq_decode_step.argtypes = [P(Config), P(CacheDesc), I, VP, VP, VP, VP, VP, S, I, VP]
         _lib = L
     return _lib
 
@@ -293,6 +295,33 @@ def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
                                     workspace.numel() * workspace.element_size(),
                                     int(max_seq_len), ctypes.byref(opts), _stream(stream)),
            "kvq_decode_attn")
+    return out
+
+
+def decode_step(cache: KvqCache, layer: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                q: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvq_decode_step: appends k_new/v_new [B][H_kv][1][D] (seq_lens already
+    counts them) and attends with q [B][Hq][D] -> out [B][Hq][D] fp32."""
+    cfg = cache.cfg
+    shape = (cfg.batch, cfg.num_kv_heads, 1, cfg.head_dim)
+    _check_input(k_new, cfg, shape, "k_new")
+    _check_input(v_new, cfg, shape, "v_new")
+    _check_input(q, cfg, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "q")
+    if out is None:
+        out = torch.empty((cfg.batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32,
+                          device=q.device)
+    elif (out.dtype != torch.float32 or not out.is_contiguous()
+          or tuple(out.shape) != (cfg.batch, cfg.num_q_heads, cfg.head_dim)):
+        raise ValueError("out: expected contiguous fp32 [B][Hq][D]")
+    if workspace is None:
+        need = decode_workspace_bytes(cfg, max_seq_len)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    desc = cache.desc()
+    _check(lib().kvq_decode_step(ctypes.byref(cfg), ctypes.byref(desc), int(layer), _ptr(k_new),
+                                 _ptr(v_new), _ptr(q), _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), int(max_seq_len),
+                                 _stream(stream)), "kvq_decode_step")
     return out
 
 

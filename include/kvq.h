@@ -352,6 +352,22 @@ kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, int la
 size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int max_seq_len,
                                   const kvq_decode_opts* opts);
 
+/* One decode step of one layer: appends one new token to every sequence
+ * (k_new, v_new: device [batch][num_kv_heads][1][head_dim] in in_dtype, as
+ * kvq_quantize_append with n_new = 1 and new_lens = NULL; seq_lens must
+ * already count the new token), then attends as kvq_decode_attn.  The
+ * stored codes and metadata and the output are bit for bit those of the two
+ * calls.  With per-token fp32 or fp16 scales (with or without a zero point)
+ * and no window, middle tier or token groups, one kernel does both: the
+ * workgroup whose split holds a sequence's new token quantizes and stores it
+ * before reading that split.  Otherwise it launches the append kernels and
+ * then the decode kernel.  Errors as kvq_quantize_append and kvq_decode_attn;
+ * KVQ_ERR_INVALID_ARG if k_new or v_new is NULL. */
+kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                           const void* k_new, const void* v_new, const void* q, float* out,
+                           void* workspace, size_t workspace_bytes, int max_seq_len,
+                           void* stream);
+
 /* kvq_decode_attn with tuning knobs (opts may be NULL). */
 kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int layer,
                               const void* q, float* out, void* workspace,

@@ -502,3 +502,45 @@ def test_repeatable_outputs():
         H.check_close(first, want, f"{wl['name']} split {split}")
         for _ in range(20):
             assert np.array_equal(H.run_decode(bt, q, split), first), f"{wl['name']}: outputs differ between runs"
+
+
+@pytest.mark.parametrize("fmt,paged,window", [
+    ("i8", False, 0), ("u4z", False, 0), ("i4", True, 0), ("u8z", False, 0), ("i2", False, 0),
+    ("i8", True, 128),
+])
+def test_decode_step(fmt, paged, window):
+    """kvq_decode_step equals kvq_quantize_append of the new tokens followed by
+    kvq_decode_attn: every cache buffer bit for bit, and the output bit for
+    bit.  Per-token fp32/fp16 scales without a window take the one-kernel
+    path (the workgroup holding the new token stores it first); the window
+    case takes the two-launch path."""
+    H.log(f"case: decode step {fmt} paged={paged} window={window}")
+    specs = {
+        "i8": dict(bits=8), "i4": dict(bits=4), "i2": dict(bits=2),
+        "u4z": dict(bits=4, zero_point=True, scale="f16"),
+        "u8z": dict(bits=8, zero_point=True, scale="f16"),
+    }
+    base = 4 if paged else 2
+    wl = synth.workload(base, batch=3, tokens=1024, key=specs[fmt], value=specs[fmt],
+                        window=window, hq=32, hkv=8)
+    pre = [1000, 300, 513]  # the new token of each lands in a block the table holds
+    bt = H.build(wl, pre, oracle=False)
+    other = K.KvqCache(bt.cfg, "cuda", bt.cache.block_table)
+    for name, buf in bt.cache.buffers.items():
+        if buf is not None:
+            other.buffers[name].copy_(buf)
+    gen = torch.Generator().manual_seed(5)
+    k1, v1 = (torch.randn((3, 8, 1, 128), generator=gen).to(torch.bfloat16).cuda() for _ in range(2))
+    lens = torch.tensor([n + 1 for n in pre], dtype=torch.int32, device="cuda")
+    bt.cache.seq_lens.copy_(lens)
+    other.seq_lens.copy_(lens)
+    q = H.to_device(H.queries(wl), wl["in_dtype"])
+    got = K.decode_step(bt.cache, 0, k1, v1, q, max(pre) + 1)
+    K.quantize_append(other, 0, k1, v1)
+    want = K.decode_attn(other, 0, q, max(pre) + 1)
+    torch.cuda.synchronize()
+    for name, buf in bt.cache.buffers.items():
+        if buf is not None:
+            assert torch.equal(buf, other.buffers[name]), f"{name} differs after the step"
+    assert torch.equal(got, want), "decode step output differs from append + decode"
+    assert bool(torch.isfinite(got).all())
