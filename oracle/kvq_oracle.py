@@ -65,11 +65,13 @@ Readings where the pages leave a step open (each restated where it is used):
   R13 the output is fp32 on the device; here fp64.
   R21 integer query (P3 "Precision floors and mixed cache formats": an 8-bit
       query against integer key codes, the integer sum converted to float
-      once before the exponential): per query head, symmetric,
-      s = fl32(amax / 127) and Q = clamp(rint(fl32(q / s)), -127, 127), both
-      divisions IEEE fp32, the kernel's precision (the pages fix none); an
-      all-zero head gets s = 1 and codes 0.  Attention then uses Q * s for
-      every token.  The exact path (the default) never quantizes the query.
+      once before the exponential): each query head is quantized by the
+      symmetric quantizer P3 prints in "The axis choice is a kernel
+      decision", in that listing's precision: s = fl64(amax / 127), kept in
+      fp64 as the listing keeps it, and Q = clamp(rint(fl64(q / s)), -127,
+      127), the same fp64 quotient as R1; an all-zero head gets s = 1 and
+      codes 0.  Attention then uses Q * s for every token.  The exact path
+      (the default) never quantizes the query.
   R20 token groups (P3 "Per-token scales and where they can live": several
       tokens under one scale): with a group size g, one scale (and zero
       point) is taken over all g*D values of g consecutive positions of a
@@ -338,14 +340,17 @@ def quantize_superscaled(v, S, bits: int):
 
 
 def quantize_query_int8(q):
-    """Reading R21: the query quantized to int8 per head (last axis), with
-    the scale and the quotient evaluated in IEEE fp32.  q holds values exact
-    in fp32.  Returns (codes int32 [..., D], scale float32 [...])."""
-    q32 = np.asarray(q, np.float32)
-    amax = np.max(np.abs(q32), axis=-1)
+    """Reading R21: the query quantized to int8 per head (last axis) by the
+    quantizer listing of P3 "The axis choice is a kernel decision": scale
+    amax / 127 and quotient q / scale, both IEEE fp64 (the listing's Python
+    floats), rounded ties to even (R1) and clamped.  q holds values exact in
+    fp32.  Returns (codes int32 [..., D], scale float64 [...])."""
+    q64 = np.asarray(q, np.float64)
+    amax = np.max(np.abs(q64), axis=-1)
     zero = amax == 0
-    s = np.where(zero, np.float32(1.0), amax / np.float32(127.0)).astype(np.float32)
-    codes = np.clip(np.rint(q32 / s[..., None]), -127, 127)
+    s = np.where(zero, 1.0, amax / 127.0)
+    codes = np.clip(rne_quotient(q64, s[..., None]), -127, 127)
+    codes = np.where(zero[..., None], 0.0, codes)
     return codes.astype(np.int32), s
 
 
@@ -689,8 +694,11 @@ def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
     A middle tier (R24) adds its int8 codes to payload and its fp32 scales
     to metadata; its unused ring slots are padding.
     padding   allocated but unused slots: the unfilled tail of the last block
-              of a paged sequence, or max_tokens - T_q quantized slots and the
-              unused bf16 ring slots of a contiguous one.
+              of a paged sequence, or max_tokens - T_q quantized slots of a
+              contiguous one, and the unused bf16 ring slots of either (the
+              ring is one fixed-size buffer per sequence and head in both
+              layouts: P2 "Metadata and block layout remain part of physical
+              memory use" counts what is allocated, not only what is used).
     total     the sum of the four.
     """
     def row(fmt):  # bytes of one token's codes
@@ -715,7 +723,7 @@ def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
         else:
             alloc_q = max_tokens if max_tokens is not None else n_q
         out["padding"] += layers * hkv * ((alloc_q - n_q) * codes + (alloc_q - n_q) // group * meta)
-        if ring and not block_tokens:
+        if ring:
             out["padding"] += layers * hkv * (ring - n_w) * d * 2 * 2
     out["total"] = out["payload"] + out["metadata"] + out["window"] + out["padding"]
     return out

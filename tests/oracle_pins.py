@@ -249,6 +249,96 @@ def pin_asym_exact(O):
         assert np.all(err[unclamped] <= sd.repeat(128, 1)[unclamped] / 2 * (1 + 1e-12))
 
 
+def _nearest_code(x: Fraction, s: Fraction, lo: int, hi: int, z: int = 0) -> int:
+    """Brute force: the code c in [lo, hi] whose grid point s (c - z) is
+    nearest to x, ties to the even c - z (independent of any rint / clamp)."""
+    best = None
+    for c in range(lo, hi + 1):
+        d = abs(x - s * (c - z))
+        key = (d, (c - z) % 2)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def pin_storage_limits(O):
+    """Reading R4 at the storage types' limits, in exact arithmetic: a scale
+    whose fp64 value rounds to 0 stores the type's smallest positive value
+    (fp16 2^-24, fp32 2^-149), an fp16 scale above 65504 stores 65504, and
+    fp16 scales in the subnormal range round to multiples of 2^-24.  Codes
+    are then the nearest points of the grid of the stored scale (brute force
+    over every code, ties to even, at 8, 4 and 2 bits, with and without a
+    zero point), so x_hat = c s_stored stays exact."""
+    F16_TINY, F32_TINY = Fraction(1, 2 ** 24), Fraction(1, 2 ** 149)
+    cases = []
+    for bits in (8, 4, 2):
+        qs, qu = (1 << (bits - 1)) - 1, (1 << bits) - 1
+        # fp16: underflow (exact quotient below 2^-25), the tie 2^-25, the
+        # subnormal range (3.3 * 2^-24), overflow (beyond 65520) and the
+        # largest finite value's neighbourhood (65510 rounds to 65504)
+        for target, want in ((Fraction(1, 2 ** 27), F16_TINY), (Fraction(1, 2 ** 25), F16_TINY),
+                             (Fraction(33, 10 * 2 ** 24), Fraction(3, 2 ** 24)),
+                             (Fraction(10 ** 6), Fraction(65504)), (Fraction(65510), Fraction(65504))):
+            cases += [("f16", bits, target, want, False), ("f16", bits, target, want, True)]
+        # fp32 (inputs exact in fp32): amax = k 2^-149 with k < qmax / 2, so
+        # amax / qmax lies below 2^-150 and rounds to 0; and a quotient in
+        # the subnormal range (7 2^-147, exact)
+        for zp, q in ((False, qs), (True, qu)):
+            if q >= 3:
+                cases.append(("f32", bits, Fraction((q - 1) // 2, q * 2 ** 149), F32_TINY, zp))
+            cases.append(("f32", bits, Fraction(7, 2 ** 147), Fraction(7, 2 ** 147), zp))
+    rng = _rng(211)
+    ran = {"f16": 0, "f32": 0}
+    for scale, bits, target, want, zp in cases:
+        qs, qu = (1 << (bits - 1)) - 1, (1 << bits) - 1
+        if True:
+            qmax = qu if zp else qs
+            amax = target * qmax            # exact: amax / qmax == target
+            famax = float(amax)
+            if Fraction(famax) != amax or (scale == "f32" and Fraction(float(np.float32(famax))) != amax):
+                continue                    # only inputs exact in the input type
+            # a vector with that max, negative entries and values on and
+            # between grid points of the expected stored scale
+            v = [famax, -famax / 3, famax / 7, 0.0]
+            v += [float(Fraction(k, 2) * want) for k in range(-2 * qs, 2 * qs + 1, 3)
+                  if abs(Fraction(k, 2) * want) <= amax]
+            v += list(rng.uniform(-famax, famax, 6))
+            if scale == "f32":
+                v = [float(np.float32(x)) for x in v]
+            xs = [Fraction(x) for x in v]
+            if zp:
+                c, st, z = O.quantize_asym(np.array(v), bits, scale)
+                lo = min(min(xs), Fraction(0))
+                hi = max(max(xs), Fraction(0))
+                span = (hi - lo) / qmax
+                # the zero-point scale is (hi - lo) / qmax; recompute the
+                # expected stored value for that quotient from the same rule
+                exp_s = _stored(span, scale)
+                assert Fraction(float(st)) == exp_s, (scale, bits, float(span), float(st))
+                ez = max(0, min(qmax, round(-lo / exp_s)))
+                assert Fraction(float(z)) == ez, (scale, bits, float(z), ez)
+                want_c = [_nearest_code(x, exp_s, 0, qmax, ez) for x in xs]
+            else:
+                c, st = O.quantize_sym(np.array(v), bits, scale)
+                assert Fraction(float(st)) == want, (scale, bits, float(target), float(st))
+                want_c = [_nearest_code(x, want, -qs, qs) for x in xs]
+            assert [int(x) for x in c] == want_c, (scale, bits, zp, float(target))
+            ran[scale] += 1
+    assert ran["f16"] >= 24 and ran["f32"] >= 9, ran   # every limit case ran
+
+
+def _stored(q: Fraction, scale: str) -> Fraction:
+    """Reading R4 written out: RN to the type (subnormals included), 0 ->
+    smallest positive value, fp16 above 65504 -> 65504."""
+    if scale == "f16":
+        r = rn16(q)
+        if r == 0:
+            return Fraction(1, 2 ** 24)
+        return min(r, Fraction(65504))
+    r = rn32(q)
+    return Fraction(1, 2 ** 149) if r == 0 else r
+
+
 def pin_sym_closed_form(O):
     """The largest-magnitude element maps to +-qmax, every element is within s/2
     of its reconstruction, codes never reach -2^(b-1), s = RN32(amax/qmax)."""
@@ -600,12 +690,13 @@ def pin_group_bytes(O):
 
 def pin_int_query(O):
     """Integer query (reading R21 of P3 "Precision floors and mixed cache
-    formats"): s is the correctly rounded fp32 quotient amax/127; each code is
-    the round-half-even of the correctly rounded fp32 quotient q/s (checked
-    on constructed near-ties too, where an fp64 quotient rounds the other
-    way); the largest element maps to +-127; |q - Q s| <= s/2 up to the fp32
-    quotient's rounding; an all-zero head gets s = 1, codes 0; and attention
-    on the integer path is attention on Q s."""
+    formats", quantized by P3's listing in "The axis choice is a kernel
+    decision"): s is the correctly rounded fp64 quotient amax/127, kept in
+    fp64; each code is the round-half-even of the correctly rounded fp64
+    quotient q/s, clamped (checked on constructed near-ties too, where an
+    fp32 quotient or an fp32 scale rounds some codes the other way); the
+    largest element maps to +-127; |q - Q s| <= s/2; an all-zero head gets
+    s = 1, codes 0; and attention on the integer path is attention on Q s."""
     rng = _rng(181)
     q = _f32(rng.standard_normal((6, 64)) * np.exp(rng.uniform(-4, 4, (6, 1))))
     q[2] = 0.0
@@ -613,24 +704,30 @@ def pin_int_query(O):
     for trial in range(10):                       # quotients within ulps of k + 1/2
         st = np.float32(rng.uniform(0.003, 0.03))
         row = _near_ties(st, 64, 300 + trial)
-        row[0] = np.float32(127.0 * float(st) * (1 + 1e-7))  # fl32(amax/127) close to st
+        row[0] = np.float32(127.0 * float(st) * (1 + 1e-7))  # amax/127 close to st
         near.append(row)
     q = np.concatenate([q, np.stack(near)])
     codes, s = O.quantize_query_int8(q)
+    flips = 0
     for h in range(len(q)):
         amax = max(abs(fr(x)) for x in q[h])
         if amax == 0:
             assert float(s[h]) == 1.0 and not codes[h].any()
             continue
-        assert Fraction(float(s[h])) == rn32(amax / 127), h
+        s_exact = rn64(amax / 127)
+        assert Fraction(float(s[h])) == s_exact, h
         for i in range(64):
-            quot = rn32(fr(q[h, i]) / Fraction(float(s[h])))   # the fp32 division
-            assert codes[h, i] == max(-127, min(127, round(quot))), (h, i)
+            want = max(-127, min(127, round(rn64(fr(q[h, i]) / s_exact))))
+            assert codes[h, i] == want, (h, i)
+            # what an fp32 scale and fp32 quotient would give
+            s32 = rn32(amax / 127)
+            flips += want != max(-127, min(127, round(rn32(fr(q[h, i]) / s32))))
         top = int(np.argmax(np.abs(q[h])))
         assert abs(codes[h, top]) == 127
         err = np.abs(q[h] - codes[h] * np.float64(s[h]))
-        # half a step, plus the fp32 quotient's rounding (|q / s| <= 127.5 < 2^7)
-        assert np.all(err <= float(s[h]) * (0.5 + 2.0 ** -16))
+        # half a step, plus the fp64 quotient's rounding (|q / s| <= 127.5 < 2^7)
+        assert np.all(err <= float(s[h]) * (0.5 + 2.0 ** -45))
+    assert flips > 0, "the near-tie rows do not separate fp64 from fp32 evaluation"
     # attention on the integer path equals attention on the reconstructed query
     fmt = O.TensorFormat(8)
     cache = O.OracleCache(1, 2, 64, fmt, fmt)
@@ -638,7 +735,8 @@ def pin_int_query(O):
     cache.append(0, k, k)
     qq = _bf16(rng.standard_normal((4, 64)))
     c, sq = O.quantize_query_int8(qq)
-    assert np.array_equal(cache.attend(0, qq, query_bits=8), cache.attend(0, c * sq.astype(np.float64)[:, None]))
+    assert np.array_equal(cache.attend(0, qq, query_bits=8),
+                          cache.attend(0, c * np.asarray(sq, np.float64)[:, None]))
     assert not np.array_equal(cache.attend(0, qq, query_bits=8), cache.attend(0, qq))
 
 
@@ -956,6 +1054,57 @@ def pin_byte_accounting(O):
     assert O.decode_traffic(i8, i8, 8, 128, lens, window=128) == sum(8 * (65536 + (n - 128) * 264) for n in lens)
     pad = O.cache_bytes(i8, i8, 1, 8, 128, [145], window=128, block_tokens=16)
     assert pad["padding"] == 8 * (16 - 17 % 16) * 264
+
+
+def pin_allocated_bytes(O):
+    """P2 "Metadata and block layout remain part of physical memory use": the
+    total of payload, metadata, window and padding is what the layout
+    allocates, written here from the buffer shapes alone (no per-sequence
+    tier split): per (sequence, head) and layer, a contiguous cache holds
+    max_tokens code rows and max_tokens / g metadata elements, a bf16 ring of
+    W (+ g) slots, a middle-tier ring of M + 32 int8 rows with fp32 scales,
+    and its per-head side data; a paged one holds whole 16-token blocks of
+    the quantized positions (counted by brute force, position by position),
+    the same ring and side data."""
+    rng = _rng(223)
+    fmts = [(O.TensorFormat(8), O.TensorFormat(8)),
+            (O.TensorFormat(4, zero_point=True, scale="f16"), O.TensorFormat(4, zero_point=True, scale="f16")),
+            (O.TensorFormat(8, "channel"), O.TensorFormat(4, scale="u8_super")),
+            (O.TensorFormat(2, scale="u8_super"), O.TensorFormat(2, scale="u8_super")),
+            (O.TensorFormat(2, zero_point=True, scale="f16"), O.TensorFormat(2, zero_point=True, scale="f16"))]
+    side = {"channel": lambda d: 4 * d}
+    for trial in range(60):
+        kf, vf = fmts[trial % len(fmts)]
+        per_token = kf.axis == "token" and kf.scale != "u8_super" and vf.scale != "u8_super"
+        g = int(rng.choice([1, 2, 4, 16])) if per_token else 1
+        W = int(rng.choice([0, 16, 128]))
+        M = int(rng.choice([0, 32, 96])) if (per_token and g == 1 and trial % 5 in (0, 1, 4)) else 0
+        paged = M == 0 and trial % 2 == 1
+        L, H, d, T = int(rng.integers(1, 3)), int(rng.integers(1, 4)), 128, 512
+        lens = [int(x) for x in rng.integers(0, T + W, 3)]
+        if M:
+            lens = [min(n, T + W + M) for n in lens]
+        got = O.cache_bytes(kf, vf, L, H, d, lens, window=W, block_tokens=16 if paged else 0,
+                            max_tokens=None if paged else T, group=g, mid=M)
+        row = d * (kf.bits + vf.bits) // 8
+        meta = O.meta_bytes_per_token(kf) + O.meta_bytes_per_token(vf)   # per metadata element
+        sd = (4 * d if kf.axis != "token" else 4 if kf.scale == "u8_super" else 0) + \
+             (4 if vf.scale == "u8_super" else 0)
+        ring = W + (g if g > 1 else 0)
+        mid_bytes = (M + 32) * (2 * d + 8) if M else 0
+        want = 0
+        for n in lens:
+            if paged:
+                # a position is stored quantized when its whole group is
+                # older than the window
+                nq = sum(1 for p in range(n) if (p // g) * g + g <= n - W)
+                blocks = -(-nq // 16)
+                main = blocks * 16 * row + blocks * (16 // g) * meta
+            else:
+                main = T * row + (T // g) * meta
+            want += L * H * (main + ring * d * 4 + mid_bytes + sd)
+        assert got["total"] == want, (trial, kf, vf, g, W, M, paged, lens, got, want)
+        assert got["total"] == got["payload"] + got["metadata"] + got["window"] + got["padding"]
 
 
 def pin_arithmetic_intensity(O):

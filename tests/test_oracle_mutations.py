@@ -60,12 +60,21 @@ def m_group_count_rounds_up(O):
     O.quantized_count = lambda n, window=0, group=1: -(-max(n - window, 0) // group) * group
 
 
-def m_int_query_fp64_division(O):
+def m_int_query_fp32_division(O):
+    def qq(q):
+        q32 = np.asarray(q, np.float32)
+        amax = np.max(np.abs(q32), axis=-1)
+        s = np.where(amax == 0, np.float32(1.0), amax / np.float32(127.0)).astype(np.float32)
+        return np.clip(np.rint(q32 / s[..., None]), -127, 127).astype(np.int32), s
+    O.quantize_query_int8 = qq
+
+
+def m_int_query_fp32_scale(O):
     def qq(q):
         q = np.asarray(q, np.float64)
         amax = np.max(np.abs(q), axis=-1)
-        s = np.where(amax == 0, 1.0, amax / 127.0)
-        return np.clip(np.rint(q / s[..., None]), -127, 127).astype(np.int32), s.astype(np.float32)
+        s = np.where(amax == 0, 1.0, amax / 127.0).astype(np.float32).astype(np.float64)
+        return np.clip(np.rint(q / s[..., None]), -127, 127).astype(np.int32), s
     O.quantize_query_int8 = qq
 
 
@@ -245,6 +254,57 @@ def m_window_keeps_one_more(O):
 def m_super_scale_over_255_times_qmax(O):
     orig = O.super_scale
     O.super_scale = lambda v, bits: (orig(v, bits).astype(np.float64) * 7 / 8).astype(np.float32)
+
+
+def m_f16_underflow_to_min_normal(O):
+    orig = O.round_to_storage
+
+    def rts(x64, scale):
+        r = orig(x64, scale)
+        if scale == "f16":
+            r = np.where(r.astype(np.float64) == 2.0 ** -24, np.float16(2.0 ** -14), r).astype(np.float16)
+        return r
+    O.round_to_storage = rts
+
+
+def m_f16_overflow_not_saturated(O):
+    O.F16_MAX = np.inf
+
+
+def m_f32_underflow_kept_zero(O):
+    O.F32_TINY = 0.0
+
+
+def m_f16_flush_subnormal_scales(O):
+    orig = O.round_to_storage
+
+    def rts(x64, scale):
+        r = orig(x64, scale)
+        if scale == "f16":
+            r64 = r.astype(np.float64)
+            r = np.where(r64 < 2.0 ** -14, np.float16(2.0 ** -24), r).astype(np.float16)
+        return r
+    O.round_to_storage = rts
+
+
+def m_ring_padding_contiguous_only(O):
+    orig = O.cache_bytes
+
+    def cb(key, value, layers, hkv, d, lens, window=0, block_tokens=0, max_tokens=None,
+           group=1, mid=0):
+        out = orig(key, value, layers, hkv, d, lens, window, block_tokens, max_tokens, group, mid)
+        if block_tokens:
+            ring = O.ring_slots(window, group)
+            for n in lens:
+                nw = O.tier_counts(n, window, mid, group)[2]
+                out["padding"] -= layers * hkv * (ring - nw) * d * 4
+            out["total"] = out["payload"] + out["metadata"] + out["window"] + out["padding"]
+        return out
+    O.cache_bytes = cb
+
+
+def m_mid_ring_without_spare_block(O):
+    O.mid_ring_slots = lambda mid: mid
 
 
 MUTATIONS = [v for k, v in sorted(globals().items()) if k.startswith("m_")]
