@@ -11,20 +11,26 @@
 // multiplies each score once after it, and a per-channel key scale is moved
 // onto the query.
 //
-// decode_split: one workgroup of 4 waves per (token split, KV
-// head, sequence).  Each wave streams 32-token tiles of its quarter of the
-// split straight from HBM into registers (coalesced 64/128-byte rows, the next
-// tile's loads in flight while the current one computes), converts codes to
-// fp16 exactly, and runs both contractions on the matrix cores:
-//   scores  S[16 tok x 16 col] += K[16 tok x 32 d] Q[32 d x 16 col]
-//   output  O[16 d x 16 col]   += V^T[16 d x 32 tok] P[32 tok x 16 col]
-// The G query heads that share the KV head occupy the 16 columns as fp16
-// high/low halves of the query (and of the weights), so every loaded tile is
-// used by all G heads and both products are exact to about 2^-22.  Online
-// softmax runs in base 2.  The 4 waves merge through LDS and the workgroup
-// writes one partial (max, sum, normalized output) per query head.  The last
-// workgroup of a (sequence, KV head) to finish, found with an arrival
-// counter, merges the partials by log-sum-exp into the fp32 output.
+// decode_split: one workgroup of 4 waves per work item (a chunk of one
+// sequence's tokens for one KV head, that sequence's bf16 window, or its
+// middle tier).  Each wave streams 32-token tiles of its quarter of the chunk
+// straight from HBM into registers with buffer loads (two tiles in flight)
+// and runs both contractions on the matrix cores, transposed so that the
+// query heads are the rows:
+//   scores  S^T[16 rows x 16 tok] += Q'[16 rows x 32 d] K^T[32 d x 16 tok]
+//           (int8: the query as an exact integer in three int8 limbs per
+//           head against the integer codes, int32 sums)
+//   output  O^T[16 rows x 16 d]   += P^T[16 rows x 32 tok] V[32 tok x 16 d]
+//           (fp16: the weights p s_V / R as (high, low) halves against the
+//           codes converted exactly to fp16)
+// The G query heads that share the KV head occupy the rows, so every loaded
+// tile is used by all G heads.  The per-token key scale multiplies each
+// score after the integer dot product; the online softmax runs in base 2.
+// The 4 waves merge through LDS and the workgroup writes one partial (max,
+// sum, normalized output) per query head; the last workgroup of a
+// (sequence, KV head) to finish, found with an arrival counter, merges the
+// partials by log-sum-exp into the fp32 output.  A (sequence, KV head) that
+// one workgroup covers writes its output directly.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -520,10 +526,10 @@ __device__ inline void value_frags(const TileRaw<KC, KM, VC, VM>& t, half8 out[8
 }
 
 // ---------------------------------------------------------------------------
-// Per-wave state of the online softmax.  The reference max m and the
-// reference value scale R move only when exceeded by 2^8 and 2^6, so the
-// accumulators are rescaled on few tiles; weights stay below 2^14 and the
-// fp16 halves keep full precision.
+// Per-wave state of the online softmax.  The reference max m moves only when
+// a score exceeds it by 2^8 (base 2), and the weight reference R only when a
+// weight p s_V exceeds it by 2^6, so the accumulators are rescaled on few
+// tiles and the fp16 weights p s_V / R stay below 64.
 // ---------------------------------------------------------------------------
 constexpr float M_SLACK = 8.0f;
 constexpr float R_SLACK = 64.0f;
@@ -560,16 +566,18 @@ struct Softmax {
 // Per-wave state of the quantized-token path.  The scores come out of the
 // matrix cores transposed (query rows x token columns), so lane (t, g) holds
 // whole scores of the HPG query heads of row group g for token t of each
-// block: HPG = 2 when G = 8, else 1 (row group g is query head g).
+// block: HPG = 2 when G = 8, else 1 (row group g is query head g).  The
+// lane also holds the output rows of those heads, so every per-head
+// reference (m, R) is uniform over a row group and local to the lane.
 template <int G>
 struct RowState {
   static constexpr int HPG = G == 8 ? 2 : 1;
-  float m[HPG];  // reference max per head (base-2 units), uniform over the row
-  float l[HPG];  // this lane's share of the running sum of 2^(s - m)
-  float z[HPG];  // this lane's share of sum w * zero_point (zero-point values)
-  float R;       // power-of-two reference of the folded value scale
-  float invR;    // 1 / R (exact)
-  f32x4 o[8];    // O^T: rows 4g + i = (head, limb), columns = features 8t + J
+  float m[HPG];     // reference max per head (base-2 units), uniform over the row
+  float l[HPG];     // this lane's share of the running sum of 2^(s - m)
+  float z[HPG];     // this lane's share of sum w * zero_point (zero-point values)
+  float R[HPG];     // power-of-two weight reference per head: w = p s_V / R
+  float invR[HPG];  // 1 / R (exact)
+  f32x4 o[8];       // O^T: rows 4g + i = (head, limb), columns = features 8t + J
 
   __device__ inline void init(float r0) {
 #pragma unroll
@@ -577,9 +585,9 @@ struct RowState {
       m[u] = NEG_INF;
       l[u] = 0.0f;
       z[u] = 0.0f;
+      R[u] = r0;
+      invR[u] = 1.0f / r0;
     }
-    R = r0;
-    invR = 1.0f / r0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -660,17 +668,38 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
     p[u][1] = exp2_fast(fmaf(sk[u][1], qs[u], -mu));
     st.l[u] = st.l[u] * f[u] + (p[u][0] + p[u][1]);
   }
-  if (VM != MK_U8) {
-    // every row group sees the same tokens, so the row maximum is
-    // wave-uniform; it is needed only when some lane's scale exceeds R SLACK
-    if (__any(fmaxf(vs[0], vs[1]) > st.R * R_SLACK)) {
-      const float sv = row16_max(fmaxf(vs[0], vs[1]));
-      const float Rn = pow2_ceil(sv);
+  // weights w = p s_V / R_u (8-bit scale codes: p u / 256, below p).  R_u
+  // follows the head's largest p s_V lazily: it moves when some weight of the
+  // tile exceeds R_SLACK, to that row's largest p s_V rounded up to a power
+  // of two, so weights stay below 64.  Tracking the product, not s_V alone,
+  // keeps the weights of the tokens that carry the output clear of fp16's
+  // subnormal floor when a token with a far larger value scale but a
+  // negligible attention weight shares the range.
+  float w[HPG][2];
 #pragma unroll
-      for (int u = 0; u < HPG; ++u) f[u] *= st.R / Rn;
-      st.R = Rn;
-      st.invR = 1.0f / Rn;
-      moved = true;
+  for (int u = 0; u < HPG; ++u) {
+    const float i0 = VM == MK_U8 ? 1.0f / 256.0f : st.invR[u];
+    w[u][0] = p[u][0] * vs[0] * i0;
+    w[u][1] = p[u][1] * vs[1] * i0;
+  }
+  if (VM != MK_U8) {
+    bool up = false;
+#pragma unroll
+    for (int u = 0; u < HPG; ++u) up |= fmaxf(w[u][0], w[u][1]) > R_SLACK;
+    if (__any(up)) {
+#pragma unroll
+      for (int u = 0; u < HPG; ++u) {
+        const float pm = row16_max(fmaxf(p[u][0] * vs[0], p[u][1] * vs[1]));
+        if (pm > st.R[u] * R_SLACK) {  // uniform over the row: its head's R moves
+          const float Rn = pow2_ceil(pm);
+          f[u] *= st.R[u] / Rn;
+          st.R[u] = Rn;
+          st.invR[u] = 1.0f / Rn;
+          w[u][0] = p[u][0] * vs[0] * st.invR[u];
+          w[u][1] = p[u][1] * vs[1] * st.invR[u];
+          moved = true;
+        }
+      }
     }
   }
   if (__any(moved)) {
@@ -681,13 +710,11 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
 #pragma unroll
     for (int u = 0; u < HPG; ++u) st.z[u] *= f[u];
   }
-  // weights w = p * s_V / R as fp16 (high, low) pairs into LDS: pwr[u] is
-  // this lane's (head, token) slot, 2 words: block 0, block 1
-  const float sc0 = VM == MK_U8 ? vs[0] * (1.0f / 256.0f) : vs[0] * st.invR;
-  const float sc1 = VM == MK_U8 ? vs[1] * (1.0f / 256.0f) : vs[1] * st.invR;
+  // the weights as fp16 (high, low) pairs into LDS: pwr[u] is this lane's
+  // (head, token) slot, 2 words: block 0, block 1
 #pragma unroll
   for (int u = 0; u < HPG; ++u) {
-    const float w0 = p[u][0] * sc0, w1 = p[u][1] * sc1;
+    const float w0 = w[u][0], w1 = w[u][1];
     if (Meta<VM>::ZP) st.z[u] += w0 * vz[0] + w1 * vz[1];
     const half2v hi = __builtin_convertvector((float2v){w0, w1}, half2v);
     const half2v lo = __builtin_convertvector((float2v){w0 - (float)hi.x, w1 - (float)hi.y}, half2v);
@@ -911,8 +938,10 @@ __device__ inline void wave_finish(Softmax& st, float scale_out, int c, int g, i
 
 // Wave epilogue of the quantized-token path: lane (t, g) writes features
 // 8t + J of its row group's heads.
+// scale_out[u]: what the accumulated weights of local head u are relative to
+// (its R, or 256 S with 8-bit scale codes).
 template <int G>
-__device__ inline void row_finish(RowState<G>& st, float scale_out, int t, int g, int wave,
+__device__ inline void row_finish(RowState<G>& st, const float* scale_out, int t, int g, int wave,
                                   Shared<G>& sh) {
   constexpr int HPG = RowState<G>::HPG;
 #pragma unroll
@@ -921,7 +950,7 @@ __device__ inline void row_finish(RowState<G>& st, float scale_out, int t, int g
     const float l = row16_sum(st.l[u]);
     const float z = row16_sum(st.z[u]);
     if (head < G) {
-      const float k = l > 0.0f ? scale_out / l : 0.0f;
+      const float k = l > 0.0f ? scale_out[u] / l : 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         sh.o[wave][head][8 * t + j] = (st.o[j][2 * u] + st.o[j][2 * u + 1] - z) * k;
@@ -1040,13 +1069,14 @@ __device__ void bf16_tokens(const DecodeArgs& a, int b, int h, const uint16_t* k
 #pragma unroll
   for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(qv[k]));
   if (a.qbits == 8) {
-    // integer query: the bf16 tokens are attended with Q s as well
+    // integer query: the bf16 tokens are attended with Q s as well (s and
+    // the quotient in fp64, Q s rounded once to fp32)
     const float hmax = rows_max(amax);
-    const float s = hmax > 0.0f ? hmax / 127.0f : 1.0f;
+    const double s = hmax > 0.0f ? (double)hmax / 127.0 : 1.0;
     amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
-      qv[k] = fminf(fmaxf(rintf(qv[k] / s), -127.0f), 127.0f) * s;
+      qv[k] = (float)(fmin(fmax(rint((double)qv[k] / s), -127.0), 127.0) * s);
       amax = fmaxf(amax, fabsf(qv[k]));
     }
   }
@@ -1528,8 +1558,11 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
     for (int n = 0; n < 32; ++n) amax = fmaxf(amax, fabsf(qv[n]));
     const float hmax = rows_max(amax);  // max over the row's 4 lanes: the head's
     float inv, sc = 0.0f;
-    if (a.qbits == 8)  // integer query: s = fl32(amax / 127), Q = rint(fl32(q / s))
-      inv = hmax > 0.0f ? hmax / 127.0f : 1.0f;
+    // integer query: s = fl64(amax / 127), Q = clamp(rint(fl64(q / s))), the
+    // cache quantizer's fp64 rule; the score scale takes s rounded to fp32
+    const double s64 = hmax > 0.0f ? (double)hmax / 127.0 : 1.0;
+    if (a.qbits == 8)
+      inv = (float)s64;
     else
       sc = q_int_scale(hmax, &inv);
     float qsum = 0.0f;
@@ -1539,7 +1572,8 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float y = qv[key_feature<KC>(j, 0, e)];
-        const float x = a.qbits == 8 ? fminf(fmaxf(rintf(y / inv), -127.0f), 127.0f) : rintf(y * sc);
+        const float x = a.qbits == 8 ? (float)fmin(fmax(rint((double)y / s64), -127.0), 127.0)
+                                     : rintf(y * sc);
         qsum += x;
         const int Q = (int)x;
         const int l2 = (int)(int8_t)(Q & 0xFF);
@@ -1608,11 +1642,10 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
     if (k < rem)
       compute_tile<KC, KM, KCH, VC, VM, G>(buf[k], t + k * TILE, w1, qa, qs, sumq, lt, g, psel, prd,
                                            pwr, nm, st);
-  float scale_out;
-  if (VM == MK_U8)
-    scale_out = 256.0f * a.v_super[(size_t)b * a.hkv + h];
-  else
-    scale_out = st.R;
+  float scale_out[HPG];
+#pragma unroll
+  for (int u = 0; u < HPG; ++u)
+    scale_out[u] = VM == MK_U8 ? 256.0f * a.v_super[(size_t)b * a.hkv + h] : st.R[u];
   row_finish<G>(st, scale_out, lt, g, wave, sh);
   block_merge<G>(a, sh, b, h, row);
 }
@@ -1695,11 +1728,15 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   }
   const int tok0 = split * a.split_tokens;
   const int tok1 = min(tok0 + a.split_tokens, si.nq);
-  if (a.k_new != nullptr && si.len > 0) {
-    // the decode step's new token: the split that holds it stores it first
-    // (the last split if the sequence overflows the plan)
-    const int p = si.len - 1;
-    if (split == min(p / a.split_tokens, pl.ns - 1)) step_append(a, b, h, p);
+  if (a.k_new != nullptr) {
+    // the decode step's new token, at position seq_lens[b] - 1 of the
+    // unclamped length: the split that holds it stores it first (the last
+    // split if the sequence overflows the plan).  A position at or past the
+    // capacity is not stored, as kvq_quantize_append skips it; si.len is
+    // the length clamped to the capacity.
+    const int p = a.seq_lens[b] - 1;
+    if (p >= 0 && p < si.len && split == min(p / a.split_tokens, pl.ns - 1))
+      step_append(a, b, h, p);
   }
   quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
       a, b, h, tok0, tok1, si.nq, direct ? DIRECT_OUT : split, a.k_codes, a.v_codes, a.k_meta,

@@ -355,9 +355,18 @@ size_t kvq_cache_bytes(const kvq_config* cfg, const int32_t* host_seq_lens, kvq_
     else
       alloc_q = std::max<size_t>((size_t)cfg->max_tokens, nq);
     b.padding += L * H * ((alloc_q - nq) * (rk + rv) + (alloc_q - nq) / g * (mk + mv));
-    if (ring && !cfg->block_tokens) b.padding += L * H * (ring > nw ? ring - nw : 0) * D * 2 * 2;
+    // the bf16 ring is a fixed buffer per (sequence, head) in both layouts
+    if (ring) b.padding += L * H * (ring > nw ? ring - nw : 0) * D * 2 * 2;
   }
   b.total = b.payload + b.metadata + b.window + b.padding;
+  // decode workspace at the library's split for the longest sequence (per
+  // call, not part of the cache's total)
+  if (check_config(cfg, true) == KVQ_OK) {
+    int longest = 0;
+    for (int i = 0; i < cfg->batch; ++i)
+      longest = std::max(longest, host_seq_lens ? host_seq_lens[i] : cfg->max_tokens);
+    b.workspace = make_plan(cfg, longest, 0).total;
+  }
   if (out) *out = b;
   return b.total;
 }
@@ -430,13 +439,19 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int max_seq_len,
   return make_plan(cfg, max_seq_len, split).total;
 }
 
-kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, int layer,
-                               const void* k_new, const void* v_new, int n_new,
-                               const int32_t* new_lens, void* stream) {
+// Validates an append and resolves its arguments to one layer; launches
+// nothing.  KVQ_OK with *empty set when there is nothing to append.
+static kvq_status prepare_append(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                                 const void* k_new, const void* v_new, int n_new,
+                                 const int32_t* new_lens, AppendArgs* out, bool* empty) {
+  *empty = false;
   kvq_status st = check_config(cfg, true);
   if (st != KVQ_OK) return st;
   if (!cache || layer < 0 || layer >= cfg->num_layers || n_new < 0) return KVQ_ERR_INVALID_ARG;
-  if (n_new == 0) return KVQ_OK;
+  if (n_new == 0) {
+    *empty = true;
+    return KVQ_OK;
+  }
   if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
   AppendArgs a{};
   const LayerSizes s = layer_sizes(cfg);
@@ -461,15 +476,29 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
   a.bt_stride = cfg->max_blocks_per_seq;
   a.in_bf16 = cfg->in_dtype == KVQ_DT_BF16;
   if (!resolve_mid(cfg, cache, layer, s, &a.mid)) return KVQ_ERR_INVALID_ARG;
+  *out = a;
+  return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                               const void* k_new, const void* v_new, int n_new,
+                               const int32_t* new_lens, void* stream) {
+  AppendArgs a{};
+  bool empty = false;
+  const kvq_status st =
+      prepare_append(cfg, cache, layer, k_new, v_new, n_new, new_lens, &a, &empty);
+  if (st != KVQ_OK || empty) return st;
   return launch_append(a, stream);
 }
 
-// kvq_decode_attn_ex, and the decode step when k_new / v_new are given.
-static kvq_status decode_impl(const kvq_config* cfg, const kvq_cache* cache, int layer,
-                              const void* q, float* out, void* workspace,
-                              size_t workspace_bytes, int max_seq_len,
-                              const kvq_decode_opts* opts, const void* k_new,
-                              const void* v_new, void* stream) {
+// Validates a decode call (configuration, pointers, options, the split
+// plan and the workspace) and resolves its arguments to one layer; launches
+// nothing.  Shared by kvq_decode_attn_ex and kvq_decode_step, which runs it
+// before its append so that a rejected step leaves the cache untouched.
+static kvq_status prepare_decode(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                                 const void* q, float* out, void* workspace,
+                                 size_t workspace_bytes, int max_seq_len,
+                                 const kvq_decode_opts* opts, DecodeArgs* args) {
   kvq_status st = check_config(cfg, true);
   if (st != KVQ_OK) return st;
   if (!cache || !q || !out || layer < 0 || layer >= cfg->num_layers || max_seq_len < 0)
@@ -532,18 +561,22 @@ static kvq_status decode_impl(const kvq_config* cfg, const kvq_cache* cache, int
   a.qbits = qbits;
   a.ev_begin = opts ? opts->split_begin_event : nullptr;
   a.ev_end = opts ? opts->split_end_event : nullptr;
-  a.k_new = k_new;
-  a.v_new = v_new;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
   if (!resolve_mid(cfg, cache, layer, s, &a.mid)) return KVQ_ERR_INVALID_ARG;
-  return launch_decode(a, stream);
+  *args = a;
+  return KVQ_OK;
 }
 
 kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int layer,
                               const void* q, float* out, void* workspace,
                               size_t workspace_bytes, int max_seq_len,
                               const kvq_decode_opts* opts, void* stream) {
-  return decode_impl(cfg, cache, layer, q, out, workspace, workspace_bytes, max_seq_len, opts,
-                     nullptr, nullptr, stream);
+  DecodeArgs a{};
+  const kvq_status st = prepare_decode(cfg, cache, layer, q, out, workspace, workspace_bytes,
+                                       max_seq_len, opts, &a);
+  if (st != KVQ_OK) return st;
+  return launch_decode(a, stream);
 }
 
 // The decode kernel quantizes the new token itself when the cache keeps
@@ -565,14 +598,24 @@ kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache, int la
   kvq_status st = check_config(cfg, true);
   if (st != KVQ_OK) return st;
   if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
-  if (!step_fusable(cfg)) {
-    st = kvq_quantize_append(cfg, cache, layer, k_new, v_new, 1, nullptr, stream);
-    if (st != KVQ_OK) return st;
-    return kvq_decode_attn(cfg, cache, layer, q, out, workspace, workspace_bytes, max_seq_len,
-                           stream);
+  // every check of both halves runs before anything is launched: a step the
+  // library rejects leaves the cache as it was
+  DecodeArgs d{};
+  st = prepare_decode(cfg, cache, layer, q, out, workspace, workspace_bytes, max_seq_len,
+                      nullptr, &d);
+  if (st != KVQ_OK) return st;
+  if (step_fusable(cfg)) {
+    d.k_new = k_new;
+    d.v_new = v_new;
+    return launch_decode(d, stream);
   }
-  return decode_impl(cfg, cache, layer, q, out, workspace, workspace_bytes, max_seq_len, nullptr,
-                     k_new, v_new, stream);
+  AppendArgs ap{};
+  bool empty = false;
+  st = prepare_append(cfg, cache, layer, k_new, v_new, 1, nullptr, &ap, &empty);
+  if (st != KVQ_OK) return st;
+  st = launch_append(ap, stream);
+  if (st != KVQ_OK) return st;
+  return launch_decode(d, stream);
 }
 
 kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, int layer,

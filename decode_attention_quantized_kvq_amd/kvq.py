@@ -63,7 +63,8 @@ class CacheDesc(ctypes.Structure):
 
 
 class Bytes(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("payload", "metadata", "window", "padding", "total")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("payload", "metadata", "window", "padding",
+                                                "workspace", "total")]
 
 
 class BufferSizes(ctypes.Structure):
@@ -165,7 +166,8 @@ def _host_lens(cfg: Config, lens: Optional[Sequence[int]]):
 
 
 def cache_bytes(cfg: Config, lens: Optional[Sequence[int]] = None) -> dict:
-    """kvq_cache_bytes: payload / metadata / window / padding / total."""
+    """kvq_cache_bytes: payload / metadata / window / padding / workspace /
+    total (total excludes the per-call decode workspace)."""
     keep, ptr = _host_lens(cfg, lens)
     out = Bytes()
     total = lib().kvq_cache_bytes(ctypes.byref(cfg), ptr, ctypes.byref(out))

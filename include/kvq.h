@@ -220,8 +220,15 @@ typedef struct {
   size_t metadata;  /* per-token scales / zero points / scale codes and
                        per-head channel scales or super-scales */
   size_t window;    /* bf16 recent tokens of K and V */
-  size_t padding;   /* allocated but unused slots */
-  size_t total;
+  size_t padding;   /* allocated but unused slots (code and metadata slots
+                       past a sequence's tokens, the unfilled tail of its last
+                       16-token block, unused bf16 ring and middle-tier
+                       slots) */
+  size_t workspace; /* bytes of the decode workspace kvq_decode_attn needs
+                       at the library's split for the longest of the
+                       sequences (0 if the kernels do not run this
+                       configuration); per call, not part of total */
+  size_t total;     /* payload + metadata + window + padding */
 } kvq_bytes;
 
 /* Bytes to allocate for each buffer of kvq_cache (0 = not used). */
@@ -255,9 +262,9 @@ kvq_status kvq_get_buffer_sizes(const kvq_config* cfg, kvq_buffer_sizes* out);
 /* Byte accounting of P2 "Cache precision is separate from weight precision"
  * (payload 2 L H_kv D T b, generalised to separate key and value widths) plus
  * metadata (P3, "Per-token scales and where they can live"), window and
- * padding.  host_seq_lens: [batch] host array, or NULL for max_tokens each.
- * Pure host arithmetic.  Returns the total (0 on an
- * invalid configuration) and fills *out when out is not NULL. */
+ * padding, and the decode workspace.  host_seq_lens: [batch] host array, or
+ * NULL for max_tokens each.  Pure host arithmetic.  Returns the total (0 on an invalid configuration) and fills
+ * *out when out is not NULL. */
 size_t kvq_cache_bytes(const kvq_config* cfg, const int32_t* host_seq_lens, kvq_bytes* out);
 
 /* Bytes one decode step reads from the cache of one layer: codes, per-token
@@ -338,7 +345,11 @@ typedef struct {
  *  Launches one kernel on stream.  Each workgroup attends over one split of
  *  a sequence's tokens for the G query heads of one KV head; the last
  *  workgroup of each (sequence, KV head) to finish merges the splits by
- *  log-sum-exp (P2, "Decode kernels are split-T and memory bound").  A
+ *  log-sum-exp.  Splitting the tokens over workgroups is this library's own
+ *  design (the pages give no kernel), made because one decode step of a
+ *  sequence must be spread over many compute units to stream the cache at
+ *  the memory's rate (P3, "What the cache holds and how it is read": the
+ *  read is memory-bound).  A
  *  (sequence, KV head) that one workgroup covers is written directly.  The
  *  library's split aims at one round of workgroups over the GPU; a cache of
  *  at most 512 quantized tokens per sequence gets a single split. */
@@ -357,12 +368,16 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int max_seq_len,
  * kvq_quantize_append with n_new = 1 and new_lens = NULL; seq_lens must
  * already count the new token), then attends as kvq_decode_attn.  The
  * stored codes and metadata and the output are bit for bit those of the two
- * calls.  With per-token fp32 or fp16 scales (with or without a zero point)
- * and no window, middle tier or token groups, one kernel does both: the
- * workgroup whose split holds a sequence's new token quantizes and stores it
- * before reading that split.  Otherwise it launches the append kernels and
- * then the decode kernel.  Errors as kvq_quantize_append and kvq_decode_attn;
- * KVQ_ERR_INVALID_ARG if k_new or v_new is NULL. */
+ * calls, also for a sequence whose length exceeds the cache's capacity (its
+ * new token is not stored, as kvq_quantize_append skips it).  With per-token
+ * fp32 or fp16 scales (with or without a zero point) and no window, middle
+ * tier or token groups, one kernel does both: the workgroup whose split
+ * holds a sequence's new token quantizes and stores it before reading that
+ * split.  Otherwise it launches the append kernels and then the decode
+ * kernel.  Every argument of both halves is checked before anything is
+ * launched, so a call that returns an error has not changed the cache.
+ * Errors as kvq_quantize_append and kvq_decode_attn; KVQ_ERR_INVALID_ARG if
+ * k_new or v_new is NULL. */
 kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache, int layer,
                            const void* k_new, const void* v_new, const void* q, float* out,
                            void* workspace, size_t workspace_bytes, int max_seq_len,

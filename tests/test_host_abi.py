@@ -64,6 +64,8 @@ def test_cache_bytes_match_oracle(wid):
     lens = synth.seq_lengths(wl)
     cfg = cfg_of(wl)
     got = K.cache_bytes(cfg, lens)
+    # the per-call decode workspace at the library's split for the longest sequence
+    assert got.pop("workspace") == K.decode_workspace_bytes(cfg, max(lens))
     want = O.cache_bytes(oracle_fmt(wl["key"]), oracle_fmt(wl["value"]), 1, wl["hkv"], wl["d"],
                          lens, wl["window"], wl["block_tokens"],
                          None if wl["block_tokens"] else wl["tokens"], group=wl.get("group", 1),
@@ -83,6 +85,7 @@ def test_middle_tier_bytes_match_oracle(window, mid):
     lens = [0, window + mid + 31, window + mid + 32, 2000]
     cfg = cfg_of(wl, mid_tokens=mid, num_layers=3)
     got = K.cache_bytes(cfg, lens)
+    assert got.pop("workspace") == K.decode_workspace_bytes(cfg, max(lens))
     want = O.cache_bytes(oracle_fmt(spec), oracle_fmt(spec), 3, wl["hkv"], wl["d"], lens, window,
                          0, wl["tokens"], mid=mid)
     assert got == want
@@ -105,6 +108,7 @@ def test_cache_bytes_metadata_cases():
                             key=spec, value=spec, num_layers=5)
         lens = [64, 10, 0]
         got = K.cache_bytes(cfg, lens)
+        assert got.pop("workspace") == K.decode_workspace_bytes(cfg, 64)
         want = O.cache_bytes(oracle_fmt(spec), oracle_fmt(spec), 5, 2, 128, lens, 0, 0, 64)
         assert got == want
         assert got["payload"] == 2 * 5 * 2 * 128 * 74 * bits // 8
@@ -235,6 +239,53 @@ def test_calls_fail_before_launch():
     # n_new == 0 is a no-op
     st = lib.kvq_quantize_append(ctypes.byref(cfg), ctypes.byref(fake), 0, 256, 256, 0, None, None)
     assert st == K.KVQ_OK
+
+
+def test_cache_bytes_workspace_field():
+    """kvq_bytes.workspace is the decode workspace at the library's split for
+    the longest sequence (max_tokens each without host lengths); it is not
+    part of the cache's total, and 0 for a configuration the kernels do not
+    run."""
+    cfg = cfg_of(synth.workload(2))
+    b = K.cache_bytes(cfg, None)
+    assert b["workspace"] == K.decode_workspace_bytes(cfg, 4096) > 0
+    assert b["total"] == b["payload"] + b["metadata"] + b["window"] + b["padding"]
+    assert K.cache_bytes(cfg, [100] * 8)["workspace"] == K.decode_workspace_bytes(cfg, 100)
+    odd = K.make_config(batch=1, num_q_heads=1, num_kv_heads=1, head_dim=64, max_tokens=64,
+                        key=dict(bits=8), value=dict(bits=8))
+    assert K.validate(odd) == K.KVQ_ERR_UNSUPPORTED
+    ob = K.cache_bytes(odd, None)
+    assert ob["total"] > 0 and ob["workspace"] == 0
+
+
+@pytest.mark.parametrize("over", [
+    dict(window=16),                                                    # append kernels, ring
+    dict(mid_tokens=32, window=16),                                     # middle tier
+    dict(key=dict(bits=8, axis="channel"), value=dict(bits=4, scale="u8_super")),
+    dict(),                                                             # the one-kernel step
+])
+def test_decode_step_checks_before_launch(over):
+    """kvq_decode_step checks every argument of its decode half before its
+    append launches anything: a step with a workspace too small, a NULL
+    query or output, or a misaligned workspace returns the error with no
+    GPU call (here, with no GPU, a launch would return KVQ_ERR_HIP), so the
+    cache is never changed by a rejected step."""
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, max_tokens=64,
+                key=dict(bits=8), value=dict(bits=8))
+    cfg = K.make_config(**{**base, **over})
+    assert K.validate(cfg) == K.KVQ_OK
+    fake = K.CacheDesc(*([256] * 8), None, 256, *([256] * 5))
+    lib = K.lib()
+    need = K.decode_workspace_bytes(cfg, 64)
+    step = lambda q, out, ws, wsb: lib.kvq_decode_step(ctypes.byref(cfg), ctypes.byref(fake), 0,
+                                                      256, 256, q, out, ws, wsb, 64, None)
+    assert step(256, 256, 256, 16) == K.KVQ_ERR_WORKSPACE
+    assert step(256, 256, 260, need) == K.KVQ_ERR_WORKSPACE
+    assert step(None, 256, 256, need) == K.KVQ_ERR_INVALID_ARG
+    assert step(256, None, 256, need) == K.KVQ_ERR_INVALID_ARG
+    st = lib.kvq_decode_step(ctypes.byref(cfg), ctypes.byref(fake), 0, None, 256, 256, 256, 256,
+                             need, 64, None)
+    assert st == K.KVQ_ERR_INVALID_ARG
 
 
 def test_workspace_grows_with_length():
