@@ -62,15 +62,19 @@ def make_config(wl, lens, num_blocks=0, max_blocks=0):
 
 
 def build(wl: dict, lens: List[int], decode_steps: int = 0, replica: int = 0,
-          oracle: bool = True, chunks: int = 1) -> Built:
+          oracle: bool = True, chunks: int = 1, tokens: Optional[dict] = None,
+          table_lens: Optional[List[int]] = None) -> Built:
     """Prefill each sequence with lens[b] - decode_steps tokens (split into
     `chunks` appends of ragged sizes), then append decode_steps single tokens;
-    the device and the oracle see the same tokens in the same appends."""
+    the device and the oracle see the same tokens in the same appends.
+    tokens: {(b, h): (k [n, D], v [n, D])} float32 arrays exact in the input
+    dtype, instead of the workload's draws.  table_lens: lengths the block
+    table of a paged cache is sized for (later appends may grow to them)."""
     B, H, D = wl["batch"], wl["hkv"], wl["d"]
     table = None
     nb = mb = 0
     if wl["block_tokens"]:
-        table, pool = synth.block_table(wl, lens, replica)
+        table, pool = synth.block_table(wl, table_lens or lens, replica)
         nb, mb = max(pool, 1), table.shape[1]
     cfg = make_config(wl, lens, nb, mb)
     assert K.validate(cfg) == K.KVQ_OK
@@ -80,7 +84,8 @@ def build(wl: dict, lens: List[int], decode_steps: int = 0, replica: int = 0,
     full = {}
     for b in range(B):
         for h in range(H):
-            full[b, h] = synth.kv_tokens(wl, b, h, lens[b], replica)
+            full[b, h] = tokens[b, h] if tokens is not None else synth.kv_tokens(wl, b, h, lens[b],
+                                                                               replica)
     pre = [max(n - decode_steps, 0) for n in lens]
     # prefill, possibly in several ragged appends
     bounds = [[(pre[b] * i) // chunks for i in range(chunks + 1)] for b in range(B)]
