@@ -19,7 +19,17 @@ warm single-replica step time, the decode-append time for one token per
 sequence, the time of append + attention back to back (the whole decode step
 of one layer), and the CPU oracle baseline.
 
-  python bench.py [--config 2] [--steps 200] [--warmup 500]
+The default workload is 4 (paged_mixed: 64 sequences of 1024-32768 tokens,
+64 query / 8 KV heads, int8 with a 128-token bf16 window in 16-token pages),
+the largest that fits one GPU.  The same run also times the decode of the
+other int8 / int4 workloads (2, 3 and 5) and records them under "also".
+
+Before the W warm-up steps the decode runs untimed for --settle-ms of GPU
+time: the GPU's clocks take some tens of milliseconds of sustained decode to
+settle (on one MI355X, after 20 warm-up steps the timed steps ran 7-14 %
+slower than after 500).
+
+  python bench.py [--config 4] [--steps 200] [--warmup 20] [--also 2,3,5]
   python bench.py --copy-probe 1073741824   (plain copy kernel, for counters)
 """
 from __future__ import annotations
@@ -44,12 +54,15 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    # untimed steps before the timed region; the GPU's clocks take some tens
-    # of milliseconds of sustained decode to settle (measured on one MI355X:
-    # after 20 warm-up steps the VALU-heavy 2-bit step ran 45.8 us, after 500
-    # steps 39.3 us)
-    p.add_argument("--warmup", type=int, default=500)
-    p.add_argument("--config", type=int, default=2, help="workload 1..8 (default 2: GQA int8)")
+    p.add_argument("--warmup", type=int, default=20, help="untimed steps before the timed region")
+    # untimed decode before the warm-up steps, in milliseconds of GPU time
+    # (clock settling; measured on one MI355X: after 20 steps the VALU-heavy
+    # 2-bit step ran 45.8 us, after 500 steps 39.3 us)
+    p.add_argument("--settle-ms", type=float, default=300.0)
+    p.add_argument("--config", type=int, default=4,
+                   help="workload 1..8 (default 4: paged int8 with a bf16 window, the largest)")
+    p.add_argument("--also", default="2,3,5",
+                   help="other workloads whose decode is timed in the same run ('' = none)")
     p.add_argument("--replicas", type=int, default=0, help="cache copies (0 = enough for 1 GiB)")
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     p.add_argument("--query-bits", type=int, default=0,
@@ -136,6 +149,7 @@ def cpu_baseline(wl, lens, seconds: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
+    host_cpus = len(os.sched_getaffinity(0))
     fmt = lambda s: O.TensorFormat(s["bits"], s.get("axis", "token"), bool(s.get("zero_point")),
                                    s.get("scale", "f32"))
     G = wl["hq"] // wl["hkv"]
@@ -178,7 +192,9 @@ def cpu_baseline(wl, lens, seconds: float):
     return {
         "value": round(total_bytes / step_s / 1e9, 3), "unit": "GB/s",
         "us_per_step": round(step_s * 1e6, 1), "cores": threads, "kind": "oracle",
-        "cpu": cpu_model(),
+        "host_cpus": host_cpus, "cpu": cpu_model(),
+        "cores_note": "cores = BLAS threads the oracle's matrix products ran on; host_cpus = "
+                      "CPUs this process may use (sched_getaffinity)",
         "sample": f"{n_groups} (sequence, KV head) group attends ({len(groups)} per step, "
                   f"{passes} pass(es) over them), {done_tokens} tokens, {elapsed:.2f} s of fp64 "
                   f"dequantize-then-attend, scaled by bytes to one full step",
@@ -254,25 +270,13 @@ def ab_path(args, wl, caches, q, out, max_len, K, torch):
     return res
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the decode "
-              "path has no multi-GPU mode (sequences and KV heads are independent, so several "
-              "GPUs would each run this same single-GPU kernel on their share).", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_probe:
-        copy_probe(args.copy_probe, max(args.steps, 1))
-        return
+def setup_workload(wid, args, K, synth, torch):
+    """Cache (and replicas), query, output and workspace of one workload."""
     import numpy as np
-    import torch
-    from decode_attention_quantized_kvq_amd import kvq as K
-    from decode_attention_quantized_kvq_amd import synth
-
-    wl = synth.workload(args.config)
+    wl = synth.workload(wid)
     lens = synth.seq_lengths(wl)
     max_len = max(lens)
-    log(f"[bench] workload {args.config} {wl['name']}: building cache")
+    log(f"[bench] workload {wid} {wl['name']}: building cache")
     t0 = time.time()
     cfg, cache = build_cache(wl, lens, K, synth, torch)
     traffic = K.decode_traffic_bytes(cfg, lens)
@@ -282,7 +286,6 @@ def main():
     caches = [cache] + [replicate(cache, K, torch) for _ in range(reps - 1)]
     torch.cuda.synchronize()
     log(f"[bench] {reps} replica(s) of {traffic / 1e6:.1f} MB built in {time.time() - t0:.1f} s")
-
     q = torch.from_numpy(np.stack([synth.queries(wl, b) for b in range(wl["batch"])]))
     q = q.to(torch.bfloat16 if wl["in_dtype"] == "bf16" else torch.float32).cuda()
     out = torch.empty((wl["batch"], wl["hq"], wl["d"]), dtype=torch.float32, device="cuda")
@@ -293,34 +296,80 @@ def main():
         K.decode_attn(caches[i % reps], 0, q, max_len, out=out, workspace=ws,
                       split_tokens=args.split, split_events=events, query_bits=args.query_bits)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # timed region: K steps between two events on the stream
+    return dict(wl=wl, lens=lens, max_len=max_len, cfg=cfg, caches=caches, reps=reps,
+                traffic=traffic, q=q, out=out, ws=ws, step=step)
+
+
+def time_decode(w, args, torch):
+    """Settles the clocks, runs the warm-up steps, then times exactly
+    args.steps decode steps between two events (ms per step), and the split
+    kernel's own duration per launch with dispatch-stamped events."""
+    step = w["step"]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(args.steps):
+    # clock settling: untimed decode for about args.settle_ms of GPU time,
+    # measured in batches of steps
+    i = 0
+    if args.settle_ms > 0:
+        settled = 0.0
+        n = 8
+        while settled < args.settle_ms:
+            e0.record()
+            for _ in range(n):
+                step(i)
+                i += 1
+            e1.record()
+            torch.cuda.synchronize()
+            settled += e0.elapsed_time(e1)
+            n = min(n * 2, 4096)
+    for _ in range(args.warmup):
         step(i)
+        i += 1
+    torch.cuda.synchronize()
+    # timed region: K steps between two events on the stream
+    e0.record()
+    for k in range(args.steps):
+        step(k)
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.2f} us/step")
-
-    # split-kernel duration: events recorded by the library around it
+    # split-kernel duration: events stamped by the dispatch itself
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(args.steps)]
     for a, b in pairs:
         a.record()
         b.record()
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, pairs[i])
+    for k in range(args.steps):
+        step(k, pairs[k])
     torch.cuda.synchronize()
     split_each = [a.elapsed_time(b) for a, b in pairs]
     split_ms = sum(split_each) / args.steps
-    log(f"[bench] split kernel: {split_ms * 1e3:.2f} us/launch")
+    return ms_step, split_ms, split_each
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the decode "
+              "path has no multi-GPU mode (sequences and KV heads are independent, so several "
+              "GPUs would each run this same single-GPU kernel on their share).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+    import torch
+    from decode_attention_quantized_kvq_amd import kvq as K
+    from decode_attention_quantized_kvq_amd import synth
+
+    w = setup_workload(args.config, args, K, synth, torch)
+    wl, lens, max_len, caches, reps = w["wl"], w["lens"], w["max_len"], w["caches"], w["reps"]
+    q, out, ws, step, traffic = w["q"], w["out"], w["ws"], w["step"], w["traffic"]
+    ms_step, split_ms, split_each = time_decode(w, args, torch)
+    log(f"[bench] {args.steps} steps: {ms_step * 1e3:.2f} us/step; split kernel "
+        f"{split_ms * 1e3:.2f} us/launch")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
 
     # warm: the same replica every step (working set may sit in the 256 MB
     # Infinity Cache; context only)
@@ -411,11 +460,12 @@ def main():
         "data": "synthetic (seeded; no dataset on the pages)",
         "config": {"workload": wl["name"], "batch": wl["batch"], "q_heads": wl["hq"],
                    "kv_heads": wl["hkv"], "head_dim": wl["d"], "tokens": max_len,
+                   "total_tokens": int(sum(lens)),
                    "key": wl["key"], "value": wl["value"], "window": wl["window"],
                    "block_tokens": wl["block_tokens"], "group_tokens": wl.get("group", 1),
                    "mid_tokens": wl.get("mid", 0), "replicas": reps,
                    "split_tokens": args.split or "auto", "query_bits": args.query_bits,
-                   "kernel_sources": sha},
+                   "settle_ms": args.settle_ms, "kernel_sources": sha},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": hbm, "kernel": "decode_split",
@@ -431,6 +481,27 @@ def main():
     }
     if ab is not None:
         result["ab_dequantize_then_decode"] = ab
+    # the decode of the other int8 / int4 workloads, timed the same way
+    also = {}
+    del w, caches, q, out, ws, step
+    torch.cuda.empty_cache()
+    for wid in [int(x) for x in args.also.split(",") if x.strip()]:
+        if wid == args.config:
+            continue
+        o = setup_workload(wid, args, K, synth, torch)
+        ms_o, split_o, _ = time_decode(o, args, torch)
+        frac = o["traffic"] / (split_o * 1e-3) / 1e9 / PEAK_HBM_GBS
+        also[o["wl"]["name"]] = {
+            "us_per_step": round(ms_o * 1e3, 2), "avg_launch_us": round(split_o * 1e3, 2),
+            "algorithmic_bytes_per_launch": o["traffic"], "frac": round(frac, 4),
+            "value_gbs": round(o["traffic"] / (ms_o * 1e-3) / 1e9, 1),
+            "traffic": load_traffic("decode_split", o["wl"]["name"], sha)}
+        log(f"[bench] also {o['wl']['name']}: {ms_o * 1e3:.2f} us/step, split kernel "
+            f"{split_o * 1e3:.2f} us, frac {frac:.4f}")
+        del o
+        torch.cuda.empty_cache()
+    if also:
+        result["also"] = also
     if not args.no_cpu:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(wl, lens, args.cpu_seconds)
