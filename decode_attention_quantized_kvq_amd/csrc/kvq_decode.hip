@@ -35,6 +35,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1857,7 +1858,46 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
+// Clears n words (the arrival counters of the no-allocation scratch).
+__global__ void __launch_bounds__(256) zero_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 }  // namespace
+
+// The scratch of kvq_decode_attn_noalloc.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address, one per GPU,
+// comes from hipGetSymbolAddress and is the only way host code refers to it.
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+uint8_t* scratch_at[MAX_DEVICES] = {};  // device address of each GPU's copy
+}  // namespace
+
+kvq_status noalloc_scratch(void* stream, uint8_t** base) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return KVQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_at[dev]) {
+    // first use on this device (the current one): its copy's address, then
+    // its arrival counters cleared by a kernel (no memset node, so the call
+    // can sit in a captured graph); every decode leaves them at zero again
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return KVQ_ERR_HIP;
+    constexpr int words = (int)(NOALLOC_COUNTER_BYTES / 4);
+    hipLaunchKernelGGL(zero_words, dim3(words / 256), dim3(256), 0, (hipStream_t)stream,
+                       (uint32_t*)p, words);
+    if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+    scratch_at[dev] = (uint8_t*)p;
+  }
+  *base = scratch_at[dev];
+  return KVQ_OK;
+}
 
 kvq_status launch_decode(const DecodeArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;

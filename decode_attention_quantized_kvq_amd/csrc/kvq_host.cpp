@@ -498,7 +498,8 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, const kvq_cache* cache, in
 static kvq_status prepare_decode(const kvq_config* cfg, const kvq_cache* cache, int layer,
                                  const void* q, float* out, void* workspace,
                                  size_t workspace_bytes, int max_seq_len,
-                                 const kvq_decode_opts* opts, DecodeArgs* args) {
+                                 const kvq_decode_opts* opts, DecodeArgs* args,
+                                 size_t counter_region = 0) {
   kvq_status st = check_config(cfg, true);
   if (st != KVQ_OK) return st;
   if (!cache || !q || !out || layer < 0 || layer >= cfg->num_layers || max_seq_len < 0)
@@ -517,7 +518,11 @@ static kvq_status prepare_decode(const kvq_config* cfg, const kvq_cache* cache, 
   // one 1-D grid of nsp x H_kv x B workgroups of 256 threads
   if ((unsigned long long)p.nsp * cfg->num_kv_heads * cfg->batch >= (1ull << 24))
     return KVQ_ERR_UNSUPPORTED;
-  if (!workspace || workspace_bytes < p.total) return KVQ_ERR_WORKSPACE;
+  // the arrival counters come first: the plan's own region, or a fixed one
+  // (counter_region bytes) that the partials never overlap
+  const size_t cnt = counter_region ? counter_region : p.cnt_bytes;
+  if (p.cnt_bytes > cnt) return KVQ_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < cnt + p.ml_bytes + p.o_bytes) return KVQ_ERR_WORKSPACE;
   if ((uintptr_t)workspace & 255) return KVQ_ERR_WORKSPACE;
   DecodeArgs a{};
   const LayerSizes s = layer_sizes(cfg);
@@ -540,8 +545,8 @@ static kvq_status prepare_decode(const kvq_config* cfg, const kvq_cache* cache, 
   a.q = q;
   a.out = out;
   a.counters = (uint32_t*)workspace;
-  a.part_ml = (float*)((uint8_t*)workspace + p.cnt_bytes);
-  a.part_o = (float*)((uint8_t*)workspace + p.cnt_bytes + p.ml_bytes);
+  a.part_ml = (float*)((uint8_t*)workspace + cnt);
+  a.part_o = (float*)((uint8_t*)workspace + cnt + p.ml_bytes);
   a.batch = cfg->batch;
   a.hq = cfg->num_q_heads;
   a.hkv = cfg->num_kv_heads;
@@ -616,6 +621,25 @@ kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache, int la
   st = launch_append(ap, stream);
   if (st != KVQ_OK) return st;
   return launch_decode(d, stream);
+}
+
+kvq_status kvq_decode_attn_noalloc(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                                   const void* q, float* out, int max_seq_len, void* stream) {
+  // Every check runs first, against the scratch's size and layout at a
+  // placeholder (aligned) address: a rejected call launches nothing and
+  // does not touch the scratch.
+  uint8_t* const placeholder = (uint8_t*)(uintptr_t)256;
+  DecodeArgs a{};
+  kvq_status st = prepare_decode(cfg, cache, layer, q, out, placeholder, NOALLOC_SCRATCH_BYTES,
+                                 max_seq_len, nullptr, &a, NOALLOC_COUNTER_BYTES);
+  if (st != KVQ_OK) return st;
+  uint8_t* base = nullptr;
+  st = noalloc_scratch(stream, &base);  // this device's copy of the scratch
+  if (st != KVQ_OK) return st;
+  a.counters = (uint32_t*)base;
+  a.part_ml = (float*)(base + ((uint8_t*)a.part_ml - placeholder));
+  a.part_o = (float*)(base + ((uint8_t*)a.part_o - placeholder));
+  return launch_decode(a, stream);
 }
 
 kvq_status kvq_decode_attn(const kvq_config* cfg, const kvq_cache* cache, int layer,

@@ -142,6 +142,17 @@ struct DequantArgs {
   TensorKind kk, vk;
 };
 
+// Scratch of kvq_decode_attn_noalloc: one array per device, held by the
+// library until the process ends.  The first NOALLOC_COUNTER_BYTES hold
+// the arrival counters (one uint32 per (sequence, KV head), at most 16384);
+// the partials follow.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
+constexpr size_t NOALLOC_COUNTER_BYTES = size_t(64) << 10;
+
+// This device's scratch address (looked up once per device, when its
+// arrival counters are also cleared by a kernel on `stream`).
+kvq_status noalloc_scratch(void* stream, uint8_t** base);
+
 kvq_status launch_append(const AppendArgs& a, void* stream);
 kvq_status launch_dequant(const DequantArgs& a, void* stream);
 kvq_status launch_decode(const DecodeArgs& a, void* stream);

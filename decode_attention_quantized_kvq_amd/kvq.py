@@ -33,6 +33,7 @@ EXPORTS = (
     "kvq_status_string", "kvq_validate", "kvq_get_buffer_sizes", "kvq_cache_bytes",
     "kvq_decode_traffic_bytes", "kvq_decode_workspace_bytes", "kvq_quantize_append",
     "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_dequantize", "kvq_decode_step",
+    "kvq_decode_attn_noalloc",
 )
 
 
@@ -118,6 +119,8 @@ def lib() -> ctypes.CDLL:
                                          P(DecodeOpts), VP]
         L.kvq_dequantize.restype = I
         L.kvq_dequantize.argtypes = [P(Config), P(CacheDesc), I, VP, VP, I, VP]
+        L.kvq_decode_attn_noalloc.restype = I
+        L.kvq_decode_attn_noalloc.argtypes = [P(Config), P(CacheDesc), I, VP, VP, I, VP]
         L.kvq_decode_step.restype = I
         L.kvq_decode_step.argtypes = [P(Config), P(CacheDesc), I, VP, VP, VP, VP, VP, S, I, VP]
         _lib = L
@@ -297,6 +300,22 @@ def decode_attn(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
                                     workspace.numel() * workspace.element_size(),
                                     int(max_seq_len), ctypes.byref(opts), _stream(stream)),
            "kvq_decode_attn")
+    return out
+
+
+def decode_attn_noalloc(cache: KvqCache, layer: int, q: torch.Tensor, max_seq_len: int,
+                        out: torch.Tensor, stream=None) -> torch.Tensor:
+    """kvq_decode_attn_noalloc: as decode_attn, with the library's own
+    per-GPU scratch instead of a workspace; `out` is caller-allocated."""
+    cfg = cache.cfg
+    _check_input(q, cfg, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "q")
+    if (out.dtype != torch.float32 or not out.is_contiguous() or not out.is_cuda
+            or tuple(out.shape) != (cfg.batch, cfg.num_q_heads, cfg.head_dim)):
+        raise ValueError("out: expected contiguous fp32 [B][Hq][D] on the GPU")
+    desc = cache.desc()
+    _check(lib().kvq_decode_attn_noalloc(ctypes.byref(cfg), ctypes.byref(desc), int(layer),
+                                         _ptr(q), _ptr(out), int(max_seq_len), _stream(stream)),
+           "kvq_decode_attn_noalloc")
     return out
 
 

@@ -383,6 +383,23 @@ kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache, int la
                            void* workspace, size_t workspace_bytes, int max_seq_len,
                            void* stream);
 
+/* kvq_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument.  The split partials and arrival
+ * counters live in a scratch array the library holds on each GPU it runs
+ * on, 16 MiB per GPU, kept until the process ends; the call itself
+ * allocates nothing.  Its first call on a device looks up that device's
+ * copy and clears its counters with a kernel on `stream`.  Accepted calls:
+ * batch x num_kv_heads <= 16384 and partial rows (batch x num_q_heads x
+ * (splits + 1 per bf16 window and middle tier)) x (head_dim + 2) x 4 bytes
+ * within the rest (about 16 MiB); a larger call returns KVQ_ERR_WORKSPACE
+ * and launches nothing.  Calls on one GPU share its scratch: calls that
+ * overlap in time on one GPU (other streams, other threads) race, and must
+ * be ordered by the caller.  Otherwise as kvq_decode_attn (same kernels,
+ * same split plan, bit-identical outputs). */
+kvq_status kvq_decode_attn_noalloc(const kvq_config* cfg, const kvq_cache* cache, int layer,
+                                   const void* q, float* out, int max_seq_len, void* stream);
+
 /* kvq_decode_attn with tuning knobs (opts may be NULL). */
 kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int layer,
                               const void* q, float* out, void* workspace,
