@@ -82,7 +82,8 @@ def log(*a):
 
 # The sources that define the decode kernel and its launch (split plan, grid,
 # workspace layout): the counter summaries are valid while these are unchanged.
-DECODE_SOURCES = ("kvq_decode.hip", "kvq_host.cpp", "kvq_internal.h", "kvq_quantize.h")
+DECODE_SOURCES = ("kvq_decode.hip", "kvq_decode_kernel.h", "kvq_decode_w4.hip", "kvq_decode_mixed.hip",
+                  "kvq_decode_w2.hip", "kvq_host.cpp", "kvq_internal.h", "kvq_quantize.h")
 
 
 def kernel_source_sha() -> str:

@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_dequant.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_w4.hip",
+           "kvq_decode_mixed.hip", "kvq_decode_w2.hip", "kvq_dequant.hip"]
 OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
