@@ -71,6 +71,9 @@ def parse():
                    help="also time the dequantize-into-temporary-storage path")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU baseline time budget")
+    p.add_argument("--phases", action="store_true",
+                   help="per-workgroup phase breakdown of the decode kernel, from the instrumented "
+                        "build (python -m decode_attention_quantized_kvq_amd.build --phase-stamps)")
     p.add_argument("--copy-probe", type=int, default=0,
                    help="run only a plain device copy of this many bytes (counter calibration)")
     return p.parse_args()
@@ -349,8 +352,73 @@ def time_decode(w, args, torch):
     return ms_step, split_ms, split_each
 
 
+PHASE_STAMP_BYTES = 65536 * 64   # the instrumented build's stamp region (end of the workspace)
+
+
+def phase_breakdown(w, args, torch, launches: int = 5):
+    """Per-workgroup phases of `launches` decode launches of the instrumented
+    build (times in us from the first workgroup's start, 100 MHz counter).
+    Each workgroup's first thread stamps: 0 start, 1 work item known, 2 query
+    ready (its first tiles in flight), 3 its wave's tiles done, 4 partial
+    stored, 5 arrival counted, 6 end; 7 holds the hardware ids."""
+    import numpy as np
+    ws = w["ws"]
+    reg = ws[ws.numel() - PHASE_STAMP_BYTES:]
+    out = []
+    for i in range(launches):
+        reg.zero_()
+        torch.cuda.synchronize()
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ev[0].record()
+        ev[1].record()
+        torch.cuda.synchronize()
+        w["step"](i, ev)
+        torch.cuda.synchronize()
+        st = reg.cpu().numpy().view(np.uint64).reshape(-1, 8).astype(np.int64)
+        n = int(np.nonzero(st[:, 0])[0].max()) + 1
+        st = st[:n]
+        t0 = st[:, 0].min()
+        rel = lambda c: (st[:, c] - t0) / 100.0
+        streamed = st[:, 3] > 0
+        end = np.where(st[:, 6] > 0, ((st[:, 6] >> 1) - t0) / 100.0, np.maximum(rel(1), rel(4)))
+        combined = (st[:, 6] & 1) == 1
+        hw, xcc = st[:, 7] & 0xFFFFFFFF, (st[:, 7] >> 32) & 0xF
+        cu = xcc * 1000 + ((hw >> 13) & 7) * 100 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 0xF)
+        cus = np.unique(cu)
+        cu_end = np.array([rel(3)[streamed & (cu == c)].max() for c in cus if (streamed & (cu == c)).any()])
+        pct = lambda x, p: round(float(np.percentile(x, p)), 2) if len(x) else None
+        out.append({
+            "kernel_us_events": round(ev[0].elapsed_time(ev[1]) * 1e3, 2),
+            "span_us": round(float(end.max()), 2), "workgroups": n, "cus": int(len(cus)),
+            "start_p50_max": [pct(rel(0), 50), pct(rel(0), 100)],
+            "item_known_after_start_p50": pct(rel(1) - rel(0), 50),
+            "query_ready_after_item_p50_p90": [pct((rel(2) - rel(1))[streamed], p) for p in (50, 90)],
+            "tiles_us_p10_p50_p90": [pct((rel(3) - rel(2))[streamed], p) for p in (10, 50, 90)],
+            "cu_tiles_done_min_p50_max": [round(float(cu_end.min()), 2), pct(cu_end, 50),
+                                          round(float(cu_end.max()), 2)],
+            "partial_stored_after_tiles_p50_p90": [pct((rel(4) - rel(3))[streamed], p) for p in (50, 90)],
+            "arrival_after_store_p50_p90": [pct((rel(5) - rel(4))[streamed & (st[:, 5] > 0)], p)
+                                            for p in (50, 90)],
+            "combine_us_p50_p90": [pct((end - rel(5))[combined], p) for p in (50, 90)],
+            "end_p50_p90_max": [pct(end, p) for p in (50, 90, 100)],
+        })
+        j = int(np.argmax(end))
+        out[-1]["last_workgroup"] = {k: round(float(v), 2) for k, v in (
+            ("start", rel(0)[j]), ("item_known", rel(1)[j]), ("query_ready", rel(2)[j]),
+            ("tiles_done", rel(3)[j]), ("partial_stored", rel(4)[j]), ("arrived", rel(5)[j]),
+            ("end", end[j]))}
+        log(f"[bench] phases launch {i}: {json.dumps(out[-1])}")
+    return out
+
+
 def main():
     args = parse()
+    if args.phases:
+        from decode_attention_quantized_kvq_amd import build as B
+        if not os.path.exists(B.PHASES_LIB):
+            raise SystemExit(f"{B.PHASES_LIB} is missing: build it with "
+                             "python -m decode_attention_quantized_kvq_amd.build --phase-stamps")
+        os.environ["KVQ_LIB"] = B.PHASES_LIB
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the decode "
               "path has no multi-GPU mode (sequences and KV heads are independent, so several "
@@ -369,6 +437,11 @@ def main():
     ms_step, split_ms, split_each = time_decode(w, args, torch)
     log(f"[bench] {args.steps} steps: {ms_step * 1e3:.2f} us/step; split kernel "
         f"{split_ms * 1e3:.2f} us/launch")
+    if args.phases:
+        ph = phase_breakdown(w, args, torch)
+        print(json.dumps({"workload": wl["name"], "avg_launch_us": round(split_ms * 1e3, 2),
+                          "kernel_sources": kernel_source_sha(), "phases": ph}), flush=True)
+        return
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
 

@@ -1,6 +1,6 @@
 """Builds libkvq.so (host code + gfx950 kernels) in this package's directory.
 
-Usage: python -m decode_attention_quantized_kvq_amd.build
+Usage: python -m decode_attention_quantized_kvq_amd.build [--phase-stamps]
 """
 import os
 import subprocess
@@ -65,5 +65,13 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+# An instrumented build, libkvq_phases.so: every decode workgroup stamps the
+# real-time counter at each phase into the workspace (bench.py --phases).
+PHASES_LIB = os.path.join(PKG, "libkvq_phases.so")
+
+
 if __name__ == "__main__":
-    print(build(verbose="-q" not in sys.argv))
+    if "--phase-stamps" in sys.argv:
+        print(build(verbose="-q" not in sys.argv, out=PHASES_LIB, defines=["KVQ_PHASE_STAMPS"]))
+    else:
+        print(build(verbose="-q" not in sys.argv))

@@ -30,10 +30,18 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int D = 128;
 constexpr int WAVES = 4;
 constexpr int TILE = 32;
-// Tiles each wave keeps in flight, by bytes per token (key + value codes):
-// narrow tiles need more of them to cover the memory latency.
+// Tiles each wave keeps in flight, by code bytes per token (key + value):
+// more than the memory needs only queues (the first data of a new work item
+// then waits behind it), fewer leaves it idle.  Measured on one MI355X
+// (non-temporal loads): 256 bytes (int8 / int8, paged 64 x 8 heads) 407 us
+// with two against 419 with one; 192 bytes (per-channel int8 keys, int4
+// values) 257 us with one against 262 with two; 128 bytes (uint4 / uint4)
+// 51.1 us with two against 53.9 with one.
 #ifndef KVQ_NB8
 #define KVQ_NB8 2
+#endif
+#ifndef KVQ_NB6
+#define KVQ_NB6 1
 #endif
 #ifndef KVQ_NB4
 #define KVQ_NB4 2
@@ -158,6 +166,22 @@ __device__ inline float pow2_ceil(float x) {
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Phase stamps of an instrumented build (KVQ_PHASE_STAMPS; the 100 MHz
+// real-time counter) written by each workgroup's first thread: 0 start,
+// 1 work item known, 2 query ready, 3 the wave's tiles done, 4 partial
+// stored, 5 arrival counted, 6 end (times 2, plus 1 if it combined),
+// 7 hardware ids (XCC id << 32 | HW_ID).  Compiled out otherwise.
+__device__ inline void phase_stamp(unsigned long long* stamps, int i, unsigned long long v) {
+#ifdef KVQ_PHASE_STAMPS
+  if (stamps != nullptr && threadIdx.x == 0 && blockIdx.x < 65536u) stamps[blockIdx.x * 8 + i] = v;
+#endif
+}
+__device__ inline void phase_stamp(unsigned long long* stamps, int i) {
+#ifdef KVQ_PHASE_STAMPS
+  phase_stamp(stamps, i, __builtin_amdgcn_s_memrealtime());
+#endif
+}
 
 // ---------------------------------------------------------------------------
 // Code formats: byte layout per token row and conversion to fp16 MFMA operands
@@ -1290,7 +1314,11 @@ __device__ void arrive_and_combine(const DecodeArgs& a, int b, int h, const Plan
     *flag = last;
   }
   __syncthreads();
+  phase_stamp(a.stamps, 5);
   if (*flag) combine_heads<G>(a, b, h, pl);
+#ifdef KVQ_PHASE_STAMPS
+  phase_stamp(a.stamps, 6, (__builtin_amdgcn_s_memrealtime() << 1) | (*flag ? 1u : 0u));
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -1514,7 +1542,7 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
   // wait counts from that order, and interleaved loads would make every wait
   // in the loop a wait for all of them.
   constexpr int ROWB = Codes<KC>::ROW + Codes<VC>::ROW;
-  constexpr int NB = ROWB >= 192 ? KVQ_NB8 : ROWB >= 128 ? KVQ_NB4 : KVQ_NB2;
+  constexpr int NB = ROWB >= 256 ? KVQ_NB8 : ROWB >= 192 ? KVQ_NB6 : ROWB >= 128 ? KVQ_NB4 : KVQ_NB2;
   TileRaw<KC, KM, VC, VM> buf[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
@@ -1598,6 +1626,7 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
   const uint32_t* prd = &sh.pw[wave][phc][4 * g][0];
   const uint32_t psel = !pvalid ? 0x0c0c0c0cu : (plimb == 0 ? 0x05040100u : 0x07060302u);
 
+  phase_stamp(a.stamps, 2);
   // 4. stream the range: compute one buffer, refill it two tiles ahead
   NibbleMasks nm;
   nm.init();
@@ -1625,12 +1654,14 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
     if (k < rem)
       compute_tile<KC, KM, KCH, VC, VM, G>(buf[k], t + k * TILE, w1, qa, qs, sumq, lt, g, psel, prd,
                                            pwr, nm, st);
+  phase_stamp(a.stamps, 3);
   float scale_out[HPG];
 #pragma unroll
   for (int u = 0; u < HPG; ++u)
     scale_out[u] = VM == MK_U8 ? 256.0f * a.v_super[(size_t)b * a.hkv + h] : st.R[u];
   row_finish<G>(st, scale_out, lt, g, wave, sh);
   block_merge<G>(a, sh, b, h, row);
+  phase_stamp(a.stamps, 4);
 }
 
 
@@ -1675,9 +1706,19 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   __shared__ int hist[WAVES][NSIZE];
   // workgroup p < batch * hkv also writes the (zero) output of pair p if
   // its sequence is empty
+  phase_stamp(a.stamps, 0);
+#ifdef KVQ_PHASE_STAMPS
+  {
+    unsigned hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    phase_stamp(a.stamps, 7, ((unsigned long long)xcc << 32) | hw);
+  }
+#endif
   const bool zduty = blockIdx.x < (unsigned)(a.batch * a.hkv);
   const int zlen = zduty ? a.seq_lens[blockIdx.x / a.hkv] : 1;
   const Item it = map_item(a, blockIdx.x, hist[threadIdx.x >> 6], TIER);
+  phase_stamp(a.stamps, 1);
   if (zduty && zlen <= 0) {
     const int zb = blockIdx.x / a.hkv, zh = blockIdx.x % a.hkv;
     for (int idx = threadIdx.x; idx < G * D; idx += WAVES * 64)

@@ -215,6 +215,9 @@ static Plan make_plan(const kvq_config* c, int max_seq_len, int split_tokens) {
   // the plan: a workspace that stays zero there serves calls with any
   // max_seq_len or split whose plan fits it
   p.total = p.cnt_bytes + p.ml_bytes + p.o_bytes;
+#ifdef KVQ_PHASE_STAMPS
+  p.total += PHASE_STAMP_BYTES;  // instrumented build: per-workgroup phase stamps
+#endif
   return p;
 }
 
@@ -522,7 +525,8 @@ static kvq_status prepare_decode(const kvq_config* cfg, const kvq_cache* cache, 
   // (counter_region bytes) that the partials never overlap
   const size_t cnt = counter_region ? counter_region : p.cnt_bytes;
   if (p.cnt_bytes > cnt) return KVQ_ERR_WORKSPACE;
-  if (!workspace || workspace_bytes < cnt + p.ml_bytes + p.o_bytes) return KVQ_ERR_WORKSPACE;
+  const size_t need = cnt + p.ml_bytes + p.o_bytes;
+  if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
   if ((uintptr_t)workspace & 255) return KVQ_ERR_WORKSPACE;
   DecodeArgs a{};
   const LayerSizes s = layer_sizes(cfg);
@@ -568,6 +572,11 @@ static kvq_status prepare_decode(const kvq_config* cfg, const kvq_cache* cache, 
   a.ev_end = opts ? opts->split_end_event : nullptr;
   a.k_new = nullptr;
   a.v_new = nullptr;
+  a.stamps = nullptr;
+#ifdef KVQ_PHASE_STAMPS
+  if (workspace_bytes >= need + PHASE_STAMP_BYTES)
+    a.stamps = (unsigned long long*)((uint8_t*)workspace + workspace_bytes - PHASE_STAMP_BYTES);
+#endif
   if (!resolve_mid(cfg, cache, layer, s, &a.mid)) return KVQ_ERR_INVALID_ARG;
   *args = a;
   return KVQ_OK;
@@ -639,6 +648,7 @@ kvq_status kvq_decode_attn_noalloc(const kvq_config* cfg, const kvq_cache* cache
   a.counters = (uint32_t*)base;
   a.part_ml = (float*)(base + ((uint8_t*)a.part_ml - placeholder));
   a.part_o = (float*)(base + ((uint8_t*)a.part_o - placeholder));
+  a.stamps = nullptr;  // no phase stamps from the scratch (instrumented builds)
   return launch_decode(a, stream);
 }
 

@@ -118,7 +118,14 @@ struct DecodeArgs {
   // for a plain decode
   const void* k_new;
   const void* v_new;
+  // phase stamps of an instrumented build (KVQ_PHASE_STAMPS): 8 words per
+  // workgroup in the workspace's last PHASE_STAMP_BYTES; null otherwise
+  unsigned long long* stamps;
 };
+
+// Instrumented builds (-DKVQ_PHASE_STAMPS) append this many bytes to the
+// decode workspace: 8 stamps of 8 bytes for each of up to 65536 workgroups.
+constexpr size_t PHASE_STAMP_BYTES = size_t(65536) * 64;
 
 // Everything a dequantize launch needs, resolved to one layer.
 struct DequantArgs {
