@@ -326,6 +326,7 @@ def time_decode(w, args, torch):
             torch.cuda.synchronize()
             settled += e0.elapsed_time(e1)
             n = min(n * 2, 4096)
+        log(f"[bench] settle: {i} steps, {settled:.1f} ms")
     for _ in range(args.warmup):
         step(i)
         i += 1
