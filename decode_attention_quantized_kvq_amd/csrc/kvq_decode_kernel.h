@@ -304,6 +304,33 @@ struct Meta {
       r0 = __builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, KVQ_CPOL);
     }
   }
+  // metadata of one token at p (one 1-8 byte load per lane)
+  __device__ inline void load_glob(const uint8_t* p) {
+#if KVQ_CPOL == 2
+#define KVQ_LDM(T, q) __builtin_nontemporal_load((const T*)(q))
+#else
+#define KVQ_LDM(T, q) (*(const T*)(q))
+#endif
+    if (MK == MK_F32 || MK == MK_F16Z) {
+      r0 = KVQ_LDM(uint32_t, p);
+    } else if (MK == MK_F32Z) {
+      const u32x2 v = KVQ_LDM(u32x2, p);
+      r0 = v.x;
+      r1 = v.y;
+    } else if (MK == MK_F16) {
+      r0 = KVQ_LDM(uint16_t, p);
+    } else if (MK == MK_U8) {
+      r0 = KVQ_LDM(uint8_t, p);
+    }
+#undef KVQ_LDM
+  }
+  // the same fields of lane (lane ^ 16)
+  __device__ inline Meta xor16() const {
+    Meta m;
+    m.r0 = BYTES ? (uint32_t)__shfl_xor((int)r0, 16) : 0u;
+    m.r1 = MK == MK_F32Z ? (uint32_t)__shfl_xor((int)r1, 16) : 0u;
+    return m;
+  }
   __device__ inline float scale() const {
     if (MK == MK_F32 || MK == MK_F32Z) return __uint_as_float(r0);
     if (MK == MK_F16 || MK == MK_F16Z)
@@ -386,6 +413,7 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const uint8_t* p, int bytes) {
 // for 64-byte (4-bit) rows.  Metadata: the element of token t's group.
 struct LaneOff {
   uint32_t k0, k1, v[4], km, vm;
+  bool odd;  // g odd: this lane loads the metadata of the tile's second block
 };
 
 template <int KC, int KM, int VC, int VM>
@@ -399,6 +427,7 @@ __device__ inline LaneOff lane_offsets(int t, int g, int gs) {
     o.v[i] = (4 * i + g) * VROW + (Codes<VC>::B8 ? 8 * t : Codes<VC>::B2 ? 2 * t : 4 * t);
   o.km = (t >> gs) * Meta<KM>::BYTES;  // token t's group
   o.vm = (t >> gs) * Meta<VM>::BYTES;
+  o.odd = g & 1;
   return o;
 }
 
@@ -410,8 +439,10 @@ struct TileRaw {
   u32x4 k[2][KB8 ? 2 : 1];   // per 16-token block (2-bit keys: .x, .y)
   u32x2 v8[VB8 ? 8 : 1];     // 8-bit values: 8 tokens x 8 bytes
   uint32_t v4[VB8 ? 1 : 8];  // 4-bit values: 8 tokens x 4 bytes; 2-bit: 2 bytes
-  Meta<KM> km[2];
-  Meta<VM> vm[2];
+  // metadata of token t of block g & 1 (lane (t, g)): one load per tensor
+  // and tile; compute_tile takes the other block's from lane (t, g ^ 1)
+  Meta<KM> km;
+  Meta<VM> vm;
 };
 
 // Loads the 32-token tile at t0 of a wave whose range ends at tend.  Every
@@ -422,10 +453,12 @@ template <bool PAGED, bool RING, int KC, int KM, int VC, int VM>
 __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int t0, int tend,
                                  const LaneOff& o) {
   constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
+  size_t slots[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const bool live = t0 + 16 * bb < tend;
     const size_t slot = block_slot<PAGED, RING>(ad, (t0 >> 4) + bb);
+    slots[bb] = slot;
     const auto rk = rsrc(ad.k + slot * KROW, live ? 16 * KROW : 0);
     if (Codes<KC>::B2) {
       const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rk, o.k0, 0, KVQ_CPOL);
@@ -444,16 +477,14 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int
       else
         t.v4[4 * bb + i] = __builtin_amdgcn_raw_buffer_load_b32(rv, o.v[i], 0, KVQ_CPOL);
     }
-    // metadata element of token slot s: s >> gs (one per token group)
-    if (Meta<KM>::BYTES)
-      t.km[bb].load_buf(rsrc(ad.km + (slot >> ad.gs) * Meta<KM>::BYTES,
-                             live ? (16 >> ad.gs) * Meta<KM>::BYTES : 0),
-                        o.km);
-    if (Meta<VM>::BYTES)
-      t.vm[bb].load_buf(rsrc(ad.vm + (slot >> ad.gs) * Meta<VM>::BYTES,
-                             live ? (16 >> ad.gs) * Meta<VM>::BYTES : 0),
-                        o.vm);
   }
+  // metadata element of token slot s: s >> gs (one per token group).  One
+  // load per tensor covers both blocks (lane (t, g): block g & 1); a block
+  // past tend reads a stored slot (block_slot clamps) whose values
+  // compute_tile masks.
+  const size_t ms = (o.odd ? slots[1] : slots[0]) >> ad.gs;
+  if (Meta<KM>::BYTES) t.km.load_glob(ad.km + ms * Meta<KM>::BYTES + o.km);
+  if (Meta<VM>::BYTES) t.vm.load_glob(ad.vm + ms * Meta<VM>::BYTES + o.vm);
 }
 
 // Key operand of the J-th score MFMA for block bb: 8 int8 values, the codes
@@ -633,6 +664,19 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
       sa[u][1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa[u][J], k1, sa[u][1], 0, 0, 0);
     }
   });
+  // metadata of token lt of blocks 0 and 1: one is this lane's, the other
+  // lane (lt, g ^ 1)'s
+  Meta<KM> kmb[2];
+  Meta<VM> vmb[2];
+  {
+    const bool odd = g & 1;
+    const Meta<KM> ko = t.km.xor16();
+    const Meta<VM> vo = t.vm.xor16();
+    kmb[0] = odd ? ko : t.km;
+    kmb[1] = odd ? t.km : ko;
+    vmb[0] = odd ? vo : t.vm;
+    vmb[1] = odd ? t.vm : vo;
+  }
   // scores before the query scale qs (> 0): sk[u][bb] for token t of block bb
   float sk[HPG][2], vs[2], vz[2];
 #pragma unroll
@@ -646,13 +690,13 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
       if (KCH) {
         v = raw;
       } else {
-        const float off = key_offset<KC>() + (Meta<KM>::ZP ? t.km[bb].zero() : 0.0f);
-        v = (off != 0.0f ? fmaf(-off, sq[u], raw) : raw) * t.km[bb].scale();
+        const float off = key_offset<KC>() + (Meta<KM>::ZP ? kmb[bb].zero() : 0.0f);
+        v = (off != 0.0f ? fmaf(-off, sq[u], raw) : raw) * kmb[bb].scale();
       }
       sk[u][bb] = valid ? v : NEG_INF;
     }
-    vs[bb] = valid ? t.vm[bb].scale() : 0.0f;
-    vz[bb] = Meta<VM>::ZP && valid ? t.vm[bb].zero() : 0.0f;
+    vs[bb] = valid ? vmb[bb].scale() : 0.0f;
+    vz[bb] = Meta<VM>::ZP && valid ? vmb[bb].zero() : 0.0f;
   }
   float f[HPG], p[HPG][2];
   bool moved = false;
@@ -763,17 +807,24 @@ __device__ inline int ring_slot(int i, int nw, int r0, int ring) {
   return ring == 0 || s < ring ? s : s - ring;
 }
 
+// knew, vnew (or null): bf16 rows read in place of ring slot pslot (a
+// decode step's new token, which another workgroup may still be writing
+// there).
 __device__ inline void load_win_tile(WinRaw& t, const uint16_t* kw, const uint16_t* vw, int t0,
-                                     int nw, int r0, int ring, int c, int g) {
+                                     int nw, int r0, int ring, int c, int g,
+                                     const uint16_t* knew = nullptr, const uint16_t* vnew = nullptr,
+                                     int pslot = -1) {
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    const uint16_t* kr = kw + (size_t)ring_slot(t0 + 16 * bb + c, nw, r0, ring) * D;
+    const int sk = ring_slot(t0 + 16 * bb + c, nw, r0, ring);
+    const uint16_t* kr = knew && sk == pslot ? knew : kw + (size_t)sk * D;
 #pragma unroll
     for (int j = 0; j < 4; ++j) t.k[bb][j] = __builtin_nontemporal_load((const u32x4*)(kr + 32 * j + 8 * g));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tv = ring_slot(t0 + 16 * bb + 4 * g + i, nw, r0, ring);
-      t.v[4 * bb + i] = __builtin_nontemporal_load((const u32x4*)(vw + (size_t)tv * D + 8 * c));
+      const int sv = ring_slot(t0 + 16 * bb + 4 * g + i, nw, r0, ring);
+      const uint16_t* vr = vnew && sv == pslot ? vnew : vw + (size_t)sv * D;
+      t.v[4 * bb + i] = __builtin_nontemporal_load((const u32x4*)(vr + 8 * c));
     }
   }
 }
@@ -1046,7 +1097,9 @@ __device__ inline SeqInfo seq_info(const DecodeArgs& a, int b) {
 // PF: keep two tiles in flight per wave (long ranges of a bf16 cache).
 template <int G, bool QB, bool PF>
 __device__ void bf16_tokens(const DecodeArgs& a, int b, int h, const uint16_t* kw,
-                            const uint16_t* vw, int r0, int ring, int nw, int row, Shared<G>& sh) {
+                            const uint16_t* vw, int r0, int ring, int nw, int row, Shared<G>& sh,
+                            const uint16_t* knew = nullptr, const uint16_t* vnew = nullptr,
+                            int pslot = -1) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1133,7 +1186,7 @@ __device__ void bf16_tokens(const DecodeArgs& a, int b, int h, const uint16_t* k
   } else {
     for (int t0 = w0; t0 < w1; t0 += TILE) {
       WinRaw t;
-      load_win_tile(t, kw, vw, t0, nw, r0, ring, c, g);
+      load_win_tile(t, kw, vw, t0, nw, r0, ring, c, g, knew, vnew, pslot);
       compute_win_tile<G>(t, t0, w1, qf, qs, g, limb, st);
     }
   }
@@ -1143,12 +1196,22 @@ __device__ void bf16_tokens(const DecodeArgs& a, int b, int h, const uint16_t* k
 
 // The bf16 tokens of a quantized cache: the window and an open token group,
 // positions [nq, nq + nw) in ring slots (nq + i) mod ring.
+// In a decode step (a.k_new set, bf16 input) ring slot (seq_lens[b] - 1)
+// mod ring, which receives the new token, is read from the input, whose bf16
+// row is what the slot receives: the workgroup that writes the slot may
+// still be reading the token it held.
 template <int G, bool QB>
 __device__ void window_split(const DecodeArgs& a, int b, int h, int q0, int nw, bool direct,
                              Shared<G>& sh) {
   const size_t head = ((size_t)b * a.hkv + h) * a.ring * D;
+  const size_t in_row = ((size_t)b * a.hkv + h) * D;
+  const bool step = a.k_new != nullptr;
+  const int p = step ? a.seq_lens[b] - 1 : -1;
   bf16_tokens<G, QB, false>(a, b, h, a.k_win + head, a.v_win + head, q0 % a.ring, a.ring, nw,
-                            direct ? DIRECT_OUT : a.n_split, sh);
+                            direct ? DIRECT_OUT : a.n_split, sh,
+                            step ? (const uint16_t*)a.k_new + in_row : nullptr,
+                            step ? (const uint16_t*)a.v_new + in_row : nullptr,
+                            p >= 0 ? p % a.ring : -1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1297,19 +1360,20 @@ __device__ void combine_heads(const DecodeArgs& a, int b, int h, const Plan& pl)
   }
 }
 
-// After this workgroup's partial is written: count it in the arrival
-// counter of (b, h); the last of the pl.total workgroups resets the counter
-// and merges.  Each thread first waits for its own partial stores to
+// After this workgroup's partial (or, in a decode step with a window, its
+// two partials) is written: count it in the arrival counter of (b, h); the
+// workgroup that brings the count to pl.total resets the counter and merges.  Each thread first waits for its own partial stores to
 // complete (they write through to memory), so the counter cannot run ahead
 // of the data it announces; no cache-wide fence is needed.
 template <int G>
-__device__ void arrive_and_combine(const DecodeArgs& a, int b, int h, const Plan& pl, int* flag) {
+__device__ void arrive_and_combine(const DecodeArgs& a, int b, int h, const Plan& pl, int* flag,
+                                   uint32_t partials = 1) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t* cnt = a.counters + (size_t)b * a.hkv + h;
-    const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = prev + 1 == (uint32_t)pl.total;
+    const uint32_t prev = __hip_atomic_fetch_add(cnt, partials, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev + partials == (uint32_t)pl.total;
     if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = last;
   }
@@ -1474,16 +1538,29 @@ __device__ Item map_item(const DecodeArgs& a, int item, int* hist, bool tier) {
   return it;
 }
 
+// A decode step with a window: waits until both waves of step_window have
+// counted their stores done in *done (LDS).
+__device__ inline void wait_stored(const int* done) {
+  while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < 2)
+    __builtin_amdgcn_s_sleep(1);
+}
+
 // Attends quantized positions [tok0, tok1) of (sequence b, KV head h) with
 // the G query heads of h and writes partial row `row` (DIRECT_OUT: the
 // output).  The codes and
 // metadata live at kc, vc, km, vm: token slot head_tok + position
 // (contiguous), through the block table (PAGED), or in a ring of rblk
 // 16-token blocks (RING, the middle tier); nend bounds the blocks read.
-template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool RING>
+struct NoPre {
+  __device__ void operator()() const {}
+};
+
+template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool RING,
+          typename Pre = NoPre>
 __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok1, int nend,
                             int row, const uint8_t* kc, const uint8_t* vc, const uint8_t* km,
-                            const uint8_t* vm, size_t head_tok, int rblk, Shared<G>& sh) {
+                            const uint8_t* vm, size_t head_tok, int rblk, Shared<G>& sh,
+                            int wait_pos = -1, const int* stored = nullptr, Pre pre = Pre()) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1543,12 +1620,23 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
   // in the loop a wait for all of them.
   constexpr int ROWB = Codes<KC>::ROW + Codes<VC>::ROW;
   constexpr int NB = ROWB >= 256 ? KVQ_NB8 : ROWB >= 192 ? KVQ_NB6 : ROWB >= 128 ? KVQ_NB4 : KVQ_NB2;
+  // a decode step's position leaving the window (wait_pos >= 0): the tile
+  // that holds it is loaded once its stores are done (wait_stored)
+  const int wtile = wait_pos >= w0 && wait_pos < w1 ? w0 + (wait_pos - w0) / TILE * TILE : 0x7fffffff;
+  // pre: work that waits for memory of its own, done while the first tiles
+  // are in flight (a decode step's move of the token leaving the window);
+  // before them if one of them waits for it
+  const bool pre_first = wtile < w0 + NB * TILE;
+  if (pre_first) pre();
   TileRaw<KC, KM, VC, VM> buf[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
+    if (w0 + k * TILE == wtile) wait_stored(stored);
     load_tile<PAGED, RING>(buf[k], ad, w0 + k * TILE, w1, lo);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (!pre_first) pre();
+  __builtin_amdgcn_sched_barrier(0);
 
   // 3. query operand: Q = rint(q 2^e) per head, |Q| < 2^22, as three int8
   //    limbs Q = l0 2^16 + l1 2^8 + l2 (each in [-128, 127])
@@ -1643,6 +1731,7 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
       compute_tile<KC, KM, KCH, VC, VM, G>(buf[k], t + k * TILE, w1, qa, qs, sumq, lt, g, psel, prd,
                                            pwr, nm, st);
       __builtin_amdgcn_sched_barrier(0);
+      if (t + (k + NB) * TILE == wtile) wait_stored(stored);
       load_tile<PAGED, RING>(buf[k], ad, t + (k + NB) * TILE, w1, lo);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1696,6 +1785,53 @@ __device__ void step_append(const DecodeArgs& a, int b, int h, int p) {
   __syncthreads();
 }
 
+// Decode step with a bf16 window (token groups of 1, no middle tier, bf16
+// input): as kvq_quantize_append with one new token, the token leaving the
+// window (position p - W, from its ring slot) is quantized into the cache
+// unless it lies past the capacity, then the new token (position p) is
+// written into the ring slot that frees (the ring holds W slots); wave 0 the
+// key, wave 1 the value.  evict: the caller attends position p - W (its
+// sequence has quantized tokens).  Each of the two waves waits for its
+// stores, then adds 1 to *done (LDS): a wave of the workgroup that loads
+// position p - W waits for 2 first (wait_stored).
+__device__ void step_window(const DecodeArgs& a, int b, int h, bool evict, int* done) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int p = a.seq_lens[b] - 1;
+  if (w >= 2) return;
+  if (p >= 0) {
+    const size_t head = (size_t)b * a.hkv + h;
+    uint16_t* ring = const_cast<uint16_t*>(w == 0 ? a.k_win : a.v_win);
+    const int e = p - a.window;
+    const int cap = a.paged ? a.bt_stride * 16 : a.max_tokens;
+    if (evict && e >= 0 && e < cap) {
+      const TensorKind k = w == 0 ? a.kk : a.vk;
+      const size_t row = (head * a.ring + (size_t)(e % a.ring)) * D;
+      auto ld = [&](int, double& x0, double& x1) {
+        x0 = qz::bf16_bits_to_f32(ring[row + 2 * lane]);
+        x1 = qz::bf16_bits_to_f32(ring[row + 2 * lane + 1]);
+      };
+      auto slot = [&](int pos) -> size_t {
+        if (a.paged) {
+          int phys = a.block_table[(size_t)b * a.bt_stride + (pos >> 4)];
+          phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
+          return ((size_t)phys * a.hkv + h) * 16 + (pos & 15);
+        }
+        return head * a.max_tokens + pos;
+      };
+      uint8_t* codes = const_cast<uint8_t*>(w == 0 ? a.k_codes : a.v_codes);
+      uint8_t* meta = const_cast<uint8_t*>(w == 0 ? a.k_meta : a.v_meta);
+      qz::quantize_group(k, ld, slot, e, 1, codes, meta, slot(e), nullptr, 1.0f, lane);
+    }
+    // the ring slot of p is the one e held: its values were read above
+    const uint16_t* src = (const uint16_t*)(w == 0 ? a.k_new : a.v_new);
+    const size_t out_row = (head * a.ring + (size_t)(p % a.ring)) * D;
+    for (int i = lane; i < D; i += 64) ring[out_row + i] = src[head * D + i];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  if (lane == 0) __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+
 template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool TIER>
 __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   __shared__ Shared<G> sh;
@@ -1703,6 +1839,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   // which the hardware sends to different XCDs, are mostly the KV heads of
   // one chunk.
   __shared__ int last_flag;
+  __shared__ int step_done;  // decode step with a window: stores done (step_window)
   __shared__ int hist[WAVES][NSIZE];
   // workgroup p < batch * hkv also writes the (zero) output of pair p if
   // its sequence is empty
@@ -1732,6 +1869,10 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   const bool direct = pl.total == 1 && !pl.overflow;
   if (it.kind == 1) {
     if (si.nw > 0) {
+      // decode step with a window, a sequence with no quantized token: the
+      // new token into the ring (nothing leaves the window); the window
+      // itself reads it from the input
+      if (a.k_new != nullptr && si.nq == 0) step_window(a, b, h, false, &step_done);
       window_split<G, QB>(a, b, h, si.nq + si.nm, si.nw, direct, sh);
       if (!direct) arrive_and_combine<G>(a, b, h, pl, &last_flag);
     }
@@ -1752,19 +1893,35 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   }
   const int tok0 = split * a.split_tokens;
   const int tok1 = min(tok0 + a.split_tokens, si.nq);
+  // decode step with a window: the workgroup of the pair's last chunk, which
+  // holds the position leaving the window, moves it into the cache and the
+  // new token into the ring; the wave whose range holds that position loads
+  // its tile once both stores are done
+  const bool evict = a.k_new != nullptr && a.ring && split == pl.ns - 1;
   if (a.k_new != nullptr) {
-    // the decode step's new token, at position seq_lens[b] - 1 of the
-    // unclamped length: the split that holds it stores it first (the last
-    // split if the sequence overflows the plan).  A position at or past the
-    // capacity is not stored, as kvq_quantize_append skips it; si.len is
-    // the length clamped to the capacity.
-    const int p = a.seq_lens[b] - 1;
-    if (p >= 0 && p < si.len && split == min(p / a.split_tokens, pl.ns - 1))
-      step_append(a, b, h, p);
+    if (a.ring) {
+      if (evict) {
+        if (threadIdx.x == 0) step_done = 0;
+        __syncthreads();
+      }
+    } else {
+      // the decode step's new token, at position seq_lens[b] - 1 of the
+      // unclamped length: the split that holds it stores it first (the last
+      // split if the sequence overflows the plan).  A position at or past
+      // the capacity is not stored, as kvq_quantize_append skips it; si.len
+      // is the length clamped to the capacity.
+      const int p = a.seq_lens[b] - 1;
+      if (p >= 0 && p < si.len && split == min(p / a.split_tokens, pl.ns - 1))
+        step_append(a, b, h, p);
+    }
   }
+  // waves 0 and 1 move the tokens once their first tiles are in flight
+  auto move = [&]() {
+    if (evict) step_window(a, b, h, true, &step_done);
+  };
   quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
       a, b, h, tok0, tok1, si.nq, direct ? DIRECT_OUT : split, a.k_codes, a.v_codes, a.k_meta,
-      a.v_meta, PAGED ? 0 : pair * a.max_tokens, 0, sh);
+      a.v_meta, PAGED ? 0 : pair * a.max_tokens, 0, sh, evict ? si.nq - 1 : -1, &step_done, move);
   if (!direct) arrive_and_combine<G>(a, b, h, pl, &last_flag);
 }
 

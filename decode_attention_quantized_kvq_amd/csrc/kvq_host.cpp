@@ -595,14 +595,17 @@ kvq_status kvq_decode_attn_ex(const kvq_config* cfg, const kvq_cache* cache, int
 
 // The decode kernel quantizes the new token itself when the cache keeps
 // per-token scales (fp32 or fp16, with or without a zero point) and has no
-// bf16 window, middle tier or token groups; otherwise the step is the append
-// followed by the decode.
+// middle tier or token groups.  With a bf16 window (and bf16 input), the
+// workgroup of each pair's last chunk quantizes the token leaving the window
+// and writes the new one into the ring, and the window's workgroup reads
+// the new token from the input.  Otherwise the step is the append followed
+// by the decode.
 static bool step_fusable(const kvq_config* c) {
   auto ok = [](const kvq_tensor_fmt& f) {
     return f.bits != 16 && f.axis == KVQ_AXIS_TOKEN && f.scale_fmt != KVQ_SCALE_U8_SUPER;
   };
-  return c->window == 0 && c->mid_tokens == 0 && token_group(c) == 1 && ok(c->key) &&
-         ok(c->value);
+  return c->mid_tokens == 0 && token_group(c) == 1 && ok(c->key) && ok(c->value) &&
+         (c->window == 0 || c->in_dtype == KVQ_DT_BF16);
 }
 
 kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache, int layer,

@@ -370,11 +370,16 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int max_seq_len,
  * stored codes and metadata and the output are bit for bit those of the two
  * calls, also for a sequence whose length exceeds the cache's capacity (its
  * new token is not stored, as kvq_quantize_append skips it).  With per-token
- * fp32 or fp16 scales (with or without a zero point) and no window, middle
- * tier or token groups, one kernel does both: the workgroup whose split
- * holds a sequence's new token quantizes and stores it before reading that
- * split.  Otherwise it launches the append kernels and then the decode
- * kernel.  Every argument of both halves is checked before anything is
+ * fp32 or fp16 scales (with or without a zero point) and no middle tier or
+ * token groups, one kernel does both.  Without a window, the workgroup whose
+ * split holds a sequence's new token quantizes and stores it before reading
+ * that split.  With a bf16 window (and in_dtype bf16), the workgroup of a
+ * (sequence, KV head)'s last split quantizes the token leaving the window
+ * from its ring slot and writes the new token into that slot before it
+ * reads the tile that holds the quantized token; the window's workgroup
+ * reads the new token from k_new, v_new (and, for a sequence with no
+ * quantized token, writes it into the ring).  Otherwise it launches the
+ * append kernels and then the decode kernel.  Every argument of both halves is checked before anything is
  * launched, so a call that returns an error has not changed the cache.
  * Errors as kvq_quantize_append and kvq_decode_attn; KVQ_ERR_INVALID_ARG if
  * k_new or v_new is NULL. */

@@ -237,16 +237,20 @@ def _copy_cache(bt):
     return other
 
 
-@pytest.mark.parametrize("fmt,paged", [(f, p) for f in STEP_FMTS for p in (False, True)])
-def test_decode_step_against_oracle(fmt, paged):
+@pytest.mark.parametrize("fmt,paged,window", [(f, p, 0) for f in STEP_FMTS for p in (False, True)]
+                         + [("i8", True, 128), ("u4z", False, 16), ("u8z", True, 16), ("i4", False, 128)])
+def test_decode_step_against_oracle(fmt, paged, window):
     """kvq_decode_step's one-kernel path against the oracle: the new token's
-    codes and metadata bit for bit, and the attention over every token
-    (the new one included) within the bar, over three consecutive steps."""
+    codes and metadata bit for bit (with a window: the token leaving it, and
+    the ring), and the attention over every token (the new one included)
+    within the bar, over three consecutive steps."""
     k_spec, v_spec = FMTS[fmt]
     wl = synth.workload(4 if paged else 2, batch=3, hq=32, hkv=8, tokens=1024, key=k_spec,
-                        value=v_spec, window=0, block_tokens=16 if paged else 0)
-    pre = [1000, 300, 513]
-    H.log(f"case: decode step vs oracle {fmt} paged={paged}")
+                        value=v_spec, window=window, block_tokens=16 if paged else 0)
+    # with a window: one sequence that evicts, one inside the window until
+    # its third step, one whose first token leaves it at the first step
+    pre = [1000, 300, 513] if window == 0 else [1000, window - 2, window]
+    H.log(f"case: decode step vs oracle {fmt} paged={paged} window={window}")
     bt = H.build(wl, pre, table_lens=[n + 3 for n in pre])
     rng = np.random.default_rng(9)
     for step in range(3):
@@ -263,32 +267,38 @@ def test_decode_step_against_oracle(fmt, paged):
         torch.cuda.synchronize()
         check_all_records(bt)
         want = np.stack([bt.oracle.attend(b, q[b]) for b in range(3)])
-        H.check_close(got.cpu().numpy().astype(np.float64), want, f"step {step} {fmt} paged={paged}")
+        H.check_close(got.cpu().numpy().astype(np.float64), want,
+                      f"step {step} {fmt} paged={paged} window={window}")
 
 
-@pytest.mark.parametrize("fmt,paged", [("i8", False), ("i8", True), ("u4z", False), ("u4z", True)])
-def test_decode_step_beyond_capacity(fmt, paged):
+@pytest.mark.parametrize("fmt,paged,window", [("i8", False, 0), ("i8", True, 0), ("u4z", False, 0),
+                                              ("u4z", True, 0), ("i8", True, 16), ("u4z", False, 16)])
+def test_decode_step_beyond_capacity(fmt, paged, window):
     """A sequence whose length already exceeds the cache's capacity: its new
-    token is not stored, by the one-kernel step as by kvq_quantize_append,
-    and no stored token is overwritten; every buffer and the output bit for
-    bit those of append + decode."""
+    token (with a window: the token leaving the window) is not stored, by the
+    one-kernel step as by kvq_quantize_append, and no stored token is
+    overwritten; every buffer and the output bit for bit those of append +
+    decode."""
     k_spec, v_spec = FMTS[fmt]
-    wl = synth.workload(4 if paged else 2, batch=3, hq=16, hkv=4, tokens=512, key=k_spec,
-                        value=v_spec, window=0, block_tokens=16 if paged else 0)
-    pre = [512, 300, 511]
-    H.log(f"case: decode step beyond capacity {fmt} paged={paged}")
-    bt = H.build(wl, pre, oracle=False, table_lens=[512, 512, 512])
+    # 512 quantized positions: a contiguous cache's max_tokens, or a paged
+    # table of 32 blocks (sized for max_tokens - window positions)
+    wl = synth.workload(4 if paged else 2, batch=3, hq=16, hkv=4,
+                        tokens=512 + (window if paged else 0), key=k_spec, value=v_spec,
+                        window=window, block_tokens=16 if paged else 0)
+    pre = [512 + window, 300, 511 + window]
+    H.log(f"case: decode step beyond capacity {fmt} paged={paged} window={window}")
+    bt = H.build(wl, pre, oracle=False, table_lens=[512 + window] * 3)
     other = _copy_cache(bt)
     gen = torch.Generator().manual_seed(3)
     k1, v1 = (torch.randn((3, 4, 1, 128), generator=gen).to(torch.bfloat16).cuda() for _ in range(2))
-    lens = torch.tensor([513, 301, 512], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([n + 1 for n in pre], dtype=torch.int32, device="cuda")
     bt.cache.seq_lens.copy_(lens)
     other.seq_lens.copy_(lens)
     before = bt.cache.buffers["k_codes"].clone()
     q = H.to_device(H.queries(wl), wl["in_dtype"])
-    got = K.decode_step(bt.cache, 0, k1, v1, q, 513)
+    got = K.decode_step(bt.cache, 0, k1, v1, q, max(pre) + 1)
     K.quantize_append(other, 0, k1, v1)
-    want = K.decode_attn(other, 0, q, 513)
+    want = K.decode_attn(other, 0, q, max(pre) + 1)
     torch.cuda.synchronize()
     for name, buf in bt.cache.buffers.items():
         if buf is not None:

@@ -504,17 +504,23 @@ def test_repeatable_outputs():
             assert np.array_equal(H.run_decode(bt, q, split), first), f"{wl['name']}: outputs differ between runs"
 
 
-@pytest.mark.parametrize("fmt,paged,window", [
-    ("i8", False, 0), ("u4z", False, 0), ("i4", True, 0), ("u8z", False, 0), ("i2", False, 0),
-    ("i8", True, 128),
+@pytest.mark.parametrize("fmt,paged,window,dt", [
+    ("i8", False, 0, "bf16"), ("u4z", False, 0, "bf16"), ("i4", True, 0, "bf16"),
+    ("u8z", False, 0, "bf16"), ("i2", False, 0, "bf16"), ("i8", True, 128, "bf16"),
+    ("i8", False, 128, "bf16"), ("u4z", True, 16, "bf16"), ("u8z", False, 16, "bf16"),
+    ("i8", False, 0, "f32"), ("i8", True, 16, "f32"),
 ])
-def test_decode_step(fmt, paged, window):
+def test_decode_step(fmt, paged, window, dt):
     """kvq_decode_step equals kvq_quantize_append of the new tokens followed by
     kvq_decode_attn: every cache buffer bit for bit, and the output bit for
-    bit.  Per-token fp32/fp16 scales without a window take the one-kernel
-    path (the workgroup holding the new token stores it first); the window
-    case takes the two-launch path."""
-    H.log(f"case: decode step {fmt} paged={paged} window={window}")
+    bit.  Per-token fp32/fp16 scales take the one-kernel path: without a
+    window the workgroup holding the new token stores it first; with one, the
+    workgroup of each pair's last chunk moves the token leaving the window
+    into the cache and the new one into the ring (sequences here: one that
+    evicts, one that stays within the window, one whose first token leaves
+    it); 2-bit codes, and a window with fp32 input, take the two-launch
+    path."""
+    H.log(f"case: decode step {fmt} paged={paged} window={window} input={dt}")
     specs = {
         "i8": dict(bits=8), "i4": dict(bits=4), "i2": dict(bits=2),
         "u4z": dict(bits=4, zero_point=True, scale="f16"),
@@ -522,15 +528,17 @@ def test_decode_step(fmt, paged, window):
     }
     base = 4 if paged else 2
     wl = synth.workload(base, batch=3, tokens=1024, key=specs[fmt], value=specs[fmt],
-                        window=window, hq=32, hkv=8)
-    pre = [1000, 300, 513]  # the new token of each lands in a block the table holds
-    bt = H.build(wl, pre, oracle=False)
+                        window=window, hq=32, hkv=8, in_dtype=dt)
+    # the new token of each lands in a block the table holds
+    pre = [1000, 300, 513] if window == 0 else [1000, window - 1, window]
+    bt = H.build(wl, pre, oracle=False, table_lens=[n + 1 for n in pre])
     other = K.KvqCache(bt.cfg, "cuda", bt.cache.block_table)
     for name, buf in bt.cache.buffers.items():
         if buf is not None:
             other.buffers[name].copy_(buf)
     gen = torch.Generator().manual_seed(5)
-    k1, v1 = (torch.randn((3, 8, 1, 128), generator=gen).to(torch.bfloat16).cuda() for _ in range(2))
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    k1, v1 = (torch.randn((3, 8, 1, 128), generator=gen).to(tdt).cuda() for _ in range(2))
     lens = torch.tensor([n + 1 for n in pre], dtype=torch.int32, device="cuda")
     bt.cache.seq_lens.copy_(lens)
     other.seq_lens.copy_(lens)
