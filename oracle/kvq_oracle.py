@@ -53,6 +53,16 @@ Readings where the pages leave a step open (each restated where it is used):
       s' = RN32(that max / qmax), and its stored codes become
       clamp(rint(fl64(c s / s'))) (re-quantized on growth); the recent
       window holds keys in bf16 until they leave it.
+  R26 a per-channel key scale held back until its estimate settles (axis
+      "channel_hold", P3 "Per-token scales and where they can live": the
+      entries can be kept in floating point until the running estimate is
+      stable).  The pages leave "stable" open; here the estimate counts as
+      stable once the recent window overflows: until a sequence's first
+      position is quantized its keys are all in the bf16 window, and the
+      channel scales are then taken, once, from the absmax over every token
+      the sequence holds at that moment (the window's as stored there, in
+      bf16, and the new ones as input), and frozen as R9's are; later
+      tokens clamp.  Without a window this is R9.
   R10 super-scaled values: per token sigma = fl64(amax/qmax); per head
       S = RN32(max sigma / 255) over the prefill, frozen afterwards;
       u = clamp(rint(fl64(sigma / S)), 1, 255) (0 for an all-zero vector);
@@ -131,9 +141,11 @@ class TensorFormat:
     axis:       "token" (one scale per token per head, P3 "Per-token scales and
                 where they can live"), "channel" (one scale per feature per
                 head, keys only, moved onto the query per P3 "The axis choice is
-                a kernel decision") or "channel_grow" (per channel, the scale
+                a kernel decision"), "channel_grow" (per channel, the scale
                 grows with the running absmax and the stored codes are
-                re-quantized, reading R22).
+                re-quantized, reading R22) or "channel_hold" (per channel, the
+                keys held in the bf16 window until the scales are fixed,
+                reading R26).
     zero_point: integer zero point (unsigned codes) when True.
     scale:      "f32", "f16" (scale and zero point stored in that type) or
                 "u8_super" (8-bit code times a per-head fp32 super-scale).
@@ -538,9 +550,9 @@ class OracleCache:
             side, fmt = self.side[b][t], self.fmt[t]
             if first and n and fmt.bits != 16:
                 # readings R9, R10: side data from every token of the first append
-                if fmt.axis != "token":
+                if fmt.axis in ("channel", "channel_grow"):
                     side.chan = channel_scales(x, fmt.bits)
-                elif fmt.scale == "u8_super":
+                elif fmt.axis == "token" and fmt.scale == "u8_super":
                     side.S = super_scale(x, fmt.bits)
             if self.window or self.group > 1:
                 pool = np.concatenate([self.win[b][t], x], axis=1)
@@ -548,7 +560,9 @@ class OracleCache:
                 leave = pool.shape[1] - keep
                 q, self.win[b][t] = pool[:, :leave], round_bf16(pool[:, leave:])
             else:
-                q = x
+                pool = q = x
+            if fmt.axis == "channel_hold" and fmt.bits != 16 and side.chan is None and q.shape[1]:
+                side.chan = self._hold_scales(pool, q, fmt)
             if self.mid:
                 # reading R24: the tokens leaving the window enter the middle
                 # tier; its oldest whole blocks of 32 leave it for the cache's
@@ -565,6 +579,14 @@ class OracleCache:
                 self._grow_channels(side, fmt, q)
             self._quantize_into(side, fmt, q, first)
         self.lens[b] = total
+
+    @staticmethod
+    def _hold_scales(held, leaving, fmt: TensorFormat):
+        """Reading R26: the channel scales fixed when a sequence's first
+        positions leave the window, from every token it holds at that moment
+        (held [Hkv, n, D]: the window's tokens and the new ones; leaving: the
+        first of them, about to be quantized)."""
+        return channel_scales(held, fmt.bits)
 
     @staticmethod
     def _mid_reconstruction(codes, s):

@@ -846,6 +846,48 @@ def pin_channel_growth(O):
     assert np.array_equal(frozen.stored(0, "k").chan, old_s)       # "channel" stays frozen
 
 
+def pin_channel_hold(O):
+    """Reading R26: with axis "channel_hold" the keys stay in the bf16 window
+    until the first position is quantized; the channel scales are then
+    RN32(max |k| / 127) over every token held at that moment (the window's
+    and the new ones), not over the first append alone (R9) nor over the
+    leaving or the new tokens alone; later tokens clamp.  A first append
+    longer than the window gives R9's scales and codes exactly."""
+    rng = _rng(205)
+    d, W = 8, 16
+    # channel 7 is large only in tokens 3 (held) and 25 (new in the second
+    # append, stays in the window); channel 6 only in token 12 (leaves with
+    # the first quantization); channel 5 only in token 2 and channel 4 only
+    # in token 0 (both held since the first append)
+    k = _bf16(rng.standard_normal((1, 40, d)))
+    k[0, 3, 7], k[0, 25, 7], k[0, 12, 6], k[0, 2, 5], k[0, 0, 4] = 40.0, -60.0, 30.0, 20.0, 25.0
+    v = _bf16(rng.standard_normal((1, 40, d)))
+    fk, fv = O.TensorFormat(8, "channel_hold"), O.TensorFormat(8)
+    cache = O.OracleCache(1, 1, d, fk, fv, window=W)
+    cache.append(0, k[:, :10], v[:, :10])            # inside the window: nothing quantized
+    assert cache.stored(0, "k").codes.shape[1] == 0
+    cache.append(0, k[:, 10:30], v[:, 10:30])        # 30 tokens: positions 0..13 leave
+    st = cache.stored(0, "k")
+    assert st.codes.shape[1] == 30 - W
+    want = [rn32(max(abs(fr(k[0, t, c])) for t in range(30)) / 127) for c in range(d)]
+    assert [Fraction(float(x)) for x in st.chan[0]] == want
+    for t in range(30, 40):                          # later tokens clamp to the fixed scales
+        cache.append(0, k[:, t:t + 1], v[:, t:t + 1])
+    st = cache.stored(0, "k")
+    assert np.array_equal(st.chan[0], np.array([float(x) for x in want], np.float32))
+    for t in range(40 - W):
+        for c in range(d):
+            assert st.codes[0, t, c] == max(-127, min(127, round(fr(k[0, t, c]) / want[c])))
+    # a first append longer than the window: exactly R9 ("channel")
+    a = O.OracleCache(1, 1, d, fk, fv, window=W)
+    b = O.OracleCache(1, 1, d, O.TensorFormat(8, "channel"), fv, window=W)
+    for c_ in (a, b):
+        c_.append(0, k[:, :25], v[:, :25])
+        c_.append(0, k[:, 25:27], v[:, 25:27])
+    assert np.array_equal(a.stored(0, "k").chan, b.stored(0, "k").chan)
+    assert np.array_equal(a.stored(0, "k").codes, b.stored(0, "k").codes)
+
+
 def pin_tier_counts(O):
     """Reading R24 by brute force: a position is in the cache's format when
     its whole block of 32 positions is at least M older than the first

@@ -307,6 +307,14 @@ def m_mid_ring_without_spare_block(O):
     O.mid_ring_slots = lambda mid: mid
 
 
+def m_hold_scales_from_leaving_tokens(O):
+    O.OracleCache._hold_scales = staticmethod(lambda held, leaving, fmt: O.channel_scales(leaving, fmt.bits))
+
+
+def m_hold_scales_skip_oldest(O):
+    O.OracleCache._hold_scales = staticmethod(lambda held, leaving, fmt: O.channel_scales(held[:, 1:], fmt.bits))
+
+
 MUTATIONS = [v for k, v in sorted(globals().items()) if k.startswith("m_")]
 
 
