@@ -15,8 +15,10 @@
 // Launch order on the caller's stream:
 //   1. append_stats: per-channel key scales and key / value super-scales of
 //      sequences whose append starts at position 0 (their prefill), then
-//      frozen; or, for growing channel scales, their update and the
-//      re-quantization of the stored codes of the channels that grew.
+//      frozen; for growing channel scales, their update and the
+//      re-quantization of the stored codes of the channels that grew; for
+//      held channel scales, their one computation when the sequence's first
+//      position leaves the window.
 //   2. append_quantize: one workgroup per (token, head, sequence); wave 0
 //      quantizes the key, wave 1 the value.  With a recent window it takes
 //      the tokens leaving the window (from the ring or from the input).
@@ -127,17 +129,38 @@ __device__ void grow_channels(const AppendArgs& a, int b, int h, const SeqRange&
   if (tid < D) chan[tid] = snew[tid];
 }
 
+// Held channel scales: the append that quantizes a sequence's first
+// position fixes its per-channel key scales, RN32(max / qmax) over every
+// token it holds: positions [0, start) from the bf16 ring (none of them is
+// quantized yet, so all are there) and the new ones from the input.
+__device__ void hold_channels(const AppendArgs& a, int b, int h, const SeqRange& r) {
+  if (quantized_count(a, r.start) != 0 || quantized_count(a, r.len) == 0) return;
+  const int tid = threadIdx.x;
+  if (tid >= D) return;
+  const size_t head = (size_t)b * a.hkv + h;
+  float amax = 0.0f;
+  for (int p = 0; p < r.len; ++p) {
+    const float x = p >= r.start
+                        ? load_in(a.k_new, (head * a.n_new + (p - r.start)) * D + tid, a.in_bf16)
+                        : bf16_bits_to_f32(a.k_win[(head * a.ring + (p % a.ring)) * D + tid]);
+    amax = fmaxf(amax, fabsf(x));
+  }
+  const int qmax = qmax_sym(code_bits(a.kk.code));
+  a.k_chan[head * D + tid] = amax == 0.0f ? 1.0f : store_f32((double)amax / qmax);
+}
+
 __global__ void __launch_bounds__(256) append_stats(AppendArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const SeqRange r = seq_range(a, b);
   if (r.newb == 0) return;
+  if (a.kk.hold) hold_channels(a, b, h, r);
   if (r.start != 0) {  // a later append: only growing channel scales change
     if (a.kk.grow) grow_channels(a, b, h, r);
     return;
   }
   const size_t in_base = ((size_t)b * a.hkv + h) * a.n_new;
   const int tid = threadIdx.x;
-  if (a.kk.channel && tid < D) {
+  if (a.kk.channel && !a.kk.hold && tid < D) {
     // Absmax of each feature over the prefill, one rounding to fp32.
     float amax = 0.0f;
     for (int i = 0; i < r.newb; ++i)
@@ -209,7 +232,7 @@ __device__ inline InputLoader input_loader(const AppendArgs& a, int w, size_t he
   return InputLoader{w == 0 ? a.k_new : a.v_new, w == 0 ? a.k_win : a.v_win, head, start, lane};
 }
 
-constexpr TensorKind MID_KIND{CK_I8, MK_F32, false, false};
+constexpr TensorKind MID_KIND{CK_I8, MK_F32, false, false, false};
 
 __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;

@@ -66,11 +66,12 @@ static size_t side_bytes(const kvq_tensor_fmt& f, int d) {
 }
 
 kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
-  TensorKind k{CK_I8, MK_NONE, false, false};
+  TensorKind k{CK_I8, MK_NONE, false, false, false};
   if (f.scale_fmt != KVQ_SCALE_F32 && f.scale_fmt != KVQ_SCALE_F16 &&
       f.scale_fmt != KVQ_SCALE_U8_SUPER)
     return KVQ_ERR_INVALID_ARG;
-  if (f.axis != KVQ_AXIS_TOKEN && f.axis != KVQ_AXIS_CHANNEL && f.axis != KVQ_AXIS_CHANNEL_GROW)
+  if (f.axis != KVQ_AXIS_TOKEN && f.axis != KVQ_AXIS_CHANNEL && f.axis != KVQ_AXIS_CHANNEL_GROW &&
+      f.axis != KVQ_AXIS_CHANNEL_HOLD)
     return KVQ_ERR_INVALID_ARG;
   if (f.zero_point != 0 && f.zero_point != 1) return KVQ_ERR_INVALID_ARG;
   if (f.bits == 16) {
@@ -94,6 +95,7 @@ kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
     if (f.bits == 2) return KVQ_ERR_UNSUPPORTED;
     k.channel = true;
     k.grow = f.axis == KVQ_AXIS_CHANNEL_GROW;
+    k.hold = f.axis == KVQ_AXIS_CHANNEL_HOLD;
     k.meta = MK_NONE;
     if (out) *out = k;
     return is_key ? KVQ_OK : KVQ_ERR_UNSUPPORTED;

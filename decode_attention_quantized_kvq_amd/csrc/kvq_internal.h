@@ -34,6 +34,7 @@ struct TensorKind {
   MetaKind meta;
   bool channel;   // per-channel scales (keys only)
   bool grow;      // ... that follow the running absmax (stored codes re-quantized)
+  bool hold;      // ... fixed when the sequence's first position leaves the window
 };
 
 // Code bytes of one token row of one head (0 for unsupported widths).

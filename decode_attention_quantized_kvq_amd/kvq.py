@@ -23,7 +23,7 @@ LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(os.path.dirname(os.path.abs
                                                      "libkvq.so")
 
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = range(5)
-AXIS = {"token": 0, "channel": 1, "channel_grow": 2}
+AXIS = {"token": 0, "channel": 1, "channel_grow": 2, "channel_hold": 3}
 SCALE = {"f32": 0, "f16": 1, "u8_super": 2}
 DTYPE = {"f32": 0, "bf16": 1}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}

@@ -132,13 +132,22 @@ typedef enum {
   KVQ_AXIS_TOKEN = 0,  /* one scale per token per head */
   KVQ_AXIS_CHANNEL = 1, /* one scale per feature per head (keys only), from
                            a sequence's first append, then frozen */
-  KVQ_AXIS_CHANNEL_GROW = 2 /* per feature per head (keys only), following the
+  KVQ_AXIS_CHANNEL_GROW = 2, /* per feature per head (keys only), following the
                            running absmax: before tokens are quantized, a
                            channel whose new keys exceed qmax s gets
                            s' = RN32(max / qmax) and its stored codes become
                            clamp(rint(fl64(c s / s'))) (P3, "Per-token scales
                            and where they can live": the estimate has to be
                            updated as the sequence grows) */
+  KVQ_AXIS_CHANNEL_HOLD = 3 /* per feature per head (keys only), the entries
+                           held in floating point until the estimate is
+                           stable (P3, "Per-token scales and where they can
+                           live"): a sequence's keys stay in the bf16 window
+                           until its first position leaves it; the scales
+                           are then fixed once from every token it holds
+                           (window and new), RN32(max / qmax), and frozen;
+                           later tokens clamp.  Without a window: as
+                           KVQ_AXIS_CHANNEL */
 } kvq_axis;
 
 /* Storage type of a per-token scale (and zero point). */

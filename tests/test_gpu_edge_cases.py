@@ -35,6 +35,7 @@ FMTS = {
     "u8z": (dict(bits=8, zero_point=True, scale="f16"), dict(bits=8, zero_point=True, scale="f16")),
     "chan_super": (dict(bits=8, axis="channel"), dict(bits=4, scale="u8_super")),
     "grow_super": (dict(bits=8, axis="channel_grow"), dict(bits=4, scale="u8_super")),
+    "hold_super": (dict(bits=8, axis="channel_hold"), dict(bits=4, scale="u8_super")),
     "i2_super": (dict(bits=2, scale="u8_super"), dict(bits=2, scale="u8_super")),
     "u2z": (dict(bits=2, zero_point=True, scale="f16"), dict(bits=2, zero_point=True, scale="f16")),
     "i8k_i4v": (dict(bits=8), dict(bits=4)),
@@ -345,7 +346,7 @@ hyp = pytest.importorskip("hypothesis")
 from hypothesis import HealthCheck, Phase, given, settings  # noqa: E402
 from hypothesis import strategies as st  # noqa: E402
 
-PROP_FMTS = ["i8", "u4z", "i4", "u8z", "chan_super", "i2_super", "u2z", "i8k_i4v"]
+PROP_FMTS = ["i8", "u4z", "i4", "u8z", "chan_super", "hold_super", "i2_super", "u2z", "i8k_i4v"]
 
 
 @settings(max_examples=40, deadline=None, derandomize=True, database=None,

@@ -367,6 +367,33 @@ def test_channel_scales_running(axis, window, paged):
     assert (changed > 0) == (axis == "channel_grow")   # growth exercised; frozen stays
 
 
+@pytest.mark.parametrize("window,paged,dt", [
+    (32, False, "bf16"), (32, True, "bf16"), (16, False, "f32"), (0, False, "bf16"),
+])
+def test_channel_hold(window, paged, dt):
+    """Per-channel key scales held until the estimate settles (R26): a
+    sequence whose prefill fits in the window keeps its keys in bf16 through
+    single-token appends until the first leaves the window, and the scales
+    are then fixed over every token it holds; one whose prefill outgrows the
+    window gets R9's.  Checked before and after the crossing: records bit for
+    bit (codes, channel scales, ring), outputs within the bar."""
+    H.log(f"case: held channel scales window={window} paged={paged} input={dt}")
+    over = dict(batch=2, tokens=256, key=dict(bits=8, axis="channel_hold"),
+                value=dict(bits=4, scale="u8_super"), window=window, in_dtype=dt)
+    if paged:
+        over.update(block_tokens=16)
+    wl = synth.workload(5, **over)
+    for lens, steps in (([100, 25], 5), ([100, 60], 40)):
+        bt = H.build(wl, lens, decode_steps=steps)
+        full_check(bt, steps=(0,))
+        if window and lens[1] - steps < window < lens[1]:
+            # sequence 1 crossed during the single-token appends: its scales
+            # are not those of its prefill alone
+            pre = np.stack([bt.inputs["kv"][1, h][0][:lens[1] - steps] for h in range(wl["hkv"])])
+            r9 = H.O.channel_scales(pre, 8)
+            assert not np.array_equal(bt.oracle.stored(1, "k").chan, r9)
+
+
 def test_empty_and_zero_sequences():
     """A sequence with no tokens gives zeros; all-zero vectors quantize to
     codes 0 with scale 1 and attend like any other token."""

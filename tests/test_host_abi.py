@@ -160,6 +160,12 @@ def test_validation_errors():
         (dict(key=dict(bits=16), value=dict(bits=16), block_tokens=16, num_blocks=8,
               max_blocks_per_seq=4), K.KVQ_ERR_UNSUPPORTED),
         (dict(value=dict(bits=8, axis="channel")), K.KVQ_ERR_UNSUPPORTED),
+        (dict(value=dict(bits=8, axis="channel_hold")), K.KVQ_ERR_UNSUPPORTED),   # keys only
+        (dict(key=dict(bits=8, axis="channel_hold", zero_point=True)), K.KVQ_ERR_INVALID_ARG),
+        (dict(key=dict(bits=8, axis="channel_hold"), value=dict(bits=4, scale="u8_super"),
+              group_tokens=2), K.KVQ_ERR_UNSUPPORTED),
+        (dict(mid_tokens=32, key=dict(bits=8, axis="channel_hold"),
+              value=dict(bits=4, scale="u8_super")), K.KVQ_ERR_UNSUPPORTED),
         (dict(window=20), K.KVQ_ERR_UNSUPPORTED),
         (dict(block_tokens=16, num_blocks=0, max_blocks_per_seq=4), K.KVQ_ERR_INVALID_ARG),
         (dict(block_tokens=32, num_blocks=8, max_blocks_per_seq=4), K.KVQ_ERR_UNSUPPORTED),
@@ -182,6 +188,10 @@ def test_validation_errors():
         dict(key=dict(bits=16), value=dict(bits=16)),   # unquantized, contiguous
         dict(key=dict(bits=8, axis="channel_grow"), value=dict(bits=4, scale="u8_super"),
              window=32),
+        dict(key=dict(bits=8, axis="channel_hold"), value=dict(bits=4, scale="u8_super"),
+             window=32),
+        dict(key=dict(bits=8, axis="channel_hold"), value=dict(bits=4, scale="u8_super"),
+             window=16, block_tokens=16, num_blocks=8, max_blocks_per_seq=4),
         dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super"), window=16),
         dict(key=dict(bits=2), value=dict(bits=2)),
         dict(key=dict(bits=2, scale="u8_super"), value=dict(bits=2, scale="u8_super")),
