@@ -1200,12 +1200,12 @@ __device__ void bf16_tokens(const DecodeArgs& a, int b, int h, const uint16_t* k
 // mod ring, which receives the new token, is read from the input, whose bf16
 // row is what the slot receives: the workgroup that writes the slot may
 // still be reading the token it held.
-template <int G, bool QB>
+template <int G, bool QB, bool STEP>
 __device__ void window_split(const DecodeArgs& a, int b, int h, int q0, int nw, bool direct,
                              Shared<G>& sh) {
   const size_t head = ((size_t)b * a.hkv + h) * a.ring * D;
   const size_t in_row = ((size_t)b * a.hkv + h) * D;
-  const bool step = a.k_new != nullptr;
+  const bool step = STEP && a.k_new != nullptr;
   const int p = step ? a.seq_lens[b] - 1 : -1;
   bf16_tokens<G, QB, false>(a, b, h, a.k_win + head, a.v_win + head, q0 % a.ring, a.ring, nw,
                             direct ? DIRECT_OUT : a.n_split, sh,
@@ -1560,7 +1560,7 @@ template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, 
 __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok1, int nend,
                             int row, const uint8_t* kc, const uint8_t* vc, const uint8_t* km,
                             const uint8_t* vm, size_t head_tok, int rblk, Shared<G>& sh,
-                            int wait_pos = -1, const int* stored = nullptr, Pre pre = Pre()) {
+                            int hold_pos = -1, Pre pre = Pre()) {
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR): keeps each wave's token loop and its addressing scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1620,22 +1620,30 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
   // in the loop a wait for all of them.
   constexpr int ROWB = Codes<KC>::ROW + Codes<VC>::ROW;
   constexpr int NB = ROWB >= 256 ? KVQ_NB8 : ROWB >= 192 ? KVQ_NB6 : ROWB >= 128 ? KVQ_NB4 : KVQ_NB2;
-  // a decode step's position leaving the window (wait_pos >= 0): the tile
-  // that holds it is loaded once its stores are done (wait_stored)
-  const int wtile = wait_pos >= w0 && wait_pos < w1 ? w0 + (wait_pos - w0) / TILE * TILE : 0x7fffffff;
-  // pre: work that waits for memory of its own, done while the first tiles
-  // are in flight (a decode step's move of the token leaving the window);
-  // before them if one of them waits for it
-  const bool pre_first = wtile < w0 + NB * TILE;
-  if (pre_first) pre();
+  // pre (a decode step's move of the token leaving the window into the
+  // cache, at hold_pos): run by the wave whose range holds that position
+  // (wave 0 if none does), so that its own later load of the position reads
+  // the stores.  Wave memory operations complete in issue order: a load
+  // issued after the wave has waited for data that it requested after the
+  // stores comes after them.  The refill of tile j follows the wait for
+  // tile j - NB, so a position in tile 2 NB or later may be moved while the
+  // first tiles are in flight; one in an earlier tile is moved first and
+  // waited for.
+  const bool mover = hold_pos >= 0 && (hold_pos >= tok0 && hold_pos < tok1
+                                           ? hold_pos >= w0 && hold_pos < w1
+                                           : wave == 0);
+  const bool move_first = mover && hold_pos < w0 + 2 * NB * TILE;
+  if (move_first) {
+    pre();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   TileRaw<KC, KM, VC, VM> buf[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
-    if (w0 + k * TILE == wtile) wait_stored(stored);
     load_tile<PAGED, RING>(buf[k], ad, w0 + k * TILE, w1, lo);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (!pre_first) pre();
+  if (mover && !move_first) pre();
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. query operand: Q = rint(q 2^e) per head, |Q| < 2^22, as three int8
@@ -1731,7 +1739,6 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
       compute_tile<KC, KM, KCH, VC, VM, G>(buf[k], t + k * TILE, w1, qa, qs, sumq, lt, g, psel, prd,
                                            pwr, nm, st);
       __builtin_amdgcn_sched_barrier(0);
-      if (t + (k + NB) * TILE == wtile) wait_stored(stored);
       load_tile<PAGED, RING>(buf[k], ad, t + (k + NB) * TILE, w1, lo);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1786,37 +1793,36 @@ __device__ void step_append(const DecodeArgs& a, int b, int h, int p) {
 }
 
 // Decode step with a bf16 window (token groups of 1, no middle tier, bf16
-// input): as kvq_quantize_append with one new token, the token leaving the
-// window (position p - W, from its ring slot) is quantized into the cache
-// unless it lies past the capacity, then the new token (position p) is
-// written into the ring slot that frees (the ring holds W slots); wave 0 the
-// key, wave 1 the value.  evict: the caller attends position p - W (its
-// sequence has quantized tokens).  Each of the two waves waits for its
-// stores, then adds 1 to *done (LDS): a wave of the workgroup that loads
-// position p - W waits for 2 first (wait_stored).
-__device__ void step_window(const DecodeArgs& a, int b, int h, bool evict, int* done) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// input), run by one wave: as kvq_quantize_append with one new token, the
+// token leaving the window (position p - W, from its ring slot) is quantized
+// into the cache unless it lies past the capacity (evict: the sequence has
+// quantized tokens), then the new token (position p) is written into the
+// ring slot that frees (the ring holds W slots); the key, then the value.
+// The stores are not waited for: the caller orders its later loads of
+// position p - W behind them.
+__device__ void step_window(const DecodeArgs& a, int b, int h, bool evict) {
+  const int lane = threadIdx.x & 63;
   const int p = a.seq_lens[b] - 1;
-  if (w >= 2) return;
-  if (p >= 0) {
-    const size_t head = (size_t)b * a.hkv + h;
+  if (p < 0) return;
+  const size_t head = (size_t)b * a.hkv + h;
+  const int e = p - a.window;
+  const int cap = a.paged ? a.bt_stride * 16 : a.max_tokens;
+  auto slot = [&](int pos) -> size_t {
+    if (a.paged) {
+      int phys = a.block_table[(size_t)b * a.bt_stride + (pos >> 4)];
+      phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
+      return ((size_t)phys * a.hkv + h) * 16 + (pos & 15);
+    }
+    return head * a.max_tokens + pos;
+  };
+  for (int w = 0; w < 2; ++w) {
     uint16_t* ring = const_cast<uint16_t*>(w == 0 ? a.k_win : a.v_win);
-    const int e = p - a.window;
-    const int cap = a.paged ? a.bt_stride * 16 : a.max_tokens;
     if (evict && e >= 0 && e < cap) {
       const TensorKind k = w == 0 ? a.kk : a.vk;
       const size_t row = (head * a.ring + (size_t)(e % a.ring)) * D;
       auto ld = [&](int, double& x0, double& x1) {
         x0 = qz::bf16_bits_to_f32(ring[row + 2 * lane]);
         x1 = qz::bf16_bits_to_f32(ring[row + 2 * lane + 1]);
-      };
-      auto slot = [&](int pos) -> size_t {
-        if (a.paged) {
-          int phys = a.block_table[(size_t)b * a.bt_stride + (pos >> 4)];
-          phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
-          return ((size_t)phys * a.hkv + h) * 16 + (pos & 15);
-        }
-        return head * a.max_tokens + pos;
       };
       uint8_t* codes = const_cast<uint8_t*>(w == 0 ? a.k_codes : a.v_codes);
       uint8_t* meta = const_cast<uint8_t*>(w == 0 ? a.k_meta : a.v_meta);
@@ -1826,20 +1832,28 @@ __device__ void step_window(const DecodeArgs& a, int b, int h, bool evict, int* 
     const uint16_t* src = (const uint16_t*)(w == 0 ? a.k_new : a.v_new);
     const size_t out_row = (head * a.ring + (size_t)(p % a.ring)) * D;
     for (int i = lane; i < D; i += 64) ring[out_row + i] = src[head * D + i];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  if (lane == 0) __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Formats whose decode step the host fuses into the decode kernel: per-token
+// fp32 / fp16 scales (with or without a zero point), no middle tier.
+template <int KM, bool KCH, int VM, bool TIER>
+constexpr bool step_format() {
+  return !TIER && !KCH && (KM == MK_F32 || KM == MK_F32Z || KM == MK_F16 || KM == MK_F16Z) &&
+         (VM == MK_F32 || VM == MK_F32Z || VM == MK_F16 || VM == MK_F16Z);
+}
 
-template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool TIER>
+// STEPK: the decode step's kernel (a.k_new set), a separate instantiation so
+// that the plain decode carries none of the step's code.
+template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool TIER,
+          bool STEPK>
 __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
+  constexpr bool STEP = STEPK && step_format<KM, KCH, VM, TIER>();
   __shared__ Shared<G> sh;
   // 1-D grid of work items, largest first (map_item).  Consecutive items,
   // which the hardware sends to different XCDs, are mostly the KV heads of
   // one chunk.
   __shared__ int last_flag;
-  __shared__ int step_done;  // decode step with a window: stores done (step_window)
   __shared__ int hist[WAVES][NSIZE];
   // workgroup p < batch * hkv also writes the (zero) output of pair p if
   // its sequence is empty
@@ -1872,8 +1886,10 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
       // decode step with a window, a sequence with no quantized token: the
       // new token into the ring (nothing leaves the window); the window
       // itself reads it from the input
-      if (a.k_new != nullptr && si.nq == 0) step_window(a, b, h, false, &step_done);
-      window_split<G, QB>(a, b, h, si.nq + si.nm, si.nw, direct, sh);
+      if (STEP && a.k_new != nullptr && si.nq == 0) {
+        if (threadIdx.x < 64) step_window(a, b, h, false);  // the window reads p from the input
+      }
+      window_split<G, QB, STEP>(a, b, h, si.nq + si.nm, si.nw, direct, sh);
       if (!direct) arrive_and_combine<G>(a, b, h, pl, &last_flag);
     }
     return;
@@ -1897,31 +1913,31 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   // holds the position leaving the window, moves it into the cache and the
   // new token into the ring; the wave whose range holds that position loads
   // its tile once both stores are done
-  const bool evict = a.k_new != nullptr && a.ring && split == pl.ns - 1;
-  if (a.k_new != nullptr) {
-    if (a.ring) {
-      if (evict) {
-        if (threadIdx.x == 0) step_done = 0;
-        __syncthreads();
+  if constexpr (STEP) {
+    const bool evict = a.k_new != nullptr && a.ring && split == pl.ns - 1;
+    if (a.k_new != nullptr) {
+      if (!a.ring) {
+        // the decode step's new token, at position seq_lens[b] - 1 of the
+        // unclamped length: the split that holds it stores it first (the
+        // last split if the sequence overflows the plan).  A position at or
+        // past the capacity is not stored, as kvq_quantize_append skips it;
+        // si.len is the length clamped to the capacity.
+        const int p = a.seq_lens[b] - 1;
+        if (p >= 0 && p < si.len && split == min(p / a.split_tokens, pl.ns - 1))
+          step_append(a, b, h, p);
       }
-    } else {
-      // the decode step's new token, at position seq_lens[b] - 1 of the
-      // unclamped length: the split that holds it stores it first (the last
-      // split if the sequence overflows the plan).  A position at or past
-      // the capacity is not stored, as kvq_quantize_append skips it; si.len
-      // is the length clamped to the capacity.
-      const int p = a.seq_lens[b] - 1;
-      if (p >= 0 && p < si.len && split == min(p / a.split_tokens, pl.ns - 1))
-        step_append(a, b, h, p);
     }
+    // the wave whose range holds the position leaving the window moves the
+    // tokens (quant_range decides when)
+    auto move = [&]() { step_window(a, b, h, true); };
+    quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
+        a, b, h, tok0, tok1, si.nq, direct ? DIRECT_OUT : split, a.k_codes, a.v_codes, a.k_meta,
+        a.v_meta, PAGED ? 0 : pair * a.max_tokens, 0, sh, evict ? si.nq - 1 : -1, move);
+  } else {
+    quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
+        a, b, h, tok0, tok1, si.nq, direct ? DIRECT_OUT : split, a.k_codes, a.v_codes, a.k_meta,
+        a.v_meta, PAGED ? 0 : pair * a.max_tokens, 0, sh);
   }
-  // waves 0 and 1 move the tokens once their first tiles are in flight
-  auto move = [&]() {
-    if (evict) step_window(a, b, h, true, &step_done);
-  };
-  quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
-      a, b, h, tok0, tok1, si.nq, direct ? DIRECT_OUT : split, a.k_codes, a.v_codes, a.k_meta,
-      a.v_meta, PAGED ? 0 : pair * a.max_tokens, 0, sh, evict ? si.nq - 1 : -1, &step_done, move);
   if (!direct) arrive_and_combine<G>(a, b, h, pl, &last_flag);
 }
 
@@ -1959,7 +1975,10 @@ __global__ void __launch_bounds__(256) decode_bf16(DecodeArgs a) {
 // is the kernel's own duration.
 template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool TIER = false>
 void launch_one(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  const auto k = decode_split<KC, KM, KCH, VC, VM, G, PAGED, QB, TIER>;
+  auto k = decode_split<KC, KM, KCH, VC, VM, G, PAGED, QB, TIER, false>;
+  if constexpr (step_format<KM, KCH, VM, TIER>()) {
+    if (a.k_new != nullptr) k = decode_split<KC, KM, KCH, VC, VM, G, PAGED, QB, TIER, true>;
+  }
   if (a.ev_begin)
     hipExtLaunchKernelGGL(k, grid, dim3(256), 0, s, (hipEvent_t)a.ev_begin, (hipEvent_t)a.ev_end, 0,
                           a);

@@ -545,8 +545,7 @@ def test_decode_step(fmt, paged, window, dt):
     workgroup of each pair's last chunk moves the token leaving the window
     into the cache and the new one into the ring (sequences here: one that
     evicts, one that stays within the window, one whose first token leaves
-    it); 2-bit codes, and a window with fp32 input, take the two-launch
-    path."""
+    it); a window with fp32 input takes the two-launch path."""
     H.log(f"case: decode step {fmt} paged={paged} window={window} input={dt}")
     specs = {
         "i8": dict(bits=8), "i4": dict(bits=4), "i2": dict(bits=2),
