@@ -293,7 +293,10 @@ def setup_workload(wid, args, K, synth, torch):
     q = torch.from_numpy(np.stack([synth.queries(wl, b) for b in range(wl["batch"])]))
     q = q.to(torch.bfloat16 if wl["in_dtype"] == "bf16" else torch.float32).cuda()
     out = torch.empty((wl["batch"], wl["hq"], wl["d"]), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(max(K.decode_workspace_bytes(cfg, max_len, args.split), 1),
+    # sized for the timed plan and for the library's own plan (the decode
+    # step takes no split option)
+    ws = torch.zeros(max(K.decode_workspace_bytes(cfg, max_len, args.split),
+                         K.decode_workspace_bytes(cfg, max_len), 1),
                      dtype=torch.uint8, device="cuda")
 
     def step(i, events=None):

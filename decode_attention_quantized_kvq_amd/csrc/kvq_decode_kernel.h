@@ -292,6 +292,7 @@ struct Meta {
 
   // metadata of one token through a buffer resource, at byte offset off
   __device__ inline void load_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    r1 = 0;  // defined for every kind: copies of the struct stay 32-bit fields
     if (MK == MK_F32 || MK == MK_F16Z) {
       r0 = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, KVQ_CPOL);
     } else if (MK == MK_F32Z) {
@@ -306,6 +307,7 @@ struct Meta {
   }
   // metadata of one token at p (one 1-8 byte load per lane)
   __device__ inline void load_glob(const uint8_t* p) {
+    r1 = 0;
 #if KVQ_CPOL == 2
 #define KVQ_LDM(T, q) __builtin_nontemporal_load((const T*)(q))
 #else
@@ -431,26 +433,29 @@ __device__ inline LaneOff lane_offsets(int t, int g, int gs) {
   return o;
 }
 
-// Raw registers of one 32-token tile.
-template <int KC, int KM, int VC, int VM>
+// Raw registers of one 32-token tile.  Metadata: PT, one load per tensor
+// and tile (lane (t, g) reads token t of block g & 1 through a per-lane
+// address, and compute_tile takes the other block's from lane (t, g ^ 1));
+// otherwise one buffer load per tensor and block (token t of each block).
+// The first costs vector ALU work and the second scalar registers (a buffer
+// descriptor per load): kernels that run out of scalar registers take PT.
+template <int KC, int KM, int VC, int VM, bool PT = false>
 struct TileRaw {
   static constexpr bool KB8 = Codes<KC>::B8;
   static constexpr bool VB8 = Codes<VC>::B8;
   u32x4 k[2][KB8 ? 2 : 1];   // per 16-token block (2-bit keys: .x, .y)
   u32x2 v8[VB8 ? 8 : 1];     // 8-bit values: 8 tokens x 8 bytes
   uint32_t v4[VB8 ? 1 : 8];  // 4-bit values: 8 tokens x 4 bytes; 2-bit: 2 bytes
-  // metadata of token t of block g & 1 (lane (t, g)): one load per tensor
-  // and tile; compute_tile takes the other block's from lane (t, g ^ 1)
-  Meta<KM> km;
-  Meta<VM> vm;
+  Meta<KM> km[PT ? 1 : 2];
+  Meta<VM> vm[PT ? 1 : 2];
 };
 
 // Loads the 32-token tile at t0 of a wave whose range ends at tend.  Every
 // load is issued whatever t0 is, so the wait counts the compiler derives stay
 // exact; a 16-token block at or past tend is read through an empty resource
 // (zeros, no memory traffic) and its tokens are masked by compute_tile.
-template <bool PAGED, bool RING, int KC, int KM, int VC, int VM>
-__device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int t0, int tend,
+template <bool PAGED, bool RING, int KC, int KM, int VC, int VM, bool PT>
+__device__ inline void load_tile(TileRaw<KC, KM, VC, VM, PT>& t, const Addr& ad, int t0, int tend,
                                  const LaneOff& o) {
   constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
   size_t slots[2];
@@ -477,21 +482,33 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM>& t, const Addr& ad, int
       else
         t.v4[4 * bb + i] = __builtin_amdgcn_raw_buffer_load_b32(rv, o.v[i], 0, KVQ_CPOL);
     }
+    // metadata element of token slot s: s >> gs (one per token group)
+    if constexpr (!PT) {
+      if (Meta<KM>::BYTES)
+        t.km[bb].load_buf(rsrc(ad.km + (slot >> ad.gs) * Meta<KM>::BYTES,
+                               live ? (16 >> ad.gs) * Meta<KM>::BYTES : 0),
+                          o.km);
+      if (Meta<VM>::BYTES)
+        t.vm[bb].load_buf(rsrc(ad.vm + (slot >> ad.gs) * Meta<VM>::BYTES,
+                               live ? (16 >> ad.gs) * Meta<VM>::BYTES : 0),
+                          o.vm);
+    }
   }
-  // metadata element of token slot s: s >> gs (one per token group).  One
-  // load per tensor covers both blocks (lane (t, g): block g & 1); a block
-  // past tend reads a stored slot (block_slot clamps) whose values
-  // compute_tile masks.
-  const size_t ms = (o.odd ? slots[1] : slots[0]) >> ad.gs;
-  if (Meta<KM>::BYTES) t.km.load_glob(ad.km + ms * Meta<KM>::BYTES + o.km);
-  if (Meta<VM>::BYTES) t.vm.load_glob(ad.vm + ms * Meta<VM>::BYTES + o.vm);
+  if constexpr (PT) {
+    // one load per tensor covers both blocks (lane (t, g): block g & 1); a
+    // block past tend reads a stored slot (block_slot clamps) whose values
+    // compute_tile masks
+    const size_t ms = (o.odd ? slots[1] : slots[0]) >> ad.gs;
+    if (Meta<KM>::BYTES) t.km[0].load_glob(ad.km + ms * Meta<KM>::BYTES + o.km);
+    if (Meta<VM>::BYTES) t.vm[0].load_glob(ad.vm + ms * Meta<VM>::BYTES + o.vm);
+  }
 }
 
 // Key operand of the J-th score MFMA for block bb: 8 int8 values, the codes
 // themselves for signed 8-bit keys, offset to signed range for the others
 // (u - 128 for unsigned bytes; nibble + 8 or the unsigned nibble, widened).
-template <int J, int KC, int KM, int VC, int VM>
-__device__ inline long key_frag(const TileRaw<KC, KM, VC, VM>& t, int bb) {
+template <int J, int KC, int KM, int VC, int VM, bool PT>
+__device__ inline long key_frag(const TileRaw<KC, KM, VC, VM, PT>& t, int bb) {
   uint32_t lo, hi;
   if constexpr (Codes<KC>::B8) {
     const u32x4 r = t.k[bb][J >> 1];
@@ -525,8 +542,8 @@ __device__ inline float key_offset() {
 
 // Value operands of the 8 output MFMAs: lane (c, g) gives feature 8c + j of
 // its 8 tokens, two tokens per fp16 pair.
-template <int KC, int KM, int VC, int VM>
-__device__ inline void value_frags(const TileRaw<KC, KM, VC, VM>& t, half8 out[8],
+template <int KC, int KM, int VC, int VM, bool PT>
+__device__ inline void value_frags(const TileRaw<KC, KM, VC, VM, PT>& t, half8 out[8],
                                    const NibbleMasks& nm) {
   constexpr bool S = Codes<VC>::SIGNED;
   uint32_t pr[8][4];  // [j][token pair]
@@ -644,8 +661,8 @@ __device__ inline int row_limb(int r) { return G == 8 ? (r & 1) : (r & 3); }
 // Rows are (query head, fp16 limb) pairs.  The weights P^T go through LDS
 // (pw, this wave's region) from the score layout to the operand layout.
 // qs[u], sumq[u]: score scale and query sum of local head u.
-template <int KC, int KM, bool KCH, int VC, int VM, int G>
-__device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, int tend,
+template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PT>
+__device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM, PT>& t, int t0, int tend,
                                     const long (*qa)[4], const float* qs, const float* sq,
                                     int lt, int g, uint32_t psel, const uint32_t* prd,
                                     uint32_t* pwr, const NibbleMasks& nm, RowState<G>& st) {
@@ -668,14 +685,20 @@ __device__ inline void compute_tile(const TileRaw<KC, KM, VC, VM>& t, int t0, in
   // lane (lt, g ^ 1)'s
   Meta<KM> kmb[2];
   Meta<VM> vmb[2];
-  {
+  if constexpr (PT) {
     const bool odd = g & 1;
-    const Meta<KM> ko = t.km.xor16();
-    const Meta<VM> vo = t.vm.xor16();
-    kmb[0] = odd ? ko : t.km;
-    kmb[1] = odd ? t.km : ko;
-    vmb[0] = odd ? vo : t.vm;
-    vmb[1] = odd ? t.vm : vo;
+    const Meta<KM> ko = t.km[0].xor16();
+    const Meta<VM> vo = t.vm[0].xor16();
+    kmb[0] = odd ? ko : t.km[0];
+    kmb[1] = odd ? t.km[0] : ko;
+    vmb[0] = odd ? vo : t.vm[0];
+    vmb[1] = odd ? t.vm[0] : vo;
+  } else {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      kmb[bb] = t.km[bb];
+      vmb[bb] = t.vm[bb];
+    }
   }
   // scores before the query scale qs (> 0): sk[u][bb] for token t of block bb
   float sk[HPG][2], vs[2], vz[2];
@@ -1556,7 +1579,7 @@ struct NoPre {
 };
 
 template <int KC, int KM, bool KCH, int VC, int VM, int G, bool PAGED, bool QB, bool RING,
-          typename Pre = NoPre>
+          bool PT, typename Pre = NoPre>
 __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok1, int nend,
                             int row, const uint8_t* kc, const uint8_t* vc, const uint8_t* km,
                             const uint8_t* vm, size_t head_tok, int rblk, Shared<G>& sh,
@@ -1637,7 +1660,7 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
     pre();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  TileRaw<KC, KM, VC, VM> buf[NB];
+  TileRaw<KC, KM, VC, VM, PT> buf[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     load_tile<PAGED, RING>(buf[k], ad, w0 + k * TILE, w1, lo);
@@ -1898,7 +1921,7 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   if constexpr (TIER) {
     if (it.kind == 3) {  // the middle tier: int8 codes, fp32 scales, in its ring
       if (si.nm > 0) {
-        quant_range<CK_I8, MK_F32, false, CK_I8, MK_F32, G, false, QB, true>(
+        quant_range<CK_I8, MK_F32, false, CK_I8, MK_F32, G, false, QB, true, true>(
             a, b, h, si.nq, si.nq + si.nm, si.nq + si.nm, direct ? DIRECT_OUT : split, a.mid.k,
             a.mid.v, (const uint8_t*)a.mid.ks, (const uint8_t*)a.mid.vs, pair * a.mid.slots,
             a.mid.slots >> 4, sh);
@@ -1930,11 +1953,11 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
     // the wave whose range holds the position leaving the window moves the
     // tokens (quant_range decides when)
     auto move = [&]() { step_window(a, b, h, true); };
-    quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
+    quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false, TIER>(
         a, b, h, tok0, tok1, si.nq, direct ? DIRECT_OUT : split, a.k_codes, a.v_codes, a.k_meta,
         a.v_meta, PAGED ? 0 : pair * a.max_tokens, 0, sh, evict ? si.nq - 1 : -1, move);
   } else {
-    quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false>(
+    quant_range<KC, KM, KCH, VC, VM, G, PAGED, QB, false, TIER>(
         a, b, h, tok0, tok1, si.nq, direct ? DIRECT_OUT : split, a.k_codes, a.v_codes, a.k_meta,
         a.v_meta, PAGED ? 0 : pair * a.max_tokens, 0, sh);
   }
