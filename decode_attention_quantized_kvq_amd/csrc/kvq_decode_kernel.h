@@ -1561,13 +1561,6 @@ __device__ Item map_item(const DecodeArgs& a, int item, int* hist, bool tier) {
   return it;
 }
 
-// A decode step with a window: waits until both waves of step_window have
-// counted their stores done in *done (LDS).
-__device__ inline void wait_stored(const int* done) {
-  while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < 2)
-    __builtin_amdgcn_s_sleep(1);
-}
-
 // Attends quantized positions [tok0, tok1) of (sequence b, KV head h) with
 // the G query heads of h and writes partial row `row` (DIRECT_OUT: the
 // output).  The codes and
@@ -1934,8 +1927,8 @@ __global__ void __launch_bounds__(256, KVQ_MINW) decode_split(DecodeArgs a) {
   const int tok1 = min(tok0 + a.split_tokens, si.nq);
   // decode step with a window: the workgroup of the pair's last chunk, which
   // holds the position leaving the window, moves it into the cache and the
-  // new token into the ring; the wave whose range holds that position loads
-  // its tile once both stores are done
+  // new token into the ring; quant_range orders the load of that position's
+  // tile behind the stores
   if constexpr (STEP) {
     const bool evict = a.k_new != nullptr && a.ring && split == pl.ns - 1;
     if (a.k_new != nullptr) {
