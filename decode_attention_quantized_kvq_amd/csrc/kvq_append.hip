@@ -59,16 +59,6 @@ __device__ inline int q_capacity(const AppendArgs& a) {
   return a.paged ? a.bt_stride * 16 : a.max_tokens;
 }
 
-// Index (in tokens) of quantized position p of (b, h) in codes/meta arrays.
-__device__ inline size_t slot_index(const AppendArgs& a, int b, int h, int p) {
-  if (a.paged) {
-    int phys = a.block_table[(size_t)b * a.bt_stride + (p >> 4)];
-    phys = clampi(phys, 0, a.num_blocks - 1);
-    return ((size_t)phys * a.hkv + h) * 16 + (p & 15);
-  }
-  return ((size_t)b * a.hkv + h) * a.max_tokens + p;
-}
-
 __device__ inline int meta_size(MetaKind m) {
   switch (m) {
     case MK_F32: return 4;
@@ -120,7 +110,7 @@ __device__ void grow_channels(const AppendArgs& a, int b, int h, const SeqRange&
   const float s0 = chan[d], s1 = snew[d];
   if (s1 != s0) {
     for (int t = tid >> 7; t < qlo; t += 2) {
-      uint8_t* cp = a.k_codes + slot_index(a, b, h, t) * (size_t)D + d;
+      uint8_t* cp = code_row(a, a.kk, a.k_codes, b, h, t) + d;
       const int c = (int)(int8_t)*cp;
       *cp = (uint8_t)clampi((int)rint((double)c * (double)s0 / (double)s1), -qmax, qmax);
     }
@@ -232,7 +222,7 @@ __device__ inline InputLoader input_loader(const AppendArgs& a, int w, size_t he
   return InputLoader{w == 0 ? a.k_new : a.v_new, w == 0 ? a.k_win : a.v_win, head, start, lane};
 }
 
-constexpr TensorKind MID_KIND{CK_I8, MK_F32, false, false, false};
+constexpr TensorKind MID_KIND{CK_I8, MK_F32, false, false, false, 128, 4, 0};
 
 __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -256,19 +246,21 @@ __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   auto ld = [&](int p, double& x0, double& x1) { in(a, p, x0, x1); };
   if (a.mid.tokens) {  // into the middle tier: int8, fp32 scale, ring slot p % slots
     auto mslot = [&](int p) { return head * a.mid.slots + (size_t)(p % a.mid.slots); };
-    quantize_group(MID_KIND, ld, mslot, p0, 1, w == 0 ? a.mid.k : a.mid.v,
-                   (uint8_t*)(w == 0 ? a.mid.ks : a.mid.vs), mslot(p0), nullptr, 1.0f, lane);
+    uint8_t* mc = w == 0 ? a.mid.k : a.mid.v;
+    auto mrow = [&](int p) { return mc + mslot(p) * (size_t)D; };
+    quantize_group(MID_KIND, ld, mrow, p0, 1, (uint8_t*)((w == 0 ? a.mid.ks : a.mid.vs) + mslot(p0)),
+                   nullptr, 1.0f, lane);
     return;
   }
-  auto slot = [&](int p) { return slot_index(a, b, h, p); };
   uint8_t* codes = w == 0 ? a.k_codes : a.v_codes;
+  auto row = [&](int p) { return code_row(a, k, codes, b, h, p); };
   if (k.code == CK_BF16) {  // unquantized (bits 16): the bf16 values themselves
     for (int j = 0; j < g; ++j) {
       double x0, x1;
       ld(p0 + j, x0, x1);
       const uint32_t v = (uint32_t)f32_to_bf16_bits((float)x0) |
                          ((uint32_t)f32_to_bf16_bits((float)x1) << 16);
-      ((uint32_t*)(codes + slot(p0 + j) * (size_t)(2 * D)))[lane] = v;
+      ((uint32_t*)row(p0 + j))[lane] = v;
     }
     return;
   }
@@ -276,8 +268,7 @@ __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   const float* chan = (w == 0 && k.channel) ? a.k_chan + head * D : nullptr;
   const float* sup = w == 0 ? a.k_super : a.v_super;
   const float super = k.meta == MK_U8 ? sup[head] : 1.0f;
-  quantize_group(k, ld, slot, p0, g, codes, meta, slot_index(a, b, h, p0) >> a.tgshift, chan,
-                 super, lane);
+  quantize_group(k, ld, row, p0, g, meta_elem(a, k, codes, meta, b, h, p0), chan, super, lane);
 }
 
 // Middle tier: the positions an append moves into the cache's format,
@@ -318,10 +309,11 @@ __global__ void __launch_bounds__(128) append_demote(AppendArgs a) {
     x0 = v0;
     x1 = v1;
   };
-  auto slot = [&](int q) { return slot_index(a, b, h, q); };
   const TensorKind k = w == 0 ? a.kk : a.vk;
-  quantize_group(k, ld, slot, p, 1, w == 0 ? a.k_codes : a.v_codes, w == 0 ? a.k_meta : a.v_meta,
-                 slot_index(a, b, h, p), nullptr, 1.0f, lane);
+  uint8_t* codes = w == 0 ? a.k_codes : a.v_codes;
+  auto row = [&](int q) { return code_row(a, k, codes, b, h, q); };
+  quantize_group(k, ld, row, p, 1, meta_elem(a, k, codes, w == 0 ? a.k_meta : a.v_meta, b, h, p),
+                 nullptr, 1.0f, lane);
 }
 
 __global__ void __launch_bounds__(128) append_window(AppendArgs a) {

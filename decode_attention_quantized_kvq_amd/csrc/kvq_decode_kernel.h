@@ -356,6 +356,7 @@ struct Addr {
   const uint8_t* km;
   const uint8_t* vm;
   int num_blocks, hkv, h;
+  int ku, vu;            // paged: bytes of one (block, head) unit of K and V
   int gs;                // log2 of the token group size (metadata per group)
   size_t head_tok;       // contiguous: first token slot of this head
   int nblk;              // blocks holding tokens
@@ -370,9 +371,10 @@ struct Addr {
 constexpr int WAVE_BLOCKS = 128;
 
 // Token slot index of block `blk` (clamped to the blocks holding tokens and,
-// when paged, to the pool); wave-uniform.  Paged lookups read the entries
-// preloaded into the wave's registers (v_readlane), so the token loop issues
-// no memory access for them.  RING: the middle tier's ring of rblk blocks.
+// when paged, to the pool), or when paged its unit index phys H_kv + h;
+// wave-uniform.  Paged lookups read the entries preloaded into the wave's
+// registers (v_readlane), so the token loop issues no memory access for
+// them.  RING: the middle tier's ring of rblk blocks.
 template <bool PAGED, bool RING = false>
 __device__ inline size_t block_slot(const Addr& ad, int blk) {
   blk = blk < ad.nblk ? blk : ad.nblk - 1;
@@ -384,7 +386,7 @@ __device__ inline size_t block_slot(const Addr& ad, int blk) {
     int phys = i < 64 ? __builtin_amdgcn_readlane(ad.ent[0], i)
                       : __builtin_amdgcn_readlane(ad.ent[1], i - 64);
     phys = phys < 0 ? 0 : (phys >= ad.num_blocks ? ad.num_blocks - 1 : phys);
-    return ((size_t)phys * ad.hkv + ad.h) * 16;
+    return (size_t)phys * ad.hkv + ad.h;
   } else {
     return ad.head_tok + (size_t)blk * 16;
   }
@@ -458,13 +460,20 @@ template <bool PAGED, bool RING, int KC, int KM, int VC, int VM, bool PT>
 __device__ inline void load_tile(TileRaw<KC, KM, VC, VM, PT>& t, const Addr& ad, int t0, int tend,
                                  const LaneOff& o) {
   constexpr int KROW = Codes<KC>::ROW, VROW = Codes<VC>::ROW;
-  size_t slots[2];
+  const uint8_t* kmb[2];
+  const uint8_t* vmb[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const bool live = t0 + 16 * bb < tend;
     const size_t slot = block_slot<PAGED, RING>(ad, (t0 >> 4) + bb);
-    slots[bb] = slot;
-    const auto rk = rsrc(ad.k + slot * KROW, live ? 16 * KROW : 0);
+    // the block's code rows and metadata: paged, its unit (16 code rows, then
+    // the metadata elements); otherwise slot rows and metadata element
+    // slot >> gs (one per token group)
+    const uint8_t* kb = PAGED ? ad.k + slot * ad.ku : ad.k + slot * KROW;
+    const uint8_t* vb = PAGED ? ad.v + slot * ad.vu : ad.v + slot * VROW;
+    kmb[bb] = PAGED ? kb + 16 * KROW : ad.km + (slot >> ad.gs) * Meta<KM>::BYTES;
+    vmb[bb] = PAGED ? vb + 16 * VROW : ad.vm + (slot >> ad.gs) * Meta<VM>::BYTES;
+    const auto rk = rsrc(kb, live ? 16 * KROW : 0);
     if (Codes<KC>::B2) {
       const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rk, o.k0, 0, KVQ_CPOL);
       t.k[bb][0] = u32x4{w.x, w.y, 0u, 0u};
@@ -472,7 +481,7 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM, PT>& t, const Addr& ad,
       t.k[bb][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k0, 0, KVQ_CPOL);
     }
     if (Codes<KC>::B8) t.k[bb][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k1, 0, KVQ_CPOL);
-    const auto rv = rsrc(ad.v + slot * VROW, live ? 16 * VROW : 0);
+    const auto rv = rsrc(vb, live ? 16 * VROW : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (Codes<VC>::B8)
@@ -482,25 +491,19 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM, PT>& t, const Addr& ad,
       else
         t.v4[4 * bb + i] = __builtin_amdgcn_raw_buffer_load_b32(rv, o.v[i], 0, KVQ_CPOL);
     }
-    // metadata element of token slot s: s >> gs (one per token group)
     if constexpr (!PT) {
       if (Meta<KM>::BYTES)
-        t.km[bb].load_buf(rsrc(ad.km + (slot >> ad.gs) * Meta<KM>::BYTES,
-                               live ? (16 >> ad.gs) * Meta<KM>::BYTES : 0),
-                          o.km);
+        t.km[bb].load_buf(rsrc(kmb[bb], live ? (16 >> ad.gs) * Meta<KM>::BYTES : 0), o.km);
       if (Meta<VM>::BYTES)
-        t.vm[bb].load_buf(rsrc(ad.vm + (slot >> ad.gs) * Meta<VM>::BYTES,
-                               live ? (16 >> ad.gs) * Meta<VM>::BYTES : 0),
-                          o.vm);
+        t.vm[bb].load_buf(rsrc(vmb[bb], live ? (16 >> ad.gs) * Meta<VM>::BYTES : 0), o.vm);
     }
   }
   if constexpr (PT) {
     // one load per tensor covers both blocks (lane (t, g): block g & 1); a
     // block past tend reads a stored slot (block_slot clamps) whose values
     // compute_tile masks
-    const size_t ms = (o.odd ? slots[1] : slots[0]) >> ad.gs;
-    if (Meta<KM>::BYTES) t.km[0].load_glob(ad.km + ms * Meta<KM>::BYTES + o.km);
-    if (Meta<VM>::BYTES) t.vm[0].load_glob(ad.vm + ms * Meta<VM>::BYTES + o.vm);
+    if (Meta<KM>::BYTES) t.km[0].load_glob((o.odd ? kmb[1] : kmb[0]) + o.km);
+    if (Meta<VM>::BYTES) t.vm[0].load_glob((o.odd ? vmb[1] : vmb[0]) + o.vm);
   }
 }
 
@@ -1610,6 +1613,8 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
   ad.km = km;
   ad.vm = vm;
   ad.num_blocks = a.num_blocks;
+  ad.ku = a.kk.unit;
+  ad.vu = a.vk.unit;
   ad.hkv = a.hkv;
   ad.h = h;
   ad.gs = a.tgshift;
@@ -1792,17 +1797,11 @@ __device__ void step_append(const DecodeArgs& a, int b, int h, int p) {
       x0 = qz::load_in(src, head * D + 2 * lane, a.in_bf16);
       x1 = qz::load_in(src, head * D + 2 * lane + 1, a.in_bf16);
     };
-    auto slot = [&](int pos) -> size_t {
-      if (a.paged) {
-        int phys = a.block_table[(size_t)b * a.bt_stride + (pos >> 4)];
-        phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
-        return ((size_t)phys * a.hkv + h) * 16 + (pos & 15);
-      }
-      return head * a.max_tokens + pos;
-    };
     uint8_t* codes = const_cast<uint8_t*>(w == 0 ? a.k_codes : a.v_codes);
     uint8_t* meta = const_cast<uint8_t*>(w == 0 ? a.k_meta : a.v_meta);
-    qz::quantize_group(k, ld, slot, p, 1, codes, meta, slot(p), nullptr, 1.0f, lane);
+    auto row = [&](int pos) { return qz::code_row(a, k, codes, b, h, pos); };
+    qz::quantize_group(k, ld, row, p, 1, qz::meta_elem(a, k, codes, meta, b, h, p), nullptr, 1.0f,
+                       lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
@@ -1823,14 +1822,6 @@ __device__ void step_window(const DecodeArgs& a, int b, int h, bool evict) {
   const size_t head = (size_t)b * a.hkv + h;
   const int e = p - a.window;
   const int cap = a.paged ? a.bt_stride * 16 : a.max_tokens;
-  auto slot = [&](int pos) -> size_t {
-    if (a.paged) {
-      int phys = a.block_table[(size_t)b * a.bt_stride + (pos >> 4)];
-      phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
-      return ((size_t)phys * a.hkv + h) * 16 + (pos & 15);
-    }
-    return head * a.max_tokens + pos;
-  };
   for (int w = 0; w < 2; ++w) {
     uint16_t* ring = const_cast<uint16_t*>(w == 0 ? a.k_win : a.v_win);
     if (evict && e >= 0 && e < cap) {
@@ -1842,7 +1833,9 @@ __device__ void step_window(const DecodeArgs& a, int b, int h, bool evict) {
       };
       uint8_t* codes = const_cast<uint8_t*>(w == 0 ? a.k_codes : a.v_codes);
       uint8_t* meta = const_cast<uint8_t*>(w == 0 ? a.k_meta : a.v_meta);
-      qz::quantize_group(k, ld, slot, e, 1, codes, meta, slot(e), nullptr, 1.0f, lane);
+      auto crow = [&](int pos) { return qz::code_row(a, k, codes, b, h, pos); };
+      qz::quantize_group(k, ld, crow, e, 1, qz::meta_elem(a, k, codes, meta, b, h, e), nullptr,
+                         1.0f, lane);
     }
     // the ring slot of p is the one e held: its values were read above
     const uint16_t* src = (const uint16_t*)(w == 0 ? a.k_new : a.v_new);

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
+#include "kvq_quantize.h"
 
 namespace kvq {
 namespace {
@@ -66,16 +67,6 @@ __device__ inline int code_of(uint64_t raw, int bits, bool sgn, int e) {
 // cache's format, [na, nq) the middle tier, the rest bf16.
 __device__ inline void dequant_position(const DequantArgs& a, size_t head, int b, int h, int p,
                                         int na, int nq, int f0) {
-  size_t slot = 0;
-  if (p < na) {
-    if (a.paged) {
-      int phys = a.block_table[(size_t)b * a.bt_stride + (p >> 4)];
-      phys = phys < 0 ? 0 : (phys >= a.num_blocks ? a.num_blocks - 1 : phys);
-      slot = ((size_t)phys * a.hkv + h) * 16 + (p & 15);
-    } else {
-      slot = head * a.max_tokens + p;
-    }
-  }
   for (int w = 0; w < 2; ++w) {
     uint16_t* out = (w ? a.v_out : a.k_out) + (head * a.out_tokens + p) * D + f0;
     uint16_t o[8];
@@ -92,26 +83,27 @@ __device__ inline void dequant_position(const DequantArgs& a, size_t head, int b
       for (int e = 0; e < 8; ++e) o[e] = bf16_of_product((float)code_of(raw, 8, true, e), s);
     } else {
       const TensorKind k = w ? a.vk : a.kk;
-      const int rowb = D * bits_of(k.code) / 8;
-      const uint8_t* row = (w ? a.v_codes : a.k_codes) + slot * rowb;
-      const uint8_t* meta = w ? a.v_meta : a.k_meta;
-      const size_t mi = slot >> a.tgshift;  // metadata element of the token's group
+      const uint8_t* codes = w ? a.v_codes : a.k_codes;
+      const uint8_t* row = qz::code_row(a, k, codes, b, h, p);
+      // the metadata element of the token's group
+      const uint8_t* me = k.channel ? nullptr
+                                    : qz::meta_elem(a, k, codes, w ? a.v_meta : a.k_meta, b, h, p);
       // value = cm * s with cm an integer: c, c - z, or c u (8-bit scale codes)
       float s = 1.0f, z = 0.0f, um = 1.0f;
       if (!k.channel) {
         if (k.meta == MK_F32) {
-          s = ((const float*)meta)[mi];
+          s = ((const float*)me)[0];
         } else if (k.meta == MK_F32Z) {
-          s = ((const float*)meta)[2 * mi];
-          z = ((const float*)meta)[2 * mi + 1];
+          s = ((const float*)me)[0];
+          z = ((const float*)me)[1];
         } else if (k.meta == MK_F16) {
-          s = (float)((const _Float16*)meta)[mi];
+          s = (float)((const _Float16*)me)[0];
         } else if (k.meta == MK_F16Z) {
-          s = (float)((const _Float16*)meta)[2 * mi];
-          z = (float)((const _Float16*)meta)[2 * mi + 1];
+          s = (float)((const _Float16*)me)[0];
+          z = (float)((const _Float16*)me)[1];
         } else if (k.meta == MK_U8) {
           s = (w ? a.v_super : a.k_super)[head];
-          um = (float)meta[mi];
+          um = (float)me[0];
         }
       }
       const int bits = bits_of(k.code);

@@ -35,12 +35,24 @@ struct TensorKind {
   bool channel;   // per-channel scales (keys only)
   bool grow;      // ... that follow the running absmax (stored codes re-quantized)
   bool hold;      // ... fixed when the sequence's first position leaves the window
+  // where the codes and metadata live: row = code bytes of one token; mb =
+  // bytes of one metadata element; unit = paged: bytes of one (block, KV
+  // head) unit, its 16 code rows then its 16 / g metadata elements, padded
+  // to whole rows (0 for a contiguous cache)
+  int row, mb, unit;
 };
 
 // Code bytes of one token row of one head (0 for unsupported widths).
 inline int row_bytes(int bits, int d) { return d * bits / 8; }
 
 int meta_bytes(const kvq_tensor_fmt& f);
+
+// Bytes of one (block, KV head) unit of a paged cache: 16 code rows, then the
+// block's 16 / g metadata elements in whole rows (P2, "Metadata and block
+// layout remain part of physical memory use": the block carries its scales).
+inline int unit_bytes(int row, int meta_block) {
+  return 16 * row + (meta_block + row - 1) / row * row;
+}
 
 // Classifies a format; returns KVQ_OK, KVQ_ERR_INVALID_ARG or
 // KVQ_ERR_UNSUPPORTED (for the kernels).  is_key: keys accept channel axis.

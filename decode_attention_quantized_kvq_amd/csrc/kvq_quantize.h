@@ -80,6 +80,31 @@ __device__ inline double f16_bits_to_f64(uint16_t h) {
 
 __device__ inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Where position p of (sequence b, KV head h) lives, for a tensor of kind k
+// (Args: any of the launch argument structs, which name the layout fields
+// alike).  Contiguous: token slot s = (b H_kv + h) max_tokens + p, code row
+// at codes + s row, metadata element s >> gs at meta.  Paged: unit u =
+// block_table[b][p / 16] H_kv + h (the entry clamped into the pool), code row
+// p mod 16 of it, and its metadata elements after its 16 rows.
+template <typename Args>
+__device__ inline size_t unit_of(const Args& a, int b, int h, int p) {
+  const int phys = clampi(a.block_table[(size_t)b * a.bt_stride + (p >> 4)], 0, a.num_blocks - 1);
+  return (size_t)phys * a.hkv + h;
+}
+template <typename Args, typename P>
+__device__ inline P* code_row(const Args& a, const TensorKind& k, P* codes, int b, int h, int p) {
+  if (a.paged) return codes + unit_of(a, b, h, p) * k.unit + (size_t)(p & 15) * k.row;
+  return codes + (((size_t)b * a.hkv + h) * a.max_tokens + p) * k.row;
+}
+template <typename Args, typename P>
+__device__ inline P* meta_elem(const Args& a, const TensorKind& k, P* codes, P* meta, int b, int h,
+                               int p) {
+  if (a.paged)
+    return codes + unit_of(a, b, h, p) * k.unit + 16 * (size_t)k.row +
+           (size_t)((p & 15) >> a.tgshift) * k.mb;
+  return meta + ((((size_t)b * a.hkv + h) * a.max_tokens + p) >> a.tgshift) * k.mb;
+}
+
 __device__ inline int rne_code(double x, double s) { return (int)rint(x / s); }
 
 __device__ inline int code_bits(CodeKind c) {
@@ -93,13 +118,13 @@ __device__ inline int qmax_zp(int bits) { return (1 << bits) - 1; }
 // Quantizes the token group at positions p0 .. p0+g-1 of one (sequence,
 // head): one scale (and zero point, or 8-bit scale code) over all its g*D
 // values, then the codes of each token.  ld(p, x0, x1) loads elements 2*lane
-// and 2*lane+1 of position p; slot(p) is its code slot; metadata element m
-// belongs to the group.  g = 1 is the per-token case.  Values are taken in
-// fp64: inputs are exact in it, and so is a middle-tier value c * s.
-template <typename Load, typename Slot>
-__device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, int g,
-                               uint8_t* codes, uint8_t* meta, size_t m, const float* chan,
-                               float super, int lane) {
+// and 2*lane+1 of position p; row(p) is the address of its code row; meta is
+// the address of the group's metadata element (unused for per-channel
+// scales).  g = 1 is the per-token case.  Values are taken in fp64: inputs
+// are exact in it, and so is a middle-tier value c * s.
+template <typename Load, typename Row>
+__device__ void quantize_group(const TensorKind k, Load ld, Row row, int p0, int g,
+                               uint8_t* meta, const float* chan, float super, int lane) {
   const int bits = code_bits(k.code);
   const bool zp = k.meta == MK_F32Z || k.meta == MK_F16Z;
   // 1. group statistics
@@ -161,17 +186,17 @@ __device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, i
   }
   if (lane == 0 && !k.channel) {
     if (k.meta == MK_U8) {
-      meta[m] = (uint8_t)u;
+      *meta = (uint8_t)u;
     } else if (k.meta == MK_F32) {
-      ((uint32_t*)meta)[m] = sbits;
+      *(uint32_t*)meta = sbits;
     } else if (k.meta == MK_F16) {
-      ((uint16_t*)meta)[m] = (uint16_t)sbits;
+      *(uint16_t*)meta = (uint16_t)sbits;
     } else if (k.meta == MK_F32Z) {
-      ((uint32_t*)meta)[2 * m] = sbits;
-      ((float*)meta)[2 * m + 1] = (float)z;
+      ((uint32_t*)meta)[0] = sbits;
+      ((float*)meta)[1] = (float)z;
     } else {
       const _Float16 zh = (_Float16)(float)z;
-      ((uint32_t*)meta)[m] = sbits | ((uint32_t)__builtin_bit_cast(uint16_t, zh) << 16);
+      *(uint32_t*)meta = sbits | ((uint32_t)__builtin_bit_cast(uint16_t, zh) << 16);
     }
   }
   // 3. codes of each token of the group
@@ -189,18 +214,18 @@ __device__ void quantize_group(const TensorKind k, Load ld, Slot slot, int p0, i
       c0 = clampi(rne_code(x0, s) + z, 0, qmax);
       c1 = clampi(rne_code(x1, s) + z, 0, qmax);
     }
-    const size_t sl = slot(p0 + j);
+    uint8_t* r = row(p0 + j);
     if (bits == 8) {
       const uint32_t v = ((uint32_t)(c0 & 0xFF)) | ((uint32_t)(c1 & 0xFF) << 8);
-      ((uint16_t*)(codes + sl * (size_t)QD))[lane] = (uint16_t)v;
+      ((uint16_t*)r)[lane] = (uint16_t)v;
     } else if (bits == 4) {
       const uint32_t v = ((uint32_t)(c0 & 0xF)) | ((uint32_t)(c1 & 0xF) << 4);
-      (codes + sl * (size_t)(QD / 2))[lane] = (uint8_t)v;
+      r[lane] = (uint8_t)v;
     } else {
       // four 2-bit codes per byte: elements 4j .. 4j+3 come from lanes 2j, 2j+1
       const uint32_t v = ((uint32_t)(c0 & 3)) | ((uint32_t)(c1 & 3) << 2);
       const uint32_t odd = (uint32_t)__shfl_xor((int)v, 1);
-      if ((lane & 1) == 0) (codes + sl * (size_t)(QD / 4))[lane >> 1] = (uint8_t)(v | (odd << 4));
+      if ((lane & 1) == 0) r[lane >> 1] = (uint8_t)(v | (odd << 4));
     }
   }
 }

@@ -102,6 +102,12 @@ Readings where the pages leave a step open (each restated where it is used):
       from its middle-tier reconstruction c * s (exact).  The cache's format
       is then a per-token one (no channel axes, no 8-bit scale codes, no token
       groups).
+  R27 where a paged block keeps its metadata (P2 "Metadata and block layout
+      remain part of physical memory use": the block layout is part of what
+      is allocated; the pages fix no layout): each (block, KV head) of a
+      paged cache is one unit, its 16 code rows followed by its 16 / g
+      metadata elements, which take whole code rows; the rest of the last of
+      those rows is padding.
   Scale underflow: a scale that rounds to 0 in its storage type is replaced by
   that type's smallest positive value (fp32 2^-149, fp16 2^-24); an fp16 scale
   above 65504 saturates to 65504.
@@ -697,6 +703,12 @@ def ring_slots(window: int = 0, group: int = 1) -> int:
     return window + (group if group > 1 else 0)
 
 
+def _unit_pad(row: int, meta_block: int) -> int:
+    """Reading R27: a paged block keeps its metadata in whole code rows after
+    its own; the unused end of the last of those rows is padding."""
+    return -(-meta_block // row) * row - meta_block
+
+
 def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
                 d: int, lens: Sequence[int], window: int = 0,
                 block_tokens: int = 0, max_tokens: Optional[int] = None,
@@ -720,7 +732,9 @@ def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
               contiguous one, and the unused bf16 ring slots of either (the
               ring is one fixed-size buffer per sequence and head in both
               layouts: P2 "Metadata and block layout remain part of physical
-              memory use" counts what is allocated, not only what is used).
+              memory use" counts what is allocated, not only what is used);
+              in a paged cache, the rest of the code rows that hold each
+              block's metadata (reading R27).
     total     the sum of the four.
     """
     def row(fmt):  # bytes of one token's codes
@@ -745,6 +759,10 @@ def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
         else:
             alloc_q = max_tokens if max_tokens is not None else n_q
         out["padding"] += layers * hkv * ((alloc_q - n_q) * codes + (alloc_q - n_q) // group * meta)
+        if block_tokens:
+            out["padding"] += layers * hkv * (alloc_q // block_tokens) * (
+                _unit_pad(row(key), block_tokens // group * meta_bytes_per_token(key))
+                + _unit_pad(row(value), block_tokens // group * meta_bytes_per_token(value)))
         if ring:
             out["padding"] += layers * hkv * (ring - n_w) * d * 2 * 2
     out["total"] = out["payload"] + out["metadata"] + out["window"] + out["padding"]

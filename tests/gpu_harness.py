@@ -166,13 +166,34 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def token_slots(bt: Built, b: int, h: int, n: int) -> np.ndarray:
-    """Slot index (in tokens) of quantized positions 0..n-1 of (b, h)."""
+def meta_elem_bytes(spec) -> int:
+    """Bytes of one metadata element of a tensor format (0: per-channel)."""
+    if spec.get("axis", "token") != "token":
+        return 0
+    scale = spec.get("scale", "f32")
+    if scale == "u8_super":
+        return 1
+    w = 4 if scale == "f32" else 2
+    return 2 * w if spec.get("zero_point") else w
+
+
+def unit_rows(wl, spec) -> int:
+    """Rows of one paged (block, KV head) unit as the header documents it: 16
+    code rows, then the block's 16 / g metadata elements in whole rows."""
+    row = wl["d"] * spec["bits"] // 8
+    meta = 16 // wl.get("group", 1) * meta_elem_bytes(spec)
+    return 16 + -(-meta // row)
+
+
+def token_slots(bt: Built, b: int, h: int, n: int, t: str = "k") -> np.ndarray:
+    """Row index (in code rows of tensor t) of quantized positions 0..n-1 of
+    (b, h)."""
     cfg = bt.cfg
     p = np.arange(n)
     if cfg.block_tokens:
         phys = bt.table[b, p // 16].astype(np.int64)
-        return (phys * cfg.num_kv_heads + h) * 16 + p % 16
+        U = unit_rows(bt.wl, bt.wl["key" if t == "k" else "value"])
+        return (phys * cfg.num_kv_heads + h) * U + p % 16
     return (b * cfg.num_kv_heads + h) * cfg.max_tokens + p
 
 
@@ -199,7 +220,7 @@ def device_records(bt: Built, t: str, b: int, h: int, n: int) -> dict:
     bits, zp, scale = spec["bits"], bool(spec.get("zero_point")), spec.get("scale", "f32")
     D = bt.wl["d"]
     row = D * bits // 8
-    slots = token_slots(bt, b, h, n)
+    slots = token_slots(bt, b, h, n, t)
     # gather the pair's rows on the device: a full-size code buffer can hold
     # several GiB
     codes_dev = bt.cache.buffers[f"{t}_codes"].view(-1, row)
@@ -209,10 +230,21 @@ def device_records(bt: Built, t: str, b: int, h: int, n: int) -> dict:
         ch = host(bt.cache.buffers["k_chan_scale"]).view(np.float32).reshape(-1, D)
         out["chan"] = ch[b * bt.cfg.num_kv_heads + h]
         return out
-    meta = host(bt.cache.buffers[f"{t}_meta"])
-    # one metadata element per token group: element slot // g of its first slot
     g = bt.wl.get("group", 1)
-    slots = slots[::g] // g
+    mb = meta_elem_bytes(spec)
+    if bt.cfg.block_tokens:
+        # paged: the elements follow the 16 code rows of each block's unit
+        p = np.arange(0, n, g)
+        unit = (bt.table[b, p // 16].astype(np.int64) * bt.cfg.num_kv_heads + h) * unit_rows(bt.wl, spec)
+        off = (unit + 16) * row + (p % 16) // g * mb
+        flat = bt.cache.buffers[f"{t}_codes"].view(-1)
+        idx = torch.from_numpy((off[:, None] + np.arange(mb)).reshape(-1)).to(flat.device)
+        meta = host(flat.index_select(0, idx))
+        slots = np.arange(len(p))
+    else:
+        meta = host(bt.cache.buffers[f"{t}_meta"])
+        # one metadata element per token group: element slot // g of its first slot
+        slots = slots[::g] // g
     if scale == "u8_super":
         out["u"] = meta[slots]
         out["S"] = host(bt.cache.buffers[f"{t}_super"]).view(np.float32)[b * bt.cfg.num_kv_heads + h]

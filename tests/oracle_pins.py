@@ -1095,7 +1095,10 @@ def pin_byte_accounting(O):
     lens = [1024, 5000, 32768]
     assert O.decode_traffic(i8, i8, 8, 128, lens, window=128) == sum(8 * (65536 + (n - 128) * 264) for n in lens)
     pad = O.cache_bytes(i8, i8, 1, 8, 128, [145], window=128, block_tokens=16)
-    assert pad["padding"] == 8 * (16 - 17 % 16) * 264
+    # 17 quantized positions in 2 blocks: 15 unused slots; and in each block
+    # of K and of V, the 16 fp32 scales (64 B) fill half of a 128-byte code
+    # row (R27)
+    assert pad["padding"] == 8 * ((16 - 17 % 16) * 264 + 2 * 2 * 64)
 
 
 def pin_allocated_bytes(O):
@@ -1107,7 +1110,9 @@ def pin_allocated_bytes(O):
     W (+ g) slots, a middle-tier ring of M + 32 int8 rows with fp32 scales,
     and its per-head side data; a paged one holds whole 16-token blocks of
     the quantized positions (counted by brute force, position by position),
-    the same ring and side data."""
+    each block of each tensor a unit of 16 code rows plus its 16 / g
+    metadata elements rounded up to whole code rows (reading R27), the same
+    ring and side data."""
     rng = _rng(223)
     fmts = [(O.TensorFormat(8), O.TensorFormat(8)),
             (O.TensorFormat(4, zero_point=True, scale="f16"), O.TensorFormat(4, zero_point=True, scale="f16")),
@@ -1141,7 +1146,11 @@ def pin_allocated_bytes(O):
                 # older than the window
                 nq = sum(1 for p in range(n) if (p // g) * g + g <= n - W)
                 blocks = -(-nq // 16)
-                main = blocks * 16 * row + blocks * (16 // g) * meta
+                main = 0
+                for f in (kf, vf):
+                    r = d * f.bits // 8
+                    m = (16 // g) * O.meta_bytes_per_token(f)
+                    main += blocks * (16 * r + math.ceil(m / r) * r)
             else:
                 main = T * row + (T // g) * meta
             want += L * H * (main + ring * d * 4 + mid_bytes + sd)

@@ -315,6 +315,14 @@ def m_hold_scales_skip_oldest(O):
     O.OracleCache._hold_scales = staticmethod(lambda held, leaving, fmt: O.channel_scales(held[:, 1:], fmt.bits))
 
 
+def m_paged_meta_rows_not_rounded(O):
+    O._unit_pad = lambda row, meta_block: 0
+
+
+def m_paged_meta_padded_to_lines(O):
+    O._unit_pad = lambda row, meta_block: -(-meta_block // 128) * 128 - meta_block
+
+
 MUTATIONS = [v for k, v in sorted(globals().items()) if k.startswith("m_")]
 
 
