@@ -222,7 +222,7 @@ __device__ inline InputLoader input_loader(const AppendArgs& a, int w, size_t he
   return InputLoader{w == 0 ? a.k_new : a.v_new, w == 0 ? a.k_win : a.v_win, head, start, lane};
 }
 
-constexpr TensorKind MID_KIND{CK_I8, MK_F32, false, false, false, 128, 4, 0};
+constexpr TensorKind MID_KIND{CK_I8, MK_F32, false, false, false, 128, 4, 0, 0};
 
 __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(128) append_quantize(AppendArgs a) {
   const float* chan = (w == 0 && k.channel) ? a.k_chan + head * D : nullptr;
   const float* sup = w == 0 ? a.k_super : a.v_super;
   const float super = k.meta == MK_U8 ? sup[head] : 1.0f;
-  quantize_group(k, ld, row, p0, g, meta_elem(a, k, codes, meta, b, h, p0), chan, super, lane);
+  quantize_group(k, ld, row, p0, g, meta_elem(a, k, meta, b, h, p0), chan, super, lane);
 }
 
 // Middle tier: the positions an append moves into the cache's format,
@@ -312,8 +312,8 @@ __global__ void __launch_bounds__(128) append_demote(AppendArgs a) {
   const TensorKind k = w == 0 ? a.kk : a.vk;
   uint8_t* codes = w == 0 ? a.k_codes : a.v_codes;
   auto row = [&](int q) { return code_row(a, k, codes, b, h, q); };
-  quantize_group(k, ld, row, p, 1, meta_elem(a, k, codes, w == 0 ? a.k_meta : a.v_meta, b, h, p),
-                 nullptr, 1.0f, lane);
+  quantize_group(k, ld, row, p, 1, meta_elem(a, k, w == 0 ? a.k_meta : a.v_meta, b, h, p), nullptr,
+                 1.0f, lane);
 }
 
 __global__ void __launch_bounds__(128) append_window(AppendArgs a) {

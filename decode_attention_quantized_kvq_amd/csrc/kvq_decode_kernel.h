@@ -466,13 +466,14 @@ __device__ inline void load_tile(TileRaw<KC, KM, VC, VM, PT>& t, const Addr& ad,
   for (int bb = 0; bb < 2; ++bb) {
     const bool live = t0 + 16 * bb < tend;
     const size_t slot = block_slot<PAGED, RING>(ad, (t0 >> 4) + bb);
-    // the block's code rows and metadata: paged, its unit (16 code rows, then
-    // the metadata elements); otherwise slot rows and metadata element
-    // slot >> gs (one per token group)
+    // the block's code rows and metadata: paged, its units (the key unit's 16
+    // code rows followed by the key and then the value metadata elements);
+    // otherwise slot rows and metadata element slot >> gs (one per token group)
     const uint8_t* kb = PAGED ? ad.k + slot * ad.ku : ad.k + slot * KROW;
     const uint8_t* vb = PAGED ? ad.v + slot * ad.vu : ad.v + slot * VROW;
     kmb[bb] = PAGED ? kb + 16 * KROW : ad.km + (slot >> ad.gs) * Meta<KM>::BYTES;
-    vmb[bb] = PAGED ? vb + 16 * VROW : ad.vm + (slot >> ad.gs) * Meta<VM>::BYTES;
+    vmb[bb] = PAGED ? kmb[bb] + (16 >> ad.gs) * Meta<KM>::BYTES
+                    : ad.vm + (slot >> ad.gs) * Meta<VM>::BYTES;
     const auto rk = rsrc(kb, live ? 16 * KROW : 0);
     if (Codes<KC>::B2) {
       const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rk, o.k0, 0, KVQ_CPOL);
@@ -1800,8 +1801,7 @@ __device__ void step_append(const DecodeArgs& a, int b, int h, int p) {
     uint8_t* codes = const_cast<uint8_t*>(w == 0 ? a.k_codes : a.v_codes);
     uint8_t* meta = const_cast<uint8_t*>(w == 0 ? a.k_meta : a.v_meta);
     auto row = [&](int pos) { return qz::code_row(a, k, codes, b, h, pos); };
-    qz::quantize_group(k, ld, row, p, 1, qz::meta_elem(a, k, codes, meta, b, h, p), nullptr, 1.0f,
-                       lane);
+    qz::quantize_group(k, ld, row, p, 1, qz::meta_elem(a, k, meta, b, h, p), nullptr, 1.0f, lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
@@ -1834,8 +1834,8 @@ __device__ void step_window(const DecodeArgs& a, int b, int h, bool evict) {
       uint8_t* codes = const_cast<uint8_t*>(w == 0 ? a.k_codes : a.v_codes);
       uint8_t* meta = const_cast<uint8_t*>(w == 0 ? a.k_meta : a.v_meta);
       auto crow = [&](int pos) { return qz::code_row(a, k, codes, b, h, pos); };
-      qz::quantize_group(k, ld, crow, e, 1, qz::meta_elem(a, k, codes, meta, b, h, e), nullptr,
-                         1.0f, lane);
+      qz::quantize_group(k, ld, crow, e, 1, qz::meta_elem(a, k, meta, b, h, e), nullptr, 1.0f,
+                         lane);
     }
     // the ring slot of p is the one e held: its values were read above
     const uint16_t* src = (const uint16_t*)(w == 0 ? a.k_new : a.v_new);

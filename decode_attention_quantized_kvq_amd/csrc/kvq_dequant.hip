@@ -87,7 +87,7 @@ __device__ inline void dequant_position(const DequantArgs& a, size_t head, int b
       const uint8_t* row = qz::code_row(a, k, codes, b, h, p);
       // the metadata element of the token's group
       const uint8_t* me = k.channel ? nullptr
-                                    : qz::meta_elem(a, k, codes, w ? a.v_meta : a.k_meta, b, h, p);
+                                    : qz::meta_elem(a, k, w ? a.v_meta : a.k_meta, b, h, p);
       // value = cm * s with cm an integer: c, c - z, or c u (8-bit scale codes)
       float s = 1.0f, z = 0.0f, um = 1.0f;
       if (!k.channel) {

@@ -26,11 +26,21 @@ int meta_bytes(const kvq_tensor_fmt& f) {
 // Tokens per scale (1 = per token).
 static int token_group(const kvq_config* c) { return c->group_tokens > 1 ? c->group_tokens : 1; }
 
-// Code row, metadata element and (paged) unit bytes of one tensor.
-static void set_layout(const kvq_config* c, const kvq_tensor_fmt& f, TensorKind* k) {
-  k->row = row_bytes(f.bits, c->head_dim);
-  k->mb = meta_bytes(f);
-  k->unit = c->block_tokens ? unit_bytes(k->row, 16 / token_group(c) * k->mb) : 0;
+// Code row, metadata element and (paged) unit bytes of the key and value
+// tensors.
+static void set_layout(const kvq_config* c, TensorKind* k, TensorKind* v) {
+  k->row = row_bytes(c->key.bits, c->head_dim);
+  v->row = row_bytes(c->value.bits, c->head_dim);
+  k->mb = meta_bytes(c->key);
+  v->mb = meta_bytes(c->value);
+  k->unit = v->unit = k->moff = v->moff = 0;
+  if (c->block_tokens) {
+    const int per = 16 / token_group(c);
+    k->unit = key_unit_bytes(k->row, per * (k->mb + v->mb));
+    v->unit = 16 * v->row;
+    k->moff = 16 * k->row;
+    v->moff = k->moff + per * k->mb;
+  }
 }
 
 // bf16 ring slots per (sequence, head): the window plus room for the
@@ -73,7 +83,7 @@ static size_t side_bytes(const kvq_tensor_fmt& f, int d) {
 }
 
 kvq_status classify(const kvq_tensor_fmt& f, bool is_key, TensorKind* out) {
-  TensorKind k{CK_I8, MK_NONE, false, false, false, 0, 0, 0};
+  TensorKind k{CK_I8, MK_NONE, false, false, false, 0, 0, 0, 0};
   if (f.scale_fmt != KVQ_SCALE_F32 && f.scale_fmt != KVQ_SCALE_F16 &&
       f.scale_fmt != KVQ_SCALE_U8_SUPER)
     return KVQ_ERR_INVALID_ARG;
@@ -241,8 +251,7 @@ static LayerSizes layer_sizes(const kvq_config* c) {
     // paged: one unit per (block, KV head), its metadata inside it
     const size_t units = (size_t)c->num_blocks * c->num_kv_heads;
     TensorKind k{}, v{};
-    set_layout(c, c->key, &k);
-    set_layout(c, c->value, &v);
+    set_layout(c, &k, &v);
     s.k_codes = units * k.unit;
     s.v_codes = units * v.unit;
   } else {
@@ -377,13 +386,10 @@ size_t kvq_cache_bytes(const kvq_config* cfg, const int32_t* host_seq_lens, kvq_
       alloc_q = std::max<size_t>((size_t)cfg->max_tokens, nq);
     b.padding += L * H * ((alloc_q - nq) * (rk + rv) + (alloc_q - nq) / g * (mk + mv));
     if (cfg->block_tokens) {
-      // the rows that hold a block's metadata, beyond the metadata itself
+      // the key rows that hold a block's metadata, beyond the metadata itself
       TensorKind k{}, v{};
-      set_layout(cfg, cfg->key, &k);
-      set_layout(cfg, cfg->value, &v);
-      const size_t meta_k = 16 / g * mk, meta_v = 16 / g * mv;
-      b.padding += L * H * alloc_q / 16 *
-                   ((k.unit - 16 * rk - meta_k) + (v.unit - 16 * rv - meta_v));
+      set_layout(cfg, &k, &v);
+      b.padding += L * H * alloc_q / 16 * (k.unit - 16 * rk - 16 / g * (mk + mv));
     }
     // the bf16 ring is a fixed buffer per (sequence, head) in both layouts
     if (ring) b.padding += L * H * (ring > nw ? ring - nw : 0) * D * 2 * 2;
@@ -425,8 +431,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int lay
   DequantArgs a{};
   classify(cfg->key, true, &a.kk);
   classify(cfg->value, false, &a.vk);
-  set_layout(cfg, cfg->key, &a.kk);
-  set_layout(cfg, cfg->value, &a.vk);
+  set_layout(cfg, &a.kk, &a.vk);
   if (a.kk.code == CK_BF16 || a.vk.code == CK_BF16) return KVQ_ERR_UNSUPPORTED;
   const LayerSizes s = layer_sizes(cfg);
   uint8_t *kc, *vc, *km, *vm;
@@ -492,8 +497,7 @@ static kvq_status prepare_append(const kvq_config* cfg, const kvq_cache* cache, 
     return KVQ_ERR_INVALID_ARG;
   classify(cfg->key, true, &a.kk);
   classify(cfg->value, false, &a.vk);
-  set_layout(cfg, cfg->key, &a.kk);
-  set_layout(cfg, cfg->value, &a.vk);
+  set_layout(cfg, &a.kk, &a.vk);
   a.k_new = k_new;
   a.v_new = v_new;
   a.new_lens = new_lens;
@@ -598,8 +602,7 @@ static kvq_status prepare_decode(const kvq_config* cfg, const kvq_cache* cache, 
   a.in_bf16 = cfg->in_dtype == KVQ_DT_BF16;
   classify(cfg->key, true, &a.kk);
   classify(cfg->value, false, &a.vk);
-  set_layout(cfg, cfg->key, &a.kk);
-  set_layout(cfg, cfg->value, &a.vk);
+  set_layout(cfg, &a.kk, &a.vk);
   a.qbits = qbits;
   a.ev_begin = opts ? opts->split_begin_event : nullptr;
   a.ev_end = opts ? opts->split_end_event : nullptr;

@@ -36,10 +36,12 @@ struct TensorKind {
   bool grow;      // ... that follow the running absmax (stored codes re-quantized)
   bool hold;      // ... fixed when the sequence's first position leaves the window
   // where the codes and metadata live: row = code bytes of one token; mb =
-  // bytes of one metadata element; unit = paged: bytes of one (block, KV
-  // head) unit, its 16 code rows then its 16 / g metadata elements, padded
-  // to whole rows (0 for a contiguous cache)
-  int row, mb, unit;
+  // bytes of one metadata element; paged caches only: unit = bytes of this
+  // tensor's (block, KV head) unit, moff = byte offset of this tensor's
+  // metadata elements in the key unit (the key unit holds 16 key code rows,
+  // then the block's key and then value metadata elements in whole key rows;
+  // a value unit holds its 16 code rows)
+  int row, mb, unit, moff;
 };
 
 // Code bytes of one token row of one head (0 for unsupported widths).
@@ -47,10 +49,11 @@ inline int row_bytes(int bits, int d) { return d * bits / 8; }
 
 int meta_bytes(const kvq_tensor_fmt& f);
 
-// Bytes of one (block, KV head) unit of a paged cache: 16 code rows, then the
-// block's 16 / g metadata elements in whole rows (P2, "Metadata and block
-// layout remain part of physical memory use": the block carries its scales).
-inline int unit_bytes(int row, int meta_block) {
+// Bytes of one (block, KV head) key unit of a paged cache: 16 key code rows,
+// then the block's key and value metadata (meta_block bytes) in whole key
+// rows (P2, "Metadata and block layout remain part of physical memory use":
+// the block carries its scales).
+inline int key_unit_bytes(int row, int meta_block) {
   return 16 * row + (meta_block + row - 1) / row * row;
 }
 

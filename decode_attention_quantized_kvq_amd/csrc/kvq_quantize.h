@@ -85,7 +85,8 @@ __device__ inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > 
 // alike).  Contiguous: token slot s = (b H_kv + h) max_tokens + p, code row
 // at codes + s row, metadata element s >> gs at meta.  Paged: unit u =
 // block_table[b][p / 16] H_kv + h (the entry clamped into the pool), code row
-// p mod 16 of it, and its metadata elements after its 16 rows.
+// p mod 16 of the tensor's unit u; the metadata elements of both tensors in
+// the key unit u, after its 16 rows (at offset k.moff).
 template <typename Args>
 __device__ inline size_t unit_of(const Args& a, int b, int h, int p) {
   const int phys = clampi(a.block_table[(size_t)b * a.bt_stride + (p >> 4)], 0, a.num_blocks - 1);
@@ -97,10 +98,9 @@ __device__ inline P* code_row(const Args& a, const TensorKind& k, P* codes, int 
   return codes + (((size_t)b * a.hkv + h) * a.max_tokens + p) * k.row;
 }
 template <typename Args, typename P>
-__device__ inline P* meta_elem(const Args& a, const TensorKind& k, P* codes, P* meta, int b, int h,
-                               int p) {
+__device__ inline P* meta_elem(const Args& a, const TensorKind& k, P* meta, int b, int h, int p) {
   if (a.paged)
-    return codes + unit_of(a, b, h, p) * k.unit + 16 * (size_t)k.row +
+    return (P*)a.k_codes + unit_of(a, b, h, p) * a.kk.unit + k.moff +
            (size_t)((p & 15) >> a.tgshift) * k.mb;
   return meta + ((((size_t)b * a.hkv + h) * a.max_tokens + p) >> a.tgshift) * k.mb;
 }

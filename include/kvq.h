@@ -64,17 +64,21 @@
  *  contiguous (block_tokens == 0):
  *    codes  [L][B][H_kv][max_tokens][row]
  *    meta   [L][B][H_kv][max_tokens / g] of the meta element below
- *  paged (block_tokens == 16): one unit per (block, KV head) and tensor,
- *    its 16 code rows followed by the block's 16 / g meta elements, which
- *    take whole rows (U = 16 + ceil(16 / g * meta bytes / row) rows, the
- *    rest of the last row unused):
- *    codes  [L][num_blocks][H_kv][U][row]   (no separate meta buffer: the
- *           k_meta / v_meta pointers are not read)
- *    quantized position p of sequence b lives in unit
- *    (block_table[b][p / 16], h), row p % 16; its meta element is
- *    (p % 16) / g, at byte 16 row + ((p % 16) / g) * (meta bytes) of the
- *    unit.  A decode reads each block's codes and scales from one place
- *    (scattered 64-byte scale runs cost about twice their bytes in time).
+ *  paged (block_tokens == 16): per (block, KV head) a key unit and a value
+ *    unit.  The key unit holds the 16 key code rows, then the block's 16 / g
+ *    key meta elements and its 16 / g value meta elements, in whole key rows
+ *    (UK = 16 + ceil(16 / g * (key + value meta bytes) / row_K) rows, the
+ *    rest of the last row unused); the value unit holds the 16 value rows:
+ *    k_codes [L][num_blocks][H_kv][UK][row_K]
+ *    v_codes [L][num_blocks][H_kv][16][row_V]
+ *    (no separate meta buffers: the k_meta / v_meta pointers are not read)
+ *    quantized position p of sequence b lives in units
+ *    (block_table[b][p / 16], h), row p % 16; its key meta element at byte
+ *    16 row_K + ((p % 16) / g) * (key meta bytes) of the key unit, its value
+ *    meta element at byte 16 row_K + (16 / g) * (key meta bytes) +
+ *    ((p % 16) / g) * (value meta bytes).  A decode reads each block's scales
+ *    with its key codes, one line for both tensors (scattered 64-byte scale
+ *    runs cost about twice their bytes in time).
  *  ring   [L][B][H_kv][R][D] bf16 with R = window (+ g if g > 1); position
  *    p sits in slot p % R
  *  middle tier (mid_tokens = M > 0): codes [L][B][H_kv][M + 32][D] int8 and
@@ -237,8 +241,8 @@ typedef struct {
   size_t window;    /* bf16 recent tokens of K and V */
   size_t padding;   /* allocated but unused slots (code and metadata slots
                        past a sequence's tokens, the unfilled tail of its last
-                       16-token block, the unused end of the rows that hold a
-                       paged block's metadata, unused bf16 ring and
+                       16-token block, the unused end of the key rows that
+                       hold a paged block's metadata, unused bf16 ring and
                        middle-tier slots) */
   size_t workspace; /* bytes of the decode workspace kvq_decode_attn needs
                        at the library's split for the longest of the

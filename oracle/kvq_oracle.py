@@ -105,9 +105,10 @@ Readings where the pages leave a step open (each restated where it is used):
   R27 where a paged block keeps its metadata (P2 "Metadata and block layout
       remain part of physical memory use": the block layout is part of what
       is allocated; the pages fix no layout): each (block, KV head) of a
-      paged cache is one unit, its 16 code rows followed by its 16 / g
-      metadata elements, which take whole code rows; the rest of the last of
-      those rows is padding.
+      paged cache is a key unit, its 16 key code rows followed by its 16 / g
+      key and then 16 / g value metadata elements in whole key code rows,
+      and a value unit of its 16 value code rows; the rest of the last
+      metadata row is padding.
   Scale underflow: a scale that rounds to 0 in its storage type is replaced by
   that type's smallest positive value (fp32 2^-149, fp16 2^-24); an fp16 scale
   above 65504 saturates to 65504.
@@ -704,8 +705,9 @@ def ring_slots(window: int = 0, group: int = 1) -> int:
 
 
 def _unit_pad(row: int, meta_block: int) -> int:
-    """Reading R27: a paged block keeps its metadata in whole code rows after
-    its own; the unused end of the last of those rows is padding."""
+    """Reading R27: a paged block keeps its key and value metadata in whole
+    key code rows after its 16 key rows; the unused end of the last of those
+    rows is padding."""
     return -(-meta_block // row) * row - meta_block
 
 
@@ -733,7 +735,7 @@ def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
               ring is one fixed-size buffer per sequence and head in both
               layouts: P2 "Metadata and block layout remain part of physical
               memory use" counts what is allocated, not only what is used);
-              in a paged cache, the rest of the code rows that hold each
+              in a paged cache, the rest of the key code rows that hold each
               block's metadata (reading R27).
     total     the sum of the four.
     """
@@ -760,9 +762,8 @@ def cache_bytes(key: TensorFormat, value: TensorFormat, layers: int, hkv: int,
             alloc_q = max_tokens if max_tokens is not None else n_q
         out["padding"] += layers * hkv * ((alloc_q - n_q) * codes + (alloc_q - n_q) // group * meta)
         if block_tokens:
-            out["padding"] += layers * hkv * (alloc_q // block_tokens) * (
-                _unit_pad(row(key), block_tokens // group * meta_bytes_per_token(key))
-                + _unit_pad(row(value), block_tokens // group * meta_bytes_per_token(value)))
+            out["padding"] += layers * hkv * (alloc_q // block_tokens) * _unit_pad(
+                row(key), block_tokens // group * meta)
         if ring:
             out["padding"] += layers * hkv * (ring - n_w) * d * 2 * 2
     out["total"] = out["payload"] + out["metadata"] + out["window"] + out["padding"]

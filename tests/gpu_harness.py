@@ -177,11 +177,15 @@ def meta_elem_bytes(spec) -> int:
     return 2 * w if spec.get("zero_point") else w
 
 
-def unit_rows(wl, spec) -> int:
-    """Rows of one paged (block, KV head) unit as the header documents it: 16
-    code rows, then the block's 16 / g metadata elements in whole rows."""
-    row = wl["d"] * spec["bits"] // 8
-    meta = 16 // wl.get("group", 1) * meta_elem_bytes(spec)
+def unit_rows(wl, t: str) -> int:
+    """Rows of one paged (block, KV head) unit of tensor t as the header
+    documents it: a key unit holds 16 key code rows, then the block's 16 / g
+    key and 16 / g value metadata elements in whole key rows; a value unit
+    its 16 value code rows."""
+    if t == "v":
+        return 16
+    row = wl["d"] * wl["key"]["bits"] // 8
+    meta = 16 // wl.get("group", 1) * (meta_elem_bytes(wl["key"]) + meta_elem_bytes(wl["value"]))
     return 16 + -(-meta // row)
 
 
@@ -192,8 +196,7 @@ def token_slots(bt: Built, b: int, h: int, n: int, t: str = "k") -> np.ndarray:
     p = np.arange(n)
     if cfg.block_tokens:
         phys = bt.table[b, p // 16].astype(np.int64)
-        U = unit_rows(bt.wl, bt.wl["key" if t == "k" else "value"])
-        return (phys * cfg.num_kv_heads + h) * U + p % 16
+        return (phys * cfg.num_kv_heads + h) * unit_rows(bt.wl, t) + p % 16
     return (b * cfg.num_kv_heads + h) * cfg.max_tokens + p
 
 
@@ -233,11 +236,14 @@ def device_records(bt: Built, t: str, b: int, h: int, n: int) -> dict:
     g = bt.wl.get("group", 1)
     mb = meta_elem_bytes(spec)
     if bt.cfg.block_tokens:
-        # paged: the elements follow the 16 code rows of each block's unit
+        # paged: the key elements, then the value elements, follow the 16
+        # code rows of each block's key unit
         p = np.arange(0, n, g)
-        unit = (bt.table[b, p // 16].astype(np.int64) * bt.cfg.num_kv_heads + h) * unit_rows(bt.wl, spec)
-        off = (unit + 16) * row + (p % 16) // g * mb
-        flat = bt.cache.buffers[f"{t}_codes"].view(-1)
+        krow = D * bt.wl["key"]["bits"] // 8
+        unit = (bt.table[b, p // 16].astype(np.int64) * bt.cfg.num_kv_heads + h) * unit_rows(bt.wl, "k")
+        first = 0 if t == "k" else 16 // g * meta_elem_bytes(bt.wl["key"])
+        off = (unit + 16) * krow + first + (p % 16) // g * mb
+        flat = bt.cache.buffers["k_codes"].view(-1)
         idx = torch.from_numpy((off[:, None] + np.arange(mb)).reshape(-1)).to(flat.device)
         meta = host(flat.index_select(0, idx))
         slots = np.arange(len(p))

@@ -1095,10 +1095,22 @@ def pin_byte_accounting(O):
     lens = [1024, 5000, 32768]
     assert O.decode_traffic(i8, i8, 8, 128, lens, window=128) == sum(8 * (65536 + (n - 128) * 264) for n in lens)
     pad = O.cache_bytes(i8, i8, 1, 8, 128, [145], window=128, block_tokens=16)
-    # 17 quantized positions in 2 blocks: 15 unused slots; and in each block
-    # of K and of V, the 16 fp32 scales (64 B) fill half of a 128-byte code
-    # row (R27)
-    assert pad["padding"] == 8 * ((16 - 17 % 16) * 264 + 2 * 2 * 64)
+    # 17 quantized positions in 2 blocks: 15 unused slots (each block's 16 K
+    # and 16 V fp32 scales fill one 128-byte key row, R27)
+    assert pad["padding"] == 8 * (16 - 17 % 16) * 264
+    pad = O.cache_bytes(a4, a4, 1, 8, 128, [145], window=128, block_tokens=16)
+    # uint4 rows of 64 B: a block's 2 x 16 fp16 scale + zero point pairs
+    # (128 B) fill two key rows
+    assert pad["padding"] == 8 * (16 - 17 % 16) * 136
+    u8s = O.TensorFormat(2, scale="u8_super")
+    pad = O.cache_bytes(u8s, u8s, 1, 8, 128, [145], window=128, block_tokens=16)
+    # 2-bit rows of 32 B: 2 x 16 scale codes (32 B) fill one key row
+    assert pad["padding"] == 8 * (16 - 17 % 16) * 66
+    kc4 = O.cache_bytes(O.TensorFormat(8, "channel"), O.TensorFormat(4, scale="u8_super"), 1, 8, 128,
+                        [145], window=128, block_tokens=16)
+    # per-channel keys have no per-token element: the 16 value scale codes
+    # take one 128-byte key row, 112 B of it unused, in each of the 2 blocks
+    assert kc4["padding"] == 8 * ((16 - 17 % 16) * 193 + 2 * 112)
 
 
 def pin_allocated_bytes(O):
@@ -1110,9 +1122,9 @@ def pin_allocated_bytes(O):
     W (+ g) slots, a middle-tier ring of M + 32 int8 rows with fp32 scales,
     and its per-head side data; a paged one holds whole 16-token blocks of
     the quantized positions (counted by brute force, position by position),
-    each block of each tensor a unit of 16 code rows plus its 16 / g
-    metadata elements rounded up to whole code rows (reading R27), the same
-    ring and side data."""
+    each block a key unit of 16 key code rows plus its key and value
+    metadata elements rounded up to whole key rows and a value unit of 16
+    value code rows (reading R27), the same ring and side data."""
     rng = _rng(223)
     fmts = [(O.TensorFormat(8), O.TensorFormat(8)),
             (O.TensorFormat(4, zero_point=True, scale="f16"), O.TensorFormat(4, zero_point=True, scale="f16")),
@@ -1146,11 +1158,9 @@ def pin_allocated_bytes(O):
                 # older than the window
                 nq = sum(1 for p in range(n) if (p // g) * g + g <= n - W)
                 blocks = -(-nq // 16)
-                main = 0
-                for f in (kf, vf):
-                    r = d * f.bits // 8
-                    m = (16 // g) * O.meta_bytes_per_token(f)
-                    main += blocks * (16 * r + math.ceil(m / r) * r)
+                rk, rv = d * kf.bits // 8, d * vf.bits // 8
+                m = (16 // g) * meta
+                main = blocks * (16 * rk + math.ceil(m / rk) * rk + 16 * rv)
             else:
                 main = T * row + (T // g) * meta
             want += L * H * (main + ring * d * 4 + mid_bytes + sd)

@@ -118,9 +118,11 @@ def test_buffer_sizes():
     wl = synth.workload(4)
     cfg = cfg_of(wl, num_layers=2)
     sz = K.buffer_sizes(cfg)
-    # paged: one unit per (block, KV head), 16 code rows of 128 B and the
-    # block's 16 fp32 scales in one more row; no separate metadata buffer
+    # paged: per (block, KV head) a key unit of 16 code rows of 128 B and one
+    # more row holding the block's 16 key and 16 value fp32 scales, and a
+    # value unit of 16 rows; no separate metadata buffers
     assert sz.k_codes == 2 * 100 * 8 * 17 * 128 and sz.k_meta == 0
+    assert sz.v_codes == 2 * 100 * 8 * 16 * 128 and sz.v_meta == 0
     assert sz.k_win == 2 * 64 * 8 * 128 * 128 * 2 and sz.k_chan_scale == 0
     wl5 = synth.workload(5)
     sz5 = K.buffer_sizes(cfg_of(wl5))
