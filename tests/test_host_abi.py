@@ -114,6 +114,34 @@ def test_cache_bytes_metadata_cases():
         assert got["payload"] == 2 * 5 * 2 * 128 * 74 * bits // 8
 
 
+def test_paged_unit_sizes():
+    """Paged units as the header documents them: a key unit of 16 key rows
+    plus the block's key and value metadata in whole key rows, a value unit
+    of 16 value rows."""
+    def paged(key, value, group=1):
+        cfg = K.make_config(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, max_tokens=0,
+                            key=key, value=value, block_tokens=16, num_blocks=10,
+                            max_blocks_per_seq=5, group_tokens=group)
+        return K.buffer_sizes(cfg)
+    units = 10 * 2
+    # uint4 with fp16 scale + zero point: 64-byte rows, 2 x 16 x 4 B = two rows
+    z4 = dict(bits=4, zero_point=True, scale="f16")
+    s = paged(z4, z4)
+    assert s.k_codes == units * 18 * 64 and s.v_codes == units * 16 * 64 and s.k_meta == s.v_meta == 0
+    # int2 with 8-bit scale codes: 32-byte rows, 2 x 16 x 1 B = one row
+    u2 = dict(bits=2, scale="u8_super")
+    s = paged(u2, u2)
+    assert s.k_codes == units * 17 * 32 and s.v_codes == units * 16 * 32
+    # per-channel int8 keys (no per-token element), int4 values with 8-bit
+    # scale codes: the 16 value codes take one 128-byte key row
+    s = paged(dict(bits=8, axis="channel"), dict(bits=4, scale="u8_super"))
+    assert s.k_codes == units * 17 * 128 and s.v_codes == units * 16 * 64
+    # uint2 with one fp16 scale + zero point per 16-token group: 2 x 4 B in
+    # one 32-byte key row
+    s = paged(dict(bits=2, zero_point=True, scale="f16"), dict(bits=2, zero_point=True, scale="f16"), 16)
+    assert s.k_codes == units * 17 * 32 and s.v_codes == units * 16 * 32
+
+
 def test_buffer_sizes():
     wl = synth.workload(4)
     cfg = cfg_of(wl, num_layers=2)
