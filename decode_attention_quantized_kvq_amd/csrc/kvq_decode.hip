@@ -13,10 +13,11 @@
 //
 // decode_split: one workgroup of 4 waves per work item (a chunk of one
 // sequence's tokens for one KV head, that sequence's bf16 window, or its
-// middle tier).  Each wave streams 32-token tiles of its quarter of the chunk
-// straight from HBM into registers with buffer loads (two tiles in flight)
-// and runs both contractions on the matrix cores, transposed so that the
-// query heads are the rows:
+// middle tier).  Each wave streams every fourth 32-token tile of the chunk
+// (the four waves read adjacent tiles at once) straight from HBM into
+// registers with buffer loads (two tiles in flight) and runs both
+// contractions on the matrix cores, transposed so that the query heads are
+// the rows:
 //   scores  S^T[16 rows x 16 tok] += Q'[16 rows x 32 d] K^T[32 d x 16 tok]
 //           (int8: the query as an exact integer in three int8 limbs per
 //           head against the integer codes, int32 sums)

@@ -335,9 +335,11 @@ typedef struct {
   int query_bits;           /* 0: the query is not quantized (its scale moves
                                onto integer limbs exactly); 8: the integer-query
                                path of P3, "Precision floors and mixed cache
-                               formats": per query head s = fl32(amax / 127),
-                               Q = rint(fl32(q / s)) in [-127, 127], and every
-                               score uses Q s (window tokens too).  8 is not
+                               formats": per query head s = fl64(amax / 127),
+                               Q = clamp(rint(fl64(q / s))) in [-127, 127]
+                               (the fp64 quotient of the cache's quantizer),
+                               and every score uses Q s, with s rounded to
+                               fp32 in the score scale (window tokens too).  8 is not
                                run with per-channel keys (KVQ_ERR_UNSUPPORTED);
                                other values are KVQ_ERR_INVALID_ARG. */
 } kvq_decode_opts;
