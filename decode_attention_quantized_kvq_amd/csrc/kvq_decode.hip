@@ -13,9 +13,10 @@
 //
 // decode_split: one workgroup of 4 waves per work item (a chunk of one
 // sequence's tokens for one KV head, that sequence's bf16 window, or its
-// middle tier).  Each wave streams every fourth 32-token tile of the chunk
-// (the four waves read adjacent tiles at once) straight from HBM into
-// registers with buffer loads (two tiles in flight) and runs both
+// middle tier).  Each wave streams its share of the chunk's 32-token tiles
+// (every fourth tile with 8-bit keys, so that the four waves read adjacent
+// tiles at once; a contiguous quarter for narrower tokens) straight from HBM
+// into registers with buffer loads (one or two tiles in flight) and runs both
 // contractions on the matrix cores, transposed so that the query heads are
 // the rows:
 //   scores  S^T[16 rows x 16 tok] += Q'[16 rows x 32 d] K^T[32 d x 16 tok]

@@ -361,11 +361,13 @@ struct Addr {
   size_t head_tok;       // contiguous: first token slot of this head
   int nblk;              // blocks holding tokens
   int rblk;              // ring (middle tier): blocks of the ring, block i in slot i mod rblk
-  // paged: block-table entries of this wave's blocks.  A wave takes every
-  // WAVES-th tile of its chunk, i.e. blocks blk0 + 2 WAVES k + c (c = 0, 1)
-  // for its k-th tile; entry e = 2k + c sits in lane e & 63 of ent[e >> 6].
+  // paged: block-table entries of this wave's blocks.  A wave whose tiles
+  // are every WAVES-th of its chunk (ilv) has blocks blk0 + 2 WAVES k + c
+  // (c = 0, 1) for its k-th tile, entry e = 2k + c; a wave with a contiguous
+  // range has blocks blk0 + e.  Entry e sits in lane e & 63 of ent[e >> 6].
   int blk0;
   int ent[2];
+  bool ilv;
 };
 
 // Table entries a wave holds: 64 tiles, 2048 of a chunk's tokens.
@@ -386,8 +388,8 @@ __device__ inline size_t block_slot(const Addr& ad, int blk) {
     // this wave's blocks; they only occur for blocks past the chunk, whose
     // loads read nothing)
     int i = blk - ad.blk0;
-    i = ((i >> 3) << 1) | (i & 1);
     static_assert(2 * WAVES == 8, "entry index: tile k of a wave starts 8 blocks after tile k - 1");
+    if (ad.ilv) i = ((i >> 3) << 1) | (i & 1);
     i = i < 0 ? 0 : (i >= WAVE_BLOCKS ? WAVE_BLOCKS - 1 : i);
     int phys = i < 64 ? __builtin_amdgcn_readlane(ad.ent[0], i)
                       : __builtin_amdgcn_readlane(ad.ent[1], i - 64);
@@ -1631,29 +1633,48 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
   ad.ent[0] = ad.ent[1] = 0;
   ad.head_tok = head_tok;
   const LaneOff lo = lane_offsets<KC, KM, VC, VM>(lt, g, a.tgshift);
-  // The chunk's tiles dealt round-robin over the waves: wave w takes tiles
+  // Tiles of the chunk per wave.  ILV: dealt round-robin, wave w takes tiles
   // w, w + WAVES, w + 2 WAVES, ... (its k-th tile starts at w0 + k STRIDE),
-  // so that the workgroup's waves read adjacent tiles at the same time.  On
-  // one MI355X a read of 268 MB in this launch shape streamed 6.46 TB/s so
-  // against 6.08 with a contiguous quarter of the chunk per wave.  Every
-  // wave masks against the chunk's end.
-  constexpr int STRIDE = WAVES * TILE;
-  const int w0 = __builtin_amdgcn_readfirstlane(tok0 + wave * TILE);
-  const int w1 = tok1;
-  const int nchunk = tok1 > tok0 ? (tok1 - tok0 + TILE - 1) / TILE : 0;
-  const int ntile = __builtin_amdgcn_readfirstlane(nchunk > wave ? (nchunk - wave + WAVES - 1) / WAVES : 0);
+  // so that the workgroup's waves read adjacent tiles at the same time, and
+  // every wave masks against the chunk's end.  Otherwise each wave streams
+  // a contiguous quarter of the chunk.  Measured on one MI355X: with 8-bit
+  // keys round-robin is faster (gqa_int8 20.1 -> 19.2-19.6 us, asym_kv
+  // 257.5 -> 252.6 us, paged_mixed unchanged); with narrower tokens it is
+  // not (int4_asym 51.5 -> 52.7 us over six runs, the 2-bit and tiered
+  // workloads unchanged).  A plain read of 268 MB in this launch shape
+  // streamed 6.46 TB/s round-robin against 6.08 in quarters.
+  constexpr int ROWB = Codes<KC>::ROW + Codes<VC>::ROW;
+  constexpr bool ILV = ROWB >= 192;
+  constexpr int STRIDE = ILV ? WAVES * TILE : TILE;
+  int w0, w1, ntile;
+  if constexpr (ILV) {
+    w0 = __builtin_amdgcn_readfirstlane(tok0 + wave * TILE);
+    w1 = tok1;
+    const int nchunk = tok1 > tok0 ? (tok1 - tok0 + TILE - 1) / TILE : 0;
+    ntile = __builtin_amdgcn_readfirstlane(nchunk > wave ? (nchunk - wave + WAVES - 1) / WAVES : 0);
+  } else {
+    const int per = (tok1 - tok0 + WAVES * TILE - 1) / (WAVES * TILE) * TILE;
+    w0 = __builtin_amdgcn_readfirstlane(tok0 + wave * per);
+    w1 = __builtin_amdgcn_readfirstlane(min(w0 + per, tok1));
+    ntile = w1 > w0 ? (w1 - w0 + TILE - 1) / TILE : 0;
+  }
+  ad.ilv = ILV;
   if constexpr (PAGED) {  // this wave's block-table entries (64 tiles, 128 blocks)
     const int32_t* row = a.block_table + (size_t)b * a.bt_stride;
     const int lim = a.bt_stride - 1;
     ad.blk0 = w0 >> 4;
-    ad.ent[0] = row[min(ad.blk0 + 2 * WAVES * (lane >> 1) + (lane & 1), lim)];
-    ad.ent[1] = row[min(ad.blk0 + 2 * WAVES * (32 + (lane >> 1)) + (lane & 1), lim)];
+    if constexpr (ILV) {
+      ad.ent[0] = row[min(ad.blk0 + 2 * WAVES * (lane >> 1) + (lane & 1), lim)];
+      ad.ent[1] = row[min(ad.blk0 + 2 * WAVES * (32 + (lane >> 1)) + (lane & 1), lim)];
+    } else {
+      ad.ent[0] = row[min(ad.blk0 + lane, lim)];
+      ad.ent[1] = row[min(ad.blk0 + 64 + lane, lim)];
+    }
   }
   // The scheduling barriers keep each tile's loads together and in order
   // (first tile, second, ..., then the refills): the compiler derives its
   // wait counts from that order, and interleaved loads would make every wait
   // in the loop a wait for all of them.
-  constexpr int ROWB = Codes<KC>::ROW + Codes<VC>::ROW;
   constexpr int NB = ROWB >= 256 ? KVQ_NB8 : ROWB >= 192 ? KVQ_NB6 : ROWB >= 128 ? KVQ_NB4 : KVQ_NB2;
   // pre (a decode step's move of the token leaving the window into the
   // cache, at hold_pos): run by the wave whose range holds that position
@@ -1664,9 +1685,8 @@ __device__ void quant_range(const DecodeArgs& a, int b, int h, int tok0, int tok
   // tile j - NB, so a position in tile 2 NB or later may be moved while the
   // first tiles are in flight; one in an earlier tile is moved first and
   // waited for.
-  const bool mover = hold_pos >= 0 && (hold_pos >= tok0 && hold_pos < tok1
-                                           ? (hold_pos - tok0) / TILE % WAVES == wave
-                                           : wave == 0);
+  const bool mine = ILV ? (hold_pos - tok0) / TILE % WAVES == wave : hold_pos >= w0 && hold_pos < w1;
+  const bool mover = hold_pos >= 0 && (hold_pos >= tok0 && hold_pos < tok1 ? mine : wave == 0);
   const bool move_first = mover && hold_pos < w0 + 2 * NB * STRIDE;
   if (move_first) {
     pre();
