@@ -578,3 +578,56 @@ def test_decode_step(fmt, paged, window, dt):
             assert torch.equal(buf, other.buffers[name]), f"{name} differs after the step"
     assert torch.equal(got, want), "decode step output differs from append + decode"
     assert bool(torch.isfinite(got).all())
+
+
+def _library_split(max_len, window, pairs):
+    """The split the host picks for 8-bit paged caches (the documented rule:
+    about 512 workgroups, a multiple of 128 tokens, 256..8192 when paged)."""
+    nq = max(max_len - window, 0)
+    per = -(-nq * pairs // 512)
+    per = -(-max(per, 1) // 128) * 128
+    return min(max(per, 256), 8192)
+
+
+def test_decode_step_late_eviction():
+    """The fused step of a paged int8 cache with a bf16 window, with the token
+    leaving the window deep in the last chunk: with 8-bit keys each wave takes
+    every fourth tile of its chunk, and a token in the wave's fifth tile or
+    later is moved into the cache while the wave's first tiles are in flight.
+    Here the split is 640 tokens (20 tiles) and the leaving tokens sit in
+    tiles 18 and 16 (waves 2 and 0, their fifth tile).  Every cache buffer
+    and the output equal those of append + decode bit for bit."""
+    H.log("case: decode step, token leaving the window in a late tile")
+    max_len = 20000
+    wl = synth.workload(4, batch=2, tokens=max_len)
+    W, pairs = wl["window"], 2 * wl["hkv"]
+    S = _library_split(max_len, W, pairs)
+    assert S == 640
+    # quantized positions after the step: the last one (the token leaving the
+    # window) at offset r of its chunk
+    nq_after = [S * 30 + 600 + 1, S * 25 + 520 + 1]
+    for n in nq_after:
+        tile = ((n - 1) % S) // 32
+        assert tile // 4 >= 4, "the leaving token must sit past the wave's first 2 NB tiles"
+    pre = [n + W - 1 for n in nq_after]
+    assert max(pre) + 1 <= max_len
+    bt = H.build(wl, pre, oracle=False, table_lens=[n + 1 for n in pre])
+    other = K.KvqCache(bt.cfg, "cuda", bt.cache.block_table)
+    for name, buf in bt.cache.buffers.items():
+        if buf is not None:
+            other.buffers[name].copy_(buf)
+    gen = torch.Generator().manual_seed(11)
+    k1, v1 = (torch.randn((2, wl["hkv"], 1, 128), generator=gen).to(torch.bfloat16).cuda()
+              for _ in range(2))
+    lens = torch.tensor([n + 1 for n in pre], dtype=torch.int32, device="cuda")
+    bt.cache.seq_lens.copy_(lens)
+    other.seq_lens.copy_(lens)
+    q = H.to_device(H.queries(wl), wl["in_dtype"])
+    got = K.decode_step(bt.cache, 0, k1, v1, q, max_len)
+    K.quantize_append(other, 0, k1, v1)
+    want = K.decode_attn(other, 0, q, max_len)
+    torch.cuda.synchronize()
+    for name, buf in bt.cache.buffers.items():
+        if buf is not None:
+            assert torch.equal(buf, other.buffers[name]), f"{name} differs after the step"
+    assert torch.equal(got, want), "decode step output differs from append + decode"
